@@ -1,0 +1,93 @@
+"""The oracle's pins are strong enough to notice plausible mistakes.
+
+Each case plants one mistake in a temporary copy of the oracle's C source (a dropped term,
+a wrong sign, a swapped operand, a wrong constant, an off-by-one index), builds it, and runs
+the oracle pin suites against the broken build in a fresh process.  Every mutant must fail
+at least one pin.  The real oracle is never modified.
+"""
+import os
+import subprocess
+import sys
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "tfp8_oracle.c")
+
+# (name, text to find, replacement, occurrence index to replace: 0 = first)
+MUTANTS = [
+    ("m2 without /B", "double m2 = sumsq / B;", "double m2 = sumsq;", 0),
+    ("alpha from m2/T", "double a = sqrt(T / m2);", "double a = sqrt(m2 / T);", 0),
+    ("no alpha clamp", "a = fmin(fmax(a, 0x1p-126), 0x1p126);\n  float alpha", "\n  float alpha", 0),
+    ("prescale dropped", "y[i] = (double)alpha * v[i];", "y[i] = v[i];", 0),
+    ("butterfly sign", "v[j + h] = a - b;", "v[j + h] = b - a;", 0),
+    ("Hadamard entry or", "(i & j)", "(i | j)", 0),
+    ("no 1/sqrt(B)", "for (int i = 0; i < B; ++i) y[i] = y[i] / rootB;", "", 0),
+    ("Qmax 240", "my / 448.0", "my / 240.0", 0),
+    ("encode half-up", "double k = nearbyint(ldexp(a, 3 - E));",
+     "double k = floor(ldexp(a, 3 - E) + 0.5);", 0),
+    ("encode subnormal half-up", "nearbyint(a * 512.0)", "floor(a * 512.0 + 0.5)", 0),
+    ("encode loses -0", "uint8_t sign = signbit(v) ? 0x80 : 0x00;",
+     "uint8_t sign = (v < 0) ? 0x80 : 0x00;", 0),
+    ("encode no saturation", "if (!(a <= 448.0)) return sign | 0x7E;", "", 0),
+    ("decode subnormal step", "ldexp((double)m, -9)", "ldexp((double)m, -10)", 0),
+    ("decode bias", "ldexp(1.0 + m / 8.0, e - 7)", "ldexp(1.0 + m / 8.0, e - 8)", 0),
+    ("bf16 round half-up", "double r = nearbyint(a / step) * step;",
+     "double r = floor(a / step + 0.5) * step;", 0),
+    ("zero block alpha 0", "*alpha_out = 1.0f;", "*alpha_out = 0.0f;", 0),
+    ("decompress no 1/alpha", "out[i] = out[i] / rootB / (double)alpha;",
+     "out[i] = out[i] / rootB;", 0),
+    ("decompress times alpha", "out[i] = out[i] / rootB / (double)alpha;",
+     "out[i] = out[i] / rootB * (double)alpha;", 0),
+    ("decompress no rotation", "  tfp8_ref_fwht(out, B);\n", "\n", 0),
+    ("decompress scale dropped", "out[i] = (double)scale * cval[i];", "out[i] = cval[i];", 0),
+    ("reduce drops last", "for (int p = 0; p < P; ++p) {\n      const uint8_t *q",
+     "for (int p = 0; p < P - 1; ++p) {\n      const uint8_t *q", 0),
+    ("reduce wrong scale index", "decompress_block(c, alpha[(int64_t)p * nb + k], scale[(int64_t)p * nb + k]",
+     "decompress_block(c, alpha[k], scale[k]", 0),
+    ("rotated reduce s/alpha swapped", "double g = (double)s / (double)alpha[(int64_t)p * nb + k];",
+     "double g = (double)alpha[(int64_t)p * nb + k] / (double)s;", 0),
+    ("rotated reduce no /448", "(double)alpha2 * ar / 448.0", "(double)alpha2 * ar", 0),
+]
+
+
+def _apply(src, find, repl, occ):
+    idx = -1
+    for _ in range(occ + 1):
+        idx = src.find(find, idx + 1)
+        assert idx >= 0, f"mutation anchor not found: {find!r}"
+    return src[:idx] + repl + src[idx + len(find):]
+
+
+def _run_mutant(case, tmpdir):
+    name, find, repl, occ = case
+    sys.path.insert(0, os.path.join(ROOT, "oracle"))
+    import build as oracle_build
+
+    src = open(SRC).read()
+    mutated = _apply(src, find, repl, occ)
+    assert mutated != src
+    d = os.path.join(tmpdir, name.replace(" ", "_").replace("/", "_"))
+    os.makedirs(d)
+    msrc = os.path.join(d, "tfp8_oracle.c")
+    with open(msrc, "w") as f:
+        f.write(mutated)
+    lib = oracle_build.build(src=msrc, out=os.path.join(d, "libmutant.so"))
+    env = dict(os.environ, TFP8_ORACLE_LIB=lib, OMP_NUM_THREADS="2")
+    cmd = [sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+           os.path.join(ROOT, "tests", "test_oracle_codec.py"),
+           os.path.join(ROOT, "tests", "test_oracle_method.py")]
+    r = subprocess.run(cmd, cwd=ROOT, env=env, capture_output=True, text=True, timeout=900)
+    return name, r.returncode, r.stdout[-1500:]
+
+
+def test_every_mutant_is_caught():
+    from concurrent.futures import ThreadPoolExecutor
+
+    workers = max(1, min(8, len(os.sched_getaffinity(0))))
+    with tempfile.TemporaryDirectory() as tmp, ThreadPoolExecutor(workers) as ex:
+        results = list(ex.map(lambda c: _run_mutant(c, tmp), MUTANTS))
+    survivors = [(n, out) for n, rc, out in results if rc != 1]
+    assert not survivors, "mutants not caught by the oracle pins: " + "; ".join(
+        f"{n}: {out}" for n, out in survivors)

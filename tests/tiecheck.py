@@ -1,0 +1,84 @@
+"""Comparison helpers shared by the oracle self-tests and the GPU parity tests.
+
+Nothing here computes any part of the compression itself: these functions only decide
+whether two results agree to the stated bar.
+
+Code agreement ("identical except at most 1 ULP at rounding ties on <= 1e-4 of elements"):
+a mismatch between a code and the reference code is admissible only when
+
+  (i)  the two codes are adjacent E4M3 values (same sign, one step apart) or the +0/-0 pair;
+  (ii) the reference's exact quotient t = y/s (the value the reference rounded) lies within
+       ``rel * |mid| + abs_`` of the midpoint between the two code values (or of 0 for a
+       +0/-0 pair), i.e. it is a rounding tie up to the other side's arithmetic error; and
+  (iii) the number of mismatches is at most ``max_frac`` of the elements.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# Exact E4M3FN values, written from the format definition (bias 7, 3 mantissa bits,
+# subnormal step 2^-9, 0x7F/0xFF NaN); independent of the oracle's decoder and checked
+# against torch.float8_e4m3fn in the oracle tests.
+_E4M3 = np.empty(256, np.float64)
+for _c in range(256):
+    _s = -1.0 if _c & 0x80 else 1.0
+    _e = (_c >> 3) & 15
+    _m = _c & 7
+    if _e == 15 and _m == 7:
+        _E4M3[_c] = np.nan
+    elif _e == 0:
+        _E4M3[_c] = _s * _m * 2.0 ** -9
+    else:
+        _E4M3[_c] = _s * (1 + _m / 8) * 2.0 ** (_e - 7)
+E4M3_VALUES = _E4M3
+
+TIE_REL = 2.0 ** -20
+TIE_ABS = 2.0 ** -11
+MAX_TIE_FRAC = 1e-4
+
+
+def code_mismatches(got: np.ndarray, ref: np.ndarray, quot: np.ndarray, rel: float = TIE_REL,
+                    abs_: float = TIE_ABS):
+    """Return (n_mismatch, n_inadmissible, first_bad_index or -1)."""
+    got = np.asarray(got, np.uint8).reshape(-1)
+    ref = np.asarray(ref, np.uint8).reshape(-1)
+    quot = np.asarray(quot, np.float64).reshape(-1)
+    bad = np.nonzero(got != ref)[0]
+    if bad.size == 0:
+        return 0, 0, -1
+    g, r, t = got[bad], ref[bad], quot[bad]
+    gs, rs = g >> 7, r >> 7
+    gm, rm = (g & 0x7F).astype(np.int32), (r & 0x7F).astype(np.int32)
+    zero_pair = (gm == 0) & (rm == 0)
+    adjacent = ((gs == rs) & (np.abs(gm - rm) == 1)) | zero_pair
+    mid = np.where(zero_pair, 0.0, 0.5 * (E4M3_VALUES[g] + E4M3_VALUES[r]))
+    near = np.abs(t - mid) <= rel * np.abs(mid) + abs_
+    ok = adjacent & near
+    nbad = int((~ok).sum())
+    first = int(bad[np.argmax(~ok)]) if nbad else -1
+    return int(bad.size), nbad, first
+
+
+def assert_codes_match(got, ref, quot, max_frac: float = MAX_TIE_FRAC, rel: float = TIE_REL,
+                       abs_: float = TIE_ABS, what: str = "codes"):
+    n = np.asarray(ref).size
+    nmis, nbad, first = code_mismatches(got, ref, quot, rel, abs_)
+    assert nbad == 0, (f"{what}: {nbad} inadmissible code mismatches of {nmis}; first at {first}: "
+                       f"got 0x{int(np.asarray(got).reshape(-1)[first]):02x} ref "
+                       f"0x{int(np.asarray(ref).reshape(-1)[first]):02x} "
+                       f"t={float(np.asarray(quot).reshape(-1)[first])!r}")
+    assert nmis <= max_frac * max(n, 1), f"{what}: {nmis} tie mismatches of {n} exceed {max_frac}"
+    return nmis
+
+
+def assert_rel_close(got, ref, rel: float, floor: float = 0.0, what: str = "values"):
+    got = np.asarray(got, np.float64).reshape(-1)
+    ref = np.asarray(ref, np.float64).reshape(-1)
+    err = np.abs(got - ref)
+    lim = rel * np.abs(ref) + floor
+    bad = np.nonzero(~(err <= lim))[0]
+    assert bad.size == 0, (f"{what}: {bad.size} of {ref.size} beyond rel {rel}; first at {bad[0]}: "
+                           f"got {got[bad[0]]!r} ref {ref[bad[0]]!r}")
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.where(ref != 0, err / np.abs(ref), 0.0)
+    return float(r.max()) if r.size else 0.0
