@@ -1,0 +1,234 @@
+"""Benchmark of the FP8 ASH + DS compression path on one MI355X.
+
+One step is one pass of the whole path over one batch of synthetic input, the
+Qwen2.5-7B-shaped tensor-parallel activation workload: P = 8 simulated rank shards of
+bfloat16 [8, 4096, 3584], block 128, target 1.0.
+
+  1. compress   all 8 shards in one call (8 x 117,440,512 elements) -> codes + alpha + s
+  2. reduce_fp8 the 8 contributions -> one requantised tensor (codes + alpha + s)
+  3. decompress the reduced tensor to bfloat16
+
+Inputs are generated on the host (seeded, see workloads/) and are resident in HBM before the
+timed region starts.  `value` is the whole step's throughput in GB/s of bfloat16 input
+(8 x 117,440,512 x 2 bytes per step).  Per-kernel durations come from HIP events recorded on
+the stream the kernels run on.  `roofline` describes the dominant kernel (compress);
+`cpu_baseline` is the FP64 CPU oracle timed on this host over a bounded sample of the same
+pipeline.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       python bench.py --copy-calibrate   (plain 1 GiB device copy, for HBM counter scaling)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused FP8 ASH+DS compress GB/s (bf16 in) and % of MI355X HBM peak"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published peak
+CID = 5
+TARGET = 1.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "compress_qwen7b_8shards_hbm_traffic.json")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "fp8_compression_tensor_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(launch_bytes_alg: float):
+    """HBM bytes per compress launch from the committed rocprofv3 counter summary, scaled by
+    the copy-kernel calibration it records; None if absent or taken on other kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return float(rec["fetch_bytes_per_launch"]) + float(rec["write_bytes_per_launch"])
+
+
+def copy_calibrate(steps: int):
+    import torch
+
+    n = 1 << 29  # 1 GiB of bfloat16
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copy-calibrate: {steps} copies of {2 * n} bytes (read {2 * n}, write {2 * n} per copy)")
+    print(json.dumps({"copy_bytes_read": 2 * n, "copy_bytes_written": 2 * n, "copies": steps}))
+
+
+def cpu_baseline(xs, budget_s: float = 20.0):
+    """Time the oracle on a bounded prefix sample of every shard (same pipeline)."""
+    import numpy as np
+
+    import oracle
+
+    cfg_b = 128
+    P = xs.shape[0]
+    cores = len(os.sched_getaffinity(0))
+    oracle.set_threads(cores)
+    xs = xs.reshape(P, -1)
+    n_full = xs.shape[1]
+
+    def run(m):  # m blocks of each shard
+        t0 = time.perf_counter()
+        sample = np.ascontiguousarray(xs[:, :m * cfg_b])
+        q, a, s = oracle.compress(sample.reshape(-1), cfg_b, TARGET)
+        qr, ar, sr = oracle.reduce_fp8(q.reshape(P, -1), a.reshape(P, -1), s.reshape(P, -1), cfg_b,
+                                       TARGET)
+        oracle.decompress(qr, ar, sr, cfg_b, np.uint16)
+        return time.perf_counter() - t0
+
+    m = 2048
+    t = run(m)
+    # scale the sample so the timed run takes about budget_s, capped at the whole tensor
+    m = int(min(n_full // cfg_b, max(m, m * budget_s / max(t, 1e-3))))
+    t = run(m)
+    gbs = P * m * cfg_b * 2 / t / 1e9
+    return {"value": gbs, "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {m} blocks ({m * cfg_b} elements) of each of the {P} shards through "
+                      f"compress -> reduce_fp8 -> decompress(bf16), float64 oracle, {t:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibrate", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(the reduce's contributions are simulated shards in one HBM).", file=sys.stderr)
+        sys.exit(2)
+
+    if args.copy_calibrate:
+        copy_calibrate(max(args.steps, 1))
+        return
+
+    from workloads import CONFIGS, make_shards
+
+    cfg = CONFIGS[CID]
+    B, P, n = cfg.block, cfg.shards, cfg.n
+    log(f"generating {P} shards of {cfg.name} (seeded) ...")
+    t0 = time.perf_counter()
+    xs = make_shards(CID)  # host generation before the GPU is touched
+    log(f"  done in {time.perf_counter() - t0:.1f} s")
+
+    import numpy as np
+    import torch
+
+    import fp8_compression_tensor_amd as tfp8
+
+    dev = torch.device("cuda:0")
+    x = torch.from_numpy(xs.reshape(-1).view(np.int16)).to(dev).view(torch.bfloat16)
+    nb = n // B
+    codes = torch.empty(P * n, dtype=torch.uint8, device=dev)
+    alpha = torch.empty(P * nb, dtype=torch.float32, device=dev)
+    scale = torch.empty(P * nb, dtype=torch.float32, device=dev)
+    rcodes = torch.empty(n, dtype=torch.uint8, device=dev)
+    ralpha = torch.empty(nb, dtype=torch.float32, device=dev)
+    rscale = torch.empty(nb, dtype=torch.float32, device=dev)
+    out = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+
+    def check(st):
+        if st != 0:
+            raise RuntimeError(tfp8.status_string(st))
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        check(tfp8.compress_raw(x.data_ptr(), tfp8.BF16, P * n, B, TARGET, codes.data_ptr(),
+                                alpha.data_ptr(), scale.data_ptr(), sh))
+        if ev is not None:
+            ev[1].record(stream)
+        check(tfp8.reduce_fp8_raw(codes.data_ptr(), alpha.data_ptr(), scale.data_ptr(), P, n, B,
+                                  TARGET, rcodes.data_ptr(), ralpha.data_ptr(), rscale.data_ptr(),
+                                  sh))
+        if ev is not None:
+            ev[2].record(stream)
+        check(tfp8.decompress_raw(rcodes.data_ptr(), ralpha.data_ptr(), rscale.data_ptr(), n, B,
+                                  out.data_ptr(), tfp8.BF16, sh))
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    log(f"timing {args.steps} steps ...")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    t_c = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps  # ms
+    t_r = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
+    t_d = sum(e[2].elapsed_time(e[3]) for e in events) / args.steps
+
+    bytes_in = P * n * 2
+    value = bytes_in / (ms_step * 1e-3) / 1e9
+    alg_c = P * n * (2 + 1 + 8.0 / B)            # compress: bf16 in, codes out, 2 fp32 per block
+    alg_r = (P + 1) * n * (1 + 8.0 / B)          # reduce: P code sets in, one out
+    alg_d = n * (1 + 8.0 / B + 2)                # decompress: codes in, bf16 out
+    ach_c = alg_c / (t_c * 1e-3) / 1e9
+    traffic = measured_traffic(alg_c)
+    roofline = {"bound": "hbm", "achieved": round(ach_c, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach_c / HBM_PEAK_GBS, 4),
+                "traffic": (round(traffic / (t_c * 1e-3) / 1e9, 1) if traffic else None),
+                "kernel": "tfp8::k_compress<128, bf16>",
+                "bytes_per_launch_algorithmic": int(alg_c),
+                "traffic_bytes_per_launch": (int(traffic) if traffic else None)}
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "qwen2.5-7b tp activation [8,4096,3584] bf16 x 8 shards, block 128, "
+                               "target 1: compress(8 stacked shards) -> reduce_fp8(P=8) -> "
+                               "decompress(bf16)",
+                   "shape": list(cfg.shape), "shards": P, "block": B, "target": TARGET},
+        "roofline": roofline,
+        "kernels_ms": {"compress": round(t_c, 4), "reduce_fp8": round(t_r, 4),
+                       "decompress": round(t_d, 4)},
+        "compress_only": {"gbps_bf16_in": round(bytes_in / (t_c * 1e-3) / 1e9, 1),
+                          "hbm_frac_algorithmic": round(ach_c / HBM_PEAK_GBS, 4)},
+        "reduce_hbm_frac_algorithmic": round(alg_r / (t_r * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "decompress_hbm_frac_algorithmic": round(alg_d / (t_d * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+    }
+    del x, codes, out
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        result["cpu_baseline"] = cpu_baseline(xs)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

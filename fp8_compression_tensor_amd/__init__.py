@@ -1,0 +1,167 @@
+"""FP8 E4M3 (ASH + DS) compression of tensor-parallel tensors on MI355X (gfx950).
+
+Thin binding of the C ABI in ``include/tfp8.h`` (``libtfp8.so``, built in this directory by
+``build.py``).  This module only marshals arguments: PyTorch supplies device memory and the
+current HIP stream, and every step of compress / decompress / reduce runs in the library's
+kernels.  There is no CPU path: without the built library, or for tensors not on a GPU, the
+calls raise.
+
+Method: page "TACO: Efficient Communication Compression of Intermediate Tensors for Scalable
+Tensor-Parallel LLM Training" (section 2.B.1-2.B.2); local reduce: page "AGoQ: Activation and
+Gradient Quantization for Memory-Efficient Distributed Training of LLMs" (section 2.B).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "compress", "decompress", "reduce_fp8", "compress_raw", "decompress_raw", "reduce_fp8_raw",
+    "status_string", "lib", "LIB_PATH", "TFP8Error", "BF16", "F32", "SUPPORTED_BLOCKS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtfp8.so")
+BF16, F32 = 0, 1
+SUPPORTED_BLOCKS = (64, 128, 256, 512)
+
+_STATUS = {0: "TFP8_OK", -1: "TFP8_E_NULL", -2: "TFP8_E_SIZE", -3: "TFP8_E_BLOCK",
+           -4: "TFP8_E_DTYPE", -5: "TFP8_E_ALIGN", -6: "TFP8_E_ARG", -7: "TFP8_E_HIP"}
+
+
+class TFP8Error(RuntimeError):
+    """A status other than TFP8_OK; ``.status`` holds the code."""
+
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run fp8_compression_tensor_amd/build.py "
+                               "(or __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
+        L.tfp8_compress.argtypes = [vp, i32, i64, i32, f32, vp, vp, vp, vp]
+        L.tfp8_compress.restype = i32
+        L.tfp8_decompress.argtypes = [vp, vp, vp, i64, i32, vp, i32, vp]
+        L.tfp8_decompress.restype = i32
+        L.tfp8_reduce_fp8.argtypes = [vp, vp, vp, i32, i64, i32, f32, vp, vp, vp, vp]
+        L.tfp8_reduce_fp8.restype = i32
+        L.tfp8_status_string.argtypes = [i32]
+        L.tfp8_status_string.restype = ctypes.c_char_p
+        L.tfp8_version.argtypes = []
+        L.tfp8_version.restype = i32
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().tfp8_status_string(int(status)).decode()
+
+
+def _check(status: int):
+    if status != 0:
+        raise TFP8Error(status, status_string(status))
+
+
+# ---------------------------------------------------------------------------------- raw calls
+# Pointers are integers (device addresses); `stream` is a raw hipStream_t (0 = default stream).
+
+def compress_raw(x_ptr: int, x_dtype: int, n: int, block: int, target: float, codes_ptr: int,
+                 alpha_ptr: int, scale_ptr: int, stream: int = 0) -> int:
+    return lib().tfp8_compress(x_ptr, x_dtype, n, block, target, codes_ptr, alpha_ptr,
+                               scale_ptr, stream)
+
+
+def decompress_raw(codes_ptr: int, alpha_ptr: int, scale_ptr: int, n: int, block: int,
+                   out_ptr: int, out_dtype: int, stream: int = 0) -> int:
+    return lib().tfp8_decompress(codes_ptr, alpha_ptr, scale_ptr, n, block, out_ptr, out_dtype,
+                                 stream)
+
+
+def reduce_fp8_raw(codes_ptr: int, alpha_ptr: int, scale_ptr: int, P: int, n: int, block: int,
+                   target: float, codes_out_ptr: int, alpha_out_ptr: int, scale_out_ptr: int,
+                   stream: int = 0) -> int:
+    return lib().tfp8_reduce_fp8(codes_ptr, alpha_ptr, scale_ptr, P, n, block, target,
+                                 codes_out_ptr, alpha_out_ptr, scale_out_ptr, stream)
+
+
+# ---------------------------------------------------------------------------- tensor wrappers
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _need_gpu(*ts):
+    for t in ts:
+        if not (isinstance(t, torch.Tensor) and t.is_cuda):
+            raise ValueError("tfp8 operates on GPU tensors only (no CPU path)")
+        if not t.is_contiguous():
+            raise ValueError("tfp8 needs contiguous tensors")
+
+
+def compress(x: torch.Tensor, block: int = 128, target: float = 1.0, out=None):
+    """x (bfloat16 or float32, any shape, numel % block == 0) ->
+    (codes uint8 of x's shape, alpha float32 [numel/block], scale float32 [numel/block])."""
+    _need_gpu(x)
+    if x.dtype == torch.bfloat16:
+        dt = BF16
+    elif x.dtype == torch.float32:
+        dt = F32
+    else:
+        raise ValueError(f"unsupported input dtype {x.dtype}")
+    n = x.numel()
+    nb = n // block if block > 0 else 0
+    if out is None:
+        codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+        alpha = torch.empty(nb, dtype=torch.float32, device=x.device)
+        scale = torch.empty(nb, dtype=torch.float32, device=x.device)
+    else:
+        codes, alpha, scale = out
+    _check(compress_raw(x.data_ptr(), dt, n, block, float(target), codes.data_ptr(),
+                        alpha.data_ptr(), scale.data_ptr(), _stream(x)))
+    return codes, alpha, scale
+
+
+def decompress(codes: torch.Tensor, alpha: torch.Tensor, scale: torch.Tensor, block: int = 128,
+               dtype: torch.dtype = torch.float32, out=None):
+    """Reconstruct a float32 or bfloat16 tensor of codes' shape."""
+    _need_gpu(codes, alpha, scale)
+    if dtype == torch.float32:
+        dt = F32
+    elif dtype == torch.bfloat16:
+        dt = BF16
+    else:
+        raise ValueError(f"unsupported output dtype {dtype}")
+    if out is None:
+        out = torch.empty(codes.shape, dtype=dtype, device=codes.device)
+    _check(decompress_raw(codes.data_ptr(), alpha.data_ptr(), scale.data_ptr(), codes.numel(),
+                          block, out.data_ptr(), dt, _stream(codes)))
+    return out
+
+
+def reduce_fp8(codes: torch.Tensor, alpha: torch.Tensor, scale: torch.Tensor, block: int = 128,
+               target: float = 1.0, out=None):
+    """codes [P, ...], alpha and scale [P, nb] -> (codes [...], alpha [nb], scale [nb])."""
+    _need_gpu(codes, alpha, scale)
+    P = codes.shape[0]
+    n = codes[0].numel()
+    nb = n // block if block > 0 else 0
+    if out is None:
+        codes_out = torch.empty(codes.shape[1:], dtype=torch.uint8, device=codes.device)
+        alpha_out = torch.empty(nb, dtype=torch.float32, device=codes.device)
+        scale_out = torch.empty(nb, dtype=torch.float32, device=codes.device)
+    else:
+        codes_out, alpha_out, scale_out = out
+    _check(reduce_fp8_raw(codes.data_ptr(), alpha.data_ptr(), scale.data_ptr(), P, n, block,
+                          float(target), codes_out.data_ptr(), alpha_out.data_ptr(),
+                          scale_out.data_ptr(), _stream(codes)))
+    return codes_out, alpha_out, scale_out

@@ -1,0 +1,134 @@
+// tfp8_device.hpp - wavefront primitives for the gfx950 FP8 ASH + DS kernels.
+//
+// Everything here works on one 64-lane wavefront.  A "group" is the set of L consecutive
+// lanes (L = 4, 8, 16 or 32) that hold one block; group reductions and butterflies only use
+// lane exchanges that stay inside the group.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tfp8 {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// DPP lane-select controls (gfx9 encoding).
+enum : int {
+  kDppXor1 = 0xB1,        // quad_perm [1,0,3,2]: lane i reads lane i^1
+  kDppXor2 = 0x4E,        // quad_perm [2,3,0,1]: lane i reads lane i^2
+  kDppHalfMirror = 0x141, // lane i reads lane i^7 inside each group of 8
+  kDppRowMirror = 0x140,  // lane i reads lane i^15 inside each row of 16
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+
+// lane i reads lane i^16 (ds_swizzle bit mode inside 32-lane halves: and 0x1F, xor 0x10)
+__device__ __forceinline__ float swz_xor16(float v) {
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+}
+
+// Max over the L lanes of a group; every lane of the group gets the result.  After the
+// xor-1 and xor-2 steps all lanes of a quad agree, so the mirror steps (xor 7, xor 15) combine
+// whole quads / half-rows exactly like xor 4 / xor 8 would.
+template <int L>
+__device__ __forceinline__ float group_max(float v) {
+  static_assert(L == 4 || L == 8 || L == 16 || L == 32, "group of 4, 8, 16 or 32 lanes");
+  v = fmaxf(v, dpp<kDppXor1>(v));
+  v = fmaxf(v, dpp<kDppXor2>(v));
+  if constexpr (L >= 8) v = fmaxf(v, dpp<kDppHalfMirror>(v));
+  if constexpr (L >= 16) v = fmaxf(v, dpp<kDppRowMirror>(v));
+  if constexpr (L >= 32) v = fmaxf(v, swz_xor16(v));
+  return v;
+}
+
+template <int L>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(L == 4 || L == 8 || L == 16 || L == 32, "group of 4, 8, 16 or 32 lanes");
+  v = v + dpp<kDppXor1>(v);
+  v = v + dpp<kDppXor2>(v);
+  if constexpr (L >= 8) v = v + dpp<kDppHalfMirror>(v);
+  if constexpr (L >= 16) v = v + dpp<kDppRowMirror>(v);
+  if constexpr (L >= 32) v = v + swz_xor16(v);
+  return v;
+}
+
+// Unnormalised Walsh-Hadamard transform of the N values a lane holds (natural order).
+template <int N>
+__device__ __forceinline__ void fwht_registers(float (&v)[N]) {
+#pragma unroll
+  for (int h = 1; h < N; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < N; i += 2 * h) {
+#pragma unroll
+      for (int k = i; k < i + h; ++k) {
+        const float a = v[k], b = v[k + h];
+        v[k] = a + b;
+        v[k + h] = a - b;
+      }
+    }
+  }
+}
+
+// Hadamard transform across the 8 lanes of a group, one fused multiply-add per value and
+// stage: value <- value + sigma * partner, with sigma = -1 on the lane of each pair that keeps
+// the difference.  Partners are lane^7 first (no xor-4 lane select exists in DPP), then lane^1
+// and lane^2, with sigma from lane bits 2, 0 and 1.  Mask 7 = 4 ^ 3, so the three masks still
+// span all lane bits; the network computes a signed permutation of the natural transform:
+// lane j ends with kLaneSign[j] * (H_8 v)[kLanePerm[j]] (worked out by enumerating the
+// network on the unit vectors).
+__device__ __forceinline__ int lane8_perm(int j) {
+  // 0,5,6,3,4,1,2,7: bit 2 flips when bits 0 and 1 differ
+  return j ^ (((j ^ (j >> 1)) & 1) << 2);
+}
+__device__ __forceinline__ float lane8_sign(int j) {
+  // + for lanes 0 and 3, - for the others
+  return (j == 0 || j == 3) ? 1.0f : -1.0f;
+}
+
+template <int N>
+__device__ __forceinline__ void fwht_lanes8(float (&v)[N], int j) {
+  const float s7 = (j & 4) ? -1.0f : 1.0f;
+  const float s1 = (j & 1) ? -1.0f : 1.0f;
+  const float s2 = (j & 2) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int r = 0; r < N; ++r) v[r] = fmaf(dpp<kDppHalfMirror>(v[r]), s7, v[r]);
+#pragma unroll
+  for (int r = 0; r < N; ++r) v[r] = fmaf(dpp<kDppXor1>(v[r]), s1, v[r]);
+#pragma unroll
+  for (int r = 0; r < N; ++r) v[r] = fmaf(dpp<kDppXor2>(v[r]), s2, v[r]);
+}
+
+// bfloat16 pair in one dword -> two floats (exact).
+__device__ __forceinline__ void widen_bf16x2(uint32_t d, float &lo, float &hi) {
+  lo = __uint_as_float(d << 16);
+  hi = __uint_as_float(d & 0xFFFF0000u);
+}
+
+// Four floats -> four E4M3FN bytes (OCP format, round to nearest even) in one dword.
+__device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
+  uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+}
+
+// Four E4M3FN bytes of one dword -> four floats (exact).
+__device__ __forceinline__ void unpack_fp8x4(uint32_t w, float &a, float &b, float &c, float &d) {
+  const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+  const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+  a = lo[0];
+  b = lo[1];
+  c = hi[0];
+  d = hi[1];
+}
+
+__device__ __forceinline__ int exponent_of(float x) { return __builtin_amdgcn_frexp_expf(x); }
+__device__ __forceinline__ float mantissa_of(float x) { return __builtin_amdgcn_frexp_mantf(x); }
+__device__ __forceinline__ float scale2(float x, int k) { return __builtin_amdgcn_ldexpf(x, k); }
+
+}  // namespace tfp8

@@ -1,0 +1,97 @@
+/*
+ * tfp8.h - C ABI of the MI355X (gfx950) FP8 ASH + DS compression library.
+ *
+ * Three operations on flat buffers in device memory, each launched asynchronously on the
+ * caller's HIP stream:
+ *
+ *   tfp8_compress    per block of `block` elements: second moment, adaptive prescale alpha_k
+ *                    that brings that energy to `target`, orthogonal Hadamard rotation,
+ *                    post-scale s_k = max|y| / 448, FP8 E4M3FN codes.  Page "TACO: Efficient
+ *                    Communication Compression of Intermediate Tensors for Scalable
+ *                    Tensor-Parallel LLM Training", sections 2.A (E4M3), 2.B.1 (adaptive
+ *                    scale-Hadamard transform), 2.B.2 (dual-scale quantization) and 2.B.3 (one
+ *                    fused kernel for the energy, the transform and the quantization).
+ *   tfp8_decompress  the inverse with both scales (same page, section 2.B.2, reconstruction).
+ *   tfp8_reduce_fp8  the local step of a two-shot all-reduce: dequantize P contributions,
+ *                    sum in FP32, requantize to the same format.  Page "AGoQ: Activation and
+ *                    Gradient Quantization for Memory-Efficient Distributed Training of LLMs",
+ *                    section 2.B (precision-preserving all-reduce); the TACO page, section
+ *                    2.B.3, puts the same step between ReduceScatter and AllGather.
+ *
+ * Definitions (readings of the pages; B = block, T = target, Q = 448):
+ *   block k covers x[kB, (k+1)B) of the flat row-major buffer; H is the Sylvester Hadamard
+ *   matrix of order B in natural order, H[i][j] = (-1)^popcount(i & j), used as H / sqrt(B);
+ *   m2 = mean(v^2);  alpha = clamp(sqrt(T / m2), 2^-126, 2^126);  y = H (alpha v) / sqrt(B);
+ *   s = max|y| / Q;  code_i = E4M3FN(y_i / s), round to nearest even.  A block whose elements
+ *   are all zero stores alpha = 1, s = 0 and codes 0x00, and reconstructs to +0.
+ *   Reconstruction: xhat = H (s dec(code)) / (sqrt(B) alpha).
+ *   Reduce: z = sum_p xhat_p, then compress z with the same B and T.
+ *
+ * Conventions shared by all entry points:
+ *   - Every data pointer is a DEVICE pointer; `stream` is a hipStream_t (NULL = default stream).
+ *   - The caller owns every buffer.  The library allocates and frees nothing and never
+ *     synchronizes; outputs are complete when the stream reaches the launch.
+ *   - Element counts are 64-bit.  n = 0 is a no-op that returns TFP8_OK.
+ *   - Supported block sizes: 64, 128, 256, 512.
+ *   - Alignment: x, out and every codes pointer 16 bytes; alpha and scale 4 bytes.
+ *   - Out-of-place only: an output range that overlaps an input range, or another output
+ *     range, is rejected with TFP8_E_ARG.
+ *   - target must be finite and within [2^-64, 2^64].
+ *   - Inputs must be finite with |x| < 2^100; other values are outside the contract (no
+ *     check, unspecified codes).
+ *   - Argument errors return before any HIP call and nothing is launched.  A launch failure
+ *     returns TFP8_E_HIP.  Faults during execution surface at the caller's next
+ *     synchronization, as for any HIP kernel.
+ */
+#ifndef TFP8_H
+#define TFP8_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TFP8_OK = 0,
+  TFP8_E_NULL = -1,  /* a required pointer is NULL (n > 0) */
+  TFP8_E_SIZE = -2,  /* n < 0, or n is not a multiple of block */
+  TFP8_E_BLOCK = -3, /* block is not one of 64, 128, 256, 512 */
+  TFP8_E_DTYPE = -4, /* dtype is not TFP8_BF16 or TFP8_F32 */
+  TFP8_E_ALIGN = -5, /* a pointer is not aligned as stated above */
+  TFP8_E_ARG = -6,   /* P < 1 or P > 64, bad target, or overlapping buffers */
+  TFP8_E_HIP = -7    /* the HIP runtime rejected the launch */
+} tfp8_status;
+
+typedef enum { TFP8_BF16 = 0, TFP8_F32 = 1 } tfp8_dtype;
+
+/* Compress x[n] (bfloat16 or float32, row-major flat) in blocks of `block`.
+ * Outputs: codes[n] (E4M3FN bytes, same element order as x), alpha[n/block], scale[n/block]
+ * (float32 per block: the prescale alpha_k and the post-scale s_k). */
+tfp8_status tfp8_compress(const void *x, tfp8_dtype x_dtype, int64_t n, int32_t block, float target,
+                          uint8_t *codes, float *alpha, float *scale, void *stream);
+
+/* Reconstruct out[n] (float32 or bfloat16, rounded to nearest even) from codes[n] and the
+ * per-block alpha[n/block], scale[n/block] written by tfp8_compress or tfp8_reduce_fp8. */
+tfp8_status tfp8_decompress(const uint8_t *codes, const float *alpha, const float *scale, int64_t n,
+                            int32_t block, void *out, tfp8_dtype out_dtype, void *stream);
+
+/* Local reduce of P contributions of the same n elements, stacked contiguously:
+ * codes[P][n], alpha[P][n/block], scale[P][n/block] (contribution p at offset p*n, p*n/block).
+ * The contributions are dequantized, summed in float32 in the order p = 0..P-1, and the sum is
+ * requantized with the same block and target into codes_out[n], alpha_out[n/block],
+ * scale_out[n/block].  1 <= P <= 64. */
+tfp8_status tfp8_reduce_fp8(const uint8_t *codes, const float *alpha, const float *scale, int32_t P,
+                            int64_t n, int32_t block, float target, uint8_t *codes_out,
+                            float *alpha_out, float *scale_out, void *stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char *tfp8_status_string(tfp8_status status);
+
+/* ABI version of this header: (major << 16) | minor. */
+int32_t tfp8_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TFP8_H */

@@ -1,0 +1,102 @@
+"""The C-ABI library loads, exports every symbol include/tfp8.h declares, and rejects bad
+arguments before touching the GPU (these calls make no HIP call, so they run without one)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tfp8.h")
+
+
+@pytest.fixture(scope="module")
+def tfp8():
+    import fp8_compression_tensor_amd as m
+
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tfp8_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_three_operations():
+    names = declared_functions()
+    for want in ("tfp8_compress", "tfp8_decompress", "tfp8_reduce_fp8", "tfp8_status_string"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(tfp8):
+    L = tfp8.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert L.tfp8_version() == (1 << 16)
+
+
+def test_status_strings(tfp8):
+    for st in range(-7, 1):
+        s = tfp8.status_string(st)
+        assert s and s != "unknown status"
+    assert tfp8.status_string(-99) == "unknown status"
+
+
+FAKE = 0x7F0000000000  # a 16-byte aligned address that is never dereferenced here
+
+
+def test_compress_argument_errors(tfp8):
+    c = tfp8.compress_raw
+    assert c(FAKE, 0, 1024, 96, 1.0, FAKE + 4096, FAKE + 8192, FAKE + 12288) == -3  # block
+    assert c(FAKE, 0, 1000, 128, 1.0, FAKE + 4096, FAKE + 8192, FAKE + 12288) == -2  # n % B
+    assert c(FAKE, 0, -128, 128, 1.0, FAKE + 4096, FAKE + 8192, FAKE + 12288) == -2
+    assert c(FAKE, 2, 1024, 128, 1.0, FAKE + 4096, FAKE + 8192, FAKE + 12288) == -4  # dtype
+    for t in (0.0, -1.0, float("inf"), float("nan"), 2.0 ** 70, 2.0 ** -70):
+        assert c(FAKE, 0, 1024, 128, t, FAKE + 4096, FAKE + 8192, FAKE + 12288) == -6
+    assert c(None, 0, 1024, 128, 1.0, FAKE + 4096, FAKE + 8192, FAKE + 12288) == -1
+    assert c(FAKE, 0, 1024, 128, 1.0, None, FAKE + 8192, FAKE + 12288) == -1
+    assert c(FAKE + 2, 0, 1024, 128, 1.0, FAKE + 4096, FAKE + 8192, FAKE + 12288) == -5
+    assert c(FAKE, 0, 1024, 128, 1.0, FAKE + 4104, FAKE + 8192, FAKE + 12288) == -5
+    assert c(FAKE, 0, 1024, 128, 1.0, FAKE + 4096, FAKE + 8194, FAKE + 12288) == -5
+    # codes overlapping the input, alpha overlapping scale
+    assert c(FAKE, 0, 1024, 128, 1.0, FAKE + 1024, FAKE + 8192, FAKE + 12288) == -6
+    assert c(FAKE, 0, 1024, 128, 1.0, FAKE + 4096, FAKE + 8192, FAKE + 8192 + 16) == -6
+    # n = 0 is a no-op, even with NULL pointers
+    assert c(None, 0, 0, 128, 1.0, None, None, None) == 0
+
+
+def test_decompress_argument_errors(tfp8):
+    d = tfp8.decompress_raw
+    assert d(FAKE, FAKE + 4096, FAKE + 8192, 1024, 100, FAKE + 16384, 1) == -3
+    assert d(FAKE, FAKE + 4096, FAKE + 8192, 1000, 128, FAKE + 16384, 1) == -2
+    assert d(FAKE, FAKE + 4096, FAKE + 8192, 1024, 128, FAKE + 16384, 5) == -4
+    assert d(FAKE, None, FAKE + 8192, 1024, 128, FAKE + 16384, 1) == -1
+    assert d(FAKE, FAKE + 4096, FAKE + 8192, 1024, 128, FAKE + 16388, 1) == -5
+    assert d(FAKE, FAKE + 4096, FAKE + 8192, 1024, 128, FAKE + 512, 1) == -6  # out over codes
+    assert d(None, None, None, 0, 128, None, 1) == 0
+
+
+def test_reduce_argument_errors(tfp8):
+    r = tfp8.reduce_fp8_raw
+    args = (FAKE, FAKE + 65536, FAKE + 81920)
+    outs = (FAKE + 131072, FAKE + 196608, FAKE + 200704)
+    assert r(*args, 4, 1024, 64 * 3, 1.0, *outs) == -3
+    assert r(*args, 4, 1000, 128, 1.0, *outs) == -2
+    assert r(*args, 0, 1024, 128, 1.0, *outs) == -6
+    assert r(*args, 65, 1024, 128, 1.0, *outs) == -6
+    assert r(*args, 4, 1024, 128, 0.0, *outs) == -6
+    assert r(FAKE, None, FAKE + 81920, 4, 1024, 128, 1.0, *outs) == -1
+    # output codes inside the stacked input codes
+    assert r(*args, 4, 1024, 128, 1.0, FAKE + 1024, outs[1], outs[2]) == -6
+    assert r(None, None, None, 4, 0, 128, 1.0, None, None, None) == 0
+
+
+def test_tensor_wrappers_refuse_cpu_tensors(tfp8):
+    import torch
+
+    x = torch.zeros(1024, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        tfp8.compress(x, 128)
+    with pytest.raises(ValueError, match="GPU"):
+        tfp8.decompress(torch.zeros(1024, dtype=torch.uint8), torch.zeros(8), torch.zeros(8), 128)

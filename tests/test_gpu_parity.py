@@ -1,0 +1,263 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the same seeded inputs.
+
+Each stage is also fed the oracle's output of the stage before it, so a mismatch names the
+stage.  Bars: codes identical except admissible rounding ties on <= 1e-4 of the elements;
+alpha and s within 1e-6 relative (zero blocks and clamped alpha exact); float32
+reconstructions within 1e-6 relative (+ 2^-149 absolute for subnormal results); bfloat16
+reconstructions identical except double-rounding ties.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import (DEV, assert_scales, bits_to_gpu, check_compress, check_decompress, cpu,
+                         f32_to_gpu, say, u8_to_gpu)
+from tiecheck import assert_codes_match, assert_rel_close
+from workloads import (CONFIGS, bf16_bits_to_f32, f32_to_bf16_bits, make_shard, make_shards,
+                       random_bf16_bits)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def tfp8():
+    import fp8_compression_tensor_amd as m
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    m.lib()  # raises if the HIP library is not built
+    return m
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _threads(oracle):
+    oracle.set_threads(min(16, len(os.sched_getaffinity(0))))
+
+
+# ----------------------------------------------------------------------------- configs 1, 2, 4
+
+@pytest.mark.parametrize("cid", [1, 2, 4])
+def test_config_compress_decompress(oracle, tfp8, cid):
+    cfg = CONFIGS[cid]
+    say(f"config {cid} ({cfg.name}), block {cfg.block}")
+    x = make_shard(cid).reshape(-1)
+    q, a, s = check_compress(oracle, tfp8, x, cfg.block, what=f"cfg{cid} compress")
+    qr, ar, sr = oracle.compress(x, cfg.block, 1.0)
+    check_decompress(oracle, tfp8, qr, ar, sr, cfg.block, what=f"cfg{cid} decompress(oracle codes)")
+    check_decompress(oracle, tfp8, q, a, s, cfg.block, what=f"cfg{cid} decompress(gpu codes)")
+
+
+# ----------------------------------------------------------------------------- config 3
+
+def test_config3_compress_reduce_decompress(oracle, tfp8):
+    cfg = CONFIGS[3]
+    B, P = cfg.block, cfg.shards
+    say(f"config 3 ({cfg.name}), block {B}, P={P}")
+    xs = make_shards(3)  # [4, 4, 2048, 4096]
+    # one call compresses the stacked shards (blocks never straddle shards)
+    q, a, s = check_compress(oracle, tfp8, xs.reshape(-1), B, what="cfg3 compress of 4 stacked shards")
+    n = cfg.n
+    q, a, s = q.reshape(P, n), a.reshape(P, -1), s.reshape(P, -1)
+    check_decompress(oracle, tfp8, q[0], a[0], s[0], B, what="cfg3 decompress shard 0")
+    _check_reduce(oracle, tfp8, q, a, s, B, what="cfg3 reduce P=4")
+
+
+def _check_reduce(oracle, tfp8, q, a, s, B, T=1.0, what="reduce"):
+    P, n = q.shape
+    qg, ag, sg = u8_to_gpu(q), f32_to_gpu(a), f32_to_gpu(s)
+    cq, ca, cs = tfp8.reduce_fp8(qg, ag, sg, B, T)
+    torch.cuda.synchronize()
+    cq, ca, cs = cpu(cq), cpu(ca), cpu(cs)
+    rq, ra, rs, rt = oracle.reduce_fp8(q, a, s, B, T, with_quot=True)
+    nmis = assert_codes_match(cq, rq, rt, what=what + " codes")
+    ea, es = assert_scales(ca, cs, ra, rs, what=what)
+    say(f"  {what}: P={P} n={n} B={B}: code tie mismatches {nmis} ({nmis / n:.2e}), "
+        f"max rel err alpha {ea:.2e} scale {es:.2e}")
+    return cq, ca, cs
+
+
+# ----------------------------------------------------------------------------- config 5
+
+def test_config5_pipeline(oracle, tfp8):
+    cfg = CONFIGS[5]
+    B, P, n = cfg.block, cfg.shards, cfg.n
+    say(f"config 5 ({cfg.name}), block {B}, P={P}: generating {P} shards")
+    xs = make_shards(5).reshape(P, n)
+    say("  compress of the 8 stacked shards (one call), checked on sampled blocks")
+    xg = bits_to_gpu(xs.reshape(-1))
+    qg, ag, sg = tfp8.compress(xg, B, 1.0)
+    torch.cuda.synchronize()
+    del xg
+    q, a, s = cpu(qg), cpu(ag), cpu(sg)
+    nbt = P * cfg.nblocks
+    rng = np.random.default_rng(55)
+    idx = np.sort(rng.choice(nbt, 131072, replace=False))
+    idx = np.union1d(idx, np.arange(0, nbt, cfg.nblocks))  # first block of every shard
+    xb = xs.reshape(nbt, B)[idx]
+    qr, ar, sr, tr = oracle.compress(xb, B, 1.0, with_quot=True)
+    nmis = assert_codes_match(q.reshape(nbt, B)[idx], qr, tr, what="cfg5 compress codes (sampled)")
+    assert_scales(a[idx], s[idx], ar, sr, what="cfg5 compress (sampled)")
+    say(f"  cfg5 compress: {idx.size} sampled blocks, code tie mismatches {nmis}")
+    # reduce and decompress on the GPU's own codes, each checked in full
+    q, a, s = q.reshape(P, n), a.reshape(P, -1), s.reshape(P, -1)
+    cq, ca, cs = _check_reduce(oracle, tfp8, q, a, s, B, what="cfg5 reduce P=8")
+    check_decompress(oracle, tfp8, cq, ca, cs, B, what="cfg5 decompress of the reduced tensor")
+
+
+# ----------------------------------------------------------------------------- edge cases
+
+def _special_blocks(B, rng):
+    """Blocks that exercise every branch: zero, -0, constant, one-hot, Hadamard-like sign
+    patterns, bfloat16-subnormal, large (2^90), small normal (2^-120), mixed magnitudes."""
+    blocks = []
+    blocks.append(np.zeros(B))
+    blocks.append(-np.zeros(B))
+    blocks.append(np.full(B, 0.75))
+    oh = np.zeros(B); oh[B // 3] = -5.5; blocks.append(oh)
+    blocks.append(np.where(rng.random(B) < 0.5, 1.0, -1.0) * 0.125)
+    blocks.append(rng.integers(-64, 65, B) * 2.0 ** -133)       # bfloat16 subnormal block
+    sub = np.zeros(B); sub[7] = 2.0 ** -133; blocks.append(sub)  # smallest bfloat16 value
+    blocks.append(rng.laplace(0, 1, B) * 2.0 ** 90)
+    blocks.append(rng.laplace(0, 1, B) * 2.0 ** -120)
+    mixed = rng.laplace(0, 1e-3, B); mixed[0] = 3.0e4; blocks.append(mixed)
+    blocks.append(rng.laplace(0, 0.02, B))
+    return np.concatenate(blocks)
+
+
+@pytest.mark.parametrize("B", [64, 128, 256, 512])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_edge_blocks_and_ragged_tails(oracle, tfp8, B, dtype):
+    rng = np.random.default_rng(B)
+    v = _special_blocks(B, rng)
+    for extra in (0, 1, 5, 13):  # ragged tile tails: block counts not a multiple of 8
+        vv = np.concatenate([v, rng.laplace(0, 0.05, extra * B)])
+        if dtype == "bf16":
+            x = f32_to_bf16_bits(vv.astype(np.float32))
+            x[B:2 * B] = 0x8000  # the second block is all -0
+        else:
+            x = vv.astype(np.float32)
+            x[B:2 * B] = -0.0
+        q, a, s = check_compress(oracle, tfp8, x, B, what=f"edge B={B} {dtype} +{extra}")
+        check_decompress(oracle, tfp8, q, a, s, B, what=f"edge B={B} {dtype} +{extra}")
+
+
+@pytest.mark.parametrize("nblocks", [1, 2, 7, 8, 9, 1000, 4097])
+def test_block_counts(oracle, tfp8, nblocks):
+    x = random_bf16_bits(nblocks * 128, seed=nblocks, scale=0.01)
+    q, a, s = check_compress(oracle, tfp8, x, 128, what=f"{nblocks} blocks")
+    check_decompress(oracle, tfp8, q, a, s, 128, what=f"{nblocks} blocks")
+
+
+@pytest.mark.parametrize("T", [2.0 ** -10, 37.5, 2.0 ** 20])
+def test_target_values(oracle, tfp8, T):
+    x = make_shard(1).reshape(-1)
+    check_compress(oracle, tfp8, x, 128, T=T, what=f"cfg1 T={T}")
+
+
+def test_constructed_exact_ties(oracle, tfp8):
+    """Rotated values placed exactly on E4M3 rounding midpoints (float32 input, B = 256):
+    x = H z / 16 with z_0 = 448 and every other z_i a midpoint between two E4M3 values in
+    [1, 16), target = float32(mean(x^2)) so the oracle's alpha is exactly 1, y = z and s = 1.
+    Every partial sum of either side's transform is a multiple of 2^-8 below 2^21 (exact in
+    float32 and float64), so both sides see the exact midpoints and must round each one to
+    the even code."""
+    from scipy.linalg import hadamard
+
+    B = 256
+    grid = 1.0 + np.arange(8) / 8.0                      # 1, 1.125, ..., 1.875
+    mids = 0.5 * (grid[:-1] + grid[1:])                  # 1.0625, ..., 1.8125
+    mids = np.concatenate([mids, [0.5 * (1.875 + 2.0)]])  # 1.9375: between 1.875 and 2
+    rng = np.random.default_rng(9)
+    Z = (rng.choice(mids, (48, B)) * rng.choice([-1.0, 1.0], (48, B))
+         * 2.0 ** rng.integers(0, 4, (48, B)))
+    Z[:, 0] = 448.0
+    X = Z @ hadamard(B).astype(np.float64) / 16.0        # rows are H z / 16 (H symmetric)
+    x32 = X.astype(np.float32)
+    assert np.array_equal(x32.astype(np.float64), X), "construction must be exact in float32"
+    for k in range(Z.shape[0]):
+        T = float(np.float32(np.mean(X[k] * X[k])))
+        q, a, s = check_compress(oracle, tfp8, x32[k], B, T=T, what=f"exact ties block {k}")
+        qr, ar, sr, tr = oracle.compress(x32[k], B, T, with_quot=True)
+        assert ar[0] == 1.0 and sr[0] == 1.0 and np.array_equal(tr, Z[k])
+        assert np.array_equal(q, qr), f"block {k}: tie rounding differs"
+
+
+# ----------------------------------------------------------------------------- reduce cases
+
+@pytest.mark.parametrize("P", [1, 2, 3, 8, 16])
+@pytest.mark.parametrize("B", [64, 128, 256, 512])
+def test_reduce_general(oracle, tfp8, P, B):
+    rng = np.random.default_rng(100 * P + B)
+    nb = 37
+    xs = [f32_to_bf16_bits((rng.laplace(0, 0.02, nb * B) * (1 + p)).astype(np.float32))
+          for p in range(P)]
+    # block 3 zero everywhere, block 5 zero in contribution 0, block 6 bfloat16-subnormal
+    for p in range(P):
+        xs[p][3 * B:4 * B] = 0
+        xs[p][6 * B:7 * B] = f32_to_bf16_bits(
+            (rng.integers(-64, 65, B) * 2.0 ** -133).astype(np.float32))
+    xs[0][5 * B:6 * B] = 0
+    enc = [oracle.compress(x, B, 1.0) for x in xs]
+    q = np.stack([e[0] for e in enc]); a = np.stack([e[1] for e in enc]); s = np.stack([e[2] for e in enc])
+    _check_reduce(oracle, tfp8, q, a, s, B, what=f"reduce P={P} B={B}")
+
+
+def test_reduce_identities(oracle, tfp8):
+    B = 128
+    x = make_shard(1).reshape(-1)
+    q, a, s = oracle.compress(x, B, 1.0)
+    # a contribution and its negation cancel: every block becomes a zero block
+    q2, a2, s2 = np.stack([q, q ^ 0x80]), np.stack([a, a]), np.stack([s, s])
+    cq, ca, cs = tfp8.reduce_fp8(u8_to_gpu(q2), f32_to_gpu(a2), f32_to_gpu(s2), B, 1.0)
+    torch.cuda.synchronize()
+    assert np.all(cpu(cq) == 0) and np.all(cpu(ca) == 1.0) and np.all(cpu(cs) == 0.0)
+    # a single contribution is left as it is (codes up to ties, s/alpha within 1e-6)
+    cq, ca, cs = tfp8.reduce_fp8(u8_to_gpu(q[None]), f32_to_gpu(a[None]), f32_to_gpu(s[None]), B, 1.0)
+    torch.cuda.synchronize()
+    # equal codes, except that a -0 code may come back as +0 (its value is zero either way)
+    assert np.array_equal(cpu(cq), np.where(q == 0x80, 0, q))
+    nz = s > 0
+    assert_rel_close(cpu(cs)[nz] / cpu(ca)[nz], s[nz].astype(np.float64) / a[nz], 1e-6,
+                     what="s/alpha under P=1")
+
+
+# ----------------------------------------------------------------------------- robustness
+
+def test_guard_bytes_untouched(tfp8):
+    B, nb = 128, 29
+    n = nb * B
+    x = bits_to_gpu(random_bf16_bits(n, seed=3))
+    pad = 4096
+    codes = torch.full((n + 2 * pad,), 0xA5, dtype=torch.uint8, device=DEV)
+    alpha = torch.full((nb + 2 * 64,), 7.0, dtype=torch.float32, device=DEV)
+    scale = torch.full((nb + 2 * 64,), 9.0, dtype=torch.float32, device=DEV)
+    out = (codes[pad:pad + n], alpha[64:64 + nb], scale[64:64 + nb])
+    tfp8.compress(x, B, 1.0, out=out)
+    dec = torch.full((n + 2 * pad,), -3.0, dtype=torch.float32, device=DEV)
+    tfp8.decompress(*out, B, torch.float32, out=dec[pad:pad + n])
+    torch.cuda.synchronize()
+    c, a, s, d = cpu(codes), cpu(alpha), cpu(scale), cpu(dec)
+    assert np.all(c[:pad] == 0xA5) and np.all(c[pad + n:] == 0xA5)
+    assert np.all(a[:64] == 7.0) and np.all(a[64 + nb:] == 7.0)
+    assert np.all(s[:64] == 9.0) and np.all(s[64 + nb:] == 9.0)
+    assert np.all(d[:pad] == -3.0) and np.all(d[pad + n:] == -3.0)
+
+
+def test_bitwise_deterministic_and_stream_safe(tfp8):
+    x = bits_to_gpu(make_shard(2).reshape(-1))
+    r1 = tfp8.compress(x, 128, 1.0)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        r2 = tfp8.compress(x, 128, 1.0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for u, v in zip(r1, r2):
+        assert torch.equal(u, v)
+
+
+def test_zero_length_is_noop(tfp8):
+    x = torch.empty(0, dtype=torch.bfloat16, device=DEV)
+    q, a, s = tfp8.compress(x, 128, 1.0)
+    assert q.numel() == 0 and a.numel() == 0
