@@ -48,6 +48,23 @@ __device__ __forceinline__ float group_max(float v) {
   return v;
 }
 
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
+}
+
+// Integer max over the L lanes of a group.
+template <int L>
+__device__ __forceinline__ int group_max_i(int v) {
+  static_assert(L == 4 || L == 8 || L == 16 || L == 32, "group of 4, 8, 16 or 32 lanes");
+  v = max(v, dpp_i<kDppXor1>(v));
+  v = max(v, dpp_i<kDppXor2>(v));
+  if constexpr (L >= 8) v = max(v, dpp_i<kDppHalfMirror>(v));
+  if constexpr (L >= 16) v = max(v, dpp_i<kDppRowMirror>(v));
+  if constexpr (L >= 32) v = max(v, __builtin_amdgcn_ds_swizzle(v, 0x401F));
+  return v;
+}
+
 template <int L>
 __device__ __forceinline__ float group_sum(float v) {
   static_assert(L == 4 || L == 8 || L == 16 || L == 32, "group of 4, 8, 16 or 32 lanes");
@@ -81,7 +98,7 @@ __device__ __forceinline__ void fwht_registers(float (&v)[N]) {
 // the difference.  Partners are lane^7 first (no xor-4 lane select exists in DPP), then lane^1
 // and lane^2, with sigma from lane bits 2, 0 and 1.  Mask 7 = 4 ^ 3, so the three masks still
 // span all lane bits; the network computes a signed permutation of the natural transform:
-// lane j ends with kLaneSign[j] * (H_8 v)[kLanePerm[j]] (worked out by enumerating the
+// lane j ends with lane8_sign(j) * (H_8 v)[lane8_perm(j)] (worked out by enumerating the
 // network on the unit vectors).
 __device__ __forceinline__ int lane8_perm(int j) {
   // 0,5,6,3,4,1,2,7: bit 2 flips when bits 0 and 1 differ
@@ -128,7 +145,6 @@ __device__ __forceinline__ void unpack_fp8x4(uint32_t w, float &a, float &b, flo
 }
 
 __device__ __forceinline__ int exponent_of(float x) { return __builtin_amdgcn_frexp_expf(x); }
-__device__ __forceinline__ float mantissa_of(float x) { return __builtin_amdgcn_frexp_mantf(x); }
 __device__ __forceinline__ float scale2(float x, int k) { return __builtin_amdgcn_ldexpf(x, k); }
 
 }  // namespace tfp8

@@ -30,7 +30,9 @@
 //
 // Reduce.  Sum of reconstructions z = sum_p H (s_p dec q_p) / (sqrt(B) alpha_p) = H r / sqrt(B)
 // with r = sum_p (s_p / alpha_p) dec(q_p); requantising z gives y' = alpha' r exactly, so the
-// reduce works on r directly with no Hadamard at all, and max|y'| = alpha' max|r|.
+// reduce works on r directly with no Hadamard at all, and max|y'| = alpha' max|r|.  The sum is
+// accumulated in float64 (as fast as unpacked float32 on this chip), which keeps it exact
+// enough that contributions which largely cancel still requantise like the exact sum.
 
 #include <math.h>
 #include <stdint.h>
@@ -272,52 +274,72 @@ __global__ __launch_bounds__(kThreads) void k_reduce(const uint8_t *__restrict__
     const bool active = blk < nb;
     const int64_t cblk = active ? blk : 0;  // inactive groups read block 0 and store nothing
 
-    // Common exponent of the dequantisation factors g_p = s_p / alpha_p, so that each g_p is
-    // formed as (mant s_p / mant alpha_p) * 2^(e_p - Emax) with no under- or overflow.
-    int Emax = -1000;
+    // Common exponent of the dequantisation factors g_p = s_p / alpha_p: every g_p is
+    // divided by 2^Emax so that the largest is near 1 and the sum rounds to a normal float32.
+    int Emax = -100000;
     for (int p = 0; p < P; ++p) {
       const float sp = scale[(int64_t)p * nb + cblk];
       const float ap = alpha[(int64_t)p * nb + cblk];
       if (sp != 0.0f) Emax = max(Emax, exponent_of(sp) - exponent_of(ap));
     }
-    if (Emax == -1000) Emax = 0;
+    if (Emax == -100000) Emax = 0;
 
-    float r[16];
+    // r = sum_p g_p dec(q_p), accumulated in float64.  g_p is cut to 49 significant bits
+    // (a relative change below 2^-48), so that its product with an E4M3 value (at most 4
+    // significant bits) is exact in float64; the only roundings are those of the running sum,
+    // each within 2^-53 of it.  Contributions that largely cancel therefore still requantise
+    // like the exact sum, and a contribution and its exact negation cancel to exactly zero.
+    double r64[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) r[i] = 0.0f;
+    for (int i = 0; i < 16; ++i) r64[i] = 0.0;
     const uint8_t *cb = codes + cblk * B + 16 * j;
     for (int p = 0; p < P; ++p) {
       const float sp = scale[(int64_t)p * nb + cblk];
       const float ap = alpha[(int64_t)p * nb + cblk];
-      const float g =
-          (sp == 0.0f)
-              ? 0.0f
-              : scale2(__fdiv_rn(mantissa_of(sp), mantissa_of(ap)),
-                       exponent_of(sp) - exponent_of(ap) - Emax);
+      double g = (sp == 0.0f) ? 0.0 : __builtin_amdgcn_ldexp((double)sp / (double)ap, -Emax);
+      g = __longlong_as_double(__double_as_longlong(g) & ~0xFLL);
       const u32x4 d = *(const u32x4 *)(cb + (int64_t)p * n);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         float a0, a1, a2, a3;
         unpack_fp8x4(d[q], a0, a1, a2, a3);
-        // product then sum (no fused multiply-add) so that a contribution and its negation
-        // cancel exactly
-        const float t0 = g * a0, t1 = g * a1, t2 = g * a2, t3 = g * a3;
-        if (p == 0) {
-          r[4 * q] = t0; r[4 * q + 1] = t1; r[4 * q + 2] = t2; r[4 * q + 3] = t3;
-        } else {
-          r[4 * q] += t0; r[4 * q + 1] += t1; r[4 * q + 2] += t2; r[4 * q + 3] += t3;
-        }
+        r64[4 * q + 0] = fma((double)a0, g, r64[4 * q + 0]);
+        r64[4 * q + 1] = fma((double)a1, g, r64[4 * q + 1]);
+        r64[4 * q + 2] = fma((double)a2, g, r64[4 * q + 2]);
+        r64[4 * q + 3] = fma((double)a3, g, r64[4 * q + 3]);
       }
     }
 
+    float r[16];
     float m = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(r[i]));
-    const float M = group_max<L>(m);
+    for (int i = 0; i < 16; ++i) {
+      r[i] = (float)r64[i];
+      m = fmaxf(m, fabsf(r[i]));
+    }
+    float M = group_max<L>(m);
+    int E = Emax;
+    if (M != 0.0f && !(M >= 0x1p-100f && M <= 0x1p100f)) {
+      // The contributions cancelled (or all were tiny): rescale the float64 sum so that its
+      // largest magnitude lies in [1, 2) before rounding it to float32.
+      double m64 = 0.0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) m64 = fmax(m64, fabs(r64[i]));
+      const int e64 = __builtin_amdgcn_frexp_exp(m64);
+      const int k = 1 - group_max_i<L>(e64);
+      m = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        r[i] = (float)__builtin_amdgcn_ldexp(r64[i], k);
+        m = fmaxf(m, fabsf(r[i]));
+      }
+      M = group_max<L>(m);
+      E -= k;
+    }
 
-    // the true sum is r * 2^Emax
+    // the true sum is r * 2^E
     float a_out, s_out;
-    requant_tail<L, 16>(r, M, Emax, TB, 448.0f, 1.0f, a_out, s_out);
+    requant_tail<L, 16>(r, M, E, TB, 448.0f, 1.0f, a_out, s_out);
     if (active) {
       u32x4 w;
 #pragma unroll
