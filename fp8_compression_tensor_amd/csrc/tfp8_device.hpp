@@ -76,11 +76,12 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
-// Unnormalised Walsh-Hadamard transform of the N values a lane holds (natural order).
-template <int N>
+// Unnormalised Walsh-Hadamard transform of the N values a lane holds (natural order),
+// starting at register stride H0 (H0 = 2 when the stride-1 stage was done at load time).
+template <int N, int H0 = 1>
 __device__ __forceinline__ void fwht_registers(float (&v)[N]) {
 #pragma unroll
-  for (int h = 1; h < N; h <<= 1) {
+  for (int h = H0; h < N; h <<= 1) {
 #pragma unroll
     for (int i = 0; i < N; i += 2 * h) {
 #pragma unroll
@@ -93,13 +94,13 @@ __device__ __forceinline__ void fwht_registers(float (&v)[N]) {
   }
 }
 
-// Hadamard transform across the 8 lanes of a group, one fused multiply-add per value and
-// stage: value <- value + sigma * partner, with sigma = -1 on the lane of each pair that keeps
-// the difference.  Partners are lane^7 first (no xor-4 lane select exists in DPP), then lane^1
-// and lane^2, with sigma from lane bits 2, 0 and 1.  Mask 7 = 4 ^ 3, so the three masks still
-// span all lane bits; the network computes a signed permutation of the natural transform:
-// lane j ends with lane8_sign(j) * (H_8 v)[lane8_perm(j)] (worked out by enumerating the
-// network on the unit vectors).
+// Hadamard transform across the 8 lanes of a group, one instruction per value and stage:
+// v_fmac_f32 with a DPP-selected partner, value <- value + sigma * partner, where sigma = -1 on
+// the lane of each pair that keeps the difference.  Partners are lane^7 first (DPP has no
+// xor-4 lane select), then lane^1 and lane^2, with sigma from lane bits 2, 0 and 1.  Mask 7 =
+// 4 ^ 3, so the three masks still span all lane bits; the network computes a signed
+// permutation of the natural transform: lane j ends with lane8_sign(j) * (H_8 v)[lane8_perm(j)]
+// (worked out by enumerating the network on the unit vectors).
 __device__ __forceinline__ int lane8_perm(int j) {
   // 0,5,6,3,4,1,2,7: bit 2 flips when bits 0 and 1 differ
   return j ^ (((j ^ (j >> 1)) & 1) << 2);
@@ -109,17 +110,61 @@ __device__ __forceinline__ float lane8_sign(int j) {
   return (j == 0 || j == 3) ? 1.0f : -1.0f;
 }
 
+// Eight in-place DPP multiply-adds in one asm block.  The compiler does not model the DPP
+// read-after-VALU-write hazard for inline asm, so the block starts with the two wait states it
+// needs; inside the block every instruction reads a register the previous two did not write.
+#define TFP8_DPP_FMAC8(CTRL, a, sgn)                                                          \
+  asm("s_nop 1\n\t"                                                                          \
+      "v_fmac_f32_dpp %0, %0, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                   \
+      "v_fmac_f32_dpp %1, %1, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                   \
+      "v_fmac_f32_dpp %2, %2, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                   \
+      "v_fmac_f32_dpp %3, %3, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                   \
+      "v_fmac_f32_dpp %4, %4, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                   \
+      "v_fmac_f32_dpp %5, %5, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                   \
+      "v_fmac_f32_dpp %6, %6, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                   \
+      "v_fmac_f32_dpp %7, %7, %8 " CTRL " row_mask:0xf bank_mask:0xf"                         \
+      : "+v"((a)[0]), "+v"((a)[1]), "+v"((a)[2]), "+v"((a)[3]), "+v"((a)[4]), "+v"((a)[5]),  \
+        "+v"((a)[6]), "+v"((a)[7])                                                          \
+      : "v"(sgn))
+
 template <int N>
 __device__ __forceinline__ void fwht_lanes8(float (&v)[N], int j) {
+  static_assert(N % 8 == 0, "lane transform works on groups of 8 registers");
   const float s7 = (j & 4) ? -1.0f : 1.0f;
   const float s1 = (j & 1) ? -1.0f : 1.0f;
   const float s2 = (j & 2) ? -1.0f : 1.0f;
 #pragma unroll
-  for (int r = 0; r < N; ++r) v[r] = fmaf(dpp<kDppHalfMirror>(v[r]), s7, v[r]);
+  for (int r = 0; r < N; r += 8) TFP8_DPP_FMAC8("row_half_mirror", &v[r], s7);
 #pragma unroll
-  for (int r = 0; r < N; ++r) v[r] = fmaf(dpp<kDppXor1>(v[r]), s1, v[r]);
+  for (int r = 0; r < N; r += 8) TFP8_DPP_FMAC8("quad_perm:[1,0,3,2]", &v[r], s1);
 #pragma unroll
-  for (int r = 0; r < N; ++r) v[r] = fmaf(dpp<kDppXor2>(v[r]), s2, v[r]);
+  for (int r = 0; r < N; r += 8) TFP8_DPP_FMAC8("quad_perm:[2,3,0,1]", &v[r], s2);
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// First butterfly of a bfloat16 pair straight from its packed dword: (lo + hi, lo - hi), with
+// v_dot2_f32_bf16 against (1, 1) and (1, -1).  Each product is exact; the sum is rounded
+// once (to within an ulp: the instruction does not round magnitude-disparate addends
+// exactly to nearest), and bfloat16 subnormals are kept.  Written as asm to get the
+// three-operand form with a zero addend (the compiler picks the accumulating form plus a
+// move that zeroes the accumulator).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b) {
+  float r;
+  asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
+__device__ __forceinline__ void bf16_pair_butterfly(uint32_t d, uint32_t ones, uint32_t plus_minus,
+                                                    float &sum, float &dif) {
+  sum = dot2_bf16(d, ones);
+  dif = dot2_bf16(d, plus_minus);
+}
+
+// acc + lo^2 + hi^2 of a packed bfloat16 pair (squares exact).
+__device__ __forceinline__ float bf16_pair_sumsq(uint32_t d, float acc) {
+  const bf16x2 x = __builtin_bit_cast(bf16x2, d);
+  return __builtin_amdgcn_fdot2_f32_bf16(x, x, acc, false);
 }
 
 // bfloat16 pair in one dword -> two floats (exact).

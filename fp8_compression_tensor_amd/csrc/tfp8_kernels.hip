@@ -44,20 +44,40 @@ namespace tfp8 {
 
 constexpr int kThreads = 256;  // 4 wavefronts per workgroup
 
+// Streaming loads and stores: every input byte is read once and every output byte written
+// once, so they go through the cache hierarchy with the non-temporal hint.
+template <class T>
+__device__ __forceinline__ T ld_stream(const T *p) {
+#if defined(TFP8_NO_NT)
+  return *p;
+#else
+  return __builtin_nontemporal_load(p);
+#endif
+}
+template <class T>
+__device__ __forceinline__ void st_stream(T v, T *p) {
+#if defined(TFP8_NO_NT)
+  *p = v;
+#else
+  __builtin_nontemporal_store(v, p);
+#endif
+}
+
 // --------------------------------------------------------------------------------------------
-// Shared tail: from the rotated values of one block (held by a group of L lanes) to codes,
-// alpha and s.
+// Range-safe scales: from the rotated values of one block (held by a group of L lanes) to the
+// code multiplier, alpha and s, for any block -- all-zero, bfloat16-subnormal or huge.
 //
-//   v      values in registers; the true values are sign * v * 2^E0
+//   v      values in registers; the true values are v * 2^E0 (times the lane sign)
 //   M      max|v| over the block (every lane of the group holds it)
-//   E0     exponent offset of v (0 for compress; the common exponent of the reduce)
+//   E0     exponent offset of v (0 for compress; the reduce's common exponent)
 //   TBB    T * B^2 for compress (v = H x unnormalised), T * B for reduce (v = r)
 //   C      448 * sqrt(B) for compress, 448 for reduce
 //   sign   +-1 lane sign folded into the code multiplier
-// Outputs u[] (pre-rounding code values) and the block's alpha and s.
+// On return v may be rescaled by a power of two, and v * code_mult are the codes' values.
 template <int L, int N>
-__device__ __forceinline__ void requant_tail(float (&v)[N], float M, int E0, float TBB, float C,
-                                             float sign, float &alpha_out, float &scale_out) {
+__device__ __forceinline__ void scales_exact(float (&v)[N], float M, int E0, float TBB, float C,
+                                             float sign, float &code_mult, float &alpha_out,
+                                             float &scale_out) {
   int E = E0;
   if (M != 0.0f && !(M >= 0x1p-100f && M <= 0x1p100f)) {
     // Bring max|v| into [1, 2) by an exact power of two so that 448 / M is a normal float.
@@ -69,28 +89,54 @@ __device__ __forceinline__ void requant_tail(float (&v)[N], float M, int E0, flo
   }
   const bool zero = (M == 0.0f);
   const float c = zero ? 0.0f : __fdiv_rn(448.0f, M);
-  const float cl = c * sign;
+  // energy from the codes' values u = v c: sum(u^2) = c^2 sum(v^2) stays in float32 range
   float su = 0.0f;
 #pragma unroll
   for (int r = 0; r < N; ++r) {
-    v[r] = fmaf(v[r], cl, 0.0f);  // + 0 turns a -0 product into +0
-    su = fmaf(v[r], v[r], su);
+    const float u = v[r] * c;
+    su = fmaf(u, u, su);
   }
   const float SU = group_sum<L>(su);
   const float a2 = c * __fsqrt_rn(__fdiv_rn(TBB, SU));
   const float alpha = fminf(fmaxf(scale2(a2, -E), 0x1p-126f), 0x1p126f);
   const float s = __fdiv_rn(scale2(alpha, E) * M, C);
+  code_mult = c * sign;
   alpha_out = zero ? 1.0f : alpha;
   scale_out = zero ? 0.0f : s;
 }
 
 // --------------------------------------------------------------------------------------------
-// K1: compress.  One wavefront handles 8 blocks per iteration of a grid-stride loop.
+// K1: compress.  One wavefront handles 8 blocks per iteration of a grid-stride loop and
+// prefetches the next iteration's input before working on the current one.
+
+template <int B, bool F32IN>
+struct CompressIn {
+  static constexpr int kRuns = B / 64;                    // 8-element runs per lane
+  static constexpr int kLoads = F32IN ? 2 * kRuns : kRuns;  // 16-byte loads per lane
+  u32x4 d[kLoads];
+};
+
+template <int B, bool F32IN>
+__device__ __forceinline__ void load_compress_in(CompressIn<B, F32IN> &in, const void *xin,
+                                                 int64_t blk, int j) {
+  if constexpr (!F32IN) {
+    const uint16_t *xb = (const uint16_t *)xin + blk * B + 8 * j;
+#pragma unroll
+    for (int g = 0; g < B / 64; ++g) in.d[g] = ld_stream((const u32x4 *)(xb + 64 * g));
+  } else {
+    const float *xb = (const float *)xin + blk * B + 8 * j;
+#pragma unroll
+    for (int g = 0; g < B / 64; ++g) {
+      in.d[2 * g] = ld_stream((const u32x4 *)(xb + 64 * g));
+      in.d[2 * g + 1] = ld_stream((const u32x4 *)(xb + 64 * g + 4));
+    }
+  }
+}
 
 template <int B, bool F32IN>
 __global__ __launch_bounds__(kThreads) void k_compress(const void *__restrict__ xin, int64_t nb,
-                                                       float TBB, float C,
-                                                       uint8_t *__restrict__ codes,
+                                                       float TBB, float sqrtTB, float C,
+                                                       float invC, uint8_t *__restrict__ codes,
                                                        float *__restrict__ alpha_out,
                                                        float *__restrict__ scale_out) {
   constexpr int N = B / 8;   // elements per lane
@@ -103,69 +149,113 @@ __global__ __launch_bounds__(kThreads) void k_compress(const void *__restrict__ 
   const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
   const int64_t nwaves = ((int64_t)gridDim.x * kThreads) >> 6;
   const int64_t ntiles = (nb + 7) >> 3;
+  // packed bfloat16 (1, 1) and (1, -1), kept in registers for v_dot2_f32_bf16
+  const uint32_t ones = 0x3F803F80u, plus_minus = 0xBF803F80u;
+
+  // Groups past the last block (ragged last tile) read the last block again and store
+  // nothing, so every load is in bounds and every register holds data.
+  CompressIn<B, F32IN> cur;
+  if (wave < ntiles) load_compress_in<B, F32IN>(cur, xin, min(wave * 8 + bw, nb - 1), j);
 
   for (int64_t tile = wave; tile < ntiles; tile += nwaves) {
     const int64_t blk = tile * 8 + bw;
     const bool active = blk < nb;
+    CompressIn<B, F32IN> nxt;
+    if (tile + nwaves < ntiles)
+      load_compress_in<B, F32IN>(nxt, xin, min((tile + nwaves) * 8 + bw, nb - 1), j);
+
+    // Widen, energy and the first butterfly stages.  Groups past the last block work on a
+    // copy of the last block and store nothing.
     float v[N];
-    if (active) {
-      if constexpr (!F32IN) {
-        const uint16_t *xb = (const uint16_t *)xin + blk * B + 8 * j;
+    float ss = 0.0f;
+    if constexpr (!F32IN) {
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const u32x4 d = *(const u32x4 *)(xb + 64 * g);
+      for (int g = 0; g < G; ++g)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) widen_bf16x2(d[q], v[8 * g + 2 * q], v[8 * g + 2 * q + 1]);
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t d = cur.d[g][q];
+          bf16_pair_butterfly(d, ones, plus_minus, v[8 * g + 2 * q], v[8 * g + 2 * q + 1]);
+          ss = bf16_pair_sumsq(d, ss);
         }
-      } else {
-        const float *xb = (const float *)xin + blk * B + 8 * j;
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const u32x4 d0 = *(const u32x4 *)(xb + 64 * g);
-          const u32x4 d1 = *(const u32x4 *)(xb + 64 * g + 4);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            v[8 * g + q] = __uint_as_float(d0[q]);
-            v[8 * g + 4 + q] = __uint_as_float(d1[q]);
-          }
-        }
-      }
+      fwht_registers<N, 2>(v);
     } else {
 #pragma unroll
-      for (int r = 0; r < N; ++r) v[r] = 0.0f;
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          v[8 * g + q] = __uint_as_float(cur.d[2 * g][q]);
+          v[8 * g + 4 + q] = __uint_as_float(cur.d[2 * g + 1][q]);
+        }
+#pragma unroll
+      for (int r = 0; r < N; ++r) ss = fmaf(v[r], v[r], ss);
+      fwht_registers<N, 1>(v);
     }
-
-    // orthogonal Hadamard rotation (unnormalised; 1/sqrt(B) and alpha are carried in s)
-    fwht_registers<N>(v);
+    // orthogonal Hadamard rotation, unnormalised: w = H x (1/sqrt(B) and alpha live in s)
     fwht_lanes8<N>(v, j);
 
     float m = 0.0f;
 #pragma unroll
     for (int r = 0; r < N; ++r) m = fmaxf(m, fabsf(v[r]));
     const float M = group_max<8>(m);
+    const float SS = group_sum<8>(ss);  // sum(x^2) of the block
 
-    float alpha, s;
-    requant_tail<8, N>(v, M, 0, TBB, C, sj, alpha, s);
+    // alpha = sqrt(T B / sum x^2), s = alpha max|w| / (448 sqrt B), codes = E4M3(448 w / max|w|).
+    // For max|w| in [2^-40, 2^60] every quantity stays normal and sum(x^2) is accurate, so the
+    // scales use the single-instruction reciprocal square root (1 ulp, inside the 1e-6 bar);
+    // the code multiplier 448 / max|w| is correctly rounded, so that a quotient that is exactly
+    // a rounding midpoint stays exact and rounds to even.  Other blocks (all-zero,
+    // bfloat16-subnormal, huge) take the range-safe path.
+    float cm, alpha, s;
+    if (M >= 0x1p-40f && M <= 0x1p60f) {
+      const float c = __fdiv_rn(448.0f, M);
+      alpha = fminf(fmaxf(sqrtTB * __builtin_amdgcn_rsqf(SS), 0x1p-126f), 0x1p126f);
+      s = alpha * M * invC;
+      cm = c * sj;
+    } else {
+      scales_exact<8, N>(v, M, 0, TBB, C, sj, cm, alpha, s);
+    }
 
     if (active) {
       uint8_t *cb = codes + blk * B + 8 * pj;
 #pragma unroll
       for (int g = 0; g < G; ++g) {
+        float u[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) u[e] = fmaf(v[8 * g + e], cm, 0.0f);  // +0 keeps zeros +0
         u32x2 w;
-        w[0] = pack_fp8x4(v[8 * g + 0], v[8 * g + 1], v[8 * g + 2], v[8 * g + 3]);
-        w[1] = pack_fp8x4(v[8 * g + 4], v[8 * g + 5], v[8 * g + 6], v[8 * g + 7]);
-        *(u32x2 *)(cb + 64 * g) = w;
+        w[0] = pack_fp8x4(u[0], u[1], u[2], u[3]);
+        w[1] = pack_fp8x4(u[4], u[5], u[6], u[7]);
+        st_stream(w, (u32x2 *)(cb + 64 * g));
       }
       if (j == 0) {
         alpha_out[blk] = alpha;
         scale_out[blk] = s;
       }
     }
+    cur = nxt;
   }
 }
 
 // --------------------------------------------------------------------------------------------
-// K2: decompress.  x = H (s dec q) / (sqrt(B) alpha), same lane layout as compress.
+// K2: decompress.  x = H (s dec q) / (sqrt(B) alpha), same lane layout as compress, with the
+// next iteration's codes and scales prefetched.
+
+template <int B>
+struct DecompressIn {
+  u32x2 d[B / 64];
+  float s, a;
+};
+
+template <int B>
+__device__ __forceinline__ void load_decompress_in(DecompressIn<B> &in, const uint8_t *codes,
+                                                   const float *alpha, const float *scale,
+                                                   int64_t blk, int j) {
+  const uint8_t *cb = codes + blk * B + 8 * j;
+#pragma unroll
+  for (int g = 0; g < B / 64; ++g) in.d[g] = ld_stream((const u32x2 *)(cb + 64 * g));
+  in.s = scale[blk];
+  in.a = alpha[blk];
+}
 
 template <int B, bool F32OUT>
 __global__ __launch_bounds__(kThreads) void k_decompress(const uint8_t *__restrict__ codes,
@@ -184,30 +274,29 @@ __global__ __launch_bounds__(kThreads) void k_decompress(const uint8_t *__restri
   const int64_t nwaves = ((int64_t)gridDim.x * kThreads) >> 6;
   const int64_t ntiles = (nb + 7) >> 3;
 
+  DecompressIn<B> cur;  // groups past the last block re-read the last block, store nothing
+  if (wave < ntiles) load_decompress_in<B>(cur, codes, alpha, scale, min(wave * 8 + bw, nb - 1), j);
+
   for (int64_t tile = wave; tile < ntiles; tile += nwaves) {
     const int64_t blk = tile * 8 + bw;
     const bool active = blk < nb;
+    DecompressIn<B> nxt;
+    if (tile + nwaves < ntiles)
+      load_decompress_in<B>(nxt, codes, alpha, scale, min((tile + nwaves) * 8 + bw, nb - 1), j);
+
     float v[N];
-    float s = 0.0f, a = 1.0f;
-    if (active) {
-      const uint8_t *cb = codes + blk * B + 8 * j;
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const u32x2 w = *(const u32x2 *)(cb + 64 * g);
-        unpack_fp8x4(w[0], v[8 * g + 0], v[8 * g + 1], v[8 * g + 2], v[8 * g + 3]);
-        unpack_fp8x4(w[1], v[8 * g + 4], v[8 * g + 5], v[8 * g + 6], v[8 * g + 7]);
-      }
-      s = scale[blk];
-      a = alpha[blk];
-    } else {
-#pragma unroll
-      for (int r = 0; r < N; ++r) v[r] = 0.0f;
+    for (int g = 0; g < G; ++g) {
+      const uint32_t w0 = cur.d[g][0], w1 = cur.d[g][1];
+      unpack_fp8x4(w0, v[8 * g + 0], v[8 * g + 1], v[8 * g + 2], v[8 * g + 3]);
+      unpack_fp8x4(w1, v[8 * g + 4], v[8 * g + 5], v[8 * g + 6], v[8 * g + 7]);
     }
+    const float s = cur.s, a = cur.a;
 
     // The decoded values are multiples of 2^-9 below 2^8.81, so every partial sum of the
     // transform is exact in float32 until it passes 2^15 (for B <= 128 only the last stage
     // can round, once).
-    fwht_registers<N>(v);
+    fwht_registers<N, 1>(v);
     fwht_lanes8<N>(v, j);
 
     // (v * s / sqrt(B)) / alpha as two products: s / (sqrt(B) alpha) alone can fall below the
@@ -226,8 +315,8 @@ __global__ __launch_bounds__(kThreads) void k_decompress(const uint8_t *__restri
             w0[q] = __float_as_uint(fmaf(v[8 * g + q], f, 0.0f) * ra);
             w1[q] = __float_as_uint(fmaf(v[8 * g + 4 + q], f, 0.0f) * ra);
           }
-          *(u32x4 *)(ob + 64 * g) = w0;
-          *(u32x4 *)(ob + 64 * g + 4) = w1;
+          st_stream(w0, (u32x4 *)(ob + 64 * g));
+          st_stream(w1, (u32x4 *)(ob + 64 * g + 4));
         }
       } else {
         __bf16 *ob = (__bf16 *)out + blk * B + 8 * pj;
@@ -241,18 +330,20 @@ __global__ __launch_bounds__(kThreads) void k_decompress(const uint8_t *__restri
             w[q] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
                    ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
           }
-          *(u32x4 *)(ob + 64 * g) = w;
+          st_stream(w, (u32x4 *)(ob + 64 * g));
         }
       }
     }
+    cur = nxt;
   }
 }
 
 // --------------------------------------------------------------------------------------------
 // K3: reduce.  B/16 lanes per block, 16 consecutive codes per lane (one 16-byte load per
-// contribution), no Hadamard.
+// contribution), no Hadamard.  PB > 0: exactly PB contributions, all loads issued before any
+// arithmetic; PB = 0: any P, in chunks of 8.
 
-template <int B>
+template <int B, int PB>
 __global__ __launch_bounds__(kThreads) void k_reduce(const uint8_t *__restrict__ codes,
                                                      const float *__restrict__ alpha,
                                                      const float *__restrict__ scale, int P,
@@ -262,6 +353,8 @@ __global__ __launch_bounds__(kThreads) void k_reduce(const uint8_t *__restrict__
                                                      float *__restrict__ scale_out) {
   constexpr int L = B / 16;    // lanes per block
   constexpr int BPW = 64 / L;  // blocks per wavefront
+  constexpr int CH = PB > 0 ? PB : 8;  // contributions loaded together
+  if constexpr (PB > 0) P = PB;
   const int lane = threadIdx.x & 63;
   const int j = lane % L;
   const int bw = lane / L;
@@ -272,41 +365,52 @@ __global__ __launch_bounds__(kThreads) void k_reduce(const uint8_t *__restrict__
   for (int64_t tile = wave; tile < ntiles; tile += nwaves) {
     const int64_t blk = tile * BPW + bw;
     const bool active = blk < nb;
-    const int64_t cblk = active ? blk : 0;  // inactive groups read block 0 and store nothing
-
-    // Common exponent of the dequantisation factors g_p = s_p / alpha_p: every g_p is
-    // divided by 2^Emax so that the largest is near 1 and the sum rounds to a normal float32.
-    int Emax = -100000;
-    for (int p = 0; p < P; ++p) {
-      const float sp = scale[(int64_t)p * nb + cblk];
-      const float ap = alpha[(int64_t)p * nb + cblk];
-      if (sp != 0.0f) Emax = max(Emax, exponent_of(sp) - exponent_of(ap));
-    }
-    if (Emax == -100000) Emax = 0;
-
-    // r = sum_p g_p dec(q_p), accumulated in float64.  g_p is cut to 49 significant bits
-    // (a relative change below 2^-48), so that its product with an E4M3 value (at most 4
-    // significant bits) is exact in float64; the only roundings are those of the running sum,
-    // each within 2^-53 of it.  Contributions that largely cancel therefore still requantise
-    // like the exact sum, and a contribution and its exact negation cancel to exactly zero.
-    double r64[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) r64[i] = 0.0;
+    const int64_t cblk = active ? blk : nb - 1;  // groups past the end re-read the last block
     const uint8_t *cb = codes + cblk * B + 16 * j;
-    for (int p = 0; p < P; ++p) {
-      const float sp = scale[(int64_t)p * nb + cblk];
-      const float ap = alpha[(int64_t)p * nb + cblk];
-      double g = (sp == 0.0f) ? 0.0 : __builtin_amdgcn_ldexp((double)sp / (double)ap, -Emax);
-      g = __longlong_as_double(__double_as_longlong(g) & ~0xFLL);
-      const u32x4 d = *(const u32x4 *)(cb + (int64_t)p * n);
+
+    // r = sum_p g_p dec(q_p) with g_p = s_p / alpha_p, accumulated in float64.  g_p is cut to
+    // 49 significant bits (a relative change below 2^-48), so that its product with an E4M3
+    // value (at most 4 significant bits) is exact in float64; the only roundings are those of
+    // the running sum, each within 2^-53 of it.  Contributions that largely cancel therefore
+    // still requantise like the exact sum, and a contribution and its exact negation cancel
+    // to exactly zero.  A zero block (s_p = 0) contributes exact zeros.
+    double r64[16];
+    for (int p0 = 0; p0 < P; p0 += CH) {
+      u32x4 d[CH];
+      float sp[CH], ap[CH];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float a0, a1, a2, a3;
-        unpack_fp8x4(d[q], a0, a1, a2, a3);
-        r64[4 * q + 0] = fma((double)a0, g, r64[4 * q + 0]);
-        r64[4 * q + 1] = fma((double)a1, g, r64[4 * q + 1]);
-        r64[4 * q + 2] = fma((double)a2, g, r64[4 * q + 2]);
-        r64[4 * q + 3] = fma((double)a3, g, r64[4 * q + 3]);
+      for (int c = 0; c < CH; ++c)
+        if (PB > 0 || p0 + c < P) {
+          d[c] = ld_stream((const u32x4 *)(cb + (int64_t)(p0 + c) * n));
+          sp[c] = scale[(int64_t)(p0 + c) * nb + cblk];
+          ap[c] = alpha[(int64_t)(p0 + c) * nb + cblk];
+        }
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        if (PB > 0 || p0 + c < P) {
+          // 1/alpha in float64: hardware reciprocal refined by two Newton steps
+          const double ad = (double)ap[c];
+          double ri = __builtin_amdgcn_rcp(ad);
+          ri = fma(ri, fma(-ad, ri, 1.0), ri);
+          ri = fma(ri, fma(-ad, ri, 1.0), ri);
+          const double g = __longlong_as_double(__double_as_longlong((double)sp[c] * ri) & ~0xFLL);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float a0, a1, a2, a3;
+            unpack_fp8x4(d[c][q], a0, a1, a2, a3);
+            if (p0 + c == 0) {
+              r64[4 * q + 0] = (double)a0 * g;
+              r64[4 * q + 1] = (double)a1 * g;
+              r64[4 * q + 2] = (double)a2 * g;
+              r64[4 * q + 3] = (double)a3 * g;
+            } else {
+              r64[4 * q + 0] = fma((double)a0, g, r64[4 * q + 0]);
+              r64[4 * q + 1] = fma((double)a1, g, r64[4 * q + 1]);
+              r64[4 * q + 2] = fma((double)a2, g, r64[4 * q + 2]);
+              r64[4 * q + 3] = fma((double)a3, g, r64[4 * q + 3]);
+            }
+          }
+        }
       }
     }
 
@@ -318,10 +422,11 @@ __global__ __launch_bounds__(kThreads) void k_reduce(const uint8_t *__restrict__
       m = fmaxf(m, fabsf(r[i]));
     }
     float M = group_max<L>(m);
-    int E = Emax;
+    int E = 0;
     if (M != 0.0f && !(M >= 0x1p-100f && M <= 0x1p100f)) {
-      // The contributions cancelled (or all were tiny): rescale the float64 sum so that its
-      // largest magnitude lies in [1, 2) before rounding it to float32.
+      // Tiny or huge sum (bfloat16-subnormal blocks, or contributions that cancelled):
+      // rescale the float64 sum so that its largest magnitude lies in [1, 2) before rounding
+      // it to float32.
       double m64 = 0.0;
 #pragma unroll
       for (int i = 0; i < 16; ++i) m64 = fmax(m64, fabs(r64[i]));
@@ -338,13 +443,15 @@ __global__ __launch_bounds__(kThreads) void k_reduce(const uint8_t *__restrict__
     }
 
     // the true sum is r * 2^E
-    float a_out, s_out;
-    requant_tail<L, 16>(r, M, E, TB, 448.0f, 1.0f, a_out, s_out);
+    float cm, a_out, s_out;
+    scales_exact<L, 16>(r, M, E, TB, 448.0f, 1.0f, cm, a_out, s_out);
     if (active) {
       u32x4 w;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) w[q] = pack_fp8x4(r[4 * q], r[4 * q + 1], r[4 * q + 2], r[4 * q + 3]);
-      *(u32x4 *)(codes_out + blk * B + 16 * j) = w;
+      for (int q = 0; q < 4; ++q)
+        w[q] = pack_fp8x4(fmaf(r[4 * q], cm, 0.0f), fmaf(r[4 * q + 1], cm, 0.0f),
+                          fmaf(r[4 * q + 2], cm, 0.0f), fmaf(r[4 * q + 3], cm, 0.0f));
+      st_stream(w, (u32x4 *)(codes_out + blk * B + 16 * j));
       if (j == 0) {
         alpha_out[blk] = a_out;
         scale_out[blk] = s_out;
@@ -357,6 +464,16 @@ __global__ __launch_bounds__(kThreads) void k_reduce(const uint8_t *__restrict__
 
 // ============================================================================================
 // Host side of the C ABI: argument checks (before any HIP call), kernel choice, launch shape.
+
+#ifndef TFP8_COMPRESS_WGS_PER_CU
+#define TFP8_COMPRESS_WGS_PER_CU 0
+#endif
+#ifndef TFP8_DECOMPRESS_WGS_PER_CU
+#define TFP8_DECOMPRESS_WGS_PER_CU 0
+#endif
+#ifndef TFP8_REDUCE_WGS_PER_CU
+#define TFP8_REDUCE_WGS_PER_CU 32
+#endif
 
 namespace {
 
@@ -380,9 +497,12 @@ bool target_ok(float t) {
   return isfinite(t) && t >= 0x1p-64f && t <= 0x1p64f;
 }
 
-// Workgroups for a grid-stride launch: one wavefront per tile up to 8 resident workgroups
-// (32 wavefronts) per compute unit.
-unsigned grid_for(int64_t tiles) {
+// Workgroups for a launch with one wavefront per tile, capped at `per_cu` workgroups per
+// compute unit (0: no cap) beyond which the wavefronts loop over tiles.  Measured on MI355X:
+// compress and decompress stream fastest with one tile per wavefront and no loop (the
+// hardware keeps the CUs fed as wavefronts retire); the reduce, whose wavefronts each carry
+// P loads in flight, is fastest with 32 workgroups per CU.
+unsigned grid_for(int64_t tiles, int per_cu) {
   static int cu_count = 0;
   if (cu_count == 0) {
     int dev = 0, cus = 0;
@@ -394,7 +514,7 @@ unsigned grid_for(int64_t tiles) {
       cu_count = 256;
   }
   const int64_t wgs = (tiles + (kThreads / 64) - 1) / (kThreads / 64);
-  const int64_t cap = (int64_t)cu_count * 8;
+  const int64_t cap = per_cu > 0 ? (int64_t)cu_count * per_cu : (int64_t)1 << 30;
   return (unsigned)(wgs < cap ? (wgs > 0 ? wgs : 1) : cap);
 }
 
@@ -406,14 +526,16 @@ template <int B>
 tfp8_status launch_compress(const void *x, bool f32, int64_t nb, float target, uint8_t *codes,
                             float *alpha, float *scale, hipStream_t st) {
   const float TBB = target * (float)B * (float)B;  // exact: powers of two
-  const float C = (float)(448.0 * sqrt((double)B));
-  const unsigned grid = grid_for((nb + 7) / 8);
+  const float sqrtTB = (float)sqrt((double)target * B);
+  const double Cd = 448.0 * sqrt((double)B);
+  const float C = (float)Cd, invC = (float)(1.0 / Cd);
+  const unsigned grid = grid_for((nb + 7) / 8, TFP8_COMPRESS_WGS_PER_CU);
   if (f32)
-    hipLaunchKernelGGL((k_compress<B, true>), dim3(grid), dim3(kThreads), 0, st, x, nb, TBB, C,
-                       codes, alpha, scale);
+    hipLaunchKernelGGL((k_compress<B, true>), dim3(grid), dim3(kThreads), 0, st, x, nb, TBB, sqrtTB,
+                       C, invC, codes, alpha, scale);
   else
-    hipLaunchKernelGGL((k_compress<B, false>), dim3(grid), dim3(kThreads), 0, st, x, nb, TBB, C,
-                       codes, alpha, scale);
+    hipLaunchKernelGGL((k_compress<B, false>), dim3(grid), dim3(kThreads), 0, st, x, nb, TBB,
+                       sqrtTB, C, invC, codes, alpha, scale);
   return launched();
 }
 
@@ -421,7 +543,7 @@ template <int B>
 tfp8_status launch_decompress(const uint8_t *codes, const float *alpha, const float *scale,
                               int64_t nb, void *out, bool f32, hipStream_t st) {
   const float inv_sqrt_b = (float)(1.0 / sqrt((double)B));
-  const unsigned grid = grid_for((nb + 7) / 8);
+  const unsigned grid = grid_for((nb + 7) / 8, TFP8_DECOMPRESS_WGS_PER_CU);
   if (f32)
     hipLaunchKernelGGL((k_decompress<B, true>), dim3(grid), dim3(kThreads), 0, st, codes, alpha,
                        scale, nb, inv_sqrt_b, out);
@@ -437,9 +559,18 @@ tfp8_status launch_reduce(const uint8_t *codes, const float *alpha, const float 
                           float *alpha_out, float *scale_out, hipStream_t st) {
   const float TB = target * (float)B;
   constexpr int BPW = 64 / (B / 16);
-  const unsigned grid = grid_for((nb + BPW - 1) / BPW);
-  hipLaunchKernelGGL((k_reduce<B>), dim3(grid), dim3(kThreads), 0, st, codes, alpha, scale, P, n,
-                     nb, TB, codes_out, alpha_out, scale_out);
+  const unsigned grid = grid_for((nb + BPW - 1) / BPW, TFP8_REDUCE_WGS_PER_CU);
+#define TFP8_LAUNCH_REDUCE(PB)                                                                 \
+  hipLaunchKernelGGL((k_reduce<B, PB>), dim3(grid), dim3(kThreads), 0, st, codes, alpha, scale, P, \
+                     n, nb, TB, codes_out, alpha_out, scale_out)
+  switch (P) {
+    case 1: TFP8_LAUNCH_REDUCE(1); break;
+    case 2: TFP8_LAUNCH_REDUCE(2); break;
+    case 4: TFP8_LAUNCH_REDUCE(4); break;
+    case 8: TFP8_LAUNCH_REDUCE(8); break;
+    default: TFP8_LAUNCH_REDUCE(0); break;
+  }
+#undef TFP8_LAUNCH_REDUCE
   return launched();
 }
 
