@@ -42,11 +42,19 @@ def log(msg):
 
 
 def kernel_source_hash() -> str:
+    """SHA-256 of the kernel sources with comments and whitespace removed, so that the counter
+    record is tied to the code it measured and not to its comments."""
+    import re
+
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "fp8_compression_tensor_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(csrc, name)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        text = re.sub(r"\s+", " ", text).strip()
+        h.update(name.encode() + b"\0" + text.encode())
     return h.hexdigest()
 
 

@@ -21,12 +21,12 @@
 //
 // Scales.  With s = max|y|/448 and y = alpha w / sqrt(B), the codes are E4M3(448 w / max|w|)
 // for every alpha (alpha cancels), so the kernel never multiplies the elements by alpha: it
-// computes c = 448 / max|w|, u = w c (the codes' pre-rounding values), and gets the energy
-// from sum(u^2) = c^2 sum(w^2) = c^2 B sum(x^2) (the rotation preserves energy), which stays
-// inside float32 range for every block.  Then
-//   alpha = clamp(c sqrt(T B^2 / sum(u^2)), 2^-126, 2^126),  s = alpha max|w| / (448 sqrt(B)).
-// Blocks whose max|w| is outside [2^-100, 2^100] (bfloat16 subnormal blocks, for one) are
-// first multiplied by an exact power of two and the exponent is carried into alpha and s.
+// computes c = 448 / max|w| and u = w c (the codes' pre-rounding values), takes the energy
+// sum(x^2) straight from the packed input, and sets
+//   alpha = clamp(sqrt(T B / sum(x^2)), 2^-126, 2^126),  s = alpha max|w| / (448 sqrt(B)).
+// Blocks whose max|w| is outside [2^-40, 2^60] (all-zero, bfloat16-subnormal, huge) go through
+// scales_exact, which first multiplies the block by an exact power of two and takes the energy
+// from sum(u^2) = c^2 B sum(x^2) (the rotation preserves energy).
 //
 // Reduce.  Sum of reconstructions z = sum_p H (s_p dec q_p) / (sqrt(B) alpha_p) = H r / sqrt(B)
 // with r = sum_p (s_p / alpha_p) dec(q_p); requantising z gives y' = alpha' r exactly, so the
