@@ -16,6 +16,7 @@ from . import build as _build
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 BF16, F32 = 0, 1
+INT8, NO_ROTATION = 1, 2  # variant flags of the *_ex oracle entry points
 
 _lib = None
 
@@ -49,6 +50,15 @@ def lib():
         L.tfp8_ref_decompress_unrounded.argtypes = [vp, vp, vp, i64, i32, vp]
         L.tfp8_ref_reduce_fp8.argtypes = [vp, vp, vp, i32, i64, i32, f32, vp, vp, vp, vp]
         L.tfp8_ref_reduce_fp8_rotated.argtypes = [vp, vp, vp, i32, i64, i32, f32, vp, vp, vp, vp]
+        L.tfp8_ref_int8_encode.argtypes = [ctypes.c_double]
+        L.tfp8_ref_int8_encode.restype = ctypes.c_uint8
+        L.tfp8_ref_int8_decode.argtypes = [ctypes.c_uint8]
+        L.tfp8_ref_int8_decode.restype = ctypes.c_double
+        L.tfp8_ref_compress_ex.argtypes = [vp, i32, i64, i32, f32, i32, vp, vp, vp, vp]
+        L.tfp8_ref_decompress_ex.argtypes = [vp, vp, vp, i64, i32, i32, vp, i32]
+        L.tfp8_ref_decompress_f64_ex.argtypes = [vp, vp, vp, i64, i32, i32, vp]
+        L.tfp8_ref_reduce_ex.argtypes = [vp, vp, vp, i32, i64, i32, f32, i32, vp, vp, vp, vp]
+        L.tfp8_ref_reduce_rotated_ex.argtypes = [vp, vp, vp, i32, i64, i32, f32, i32, vp, vp, vp, vp]
         L.tfp8_ref_set_threads.argtypes = [i32]
         L.tfp8_ref_set_threads.restype = i32
         _lib = L
@@ -89,6 +99,14 @@ def e4m3_decode_table() -> np.ndarray:
     return np.array([e4m3_decode(c) for c in range(256)], dtype=np.float64)
 
 
+def int8_encode(v: float) -> int:
+    return int(lib().tfp8_ref_int8_encode(float(v)))
+
+
+def int8_decode(c: int) -> float:
+    return float(lib().tfp8_ref_int8_decode(int(c)))
+
+
 def round_bf16(v: float) -> int:
     return int(lib().tfp8_ref_round_bf16(float(v)))
 
@@ -110,7 +128,7 @@ def hadamard_dense(v: np.ndarray) -> np.ndarray:
     return out
 
 
-def compress(x, block: int, target: float = 1.0, with_quot: bool = False):
+def compress(x, block: int, target: float = 1.0, with_quot: bool = False, flags: int = 0):
     """-> codes uint8[n], alpha f32[nb], scale f32[nb] (+ quot f64[n] if with_quot)."""
     x, dt = _input(x)
     n = x.size
@@ -119,8 +137,8 @@ def compress(x, block: int, target: float = 1.0, with_quot: bool = False):
     alpha = np.empty(nb, np.float32)
     scale = np.empty(nb, np.float32)
     quot = np.empty(n, np.float64) if with_quot else None
-    _check(lib().tfp8_ref_compress(_ptr(x), dt, n, block, target, _ptr(codes), _ptr(alpha),
-                                   _ptr(scale), _ptr(quot)))
+    _check(lib().tfp8_ref_compress_ex(_ptr(x), dt, n, block, target, flags, _ptr(codes), _ptr(alpha),
+                                      _ptr(scale), _ptr(quot)))
     return (codes, alpha, scale, quot) if with_quot else (codes, alpha, scale)
 
 
@@ -135,7 +153,7 @@ def compress_unrounded(x, block: int, target: float = 1.0):
     return t, alpha, scale
 
 
-def decompress(codes, alpha, scale, block: int, out_dtype=np.float32):
+def decompress(codes, alpha, scale, block: int, out_dtype=np.float32, flags: int = 0):
     codes = np.ascontiguousarray(codes, np.uint8).reshape(-1)
     alpha = np.ascontiguousarray(alpha, np.float32)
     scale = np.ascontiguousarray(scale, np.float32)
@@ -144,17 +162,18 @@ def decompress(codes, alpha, scale, block: int, out_dtype=np.float32):
         out, dt = np.empty(n, np.float32), F32
     else:
         out, dt = np.empty(n, np.uint16), BF16
-    _check(lib().tfp8_ref_decompress(_ptr(codes), _ptr(alpha), _ptr(scale), n, block, _ptr(out), dt))
+    _check(lib().tfp8_ref_decompress_ex(_ptr(codes), _ptr(alpha), _ptr(scale), n, block, flags,
+                                        _ptr(out), dt))
     return out
 
 
-def decompress_f64(codes, alpha, scale, block: int):
+def decompress_f64(codes, alpha, scale, block: int, flags: int = 0):
     codes = np.ascontiguousarray(codes, np.uint8).reshape(-1)
     alpha = np.ascontiguousarray(alpha, np.float32)
     scale = np.ascontiguousarray(scale, np.float32)
     out = np.empty(codes.size, np.float64)
-    _check(lib().tfp8_ref_decompress_f64(_ptr(codes), _ptr(alpha), _ptr(scale), codes.size, block,
-                                         _ptr(out)))
+    _check(lib().tfp8_ref_decompress_f64_ex(_ptr(codes), _ptr(alpha), _ptr(scale), codes.size,
+                                            block, flags, _ptr(out)))
     return out
 
 
@@ -168,7 +187,7 @@ def decompress_unrounded(t, alpha, scale, block: int):
     return out
 
 
-def _reduce(fn, codes, alpha, scale, block, target, with_quot):
+def _reduce(fn, codes, alpha, scale, block, target, with_quot, flags):
     codes = np.ascontiguousarray(codes, np.uint8)
     P = codes.shape[0]
     codes = codes.reshape(P, -1)
@@ -179,19 +198,22 @@ def _reduce(fn, codes, alpha, scale, block, target, with_quot):
     ao = np.empty(n // block, np.float32)
     so = np.empty(n // block, np.float32)
     quot = np.empty(n, np.float64) if with_quot else None
-    _check(fn(_ptr(codes), _ptr(alpha), _ptr(scale), P, n, block, target, _ptr(qo), _ptr(ao),
+    _check(fn(_ptr(codes), _ptr(alpha), _ptr(scale), P, n, block, target, flags, _ptr(qo), _ptr(ao),
               _ptr(so), _ptr(quot)))
     return (qo, ao, so, quot) if with_quot else (qo, ao, so)
 
 
-def reduce_fp8(codes, alpha, scale, block: int, target: float = 1.0, with_quot: bool = False):
+def reduce_fp8(codes, alpha, scale, block: int, target: float = 1.0, with_quot: bool = False,
+               flags: int = 0):
     """codes [P, n], alpha/scale [P, nb] -> codes [n], alpha [nb], scale [nb] (by definition)."""
-    return _reduce(lib().tfp8_ref_reduce_fp8, codes, alpha, scale, block, target, with_quot)
+    return _reduce(lib().tfp8_ref_reduce_ex, codes, alpha, scale, block, target, with_quot, flags)
 
 
-def reduce_fp8_rotated(codes, alpha, scale, block: int, target: float = 1.0, with_quot: bool = False):
+def reduce_fp8_rotated(codes, alpha, scale, block: int, target: float = 1.0, with_quot: bool = False,
+                       flags: int = 0):
     """Same result by the rotated-domain route (no Hadamard)."""
-    return _reduce(lib().tfp8_ref_reduce_fp8_rotated, codes, alpha, scale, block, target, with_quot)
+    return _reduce(lib().tfp8_ref_reduce_rotated_ex, codes, alpha, scale, block, target, with_quot,
+                   flags)
 
 
 def raw_status(name: str, *args) -> int:

@@ -18,7 +18,7 @@
  *     [2^-126, 2^126] so that alpha and 1/alpha are normal fp32 numbers;
  *   - the rotation is the Sylvester Hadamard in natural order, normalised by 1/sqrt(block),
  *     with no random signs;
- *   - the post-scale is s = max|y| / 448 (448 = largest E4M3FN value);
+ *   - the post-scale is s = max|y| / 448 (448 = largest E4M3FN value; 127 for the INT8 codes);
  *   - codes are OCP E4M3FN, round-to-nearest-even, saturating, sign kept on zero;
  *   - an all-zero block (tested on max|v|, not on m2) stores alpha = 1, s = 0, codes 0x00 and
  *     reconstructs to +0;
@@ -96,6 +96,29 @@ uint16_t tfp8_ref_round_bf16(double v) {
   return sign | (uint16_t)(u >> 16);
 }
 
+/* INT8 code for the fallback the TACO page keeps for hardware without FP8 (section 5): a
+   two's complement byte, round to nearest even, saturating at +-127 (symmetric, so -128 is
+   never produced; it still decodes to -128). */
+uint8_t tfp8_ref_int8_encode(double v) {
+  double k = nearbyint(v);
+  if (k > 127.0) k = 127.0;
+  if (k < -127.0) k = -127.0;
+  return (uint8_t)(int8_t)k;
+}
+
+double tfp8_ref_int8_decode(uint8_t code) { return (double)(int8_t)code; }
+
+static double code_value(uint8_t code, int flags) {
+  return (flags & TFP8_REF_INT8) ? tfp8_ref_int8_decode(code) : tfp8_ref_e4m3_decode(code);
+}
+
+static uint8_t code_encode(double t, int flags) {
+  return (flags & TFP8_REF_INT8) ? tfp8_ref_int8_encode(t) : tfp8_ref_e4m3_encode(t);
+}
+
+/* Q_max: the largest code value the post-scale maps the block's peak to. */
+static double code_qmax(int flags) { return (flags & TFP8_REF_INT8) ? 127.0 : 448.0; }
+
 /* ---------------------------------------------------------------------------------------- */
 /* Hadamard ([TACO] section 2.B.1: an orthogonal Hadamard rotation).                          */
 
@@ -153,8 +176,8 @@ static double load_elem(const void *x, int dtype, int64_t i) {
 /* ASH + DS on one block of float64 values v[0..B) ([TACO] sections 2.B.1 and 2.B.2).        */
 /* If `quot` is not NULL it receives y_i / s; if `codes` is NULL the rounding is skipped.     */
 
-static void compress_block(const double *v, int B, double T, uint8_t *codes, float *alpha_out,
-                           float *scale_out, double *quot) {
+static void compress_block(const double *v, int B, double T, int flags, uint8_t *codes,
+                           float *alpha_out, float *scale_out, double *quot) {
   double ax = 0.0;
   for (int i = 0; i < B; ++i) ax = fmax(ax, fabs(v[i]));
   if (ax == 0.0) { /* all-zero block: nothing to scale */
@@ -174,20 +197,22 @@ static void compress_block(const double *v, int B, double T, uint8_t *codes, flo
   double a = sqrt(T / m2);
   a = fmin(fmax(a, 0x1p-126), 0x1p126);
   float alpha = (float)a;
-  /* orthogonal Hadamard rotation of the prescaled block */
+  /* orthogonal Hadamard rotation of the prescaled block (left out for the ablation variant) */
   double *y = (double *)malloc(sizeof(double) * (size_t)B);
   for (int i = 0; i < B; ++i) y[i] = (double)alpha * v[i];
-  tfp8_ref_fwht(y, B);
-  double rootB = sqrt((double)B);
-  for (int i = 0; i < B; ++i) y[i] = y[i] / rootB;
-  /* post-scale: largest rotated magnitude lands on Q_max = 448 */
+  if (!(flags & TFP8_REF_NO_ROTATION)) {
+    tfp8_ref_fwht(y, B);
+    double rootB = sqrt((double)B);
+    for (int i = 0; i < B; ++i) y[i] = y[i] / rootB;
+  }
+  /* post-scale: largest rotated magnitude lands on Q_max (448 for E4M3) */
   double my = 0.0;
   for (int i = 0; i < B; ++i) my = fmax(my, fabs(y[i]));
-  float s = (float)(my / 448.0);
+  float s = (float)(my / code_qmax(flags));
   for (int i = 0; i < B; ++i) {
     double t = y[i] / (double)s;
     if (quot) quot[i] = t;
-    if (codes) codes[i] = tfp8_ref_e4m3_encode(t);
+    if (codes) codes[i] = code_encode(t, flags);
   }
   *alpha_out = alpha;
   *scale_out = s;
@@ -197,25 +222,33 @@ static void compress_block(const double *v, int B, double T, uint8_t *codes, flo
 /* Inverse of one block from the code values c_j = dec(q_j) (or unrounded quotients):
    x_i = (1/sqrt(B)) * sum_j H[i][j] (s * c_j) / alpha ([TACO] section 2.B.2, reconstruction
    with both scales; H is symmetric and (H/sqrt(B))^2 = I). */
-static void decompress_block(const double *cval, float alpha, float scale, int B, double *out) {
+static void decompress_block(const double *cval, float alpha, float scale, int B, int flags,
+                             double *out) {
   if (scale == 0.0f) {
     for (int i = 0; i < B; ++i) out[i] = 0.0;
     return;
   }
   for (int i = 0; i < B; ++i) out[i] = (double)scale * cval[i];
-  tfp8_ref_fwht(out, B);
-  double rootB = sqrt((double)B);
-  for (int i = 0; i < B; ++i) out[i] = out[i] / rootB / (double)alpha;
+  if (!(flags & TFP8_REF_NO_ROTATION)) {
+    tfp8_ref_fwht(out, B);
+    double rootB = sqrt((double)B);
+    for (int i = 0; i < B; ++i) out[i] = out[i] / rootB;
+  }
+  for (int i = 0; i < B; ++i) out[i] = out[i] / (double)alpha;
 }
 
 /* ---------------------------------------------------------------------------------------- */
 
-int tfp8_ref_compress(const void *x, int x_dtype, int64_t n, int block, float target,
-                      uint8_t *codes, float *alpha, float *scale, double *quot) {
+static int check_flags(int flags) {
+  return (flags & ~(TFP8_REF_INT8 | TFP8_REF_NO_ROTATION)) ? TFP8_REF_E_ARG : TFP8_REF_OK;
+}
+
+int tfp8_ref_compress_ex(const void *x, int x_dtype, int64_t n, int block, float target, int flags,
+                         uint8_t *codes, float *alpha, float *scale, double *quot) {
   int st = check_common(n, block);
   if (st) return st;
   if (x_dtype != TFP8_REF_BF16 && x_dtype != TFP8_REF_F32) return TFP8_REF_E_DTYPE;
-  if ((st = check_target(target))) return st;
+  if ((st = check_target(target)) || (st = check_flags(flags))) return st;
   if (n == 0) return TFP8_REF_OK;
   if (!x || !codes || !alpha || !scale) return TFP8_REF_E_NULL;
   int64_t nb = n / block;
@@ -223,11 +256,16 @@ int tfp8_ref_compress(const void *x, int x_dtype, int64_t n, int block, float ta
   for (int64_t k = 0; k < nb; ++k) {
     double *v = (double *)malloc(sizeof(double) * (size_t)block);
     for (int i = 0; i < block; ++i) v[i] = load_elem(x, x_dtype, k * block + i);
-    compress_block(v, block, (double)target, codes + k * block, alpha + k, scale + k,
+    compress_block(v, block, (double)target, flags, codes + k * block, alpha + k, scale + k,
                    quot ? quot + k * block : NULL);
     free(v);
   }
   return TFP8_REF_OK;
+}
+
+int tfp8_ref_compress(const void *x, int x_dtype, int64_t n, int block, float target,
+                      uint8_t *codes, float *alpha, float *scale, double *quot) {
+  return tfp8_ref_compress_ex(x, x_dtype, n, block, target, 0, codes, alpha, scale, quot);
 }
 
 int tfp8_ref_compress_unrounded(const void *x, int x_dtype, int64_t n, int block, float target,
@@ -243,33 +281,38 @@ int tfp8_ref_compress_unrounded(const void *x, int x_dtype, int64_t n, int block
   for (int64_t k = 0; k < nb; ++k) {
     double *v = (double *)malloc(sizeof(double) * (size_t)block);
     for (int i = 0; i < block; ++i) v[i] = load_elem(x, x_dtype, k * block + i);
-    compress_block(v, block, (double)target, NULL, alpha + k, scale + k, t + k * block);
+    compress_block(v, block, (double)target, 0, NULL, alpha + k, scale + k, t + k * block);
     free(v);
   }
   return TFP8_REF_OK;
 }
 
-int tfp8_ref_decompress_f64(const uint8_t *codes, const float *alpha, const float *scale, int64_t n,
-                            int block, double *out) {
+int tfp8_ref_decompress_f64_ex(const uint8_t *codes, const float *alpha, const float *scale,
+                               int64_t n, int block, int flags, double *out) {
   int st = check_common(n, block);
-  if (st) return st;
+  if (st || (st = check_flags(flags))) return st;
   if (n == 0) return TFP8_REF_OK;
   if (!codes || !alpha || !scale || !out) return TFP8_REF_E_NULL;
   int64_t nb = n / block;
 #pragma omp parallel for num_threads(g_threads) schedule(static)
   for (int64_t k = 0; k < nb; ++k) {
     double *c = (double *)malloc(sizeof(double) * (size_t)block);
-    for (int i = 0; i < block; ++i) c[i] = tfp8_ref_e4m3_decode(codes[k * block + i]);
-    decompress_block(c, alpha[k], scale[k], block, out + k * block);
+    for (int i = 0; i < block; ++i) c[i] = code_value(codes[k * block + i], flags);
+    decompress_block(c, alpha[k], scale[k], block, flags, out + k * block);
     free(c);
   }
   return TFP8_REF_OK;
 }
 
-int tfp8_ref_decompress(const uint8_t *codes, const float *alpha, const float *scale, int64_t n,
-                        int block, void *out, int out_dtype) {
+int tfp8_ref_decompress_f64(const uint8_t *codes, const float *alpha, const float *scale, int64_t n,
+                            int block, double *out) {
+  return tfp8_ref_decompress_f64_ex(codes, alpha, scale, n, block, 0, out);
+}
+
+int tfp8_ref_decompress_ex(const uint8_t *codes, const float *alpha, const float *scale, int64_t n,
+                           int block, int flags, void *out, int out_dtype) {
   int st = check_common(n, block);
-  if (st) return st;
+  if (st || (st = check_flags(flags))) return st;
   if (out_dtype != TFP8_REF_BF16 && out_dtype != TFP8_REF_F32) return TFP8_REF_E_DTYPE;
   if (n == 0) return TFP8_REF_OK;
   if (!codes || !alpha || !scale || !out) return TFP8_REF_E_NULL;
@@ -278,8 +321,8 @@ int tfp8_ref_decompress(const uint8_t *codes, const float *alpha, const float *s
   for (int64_t k = 0; k < nb; ++k) {
     double *c = (double *)malloc(sizeof(double) * (size_t)block);
     double *r = (double *)malloc(sizeof(double) * (size_t)block);
-    for (int i = 0; i < block; ++i) c[i] = tfp8_ref_e4m3_decode(codes[k * block + i]);
-    decompress_block(c, alpha[k], scale[k], block, r);
+    for (int i = 0; i < block; ++i) c[i] = code_value(codes[k * block + i], flags);
+    decompress_block(c, alpha[k], scale[k], block, flags, r);
     for (int i = 0; i < block; ++i) {
       if (out_dtype == TFP8_REF_F32)
         ((float *)out)[k * block + i] = (float)r[i];
@@ -292,6 +335,11 @@ int tfp8_ref_decompress(const uint8_t *codes, const float *alpha, const float *s
   return TFP8_REF_OK;
 }
 
+int tfp8_ref_decompress(const uint8_t *codes, const float *alpha, const float *scale, int64_t n,
+                        int block, void *out, int out_dtype) {
+  return tfp8_ref_decompress_ex(codes, alpha, scale, n, block, 0, out, out_dtype);
+}
+
 int tfp8_ref_decompress_unrounded(const double *t, const float *alpha, const float *scale,
                                   int64_t n, int block, double *out) {
   int st = check_common(n, block);
@@ -300,7 +348,7 @@ int tfp8_ref_decompress_unrounded(const double *t, const float *alpha, const flo
   if (!t || !alpha || !scale || !out) return TFP8_REF_E_NULL;
   int64_t nb = n / block;
 #pragma omp parallel for num_threads(g_threads) schedule(static)
-  for (int64_t k = 0; k < nb; ++k) decompress_block(t + k * block, alpha[k], scale[k], block, out + k * block);
+  for (int64_t k = 0; k < nb; ++k) decompress_block(t + k * block, alpha[k], scale[k], block, 0, out + k * block);
   return TFP8_REF_OK;
 }
 
@@ -310,21 +358,22 @@ int tfp8_ref_decompress_unrounded(const double *t, const float *alpha, const flo
 /* AllGather).  The oracle sums in float64.                                                  */
 
 static int check_reduce(const uint8_t *codes, const float *alpha, const float *scale, int P,
-                        int64_t n, int block, float target, uint8_t *codes_out, float *alpha_out,
-                        float *scale_out) {
+                        int64_t n, int block, float target, int flags, uint8_t *codes_out,
+                        float *alpha_out, float *scale_out) {
   int st = check_common(n, block);
   if (st) return st;
   if (P < 1) return TFP8_REF_E_ARG;
-  if ((st = check_target(target))) return st;
+  if ((st = check_target(target)) || (st = check_flags(flags))) return st;
   if (n == 0) return TFP8_REF_OK;
   if (!codes || !alpha || !scale || !codes_out || !alpha_out || !scale_out) return TFP8_REF_E_NULL;
   return TFP8_REF_OK;
 }
 
-int tfp8_ref_reduce_fp8(const uint8_t *codes, const float *alpha, const float *scale, int P,
-                        int64_t n, int block, float target, uint8_t *codes_out, float *alpha_out,
-                        float *scale_out, double *quot) {
-  int st = check_reduce(codes, alpha, scale, P, n, block, target, codes_out, alpha_out, scale_out);
+int tfp8_ref_reduce_ex(const uint8_t *codes, const float *alpha, const float *scale, int P,
+                       int64_t n, int block, float target, int flags, uint8_t *codes_out,
+                       float *alpha_out, float *scale_out, double *quot) {
+  int st = check_reduce(codes, alpha, scale, P, n, block, target, flags, codes_out, alpha_out,
+                        scale_out);
   if (st || n == 0) return st;
   int64_t nb = n / block;
 #pragma omp parallel for num_threads(g_threads) schedule(static)
@@ -334,12 +383,12 @@ int tfp8_ref_reduce_fp8(const uint8_t *codes, const float *alpha, const float *s
     double *xh = (double *)malloc(sizeof(double) * (size_t)block);
     for (int p = 0; p < P; ++p) {
       const uint8_t *q = codes + (int64_t)p * n + k * block;
-      for (int i = 0; i < block; ++i) c[i] = tfp8_ref_e4m3_decode(q[i]);
-      decompress_block(c, alpha[(int64_t)p * nb + k], scale[(int64_t)p * nb + k], block, xh);
+      for (int i = 0; i < block; ++i) c[i] = code_value(q[i], flags);
+      decompress_block(c, alpha[(int64_t)p * nb + k], scale[(int64_t)p * nb + k], block, flags, xh);
       for (int i = 0; i < block; ++i) z[i] += xh[i];
     }
-    compress_block(z, block, (double)target, codes_out + k * block, alpha_out + k, scale_out + k,
-                   quot ? quot + k * block : NULL);
+    compress_block(z, block, (double)target, flags, codes_out + k * block, alpha_out + k,
+                   scale_out + k, quot ? quot + k * block : NULL);
     free(z);
     free(c);
     free(xh);
@@ -347,26 +396,36 @@ int tfp8_ref_reduce_fp8(const uint8_t *codes, const float *alpha, const float *s
   return TFP8_REF_OK;
 }
 
-int tfp8_ref_reduce_fp8_rotated(const uint8_t *codes, const float *alpha, const float *scale,
-                                int P, int64_t n, int block, float target, uint8_t *codes_out,
-                                float *alpha_out, float *scale_out, double *quot) {
-  int st = check_reduce(codes, alpha, scale, P, n, block, target, codes_out, alpha_out, scale_out);
+int tfp8_ref_reduce_fp8(const uint8_t *codes, const float *alpha, const float *scale, int P,
+                        int64_t n, int block, float target, uint8_t *codes_out, float *alpha_out,
+                        float *scale_out, double *quot) {
+  return tfp8_ref_reduce_ex(codes, alpha, scale, P, n, block, target, 0, codes_out, alpha_out,
+                            scale_out, quot);
+}
+
+int tfp8_ref_reduce_rotated_ex(const uint8_t *codes, const float *alpha, const float *scale, int P,
+                               int64_t n, int block, float target, int flags, uint8_t *codes_out,
+                               float *alpha_out, float *scale_out, double *quot) {
+  int st = check_reduce(codes, alpha, scale, P, n, block, target, flags, codes_out, alpha_out,
+                        scale_out);
   if (st || n == 0) return st;
   int64_t nb = n / block;
   double T = (double)target;
+  double Q = code_qmax(flags);
 #pragma omp parallel for num_threads(g_threads) schedule(static)
   for (int64_t k = 0; k < nb; ++k) {
     /* The sum z = sum_p H(s_p dec q_p)/(sqrt(B) alpha_p) equals H r / sqrt(B) with
        r = sum_p (s_p/alpha_p) dec(q_p).  Because H/sqrt(B) is orthogonal and its own inverse:
        mean(z^2) = mean(r^2), z = 0 exactly when r = 0, and the rotated prescaled sum is
-       y = (1/sqrt(B)) H (alpha z) = alpha r.  So no Hadamard is applied at all. */
+       y = (1/sqrt(B)) H (alpha z) = alpha r.  So no Hadamard is applied at all.  (Without the
+       rotation, z = r directly and the same holds.) */
     double *r = (double *)calloc((size_t)block, sizeof(double));
     for (int p = 0; p < P; ++p) {
       float s = scale[(int64_t)p * nb + k];
       if (s == 0.0f) continue;
       double g = (double)s / (double)alpha[(int64_t)p * nb + k];
       const uint8_t *q = codes + (int64_t)p * n + k * block;
-      for (int i = 0; i < block; ++i) r[i] += g * tfp8_ref_e4m3_decode(q[i]);
+      for (int i = 0; i < block; ++i) r[i] += g * code_value(q[i], flags);
     }
     double ar = 0.0, sumsq = 0.0;
     for (int i = 0; i < block; ++i) {
@@ -387,15 +446,22 @@ int tfp8_ref_reduce_fp8_rotated(const uint8_t *codes, const float *alpha, const 
     double a = sqrt(T / (sumsq / block));
     a = fmin(fmax(a, 0x1p-126), 0x1p126);
     float alpha2 = (float)a;
-    float s2 = (float)((double)alpha2 * ar / 448.0);
+    float s2 = (float)((double)alpha2 * ar / Q);
     for (int i = 0; i < block; ++i) {
       double t = (double)alpha2 * r[i] / (double)s2;
       if (quot) quot[k * block + i] = t;
-      qo[i] = tfp8_ref_e4m3_encode(t);
+      qo[i] = code_encode(t, flags);
     }
     alpha_out[k] = alpha2;
     scale_out[k] = s2;
     free(r);
   }
   return TFP8_REF_OK;
+}
+
+int tfp8_ref_reduce_fp8_rotated(const uint8_t *codes, const float *alpha, const float *scale,
+                                int P, int64_t n, int block, float target, uint8_t *codes_out,
+                                float *alpha_out, float *scale_out, double *quot) {
+  return tfp8_ref_reduce_rotated_ex(codes, alpha, scale, P, n, block, target, 0, codes_out,
+                                    alpha_out, scale_out, quot);
 }

@@ -36,6 +36,13 @@ enum {
 
 enum { TFP8_REF_BF16 = 0, TFP8_REF_F32 = 1 };
 
+/* Variant flags of the *_ex functions (0 = the method as defined on the TACO page):
+ *   TFP8_REF_INT8         codes are int8 (two's complement, round to nearest even, saturating
+ *                         at +-127) with Q_max = 127: the INT8 fallback the TACO page mentions for
+ *                         hardware without FP8 (section 5);
+ *   TFP8_REF_NO_ROTATION  the Hadamard rotation is left out (identity), for ablations. */
+enum { TFP8_REF_INT8 = 1, TFP8_REF_NO_ROTATION = 2 };
+
 /* E4M3FN (max 448, no infinities, 0x7F/0xFF NaN): encode v with round-to-nearest-even,
  * saturating at +-448, sign taken from v (so a tiny negative gives 0x80). */
 uint8_t tfp8_ref_e4m3_encode(double v);
@@ -84,6 +91,22 @@ int tfp8_ref_reduce_fp8(const uint8_t *codes, const float *alpha, const float *s
 int tfp8_ref_reduce_fp8_rotated(const uint8_t *codes, const float *alpha, const float *scale,
                                 int P, int64_t n, int block, float target, uint8_t *codes_out,
                                 float *alpha_out, float *scale_out, double *quot);
+
+/* Variants selected by `flags` (TFP8_REF_INT8, TFP8_REF_NO_ROTATION); same arguments otherwise. */
+uint8_t tfp8_ref_int8_encode(double v);
+double tfp8_ref_int8_decode(uint8_t code);
+int tfp8_ref_compress_ex(const void *x, int x_dtype, int64_t n, int block, float target, int flags,
+                         uint8_t *codes, float *alpha, float *scale, double *quot);
+int tfp8_ref_decompress_ex(const uint8_t *codes, const float *alpha, const float *scale, int64_t n,
+                           int block, int flags, void *out, int out_dtype);
+int tfp8_ref_decompress_f64_ex(const uint8_t *codes, const float *alpha, const float *scale,
+                               int64_t n, int block, int flags, double *out);
+int tfp8_ref_reduce_ex(const uint8_t *codes, const float *alpha, const float *scale, int P,
+                       int64_t n, int block, float target, int flags, uint8_t *codes_out,
+                       float *alpha_out, float *scale_out, double *quot);
+int tfp8_ref_reduce_rotated_ex(const uint8_t *codes, const float *alpha, const float *scale, int P,
+                               int64_t n, int block, float target, int flags, uint8_t *codes_out,
+                               float *alpha_out, float *scale_out, double *quot);
 
 /* Threads used by the block loops (OpenMP); returns the count in effect. */
 int tfp8_ref_set_threads(int threads);

@@ -24,7 +24,7 @@ MUTANTS = [
     ("butterfly sign", "v[j + h] = a - b;", "v[j + h] = b - a;", 0),
     ("Hadamard entry or", "(i & j)", "(i | j)", 0),
     ("no 1/sqrt(B)", "for (int i = 0; i < B; ++i) y[i] = y[i] / rootB;", "", 0),
-    ("Qmax 240", "my / 448.0", "my / 240.0", 0),
+    ("Qmax 240", "? 127.0 : 448.0", "? 127.0 : 240.0", 0),
     ("encode half-up", "double k = nearbyint(ldexp(a, 3 - E));",
      "double k = floor(ldexp(a, 3 - E) + 0.5);", 0),
     ("encode subnormal half-up", "nearbyint(a * 512.0)", "floor(a * 512.0 + 0.5)", 0),
@@ -36,10 +36,10 @@ MUTANTS = [
     ("bf16 round half-up", "double r = nearbyint(a / step) * step;",
      "double r = floor(a / step + 0.5) * step;", 0),
     ("zero block alpha 0", "*alpha_out = 1.0f;", "*alpha_out = 0.0f;", 0),
-    ("decompress no 1/alpha", "out[i] = out[i] / rootB / (double)alpha;",
-     "out[i] = out[i] / rootB;", 0),
-    ("decompress times alpha", "out[i] = out[i] / rootB / (double)alpha;",
-     "out[i] = out[i] / rootB * (double)alpha;", 0),
+    ("decompress no 1/alpha", "for (int i = 0; i < B; ++i) out[i] = out[i] / (double)alpha;",
+     "", 0),
+    ("decompress times alpha", "out[i] = out[i] / (double)alpha;",
+     "out[i] = out[i] * (double)alpha;", 0),
     ("decompress no rotation", "  tfp8_ref_fwht(out, B);\n", "\n", 0),
     ("decompress scale dropped", "out[i] = (double)scale * cval[i];", "out[i] = cval[i];", 0),
     ("reduce drops last", "for (int p = 0; p < P; ++p) {\n      const uint8_t *q",
@@ -48,7 +48,18 @@ MUTANTS = [
      "decompress_block(c, alpha[k], scale[k]", 0),
     ("rotated reduce s/alpha swapped", "double g = (double)s / (double)alpha[(int64_t)p * nb + k];",
      "double g = (double)alpha[(int64_t)p * nb + k] / (double)s;", 0),
-    ("rotated reduce no /448", "(double)alpha2 * ar / 448.0", "(double)alpha2 * ar", 0),
+    ("rotated reduce no /Qmax", "double Q = code_qmax(flags);", "double Q = 1.0;", 0),
+    ("INT8 Qmax 128", "? 127.0 : 448.0", "? 128.0 : 448.0", 0),
+    ("INT8 decode unsigned", "return (double)(int8_t)code;", "return (double)code;", 0),
+    ("INT8 encode half-up", "double k = nearbyint(v);", "double k = floor(v + 0.5);", 0),
+    ("INT8 values decoded as E4M3",
+     "return (flags & TFP8_REF_INT8) ? tfp8_ref_int8_decode(code) : tfp8_ref_e4m3_decode(code);",
+     "return tfp8_ref_e4m3_decode(code);", 0),
+    ("compress ignores no-rotation", "if (!(flags & TFP8_REF_NO_ROTATION)) {\n    tfp8_ref_fwht(y, B);",
+     "if (1) {\n    tfp8_ref_fwht(y, B);", 0),
+    ("decompress ignores no-rotation",
+     "if (!(flags & TFP8_REF_NO_ROTATION)) {\n    tfp8_ref_fwht(out, B);",
+     "if (1) {\n    tfp8_ref_fwht(out, B);", 0),
 ]
 
 
@@ -77,7 +88,8 @@ def _run_mutant(case, tmpdir):
     env = dict(os.environ, TFP8_ORACLE_LIB=lib, OMP_NUM_THREADS="2")
     cmd = [sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
            os.path.join(ROOT, "tests", "test_oracle_codec.py"),
-           os.path.join(ROOT, "tests", "test_oracle_method.py")]
+           os.path.join(ROOT, "tests", "test_oracle_method.py"),
+           os.path.join(ROOT, "tests", "test_oracle_variants.py")]
     r = subprocess.run(cmd, cwd=ROOT, env=env, capture_output=True, text=True, timeout=900)
     return name, r.returncode, r.stdout[-1500:]
 
