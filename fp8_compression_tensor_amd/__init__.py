@@ -20,10 +20,12 @@ import torch
 __all__ = [
     "compress", "decompress", "reduce_fp8", "compress_raw", "decompress_raw", "reduce_fp8_raw",
     "status_string", "lib", "LIB_PATH", "TFP8Error", "BF16", "F32", "SUPPORTED_BLOCKS",
+    "FLAG_INT8", "FLAG_NO_ROTATION",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtfp8.so")
 BF16, F32 = 0, 1
+FLAG_INT8, FLAG_NO_ROTATION = 1, 2  # variant flags of the *_ex entry points (include/tfp8.h)
 SUPPORTED_BLOCKS = (64, 128, 256, 512)
 
 _STATUS = {0: "TFP8_OK", -1: "TFP8_E_NULL", -2: "TFP8_E_SIZE", -3: "TFP8_E_BLOCK",
@@ -55,6 +57,13 @@ def lib() -> ctypes.CDLL:
         L.tfp8_decompress.restype = i32
         L.tfp8_reduce_fp8.argtypes = [vp, vp, vp, i32, i64, i32, f32, vp, vp, vp, vp]
         L.tfp8_reduce_fp8.restype = i32
+        u32 = ctypes.c_uint32
+        L.tfp8_compress_ex.argtypes = [vp, i32, i64, i32, f32, u32, vp, vp, vp, vp]
+        L.tfp8_compress_ex.restype = i32
+        L.tfp8_decompress_ex.argtypes = [vp, vp, vp, i64, i32, u32, vp, i32, vp]
+        L.tfp8_decompress_ex.restype = i32
+        L.tfp8_reduce_ex.argtypes = [vp, vp, vp, i32, i64, i32, f32, u32, vp, vp, vp, vp]
+        L.tfp8_reduce_ex.restype = i32
         L.tfp8_status_string.argtypes = [i32]
         L.tfp8_status_string.restype = ctypes.c_char_p
         L.tfp8_version.argtypes = []
@@ -76,20 +85,29 @@ def _check(status: int):
 # Pointers are integers (device addresses); `stream` is a raw hipStream_t (0 = default stream).
 
 def compress_raw(x_ptr: int, x_dtype: int, n: int, block: int, target: float, codes_ptr: int,
-                 alpha_ptr: int, scale_ptr: int, stream: int = 0) -> int:
+                 alpha_ptr: int, scale_ptr: int, stream: int = 0, flags: int = 0) -> int:
+    if flags:
+        return lib().tfp8_compress_ex(x_ptr, x_dtype, n, block, target, flags, codes_ptr,
+                                      alpha_ptr, scale_ptr, stream)
     return lib().tfp8_compress(x_ptr, x_dtype, n, block, target, codes_ptr, alpha_ptr,
                                scale_ptr, stream)
 
 
 def decompress_raw(codes_ptr: int, alpha_ptr: int, scale_ptr: int, n: int, block: int,
-                   out_ptr: int, out_dtype: int, stream: int = 0) -> int:
+                   out_ptr: int, out_dtype: int, stream: int = 0, flags: int = 0) -> int:
+    if flags:
+        return lib().tfp8_decompress_ex(codes_ptr, alpha_ptr, scale_ptr, n, block, flags, out_ptr,
+                                        out_dtype, stream)
     return lib().tfp8_decompress(codes_ptr, alpha_ptr, scale_ptr, n, block, out_ptr, out_dtype,
                                  stream)
 
 
 def reduce_fp8_raw(codes_ptr: int, alpha_ptr: int, scale_ptr: int, P: int, n: int, block: int,
                    target: float, codes_out_ptr: int, alpha_out_ptr: int, scale_out_ptr: int,
-                   stream: int = 0) -> int:
+                   stream: int = 0, flags: int = 0) -> int:
+    if flags:
+        return lib().tfp8_reduce_ex(codes_ptr, alpha_ptr, scale_ptr, P, n, block, target, flags,
+                                    codes_out_ptr, alpha_out_ptr, scale_out_ptr, stream)
     return lib().tfp8_reduce_fp8(codes_ptr, alpha_ptr, scale_ptr, P, n, block, target,
                                  codes_out_ptr, alpha_out_ptr, scale_out_ptr, stream)
 
@@ -108,7 +126,7 @@ def _need_gpu(*ts):
             raise ValueError("tfp8 needs contiguous tensors")
 
 
-def compress(x: torch.Tensor, block: int = 128, target: float = 1.0, out=None):
+def compress(x: torch.Tensor, block: int = 128, target: float = 1.0, out=None, flags: int = 0):
     """x (bfloat16 or float32, any shape, numel % block == 0) ->
     (codes uint8 of x's shape, alpha float32 [numel/block], scale float32 [numel/block])."""
     _need_gpu(x)
@@ -127,12 +145,12 @@ def compress(x: torch.Tensor, block: int = 128, target: float = 1.0, out=None):
     else:
         codes, alpha, scale = out
     _check(compress_raw(x.data_ptr(), dt, n, block, float(target), codes.data_ptr(),
-                        alpha.data_ptr(), scale.data_ptr(), _stream(x)))
+                        alpha.data_ptr(), scale.data_ptr(), _stream(x), flags))
     return codes, alpha, scale
 
 
 def decompress(codes: torch.Tensor, alpha: torch.Tensor, scale: torch.Tensor, block: int = 128,
-               dtype: torch.dtype = torch.float32, out=None):
+               dtype: torch.dtype = torch.float32, out=None, flags: int = 0):
     """Reconstruct a float32 or bfloat16 tensor of codes' shape."""
     _need_gpu(codes, alpha, scale)
     if dtype == torch.float32:
@@ -144,12 +162,12 @@ def decompress(codes: torch.Tensor, alpha: torch.Tensor, scale: torch.Tensor, bl
     if out is None:
         out = torch.empty(codes.shape, dtype=dtype, device=codes.device)
     _check(decompress_raw(codes.data_ptr(), alpha.data_ptr(), scale.data_ptr(), codes.numel(),
-                          block, out.data_ptr(), dt, _stream(codes)))
+                          block, out.data_ptr(), dt, _stream(codes), flags))
     return out
 
 
 def reduce_fp8(codes: torch.Tensor, alpha: torch.Tensor, scale: torch.Tensor, block: int = 128,
-               target: float = 1.0, out=None):
+               target: float = 1.0, out=None, flags: int = 0):
     """codes [P, ...], alpha and scale [P, nb] -> (codes [...], alpha [nb], scale [nb])."""
     _need_gpu(codes, alpha, scale)
     P = codes.shape[0]
@@ -163,5 +181,5 @@ def reduce_fp8(codes: torch.Tensor, alpha: torch.Tensor, scale: torch.Tensor, bl
         codes_out, alpha_out, scale_out = out
     _check(reduce_fp8_raw(codes.data_ptr(), alpha.data_ptr(), scale.data_ptr(), P, n, block,
                           float(target), codes_out.data_ptr(), alpha_out.data_ptr(),
-                          scale_out.data_ptr(), _stream(codes)))
+                          scale_out.data_ptr(), _stream(codes), flags))
     return codes_out, alpha_out, scale_out

@@ -189,6 +189,24 @@ __device__ __forceinline__ void unpack_fp8x4(uint32_t w, float &a, float &b, flo
   d = hi[1];
 }
 
+// INT8 codes.  fma(w, c, 1.5 * 2^23) rounds w * c to the nearest integer k (ties to even) in
+// a single rounding, for |w c| < 2^22, and leaves k in the low bits of the result: the low byte
+// of its bit pattern is k as a two's complement byte.
+constexpr float kInt8Magic = 12582912.0f;  // 1.5 * 2^23
+
+__device__ __forceinline__ uint32_t pack_int8x4_rounded(float a, float b, float c, float d) {
+  return (__float_as_uint(a) & 0xFFu) | ((__float_as_uint(b) & 0xFFu) << 8) |
+         ((__float_as_uint(c) & 0xFFu) << 16) | (__float_as_uint(d) << 24);
+}
+
+// Four INT8 codes of one dword -> four floats (exact).
+__device__ __forceinline__ void unpack_int8x4(uint32_t w, float &a, float &b, float &c, float &d) {
+  a = (float)(int)(int8_t)(w & 0xFFu);
+  b = (float)(int)(int8_t)((w >> 8) & 0xFFu);
+  c = (float)(int)(int8_t)((w >> 16) & 0xFFu);
+  d = (float)((int)w >> 24);
+}
+
 __device__ __forceinline__ int exponent_of(float x) { return __builtin_amdgcn_frexp_expf(x); }
 __device__ __forceinline__ float scale2(float x, int k) { return __builtin_amdgcn_ldexpf(x, k); }
 

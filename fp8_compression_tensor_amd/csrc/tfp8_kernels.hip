@@ -44,6 +44,33 @@ namespace tfp8 {
 
 constexpr int kThreads = 256;  // 4 wavefronts per workgroup
 
+// Variant bits of the *_ex entry points, as compile-time kernel parameters.
+constexpr int kInt8 = 1;        // INT8 codes, Q_max = 127 (else E4M3, Q_max = 448)
+constexpr int kNoRotation = 2;  // leave the Hadamard out (ablation)
+
+template <int FLAGS>
+constexpr float qmax_of() { return (FLAGS & kInt8) ? 127.0f : 448.0f; }
+
+// Codes of four values v * cm (cm: code multiplier with any lane sign folded in).
+template <int FLAGS>
+__device__ __forceinline__ uint32_t encode4(float a, float b, float c, float d, float cm) {
+  if constexpr (FLAGS & kInt8) {
+    return pack_int8x4_rounded(fmaf(a, cm, kInt8Magic), fmaf(b, cm, kInt8Magic),
+                               fmaf(c, cm, kInt8Magic), fmaf(d, cm, kInt8Magic));
+  } else {
+    // + 0 turns a -0 product into +0
+    return pack_fp8x4(fmaf(a, cm, 0.0f), fmaf(b, cm, 0.0f), fmaf(c, cm, 0.0f), fmaf(d, cm, 0.0f));
+  }
+}
+
+template <int FLAGS>
+__device__ __forceinline__ void decode4(uint32_t w, float &a, float &b, float &c, float &d) {
+  if constexpr (FLAGS & kInt8)
+    unpack_int8x4(w, a, b, c, d);
+  else
+    unpack_fp8x4(w, a, b, c, d);
+}
+
 // Streaming loads and stores: every input byte is read once and every output byte written
 // once, so they go through the cache hierarchy with the non-temporal hint.
 template <class T>
@@ -70,17 +97,19 @@ __device__ __forceinline__ void st_stream(T v, T *p) {
 //   v      values in registers; the true values are v * 2^E0 (times the lane sign)
 //   M      max|v| over the block (every lane of the group holds it)
 //   E0     exponent offset of v (0 for compress; the reduce's common exponent)
-//   TBB    T * B^2 for compress (v = H x unnormalised), T * B for reduce (v = r)
-//   C      448 * sqrt(B) for compress, 448 for reduce
+//   TBB    T * B^2 for compress (v = H x unnormalised), T * B for reduce and for compress
+//          without the rotation (v = r or v = x)
+//   Q      Q_max (448 for E4M3 codes, 127 for INT8 codes)
+//   C      Q * sqrt(B) for compress, Q for reduce and for compress without the rotation
 //   sign   +-1 lane sign folded into the code multiplier
 // On return v may be rescaled by a power of two, and v * code_mult are the codes' values.
 template <int L, int N>
-__device__ __forceinline__ void scales_exact(float (&v)[N], float M, int E0, float TBB, float C,
-                                             float sign, float &code_mult, float &alpha_out,
-                                             float &scale_out) {
+__device__ __forceinline__ void scales_exact(float (&v)[N], float M, int E0, float TBB, float Q,
+                                             float C, float sign, float &code_mult,
+                                             float &alpha_out, float &scale_out) {
   int E = E0;
   if (M != 0.0f && !(M >= 0x1p-100f && M <= 0x1p100f)) {
-    // Bring max|v| into [1, 2) by an exact power of two so that 448 / M is a normal float.
+    // Bring max|v| into [1, 2) by an exact power of two so that Q / M is a normal float.
     const int k = 1 - exponent_of(M);
 #pragma unroll
     for (int r = 0; r < N; ++r) v[r] = scale2(v[r], k);
@@ -88,7 +117,7 @@ __device__ __forceinline__ void scales_exact(float (&v)[N], float M, int E0, flo
     E -= k;
   }
   const bool zero = (M == 0.0f);
-  const float c = zero ? 0.0f : __fdiv_rn(448.0f, M);
+  const float c = zero ? 0.0f : __fdiv_rn(Q, M);
   // energy from the codes' values u = v c: sum(u^2) = c^2 sum(v^2) stays in float32 range
   float su = 0.0f;
 #pragma unroll
@@ -133,7 +162,7 @@ __device__ __forceinline__ void load_compress_in(CompressIn<B, F32IN> &in, const
   }
 }
 
-template <int B, bool F32IN>
+template <int B, bool F32IN, int FLAGS>
 __global__ __launch_bounds__(kThreads) void k_compress(const void *__restrict__ xin, int64_t nb,
                                                        float TBB, float sqrtTB, float C,
                                                        float invC, uint8_t *__restrict__ codes,
@@ -141,11 +170,13 @@ __global__ __launch_bounds__(kThreads) void k_compress(const void *__restrict__ 
                                                        float *__restrict__ scale_out) {
   constexpr int N = B / 8;   // elements per lane
   constexpr int G = N / 8;   // runs of 8 consecutive elements per lane
+  constexpr bool ROT = !(FLAGS & kNoRotation);
+  constexpr float Q = qmax_of<FLAGS>();
   const int lane = threadIdx.x & 63;
   const int j = lane & 7;
   const int bw = lane >> 3;
-  const int pj = lane8_perm(j);
-  const float sj = lane8_sign(j);
+  const int pj = ROT ? lane8_perm(j) : j;
+  const float sj = ROT ? lane8_sign(j) : 1.0f;
   const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
   const int64_t nwaves = ((int64_t)gridDim.x * kThreads) >> 6;
   const int64_t ntiles = (nb + 7) >> 3;
@@ -174,10 +205,13 @@ __global__ __launch_bounds__(kThreads) void k_compress(const void *__restrict__ 
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const uint32_t d = cur.d[g][q];
-          bf16_pair_butterfly(d, ones, plus_minus, v[8 * g + 2 * q], v[8 * g + 2 * q + 1]);
+          if constexpr (ROT)
+            bf16_pair_butterfly(d, ones, plus_minus, v[8 * g + 2 * q], v[8 * g + 2 * q + 1]);
+          else
+            widen_bf16x2(d, v[8 * g + 2 * q], v[8 * g + 2 * q + 1]);
           ss = bf16_pair_sumsq(d, ss);
         }
-      fwht_registers<N, 2>(v);
+      if constexpr (ROT) fwht_registers<N, 2>(v);
     } else {
 #pragma unroll
       for (int g = 0; g < G; ++g)
@@ -188,10 +222,10 @@ __global__ __launch_bounds__(kThreads) void k_compress(const void *__restrict__ 
         }
 #pragma unroll
       for (int r = 0; r < N; ++r) ss = fmaf(v[r], v[r], ss);
-      fwht_registers<N, 1>(v);
+      if constexpr (ROT) fwht_registers<N, 1>(v);
     }
     // orthogonal Hadamard rotation, unnormalised: w = H x (1/sqrt(B) and alpha live in s)
-    fwht_lanes8<N>(v, j);
+    if constexpr (ROT) fwht_lanes8<N>(v, j);
 
     float m = 0.0f;
 #pragma unroll
@@ -199,32 +233,30 @@ __global__ __launch_bounds__(kThreads) void k_compress(const void *__restrict__ 
     const float M = group_max<8>(m);
     const float SS = group_sum<8>(ss);  // sum(x^2) of the block
 
-    // alpha = sqrt(T B / sum x^2), s = alpha max|w| / (448 sqrt B), codes = E4M3(448 w / max|w|).
+    // alpha = sqrt(T B / sum x^2), s = alpha max|w| / (Q sqrt B), codes = code(Q w / max|w|)
+    // (Q = 448 for E4M3; without the rotation w = x and s = alpha max|x| / Q).
     // For max|w| in [2^-40, 2^60] every quantity stays normal and sum(x^2) is accurate, so the
     // scales use the single-instruction reciprocal square root (1 ulp, inside the 1e-6 bar);
-    // the code multiplier 448 / max|w| is correctly rounded, so that a quotient that is exactly
+    // the code multiplier Q / max|w| is correctly rounded, so that a quotient that is exactly
     // a rounding midpoint stays exact and rounds to even.  Other blocks (all-zero,
     // bfloat16-subnormal, huge) take the range-safe path.
     float cm, alpha, s;
     if (M >= 0x1p-40f && M <= 0x1p60f) {
-      const float c = __fdiv_rn(448.0f, M);
+      const float c = __fdiv_rn(Q, M);
       alpha = fminf(fmaxf(sqrtTB * __builtin_amdgcn_rsqf(SS), 0x1p-126f), 0x1p126f);
       s = alpha * M * invC;
       cm = c * sj;
     } else {
-      scales_exact<8, N>(v, M, 0, TBB, C, sj, cm, alpha, s);
+      scales_exact<8, N>(v, M, 0, TBB, Q, C, sj, cm, alpha, s);
     }
 
     if (active) {
       uint8_t *cb = codes + blk * B + 8 * pj;
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        float u[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) u[e] = fmaf(v[8 * g + e], cm, 0.0f);  // +0 keeps zeros +0
         u32x2 w;
-        w[0] = pack_fp8x4(u[0], u[1], u[2], u[3]);
-        w[1] = pack_fp8x4(u[4], u[5], u[6], u[7]);
+        w[0] = encode4<FLAGS>(v[8 * g + 0], v[8 * g + 1], v[8 * g + 2], v[8 * g + 3], cm);
+        w[1] = encode4<FLAGS>(v[8 * g + 4], v[8 * g + 5], v[8 * g + 6], v[8 * g + 7], cm);
         st_stream(w, (u32x2 *)(cb + 64 * g));
       }
       if (j == 0) {
@@ -257,7 +289,7 @@ __device__ __forceinline__ void load_decompress_in(DecompressIn<B> &in, const ui
   in.a = alpha[blk];
 }
 
-template <int B, bool F32OUT>
+template <int B, bool F32OUT, int FLAGS>
 __global__ __launch_bounds__(kThreads) void k_decompress(const uint8_t *__restrict__ codes,
                                                          const float *__restrict__ alpha,
                                                          const float *__restrict__ scale,
@@ -265,11 +297,12 @@ __global__ __launch_bounds__(kThreads) void k_decompress(const uint8_t *__restri
                                                          void *__restrict__ out) {
   constexpr int N = B / 8;
   constexpr int G = N / 8;
+  constexpr bool ROT = !(FLAGS & kNoRotation);
   const int lane = threadIdx.x & 63;
   const int j = lane & 7;
   const int bw = lane >> 3;
-  const int pj = lane8_perm(j);
-  const float sj = lane8_sign(j);
+  const int pj = ROT ? lane8_perm(j) : j;
+  const float sj = ROT ? lane8_sign(j) : 1.0f;
   const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
   const int64_t nwaves = ((int64_t)gridDim.x * kThreads) >> 6;
   const int64_t ntiles = (nb + 7) >> 3;
@@ -288,16 +321,18 @@ __global__ __launch_bounds__(kThreads) void k_decompress(const uint8_t *__restri
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const uint32_t w0 = cur.d[g][0], w1 = cur.d[g][1];
-      unpack_fp8x4(w0, v[8 * g + 0], v[8 * g + 1], v[8 * g + 2], v[8 * g + 3]);
-      unpack_fp8x4(w1, v[8 * g + 4], v[8 * g + 5], v[8 * g + 6], v[8 * g + 7]);
+      decode4<FLAGS>(w0, v[8 * g + 0], v[8 * g + 1], v[8 * g + 2], v[8 * g + 3]);
+      decode4<FLAGS>(w1, v[8 * g + 4], v[8 * g + 5], v[8 * g + 6], v[8 * g + 7]);
     }
     const float s = cur.s, a = cur.a;
 
-    // The decoded values are multiples of 2^-9 below 2^8.81, so every partial sum of the
-    // transform is exact in float32 until it passes 2^15 (for B <= 128 only the last stage
-    // can round, once).
-    fwht_registers<N, 1>(v);
-    fwht_lanes8<N>(v, j);
+    // The decoded values are multiples of 2^-9 below 2^8.81 (E4M3) or integers below 2^7
+    // (INT8), so every partial sum of the transform is exact in float32 until it passes 2^15
+    // (E4M3; for B <= 128 only the last stage can round, once) or 2^24 (INT8: never).
+    if constexpr (ROT) {
+      fwht_registers<N, 1>(v);
+      fwht_lanes8<N>(v, j);
+    }
 
     // (v * s / sqrt(B)) / alpha as two products: s / (sqrt(B) alpha) alone can fall below the
     // normal range when alpha is large, the two-step form only rounds the final value there.
@@ -343,7 +378,7 @@ __global__ __launch_bounds__(kThreads) void k_decompress(const uint8_t *__restri
 // contribution), no Hadamard.  PB > 0: exactly PB contributions, all loads issued before any
 // arithmetic; PB = 0: any P, in chunks of 8.
 
-template <int B, int PB>
+template <int B, int PB, int FLAGS>
 __global__ __launch_bounds__(kThreads) void k_reduce(const uint8_t *__restrict__ codes,
                                                      const float *__restrict__ alpha,
                                                      const float *__restrict__ scale, int P,
@@ -354,6 +389,9 @@ __global__ __launch_bounds__(kThreads) void k_reduce(const uint8_t *__restrict__
   constexpr int L = B / 16;    // lanes per block
   constexpr int BPW = 64 / L;  // blocks per wavefront
   constexpr int CH = PB > 0 ? PB : 8;  // contributions loaded together
+  // low bits of g cleared so that g times a code value is exact in float64: E4M3 values have
+  // at most 4 significant bits (g keeps 49), INT8 values at most 7 (g keeps 46)
+  constexpr long long kGMask = (FLAGS & kInt8) ? ~0x7FLL : ~0xFLL;
   if constexpr (PB > 0) P = PB;
   const int lane = threadIdx.x & 63;
   const int j = lane % L;
@@ -369,8 +407,8 @@ __global__ __launch_bounds__(kThreads) void k_reduce(const uint8_t *__restrict__
     const uint8_t *cb = codes + cblk * B + 16 * j;
 
     // r = sum_p g_p dec(q_p) with g_p = s_p / alpha_p, accumulated in float64.  g_p is cut to
-    // 49 significant bits (a relative change below 2^-48), so that its product with an E4M3
-    // value (at most 4 significant bits) is exact in float64; the only roundings are those of
+    // 49 significant bits (46 for INT8 codes; a relative change below 2^-45), so that its
+    // product with a code value is exact in float64; the only roundings are those of
     // the running sum, each within 2^-53 of it.  Contributions that largely cancel therefore
     // still requantise like the exact sum, and a contribution and its exact negation cancel
     // to exactly zero.  A zero block (s_p = 0) contributes exact zeros.
@@ -393,11 +431,11 @@ __global__ __launch_bounds__(kThreads) void k_reduce(const uint8_t *__restrict__
           double ri = __builtin_amdgcn_rcp(ad);
           ri = fma(ri, fma(-ad, ri, 1.0), ri);
           ri = fma(ri, fma(-ad, ri, 1.0), ri);
-          const double g = __longlong_as_double(__double_as_longlong((double)sp[c] * ri) & ~0xFLL);
+          const double g = __longlong_as_double(__double_as_longlong((double)sp[c] * ri) & kGMask);
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             float a0, a1, a2, a3;
-            unpack_fp8x4(d[c][q], a0, a1, a2, a3);
+            decode4<FLAGS>(d[c][q], a0, a1, a2, a3);
             if (p0 + c == 0) {
               r64[4 * q + 0] = (double)a0 * g;
               r64[4 * q + 1] = (double)a1 * g;
@@ -444,13 +482,13 @@ __global__ __launch_bounds__(kThreads) void k_reduce(const uint8_t *__restrict__
 
     // the true sum is r * 2^E
     float cm, a_out, s_out;
-    scales_exact<L, 16>(r, M, E, TB, 448.0f, 1.0f, cm, a_out, s_out);
+    constexpr float Q = qmax_of<FLAGS>();
+    scales_exact<L, 16>(r, M, E, TB, Q, Q, 1.0f, cm, a_out, s_out);
     if (active) {
       u32x4 w;
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        w[q] = pack_fp8x4(fmaf(r[4 * q], cm, 0.0f), fmaf(r[4 * q + 1], cm, 0.0f),
-                          fmaf(r[4 * q + 2], cm, 0.0f), fmaf(r[4 * q + 3], cm, 0.0f));
+        w[q] = encode4<FLAGS>(r[4 * q], r[4 * q + 1], r[4 * q + 2], r[4 * q + 3], cm);
       st_stream(w, (u32x4 *)(codes_out + blk * B + 16 * j));
       if (j == 0) {
         alpha_out[blk] = a_out;
@@ -522,47 +560,67 @@ tfp8_status launched() {
   return hipGetLastError() == hipSuccess ? TFP8_OK : TFP8_E_HIP;
 }
 
-template <int B>
-tfp8_status launch_compress(const void *x, bool f32, int64_t nb, float target, uint8_t *codes,
-                            float *alpha, float *scale, hipStream_t st) {
-  const float TBB = target * (float)B * (float)B;  // exact: powers of two
+template <int B, bool F32, int FLAGS>
+void launch_compress_t(const void *x, int64_t nb, float target, uint8_t *codes, float *alpha,
+                       float *scale, hipStream_t st) {
+  constexpr bool ROT = !(FLAGS & kNoRotation);
+  const double Q = qmax_of<FLAGS>();
+  // energy of v: sum(v^2) = B sum(x^2) with the (unnormalised) rotation, sum(x^2) without
+  const float TBB = target * (float)B * (ROT ? (float)B : 1.0f);  // exact: powers of two
   const float sqrtTB = (float)sqrt((double)target * B);
-  const double Cd = 448.0 * sqrt((double)B);
+  const double Cd = ROT ? Q * sqrt((double)B) : Q;
   const float C = (float)Cd, invC = (float)(1.0 / Cd);
   const unsigned grid = grid_for((nb + 7) / 8, TFP8_COMPRESS_WGS_PER_CU);
-  if (f32)
-    hipLaunchKernelGGL((k_compress<B, true>), dim3(grid), dim3(kThreads), 0, st, x, nb, TBB, sqrtTB,
-                       C, invC, codes, alpha, scale);
-  else
-    hipLaunchKernelGGL((k_compress<B, false>), dim3(grid), dim3(kThreads), 0, st, x, nb, TBB,
-                       sqrtTB, C, invC, codes, alpha, scale);
+  hipLaunchKernelGGL((k_compress<B, F32, FLAGS>), dim3(grid), dim3(kThreads), 0, st, x, nb, TBB,
+                     sqrtTB, C, invC, codes, alpha, scale);
+}
+
+template <int B, bool F32>
+tfp8_status launch_compress(const void *x, int64_t nb, float target, uint32_t flags,
+                            uint8_t *codes, float *alpha, float *scale, hipStream_t st) {
+  switch (flags) {
+    case 0: launch_compress_t<B, F32, 0>(x, nb, target, codes, alpha, scale, st); break;
+    case kInt8: launch_compress_t<B, F32, kInt8>(x, nb, target, codes, alpha, scale, st); break;
+    case kNoRotation: launch_compress_t<B, F32, kNoRotation>(x, nb, target, codes, alpha, scale, st); break;
+    default: launch_compress_t<B, F32, kInt8 | kNoRotation>(x, nb, target, codes, alpha, scale, st); break;
+  }
   return launched();
 }
 
-template <int B>
-tfp8_status launch_decompress(const uint8_t *codes, const float *alpha, const float *scale,
-                              int64_t nb, void *out, bool f32, hipStream_t st) {
-  const float inv_sqrt_b = (float)(1.0 / sqrt((double)B));
+template <int B, bool F32, int FLAGS>
+void launch_decompress_t(const uint8_t *codes, const float *alpha, const float *scale, int64_t nb,
+                         void *out, hipStream_t st) {
+  constexpr bool ROT = !(FLAGS & kNoRotation);
+  const float inv_sqrt_b = ROT ? (float)(1.0 / sqrt((double)B)) : 1.0f;
   const unsigned grid = grid_for((nb + 7) / 8, TFP8_DECOMPRESS_WGS_PER_CU);
-  if (f32)
-    hipLaunchKernelGGL((k_decompress<B, true>), dim3(grid), dim3(kThreads), 0, st, codes, alpha,
-                       scale, nb, inv_sqrt_b, out);
-  else
-    hipLaunchKernelGGL((k_decompress<B, false>), dim3(grid), dim3(kThreads), 0, st, codes, alpha,
-                       scale, nb, inv_sqrt_b, out);
+  hipLaunchKernelGGL((k_decompress<B, F32, FLAGS>), dim3(grid), dim3(kThreads), 0, st, codes,
+                     alpha, scale, nb, inv_sqrt_b, out);
+}
+
+template <int B, bool F32>
+tfp8_status launch_decompress(const uint8_t *codes, const float *alpha, const float *scale,
+                              int64_t nb, uint32_t flags, void *out, hipStream_t st) {
+  switch (flags) {
+    case 0: launch_decompress_t<B, F32, 0>(codes, alpha, scale, nb, out, st); break;
+    case kInt8: launch_decompress_t<B, F32, kInt8>(codes, alpha, scale, nb, out, st); break;
+    case kNoRotation: launch_decompress_t<B, F32, kNoRotation>(codes, alpha, scale, nb, out, st); break;
+    default: launch_decompress_t<B, F32, kInt8 | kNoRotation>(codes, alpha, scale, nb, out, st); break;
+  }
   return launched();
 }
 
-template <int B>
-tfp8_status launch_reduce(const uint8_t *codes, const float *alpha, const float *scale, int P,
-                          int64_t n, int64_t nb, float target, uint8_t *codes_out,
-                          float *alpha_out, float *scale_out, hipStream_t st) {
+template <int B, int FLAGS>
+void launch_reduce_t(const uint8_t *codes, const float *alpha, const float *scale, int P,
+                     int64_t n, int64_t nb, float target, uint8_t *codes_out, float *alpha_out,
+                     float *scale_out, hipStream_t st) {
+  // the reduce works on r = sum_p g_p dec(q_p) directly, with or without the rotation: its
+  // energy is that of the sum, sum(r^2) = sum(z^2)
   const float TB = target * (float)B;
   constexpr int BPW = 64 / (B / 16);
   const unsigned grid = grid_for((nb + BPW - 1) / BPW, TFP8_REDUCE_WGS_PER_CU);
-#define TFP8_LAUNCH_REDUCE(PB)                                                                 \
-  hipLaunchKernelGGL((k_reduce<B, PB>), dim3(grid), dim3(kThreads), 0, st, codes, alpha, scale, P, \
-                     n, nb, TB, codes_out, alpha_out, scale_out)
+#define TFP8_LAUNCH_REDUCE(PB)                                                                  \
+  hipLaunchKernelGGL((k_reduce<B, PB, FLAGS>), dim3(grid), dim3(kThreads), 0, st, codes, alpha, \
+                     scale, P, n, nb, TB, codes_out, alpha_out, scale_out)
   switch (P) {
     case 1: TFP8_LAUNCH_REDUCE(1); break;
     case 2: TFP8_LAUNCH_REDUCE(2); break;
@@ -571,6 +629,18 @@ tfp8_status launch_reduce(const uint8_t *codes, const float *alpha, const float 
     default: TFP8_LAUNCH_REDUCE(0); break;
   }
 #undef TFP8_LAUNCH_REDUCE
+}
+
+template <int B>
+tfp8_status launch_reduce(const uint8_t *codes, const float *alpha, const float *scale, int P,
+                          int64_t n, int64_t nb, float target, uint32_t flags, uint8_t *codes_out,
+                          float *alpha_out, float *scale_out, hipStream_t st) {
+  if (flags & kInt8)
+    launch_reduce_t<B, kInt8>(codes, alpha, scale, P, n, nb, target, codes_out, alpha_out,
+                              scale_out, st);
+  else
+    launch_reduce_t<B, 0>(codes, alpha, scale, P, n, nb, target, codes_out, alpha_out, scale_out,
+                          st);
   return launched();
 }
 
@@ -578,7 +648,7 @@ tfp8_status launch_reduce(const uint8_t *codes, const float *alpha, const float 
 
 extern "C" {
 
-int32_t tfp8_version(void) { return (1 << 16) | 0; }
+int32_t tfp8_version(void) { return (1 << 16) | 1; }
 
 const char *tfp8_status_string(tfp8_status status) {
   switch (status) {
@@ -594,12 +664,13 @@ const char *tfp8_status_string(tfp8_status status) {
   return "unknown status";
 }
 
-tfp8_status tfp8_compress(const void *x, tfp8_dtype x_dtype, int64_t n, int32_t block, float target,
-                          uint8_t *codes, float *alpha, float *scale, void *stream) {
+tfp8_status tfp8_compress_ex(const void *x, tfp8_dtype x_dtype, int64_t n, int32_t block,
+                             float target, uint32_t flags, uint8_t *codes, float *alpha,
+                             float *scale, void *stream) {
   if (!block_ok(block)) return TFP8_E_BLOCK;
   if (n < 0 || n % block != 0) return TFP8_E_SIZE;
   if (x_dtype != TFP8_BF16 && x_dtype != TFP8_F32) return TFP8_E_DTYPE;
-  if (!target_ok(target)) return TFP8_E_ARG;
+  if (!target_ok(target) || (flags & ~TFP8_FLAGS_ALL)) return TFP8_E_ARG;
   if (n == 0) return TFP8_OK;
   if (!x || !codes || !alpha || !scale) return TFP8_E_NULL;
   if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(alpha, 4) || !aligned(scale, 4))
@@ -612,19 +683,32 @@ tfp8_status tfp8_compress(const void *x, tfp8_dtype x_dtype, int64_t n, int32_t 
     return TFP8_E_ARG;
   hipStream_t st = (hipStream_t)stream;
   const bool f32 = x_dtype == TFP8_F32;
+#define TFP8_CASE(BB)                                                                         \
+  case BB:                                                                                    \
+    return f32 ? launch_compress<BB, true>(x, nb, target, flags, codes, alpha, scale, st)     \
+               : launch_compress<BB, false>(x, nb, target, flags, codes, alpha, scale, st);
   switch (block) {
-    case 64: return launch_compress<64>(x, f32, nb, target, codes, alpha, scale, st);
-    case 128: return launch_compress<128>(x, f32, nb, target, codes, alpha, scale, st);
-    case 256: return launch_compress<256>(x, f32, nb, target, codes, alpha, scale, st);
-    default: return launch_compress<512>(x, f32, nb, target, codes, alpha, scale, st);
+    TFP8_CASE(64)
+    TFP8_CASE(128)
+    TFP8_CASE(256)
+    TFP8_CASE(512)
   }
+#undef TFP8_CASE
+  return TFP8_E_BLOCK;
 }
 
-tfp8_status tfp8_decompress(const uint8_t *codes, const float *alpha, const float *scale, int64_t n,
-                            int32_t block, void *out, tfp8_dtype out_dtype, void *stream) {
+tfp8_status tfp8_compress(const void *x, tfp8_dtype x_dtype, int64_t n, int32_t block, float target,
+                          uint8_t *codes, float *alpha, float *scale, void *stream) {
+  return tfp8_compress_ex(x, x_dtype, n, block, target, 0, codes, alpha, scale, stream);
+}
+
+tfp8_status tfp8_decompress_ex(const uint8_t *codes, const float *alpha, const float *scale,
+                               int64_t n, int32_t block, uint32_t flags, void *out,
+                               tfp8_dtype out_dtype, void *stream) {
   if (!block_ok(block)) return TFP8_E_BLOCK;
   if (n < 0 || n % block != 0) return TFP8_E_SIZE;
   if (out_dtype != TFP8_BF16 && out_dtype != TFP8_F32) return TFP8_E_DTYPE;
+  if (flags & ~TFP8_FLAGS_ALL) return TFP8_E_ARG;
   if (n == 0) return TFP8_OK;
   if (!codes || !alpha || !scale || !out) return TFP8_E_NULL;
   if (!aligned(out, 16) || !aligned(codes, 16) || !aligned(alpha, 4) || !aligned(scale, 4))
@@ -636,20 +720,31 @@ tfp8_status tfp8_decompress(const uint8_t *codes, const float *alpha, const floa
     return TFP8_E_ARG;
   hipStream_t st = (hipStream_t)stream;
   const bool f32 = out_dtype == TFP8_F32;
+#define TFP8_CASE(BB)                                                                        \
+  case BB:                                                                                   \
+    return f32 ? launch_decompress<BB, true>(codes, alpha, scale, nb, flags, out, st)        \
+               : launch_decompress<BB, false>(codes, alpha, scale, nb, flags, out, st);
   switch (block) {
-    case 64: return launch_decompress<64>(codes, alpha, scale, nb, out, f32, st);
-    case 128: return launch_decompress<128>(codes, alpha, scale, nb, out, f32, st);
-    case 256: return launch_decompress<256>(codes, alpha, scale, nb, out, f32, st);
-    default: return launch_decompress<512>(codes, alpha, scale, nb, out, f32, st);
+    TFP8_CASE(64)
+    TFP8_CASE(128)
+    TFP8_CASE(256)
+    TFP8_CASE(512)
   }
+#undef TFP8_CASE
+  return TFP8_E_BLOCK;
 }
 
-tfp8_status tfp8_reduce_fp8(const uint8_t *codes, const float *alpha, const float *scale, int32_t P,
-                            int64_t n, int32_t block, float target, uint8_t *codes_out,
-                            float *alpha_out, float *scale_out, void *stream) {
+tfp8_status tfp8_decompress(const uint8_t *codes, const float *alpha, const float *scale, int64_t n,
+                            int32_t block, void *out, tfp8_dtype out_dtype, void *stream) {
+  return tfp8_decompress_ex(codes, alpha, scale, n, block, 0, out, out_dtype, stream);
+}
+
+tfp8_status tfp8_reduce_ex(const uint8_t *codes, const float *alpha, const float *scale, int32_t P,
+                           int64_t n, int32_t block, float target, uint32_t flags,
+                           uint8_t *codes_out, float *alpha_out, float *scale_out, void *stream) {
   if (!block_ok(block)) return TFP8_E_BLOCK;
   if (n < 0 || n % block != 0) return TFP8_E_SIZE;
-  if (P < 1 || P > 64 || !target_ok(target)) return TFP8_E_ARG;
+  if (P < 1 || P > 64 || !target_ok(target) || (flags & ~TFP8_FLAGS_ALL)) return TFP8_E_ARG;
   if (n == 0) return TFP8_OK;
   if (!codes || !alpha || !scale || !codes_out || !alpha_out || !scale_out) return TFP8_E_NULL;
   if (!aligned(codes, 16) || !aligned(codes_out, 16) || !aligned(alpha, 4) || !aligned(scale, 4) ||
@@ -668,11 +763,19 @@ tfp8_status tfp8_reduce_fp8(const uint8_t *codes, const float *alpha, const floa
   }
   hipStream_t st = (hipStream_t)stream;
   switch (block) {
-    case 64: return launch_reduce<64>(codes, alpha, scale, P, n, nb, target, codes_out, alpha_out, scale_out, st);
-    case 128: return launch_reduce<128>(codes, alpha, scale, P, n, nb, target, codes_out, alpha_out, scale_out, st);
-    case 256: return launch_reduce<256>(codes, alpha, scale, P, n, nb, target, codes_out, alpha_out, scale_out, st);
-    default: return launch_reduce<512>(codes, alpha, scale, P, n, nb, target, codes_out, alpha_out, scale_out, st);
+    case 64: return launch_reduce<64>(codes, alpha, scale, P, n, nb, target, flags, codes_out, alpha_out, scale_out, st);
+    case 128: return launch_reduce<128>(codes, alpha, scale, P, n, nb, target, flags, codes_out, alpha_out, scale_out, st);
+    case 256: return launch_reduce<256>(codes, alpha, scale, P, n, nb, target, flags, codes_out, alpha_out, scale_out, st);
+    case 512: return launch_reduce<512>(codes, alpha, scale, P, n, nb, target, flags, codes_out, alpha_out, scale_out, st);
   }
+  return TFP8_E_BLOCK;
+}
+
+tfp8_status tfp8_reduce_fp8(const uint8_t *codes, const float *alpha, const float *scale, int32_t P,
+                            int64_t n, int32_t block, float target, uint8_t *codes_out,
+                            float *alpha_out, float *scale_out, void *stream) {
+  return tfp8_reduce_ex(codes, alpha, scale, P, n, block, target, 0, codes_out, alpha_out,
+                        scale_out, stream);
 }
 
 }  // extern "C"

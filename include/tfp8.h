@@ -13,7 +13,7 @@
  *                    fused kernel for the energy, the transform and the quantization).
  *   tfp8_decompress  the inverse with both scales (same page, section 2.B.2, reconstruction).
  *   tfp8_reduce_fp8  the local step of a two-shot all-reduce: dequantize P contributions,
- *                    sum in FP32, requantize to the same format.  Page "AGoQ: Activation and
+ *                    sum them, requantize to the same format.  Page "AGoQ: Activation and
  *                    Gradient Quantization for Memory-Efficient Distributed Training of LLMs",
  *                    section 2.B (precision-preserving all-reduce); the TACO page, section
  *                    2.B.3, puts the same step between ReduceScatter and AllGather.
@@ -59,11 +59,22 @@ typedef enum {
   TFP8_E_BLOCK = -3, /* block is not one of 64, 128, 256, 512 */
   TFP8_E_DTYPE = -4, /* dtype is not TFP8_BF16 or TFP8_F32 */
   TFP8_E_ALIGN = -5, /* a pointer is not aligned as stated above */
-  TFP8_E_ARG = -6,   /* P < 1 or P > 64, bad target, or overlapping buffers */
+  TFP8_E_ARG = -6,   /* P < 1 or P > 64, bad target, unknown flags, or overlapping buffers */
   TFP8_E_HIP = -7    /* the HIP runtime rejected the launch */
 } tfp8_status;
 
 typedef enum { TFP8_BF16 = 0, TFP8_F32 = 1 } tfp8_dtype;
+
+/* Variant flags of the *_ex entry points (0 = the method as defined above):
+ *   TFP8_FLAG_INT8         codes are int8 (two's complement, round to nearest even, saturating at
+ *                          +-127) with Q_max = 127 instead of E4M3 with 448: the INT8 fallback the
+ *                          TACO page keeps for hardware without FP8 (section 5).  Compress,
+ *                          decompress and reduce must be called with the same flags.
+ *   TFP8_FLAG_NO_ROTATION  leave the Hadamard rotation out (H = identity): plain per-block
+ *                          dual-scale quantization, for ablations of the transform. */
+#define TFP8_FLAG_INT8 1u
+#define TFP8_FLAG_NO_ROTATION 2u
+#define TFP8_FLAGS_ALL (TFP8_FLAG_INT8 | TFP8_FLAG_NO_ROTATION)
 
 /* Compress x[n] (bfloat16 or float32, row-major flat) in blocks of `block`.
  * Outputs: codes[n] (E4M3FN bytes, same element order as x), alpha[n/block], scale[n/block]
@@ -78,12 +89,26 @@ tfp8_status tfp8_decompress(const uint8_t *codes, const float *alpha, const floa
 
 /* Local reduce of P contributions of the same n elements, stacked contiguously:
  * codes[P][n], alpha[P][n/block], scale[P][n/block] (contribution p at offset p*n, p*n/block).
- * The contributions are dequantized, summed in float32 in the order p = 0..P-1, and the sum is
- * requantized with the same block and target into codes_out[n], alpha_out[n/block],
- * scale_out[n/block].  1 <= P <= 64. */
+ * The contributions are dequantized and summed in the order p = 0..P-1 (float64 accumulation:
+ * at least as precise as the FP32 sum of the AGoQ page, and exact for contributions that
+ * cancel), and the sum is requantized with the same block and target into codes_out[n],
+ * alpha_out[n/block], scale_out[n/block].  1 <= P <= 64. */
 tfp8_status tfp8_reduce_fp8(const uint8_t *codes, const float *alpha, const float *scale, int32_t P,
                             int64_t n, int32_t block, float target, uint8_t *codes_out,
                             float *alpha_out, float *scale_out, void *stream);
+
+/* The same three operations with variant flags (TFP8_FLAG_*); unknown bits give TFP8_E_ARG.
+ * tfp8_compress, tfp8_decompress and tfp8_reduce_fp8 are these with flags = 0.  The reduce only
+ * needs the code format: its result is the same with or without the rotation. */
+tfp8_status tfp8_compress_ex(const void *x, tfp8_dtype x_dtype, int64_t n, int32_t block,
+                             float target, uint32_t flags, uint8_t *codes, float *alpha,
+                             float *scale, void *stream);
+tfp8_status tfp8_decompress_ex(const uint8_t *codes, const float *alpha, const float *scale,
+                               int64_t n, int32_t block, uint32_t flags, void *out,
+                               tfp8_dtype out_dtype, void *stream);
+tfp8_status tfp8_reduce_ex(const uint8_t *codes, const float *alpha, const float *scale, int32_t P,
+                           int64_t n, int32_t block, float target, uint32_t flags,
+                           uint8_t *codes_out, float *alpha_out, float *scale_out, void *stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char *tfp8_status_string(tfp8_status status);

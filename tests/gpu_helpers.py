@@ -7,7 +7,7 @@ import sys
 import numpy as np
 import torch
 
-from tiecheck import assert_codes_match, assert_rel_close
+from tiecheck import FLAG_INT8, assert_codes_match, assert_rel_close, tie_cap
 
 DEV = torch.device("cuda:0")
 
@@ -77,31 +77,52 @@ def assert_bf16_match(got_bits, ref_bits, ref_f64, rel=2.0 ** -20, what="bf16 ou
     return int(bad.size)
 
 
-def check_compress(oracle, tfp8, x: np.ndarray, B: int, T: float = 1.0, what="compress"):
+def check_compress(oracle, tfp8, x: np.ndarray, B: int, T: float = 1.0, what="compress",
+                   flags: int = 0):
     """GPU compress of host input x (uint16 bfloat16 bits or float32) vs the oracle.
     Returns (gpu codes, alpha, scale) as numpy arrays."""
     xg = bits_to_gpu(x) if x.dtype == np.uint16 else f32_to_gpu(x)
-    q, a, s = tfp8.compress(xg.reshape(-1), B, T)
+    q, a, s = tfp8.compress(xg.reshape(-1), B, T, flags=flags)
     torch.cuda.synchronize()
     q, a, s = cpu(q), cpu(a), cpu(s)
-    qr, ar, sr, tr = oracle.compress(x.reshape(-1), B, T, with_quot=True)
-    nmis = assert_codes_match(q, qr, tr, what=what + " codes")
+    qr, ar, sr, tr = oracle.compress(x.reshape(-1), B, T, with_quot=True, flags=flags)
+    nmis = assert_codes_match(q, qr, tr, max_frac=tie_cap(flags), what=what + " codes",
+                              int8=bool(flags & FLAG_INT8))
     ea, es = assert_scales(a, s, ar, sr, what=what)
-    say(f"  {what}: n={x.size} B={B} T={T}: code tie mismatches {nmis} "
+    say(f"  {what}: n={x.size} B={B} T={T} flags={flags}: code tie mismatches {nmis} "
         f"({nmis / max(x.size, 1):.2e}), max rel err alpha {ea:.2e} scale {es:.2e}")
     return q, a, s
 
 
-def check_decompress(oracle, tfp8, q, a, s, B: int, what="decompress"):
+def check_decompress(oracle, tfp8, q, a, s, B: int, what="decompress", flags: int = 0):
     """GPU decompress of the given codes and scales vs the oracle, float32 and bfloat16."""
     qg, ag, sg = u8_to_gpu(q.reshape(-1)), f32_to_gpu(a), f32_to_gpu(s)
-    o32 = tfp8.decompress(qg, ag, sg, B, torch.float32)
-    o16 = tfp8.decompress(qg, ag, sg, B, torch.bfloat16)
+    o32 = tfp8.decompress(qg, ag, sg, B, torch.float32, flags=flags)
+    o16 = tfp8.decompress(qg, ag, sg, B, torch.bfloat16, flags=flags)
     torch.cuda.synchronize()
-    r64 = oracle.decompress_f64(q, a, s, B)
-    r32 = oracle.decompress(q, a, s, B, np.float32)
-    r16 = oracle.decompress(q, a, s, B, np.uint16)
+    r64 = oracle.decompress_f64(q, a, s, B, flags=flags)
+    r32 = oracle.decompress(q, a, s, B, np.float32, flags=flags)
+    r16 = oracle.decompress(q, a, s, B, np.uint16, flags=flags)
     e32 = assert_rel_close(cpu(o32), r32, 1e-6, 2.0 ** -149, what=what + " f32")
     n16 = assert_bf16_match(gpu_bf16_bits(o16), r16, r64, what=what + " bf16")
-    say(f"  {what}: n={q.size} B={B}: max rel err f32 {e32:.2e}, bf16 tie mismatches {n16}")
+    normal = np.abs(r32) >= 2.0 ** -126
+    e32n = float((np.abs(cpu(o32)[normal] - r32[normal]) / np.abs(r32[normal])).max()) if normal.any() else 0.0
+    say(f"  {what}: n={q.size} B={B} flags={flags}: max rel err f32 (normal results) {e32n:.2e}, "
+        f"bf16 tie mismatches {n16}")
     return o32
+
+
+def check_reduce(oracle, tfp8, q, a, s, B, T=1.0, what="reduce", flags: int = 0):
+    """GPU reduce of stacked codes/scales [P, ...] vs the oracle's reduce by definition."""
+    P, n = q.shape
+    qg, ag, sg = u8_to_gpu(q), f32_to_gpu(a), f32_to_gpu(s)
+    cq, ca, cs = tfp8.reduce_fp8(qg, ag, sg, B, T, flags=flags)
+    torch.cuda.synchronize()
+    cq, ca, cs = cpu(cq), cpu(ca), cpu(cs)
+    rq, ra, rs, rt = oracle.reduce_fp8(q, a, s, B, T, with_quot=True, flags=flags)
+    nmis = assert_codes_match(cq, rq, rt, max_frac=tie_cap(flags), what=what + " codes",
+                              int8=bool(flags & FLAG_INT8))
+    ea, es = assert_scales(ca, cs, ra, rs, what=what)
+    say(f"  {what}: P={P} n={n} B={B} flags={flags}: code tie mismatches {nmis} ({nmis / n:.2e}), "
+        f"max rel err alpha {ea:.2e} scale {es:.2e}")
+    return cq, ca, cs

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol(tfp8):
     L = tfp8.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert L.tfp8_version() == (1 << 16)
+    assert L.tfp8_version() >> 16 == 1
 
 
 def test_status_strings(tfp8):
@@ -64,6 +64,17 @@ def test_compress_argument_errors(tfp8):
     assert c(FAKE, 0, 1024, 128, 1.0, FAKE + 4096, FAKE + 8192, FAKE + 8192 + 16) == -6
     # n = 0 is a no-op, even with NULL pointers
     assert c(None, 0, 0, 128, 1.0, None, None, None) == 0
+
+
+def test_unknown_flags_are_rejected(tfp8):
+    assert tfp8.compress_raw(FAKE, 0, 1024, 128, 1.0, FAKE + 4096, FAKE + 8192, FAKE + 12288,
+                             0, 4) == -6
+    assert tfp8.decompress_raw(FAKE, FAKE + 4096, FAKE + 8192, 1024, 128, FAKE + 16384, 1,
+                               0, 8) == -6
+    assert tfp8.reduce_fp8_raw(FAKE, FAKE + 65536, FAKE + 81920, 4, 1024, 128, 1.0, FAKE + 131072,
+                               FAKE + 196608, FAKE + 200704, 0, 16) == -6
+    # valid flags pass the checks (then n = 0 returns before any launch)
+    assert tfp8.compress_raw(None, 0, 0, 128, 1.0, None, None, None, 0, 3) == 0
 
 
 def test_decompress_argument_errors(tfp8):

@@ -12,8 +12,8 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import (DEV, assert_scales, bits_to_gpu, check_compress, check_decompress, cpu,
-                         f32_to_gpu, say, u8_to_gpu)
+from gpu_helpers import (DEV, assert_scales, bits_to_gpu, check_compress, check_decompress,
+                         check_reduce, cpu, f32_to_gpu, say, u8_to_gpu)
 from tiecheck import assert_codes_match, assert_rel_close
 from workloads import (CONFIGS, bf16_bits_to_f32, f32_to_bf16_bits, make_shard, make_shards,
                        random_bf16_bits)
@@ -64,17 +64,7 @@ def test_config3_compress_reduce_decompress(oracle, tfp8):
 
 
 def _check_reduce(oracle, tfp8, q, a, s, B, T=1.0, what="reduce"):
-    P, n = q.shape
-    qg, ag, sg = u8_to_gpu(q), f32_to_gpu(a), f32_to_gpu(s)
-    cq, ca, cs = tfp8.reduce_fp8(qg, ag, sg, B, T)
-    torch.cuda.synchronize()
-    cq, ca, cs = cpu(cq), cpu(ca), cpu(cs)
-    rq, ra, rs, rt = oracle.reduce_fp8(q, a, s, B, T, with_quot=True)
-    nmis = assert_codes_match(cq, rq, rt, what=what + " codes")
-    ea, es = assert_scales(ca, cs, ra, rs, what=what)
-    say(f"  {what}: P={P} n={n} B={B}: code tie mismatches {nmis} ({nmis / n:.2e}), "
-        f"max rel err alpha {ea:.2e} scale {es:.2e}")
-    return cq, ca, cs
+    return check_reduce(oracle, tfp8, q, a, s, B, T, what=what)
 
 
 # ----------------------------------------------------------------------------- config 5
@@ -261,3 +251,45 @@ def test_zero_length_is_noop(tfp8):
     x = torch.empty(0, dtype=torch.bfloat16, device=DEV)
     q, a, s = tfp8.compress(x, 128, 1.0)
     assert q.numel() == 0 and a.numel() == 0
+
+
+# ----------------------------------------------------------------------------- variants
+
+VARIANTS = [1, 2, 3]  # INT8 codes, no rotation, both
+
+
+@pytest.mark.parametrize("flags", VARIANTS)
+@pytest.mark.parametrize("cid", [1, 2])
+def test_variant_configs(oracle, tfp8, cid, flags):
+    cfg = CONFIGS[cid]
+    x = make_shard(cid).reshape(-1)
+    q, a, s = check_compress(oracle, tfp8, x, cfg.block, what=f"cfg{cid} compress", flags=flags)
+    check_decompress(oracle, tfp8, q, a, s, cfg.block, what=f"cfg{cid} decompress", flags=flags)
+
+
+@pytest.mark.parametrize("flags", VARIANTS)
+@pytest.mark.parametrize("B", [64, 128, 256, 512])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_variant_edge_blocks(oracle, tfp8, B, dtype, flags):
+    rng = np.random.default_rng(B + 7)
+    v = np.concatenate([_special_blocks(B, rng), rng.laplace(0, 0.05, 5 * B)])
+    x = f32_to_bf16_bits(v.astype(np.float32)) if dtype == "bf16" else v.astype(np.float32)
+    q, a, s = check_compress(oracle, tfp8, x, B, what=f"edge B={B} {dtype}", flags=flags)
+    check_decompress(oracle, tfp8, q, a, s, B, what=f"edge B={B} {dtype}", flags=flags)
+
+
+@pytest.mark.parametrize("flags", VARIANTS)
+@pytest.mark.parametrize("P,B", [(1, 128), (3, 64), (8, 128), (4, 256), (5, 512)])
+def test_variant_reduce(oracle, tfp8, P, B, flags):
+    rng = np.random.default_rng(100 * P + B + flags)
+    nb = 29
+    xs = [f32_to_bf16_bits((rng.laplace(0, 0.02, nb * B) * (1 + p)).astype(np.float32))
+          for p in range(P)]
+    for p in range(P):
+        xs[p][3 * B:4 * B] = 0
+        xs[p][6 * B:7 * B] = f32_to_bf16_bits(
+            (rng.integers(-64, 65, B) * 2.0 ** -133).astype(np.float32))
+    enc = [oracle.compress(x, B, 1.0, flags=flags) for x in xs]
+    q = np.stack([e[0] for e in enc]); a = np.stack([e[1] for e in enc]); s = np.stack([e[2] for e in enc])
+    cq, ca, cs = check_reduce(oracle, tfp8, q, a, s, B, what=f"reduce P={P} B={B}", flags=flags)
+    check_decompress(oracle, tfp8, cq, ca, cs, B, what=f"reduced P={P} B={B}", flags=flags)

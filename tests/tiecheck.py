@@ -44,11 +44,13 @@ FLAG_INT8, FLAG_NO_ROTATION = 1, 2
 
 def tie_cap(flags: int) -> float:
     """Largest admissible fraction of tie mismatches.  1e-4 for the method.  With the rotation
-    left out (an ablation variant), E4M3 codes are taken straight from bfloat16 inputs, whose
-    ratios to the block peak land exactly on E4M3 rounding midpoints for ~2e-3 of the elements
-    (both sit on a coarse dyadic grid); those exact ties may round either way depending on the
-    last bit of the fp32 scale, so the cap for that variant is 1e-2."""
-    return 1e-2 if (flags & FLAG_NO_ROTATION) and not (flags & FLAG_INT8) else MAX_TIE_FRAC
+    left out (an ablation variant) the codes are taken straight from ratios of bfloat16 inputs
+    to the block peak, and those ratios land exactly on rounding midpoints far more often:
+    ~2e-3 of the elements for E4M3 (both grids are coarse and dyadic), and for INT8 whenever
+    the peak's significand divides evenly (a peak of 127 * 2^k makes every quotient dyadic).
+    Such exact ties may round either way depending on the last bit of the fp32 scale, so the
+    cap for those variants is 1e-2."""
+    return 1e-2 if (flags & FLAG_NO_ROTATION) else MAX_TIE_FRAC
 
 
 def code_mismatches(got: np.ndarray, ref: np.ndarray, quot: np.ndarray, rel: float = TIE_REL,
