@@ -59,6 +59,9 @@ def lib():
         L.tfp8_ref_decompress_f64_ex.argtypes = [vp, vp, vp, i64, i32, i32, vp]
         L.tfp8_ref_reduce_ex.argtypes = [vp, vp, vp, i32, i64, i32, f32, i32, vp, vp, vp, vp]
         L.tfp8_ref_reduce_rotated_ex.argtypes = [vp, vp, vp, i32, i64, i32, f32, i32, vp, vp, vp, vp]
+        L.tfp8_ref_accumulate_ex.argtypes = [vp, vp, vp, vp, i32, i64, i32, f32, i32, vp, vp, vp, vp]
+        L.tfp8_ref_accumulate_rotated_ex.argtypes = [vp, vp, vp, vp, i32, i64, i32, f32, i32, vp, vp,
+                                                     vp, vp]
         L.tfp8_ref_set_threads.argtypes = [i32]
         L.tfp8_ref_set_threads.restype = i32
         _lib = L
@@ -214,6 +217,35 @@ def reduce_fp8_rotated(codes, alpha, scale, block: int, target: float = 1.0, wit
     """Same result by the rotated-domain route (no Hadamard)."""
     return _reduce(lib().tfp8_ref_reduce_rotated_ex, codes, alpha, scale, block, target, with_quot,
                    flags)
+
+
+def _accumulate(fn, codes, alpha, scale, grad, block, target, with_quot, flags):
+    codes = np.ascontiguousarray(codes, np.uint8).reshape(-1)
+    alpha = np.ascontiguousarray(alpha, np.float32)
+    scale = np.ascontiguousarray(scale, np.float32)
+    grad, gdt = _input(grad)
+    n = codes.size
+    qo = np.empty(n, np.uint8)
+    ao = np.empty(n // block, np.float32)
+    so = np.empty(n // block, np.float32)
+    quot = np.empty(n, np.float64) if with_quot else None
+    _check(fn(_ptr(codes), _ptr(alpha), _ptr(scale), _ptr(grad), gdt, n, block, target, flags,
+              _ptr(qo), _ptr(ao), _ptr(so), _ptr(quot)))
+    return (qo, ao, so, quot) if with_quot else (qo, ao, so)
+
+
+def accumulate(codes, alpha, scale, grad, block: int, target: float = 1.0, with_quot: bool = False,
+               flags: int = 0):
+    """Compressed main gradient + dense local gradient (bf16 bits or fp32) -> compressed sum."""
+    return _accumulate(lib().tfp8_ref_accumulate_ex, codes, alpha, scale, grad, block, target,
+                       with_quot, flags)
+
+
+def accumulate_rotated(codes, alpha, scale, grad, block: int, target: float = 1.0,
+                       with_quot: bool = False, flags: int = 0):
+    """Same result formed in the rotated domain."""
+    return _accumulate(lib().tfp8_ref_accumulate_rotated_ex, codes, alpha, scale, grad, block,
+                       target, with_quot, flags)
 
 
 def raw_status(name: str, *args) -> int:

@@ -465,3 +465,100 @@ int tfp8_ref_reduce_fp8_rotated(const uint8_t *codes, const float *alpha, const 
   return tfp8_ref_reduce_rotated_ex(codes, alpha, scale, P, n, block, target, 0, codes_out,
                                     alpha_out, scale_out, quot);
 }
+
+/* ---------------------------------------------------------------------------------------- */
+/* Local gradient accumulation ([AGoQ] section 2.B: dequantize the FP8 main gradient, add the  */
+/* new local gradient, quantize the sum again).  The oracle forms the sum in float64.          */
+
+static int check_accumulate(const uint8_t *codes, const float *alpha, const float *scale,
+                            const void *grad, int grad_dtype, int64_t n, int block, float target,
+                            int flags, uint8_t *codes_out, float *alpha_out, float *scale_out) {
+  int st = check_common(n, block);
+  if (st) return st;
+  if (grad_dtype != TFP8_REF_BF16 && grad_dtype != TFP8_REF_F32) return TFP8_REF_E_DTYPE;
+  if ((st = check_target(target)) || (st = check_flags(flags))) return st;
+  if (n == 0) return TFP8_REF_OK;
+  if (!codes || !alpha || !scale || !grad || !codes_out || !alpha_out || !scale_out)
+    return TFP8_REF_E_NULL;
+  return TFP8_REF_OK;
+}
+
+int tfp8_ref_accumulate_ex(const uint8_t *codes, const float *alpha, const float *scale,
+                           const void *grad, int grad_dtype, int64_t n, int block, float target,
+                           int flags, uint8_t *codes_out, float *alpha_out, float *scale_out,
+                           double *quot) {
+  int st = check_accumulate(codes, alpha, scale, grad, grad_dtype, n, block, target, flags,
+                            codes_out, alpha_out, scale_out);
+  if (st || n == 0) return st;
+  int64_t nb = n / block;
+#pragma omp parallel for num_threads(g_threads) schedule(static)
+  for (int64_t k = 0; k < nb; ++k) {
+    double *c = (double *)malloc(sizeof(double) * (size_t)block);
+    double *z = (double *)malloc(sizeof(double) * (size_t)block);
+    for (int i = 0; i < block; ++i) c[i] = code_value(codes[k * block + i], flags);
+    decompress_block(c, alpha[k], scale[k], block, flags, z);
+    for (int i = 0; i < block; ++i) z[i] += load_elem(grad, grad_dtype, k * block + i);
+    compress_block(z, block, (double)target, flags, codes_out + k * block, alpha_out + k,
+                   scale_out + k, quot ? quot + k * block : NULL);
+    free(c);
+    free(z);
+  }
+  return TFP8_REF_OK;
+}
+
+int tfp8_ref_accumulate_rotated_ex(const uint8_t *codes, const float *alpha, const float *scale,
+                                   const void *grad, int grad_dtype, int64_t n, int block,
+                                   float target, int flags, uint8_t *codes_out, float *alpha_out,
+                                   float *scale_out, double *quot) {
+  int st = check_accumulate(codes, alpha, scale, grad, grad_dtype, n, block, target, flags,
+                            codes_out, alpha_out, scale_out);
+  if (st || n == 0) return st;
+  int64_t nb = n / block;
+  const int rotate = !(flags & TFP8_REF_NO_ROTATION);
+  const double Q = code_qmax(flags);
+  const double rootB = sqrt((double)block);
+#pragma omp parallel for num_threads(g_threads) schedule(static)
+  for (int64_t k = 0; k < nb; ++k) {
+    /* w = H z with H unnormalised: H x_hat = sqrt(B) (s/alpha) dec(q) because (H/sqrt(B))^2 = I;
+       without the rotation, w = z = (s/alpha) dec(q) + g. */
+    double *w = (double *)malloc(sizeof(double) * (size_t)block);
+    for (int i = 0; i < block; ++i) w[i] = load_elem(grad, grad_dtype, k * block + i);
+    if (rotate) tfp8_ref_fwht(w, block);
+    double g = (scale[k] == 0.0f) ? 0.0 : (double)scale[k] / (double)alpha[k];
+    if (rotate) g *= rootB;
+    for (int i = 0; i < block; ++i) w[i] += g * code_value(codes[k * block + i], flags);
+    /* energy: sum(z^2) = sum(w^2) / B with the rotation (Parseval), sum(w^2) without */
+    double aw = 0.0, sumsq = 0.0;
+    for (int i = 0; i < block; ++i) {
+      aw = fmax(aw, fabs(w[i]));
+      sumsq += w[i] * w[i];
+    }
+    uint8_t *qo = codes_out + k * block;
+    if (aw == 0.0) {
+      alpha_out[k] = 1.0f;
+      scale_out[k] = 0.0f;
+      for (int i = 0; i < block; ++i) {
+        qo[i] = 0x00;
+        if (quot) quot[k * block + i] = 0.0;
+      }
+      free(w);
+      continue;
+    }
+    double m2 = (rotate ? sumsq / block : sumsq) / block;
+    double a = sqrt((double)target / m2);
+    a = fmin(fmax(a, 0x1p-126), 0x1p126);
+    float alpha2 = (float)a;
+    /* y = alpha H z / sqrt(B) = alpha w / sqrt(B) (rotated), alpha z (not rotated) */
+    double div = rotate ? rootB : 1.0;
+    float s2 = (float)((double)alpha2 * aw / div / Q);
+    for (int i = 0; i < block; ++i) {
+      double t = (double)alpha2 * w[i] / div / (double)s2;
+      if (quot) quot[k * block + i] = t;
+      qo[i] = code_encode(t, flags);
+    }
+    alpha_out[k] = alpha2;
+    scale_out[k] = s2;
+    free(w);
+  }
+  return TFP8_REF_OK;
+}

@@ -108,6 +108,21 @@ int tfp8_ref_reduce_rotated_ex(const uint8_t *codes, const float *alpha, const f
                                int64_t n, int block, float target, int flags, uint8_t *codes_out,
                                float *alpha_out, float *scale_out, double *quot);
 
+/* Local gradient accumulation ("AGoQ: Activation and Gradient Quantization for Memory-Efficient
+ * Distributed Training of LLMs", section 2.B): the compressed main gradient (codes, alpha, scale)
+ * is reconstructed, the dense local gradient grad[n] (bf16 bits or fp32) is added, and the sum is
+ * compressed again with the same block, target and flags.  By the definition (float64). */
+int tfp8_ref_accumulate_ex(const uint8_t *codes, const float *alpha, const float *scale,
+                           const void *grad, int grad_dtype, int64_t n, int block, float target,
+                           int flags, uint8_t *codes_out, float *alpha_out, float *scale_out,
+                           double *quot);
+/* The same sum formed in the rotated domain: H z = sqrt(B) (s/alpha) dec(q) + H g (unnormalised
+ * H), so only the dense gradient is transformed.  A second route used to cross-check the first. */
+int tfp8_ref_accumulate_rotated_ex(const uint8_t *codes, const float *alpha, const float *scale,
+                                   const void *grad, int grad_dtype, int64_t n, int block,
+                                   float target, int flags, uint8_t *codes_out, float *alpha_out,
+                                   float *scale_out, double *quot);
+
 /* Threads used by the block loops (OpenMP); returns the count in effect. */
 int tfp8_ref_set_threads(int threads);
 

@@ -57,6 +57,9 @@ MUTANTS = [
      "return tfp8_ref_e4m3_decode(code);", 0),
     ("compress ignores no-rotation", "if (!(flags & TFP8_REF_NO_ROTATION)) {\n    tfp8_ref_fwht(y, B);",
      "if (1) {\n    tfp8_ref_fwht(y, B);", 0),
+    ("accumulate drops the local gradient",
+     "for (int i = 0; i < block; ++i) z[i] += load_elem(grad, grad_dtype, k * block + i);", "", 0),
+    ("rotated accumulate drops sqrt(B)", "if (rotate) g *= rootB;", "", 0),
     ("decompress ignores no-rotation",
      "if (!(flags & TFP8_REF_NO_ROTATION)) {\n    tfp8_ref_fwht(out, B);",
      "if (1) {\n    tfp8_ref_fwht(out, B);", 0),
@@ -89,7 +92,8 @@ def _run_mutant(case, tmpdir):
     cmd = [sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
            os.path.join(ROOT, "tests", "test_oracle_codec.py"),
            os.path.join(ROOT, "tests", "test_oracle_method.py"),
-           os.path.join(ROOT, "tests", "test_oracle_variants.py")]
+           os.path.join(ROOT, "tests", "test_oracle_variants.py"),
+           os.path.join(ROOT, "tests", "test_oracle_accumulate.py")]
     r = subprocess.run(cmd, cwd=ROOT, env=env, capture_output=True, text=True, timeout=900)
     return name, r.returncode, r.stdout[-1500:]
 
