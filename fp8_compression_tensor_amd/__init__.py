@@ -20,7 +20,7 @@ import torch
 __all__ = [
     "compress", "decompress", "reduce_fp8", "compress_raw", "decompress_raw", "reduce_fp8_raw",
     "status_string", "lib", "LIB_PATH", "TFP8Error", "BF16", "F32", "SUPPORTED_BLOCKS",
-    "FLAG_INT8", "FLAG_NO_ROTATION",
+    "FLAG_INT8", "FLAG_NO_ROTATION", "accumulate", "accumulate_raw",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtfp8.so")
@@ -64,6 +64,8 @@ def lib() -> ctypes.CDLL:
         L.tfp8_decompress_ex.restype = i32
         L.tfp8_reduce_ex.argtypes = [vp, vp, vp, i32, i64, i32, f32, u32, vp, vp, vp, vp]
         L.tfp8_reduce_ex.restype = i32
+        L.tfp8_accumulate.argtypes = [vp, vp, vp, vp, i32, i64, i32, f32, u32, vp, vp, vp, vp]
+        L.tfp8_accumulate.restype = i32
         L.tfp8_status_string.argtypes = [i32]
         L.tfp8_status_string.restype = ctypes.c_char_p
         L.tfp8_version.argtypes = []
@@ -110,6 +112,13 @@ def reduce_fp8_raw(codes_ptr: int, alpha_ptr: int, scale_ptr: int, P: int, n: in
                                     codes_out_ptr, alpha_out_ptr, scale_out_ptr, stream)
     return lib().tfp8_reduce_fp8(codes_ptr, alpha_ptr, scale_ptr, P, n, block, target,
                                  codes_out_ptr, alpha_out_ptr, scale_out_ptr, stream)
+
+
+def accumulate_raw(codes_ptr: int, alpha_ptr: int, scale_ptr: int, grad_ptr: int, grad_dtype: int,
+                   n: int, block: int, target: float, codes_out_ptr: int, alpha_out_ptr: int,
+                   scale_out_ptr: int, stream: int = 0, flags: int = 0) -> int:
+    return lib().tfp8_accumulate(codes_ptr, alpha_ptr, scale_ptr, grad_ptr, grad_dtype, n, block,
+                                 target, flags, codes_out_ptr, alpha_out_ptr, scale_out_ptr, stream)
 
 
 # ---------------------------------------------------------------------------- tensor wrappers
@@ -183,3 +192,27 @@ def reduce_fp8(codes: torch.Tensor, alpha: torch.Tensor, scale: torch.Tensor, bl
                           float(target), codes_out.data_ptr(), alpha_out.data_ptr(),
                           scale_out.data_ptr(), _stream(codes), flags))
     return codes_out, alpha_out, scale_out
+
+
+def accumulate(codes: torch.Tensor, alpha: torch.Tensor, scale: torch.Tensor, grad: torch.Tensor,
+               block: int = 128, target: float = 1.0, out=None, flags: int = 0, inplace: bool = False):
+    """Compressed main gradient + dense local gradient (bfloat16 or float32, same numel) ->
+    compressed sum.  inplace=True overwrites (codes, alpha, scale) and returns them."""
+    _need_gpu(codes, alpha, scale, grad)
+    if grad.dtype == torch.bfloat16:
+        dt = BF16
+    elif grad.dtype == torch.float32:
+        dt = F32
+    else:
+        raise ValueError(f"unsupported gradient dtype {grad.dtype}")
+    n = codes.numel()
+    if grad.numel() != n:
+        raise ValueError("grad and codes must have the same number of elements")
+    if inplace:
+        out = (codes, alpha, scale)
+    elif out is None:
+        out = (torch.empty_like(codes), torch.empty_like(alpha), torch.empty_like(scale))
+    _check(accumulate_raw(codes.data_ptr(), alpha.data_ptr(), scale.data_ptr(), grad.data_ptr(), dt,
+                          n, block, float(target), out[0].data_ptr(), out[1].data_ptr(),
+                          out[2].data_ptr(), _stream(codes), flags))
+    return out

@@ -143,28 +143,87 @@ __device__ __forceinline__ void fwht_lanes8(float (&v)[N], int j) {
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// First butterfly of a bfloat16 pair straight from its packed dword: (lo + hi, lo - hi), with
-// v_dot2_f32_bf16 against (1, 1) and (1, -1).  Each product is exact; the sum is rounded
-// once (to within an ulp: the instruction does not round magnitude-disparate addends
-// exactly to nearest), and bfloat16 subnormals are kept.  Written as asm to get the
-// three-operand form with a zero addend (the compiler picks the accumulating form plus a
-// move that zeroes the accumulator).
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b) {
-  float r;
-  asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
-  return r;
-}
-
-__device__ __forceinline__ void bf16_pair_butterfly(uint32_t d, uint32_t ones, uint32_t plus_minus,
-                                                    float &sum, float &dif) {
-  sum = dot2_bf16(d, ones);
-  dif = dot2_bf16(d, plus_minus);
+// First butterfly of four packed bfloat16 pairs (one dword each): o[2q] = lo_q + hi_q and
+// o[2q + 1] = lo_q - hi_q, with v_dot2_f32_bf16 against (1, 1) and (1, -1).  Each product is
+// exact; the sum is rounded once (to within an ulp: the instruction does not round
+// magnitude-disparate addends exactly to nearest), and bfloat16 subnormals are kept.  Written
+// as asm to get the three-operand form with a zero addend (the compiler picks the accumulating
+// form plus a move that zeroes the accumulator).  A DOT result must wait three states before
+// another VALU instruction reads or overwrites it, and the compiler inserts those waits only
+// around DOT instructions it emits itself, so the block ends with them (and starts with two,
+// for inputs written just before).  Early-clobber outputs keep every result out of the
+// registers of the inputs that later instructions of the block still read.
+__device__ __forceinline__ void bf16_butterfly4(uint32_t d0, uint32_t d1, uint32_t d2, uint32_t d3,
+                                                uint32_t ones, uint32_t plus_minus, float *o) {
+  asm("s_nop 1\n\t"
+      "v_dot2_f32_bf16 %0, %8, %12, 0\n\t"
+      "v_dot2_f32_bf16 %1, %8, %13, 0\n\t"
+      "v_dot2_f32_bf16 %2, %9, %12, 0\n\t"
+      "v_dot2_f32_bf16 %3, %9, %13, 0\n\t"
+      "v_dot2_f32_bf16 %4, %10, %12, 0\n\t"
+      "v_dot2_f32_bf16 %5, %10, %13, 0\n\t"
+      "v_dot2_f32_bf16 %6, %11, %12, 0\n\t"
+      "v_dot2_f32_bf16 %7, %11, %13, 0\n\t"
+      "s_nop 2"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]),
+        "=&v"(o[6]), "=&v"(o[7])
+      : "v"(d0), "v"(d1), "v"(d2), "v"(d3), "v"(ones), "v"(plus_minus));
 }
 
 // acc + lo^2 + hi^2 of a packed bfloat16 pair (squares exact).
 __device__ __forceinline__ float bf16_pair_sumsq(uint32_t d, float acc) {
   const bf16x2 x = __builtin_bit_cast(bf16x2, d);
   return __builtin_amdgcn_fdot2_f32_bf16(x, x, acc, false);
+}
+
+// ---- float64 versions, for the rare blocks that need an exact transform ----------------------
+
+template <int CTRL>
+__device__ __forceinline__ double dpp64(double v) {
+  const unsigned long long u = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_mov_dpp((int)(u & 0xFFFFFFFFull), CTRL, 0xF, 0xF, true);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(u >> 32), CTRL, 0xF, 0xF, true);
+  return __longlong_as_double(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
+}
+
+template <int N>
+__device__ __forceinline__ void fwht_registers64(double (&v)[N]) {
+#pragma unroll
+  for (int h = 1; h < N; h <<= 1)
+#pragma unroll
+    for (int i = 0; i < N; i += 2 * h)
+#pragma unroll
+      for (int k = i; k < i + h; ++k) {
+        const double a = v[k], b = v[k + h];
+        v[k] = a + b;
+        v[k + h] = a - b;
+      }
+}
+
+// the same lane network as fwht_lanes8, on float64 values
+template <int N>
+__device__ __forceinline__ void fwht_lanes8_64(double (&v)[N], int j) {
+  const double s7 = (j & 4) ? -1.0 : 1.0;
+  const double s1 = (j & 1) ? -1.0 : 1.0;
+  const double s2 = (j & 2) ? -1.0 : 1.0;
+#pragma unroll
+  for (int r = 0; r < N; ++r) v[r] = fma(dpp64<kDppHalfMirror>(v[r]), s7, v[r]);
+#pragma unroll
+  for (int r = 0; r < N; ++r) v[r] = fma(dpp64<kDppXor1>(v[r]), s1, v[r]);
+#pragma unroll
+  for (int r = 0; r < N; ++r) v[r] = fma(dpp64<kDppXor2>(v[r]), s2, v[r]);
+}
+
+__device__ __forceinline__ double group8_max64(double v) {
+  v = fmax(v, dpp64<kDppXor1>(v));
+  v = fmax(v, dpp64<kDppXor2>(v));
+  return fmax(v, dpp64<kDppHalfMirror>(v));
+}
+
+__device__ __forceinline__ double group8_sum64(double v) {
+  v = v + dpp64<kDppXor1>(v);
+  v = v + dpp64<kDppXor2>(v);
+  return v + dpp64<kDppHalfMirror>(v);
 }
 
 // bfloat16 pair in one dword -> two floats (exact).
@@ -208,6 +267,7 @@ __device__ __forceinline__ void unpack_int8x4(uint32_t w, float &a, float &b, fl
 }
 
 __device__ __forceinline__ int exponent_of(float x) { return __builtin_amdgcn_frexp_expf(x); }
+__device__ __forceinline__ float mantissa_of(float x) { return __builtin_amdgcn_frexp_mantf(x); }
 __device__ __forceinline__ float scale2(float x, int k) { return __builtin_amdgcn_ldexpf(x, k); }
 
 }  // namespace tfp8

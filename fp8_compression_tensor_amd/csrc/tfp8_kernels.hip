@@ -201,16 +201,17 @@ __global__ __launch_bounds__(kThreads) void k_compress(const void *__restrict__ 
     float ss = 0.0f;
     if constexpr (!F32IN) {
 #pragma unroll
-      for (int g = 0; g < G; ++g)
+      for (int g = 0; g < G; ++g) {
+        const u32x4 d = cur.d[g];
+        if constexpr (ROT) {
+          bf16_butterfly4(d[0], d[1], d[2], d[3], ones, plus_minus, &v[8 * g]);
+        } else {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t d = cur.d[g][q];
-          if constexpr (ROT)
-            bf16_pair_butterfly(d, ones, plus_minus, v[8 * g + 2 * q], v[8 * g + 2 * q + 1]);
-          else
-            widen_bf16x2(d, v[8 * g + 2 * q], v[8 * g + 2 * q + 1]);
-          ss = bf16_pair_sumsq(d, ss);
+          for (int q = 0; q < 4; ++q) widen_bf16x2(d[q], v[8 * g + 2 * q], v[8 * g + 2 * q + 1]);
         }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) ss = bf16_pair_sumsq(d[q], ss);
+      }
       if constexpr (ROT) fwht_registers<N, 2>(v);
     } else {
 #pragma unroll
@@ -498,6 +499,188 @@ __global__ __launch_bounds__(kThreads) void k_reduce(const uint8_t *__restrict__
   }
 }
 
+// --------------------------------------------------------------------------------------------
+// K4: local gradient accumulation.  The compressed main gradient (codes, alpha, s) plus a dense
+// local gradient g, requantised.  In the rotated domain the main gradient needs no transform:
+// H xhat = sqrt(B) (s / alpha) dec(q) (H unnormalised, (H / sqrt(B))^2 = I), so
+//   w = H z = H g + sqrt(B) (s / alpha) dec(q),
+// and w is requantised exactly like compress requantises H x.  Same lane layout as compress;
+// each lane reads the main gradient's codes at the positions it will write, so the call may
+// work in place.
+
+template <int B, bool F32IN, int FLAGS>
+__global__ __launch_bounds__(kThreads) void k_accumulate(
+    const uint8_t *codes, const float *alpha, const float *scale, const void *__restrict__ grad,
+    int64_t nb, float TBB, float sqrtTBB, float gscale, double gscale64, float C, double Cd64,
+    float invC, uint8_t *codes_out, float *alpha_out, float *scale_out) {
+  constexpr int N = B / 8;
+  constexpr int G = N / 8;
+  constexpr bool ROT = !(FLAGS & kNoRotation);
+  constexpr float Q = qmax_of<FLAGS>();
+  const int lane = threadIdx.x & 63;
+  const int j = lane & 7;
+  const int bw = lane >> 3;
+  const int pj = ROT ? lane8_perm(j) : j;
+  const float sj = ROT ? lane8_sign(j) : 1.0f;
+  const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
+  const int64_t nwaves = ((int64_t)gridDim.x * kThreads) >> 6;
+  const int64_t ntiles = (nb + 7) >> 3;
+  const uint32_t ones = 0x3F803F80u, plus_minus = 0xBF803F80u;
+
+  for (int64_t tile = wave; tile < ntiles; tile += nwaves) {
+    const int64_t blk = tile * 8 + bw;
+    const bool active = blk < nb;
+    const int64_t cblk = active ? blk : nb - 1;  // groups past the end re-read the last block
+    CompressIn<B, F32IN> in;
+    load_compress_in<B, F32IN>(in, grad, cblk, j);
+    u32x2 qd[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) qd[g] = *(const u32x2 *)(codes + cblk * B + 64 * g + 8 * pj);
+    const float sp = scale[cblk], ap = alpha[cblk];
+
+    float v[N];
+    if constexpr (!F32IN) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const u32x4 d = in.d[g];
+        if constexpr (ROT) {
+          bf16_butterfly4(d[0], d[1], d[2], d[3], ones, plus_minus, &v[8 * g]);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) widen_bf16x2(d[q], v[8 * g + 2 * q], v[8 * g + 2 * q + 1]);
+        }
+      }
+      if constexpr (ROT) fwht_registers<N, 2>(v);
+    } else {
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          v[8 * g + q] = __uint_as_float(in.d[2 * g][q]);
+          v[8 * g + 4 + q] = __uint_as_float(in.d[2 * g + 1][q]);
+        }
+      if constexpr (ROT) fwht_registers<N, 1>(v);
+    }
+    if constexpr (ROT) fwht_lanes8<N>(v, j);  // lane j: sj * (H g) at positions 64g + 8 pj + e
+
+    float mh = 0.0f;  // largest |H g| of the block
+#pragma unroll
+    for (int r = 0; r < N; ++r) mh = fmaxf(mh, fabsf(v[r]));
+    mh = group_max<8>(mh);
+
+    // Add the main gradient in the same (signed, permuted) positions, with factor
+    // gscale * s / alpha.
+    const int es = exponent_of(sp), ea = exponent_of(ap);
+    const bool in_range = (sp == 0.0f) || (es - ea > -100 && es - ea < 100);
+    const float gm = (sp == 0.0f || !in_range) ? 0.0f : sj * (gscale * __fdiv_rn(sp, ap));
+    float d[N];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      decode4<FLAGS>(qd[g][0], d[8 * g + 0], d[8 * g + 1], d[8 * g + 2], d[8 * g + 3]);
+      decode4<FLAGS>(qd[g][1], d[8 * g + 4], d[8 * g + 5], d[8 * g + 6], d[8 * g + 7]);
+    }
+#pragma unroll
+    for (int r = 0; r < N; ++r) v[r] = fmaf(d[r], gm, v[r]);
+
+    float m = 0.0f;
+#pragma unroll
+    for (int r = 0; r < N; ++r) m = fmaxf(m, fabsf(v[r]));
+    const float M = group_max<8>(m);
+
+    // float32 keeps the energy and the peak to ~1e-7 unless the two terms cancel (the sum's
+    // peak under half the larger term's: about 1e-4 of the blocks of gradients with shared
+    // outlier channels) or s / alpha leaves the normal range (alpha clamped at 2^126 on a
+    // bfloat16-subnormal main block).  Those blocks are redone in float64, where the transform
+    // of a bfloat16 block is exact and the sum rounds once.
+    const bool exact64 = !in_range || M < 0.5f * fmaxf(mh, fabsf(gm) * Q);
+    float cm, a_out, s_out;
+    if (!exact64 && M >= 0x1p-40f && M <= 0x1p60f) {
+      // energy of z from the codes' values u = w c (Parseval): alpha = c sqrt(T B^2 / sum u^2)
+      const float c = __fdiv_rn(Q, M);
+      float su = 0.0f;
+#pragma unroll
+      for (int r = 0; r < N; ++r) {
+        const float u = v[r] * c;
+        su = fmaf(u, u, su);
+      }
+      const float SU = group_sum<8>(su);
+      a_out = fminf(fmaxf(c * sqrtTBB * __builtin_amdgcn_rsqf(SU), 0x1p-126f), 0x1p126f);
+      s_out = a_out * M * invC;
+      cm = c * sj;
+    } else if (!exact64) {
+      scales_exact<8, N>(v, M, 0, TBB, Q, C, sj, cm, a_out, s_out);
+    } else {
+      double w[N];
+      if constexpr (!F32IN) {
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float lo, hi;
+            widen_bf16x2(in.d[g][q], lo, hi);
+            w[8 * g + 2 * q] = lo;
+            w[8 * g + 2 * q + 1] = hi;
+          }
+      } else {
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            w[8 * g + q] = __uint_as_float(in.d[2 * g][q]);
+            w[8 * g + 4 + q] = __uint_as_float(in.d[2 * g + 1][q]);
+          }
+      }
+      if constexpr (ROT) {
+        fwht_registers64<N>(w);
+        fwht_lanes8_64<N>(w, j);
+      }
+      const double gm64 = (sp == 0.0f) ? 0.0 : sj * ((double)gscale64 * ((double)sp / (double)ap));
+      double m64 = 0.0, ss64 = 0.0;
+#pragma unroll
+      for (int r = 0; r < N; ++r) {
+        w[r] = fma((double)d[r], gm64, w[r]);
+        m64 = fmax(m64, fabs(w[r]));
+        ss64 = fma(w[r], w[r], ss64);
+      }
+      m64 = group8_max64(m64);
+      ss64 = group8_sum64(ss64);
+      if (m64 == 0.0) {
+        cm = 0.0f;
+        a_out = 1.0f;
+        s_out = 0.0f;
+#pragma unroll
+        for (int r = 0; r < N; ++r) v[r] = 0.0f;
+      } else {
+        // the codes' values: w / m64 in float32 after an exact power-of-two rescale
+        const int k = 1 - __builtin_amdgcn_frexp_exp(m64);
+#pragma unroll
+        for (int r = 0; r < N; ++r) v[r] = (float)__builtin_amdgcn_ldexp(w[r], k);
+        const float Mk = (float)__builtin_amdgcn_ldexp(m64, k);
+        cm = sj * __fdiv_rn(Q, Mk);
+        // alpha = sqrt(T B / sum z^2) with sum z^2 = sum w^2 / B (rotated) or sum w^2
+        const double a64 = sqrt((double)TBB / ss64);
+        a_out = (float)fmin(fmax(a64, 0x1p-126), 0x1p126);
+        s_out = (float)((double)a_out * m64 / (double)Cd64);
+      }
+    }
+
+    if (active) {
+      uint8_t *cb = codes_out + blk * B + 8 * pj;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        u32x2 w;
+        w[0] = encode4<FLAGS>(v[8 * g + 0], v[8 * g + 1], v[8 * g + 2], v[8 * g + 3], cm);
+        w[1] = encode4<FLAGS>(v[8 * g + 4], v[8 * g + 5], v[8 * g + 6], v[8 * g + 7], cm);
+        *(u32x2 *)(cb + 64 * g) = w;
+      }
+      if (j == 0) {
+        alpha_out[blk] = a_out;
+        scale_out[blk] = s_out;
+      }
+    }
+  }
+}
+
 }  // namespace tfp8
 
 // ============================================================================================
@@ -644,11 +827,43 @@ tfp8_status launch_reduce(const uint8_t *codes, const float *alpha, const float 
   return launched();
 }
 
+template <int B, bool F32, int FLAGS>
+void launch_accumulate_t(const uint8_t *codes, const float *alpha, const float *scale,
+                         const void *grad, int64_t nb, float target, uint8_t *codes_out,
+                         float *alpha_out, float *scale_out, hipStream_t st) {
+  constexpr bool ROT = !(FLAGS & kNoRotation);
+  const double Q = qmax_of<FLAGS>();
+  const float TBB = target * (float)B * (ROT ? (float)B : 1.0f);
+  const float sqrtTBB = (float)sqrt((double)target * B * (ROT ? B : 1));
+  const float gscale = ROT ? (float)sqrt((double)B) : 1.0f;
+  const double Cd = ROT ? Q * sqrt((double)B) : Q;
+  const float C = (float)Cd, invC = (float)(1.0 / Cd);
+  const unsigned grid = grid_for((nb + 7) / 8, TFP8_COMPRESS_WGS_PER_CU);
+  const double gscale64 = ROT ? sqrt((double)B) : 1.0;
+  hipLaunchKernelGGL((k_accumulate<B, F32, FLAGS>), dim3(grid), dim3(kThreads), 0, st, codes,
+                     alpha, scale, grad, nb, TBB, sqrtTBB, gscale, gscale64, C, Cd, invC,
+                     codes_out, alpha_out, scale_out);
+}
+
+template <int B, bool F32>
+tfp8_status launch_accumulate(const uint8_t *codes, const float *alpha, const float *scale,
+                              const void *grad, int64_t nb, float target, uint32_t flags,
+                              uint8_t *codes_out, float *alpha_out, float *scale_out,
+                              hipStream_t st) {
+  switch (flags) {
+    case 0: launch_accumulate_t<B, F32, 0>(codes, alpha, scale, grad, nb, target, codes_out, alpha_out, scale_out, st); break;
+    case kInt8: launch_accumulate_t<B, F32, kInt8>(codes, alpha, scale, grad, nb, target, codes_out, alpha_out, scale_out, st); break;
+    case kNoRotation: launch_accumulate_t<B, F32, kNoRotation>(codes, alpha, scale, grad, nb, target, codes_out, alpha_out, scale_out, st); break;
+    default: launch_accumulate_t<B, F32, kInt8 | kNoRotation>(codes, alpha, scale, grad, nb, target, codes_out, alpha_out, scale_out, st); break;
+  }
+  return launched();
+}
+
 }  // namespace
 
 extern "C" {
 
-int32_t tfp8_version(void) { return (1 << 16) | 1; }
+int32_t tfp8_version(void) { return (1 << 16) | 2; }
 
 const char *tfp8_status_string(tfp8_status status) {
   switch (status) {
@@ -776,6 +991,53 @@ tfp8_status tfp8_reduce_fp8(const uint8_t *codes, const float *alpha, const floa
                             float *alpha_out, float *scale_out, void *stream) {
   return tfp8_reduce_ex(codes, alpha, scale, P, n, block, target, 0, codes_out, alpha_out,
                         scale_out, stream);
+}
+
+tfp8_status tfp8_accumulate(const uint8_t *codes, const float *alpha, const float *scale,
+                            const void *grad, tfp8_dtype grad_dtype, int64_t n, int32_t block,
+                            float target, uint32_t flags, uint8_t *codes_out, float *alpha_out,
+                            float *scale_out, void *stream) {
+  if (!block_ok(block)) return TFP8_E_BLOCK;
+  if (n < 0 || n % block != 0) return TFP8_E_SIZE;
+  if (grad_dtype != TFP8_BF16 && grad_dtype != TFP8_F32) return TFP8_E_DTYPE;
+  if (!target_ok(target) || (flags & ~TFP8_FLAGS_ALL)) return TFP8_E_ARG;
+  if (n == 0) return TFP8_OK;
+  if (!codes || !alpha || !scale || !grad || !codes_out || !alpha_out || !scale_out)
+    return TFP8_E_NULL;
+  if (!aligned(codes, 16) || !aligned(codes_out, 16) || !aligned(grad, 16) || !aligned(alpha, 4) ||
+      !aligned(scale, 4) || !aligned(alpha_out, 4) || !aligned(scale_out, 4))
+    return TFP8_E_ALIGN;
+  const int64_t nb = n / block;
+  // In place is allowed: each output may be exactly its input.  Any other overlap is rejected.
+  const Range rq = range_of(codes, n), ra = range_of(alpha, nb * 4), rs = range_of(scale, nb * 4),
+              rg = range_of(grad, n * (grad_dtype == TFP8_F32 ? 4 : 2));
+  const Range oq = range_of(codes_out, n), oa = range_of(alpha_out, nb * 4),
+              os = range_of(scale_out, nb * 4);
+  const Range outs[3] = {oq, oa, os};
+  const Range same[3] = {rq, ra, rs};
+  const Range ins[4] = {rq, ra, rs, rg};
+  for (int i = 0; i < 3; ++i) {
+    for (int k = 0; k < 4; ++k)
+      if (overlap(outs[i], ins[k]) && !(k == i && outs[i].lo == same[i].lo)) return TFP8_E_ARG;
+    for (int k = i + 1; k < 3; ++k)
+      if (overlap(outs[i], outs[k])) return TFP8_E_ARG;
+  }
+  hipStream_t st = (hipStream_t)stream;
+  const bool f32 = grad_dtype == TFP8_F32;
+#define TFP8_CASE(BB)                                                                          \
+  case BB:                                                                                     \
+    return f32 ? launch_accumulate<BB, true>(codes, alpha, scale, grad, nb, target, flags,     \
+                                             codes_out, alpha_out, scale_out, st)              \
+               : launch_accumulate<BB, false>(codes, alpha, scale, grad, nb, target, flags,    \
+                                              codes_out, alpha_out, scale_out, st);
+  switch (block) {
+    TFP8_CASE(64)
+    TFP8_CASE(128)
+    TFP8_CASE(256)
+    TFP8_CASE(512)
+  }
+#undef TFP8_CASE
+  return TFP8_E_BLOCK;
 }
 
 }  // extern "C"

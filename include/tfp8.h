@@ -34,8 +34,8 @@
  *   - Element counts are 64-bit.  n = 0 is a no-op that returns TFP8_OK.
  *   - Supported block sizes: 64, 128, 256, 512.
  *   - Alignment: x, out and every codes pointer 16 bytes; alpha and scale 4 bytes.
- *   - Out-of-place only: an output range that overlaps an input range, or another output
- *     range, is rejected with TFP8_E_ARG.
+ *   - Out-of-place (except tfp8_accumulate, which may work in place): an output range that
+ *     overlaps an input range, or another output range, is rejected with TFP8_E_ARG.
  *   - target must be finite and within [2^-64, 2^64].
  *   - Inputs must be finite with |x| < 2^100; other values are outside the contract (no
  *     check, unspecified codes).
@@ -109,6 +109,21 @@ tfp8_status tfp8_decompress_ex(const uint8_t *codes, const float *alpha, const f
 tfp8_status tfp8_reduce_ex(const uint8_t *codes, const float *alpha, const float *scale, int32_t P,
                            int64_t n, int32_t block, float target, uint32_t flags,
                            uint8_t *codes_out, float *alpha_out, float *scale_out, void *stream);
+
+/* Local gradient accumulation: the compressed main gradient (codes[n], alpha[n/block],
+ * scale[n/block], as written by tfp8_compress_ex with the same flags) is dequantized, the dense
+ * local gradient grad[n] (bfloat16 or float32) is added, and the sum is requantized with the same
+ * block, target and flags into codes_out, alpha_out, scale_out.  Page "AGoQ: Activation and
+ * Gradient Quantization for Memory-Efficient Distributed Training of LLMs", section 2.B (local
+ * accumulation of FP8 gradients across micro-batches).  The sum is formed in float32 (the page
+ * names FP16/BF16 as its minimum precision), and in float64 for blocks where the two terms
+ * cancel to under half of the larger one or s/alpha leaves float32's normal range.  Unlike the other calls this one may work in place:
+ * each of codes_out, alpha_out, scale_out may be exactly its input (any other overlap is
+ * TFP8_E_ARG).  grad must be 16-byte aligned. */
+tfp8_status tfp8_accumulate(const uint8_t *codes, const float *alpha, const float *scale,
+                            const void *grad, tfp8_dtype grad_dtype, int64_t n, int32_t block,
+                            float target, uint32_t flags, uint8_t *codes_out, float *alpha_out,
+                            float *scale_out, void *stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char *tfp8_status_string(tfp8_status status);

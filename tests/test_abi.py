@@ -103,6 +103,24 @@ def test_reduce_argument_errors(tfp8):
     assert r(None, None, None, 4, 0, 128, 1.0, None, None, None) == 0
 
 
+def test_accumulate_argument_errors(tfp8):
+    a = tfp8.accumulate_raw
+    ins = (FAKE, FAKE + 8192, FAKE + 12288, FAKE + 16384)
+    outs = (FAKE + 32768, FAKE + 40960, FAKE + 45056)
+    assert a(*ins, 0, 1024, 96, 1.0, *outs) == -3
+    assert a(*ins, 0, 1000, 128, 1.0, *outs) == -2
+    assert a(*ins, 7, 1024, 128, 1.0, *outs) == -4
+    assert a(*ins, 0, 1024, 128, 0.0, *outs) == -6
+    assert a(*ins, 0, 1024, 128, 1.0, *outs, 0, 8) == -6
+    assert a(FAKE, FAKE + 8192, FAKE + 12288, None, 0, 1024, 128, 1.0, *outs) == -1
+    assert a(FAKE, FAKE + 8192, FAKE + 12288, FAKE + 16386, 0, 1024, 128, 1.0, *outs) == -5
+    # output codes over the gradient, or shifted into the input codes: rejected
+    assert a(*ins, 0, 1024, 128, 1.0, FAKE + 16384, outs[1], outs[2]) == -6
+    assert a(*ins, 0, 1024, 128, 1.0, FAKE + 16, outs[1], outs[2]) == -6
+    # exactly in place: accepted (n = 0 makes it a no-op, so nothing is launched)
+    assert a(*ins, 0, 0, 128, 1.0, FAKE, FAKE + 8192, FAKE + 12288) == 0
+
+
 def test_tensor_wrappers_refuse_cpu_tensors(tfp8):
     import torch
 

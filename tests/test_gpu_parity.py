@@ -293,3 +293,59 @@ def test_variant_reduce(oracle, tfp8, P, B, flags):
     q = np.stack([e[0] for e in enc]); a = np.stack([e[1] for e in enc]); s = np.stack([e[2] for e in enc])
     cq, ca, cs = check_reduce(oracle, tfp8, q, a, s, B, what=f"reduce P={P} B={B}", flags=flags)
     check_decompress(oracle, tfp8, cq, ca, cs, B, what=f"reduced P={P} B={B}", flags=flags)
+
+
+# ----------------------------------------------------------------------------- accumulate
+
+def _check_accumulate(oracle, tfp8, q, a, s, g, B, what, flags=0, inplace=False):
+    from tiecheck import FLAG_INT8, tie_cap
+
+    gg = bits_to_gpu(g) if g.dtype == np.uint16 else f32_to_gpu(g)
+    qg, ag, sg = u8_to_gpu(q), f32_to_gpu(a), f32_to_gpu(s)
+    cq, ca, cs = tfp8.accumulate(qg, ag, sg, gg, B, 1.0, flags=flags, inplace=inplace)
+    torch.cuda.synchronize()
+    if inplace:
+        assert cq.data_ptr() == qg.data_ptr()
+    cq, ca, cs = cpu(cq), cpu(ca), cpu(cs)
+    rq, ra, rs, rt = oracle.accumulate(q, a, s, g, B, 1.0, with_quot=True, flags=flags)
+    nmis = assert_codes_match(cq, rq, rt, max_frac=tie_cap(flags), what=what + " codes",
+                              int8=bool(flags & FLAG_INT8))
+    ea, es = assert_scales(ca, cs, ra, rs, what=what)
+    say(f"  {what}: n={q.size} B={B} flags={flags} inplace={inplace}: code tie mismatches {nmis} "
+        f"({nmis / q.size:.2e}), max rel err alpha {ea:.2e} scale {es:.2e}")
+    return cq, ca, cs
+
+
+def test_accumulate_gradient_workload(oracle, tfp8):
+    # the GPT-13B-shaped gradient workload: main gradient = shard 0 compressed, local = shard 1
+    cfg = CONFIGS[4]
+    B = cfg.block
+    x0, x1 = make_shard(4, 0).reshape(-1), make_shard(4, 1).reshape(-1)
+    q, a, s = oracle.compress(x0, B, 1.0)
+    _check_accumulate(oracle, tfp8, q, a, s, x1, B, "cfg4 accumulate")
+    _check_accumulate(oracle, tfp8, q, a, s, x1, B, "cfg4 accumulate in place", inplace=True)
+
+
+@pytest.mark.parametrize("flags", [0, 1, 2, 3])
+@pytest.mark.parametrize("B", [64, 128, 256, 512])
+@pytest.mark.parametrize("gdtype", ["bf16", "f32"])
+def test_accumulate_edges(oracle, tfp8, B, gdtype, flags):
+    rng = np.random.default_rng(B + flags)
+    main = np.concatenate([_special_blocks(B, rng), rng.laplace(0, 0.05, 3 * B)])
+    local = rng.laplace(0, 0.03, main.size)
+    local[:B] = 0                               # zero local gradient on a zero main block
+    local[2 * B:3 * B] = 0                      # zero local gradient on a nonzero block
+    local[5 * B:6 * B] *= 2.0 ** -130           # tiny local gradient on the subnormal block
+    xm = f32_to_bf16_bits(main.astype(np.float32))
+    q, a, s = oracle.compress(xm, B, 1.0, flags=flags)
+    g = f32_to_bf16_bits(local.astype(np.float32)) if gdtype == "bf16" else local.astype(np.float32)
+    _check_accumulate(oracle, tfp8, q, a, s, g, B, f"accumulate B={B} {gdtype}", flags=flags)
+
+
+def test_accumulate_zero_main_gradient_equals_compress(oracle, tfp8):
+    B, nb = 128, 77
+    g = random_bf16_bits(nb * B, seed=12, scale=0.2)
+    q = np.zeros(nb * B, np.uint8); a = np.ones(nb, np.float32); s = np.zeros(nb, np.float32)
+    cq, ca, cs = _check_accumulate(oracle, tfp8, q, a, s, g, B, "accumulate onto zero")
+    pq, pa, ps = check_compress(oracle, tfp8, g, B, what="compress of the same gradient")
+    assert np.array_equal(cq, pq)
