@@ -13,7 +13,9 @@ timed region starts.  `value` is the whole step's throughput in GB/s of bfloat16
 (8 x 117,440,512 x 2 bytes per step), from the wall clock around exactly K steps.  Per-kernel
 durations come from HIP events on the kernels' stream around every kernel of the timed steps.  `roofline` describes the dominant kernel (compress);
 `cpu_baseline` is the FP64 CPU oracle timed on this host over a bounded sample of the same
-pipeline.
+pipeline.  After the timed steps each kernel, and the local gradient accumulation (main
+gradient = compressed shard 0, local gradient = shard 1), is also timed over K back-to-back
+launches; those figures are reported beside the step and are not part of `value`.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
        python bench.py --copy-calibrate   (plain 1 GiB device copy, for HBM counter scaling)
@@ -228,6 +230,17 @@ def main():
            "reduce_fp8": round(per_launch_ms(k_reduce), 4),
            "decompress": round(per_launch_ms(k_decompress), 4)}
 
+    # Local gradient accumulation, measured on its own (not part of the step): main gradient =
+    # the compressed shard 0 (codes, alpha, s as left by the last compress), local gradient =
+    # shard 1 in bfloat16, sum requantised out of place into the reduce's output buffers.
+    def k_accumulate():
+        check(tfp8.accumulate_raw(codes.data_ptr(), alpha.data_ptr(), scale.data_ptr(),
+                                  x.data_ptr() + 2 * n, tfp8.BF16, n, B, TARGET, rcodes.data_ptr(),
+                                  ralpha.data_ptr(), rscale.data_ptr(), sh))
+
+    t_a = per_launch_ms(k_accumulate)
+    alg_a = n * (2 + 2 * (1 + 8.0 / B))          # grad in, codes + scales in and out
+
     bytes_in = P * n * 2
     value = bytes_in / (ms_step * 1e-3) / 1e9
     alg_c = P * n * (2 + 1 + 8.0 / B)            # compress: bf16 in, codes out, 2 fp32 per block
@@ -238,7 +251,7 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(ach_c, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach_c / HBM_PEAK_GBS, 4),
                 "traffic": (round(traffic / (t_c * 1e-3) / 1e9, 1) if traffic else None),
-                "kernel": "tfp8::k_compress<128, false>",
+                "kernel": "tfp8::k_compress<128, false, 0>",
                 "bytes_per_launch_algorithmic": int(alg_c),
                 "traffic_bytes_per_launch": (int(traffic) if traffic else None)}
     result = {
@@ -259,6 +272,13 @@ def main():
                           "hbm_frac_algorithmic": round(ach_c / HBM_PEAK_GBS, 4)},
         "reduce_hbm_frac_algorithmic": round(alg_r / (t_r * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "decompress_hbm_frac_algorithmic": round(alg_d / (t_d * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "accumulate": {"kernel": "tfp8::k_accumulate<128, false, 0>",
+                       "workload": "main gradient = compressed shard 0, local = bf16 shard 1, "
+                                   "[8,4096,3584], block 128, out of place",
+                       "ms_per_launch": round(t_a, 4),
+                       "bytes_per_launch_algorithmic": int(alg_a),
+                       "gbps_algorithmic": round(alg_a / (t_a * 1e-3) / 1e9, 1),
+                       "hbm_frac_algorithmic": round(alg_a / (t_a * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
     }
     del x, codes, out
     if not args.no_cpu_baseline:
