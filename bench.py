@@ -13,9 +13,10 @@ timed region starts.  `value` is the whole step's throughput in GB/s of bfloat16
 (8 x 117,440,512 x 2 bytes per step), from the wall clock around exactly K steps.  Per-kernel
 durations come from HIP events on the kernels' stream around every kernel of the timed steps.  `roofline` describes the dominant kernel (compress);
 `cpu_baseline` is the FP64 CPU oracle timed on this host over a bounded sample of the same
-pipeline.  After the timed steps each kernel, and the local gradient accumulation (main
-gradient = compressed shard 0, local gradient = shard 1), is also timed over K back-to-back
-launches; those figures are reported beside the step and are not part of `value`.
+pipeline.  After the timed steps each kernel is also timed over K back-to-back launches, and
+so is the local gradient accumulation on its own workload (GPT-13B-shaped gradients
+[4, 4096, 5120], block 128: main gradient = compressed shard 0, local gradient = shard 1);
+those figures are reported beside the step and are not part of `value`.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
        python bench.py --copy-calibrate   (plain 1 GiB device copy, for HBM counter scaling)
@@ -35,6 +36,7 @@ sys.path.insert(0, ROOT)
 METRIC = "fused FP8 ASH+DS compress GB/s (bf16 in) and % of MI355X HBM peak"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published peak
 CID = 5
+ACC_CID = 4  # GPT-13B-shaped gradients, for the local gradient accumulation
 TARGET = 1.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "compress_qwen7b_8shards_hbm_traffic.json")
 
@@ -148,6 +150,10 @@ def main():
     t0 = time.perf_counter()
     xs = make_shards(CID)  # host generation before the GPU is touched
     log(f"  done in {time.perf_counter() - t0:.1f} s")
+    # the local gradient accumulation's own workload: GPT-13B-shaped gradients, shard 0 as the
+    # main gradient (compressed on the GPU below) and shard 1 as the local gradient
+    gcfg = CONFIGS[ACC_CID]
+    gs = make_shards(ACC_CID, count=2)
 
     import numpy as np
     import torch
@@ -231,15 +237,24 @@ def main():
            "decompress": round(per_launch_ms(k_decompress), 4)}
 
     # Local gradient accumulation, measured on its own (not part of the step): main gradient =
-    # the compressed shard 0 (codes, alpha, s as left by the last compress), local gradient =
-    # shard 1 in bfloat16, sum requantised out of place into the reduce's output buffers.
+    # the compressed shard 0 of the gradient workload, local gradient = its shard 1 (bfloat16),
+    # sum requantised out of place.
+    gn, gB = gcfg.n, gcfg.block
+    g = torch.from_numpy(gs.reshape(-1).view(np.int16)).to(dev).view(torch.bfloat16)
+    gq = torch.empty(2 * gn, dtype=torch.uint8, device=dev)
+    ga = torch.empty(2 * gn // gB, dtype=torch.float32, device=dev)
+    gsc = torch.empty(2 * gn // gB, dtype=torch.float32, device=dev)
+    check(tfp8.compress_raw(g.data_ptr(), tfp8.BF16, gn, gB, TARGET, gq.data_ptr(), ga.data_ptr(),
+                            gsc.data_ptr(), sh))
+
     def k_accumulate():
-        check(tfp8.accumulate_raw(codes.data_ptr(), alpha.data_ptr(), scale.data_ptr(),
-                                  x.data_ptr() + 2 * n, tfp8.BF16, n, B, TARGET, rcodes.data_ptr(),
-                                  ralpha.data_ptr(), rscale.data_ptr(), sh))
+        check(tfp8.accumulate_raw(gq.data_ptr(), ga.data_ptr(), gsc.data_ptr(),
+                                  g.data_ptr() + 2 * gn, tfp8.BF16, gn, gB, TARGET,
+                                  gq.data_ptr() + gn, ga.data_ptr() + 4 * (gn // gB),
+                                  gsc.data_ptr() + 4 * (gn // gB), sh))
 
     t_a = per_launch_ms(k_accumulate)
-    alg_a = n * (2 + 2 * (1 + 8.0 / B))          # grad in, codes + scales in and out
+    alg_a = gn * (2 + 2 * (1 + 8.0 / gB))        # grad in, codes + scales in and out
 
     bytes_in = P * n * 2
     value = bytes_in / (ms_step * 1e-3) / 1e9
@@ -272,15 +287,16 @@ def main():
                           "hbm_frac_algorithmic": round(ach_c / HBM_PEAK_GBS, 4)},
         "reduce_hbm_frac_algorithmic": round(alg_r / (t_r * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "decompress_hbm_frac_algorithmic": round(alg_d / (t_d * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "accumulate": {"kernel": "tfp8::k_accumulate<128, false, 0>",
-                       "workload": "main gradient = compressed shard 0, local = bf16 shard 1, "
-                                   "[8,4096,3584], block 128, out of place",
+        "accumulate": {"kernel": "tfp8::k_accumulate<128, false, 0> + k_accumulate_fix",
+                       "workload": f"gpt-13b gradients {list(gcfg.shape)} bf16, block {gB}: "
+                                   "main gradient = compressed shard 0, local = shard 1, "
+                                   "out of place",
                        "ms_per_launch": round(t_a, 4),
                        "bytes_per_launch_algorithmic": int(alg_a),
                        "gbps_algorithmic": round(alg_a / (t_a * 1e-3) / 1e9, 1),
                        "hbm_frac_algorithmic": round(alg_a / (t_a * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
     }
-    del x, codes, out
+    del x, codes, out, g, gq
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
         result["cpu_baseline"] = cpu_baseline(xs)

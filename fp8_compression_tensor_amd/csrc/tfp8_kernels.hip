@@ -507,12 +507,22 @@ __global__ __launch_bounds__(kThreads) void k_reduce(const uint8_t *__restrict__
 // and w is requantised exactly like compress requantises H x.  Same lane layout as compress;
 // each lane reads the main gradient's codes at the positions it will write, so the call may
 // work in place.
+//
+// Two launches.  k_accumulate works in float32: its rounding errors are ~2^-24 of the larger
+// of the two terms (the float32 transform of g, the product with the factor), which keeps the
+// energy and the codes' values to the accuracy of compress as long as the terms do not cancel.
+// Where they do (the sum's peak under half the larger term's: about 1e-4 of the blocks of
+// independent gradients, but 15% of blocks that share outlier channels of random sign) it sets
+// the block aside: it writes only alpha_out = -alpha (alpha is otherwise positive), so the
+// block's inputs stay intact even in place.  k_accumulate_fix finds those blocks and redoes them
+// in float64, where the transform of a bfloat16 block is exact and the sum rounds once.  Keeping
+// the float64 code out of the streaming kernel halves its registers and doubles its occupancy.
 
 template <int B, bool F32IN, int FLAGS>
 __global__ __launch_bounds__(kThreads) void k_accumulate(
     const uint8_t *codes, const float *alpha, const float *scale, const void *__restrict__ grad,
-    int64_t nb, float TBB, float sqrtTBB, float gscale, double gscale64, float C, double Cd64,
-    float invC, uint8_t *codes_out, float *alpha_out, float *scale_out) {
+    int64_t nb, float TBB, float sqrtTBB, float gscale, float C, float invC, uint8_t *codes_out,
+    float *alpha_out, float *scale_out) {
   constexpr int N = B / 8;
   constexpr int G = N / 8;
   constexpr bool ROT = !(FLAGS & kNoRotation);
@@ -569,113 +579,215 @@ __global__ __launch_bounds__(kThreads) void k_accumulate(
     mh = group_max<8>(mh);
 
     // Add the main gradient in the same (signed, permuted) positions, with factor
-    // gscale * s / alpha.
+    // gscale * s / alpha.  Where s / alpha leaves float32's range (alpha clamped at 2^126 on a
+    // bfloat16-subnormal main block) both terms are carried as v * 2^E0, E0 the larger of their
+    // exponents (|gscale (s / alpha) dec| < 2^(es - ea + 15)), with the factor's mantissa and
+    // exponent apart.
     const int es = exponent_of(sp), ea = exponent_of(ap);
     const bool in_range = (sp == 0.0f) || (es - ea > -100 && es - ea < 100);
-    const float gm = (sp == 0.0f || !in_range) ? 0.0f : sj * (gscale * __fdiv_rn(sp, ap));
-    float d[N];
+    float gm;
+    int E0 = 0;
+    if (in_range) {
+      gm = (sp == 0.0f) ? 0.0f : sj * (gscale * __fdiv_rn(sp, ap));
+    } else {
+      E0 = max(mh == 0.0f ? -(1 << 20) : exponent_of(mh), es - ea + 15);
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      decode4<FLAGS>(qd[g][0], d[8 * g + 0], d[8 * g + 1], d[8 * g + 2], d[8 * g + 3]);
-      decode4<FLAGS>(qd[g][1], d[8 * g + 4], d[8 * g + 5], d[8 * g + 6], d[8 * g + 7]);
+      for (int r = 0; r < N; ++r) v[r] = scale2(v[r], -E0);
+      mh = scale2(mh, -E0);
+      gm = sj * scale2(gscale * __fdiv_rn(mantissa_of(sp), mantissa_of(ap)), es - ea - E0);
     }
 #pragma unroll
-    for (int r = 0; r < N; ++r) v[r] = fmaf(d[r], gm, v[r]);
+    for (int g = 0; g < G; ++g) {
+      float d[8];
+      decode4<FLAGS>(qd[g][0], d[0], d[1], d[2], d[3]);
+      decode4<FLAGS>(qd[g][1], d[4], d[5], d[6], d[7]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[8 * g + e] = fmaf(d[e], gm, v[8 * g + e]);
+    }
 
     float m = 0.0f;
 #pragma unroll
     for (int r = 0; r < N; ++r) m = fmaxf(m, fabsf(v[r]));
     const float M = group_max<8>(m);
 
-    // float32 keeps the energy and the peak to ~1e-7 unless the two terms cancel (the sum's
-    // peak under half the larger term's: about 1e-4 of the blocks of gradients with shared
-    // outlier channels) or s / alpha leaves the normal range (alpha clamped at 2^126 on a
-    // bfloat16-subnormal main block).  Those blocks are redone in float64, where the transform
-    // of a bfloat16 block is exact and the sum rounds once.
-    const bool exact64 = !in_range || M < 0.5f * fmaxf(mh, fabsf(gm) * Q);
-    float cm, a_out, s_out;
-    if (!exact64 && M >= 0x1p-40f && M <= 0x1p60f) {
-      // energy of z from the codes' values u = w c (Parseval): alpha = c sqrt(T B^2 / sum u^2)
-      const float c = __fdiv_rn(Q, M);
-      float su = 0.0f;
+    // float32 keeps w to ~2^-24 of the larger term; where the terms cancel that is too coarse
+    // (see above), and the block is left to k_accumulate_fix
+    const bool defer = M < 0.5f * fmaxf(mh, fabsf(gm) * Q);
+    float cm = 0.0f, a_out = 1.0f, s_out = 0.0f;
+    if (!defer) {
+      if (E0 == 0 && M >= 0x1p-40f && M <= 0x1p60f) {
+        // energy of z from the codes' values u = w c (Parseval): alpha = c sqrt(T B^2 / sum u^2)
+        const float c = __fdiv_rn(Q, M);
+        float su = 0.0f;
 #pragma unroll
-      for (int r = 0; r < N; ++r) {
-        const float u = v[r] * c;
-        su = fmaf(u, u, su);
-      }
-      const float SU = group_sum<8>(su);
-      a_out = fminf(fmaxf(c * sqrtTBB * __builtin_amdgcn_rsqf(SU), 0x1p-126f), 0x1p126f);
-      s_out = a_out * M * invC;
-      cm = c * sj;
-    } else if (!exact64) {
-      scales_exact<8, N>(v, M, 0, TBB, Q, C, sj, cm, a_out, s_out);
-    } else {
-      double w[N];
-      if constexpr (!F32IN) {
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            float lo, hi;
-            widen_bf16x2(in.d[g][q], lo, hi);
-            w[8 * g + 2 * q] = lo;
-            w[8 * g + 2 * q + 1] = hi;
-          }
+        for (int r = 0; r < N; ++r) {
+          const float u = v[r] * c;
+          su = fmaf(u, u, su);
+        }
+        const float SU = group_sum<8>(su);
+        a_out = fminf(fmaxf(c * sqrtTBB * __builtin_amdgcn_rsqf(SU), 0x1p-126f), 0x1p126f);
+        s_out = a_out * M * invC;
+        cm = c * sj;
       } else {
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            w[8 * g + q] = __uint_as_float(in.d[2 * g][q]);
-            w[8 * g + 4 + q] = __uint_as_float(in.d[2 * g + 1][q]);
-          }
-      }
-      if constexpr (ROT) {
-        fwht_registers64<N>(w);
-        fwht_lanes8_64<N>(w, j);
-      }
-      const double gm64 = (sp == 0.0f) ? 0.0 : sj * ((double)gscale64 * ((double)sp / (double)ap));
-      double m64 = 0.0, ss64 = 0.0;
-#pragma unroll
-      for (int r = 0; r < N; ++r) {
-        w[r] = fma((double)d[r], gm64, w[r]);
-        m64 = fmax(m64, fabs(w[r]));
-        ss64 = fma(w[r], w[r], ss64);
-      }
-      m64 = group8_max64(m64);
-      ss64 = group8_sum64(ss64);
-      if (m64 == 0.0) {
-        cm = 0.0f;
-        a_out = 1.0f;
-        s_out = 0.0f;
-#pragma unroll
-        for (int r = 0; r < N; ++r) v[r] = 0.0f;
-      } else {
-        // the codes' values: w / m64 in float32 after an exact power-of-two rescale
-        const int k = 1 - __builtin_amdgcn_frexp_exp(m64);
-#pragma unroll
-        for (int r = 0; r < N; ++r) v[r] = (float)__builtin_amdgcn_ldexp(w[r], k);
-        const float Mk = (float)__builtin_amdgcn_ldexp(m64, k);
-        cm = sj * __fdiv_rn(Q, Mk);
-        // alpha = sqrt(T B / sum z^2) with sum z^2 = sum w^2 / B (rotated) or sum w^2
-        const double a64 = sqrt((double)TBB / ss64);
-        a_out = (float)fmin(fmax(a64, 0x1p-126), 0x1p126);
-        s_out = (float)((double)a_out * m64 / (double)Cd64);
+        scales_exact<8, N>(v, M, E0, TBB, Q, C, sj, cm, a_out, s_out);
       }
     }
 
     if (active) {
-      uint8_t *cb = codes_out + blk * B + 8 * pj;
+      if (!defer) {
+        uint8_t *cb = codes_out + blk * B + 8 * pj;
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        u32x2 w;
-        w[0] = encode4<FLAGS>(v[8 * g + 0], v[8 * g + 1], v[8 * g + 2], v[8 * g + 3], cm);
-        w[1] = encode4<FLAGS>(v[8 * g + 4], v[8 * g + 5], v[8 * g + 6], v[8 * g + 7], cm);
-        *(u32x2 *)(cb + 64 * g) = w;
+        for (int g = 0; g < G; ++g) {
+          u32x2 w;
+          w[0] = encode4<FLAGS>(v[8 * g + 0], v[8 * g + 1], v[8 * g + 2], v[8 * g + 3], cm);
+          w[1] = encode4<FLAGS>(v[8 * g + 4], v[8 * g + 5], v[8 * g + 6], v[8 * g + 7], cm);
+          *(u32x2 *)(cb + 64 * g) = w;
+        }
+        if (j == 0) {
+          alpha_out[blk] = a_out;
+          scale_out[blk] = s_out;
+        }
+      } else if (j == 0) {
+        alpha_out[blk] = -ap;
       }
-      if (j == 0) {
-        alpha_out[blk] = a_out;
-        scale_out[blk] = s_out;
+    }
+  }
+}
+
+// One set-aside block in float64, by the group of eight lanes j = 0..7 that holds it (lane
+// layout of k_accumulate).  Its codes and s are still those of the main gradient (never
+// written) and alpha_out holds -alpha.  `active` = 0: work on the block but store nothing.
+template <int B, bool F32IN, int FLAGS>
+__device__ __forceinline__ void accumulate_block_f64(
+    const uint8_t *codes, const float *scale, const void *__restrict__ grad, int64_t blk,
+    bool active, int j, double TBB, double gscale, double Cd, uint8_t *codes_out,
+    float *alpha_out, float *scale_out) {
+  constexpr int N = B / 8;
+  constexpr int G = N / 8;
+  constexpr bool ROT = !(FLAGS & kNoRotation);
+  constexpr float Q = qmax_of<FLAGS>();
+  const int pj = ROT ? lane8_perm(j) : j;
+  const float sj = ROT ? lane8_sign(j) : 1.0f;
+
+  CompressIn<B, F32IN> in;
+  load_compress_in<B, F32IN>(in, grad, blk, j);
+  u32x2 qd[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) qd[g] = *(const u32x2 *)(codes + blk * B + 64 * g + 8 * pj);
+  const float sp = scale[blk], ap = -alpha_out[blk];
+
+  double w[N];
+  if constexpr (!F32IN) {
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float lo, hi;
+        widen_bf16x2(in.d[g][q], lo, hi);
+        w[8 * g + 2 * q] = lo;
+        w[8 * g + 2 * q + 1] = hi;
+      }
+  } else {
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        w[8 * g + q] = __uint_as_float(in.d[2 * g][q]);
+        w[8 * g + 4 + q] = __uint_as_float(in.d[2 * g + 1][q]);
+      }
+  }
+  if constexpr (ROT) {
+    fwht_registers64<N>(w);
+    fwht_lanes8_64<N>(w, j);  // lane j: sj * (H g) at positions 64g + 8 pj + e
+  }
+  const double gm = (sp == 0.0f) ? 0.0 : (double)sj * (gscale * ((double)sp / (double)ap));
+  double m64 = 0.0, ss64 = 0.0;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float d[8];
+    decode4<FLAGS>(qd[g][0], d[0], d[1], d[2], d[3]);
+    decode4<FLAGS>(qd[g][1], d[4], d[5], d[6], d[7]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const double x = fma((double)d[e], gm, w[8 * g + e]);
+      w[8 * g + e] = x;
+      m64 = fmax(m64, fabs(x));
+      ss64 = fma(x, x, ss64);
+    }
+  }
+  m64 = group8_max64(m64);
+  ss64 = group8_sum64(ss64);
+
+  float v[N], cm, a_out, s_out;
+  if (m64 == 0.0) {
+    cm = 0.0f;
+    a_out = 1.0f;
+    s_out = 0.0f;
+#pragma unroll
+    for (int r = 0; r < N; ++r) v[r] = 0.0f;
+  } else {
+    // the codes' values: w / max|w| in float32 after an exact power-of-two rescale
+    const int e2 = 1 - __builtin_amdgcn_frexp_exp(m64);
+#pragma unroll
+    for (int r = 0; r < N; ++r) v[r] = (float)__builtin_amdgcn_ldexp(w[r], e2);
+    cm = sj * __fdiv_rn(Q, (float)__builtin_amdgcn_ldexp(m64, e2));
+    // alpha = sqrt(T B / sum z^2), sum z^2 = sum w^2 / B (rotated) or sum w^2: TBB / sum w^2
+    const double a64 = sqrt(TBB / ss64);
+    a_out = (float)fmin(fmax(a64, 0x1p-126), 0x1p126);
+    s_out = (float)((double)a_out * m64 / Cd);
+  }
+  if (active) {
+    uint8_t *cb = codes_out + blk * B + 8 * pj;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      u32x2 q;
+      q[0] = encode4<FLAGS>(v[8 * g + 0], v[8 * g + 1], v[8 * g + 2], v[8 * g + 3], cm);
+      q[1] = encode4<FLAGS>(v[8 * g + 4], v[8 * g + 5], v[8 * g + 6], v[8 * g + 7], cm);
+      *(u32x2 *)(cb + 64 * g) = q;
+    }
+    if (j == 0) {
+      alpha_out[blk] = a_out;
+      scale_out[blk] = s_out;
+    }
+  }
+}
+
+// Finds the blocks k_accumulate set aside (alpha_out < 0) and redoes them in float64.  A
+// wavefront reads the alphas of kRuns x 64 consecutive blocks at once (kRuns loads in flight per
+// lane), then takes the runs of 64 in turn and works through each run's marked blocks eight at a
+// time, one group of eight lanes per block.
+template <int B, bool F32IN, int FLAGS>
+__global__ __launch_bounds__(kThreads) void k_accumulate_fix(
+    const uint8_t *codes, const float *scale, const void *__restrict__ grad, int64_t nb,
+    double TBB, double gscale, double Cd, uint8_t *codes_out, float *alpha_out, float *scale_out) {
+  constexpr int kRuns = 8;
+  const int lane = threadIdx.x & 63;
+  const int j = lane & 7;
+  const int bw = lane >> 3;
+  const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
+  const int64_t nwaves = ((int64_t)gridDim.x * kThreads) >> 6;
+  const int64_t nscan = (nb + 64 * kRuns - 1) / (64 * kRuns);
+
+  for (int64_t t = wave; t < nscan; t += nwaves) {
+    float am[kRuns];
+#pragma unroll
+    for (int run = 0; run < kRuns; ++run) {
+      const int64_t b = (t * kRuns + run) * 64 + lane;
+      am[run] = b < nb ? alpha_out[b] : 1.0f;
+    }
+    for (int run = 0; run < kRuns; ++run) {
+      const int64_t base = (t * kRuns + run) * 64;
+      uint64_t mask = __ballot(am[run] < 0.0f);
+      while (mask != 0) {
+        // group bw takes the bw-th remaining marked block; groups without one redo the first
+        // (their loads precede every store of the wavefront) and store nothing
+        uint64_t mine = mask;
+        for (int i = 0; i < bw; ++i) mine &= mine - 1;
+        const bool active = mine != 0;
+        const int64_t blk = base + __builtin_ctzll(active ? mine : mask);
+        for (int i = 0; i < 8; ++i) mask &= mask - 1;
+        accumulate_block_f64<B, F32IN, FLAGS>(codes, scale, grad, blk, active, j, TBB, gscale, Cd,
+                                              codes_out, alpha_out, scale_out);
       }
     }
   }
@@ -694,6 +806,9 @@ __global__ __launch_bounds__(kThreads) void k_accumulate(
 #endif
 #ifndef TFP8_REDUCE_WGS_PER_CU
 #define TFP8_REDUCE_WGS_PER_CU 32
+#endif
+#ifndef TFP8_ACCUMULATE_FIX_WGS_PER_CU
+#define TFP8_ACCUMULATE_FIX_WGS_PER_CU 0
 #endif
 
 namespace {
@@ -833,16 +948,20 @@ void launch_accumulate_t(const uint8_t *codes, const float *alpha, const float *
                          float *alpha_out, float *scale_out, hipStream_t st) {
   constexpr bool ROT = !(FLAGS & kNoRotation);
   const double Q = qmax_of<FLAGS>();
-  const float TBB = target * (float)B * (ROT ? (float)B : 1.0f);
-  const float sqrtTBB = (float)sqrt((double)target * B * (ROT ? B : 1));
-  const float gscale = ROT ? (float)sqrt((double)B) : 1.0f;
+  const double TBBd = (double)target * B * (ROT ? B : 1);  // exact: powers of two
+  const float TBB = (float)TBBd;
+  const float sqrtTBB = (float)sqrt(TBBd);
+  const double gscale = ROT ? sqrt((double)B) : 1.0;
   const double Cd = ROT ? Q * sqrt((double)B) : Q;
   const float C = (float)Cd, invC = (float)(1.0 / Cd);
   const unsigned grid = grid_for((nb + 7) / 8, TFP8_COMPRESS_WGS_PER_CU);
-  const double gscale64 = ROT ? sqrt((double)B) : 1.0;
   hipLaunchKernelGGL((k_accumulate<B, F32, FLAGS>), dim3(grid), dim3(kThreads), 0, st, codes,
-                     alpha, scale, grad, nb, TBB, sqrtTBB, gscale, gscale64, C, Cd, invC,
-                     codes_out, alpha_out, scale_out);
+                     alpha, scale, grad, nb, TBB, sqrtTBB, (float)gscale, C, invC, codes_out,
+                     alpha_out, scale_out);
+  // the set-aside blocks: codes and s from the inputs (untouched for them), -alpha from alpha_out
+  const unsigned grid_fix = grid_for((nb + 511) / 512, TFP8_ACCUMULATE_FIX_WGS_PER_CU);
+  hipLaunchKernelGGL((k_accumulate_fix<B, F32, FLAGS>), dim3(grid_fix), dim3(kThreads), 0, st,
+                     codes, scale, grad, nb, TBBd, gscale, Cd, codes_out, alpha_out, scale_out);
 }
 
 template <int B, bool F32>

@@ -342,6 +342,29 @@ def test_accumulate_edges(oracle, tfp8, B, gdtype, flags):
     _check_accumulate(oracle, tfp8, q, a, s, g, B, f"accumulate B={B} {gdtype}", flags=flags)
 
 
+@pytest.mark.parametrize("inplace", [False, True])
+@pytest.mark.parametrize("flags", [0, 1])
+@pytest.mark.parametrize("B,gdtype", [(128, "bf16"), (256, "f32"), (64, "bf16")])
+def test_accumulate_cancelling_blocks(oracle, tfp8, B, gdtype, flags, inplace):
+    # local gradient ~ minus the main gradient on most blocks, so that the sum is about the main
+    # gradient's quantisation error: those blocks take the float64 path, many per 64-block scan
+    # tile (more than eight, so the tile is worked through in several rounds), over several
+    # tiles and a ragged last one (nb = 3 * 64 + 11)
+    rng = np.random.default_rng(1000 + B + 7 * flags + inplace)
+    nb = 3 * 64 + 11
+    main = rng.laplace(0, 0.05, nb * B)
+    main[5 * B + 3] = 40.0                                   # one outlier block
+    xm = f32_to_bf16_bits(main.astype(np.float32))
+    q, a, s = oracle.compress(xm, B, 1.0, flags=flags)
+    local = -bf16_bits_to_f32(xm).astype(np.float64) + rng.normal(0, 1e-4, nb * B)
+    keep = rng.random(nb) < 0.25                             # blocks that do not cancel
+    keep[64:64 + 20] = False                                 # a tile with 20+ cancelling blocks
+    local.reshape(nb, B)[keep] = rng.laplace(0, 0.03, (int(keep.sum()), B))
+    g = f32_to_bf16_bits(local.astype(np.float32)) if gdtype == "bf16" else local.astype(np.float32)
+    _check_accumulate(oracle, tfp8, q, a, s, g, B, f"cancelling B={B} {gdtype}", flags=flags,
+                      inplace=inplace)
+
+
 def test_accumulate_zero_main_gradient_equals_compress(oracle, tfp8):
     B, nb = 128, 77
     g = random_bf16_bits(nb * B, seed=12, scale=0.2)

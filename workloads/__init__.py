@@ -200,16 +200,13 @@ def make_shard(cid: int, shard: int = 0) -> np.ndarray:
     return _MAKERS[cid](shard)
 
 
-def _make_one(args):
-    cid, p = args
-    return make_shard(cid, p)
-
-
 def make_shards(cid: int, count: int | None = None, workers: int | None = None) -> np.ndarray:
     """All P shards of a config stacked as [P, *shape] (shard p uses seed p).
 
-    Shards are independent, so they are drawn in a process pool of ``workers``
-    processes (default: up to 8, bounded by the CPUs this process may use)."""
+    Shards are independent, so they are drawn by a pool of ``workers`` threads (default: up to
+    8, bounded by the CPUs this process may use): numpy's bulk generators and array operations
+    release the GIL.  Threads rather than processes, so that nothing is forked (forking under a
+    profiler's injected runtime, or after the GPU runtime is up, is unsafe)."""
     cfg = CONFIGS[cid]
     P = cfg.shards if count is None else count
     if workers is None:
@@ -219,12 +216,13 @@ def make_shards(cid: int, count: int | None = None, workers: int | None = None) 
         for p in range(P):
             out[p] = make_shard(cid, p)
         return out
-    import multiprocessing as mp
+    from concurrent.futures import ThreadPoolExecutor
 
-    ctx = mp.get_context("fork")
-    with ctx.Pool(workers) as pool:
-        for p, arr in enumerate(pool.imap(_make_one, [(cid, p) for p in range(P)])):
-            out[p] = arr
+    def fill(p):
+        out[p] = make_shard(cid, p)
+
+    with ThreadPoolExecutor(workers) as ex:
+        list(ex.map(fill, range(P)))
     return out
 
 
