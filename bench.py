@@ -45,13 +45,13 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(csrc: str | None = None) -> str:
     """SHA-256 of the kernel sources with comments and whitespace removed, so that the counter
     record is tied to the code it measured and not to its comments."""
     import re
 
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "fp8_compression_tensor_amd", "csrc")
+    csrc = csrc or os.path.join(ROOT, "fp8_compression_tensor_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
         with open(os.path.join(csrc, name)) as f:
             text = f.read()
@@ -62,15 +62,15 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(launch_bytes_alg: float):
+def measured_traffic(path: str = TRAFFIC_FILE, csrc: str | None = None):
     """HBM bytes per compress launch from the committed rocprofv3 counter summary, scaled by
     the copy-kernel calibration it records; None if absent or taken on other kernel source."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha256") != kernel_source_hash():
+    if rec.get("kernel_source_sha256") != kernel_source_hash(csrc):
         return None
     return float(rec["fetch_bytes_per_launch"]) + float(rec["write_bytes_per_launch"])
 
@@ -262,7 +262,7 @@ def main():
     alg_r = (P + 1) * n * (1 + 8.0 / B)          # reduce: P code sets in, one out
     alg_d = n * (1 + 8.0 / B + 2)                # decompress: codes in, bf16 out
     ach_c = alg_c / (t_c * 1e-3) / 1e9
-    traffic = measured_traffic(alg_c)
+    traffic = measured_traffic()
     roofline = {"bound": "hbm", "achieved": round(ach_c, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach_c / HBM_PEAK_GBS, 4),
                 "traffic": (round(traffic / (t_c * 1e-3) / 1e9, 1) if traffic else None),
