@@ -23,10 +23,14 @@ pytestmark = pytest.mark.skipif(shutil.which("hipcc") is None, reason="hipcc not
 
 @pytest.fixture(scope="module")
 def kernels(tmp_path_factory):
-    import sys
+    import importlib.util
 
-    sys.path.insert(0, os.path.join(ROOT, "fp8_compression_tensor_amd"))
-    from build import HIPCC_FLAGS
+    # the library's build flags, loaded under a private name (no sys.path or module clash)
+    spec = importlib.util.spec_from_file_location(
+        "_tfp8_lib_build", os.path.join(ROOT, "fp8_compression_tensor_amd", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    HIPCC_FLAGS = mod.HIPCC_FLAGS
 
     out = str(tmp_path_factory.mktemp("asm") / "k.s")
     flags = [f for f in HIPCC_FLAGS if f not in ("-shared", "-fPIC")]
