@@ -12,8 +12,8 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import (DEV, assert_scales, bits_to_gpu, check_compress, check_decompress,
-                         check_reduce, cpu, f32_to_gpu, say, u8_to_gpu)
+from gpu_helpers import (DEV, assert_bf16_match, assert_scales, bits_to_gpu, check_compress,
+                         check_decompress, check_reduce, cpu, f32_to_gpu, say, u8_to_gpu)
 from tiecheck import assert_codes_match, assert_rel_close
 from workloads import (CONFIGS, bf16_bits_to_f32, f32_to_bf16_bits, make_shard, make_shards,
                        random_bf16_bits)
@@ -372,3 +372,75 @@ def test_accumulate_zero_main_gradient_equals_compress(oracle, tfp8):
     cq, ca, cs = _check_accumulate(oracle, tfp8, q, a, s, g, B, "accumulate onto zero")
     pq, pa, ps = check_compress(oracle, tfp8, g, B, what="compress of the same gradient")
     assert np.array_equal(cq, pq)
+
+
+def test_offsets_beyond_2_31_elements(oracle, tfp8):
+    # n = 513 * 2^22 > 2^31 elements: element indexes pass 2^31, bfloat16 byte offsets pass
+    # 2^32 and code byte offsets pass 2^31.  The input is one random tile of 2^22 elements in
+    # seven power-of-two scalings (tile t scaled by 2^((t mod 7) - 3)), so a read at an offset
+    # cut to 32 bits (512 tiles away) lands on a tile of another scale.  Each stage is fed the
+    # oracle's output of the stage before; outputs are compared on sampled blocks: both ends,
+    # the 128 blocks around element 2^31, and 2048 random blocks.
+    B, T, tile, ntiles = 128, 1.0, 1 << 22, 513
+    n, nb, shift = ntiles * tile, ntiles * tile // B, tile // B
+    base = bf16_bits_to_f32(random_bf16_bits(tile, seed=2031, scale=0.05))
+    variants = [f32_to_bf16_bits(base * np.float32(2.0 ** ((t % 7) - 3))) for t in range(7)]
+    x = np.empty(n, np.uint16)
+    for t in range(ntiles):
+        x[t * tile:(t + 1) * tile] = variants[t % 7]
+    b31 = (1 << 31) // B
+    rng = np.random.default_rng(2031)
+    idx = np.unique(np.concatenate([np.arange(64), np.arange(nb - 64, nb),
+                                    np.arange(b31 - 64, b31 + 64), rng.integers(0, nb, 2048)]))
+    idx_g = torch.from_numpy(idx).to(DEV)
+    prev = (idx - shift) % nb  # block k of a copy rolled by one tile holds block k - shift
+    blocks = lambda a, rows: np.ascontiguousarray(np.asarray(a).reshape(nb, -1)[rows]).reshape(-1)
+    say(f"  offsets: n = 2^31 + {n - (1 << 31)}, {idx.size} sampled blocks")
+
+    q_o, a_o, s_o = oracle.compress(x, B, T)  # every block: the later stages' input
+    xg = bits_to_gpu(x)
+
+    # compress
+    q, a, s = tfp8.compress(xg, B, T)
+    torch.cuda.synchronize()
+    rq, ra, rs, rt = oracle.compress(blocks(x, idx), B, T, with_quot=True)
+    nmis = assert_codes_match(cpu(q.view(nb, B)[idx_g]).reshape(-1), rq, rt, what="offsets compress")
+    assert_scales(cpu(a[idx_g]), cpu(s[idx_g]), ra, rs, what="offsets compress")
+    del q, a, s
+    say(f"  offsets compress: tie mismatches {nmis}")
+
+    # decompress of the oracle's codes
+    qg, ag, sg = u8_to_gpu(q_o), f32_to_gpu(a_o), f32_to_gpu(s_o)
+    out = tfp8.decompress(qg, ag, sg, B, torch.bfloat16)
+    torch.cuda.synchronize()
+    got = out.view(nb, B)[idx_g].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    del out
+    qi, ai, si = blocks(q_o, idx), a_o[idx], s_o[idx]
+    assert_bf16_match(got, oracle.decompress(qi, ai, si, B, np.uint16),
+                      oracle.decompress_f64(qi, ai, si, B), what="offsets decompress")
+
+    # reduce: contribution 0 = the oracle's codes, contribution 1 = the same rolled by one tile
+    sq = torch.empty((2, n), dtype=torch.uint8, device=DEV)
+    sa = torch.empty((2, nb), dtype=torch.float32, device=DEV)
+    ss = torch.empty((2, nb), dtype=torch.float32, device=DEV)
+    sq[0] = qg; sq[1, tile:] = qg[:-tile]; sq[1, :tile] = qg[-tile:]
+    for dst, src in ((sa, ag), (ss, sg)):
+        dst[0] = src; dst[1, shift:] = src[:-shift]; dst[1, :shift] = src[-shift:]
+    cq, ca, cs = tfp8.reduce_fp8(sq, sa, ss, B, T)
+    torch.cuda.synchronize()
+    del sq, sa, ss
+    rq, ra, rs, rt = oracle.reduce_fp8(np.stack([qi, blocks(q_o, prev)]),
+                                       np.stack([ai, a_o[prev]]), np.stack([si, s_o[prev]]), B, T,
+                                       with_quot=True)
+    assert_codes_match(cpu(cq.view(nb, B)[idx_g]).reshape(-1), rq, rt, what="offsets reduce")
+    assert_scales(cpu(ca[idx_g]), cpu(cs[idx_g]), ra, rs, what="offsets reduce")
+    del cq, ca, cs
+
+    # accumulate in place: main gradient = the oracle's codes, local gradient = x rolled by a tile
+    xr = torch.roll(xg, tile)
+    del xg
+    tfp8.accumulate(qg, ag, sg, xr, B, T, inplace=True)
+    torch.cuda.synchronize()
+    rq, ra, rs, rt = oracle.accumulate(qi, ai, si, blocks(x, prev), B, T, with_quot=True)
+    assert_codes_match(cpu(qg.view(nb, B)[idx_g]).reshape(-1), rq, rt, what="offsets accumulate")
+    assert_scales(cpu(ag[idx_g]), cpu(sg[idx_g]), ra, rs, what="offsets accumulate")
