@@ -20,6 +20,8 @@ those figures are reported beside the step and are not part of `value`.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
        python bench.py --copy-calibrate   (plain 1 GiB device copy, for HBM counter scaling)
+       python bench.py --all-configs      (every operation on every workload, warm and with the
+                                           caches flushed, beside a same-shape copy)
 """
 from __future__ import annotations
 
@@ -116,9 +118,169 @@ def cpu_baseline(xs, budget_s: float = 20.0):
     m = int(min(n_full // cfg_b, max(m, m * budget_s / max(t, 1e-3))))
     t = run(m)
     gbs = P * m * cfg_b * 2 / t / 1e9
+    # the same on one thread, over a sample of about budget_s / 4
+    oracle.set_threads(1)
+    m1 = 512
+    t1 = run(m1)
+    m1 = int(min(n_full // cfg_b, max(m1, m1 * budget_s / 4 / max(t1, 1e-3))))
+    t1 = run(m1)
+    oracle.set_threads(cores)
     return {"value": gbs, "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": f"first {m} blocks ({m * cfg_b} elements) of each of the {P} shards through "
-                      f"compress -> reduce_fp8 -> decompress(bf16), float64 oracle, {t:.1f} s wall"}
+                      f"compress -> reduce_fp8 -> decompress(bf16), float64 oracle, {t:.1f} s wall",
+            "single_thread_value": P * m1 * cfg_b * 2 / t1 / 1e9,
+            "single_thread_sample": f"first {m1} blocks of each shard, {t1:.1f} s wall",
+            "cpu_model": cpu_model()}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def all_configs(reps: int):
+    """Every operation on every workload, warm and with the caches flushed, beside a
+    same-shape copy; one JSON object on stdout, a table on stderr."""
+    import statistics
+
+    import numpy as np
+    import torch
+
+    from workloads import CONFIGS, make_shards
+
+    host = {}
+    for cid, cfg in CONFIGS.items():
+        host[cid] = make_shards(cid, count=max(cfg.shards, 2 if cid == 4 else 1))
+    log("inputs generated")
+
+    import fp8_compression_tensor_amd as tfp8
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB, > L2 + MALL
+
+    def check(st):
+        if st != 0:
+            raise RuntimeError(tfp8.status_string(st))
+
+    def timed(fn, flushed):
+        ts = []
+        for i in range(reps + 3):
+            if flushed:
+                flush.sum()  # reads 1 GiB: evicts the caches without leaving dirty lines
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            b.synchronize()
+            if i >= 3:
+                ts.append(a.elapsed_time(b) * 1e3)
+        return statistics.median(ts), min(ts)
+
+    rows = []
+
+    def measure(cid, op, fn, alg_bytes, elements, B, P, bf16_in=None, copy_fn=None):
+        wm, wn = timed(fn, False)
+        fm, fn_ = timed(fn, True)
+        row = {"config": cid, "op": op, "elements": elements, "block": B, "P": P,
+               "bytes_algorithmic": int(alg_bytes), "warm_us_median": round(wm, 2),
+               "warm_us_min": round(wn, 2), "flushed_us_median": round(fm, 2),
+               "flushed_us_min": round(fn_, 2),
+               "flushed_GBps": round(alg_bytes / (fm * 1e-6) / 1e9, 1),
+               "flushed_frac_of_peak": round(alg_bytes / (fm * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        if bf16_in is not None:
+            row["bf16_in_GBps_flushed"] = round(bf16_in / (fm * 1e-6) / 1e9, 1)
+        if copy_fn is not None:
+            cfn, cbytes = copy_fn
+            cm, _ = timed(cfn, True)
+            row["copy_GBps_flushed"] = round(cbytes / (cm * 1e-6) / 1e9, 1)
+            row["ratio_to_copy"] = round(row["flushed_GBps"] / row["copy_GBps_flushed"], 4)
+        rows.append(row)
+        log(f"cfg {cid} {op:28s} n={elements:>10d} B={B} P={P}: warm {wm:9.1f} us, flushed "
+            f"{fm:9.1f} us = {row['flushed_GBps']:7.1f} GB/s ({100 * row['flushed_frac_of_peak']:.1f}%)"
+            + (f", vs 2:1 add {row['copy_GBps_flushed']:.0f} GB/s: {row['ratio_to_copy']:.3f}"
+               if copy_fn is not None else ""))
+
+    for cid, cfg in CONFIGS.items():
+        B, P, n = cfg.block, cfg.shards, cfg.n
+        nb = n // B
+        xs = host[cid]
+        x = torch.from_numpy(xs.reshape(-1).view(np.int16)).to(dev)
+        xb = x.view(torch.bfloat16)
+        ntot = P * n
+        q = torch.empty(max(ntot, n), dtype=torch.uint8, device=dev)
+        al = torch.empty(max(ntot, n) // B, dtype=torch.float32, device=dev)
+        sc = torch.empty_like(al)
+        ya = torch.empty(ntot, dtype=torch.int16, device=dev).fill_(3)
+        yc = torch.empty(ntot, dtype=torch.int16, device=dev)
+
+        def comp(m):
+            return lambda: check(tfp8.compress_raw(xb.data_ptr(), tfp8.BF16, m, B, TARGET,
+                                                   q.data_ptr(), al.data_ptr(), sc.data_ptr(),
+                                                   stream.cuda_stream))
+
+        def copy(m):
+            # a same-ratio reference: two int16 reads and one int16 write per element
+            return (lambda: torch.add(x[:m], ya[:m], out=yc[:m])), 6 * m
+
+        measure(cid, "compress", comp(n), n * (3 + 8 / B), n, B, 1, 2 * n, copy(n))
+        if P > 1:
+            measure(cid, f"compress {P} stacked shards", comp(ntot), ntot * (3 + 8 / B), ntot, B,
+                    P, 2 * ntot, copy(ntot))
+        comp(ntot)()  # codes of every shard, for the stages below
+        for dt, name, ob in ((torch.bfloat16, "decompress bf16", 2), (torch.float32,
+                                                                      "decompress fp32", 4)):
+            out = torch.empty(n, dtype=dt, device=dev)
+            code = tfp8.BF16 if dt == torch.bfloat16 else tfp8.F32
+            fn = (lambda out=out, code=code: check(tfp8.decompress_raw(
+                q.data_ptr(), al.data_ptr(), sc.data_ptr(), n, B, out.data_ptr(), code,
+                stream.cuda_stream)))
+            measure(cid, name, fn, n * (1 + 8 / B + ob), n, B, 1)
+            del out
+        if P > 1:
+            rq = torch.empty(n, dtype=torch.uint8, device=dev)
+            ra = torch.empty(nb, dtype=torch.float32, device=dev)
+            rs = torch.empty_like(ra)
+            fn = lambda: check(tfp8.reduce_fp8_raw(q.data_ptr(), al.data_ptr(), sc.data_ptr(), P,
+                                                   n, B, TARGET, rq.data_ptr(), ra.data_ptr(),
+                                                   rs.data_ptr(), stream.cuda_stream))
+            measure(cid, f"reduce P={P}, {P} x n", fn, (P + 1) * n * (1 + 8 / B), n, B, P)
+            # one rank's share in a P-way reduce-scatter: chunk 0 of every shard, n/P each
+            c = n // P
+            cq = q[:ntot].view(P, n)[:, :c].contiguous()
+            ca = al[:ntot // B].view(P, nb)[:, :c // B].contiguous()
+            cs = sc[:ntot // B].view(P, nb)[:, :c // B].contiguous()
+            fn = lambda: check(tfp8.reduce_fp8_raw(cq.data_ptr(), ca.data_ptr(), cs.data_ptr(), P,
+                                                   c, B, TARGET, rq.data_ptr(), ra.data_ptr(),
+                                                   rs.data_ptr(), stream.cuda_stream))
+            measure(cid, f"reduce P={P}, {P} x n/{P} (one rank)", fn, (P + 1) * c * (1 + 8 / B),
+                    c, B, P)
+            del rq, ra, rs, cq, ca, cs
+        if cid == 4:
+            # gradient accumulation: main = compressed shard 0, local = shard 1
+            comp(n)()
+            oq = torch.empty(n, dtype=torch.uint8, device=dev)
+            oa = torch.empty(nb, dtype=torch.float32, device=dev)
+            os_ = torch.empty_like(oa)
+            fn = lambda: check(tfp8.accumulate_raw(q.data_ptr(), al.data_ptr(), sc.data_ptr(),
+                                                   xb.data_ptr() + 2 * n, tfp8.BF16, n, B,
+                                                   TARGET, oq.data_ptr(), oa.data_ptr(),
+                                                   os_.data_ptr(), stream.cuda_stream))
+            measure(cid, "accumulate (main + local)", fn, n * (4 + 16 / B), n, B, 1)
+            del oq, oa, os_
+        del x, xb, q, al, sc, ya, yc
+        torch.cuda.empty_cache()
+    print(json.dumps({"mode": "all-configs", "reps": reps, "peak_GBps": HBM_PEAK_GBS,
+                      "copy": "torch.add of two int16 tensors into a third, same element count "
+                              "(read:write 2:1 as compress), flushed; ratio = GB/s over its GB/s",
+                      "flush": "a 1 GiB read (sum) between launches",
+                      "rows": rows}), flush=True)
 
 
 def main():
@@ -131,6 +293,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibrate", action="store_true")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="time every operation on every workload, warm and flushed (own JSON)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -140,6 +304,9 @@ def main():
 
     if args.copy_calibrate:
         copy_calibrate(max(args.steps, 1))
+        return
+    if args.all_configs:
+        all_configs(max(min(args.steps, 50), 5))
         return
 
     from workloads import CONFIGS, make_shards
