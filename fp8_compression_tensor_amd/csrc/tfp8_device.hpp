@@ -176,56 +176,6 @@ __device__ __forceinline__ float bf16_pair_sumsq(uint32_t d, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(x, x, acc, false);
 }
 
-// ---- float64 versions, for the rare blocks that need an exact transform ----------------------
-
-template <int CTRL>
-__device__ __forceinline__ double dpp64(double v) {
-  const unsigned long long u = __double_as_longlong(v);
-  const int lo = __builtin_amdgcn_mov_dpp((int)(u & 0xFFFFFFFFull), CTRL, 0xF, 0xF, true);
-  const int hi = __builtin_amdgcn_mov_dpp((int)(u >> 32), CTRL, 0xF, 0xF, true);
-  return __longlong_as_double(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
-}
-
-template <int N>
-__device__ __forceinline__ void fwht_registers64(double (&v)[N]) {
-#pragma unroll
-  for (int h = 1; h < N; h <<= 1)
-#pragma unroll
-    for (int i = 0; i < N; i += 2 * h)
-#pragma unroll
-      for (int k = i; k < i + h; ++k) {
-        const double a = v[k], b = v[k + h];
-        v[k] = a + b;
-        v[k + h] = a - b;
-      }
-}
-
-// the same lane network as fwht_lanes8, on float64 values
-template <int N>
-__device__ __forceinline__ void fwht_lanes8_64(double (&v)[N], int j) {
-  const double s7 = (j & 4) ? -1.0 : 1.0;
-  const double s1 = (j & 1) ? -1.0 : 1.0;
-  const double s2 = (j & 2) ? -1.0 : 1.0;
-#pragma unroll
-  for (int r = 0; r < N; ++r) v[r] = fma(dpp64<kDppHalfMirror>(v[r]), s7, v[r]);
-#pragma unroll
-  for (int r = 0; r < N; ++r) v[r] = fma(dpp64<kDppXor1>(v[r]), s1, v[r]);
-#pragma unroll
-  for (int r = 0; r < N; ++r) v[r] = fma(dpp64<kDppXor2>(v[r]), s2, v[r]);
-}
-
-__device__ __forceinline__ double group8_max64(double v) {
-  v = fmax(v, dpp64<kDppXor1>(v));
-  v = fmax(v, dpp64<kDppXor2>(v));
-  return fmax(v, dpp64<kDppHalfMirror>(v));
-}
-
-__device__ __forceinline__ double group8_sum64(double v) {
-  v = v + dpp64<kDppXor1>(v);
-  v = v + dpp64<kDppXor2>(v);
-  return v + dpp64<kDppHalfMirror>(v);
-}
-
 // bfloat16 pair in one dword -> two floats (exact).
 __device__ __forceinline__ void widen_bf16x2(uint32_t d, float &lo, float &hi) {
   lo = __uint_as_float(d << 16);

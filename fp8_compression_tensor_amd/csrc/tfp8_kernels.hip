@@ -515,8 +515,8 @@ __global__ __launch_bounds__(kThreads) void k_reduce(const uint8_t *__restrict__
 // independent gradients, but 15% of blocks that share outlier channels of random sign) it sets
 // the block aside: it writes only alpha_out = -alpha (alpha is otherwise positive), so the
 // block's inputs stay intact even in place.  k_accumulate_fix finds those blocks and redoes them
-// in float64, where the transform of a bfloat16 block is exact and the sum rounds once.  Keeping
-// the float64 code out of the streaming kernel halves its registers and doubles its occupancy.
+// with an exact split of the transform (below).  Keeping that code out of the streaming kernel
+// keeps the streaming kernel's registers, and so its occupancy, at those of compress.
 
 template <int B, bool F32IN, int FLAGS>
 __global__ __launch_bounds__(kThreads) void k_accumulate(
@@ -654,18 +654,27 @@ __global__ __launch_bounds__(kThreads) void k_accumulate(
   }
 }
 
-// One set-aside block in float64, by the group of eight lanes j = 0..7 that holds it (lane
-// layout of k_accumulate).  Its codes and s are still those of the main gradient (never
-// written) and alpha_out holds -alpha.  `active` = 0: work on the block but store nothing.
+// One set-aside block, by the group of eight lanes j = 0..7 that holds it (lane layout of
+// k_accumulate).  Its codes and s are still those of the main gradient (never written) and
+// alpha_out holds -alpha.  `active` = 0: work on the block but store nothing.
+//
+// Exact where the terms cancel, in float32.  g is scaled by 2^(K - E), E bounding the exponents
+// of both terms, and split into integers r = rint(t) and remainders l = t - r in [-1/2, 1/2].
+// |r| <= 2^K with K = 24 - log2(B), so every partial sum of H r is an integer of at most 2^24
+// and the transform of r is exact; the transform of l errs by ~2^-18 of 2^K at most.  The main
+// term is added to H r by one FMA with the high part of its factor (the product is exact, so the
+// cancellation happens inside the FMA and the sum rounds once), then its low part and H l.
 template <int B, bool F32IN, int FLAGS>
-__device__ __forceinline__ void accumulate_block_f64(
+__device__ __forceinline__ void accumulate_block_split(
     const uint8_t *codes, const float *scale, const void *__restrict__ grad, int64_t blk,
-    bool active, int j, double TBB, double gscale, double Cd, uint8_t *codes_out,
-    float *alpha_out, float *scale_out) {
+    bool active, int j, float TBB, float C, double gscale, uint8_t *codes_out, float *alpha_out,
+    float *scale_out) {
   constexpr int N = B / 8;
   constexpr int G = N / 8;
   constexpr bool ROT = !(FLAGS & kNoRotation);
   constexpr float Q = qmax_of<FLAGS>();
+  constexpr int K = 24 - (B == 64 ? 6 : B == 128 ? 7 : B == 256 ? 8 : 9);
+  constexpr int kNone = -(1 << 20);
   const int pj = ROT ? lane8_perm(j) : j;
   const float sj = ROT ? lane8_sign(j) : 1.0f;
 
@@ -676,32 +685,44 @@ __device__ __forceinline__ void accumulate_block_f64(
   for (int g = 0; g < G; ++g) qd[g] = *(const u32x2 *)(codes + blk * B + 64 * g + 8 * pj);
   const float sp = scale[blk], ap = -alpha_out[blk];
 
-  double w[N];
+  float r[N], l[N];
   if constexpr (!F32IN) {
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float lo, hi;
-        widen_bf16x2(in.d[g][q], lo, hi);
-        w[8 * g + 2 * q] = lo;
-        w[8 * g + 2 * q + 1] = hi;
-      }
+      for (int q = 0; q < 4; ++q) widen_bf16x2(in.d[g][q], r[8 * g + 2 * q], r[8 * g + 2 * q + 1]);
   } else {
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        w[8 * g + q] = __uint_as_float(in.d[2 * g][q]);
-        w[8 * g + 4 + q] = __uint_as_float(in.d[2 * g + 1][q]);
+        r[8 * g + q] = __uint_as_float(in.d[2 * g][q]);
+        r[8 * g + 4 + q] = __uint_as_float(in.d[2 * g + 1][q]);
       }
   }
-  if constexpr (ROT) {
-    fwht_registers64<N>(w);
-    fwht_lanes8_64<N>(w, j);  // lane j: sj * (H g) at positions 64g + 8 pj + e
+  float mg = 0.0f;
+#pragma unroll
+  for (int i = 0; i < N; ++i) mg = fmaxf(mg, fabsf(r[i]));
+  mg = group_max<8>(mg);
+  // the main term's factor sj * gscale * s / alpha; |factor * dec| <= |factor| * Q
+  const double f = (sp == 0.0f) ? 0.0 : (double)sj * (gscale * ((double)sp / (double)ap));
+  const int Eg = (mg == 0.0f) ? kNone : exponent_of(mg);
+  const int Ef = (f == 0.0) ? kNone : __builtin_amdgcn_frexp_exp(fabs(f) * (double)Q);
+  const int E = max(Eg, Ef) == kNone ? 0 : max(Eg, Ef);  // |g|, |main term| < 2^E
+  const double ft = __builtin_amdgcn_ldexp(f, K - E);
+  const float hi = (float)ft, lo = (float)(ft - (double)hi);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const float t = scale2(r[i], K - E);
+    r[i] = __builtin_rintf(t);
+    l[i] = t - r[i];
   }
-  const double gm = (sp == 0.0f) ? 0.0 : (double)sj * (gscale * ((double)sp / (double)ap));
-  double m64 = 0.0, ss64 = 0.0;
+  if constexpr (ROT) {
+    fwht_registers<N, 1>(r);
+    fwht_lanes8<N>(r, j);  // lane j: sj * (H r) at positions 64g + 8 pj + e
+    fwht_registers<N, 1>(l);
+    fwht_lanes8<N>(l, j);
+  }
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     float d[8];
@@ -709,40 +730,24 @@ __device__ __forceinline__ void accumulate_block_f64(
     decode4<FLAGS>(qd[g][1], d[4], d[5], d[6], d[7]);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const double x = fma((double)d[e], gm, w[8 * g + e]);
-      w[8 * g + e] = x;
-      m64 = fmax(m64, fabs(x));
-      ss64 = fma(x, x, ss64);
+      float w = fmaf(d[e], hi, r[8 * g + e]);
+      w = fmaf(d[e], lo, w);
+      r[8 * g + e] = w + l[8 * g + e];
     }
   }
-  m64 = group8_max64(m64);
-  ss64 = group8_sum64(ss64);
-
-  float v[N], cm, a_out, s_out;
-  if (m64 == 0.0) {
-    cm = 0.0f;
-    a_out = 1.0f;
-    s_out = 0.0f;
+  float m = 0.0f;
 #pragma unroll
-    for (int r = 0; r < N; ++r) v[r] = 0.0f;
-  } else {
-    // the codes' values: w / max|w| in float32 after an exact power-of-two rescale
-    const int e2 = 1 - __builtin_amdgcn_frexp_exp(m64);
-#pragma unroll
-    for (int r = 0; r < N; ++r) v[r] = (float)__builtin_amdgcn_ldexp(w[r], e2);
-    cm = sj * __fdiv_rn(Q, (float)__builtin_amdgcn_ldexp(m64, e2));
-    // alpha = sqrt(T B / sum z^2), sum z^2 = sum w^2 / B (rotated) or sum w^2: TBB / sum w^2
-    const double a64 = sqrt(TBB / ss64);
-    a_out = (float)fmin(fmax(a64, 0x1p-126), 0x1p126);
-    s_out = (float)((double)a_out * m64 / Cd);
-  }
+  for (int i = 0; i < N; ++i) m = fmaxf(m, fabsf(r[i]));
+  const float M = group_max<8>(m);
+  float cm, a_out, s_out;
+  scales_exact<8, N>(r, M, E - K, TBB, Q, C, sj, cm, a_out, s_out);
   if (active) {
     uint8_t *cb = codes_out + blk * B + 8 * pj;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       u32x2 q;
-      q[0] = encode4<FLAGS>(v[8 * g + 0], v[8 * g + 1], v[8 * g + 2], v[8 * g + 3], cm);
-      q[1] = encode4<FLAGS>(v[8 * g + 4], v[8 * g + 5], v[8 * g + 6], v[8 * g + 7], cm);
+      q[0] = encode4<FLAGS>(r[8 * g + 0], r[8 * g + 1], r[8 * g + 2], r[8 * g + 3], cm);
+      q[1] = encode4<FLAGS>(r[8 * g + 4], r[8 * g + 5], r[8 * g + 6], r[8 * g + 7], cm);
       *(u32x2 *)(cb + 64 * g) = q;
     }
     if (j == 0) {
@@ -752,15 +757,15 @@ __device__ __forceinline__ void accumulate_block_f64(
   }
 }
 
-// Finds the blocks k_accumulate set aside (alpha_out < 0) and redoes them in float64.  A
-// wavefront reads the alphas of kRuns x 64 consecutive blocks at once (kRuns loads in flight per
-// lane), then takes the runs of 64 in turn and works through each run's marked blocks eight at a
-// time, one group of eight lanes per block.
+// Finds the blocks k_accumulate set aside (alpha_out < 0) and redoes them.  A wavefront reads the
+// alphas of kRuns x 64 consecutive blocks at once (kRuns loads in flight per lane), then takes
+// the runs of 64 in turn and works through each run's marked blocks eight at a time, one group
+// of eight lanes per block.
 template <int B, bool F32IN, int FLAGS>
 __global__ __launch_bounds__(kThreads) void k_accumulate_fix(
     const uint8_t *codes, const float *scale, const void *__restrict__ grad, int64_t nb,
-    double TBB, double gscale, double Cd, uint8_t *codes_out, float *alpha_out, float *scale_out) {
-  constexpr int kRuns = 8;
+    float TBB, float C, double gscale, uint8_t *codes_out, float *alpha_out, float *scale_out) {
+  constexpr int kRuns = 2;
   const int lane = threadIdx.x & 63;
   const int j = lane & 7;
   const int bw = lane >> 3;
@@ -786,8 +791,8 @@ __global__ __launch_bounds__(kThreads) void k_accumulate_fix(
         const bool active = mine != 0;
         const int64_t blk = base + __builtin_ctzll(active ? mine : mask);
         for (int i = 0; i < 8; ++i) mask &= mask - 1;
-        accumulate_block_f64<B, F32IN, FLAGS>(codes, scale, grad, blk, active, j, TBB, gscale, Cd,
-                                              codes_out, alpha_out, scale_out);
+        accumulate_block_split<B, F32IN, FLAGS>(codes, scale, grad, blk, active, j, TBB, C,
+                                                gscale, codes_out, alpha_out, scale_out);
       }
     }
   }
@@ -959,9 +964,9 @@ void launch_accumulate_t(const uint8_t *codes, const float *alpha, const float *
                      alpha, scale, grad, nb, TBB, sqrtTBB, (float)gscale, C, invC, codes_out,
                      alpha_out, scale_out);
   // the set-aside blocks: codes and s from the inputs (untouched for them), -alpha from alpha_out
-  const unsigned grid_fix = grid_for((nb + 511) / 512, TFP8_ACCUMULATE_FIX_WGS_PER_CU);
+  const unsigned grid_fix = grid_for((nb + 127) / 128, TFP8_ACCUMULATE_FIX_WGS_PER_CU);
   hipLaunchKernelGGL((k_accumulate_fix<B, F32, FLAGS>), dim3(grid_fix), dim3(kThreads), 0, st,
-                     codes, scale, grad, nb, TBBd, gscale, Cd, codes_out, alpha_out, scale_out);
+                     codes, scale, grad, nb, TBB, C, gscale, codes_out, alpha_out, scale_out);
 }
 
 template <int B, bool F32>

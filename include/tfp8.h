@@ -116,8 +116,9 @@ tfp8_status tfp8_reduce_ex(const uint8_t *codes, const float *alpha, const float
  * block, target and flags into codes_out, alpha_out, scale_out.  Page "AGoQ: Activation and
  * Gradient Quantization for Memory-Efficient Distributed Training of LLMs", section 2.B (local
  * accumulation of FP8 gradients across micro-batches).  The sum is formed in float32 (the page
- * names FP16/BF16 as its minimum precision), and in float64 for blocks where the two terms
- * cancel to under half of the larger one or s/alpha leaves float32's normal range.  Unlike the other calls this one may work in place:
+ * names FP16/BF16 as its minimum precision); blocks where the two terms cancel to under half of
+ * the larger one are redone by a second kernel with an exact float32 split of the transform, so
+ * that the result matches the exact sum.  Unlike the other calls this one may work in place:
  * each of codes_out, alpha_out, scale_out may be exactly its input (any other overlap is
  * TFP8_E_ARG).  grad must be 16-byte aligned. */
 tfp8_status tfp8_accumulate(const uint8_t *codes, const float *alpha, const float *scale,

@@ -342,6 +342,16 @@ def test_accumulate_edges(oracle, tfp8, B, gdtype, flags):
     _check_accumulate(oracle, tfp8, q, a, s, g, B, f"accumulate B={B} {gdtype}", flags=flags)
 
 
+def test_accumulate_activation_shards_with_shared_outliers(oracle, tfp8):
+    # the Qwen2.5-7B-shaped activation shards 0 and 1 as main and local gradient: their shared
+    # outlier channels have random signs, so about 15% of the blocks cancel and take the exact
+    # split path; full size, every element compared
+    cfg = CONFIGS[5]
+    xs = make_shards(5, count=2).reshape(2, -1)
+    q, a, s = oracle.compress(xs[0], cfg.block, 1.0)
+    _check_accumulate(oracle, tfp8, q, a, s, xs[1], cfg.block, "qwen shards accumulate")
+
+
 @pytest.mark.parametrize("inplace", [False, True])
 @pytest.mark.parametrize("flags", [0, 1])
 @pytest.mark.parametrize("B,gdtype", [(128, "bf16"), (256, "f32"), (64, "bf16")])
