@@ -78,9 +78,10 @@ def assert_bf16_match(got_bits, ref_bits, ref_f64, rel=2.0 ** -20, what="bf16 ou
 
 
 def check_compress(oracle, tfp8, x: np.ndarray, B: int, T: float = 1.0, what="compress",
-                   flags: int = 0):
+                   flags: int = 0, gpu: bool = False):
     """GPU compress of host input x (uint16 bfloat16 bits or float32) vs the oracle.
-    Returns (gpu codes, alpha, scale) as numpy arrays."""
+    Returns the oracle's (codes, alpha, scale), the input of any later stage (no oracle input
+    ever comes from the GPU), or with gpu=True the GPU's, as numpy arrays."""
     xg = bits_to_gpu(x) if x.dtype == np.uint16 else f32_to_gpu(x)
     q, a, s = tfp8.compress(xg.reshape(-1), B, T, flags=flags)
     torch.cuda.synchronize()
@@ -91,7 +92,7 @@ def check_compress(oracle, tfp8, x: np.ndarray, B: int, T: float = 1.0, what="co
     ea, es = assert_scales(a, s, ar, sr, what=what)
     say(f"  {what}: n={x.size} B={B} T={T} flags={flags}: code tie mismatches {nmis} "
         f"({nmis / max(x.size, 1):.2e}), max rel err alpha {ea:.2e} scale {es:.2e}")
-    return q, a, s
+    return (q, a, s) if gpu else (qr, ar, sr)
 
 
 def check_decompress(oracle, tfp8, q, a, s, B: int, what="decompress", flags: int = 0):
@@ -112,8 +113,10 @@ def check_decompress(oracle, tfp8, q, a, s, B: int, what="decompress", flags: in
     return o32
 
 
-def check_reduce(oracle, tfp8, q, a, s, B, T=1.0, what="reduce", flags: int = 0):
-    """GPU reduce of stacked codes/scales [P, ...] vs the oracle's reduce by definition."""
+def check_reduce(oracle, tfp8, q, a, s, B, T=1.0, what="reduce", flags: int = 0,
+                 gpu: bool = False):
+    """GPU reduce of stacked codes/scales [P, ...] vs the oracle's reduce by definition.
+    Returns the oracle's (codes, alpha, scale), or with gpu=True the GPU's."""
     P, n = q.shape
     qg, ag, sg = u8_to_gpu(q), f32_to_gpu(a), f32_to_gpu(s)
     cq, ca, cs = tfp8.reduce_fp8(qg, ag, sg, B, T, flags=flags)
@@ -125,4 +128,4 @@ def check_reduce(oracle, tfp8, q, a, s, B, T=1.0, what="reduce", flags: int = 0)
     ea, es = assert_scales(ca, cs, ra, rs, what=what)
     say(f"  {what}: P={P} n={n} B={B} flags={flags}: code tie mismatches {nmis} ({nmis / n:.2e}), "
         f"max rel err alpha {ea:.2e} scale {es:.2e}")
-    return cq, ca, cs
+    return (cq, ca, cs) if gpu else (rq, ra, rs)
