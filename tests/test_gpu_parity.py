@@ -177,7 +177,7 @@ def test_constructed_exact_ties(oracle, tfp8):
 
 # ----------------------------------------------------------------------------- reduce cases
 
-@pytest.mark.parametrize("P", [1, 2, 3, 8, 16])
+@pytest.mark.parametrize("P", [1, 2, 3, 8, 16, 33, 64])
 @pytest.mark.parametrize("B", [64, 128, 256, 512])
 def test_reduce_general(oracle, tfp8, P, B):
     rng = np.random.default_rng(100 * P + B)
