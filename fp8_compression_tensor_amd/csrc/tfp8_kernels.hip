@@ -8,8 +8,8 @@
 // requantize).  The pages give no kernel design for this hardware; what follows is laid out
 // for CDNA4 wavefronts.
 //
-// Layout.  A block of B elements is held by a group of 8 lanes (compress, decompress) or
-// B/16 lanes (reduce).  In compress and decompress, lane j of a group holds B/8 elements as
+// Layout.  A block of B elements is held by a group of 8 lanes (compress, decompress,
+// accumulate) or B/16 lanes (reduce).  In the 8-lane kernels lane j of a group holds B/8 elements as
 // B/64 runs of 8 consecutive elements, run g covering elements [64g + 8j, 64g + 8j + 8) of the
 // block: each 8-lane group reads or writes whole 128-byte lines of bfloat16 input.  Index bits
 // 0-2 and 6.. live in registers, bits 3-5 across the 8 lanes.
@@ -33,6 +33,14 @@
 // reduce works on r directly with no Hadamard at all, and max|y'| = alpha' max|r|.  The sum is
 // accumulated in float64 (as fast as unpacked float32 on this chip), which keeps it exact
 // enough that contributions which largely cancel still requantise like the exact sum.
+//
+// Accumulate (AGoQ page, section 2.B, local accumulation).  A compressed main gradient plus a
+// dense local gradient, requantised, also in the rotated domain: only the local gradient is
+// transformed.  Blocks where the two cancel are redone by a second kernel with an exact split
+// of the transform (K4 below).
+//
+// Variants.  Every kernel is a template on FLAGS: INT8 codes (Q_max = 127, the TACO page's INT8
+// fallback, section 5) and the rotation left out (ablation), alone or together.
 
 #include <math.h>
 #include <stdint.h>
