@@ -140,10 +140,16 @@ def test_block_counts(oracle, tfp8, nblocks):
     check_decompress(oracle, tfp8, q, a, s, 128, what=f"{nblocks} blocks")
 
 
-@pytest.mark.parametrize("T", [2.0 ** -10, 37.5, 2.0 ** 20])
+@pytest.mark.parametrize("T", [2.0 ** -64, 2.0 ** -10, 37.5, 2.0 ** 20, 2.0 ** 64])
 def test_target_values(oracle, tfp8, T):
+    # the contract's bounds 2^-64 and 2^64 included; compress, reduce and accumulate
     x = make_shard(1).reshape(-1)
-    check_compress(oracle, tfp8, x, 128, T=T, what=f"cfg1 T={T}")
+    q, a, s = check_compress(oracle, tfp8, x, 128, T=T, what=f"cfg1 T={T}")
+    xr = np.stack([make_shard(1, p).reshape(-1) for p in range(3)])
+    enc = [oracle.compress(v, 128, T) for v in xr]
+    check_reduce(oracle, tfp8, np.stack([e[0] for e in enc]), np.stack([e[1] for e in enc]),
+                 np.stack([e[2] for e in enc]), 128, T, what=f"reduce T={T}")
+    _check_accumulate(oracle, tfp8, q, a, s, xr[1], 128, f"accumulate T={T}", T=T)
 
 
 def test_constructed_exact_ties(oracle, tfp8):
@@ -299,17 +305,17 @@ def test_variant_reduce(oracle, tfp8, P, B, flags):
 
 # ----------------------------------------------------------------------------- accumulate
 
-def _check_accumulate(oracle, tfp8, q, a, s, g, B, what, flags=0, inplace=False):
+def _check_accumulate(oracle, tfp8, q, a, s, g, B, what, flags=0, inplace=False, T=1.0):
     from tiecheck import FLAG_INT8, tie_cap
 
     gg = bits_to_gpu(g) if g.dtype == np.uint16 else f32_to_gpu(g)
     qg, ag, sg = u8_to_gpu(q), f32_to_gpu(a), f32_to_gpu(s)
-    cq, ca, cs = tfp8.accumulate(qg, ag, sg, gg, B, 1.0, flags=flags, inplace=inplace)
+    cq, ca, cs = tfp8.accumulate(qg, ag, sg, gg, B, T, flags=flags, inplace=inplace)
     torch.cuda.synchronize()
     if inplace:
         assert cq.data_ptr() == qg.data_ptr()
     cq, ca, cs = cpu(cq), cpu(ca), cpu(cs)
-    rq, ra, rs, rt = oracle.accumulate(q, a, s, g, B, 1.0, with_quot=True, flags=flags)
+    rq, ra, rs, rt = oracle.accumulate(q, a, s, g, B, T, with_quot=True, flags=flags)
     nmis = assert_codes_match(cq, rq, rt, max_frac=tie_cap(flags), what=what + " codes",
                               int8=bool(flags & FLAG_INT8))
     ea, es = assert_scales(ca, cs, ra, rs, what=what)
