@@ -45,6 +45,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/tfp8.h"
 #include "tfp8_device.hpp"
 
@@ -83,19 +85,11 @@ __device__ __forceinline__ void decode4(uint32_t w, float &a, float &b, float &c
 // once, so they go through the cache hierarchy with the non-temporal hint.
 template <class T>
 __device__ __forceinline__ T ld_stream(const T *p) {
-#if defined(TFP8_NO_NT)
-  return *p;
-#else
   return __builtin_nontemporal_load(p);
-#endif
 }
 template <class T>
 __device__ __forceinline__ void st_stream(T v, T *p) {
-#if defined(TFP8_NO_NT)
-  *p = v;
-#else
   __builtin_nontemporal_store(v, p);
-#endif
 }
 
 // --------------------------------------------------------------------------------------------
@@ -851,19 +845,26 @@ bool target_ok(float t) {
 // compress and decompress stream fastest with one tile per wavefront and no loop (the
 // hardware keeps the CUs fed as wavefronts retire); the reduce, whose wavefronts each carry
 // P loads in flight, is fastest with 32 workgroups per CU.
-unsigned grid_for(int64_t tiles, int per_cu) {
-  static int cu_count = 0;
-  if (cu_count == 0) {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-        cus > 0)
-      cu_count = cus;
-    else
-      cu_count = 256;
+int cu_count() {
+  // compute units of the current device, looked up once per device (any thread may race to
+  // fill an entry; they all store the same value)
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> by_device[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int cus = by_device[dev].load(std::memory_order_relaxed);
+  if (cus <= 0) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    by_device[dev].store(cus, std::memory_order_relaxed);
   }
+  return cus;
+}
+
+unsigned grid_for(int64_t tiles, int per_cu) {
   const int64_t wgs = (tiles + (kThreads / 64) - 1) / (kThreads / 64);
-  const int64_t cap = per_cu > 0 ? (int64_t)cu_count * per_cu : (int64_t)1 << 30;
+  const int64_t cap = per_cu > 0 ? (int64_t)cu_count() * per_cu : (int64_t)1 << 30;
   return (unsigned)(wgs < cap ? (wgs > 0 ? wgs : 1) : cap);
 }
 
