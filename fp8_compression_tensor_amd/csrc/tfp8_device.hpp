@@ -141,6 +141,39 @@ __device__ __forceinline__ void fwht_lanes8(float (&v)[N], int j) {
   for (int r = 0; r < N; r += 8) TFP8_DPP_FMAC8("quad_perm:[2,3,0,1]", &v[r], s2);
 }
 
+// The same over the lanes of a block of any supported width: 8 lanes as above, or 4 lanes with
+// partners lane^1 and lane^2 (quad_perm), sigma from lane bits 0 and 1.  The 4-lane network
+// keeps the natural order and leaves lane j with (-1)^popcount(j) * (H_4 v)[j] (enumerated on
+// the unit vectors like the 8-lane one).
+constexpr int lanes_per_block(int B) { return B == 64 ? 4 : 8; }
+
+template <int L>
+__device__ __forceinline__ int lane_perm(int j) {
+  static_assert(L == 4 || L == 8, "4 or 8 lanes per block");
+  if constexpr (L == 8) return lane8_perm(j);
+  return j;
+}
+template <int L>
+__device__ __forceinline__ float lane_sign(int j) {
+  static_assert(L == 4 || L == 8, "4 or 8 lanes per block");
+  if constexpr (L == 8) return lane8_sign(j);
+  return (j == 0 || j == 3) ? 1.0f : -1.0f;
+}
+template <int L, int N>
+__device__ __forceinline__ void fwht_lanes(float (&v)[N], int j) {
+  static_assert(L == 4 || L == 8, "4 or 8 lanes per block");
+  if constexpr (L == 8) {
+    fwht_lanes8<N>(v, j);
+  } else {
+    const float s1 = (j & 1) ? -1.0f : 1.0f;
+    const float s2 = (j & 2) ? -1.0f : 1.0f;
+#pragma unroll
+    for (int r = 0; r < N; r += 8) TFP8_DPP_FMAC8("quad_perm:[1,0,3,2]", &v[r], s1);
+#pragma unroll
+    for (int r = 0; r < N; r += 8) TFP8_DPP_FMAC8("quad_perm:[2,3,0,1]", &v[r], s2);
+  }
+}
+
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // First butterfly of four packed bfloat16 pairs (one dword each): o[2q] = lo_q + hi_q and

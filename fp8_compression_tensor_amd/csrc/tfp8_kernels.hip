@@ -8,11 +8,12 @@
 // requantize).  The pages give no kernel design for this hardware; what follows is laid out
 // for CDNA4 wavefronts.
 //
-// Layout.  A block of B elements is held by a group of 8 lanes (compress, decompress,
-// accumulate) or B/16 lanes (reduce).  In the 8-lane kernels lane j of a group holds B/8 elements as
-// B/64 runs of 8 consecutive elements, run g covering elements [64g + 8j, 64g + 8j + 8) of the
-// block: each 8-lane group reads or writes whole 128-byte lines of bfloat16 input.  Index bits
-// 0-2 and 6.. live in registers, bits 3-5 across the 8 lanes.
+// Layout.  A block of B elements is held by a group of L lanes (compress and accumulate:
+// L = 8, or 4 at B = 64 so that a lane still holds 16 elements; decompress: L = 8) or B/16
+// lanes (reduce).  In the L-lane kernels lane j of a group holds B/L elements as runs of 8 consecutive
+// elements, run g covering elements [8Lg + 8j, 8Lg + 8j + 8) of the block: each group reads or
+// writes whole runs of 8L consecutive elements.  At L = 8 index bits 0-2 and 6.. live in
+// registers, bits 3-5 across the lanes.
 //
 // Transform.  w = H x (unnormalised) is computed by an in-register FWHT over the register
 // bits and a 3-stage DPP butterfly over the lane bits (tfp8_device.hpp), which leaves lane j
@@ -137,29 +138,34 @@ __device__ __forceinline__ void scales_exact(float (&v)[N], float M, int E0, flo
 }
 
 // --------------------------------------------------------------------------------------------
-// K1: compress.  One wavefront handles 8 blocks per iteration of a grid-stride loop and
-// prefetches the next iteration's input before working on the current one.
+// K1: compress.  One wavefront handles a tile of 64 / L blocks (L = 8 lanes per block, 4 at
+// B = 64) per iteration of a grid-stride loop and prefetches the next iteration's input before
+// working on the current one.
 
 template <int B, bool F32IN>
 struct CompressIn {
-  static constexpr int kRuns = B / 64;                    // 8-element runs per lane
-  static constexpr int kLoads = F32IN ? 2 * kRuns : kRuns;  // 16-byte loads per lane
+  static constexpr int kRuns = B / (8 * lanes_per_block(B));  // 8-element runs per lane
+  static constexpr int kLoads = F32IN ? 2 * kRuns : kRuns;      // 16-byte loads per lane
   u32x4 d[kLoads];
 };
 
+// Lane j of a block's group holds the runs of 8 elements [RS g + 8 j, RS g + 8 j + 8), where
+// RS = 8 L is the run stride for L lanes per block.
 template <int B, bool F32IN>
 __device__ __forceinline__ void load_compress_in(CompressIn<B, F32IN> &in, const void *xin,
                                                  int64_t blk, int j) {
+  constexpr int RS = 8 * lanes_per_block(B);
+  constexpr int G = CompressIn<B, F32IN>::kRuns;
   if constexpr (!F32IN) {
     const uint16_t *xb = (const uint16_t *)xin + blk * B + 8 * j;
 #pragma unroll
-    for (int g = 0; g < B / 64; ++g) in.d[g] = ld_stream((const u32x4 *)(xb + 64 * g));
+    for (int g = 0; g < G; ++g) in.d[g] = ld_stream((const u32x4 *)(xb + RS * g));
   } else {
     const float *xb = (const float *)xin + blk * B + 8 * j;
 #pragma unroll
-    for (int g = 0; g < B / 64; ++g) {
-      in.d[2 * g] = ld_stream((const u32x4 *)(xb + 64 * g));
-      in.d[2 * g + 1] = ld_stream((const u32x4 *)(xb + 64 * g + 4));
+    for (int g = 0; g < G; ++g) {
+      in.d[2 * g] = ld_stream((const u32x4 *)(xb + RS * g));
+      in.d[2 * g + 1] = ld_stream((const u32x4 *)(xb + RS * g + 4));
     }
   }
 }
@@ -170,32 +176,35 @@ __global__ __launch_bounds__(kThreads) void k_compress(const void *__restrict__ 
                                                        float invC, uint8_t *__restrict__ codes,
                                                        float *__restrict__ alpha_out,
                                                        float *__restrict__ scale_out) {
-  constexpr int N = B / 8;   // elements per lane
-  constexpr int G = N / 8;   // runs of 8 consecutive elements per lane
+  constexpr int L = lanes_per_block(B);  // lanes per block
+  constexpr int BPW = 64 / L;            // blocks per wavefront (one tile)
+  constexpr int RS = 8 * L;              // run stride
+  constexpr int N = B / L;               // elements per lane
+  constexpr int G = N / 8;               // runs of 8 consecutive elements per lane
   constexpr bool ROT = !(FLAGS & kNoRotation);
   constexpr float Q = qmax_of<FLAGS>();
   const int lane = threadIdx.x & 63;
-  const int j = lane & 7;
-  const int bw = lane >> 3;
-  const int pj = ROT ? lane8_perm(j) : j;
-  const float sj = ROT ? lane8_sign(j) : 1.0f;
+  const int j = lane & (L - 1);
+  const int bw = lane / L;
+  const int pj = ROT ? lane_perm<L>(j) : j;
+  const float sj = ROT ? lane_sign<L>(j) : 1.0f;
   const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
   const int64_t nwaves = ((int64_t)gridDim.x * kThreads) >> 6;
-  const int64_t ntiles = (nb + 7) >> 3;
+  const int64_t ntiles = (int64_t)(((uint64_t)nb + BPW - 1) / BPW);  // nb >= 0
   // packed bfloat16 (1, 1) and (1, -1), kept in registers for v_dot2_f32_bf16
   const uint32_t ones = 0x3F803F80u, plus_minus = 0xBF803F80u;
 
   // Groups past the last block (ragged last tile) read the last block again and store
   // nothing, so every load is in bounds and every register holds data.
   CompressIn<B, F32IN> cur;
-  if (wave < ntiles) load_compress_in<B, F32IN>(cur, xin, min(wave * 8 + bw, nb - 1), j);
+  if (wave < ntiles) load_compress_in<B, F32IN>(cur, xin, min(wave * BPW + bw, nb - 1), j);
 
   for (int64_t tile = wave; tile < ntiles; tile += nwaves) {
-    const int64_t blk = tile * 8 + bw;
+    const int64_t blk = tile * BPW + bw;
     const bool active = blk < nb;
     CompressIn<B, F32IN> nxt;
     if (tile + nwaves < ntiles)
-      load_compress_in<B, F32IN>(nxt, xin, min((tile + nwaves) * 8 + bw, nb - 1), j);
+      load_compress_in<B, F32IN>(nxt, xin, min((tile + nwaves) * BPW + bw, nb - 1), j);
 
     // Widen, energy and the first butterfly stages.  Groups past the last block work on a
     // copy of the last block and store nothing.
@@ -228,13 +237,13 @@ __global__ __launch_bounds__(kThreads) void k_compress(const void *__restrict__ 
       if constexpr (ROT) fwht_registers<N, 1>(v);
     }
     // orthogonal Hadamard rotation, unnormalised: w = H x (1/sqrt(B) and alpha live in s)
-    if constexpr (ROT) fwht_lanes8<N>(v, j);
+    if constexpr (ROT) fwht_lanes<L, N>(v, j);
 
     float m = 0.0f;
 #pragma unroll
     for (int r = 0; r < N; ++r) m = fmaxf(m, fabsf(v[r]));
-    const float M = group_max<8>(m);
-    const float SS = group_sum<8>(ss);  // sum(x^2) of the block
+    const float M = group_max<L>(m);
+    const float SS = group_sum<L>(ss);  // sum(x^2) of the block
 
     // alpha = sqrt(T B / sum x^2), s = alpha max|w| / (Q sqrt B), codes = code(Q w / max|w|)
     // (Q = 448 for E4M3; without the rotation w = x and s = alpha max|x| / Q).
@@ -250,7 +259,7 @@ __global__ __launch_bounds__(kThreads) void k_compress(const void *__restrict__ 
       s = alpha * M * invC;
       cm = c * sj;
     } else {
-      scales_exact<8, N>(v, M, 0, TBB, Q, C, sj, cm, alpha, s);
+      scales_exact<L, N>(v, M, 0, TBB, Q, C, sj, cm, alpha, s);
     }
 
     if (active) {
@@ -260,7 +269,7 @@ __global__ __launch_bounds__(kThreads) void k_compress(const void *__restrict__ 
         u32x2 w;
         w[0] = encode4<FLAGS>(v[8 * g + 0], v[8 * g + 1], v[8 * g + 2], v[8 * g + 3], cm);
         w[1] = encode4<FLAGS>(v[8 * g + 4], v[8 * g + 5], v[8 * g + 6], v[8 * g + 7], cm);
-        st_stream(w, (u32x2 *)(cb + 64 * g));
+        st_stream(w, (u32x2 *)(cb + RS * g));
       }
       if (j == 0) {
         alpha_out[blk] = alpha;
@@ -275,9 +284,13 @@ __global__ __launch_bounds__(kThreads) void k_compress(const void *__restrict__ 
 // K2: decompress.  x = H (s dec q) / (sqrt(B) alpha), same lane layout as compress, with the
 // next iteration's codes and scales prefetched.
 
+// Decompress keeps 8 lanes per block at every B: its per-block work is small, and at B = 64
+// the 8-lane group reads each block's codes, and writes its output, in whole lines.
+constexpr int decompress_lanes(int) { return 8; }
+
 template <int B>
 struct DecompressIn {
-  u32x2 d[B / 64];
+  u32x2 d[B / (8 * decompress_lanes(B))];
   float s, a;
 };
 
@@ -285,9 +298,10 @@ template <int B>
 __device__ __forceinline__ void load_decompress_in(DecompressIn<B> &in, const uint8_t *codes,
                                                    const float *alpha, const float *scale,
                                                    int64_t blk, int j) {
+  constexpr int RS = 8 * decompress_lanes(B);
   const uint8_t *cb = codes + blk * B + 8 * j;
 #pragma unroll
-  for (int g = 0; g < B / 64; ++g) in.d[g] = ld_stream((const u32x2 *)(cb + 64 * g));
+  for (int g = 0; g < B / RS; ++g) in.d[g] = ld_stream((const u32x2 *)(cb + RS * g));
   in.s = scale[blk];
   in.a = alpha[blk];
 }
@@ -298,27 +312,31 @@ __global__ __launch_bounds__(kThreads) void k_decompress(const uint8_t *__restri
                                                          const float *__restrict__ scale,
                                                          int64_t nb, float inv_sqrt_b,
                                                          void *__restrict__ out) {
-  constexpr int N = B / 8;
+  constexpr int L = decompress_lanes(B);
+  constexpr int BPW = 64 / L;
+  constexpr int RS = 8 * L;
+  constexpr int N = B / L;
   constexpr int G = N / 8;
   constexpr bool ROT = !(FLAGS & kNoRotation);
   const int lane = threadIdx.x & 63;
-  const int j = lane & 7;
-  const int bw = lane >> 3;
-  const int pj = ROT ? lane8_perm(j) : j;
-  const float sj = ROT ? lane8_sign(j) : 1.0f;
+  const int j = lane & (L - 1);
+  const int bw = lane / L;
+  const int pj = ROT ? lane_perm<L>(j) : j;
+  const float sj = ROT ? lane_sign<L>(j) : 1.0f;
   const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
   const int64_t nwaves = ((int64_t)gridDim.x * kThreads) >> 6;
-  const int64_t ntiles = (nb + 7) >> 3;
+  const int64_t ntiles = (int64_t)(((uint64_t)nb + BPW - 1) / BPW);  // nb >= 0
 
   DecompressIn<B> cur;  // groups past the last block re-read the last block, store nothing
-  if (wave < ntiles) load_decompress_in<B>(cur, codes, alpha, scale, min(wave * 8 + bw, nb - 1), j);
+  if (wave < ntiles)
+    load_decompress_in<B>(cur, codes, alpha, scale, min(wave * BPW + bw, nb - 1), j);
 
   for (int64_t tile = wave; tile < ntiles; tile += nwaves) {
-    const int64_t blk = tile * 8 + bw;
+    const int64_t blk = tile * BPW + bw;
     const bool active = blk < nb;
     DecompressIn<B> nxt;
     if (tile + nwaves < ntiles)
-      load_decompress_in<B>(nxt, codes, alpha, scale, min((tile + nwaves) * 8 + bw, nb - 1), j);
+      load_decompress_in<B>(nxt, codes, alpha, scale, min((tile + nwaves) * BPW + bw, nb - 1), j);
 
     float v[N];
 #pragma unroll
@@ -334,7 +352,7 @@ __global__ __launch_bounds__(kThreads) void k_decompress(const uint8_t *__restri
     // (E4M3; for B <= 128 only the last stage can round, once) or 2^24 (INT8: never).
     if constexpr (ROT) {
       fwht_registers<N, 1>(v);
-      fwht_lanes8<N>(v, j);
+      fwht_lanes<L, N>(v, j);
     }
 
     // (v * s / sqrt(B)) / alpha as two products: s / (sqrt(B) alpha) alone can fall below the
@@ -353,8 +371,8 @@ __global__ __launch_bounds__(kThreads) void k_decompress(const uint8_t *__restri
             w0[q] = __float_as_uint(fmaf(v[8 * g + q], f, 0.0f) * ra);
             w1[q] = __float_as_uint(fmaf(v[8 * g + 4 + q], f, 0.0f) * ra);
           }
-          st_stream(w0, (u32x4 *)(ob + 64 * g));
-          st_stream(w1, (u32x4 *)(ob + 64 * g + 4));
+          st_stream(w0, (u32x4 *)(ob + RS * g));
+          st_stream(w1, (u32x4 *)(ob + RS * g + 4));
         }
       } else {
         __bf16 *ob = (__bf16 *)out + blk * B + 8 * pj;
@@ -368,7 +386,7 @@ __global__ __launch_bounds__(kThreads) void k_decompress(const uint8_t *__restri
             w[q] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
                    ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
           }
-          st_stream(w, (u32x4 *)(ob + 64 * g));
+          st_stream(w, (u32x4 *)(ob + RS * g));
         }
       }
     }
@@ -401,7 +419,7 @@ __global__ __launch_bounds__(kThreads) void k_reduce(const uint8_t *__restrict__
   const int bw = lane / L;
   const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
   const int64_t nwaves = ((int64_t)gridDim.x * kThreads) >> 6;
-  const int64_t ntiles = (nb + BPW - 1) / BPW;
+  const int64_t ntiles = (int64_t)(((uint64_t)nb + BPW - 1) / BPW);  // nb >= 0
 
   for (int64_t tile = wave; tile < ntiles; tile += nwaves) {
     const int64_t blk = tile * BPW + bw;
@@ -525,29 +543,32 @@ __global__ __launch_bounds__(kThreads) void k_accumulate(
     const uint8_t *codes, const float *alpha, const float *scale, const void *__restrict__ grad,
     int64_t nb, float TBB, float sqrtTBB, float gscale, float C, float invC, uint8_t *codes_out,
     float *alpha_out, float *scale_out) {
-  constexpr int N = B / 8;
+  constexpr int L = lanes_per_block(B);
+  constexpr int BPW = 64 / L;
+  constexpr int RS = 8 * L;
+  constexpr int N = B / L;
   constexpr int G = N / 8;
   constexpr bool ROT = !(FLAGS & kNoRotation);
   constexpr float Q = qmax_of<FLAGS>();
   const int lane = threadIdx.x & 63;
-  const int j = lane & 7;
-  const int bw = lane >> 3;
-  const int pj = ROT ? lane8_perm(j) : j;
-  const float sj = ROT ? lane8_sign(j) : 1.0f;
+  const int j = lane & (L - 1);
+  const int bw = lane / L;
+  const int pj = ROT ? lane_perm<L>(j) : j;
+  const float sj = ROT ? lane_sign<L>(j) : 1.0f;
   const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
   const int64_t nwaves = ((int64_t)gridDim.x * kThreads) >> 6;
-  const int64_t ntiles = (nb + 7) >> 3;
+  const int64_t ntiles = (int64_t)(((uint64_t)nb + BPW - 1) / BPW);  // nb >= 0
   const uint32_t ones = 0x3F803F80u, plus_minus = 0xBF803F80u;
 
   for (int64_t tile = wave; tile < ntiles; tile += nwaves) {
-    const int64_t blk = tile * 8 + bw;
+    const int64_t blk = tile * BPW + bw;
     const bool active = blk < nb;
     const int64_t cblk = active ? blk : nb - 1;  // groups past the end re-read the last block
     CompressIn<B, F32IN> in;
     load_compress_in<B, F32IN>(in, grad, cblk, j);
     u32x2 qd[G];
 #pragma unroll
-    for (int g = 0; g < G; ++g) qd[g] = *(const u32x2 *)(codes + cblk * B + 64 * g + 8 * pj);
+    for (int g = 0; g < G; ++g) qd[g] = *(const u32x2 *)(codes + cblk * B + RS * g + 8 * pj);
     const float sp = scale[cblk], ap = alpha[cblk];
 
     float v[N];
@@ -573,12 +594,12 @@ __global__ __launch_bounds__(kThreads) void k_accumulate(
         }
       if constexpr (ROT) fwht_registers<N, 1>(v);
     }
-    if constexpr (ROT) fwht_lanes8<N>(v, j);  // lane j: sj * (H g) at positions 64g + 8 pj + e
+    if constexpr (ROT) fwht_lanes<L, N>(v, j);  // lane j: sj * (H g) at positions RS g + 8 pj + e
 
     float mh = 0.0f;  // largest |H g| of the block
 #pragma unroll
     for (int r = 0; r < N; ++r) mh = fmaxf(mh, fabsf(v[r]));
-    mh = group_max<8>(mh);
+    mh = group_max<L>(mh);
 
     // Add the main gradient in the same (signed, permuted) positions, with factor
     // gscale * s / alpha.  Where s / alpha leaves float32's range (alpha clamped at 2^126 on a
@@ -610,7 +631,7 @@ __global__ __launch_bounds__(kThreads) void k_accumulate(
     float m = 0.0f;
 #pragma unroll
     for (int r = 0; r < N; ++r) m = fmaxf(m, fabsf(v[r]));
-    const float M = group_max<8>(m);
+    const float M = group_max<L>(m);
 
     // float32 keeps w to ~2^-24 of the larger term; where the terms cancel that is too coarse
     // (see above), and the block is left to k_accumulate_fix
@@ -626,12 +647,12 @@ __global__ __launch_bounds__(kThreads) void k_accumulate(
           const float u = v[r] * c;
           su = fmaf(u, u, su);
         }
-        const float SU = group_sum<8>(su);
+        const float SU = group_sum<L>(su);
         a_out = fminf(fmaxf(c * sqrtTBB * __builtin_amdgcn_rsqf(SU), 0x1p-126f), 0x1p126f);
         s_out = a_out * M * invC;
         cm = c * sj;
       } else {
-        scales_exact<8, N>(v, M, E0, TBB, Q, C, sj, cm, a_out, s_out);
+        scales_exact<L, N>(v, M, E0, TBB, Q, C, sj, cm, a_out, s_out);
       }
     }
 
@@ -643,7 +664,7 @@ __global__ __launch_bounds__(kThreads) void k_accumulate(
           u32x2 w;
           w[0] = encode4<FLAGS>(v[8 * g + 0], v[8 * g + 1], v[8 * g + 2], v[8 * g + 3], cm);
           w[1] = encode4<FLAGS>(v[8 * g + 4], v[8 * g + 5], v[8 * g + 6], v[8 * g + 7], cm);
-          *(u32x2 *)(cb + 64 * g) = w;
+          *(u32x2 *)(cb + RS * g) = w;
         }
         if (j == 0) {
           alpha_out[blk] = a_out;
@@ -656,7 +677,7 @@ __global__ __launch_bounds__(kThreads) void k_accumulate(
   }
 }
 
-// One set-aside block, by the group of eight lanes j = 0..7 that holds it (lane layout of
+// One set-aside block, by the group of L lanes j = 0..L-1 that holds it (lane layout of
 // k_accumulate).  Its codes and s are still those of the main gradient (never written) and
 // alpha_out holds -alpha.  `active` = 0: work on the block but store nothing.
 //
@@ -671,20 +692,22 @@ __device__ __forceinline__ void accumulate_block_split(
     const uint8_t *codes, const float *scale, const void *__restrict__ grad, int64_t blk,
     bool active, int j, float TBB, float C, double gscale, uint8_t *codes_out, float *alpha_out,
     float *scale_out) {
-  constexpr int N = B / 8;
+  constexpr int L = lanes_per_block(B);
+  constexpr int RS = 8 * L;
+  constexpr int N = B / L;
   constexpr int G = N / 8;
   constexpr bool ROT = !(FLAGS & kNoRotation);
   constexpr float Q = qmax_of<FLAGS>();
   constexpr int K = 24 - (B == 64 ? 6 : B == 128 ? 7 : B == 256 ? 8 : 9);
   constexpr int kNone = -(1 << 20);
-  const int pj = ROT ? lane8_perm(j) : j;
-  const float sj = ROT ? lane8_sign(j) : 1.0f;
+  const int pj = ROT ? lane_perm<L>(j) : j;
+  const float sj = ROT ? lane_sign<L>(j) : 1.0f;
 
   CompressIn<B, F32IN> in;
   load_compress_in<B, F32IN>(in, grad, blk, j);
   u32x2 qd[G];
 #pragma unroll
-  for (int g = 0; g < G; ++g) qd[g] = *(const u32x2 *)(codes + blk * B + 64 * g + 8 * pj);
+  for (int g = 0; g < G; ++g) qd[g] = *(const u32x2 *)(codes + blk * B + RS * g + 8 * pj);
   const float sp = scale[blk], ap = -alpha_out[blk];
 
   float r[N], l[N];
@@ -705,7 +728,7 @@ __device__ __forceinline__ void accumulate_block_split(
   float mg = 0.0f;
 #pragma unroll
   for (int i = 0; i < N; ++i) mg = fmaxf(mg, fabsf(r[i]));
-  mg = group_max<8>(mg);
+  mg = group_max<L>(mg);
   // the main term's factor sj * gscale * s / alpha; |factor * dec| <= |factor| * Q
   const double f = (sp == 0.0f) ? 0.0 : (double)sj * (gscale * ((double)sp / (double)ap));
   const int Eg = (mg == 0.0f) ? kNone : exponent_of(mg);
@@ -721,9 +744,9 @@ __device__ __forceinline__ void accumulate_block_split(
   }
   if constexpr (ROT) {
     fwht_registers<N, 1>(r);
-    fwht_lanes8<N>(r, j);  // lane j: sj * (H r) at positions 64g + 8 pj + e
+    fwht_lanes<L, N>(r, j);  // lane j: sj * (H r) at positions RS g + 8 pj + e
     fwht_registers<N, 1>(l);
-    fwht_lanes8<N>(l, j);
+    fwht_lanes<L, N>(l, j);
   }
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -740,9 +763,9 @@ __device__ __forceinline__ void accumulate_block_split(
   float m = 0.0f;
 #pragma unroll
   for (int i = 0; i < N; ++i) m = fmaxf(m, fabsf(r[i]));
-  const float M = group_max<8>(m);
+  const float M = group_max<L>(m);
   float cm, a_out, s_out;
-  scales_exact<8, N>(r, M, E - K, TBB, Q, C, sj, cm, a_out, s_out);
+  scales_exact<L, N>(r, M, E - K, TBB, Q, C, sj, cm, a_out, s_out);
   if (active) {
     uint8_t *cb = codes_out + blk * B + 8 * pj;
 #pragma unroll
@@ -750,7 +773,7 @@ __device__ __forceinline__ void accumulate_block_split(
       u32x2 q;
       q[0] = encode4<FLAGS>(r[8 * g + 0], r[8 * g + 1], r[8 * g + 2], r[8 * g + 3], cm);
       q[1] = encode4<FLAGS>(r[8 * g + 4], r[8 * g + 5], r[8 * g + 6], r[8 * g + 7], cm);
-      *(u32x2 *)(cb + 64 * g) = q;
+      *(u32x2 *)(cb + RS * g) = q;
     }
     if (j == 0) {
       alpha_out[blk] = a_out;
@@ -761,16 +784,18 @@ __device__ __forceinline__ void accumulate_block_split(
 
 // Finds the blocks k_accumulate set aside (alpha_out < 0) and redoes them.  A wavefront reads the
 // alphas of kRuns x 64 consecutive blocks at once (kRuns loads in flight per lane), then takes
-// the runs of 64 in turn and works through each run's marked blocks eight at a time, one group
-// of eight lanes per block.
+// the runs of 64 in turn and works through each run's marked blocks 64 / L at a time, one group
+// of L lanes per block.
 template <int B, bool F32IN, int FLAGS>
 __global__ __launch_bounds__(kThreads) void k_accumulate_fix(
     const uint8_t *codes, const float *scale, const void *__restrict__ grad, int64_t nb,
     float TBB, float C, double gscale, uint8_t *codes_out, float *alpha_out, float *scale_out) {
   constexpr int kRuns = 2;
+  constexpr int L = lanes_per_block(B);
+  constexpr int BPW = 64 / L;  // blocks worked on at once: one per group of L lanes
   const int lane = threadIdx.x & 63;
-  const int j = lane & 7;
-  const int bw = lane >> 3;
+  const int j = lane & (L - 1);
+  const int bw = lane / L;
   const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
   const int64_t nwaves = ((int64_t)gridDim.x * kThreads) >> 6;
   const int64_t nscan = (nb + 64 * kRuns - 1) / (64 * kRuns);
@@ -792,7 +817,7 @@ __global__ __launch_bounds__(kThreads) void k_accumulate_fix(
         for (int i = 0; i < bw; ++i) mine &= mine - 1;
         const bool active = mine != 0;
         const int64_t blk = base + __builtin_ctzll(active ? mine : mask);
-        for (int i = 0; i < 8; ++i) mask &= mask - 1;
+        for (int i = 0; i < BPW; ++i) mask &= mask - 1;
         accumulate_block_split<B, F32IN, FLAGS>(codes, scale, grad, blk, active, j, TBB, C,
                                                 gscale, codes_out, alpha_out, scale_out);
       }
@@ -882,7 +907,8 @@ void launch_compress_t(const void *x, int64_t nb, float target, uint8_t *codes, 
   const float sqrtTB = (float)sqrt((double)target * B);
   const double Cd = ROT ? Q * sqrt((double)B) : Q;
   const float C = (float)Cd, invC = (float)(1.0 / Cd);
-  const unsigned grid = grid_for((nb + 7) / 8, TFP8_COMPRESS_WGS_PER_CU);
+  constexpr int BPW = 64 / lanes_per_block(B);  // blocks per tile
+  const unsigned grid = grid_for((nb + BPW - 1) / BPW, TFP8_COMPRESS_WGS_PER_CU);
   hipLaunchKernelGGL((k_compress<B, F32, FLAGS>), dim3(grid), dim3(kThreads), 0, st, x, nb, TBB,
                      sqrtTB, C, invC, codes, alpha, scale);
 }
@@ -904,7 +930,8 @@ void launch_decompress_t(const uint8_t *codes, const float *alpha, const float *
                          void *out, hipStream_t st) {
   constexpr bool ROT = !(FLAGS & kNoRotation);
   const float inv_sqrt_b = ROT ? (float)(1.0 / sqrt((double)B)) : 1.0f;
-  const unsigned grid = grid_for((nb + 7) / 8, TFP8_DECOMPRESS_WGS_PER_CU);
+  constexpr int BPW = 64 / decompress_lanes(B);  // blocks per tile
+  const unsigned grid = grid_for((nb + BPW - 1) / BPW, TFP8_DECOMPRESS_WGS_PER_CU);
   hipLaunchKernelGGL((k_decompress<B, F32, FLAGS>), dim3(grid), dim3(kThreads), 0, st, codes,
                      alpha, scale, nb, inv_sqrt_b, out);
 }
@@ -968,7 +995,8 @@ void launch_accumulate_t(const uint8_t *codes, const float *alpha, const float *
   const double gscale = ROT ? sqrt((double)B) : 1.0;
   const double Cd = ROT ? Q * sqrt((double)B) : Q;
   const float C = (float)Cd, invC = (float)(1.0 / Cd);
-  const unsigned grid = grid_for((nb + 7) / 8, TFP8_COMPRESS_WGS_PER_CU);
+  constexpr int BPW = 64 / lanes_per_block(B);  // blocks per tile
+  const unsigned grid = grid_for((nb + BPW - 1) / BPW, TFP8_COMPRESS_WGS_PER_CU);
   hipLaunchKernelGGL((k_accumulate<B, F32, FLAGS>), dim3(grid), dim3(kThreads), 0, st, codes,
                      alpha, scale, grad, nb, TBB, sqrtTBB, (float)gscale, C, invC, codes_out,
                      alpha_out, scale_out);
