@@ -11,7 +11,7 @@
  *   [AGoQ] "AGoQ: Activation and Gradient Quantization for Memory-Efficient Distributed
  *          Training of LLMs".
  *
- * Readings where the pages leave a step open (every one is listed in the design notes):
+ * Readings where the pages leave a step open:
  *   - a block is `block` consecutive elements of the flat buffer; the Hadamard size is `block`;
  *   - the "second moment (energy)" is the raw mean of squares m2 = sum(v^2)/block;
  *   - the prescale brings that energy to the target: alpha = sqrt(target/m2), clamped to
@@ -22,7 +22,15 @@
  *   - codes are OCP E4M3FN, round-to-nearest-even, saturating, sign kept on zero;
  *   - an all-zero block (tested on max|v|, not on m2) stores alpha = 1, s = 0, codes 0x00 and
  *     reconstructs to +0;
- *   - both scales are stored as fp32 and every later step uses the stored values.
+ *   - both scales are stored as fp32 and every later step uses the stored values;
+ *   - the INT8 variant uses two's-complement codes, round-to-nearest-even, saturating at +-127,
+ *     with Q_max = 127; the no-rotation variant replaces H by the identity;
+ *   - the local accumulation reconstructs the main gradient, adds the local gradient and
+ *     compresses the sum with the same block, target and variant.
+ *
+ * Parity unpinned: the default target (1), the alpha clamp bounds and the Sylvester order
+ * without random signs are conventions the pages do not fix, so no test can tie them to the
+ * pages; the tests pin everything the oracle computes given them.
  */
 #include "tfp8_oracle.h"
 
