@@ -42,6 +42,10 @@
  *   - Argument errors return before any HIP call and nothing is launched.  A launch failure
  *     returns TFP8_E_HIP.  Faults during execution surface at the caller's next
  *     synchronization, as for any HIP kernel.
+ *   - Every entry point may be called from several host threads at once: the library keeps no
+ *     state beyond a per-device count of compute units, looked up once.  Work launched on the
+ *     same buffers from different streams is ordered only by the caller.
+ *   - Launches go to the current HIP device; the pointers must belong to it.
  */
 #ifndef TFP8_H
 #define TFP8_H
