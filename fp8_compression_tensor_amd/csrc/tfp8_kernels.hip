@@ -1030,7 +1030,7 @@ const char *tfp8_status_string(tfp8_status status) {
   switch (status) {
     case TFP8_OK: return "ok";
     case TFP8_E_NULL: return "a required pointer is NULL";
-    case TFP8_E_SIZE: return "n is negative or not a multiple of the block size";
+    case TFP8_E_SIZE: return "n is negative, above 2^40, or not a multiple of the block size";
     case TFP8_E_BLOCK: return "unsupported block size (use 64, 128, 256 or 512)";
     case TFP8_E_DTYPE: return "unsupported dtype (use TFP8_BF16 or TFP8_F32)";
     case TFP8_E_ALIGN: return "misaligned pointer (16 bytes for data, 4 for scales)";
@@ -1044,7 +1044,7 @@ tfp8_status tfp8_compress_ex(const void *x, tfp8_dtype x_dtype, int64_t n, int32
                              float target, uint32_t flags, uint8_t *codes, float *alpha,
                              float *scale, void *stream) {
   if (!block_ok(block)) return TFP8_E_BLOCK;
-  if (n < 0 || n % block != 0) return TFP8_E_SIZE;
+  if (n < 0 || n > TFP8_MAX_N || n % block != 0) return TFP8_E_SIZE;
   if (x_dtype != TFP8_BF16 && x_dtype != TFP8_F32) return TFP8_E_DTYPE;
   if (!target_ok(target) || (flags & ~TFP8_FLAGS_ALL)) return TFP8_E_ARG;
   if (n == 0) return TFP8_OK;
@@ -1082,7 +1082,7 @@ tfp8_status tfp8_decompress_ex(const uint8_t *codes, const float *alpha, const f
                                int64_t n, int32_t block, uint32_t flags, void *out,
                                tfp8_dtype out_dtype, void *stream) {
   if (!block_ok(block)) return TFP8_E_BLOCK;
-  if (n < 0 || n % block != 0) return TFP8_E_SIZE;
+  if (n < 0 || n > TFP8_MAX_N || n % block != 0) return TFP8_E_SIZE;
   if (out_dtype != TFP8_BF16 && out_dtype != TFP8_F32) return TFP8_E_DTYPE;
   if (flags & ~TFP8_FLAGS_ALL) return TFP8_E_ARG;
   if (n == 0) return TFP8_OK;
@@ -1119,7 +1119,7 @@ tfp8_status tfp8_reduce_ex(const uint8_t *codes, const float *alpha, const float
                            int64_t n, int32_t block, float target, uint32_t flags,
                            uint8_t *codes_out, float *alpha_out, float *scale_out, void *stream) {
   if (!block_ok(block)) return TFP8_E_BLOCK;
-  if (n < 0 || n % block != 0) return TFP8_E_SIZE;
+  if (n < 0 || n > TFP8_MAX_N || n % block != 0) return TFP8_E_SIZE;
   if (P < 1 || P > 64 || !target_ok(target) || (flags & ~TFP8_FLAGS_ALL)) return TFP8_E_ARG;
   if (n == 0) return TFP8_OK;
   if (!codes || !alpha || !scale || !codes_out || !alpha_out || !scale_out) return TFP8_E_NULL;
@@ -1159,7 +1159,7 @@ tfp8_status tfp8_accumulate(const uint8_t *codes, const float *alpha, const floa
                             float target, uint32_t flags, uint8_t *codes_out, float *alpha_out,
                             float *scale_out, void *stream) {
   if (!block_ok(block)) return TFP8_E_BLOCK;
-  if (n < 0 || n % block != 0) return TFP8_E_SIZE;
+  if (n < 0 || n > TFP8_MAX_N || n % block != 0) return TFP8_E_SIZE;
   if (grad_dtype != TFP8_BF16 && grad_dtype != TFP8_F32) return TFP8_E_DTYPE;
   if (!target_ok(target) || (flags & ~TFP8_FLAGS_ALL)) return TFP8_E_ARG;
   if (n == 0) return TFP8_OK;

@@ -31,7 +31,9 @@
  *   - Every data pointer is a DEVICE pointer; `stream` is a hipStream_t (NULL = default stream).
  *   - The caller owns every buffer.  The library allocates and frees nothing and never
  *     synchronizes; outputs are complete when the stream reaches the launch.
- *   - Element counts are 64-bit.  n = 0 is a no-op that returns TFP8_OK.
+ *   - Element counts are 64-bit, at most TFP8_MAX_N (2^40, several times any one GPU's
+ *     memory, so that no byte count or address computed from n can overflow).  n = 0 is a
+ *     no-op that returns TFP8_OK.
  *   - Supported block sizes: 64, 128, 256, 512.
  *   - Alignment: x, out and every codes pointer 16 bytes; alpha and scale 4 bytes.
  *   - Out-of-place (except tfp8_accumulate, which may work in place): an output range that
@@ -59,7 +61,7 @@ extern "C" {
 typedef enum {
   TFP8_OK = 0,
   TFP8_E_NULL = -1,  /* a required pointer is NULL (n > 0) */
-  TFP8_E_SIZE = -2,  /* n < 0, or n is not a multiple of block */
+  TFP8_E_SIZE = -2,  /* n < 0, n > TFP8_MAX_N, or n is not a multiple of block */
   TFP8_E_BLOCK = -3, /* block is not one of 64, 128, 256, 512 */
   TFP8_E_DTYPE = -4, /* dtype is not TFP8_BF16 or TFP8_F32 */
   TFP8_E_ALIGN = -5, /* a pointer is not aligned as stated above */
@@ -68,6 +70,8 @@ typedef enum {
 } tfp8_status;
 
 typedef enum { TFP8_BF16 = 0, TFP8_F32 = 1 } tfp8_dtype;
+
+#define TFP8_MAX_N ((int64_t)1 << 40)
 
 /* Variant flags of the *_ex entry points (0 = the method as defined above):
  *   TFP8_FLAG_INT8         codes are int8 (two's complement, round to nearest even, saturating at

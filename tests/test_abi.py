@@ -51,6 +51,15 @@ def test_compress_argument_errors(tfp8):
     assert c(FAKE, 0, 1024, 96, 1.0, FAKE + 4096, FAKE + 8192, FAKE + 12288) == -3  # block
     assert c(FAKE, 0, 1000, 128, 1.0, FAKE + 4096, FAKE + 8192, FAKE + 12288) == -2  # n % B
     assert c(FAKE, 0, -128, 128, 1.0, FAKE + 4096, FAKE + 8192, FAKE + 12288) == -2
+    # above the 2^40 maximum (byte counts of such sizes could overflow)
+    big = (1 << 40) + 128
+    assert c(FAKE, 0, big, 128, 1.0, FAKE + 4096, FAKE + 8192, FAKE + 12288) == -2
+    assert c(FAKE, 1, 1 << 62, 128, 1.0, FAKE + 4096, FAKE + 8192, FAKE + 12288) == -2
+    assert tfp8.decompress_raw(FAKE, FAKE + 4096, FAKE + 8192, big, 128, FAKE + 16384, 1) == -2
+    assert tfp8.reduce_fp8_raw(FAKE, FAKE + 65536, FAKE + 81920, 4, big, 128, 1.0, FAKE + 131072,
+                               FAKE + 196608, FAKE + 200704) == -2
+    assert tfp8.accumulate_raw(FAKE, FAKE + 8192, FAKE + 12288, FAKE + 16384, 0, big, 128, 1.0,
+                               FAKE + 32768, FAKE + 40960, FAKE + 45056) == -2
     assert c(FAKE, 2, 1024, 128, 1.0, FAKE + 4096, FAKE + 8192, FAKE + 12288) == -4  # dtype
     for t in (0.0, -1.0, float("inf"), float("nan"), 2.0 ** 70, 2.0 ** -70):
         assert c(FAKE, 0, 1024, 128, t, FAKE + 4096, FAKE + 8192, FAKE + 12288) == -6
