@@ -30,7 +30,7 @@ def test_source_hash_ignores_comments_and_whitespace(tmp_path):
     text = f.read_text()
     f.write_text("// a new comment\n/* and a block\n comment */\n" + text.replace("\n", "\n\n", 3))
     assert bench.kernel_source_hash(str(copy)) == h0
-    f.write_text(text.replace("kThreads", "kThreadz", 1))
+    f.write_text(text + "\nstatic const int one_more_constant = 1;\n")
     assert bench.kernel_source_hash(str(copy)) != h0
 
 
