@@ -53,56 +53,16 @@
 
 namespace tfp8 {
 
-// Workgroup size of each kernel.  No kernel shares anything between its wavefronts (no LDS, no
-// barriers), so the size only decides how wavefront slots are handed out and given back: a
-// workgroup's slots are freed when its last wavefront ends.
-#ifndef TFP8_COMPRESS_THREADS
-#define TFP8_COMPRESS_THREADS 64
-#endif
-#ifndef TFP8_DECOMPRESS_THREADS
-#define TFP8_DECOMPRESS_THREADS 256
-#endif
-#ifndef TFP8_REDUCE_THREADS
-#define TFP8_REDUCE_THREADS 256
-#endif
-#ifndef TFP8_ACCUMULATE_THREADS
-#define TFP8_ACCUMULATE_THREADS 256
-#endif
-#ifndef TFP8_COMPRESS_XCD_REMAP
-#define TFP8_COMPRESS_XCD_REMAP 1
-#endif
-#ifndef TFP8_DECOMPRESS_XCD_REMAP
-#define TFP8_DECOMPRESS_XCD_REMAP 0
-#endif
-#ifndef TFP8_REDUCE_XCD_REMAP
-#define TFP8_REDUCE_XCD_REMAP 0
-#endif
-#ifndef TFP8_ACCUMULATE_XCD_REMAP
-#define TFP8_ACCUMULATE_XCD_REMAP 0
-#endif
-constexpr int kCompressThreads = TFP8_COMPRESS_THREADS;
-constexpr int kDecompressThreads = TFP8_DECOMPRESS_THREADS;
-constexpr int kReduceThreads = TFP8_REDUCE_THREADS;
-constexpr int kAccumulateThreads = TFP8_ACCUMULATE_THREADS;
-constexpr int kFixThreads = 256;
-constexpr bool kCompressRemap = TFP8_COMPRESS_XCD_REMAP != 0;
-constexpr bool kDecompressRemap = TFP8_DECOMPRESS_XCD_REMAP != 0;
-constexpr bool kReduceRemap = TFP8_REDUCE_XCD_REMAP != 0;
-constexpr bool kAccumulateRemap = TFP8_ACCUMULATE_XCD_REMAP != 0;
+constexpr int kThreads = 256;  // 4 wavefronts per workgroup (compress: 1 or 4, see its launch)
 
-// Global index of this wavefront among the launch's gridDim.x * NT / 64.  With the remap on,
-// workgroup b (handed to XCD b mod 8 by the dispatcher's round robin) takes the slot
-// (b mod 8) * gridDim.x / 8 + b / 8, so that each XCD streams one contiguous eighth of the
-// tiles; the host then launches a multiple of 8 workgroups.
-template <int NT, bool REMAP>
-__device__ __forceinline__ int64_t wave_index() {
+// Index of this wavefront among the launch's, for kernels launched with any workgroup size.  With
+// `remap`, workgroup b, which the dispatcher hands to XCD b mod 8 in round robin, takes the slot
+// (b mod 8) * gridDim.x / 8 + b / 8, so that each XCD streams one contiguous eighth of the tiles
+// (the host then launches a multiple of 8 workgroups).
+__device__ __forceinline__ int64_t wave_index(bool remap) {
   int64_t b = blockIdx.x;
-  if constexpr (REMAP) b = (b & 7) * (int64_t)(gridDim.x >> 3) + (b >> 3);
-  return (b * NT + threadIdx.x) >> 6;
-}
-template <int NT>
-__device__ __forceinline__ int64_t wave_count() {
-  return ((int64_t)gridDim.x * NT) >> 6;
+  if (remap) b = (b & 7) * (int64_t)(gridDim.x >> 3) + (b >> 3);
+  return (b * blockDim.x + threadIdx.x) >> 6;
 }
 
 // Variant bits of the *_ex entry points, as compile-time kernel parameters.
@@ -221,11 +181,11 @@ __device__ __forceinline__ void load_compress_in(CompressIn<B, F32IN> &in, const
 }
 
 template <int B, bool F32IN, int FLAGS>
-__global__ __launch_bounds__(kCompressThreads) void k_compress(const void *__restrict__ xin, int64_t nb,
+__global__ __launch_bounds__(kThreads) void k_compress(const void *__restrict__ xin, int64_t nb,
                                                        float TBB, float sqrtTB, float C,
                                                        float invC, uint8_t *__restrict__ codes,
                                                        float *__restrict__ alpha_out,
-                                                       float *__restrict__ scale_out) {
+                                                       float *__restrict__ scale_out, bool remap) {
   constexpr int L = lanes_per_block(B);  // lanes per block
   constexpr int BPW = 64 / L;            // blocks per wavefront (one tile)
   constexpr int RS = 8 * L;              // run stride
@@ -238,8 +198,8 @@ __global__ __launch_bounds__(kCompressThreads) void k_compress(const void *__res
   const int bw = lane / L;
   const int pj = ROT ? lane_perm<L>(j) : j;
   const float sj = ROT ? lane_sign<L>(j) : 1.0f;
-  const int64_t wave = wave_index<kCompressThreads, kCompressRemap>();
-  const int64_t nwaves = wave_count<kCompressThreads>();
+  const int64_t wave = wave_index(remap);
+  const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
   const int64_t ntiles = (int64_t)(((uint64_t)nb + BPW - 1) / BPW);  // nb >= 0
   // packed bfloat16 (1, 1) and (1, -1), kept in registers for v_dot2_f32_bf16
   const uint32_t ones = 0x3F803F80u, plus_minus = 0xBF803F80u;
@@ -357,7 +317,7 @@ __device__ __forceinline__ void load_decompress_in(DecompressIn<B> &in, const ui
 }
 
 template <int B, bool F32OUT, int FLAGS>
-__global__ __launch_bounds__(kDecompressThreads) void k_decompress(const uint8_t *__restrict__ codes,
+__global__ __launch_bounds__(kThreads) void k_decompress(const uint8_t *__restrict__ codes,
                                                          const float *__restrict__ alpha,
                                                          const float *__restrict__ scale,
                                                          int64_t nb, float inv_sqrt_b,
@@ -373,8 +333,8 @@ __global__ __launch_bounds__(kDecompressThreads) void k_decompress(const uint8_t
   const int bw = lane / L;
   const int pj = ROT ? lane_perm<L>(j) : j;
   const float sj = ROT ? lane_sign<L>(j) : 1.0f;
-  const int64_t wave = wave_index<kDecompressThreads, kDecompressRemap>();
-  const int64_t nwaves = wave_count<kDecompressThreads>();
+  const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
+  const int64_t nwaves = ((int64_t)gridDim.x * kThreads) >> 6;
   const int64_t ntiles = (int64_t)(((uint64_t)nb + BPW - 1) / BPW);  // nb >= 0
 
   DecompressIn<B> cur;  // groups past the last block re-read the last block, store nothing
@@ -450,7 +410,7 @@ __global__ __launch_bounds__(kDecompressThreads) void k_decompress(const uint8_t
 // arithmetic; PB = 0: any P, in chunks of 8.
 
 template <int B, int PB, int FLAGS>
-__global__ __launch_bounds__(kReduceThreads) void k_reduce(const uint8_t *__restrict__ codes,
+__global__ __launch_bounds__(kThreads) void k_reduce(const uint8_t *__restrict__ codes,
                                                      const float *__restrict__ alpha,
                                                      const float *__restrict__ scale, int P,
                                                      int64_t n, int64_t nb, float TB,
@@ -467,8 +427,8 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce(const uint8_t *__rest
   const int lane = threadIdx.x & 63;
   const int j = lane % L;
   const int bw = lane / L;
-  const int64_t wave = wave_index<kReduceThreads, kReduceRemap>();
-  const int64_t nwaves = wave_count<kReduceThreads>();
+  const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
+  const int64_t nwaves = ((int64_t)gridDim.x * kThreads) >> 6;
   const int64_t ntiles = (int64_t)(((uint64_t)nb + BPW - 1) / BPW);  // nb >= 0
 
   for (int64_t tile = wave; tile < ntiles; tile += nwaves) {
@@ -589,7 +549,7 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce(const uint8_t *__rest
 // keeps the streaming kernel's registers, and so its occupancy, at those of compress.
 
 template <int B, bool F32IN, int FLAGS>
-__global__ __launch_bounds__(kAccumulateThreads) void k_accumulate(
+__global__ __launch_bounds__(kThreads) void k_accumulate(
     const uint8_t *codes, const float *alpha, const float *scale, const void *__restrict__ grad,
     int64_t nb, float TBB, float sqrtTBB, float gscale, float C, float invC, uint8_t *codes_out,
     float *alpha_out, float *scale_out) {
@@ -605,8 +565,8 @@ __global__ __launch_bounds__(kAccumulateThreads) void k_accumulate(
   const int bw = lane / L;
   const int pj = ROT ? lane_perm<L>(j) : j;
   const float sj = ROT ? lane_sign<L>(j) : 1.0f;
-  const int64_t wave = wave_index<kAccumulateThreads, kAccumulateRemap>();
-  const int64_t nwaves = wave_count<kAccumulateThreads>();
+  const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
+  const int64_t nwaves = ((int64_t)gridDim.x * kThreads) >> 6;
   const int64_t ntiles = (int64_t)(((uint64_t)nb + BPW - 1) / BPW);  // nb >= 0
   const uint32_t ones = 0x3F803F80u, plus_minus = 0xBF803F80u;
 
@@ -837,7 +797,7 @@ __device__ __forceinline__ void accumulate_block_split(
 // the runs of 64 in turn and works through each run's marked blocks 64 / L at a time, one group
 // of L lanes per block.
 template <int B, bool F32IN, int FLAGS>
-__global__ __launch_bounds__(kFixThreads) void k_accumulate_fix(
+__global__ __launch_bounds__(kThreads) void k_accumulate_fix(
     const uint8_t *codes, const float *scale, const void *__restrict__ grad, int64_t nb,
     float TBB, float C, double gscale, uint8_t *codes_out, float *alpha_out, float *scale_out) {
   constexpr int kRuns = 2;
@@ -846,8 +806,8 @@ __global__ __launch_bounds__(kFixThreads) void k_accumulate_fix(
   const int lane = threadIdx.x & 63;
   const int j = lane & (L - 1);
   const int bw = lane / L;
-  const int64_t wave = wave_index<kFixThreads, false>();
-  const int64_t nwaves = wave_count<kFixThreads>();
+  const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
+  const int64_t nwaves = ((int64_t)gridDim.x * kThreads) >> 6;
   const int64_t nscan = (nb + 64 * kRuns - 1) / (64 * kRuns);
 
   for (int64_t t = wave; t < nscan; t += nwaves) {
@@ -919,9 +879,7 @@ bool target_ok(float t) {
 // compute unit (0: no cap) beyond which the wavefronts loop over tiles.  Measured on MI355X:
 // compress and decompress stream fastest with one tile per wavefront and no loop (the
 // hardware keeps the CUs fed as wavefronts retire); the reduce, whose wavefronts each carry
-// P loads in flight, is fastest with 32 workgroups per CU.  Giving each XCD a contiguous
-// eighth of the tiles speeds compress up by 2% (8 bf16 shards of 4096 x 3584: 450 -> 440 us)
-// and slows decompress and the reduce down, so only compress uses it.
+// P loads in flight, is fastest with 32 workgroups per CU.
 int cu_count() {
   // compute units of the current device, looked up once per device (any thread may race to
   // fill an entry; they all store the same value)
@@ -939,10 +897,16 @@ int cu_count() {
   return cus;
 }
 
+// Compress of a large input is 2-4% faster with 64-thread workgroups and each XCD on a
+// contiguous eighth of the tiles: 77% -> 80% of HBM peak for every bf16 input measured from
+// 1.9 to 4.3 GB.  At 1.1 GB the two shapes tie, and on inputs of 134-268 MB the remapped one is
+// 3-10% slower, hence the threshold.  Decompress and the reduce were slower remapped.
+constexpr int64_t kCompressRemapMinBytes = (int64_t)3 << 29;  // 1.5 GiB of input
+
 // The cap without `per_cu` keeps gridDim.x * nt (the work-items of the launch, a 32-bit count
 // in the dispatch packet) at 2^30; larger inputs loop.  Under the XCD remap the count is
 // rounded up to a multiple of 8, and the extra wavefronts find no tile.
-unsigned grid_for(int64_t tiles, int per_cu, int nt, bool remap) {
+unsigned grid_for(int64_t tiles, int per_cu, int nt = kThreads, bool remap = false) {
   const int64_t wgs = (tiles + (nt / 64) - 1) / (nt / 64);
   const int64_t cap = per_cu > 0 ? (int64_t)cu_count() * per_cu : ((int64_t)1 << 30) / nt;
   int64_t g = wgs < cap ? (wgs > 0 ? wgs : 1) : cap;
@@ -965,10 +929,13 @@ void launch_compress_t(const void *x, int64_t nb, float target, uint8_t *codes, 
   const double Cd = ROT ? Q * sqrt((double)B) : Q;
   const float C = (float)Cd, invC = (float)(1.0 / Cd);
   constexpr int BPW = 64 / lanes_per_block(B);  // blocks per tile
-  const unsigned grid =
-      grid_for((nb + BPW - 1) / BPW, TFP8_COMPRESS_WGS_PER_CU, kCompressThreads, kCompressRemap);
-  hipLaunchKernelGGL((k_compress<B, F32, FLAGS>), dim3(grid), dim3(kCompressThreads), 0, st, x, nb, TBB,
-                     sqrtTB, C, invC, codes, alpha, scale);
+  // Large inputs stream faster with one wavefront per workgroup and each XCD on a contiguous
+  // eighth of the tiles; smaller ones with 4 wavefronts per workgroup in dispatch order.
+  const bool remap = nb * B * (F32 ? 4 : 2) >= kCompressRemapMinBytes;
+  const int nt = remap ? 64 : kThreads;
+  const unsigned grid = grid_for((nb + BPW - 1) / BPW, TFP8_COMPRESS_WGS_PER_CU, nt, remap);
+  hipLaunchKernelGGL((k_compress<B, F32, FLAGS>), dim3(grid), dim3(nt), 0, st, x, nb, TBB,
+                     sqrtTB, C, invC, codes, alpha, scale, remap);
 }
 
 template <int B, bool F32>
@@ -989,9 +956,8 @@ void launch_decompress_t(const uint8_t *codes, const float *alpha, const float *
   constexpr bool ROT = !(FLAGS & kNoRotation);
   const float inv_sqrt_b = ROT ? (float)(1.0 / sqrt((double)B)) : 1.0f;
   constexpr int BPW = 64 / decompress_lanes(B);  // blocks per tile
-  const unsigned grid = grid_for((nb + BPW - 1) / BPW, TFP8_DECOMPRESS_WGS_PER_CU,
-                                 kDecompressThreads, kDecompressRemap);
-  hipLaunchKernelGGL((k_decompress<B, F32, FLAGS>), dim3(grid), dim3(kDecompressThreads), 0, st, codes,
+  const unsigned grid = grid_for((nb + BPW - 1) / BPW, TFP8_DECOMPRESS_WGS_PER_CU);
+  hipLaunchKernelGGL((k_decompress<B, F32, FLAGS>), dim3(grid), dim3(kThreads), 0, st, codes,
                      alpha, scale, nb, inv_sqrt_b, out);
 }
 
@@ -1015,10 +981,9 @@ void launch_reduce_t(const uint8_t *codes, const float *alpha, const float *scal
   // energy is that of the sum, sum(r^2) = sum(z^2)
   const float TB = target * (float)B;
   constexpr int BPW = 64 / (B / 16);
-  const unsigned grid =
-      grid_for((nb + BPW - 1) / BPW, TFP8_REDUCE_WGS_PER_CU, kReduceThreads, kReduceRemap);
+  const unsigned grid = grid_for((nb + BPW - 1) / BPW, TFP8_REDUCE_WGS_PER_CU);
 #define TFP8_LAUNCH_REDUCE(PB)                                                                  \
-  hipLaunchKernelGGL((k_reduce<B, PB, FLAGS>), dim3(grid), dim3(kReduceThreads), 0, st, codes, alpha, \
+  hipLaunchKernelGGL((k_reduce<B, PB, FLAGS>), dim3(grid), dim3(kThreads), 0, st, codes, alpha, \
                      scale, P, n, nb, TB, codes_out, alpha_out, scale_out)
   switch (P) {
     case 1: TFP8_LAUNCH_REDUCE(1); break;
@@ -1056,15 +1021,13 @@ void launch_accumulate_t(const uint8_t *codes, const float *alpha, const float *
   const double Cd = ROT ? Q * sqrt((double)B) : Q;
   const float C = (float)Cd, invC = (float)(1.0 / Cd);
   constexpr int BPW = 64 / lanes_per_block(B);  // blocks per tile
-  const unsigned grid = grid_for((nb + BPW - 1) / BPW, TFP8_COMPRESS_WGS_PER_CU,
-                                 kAccumulateThreads, kAccumulateRemap);
-  hipLaunchKernelGGL((k_accumulate<B, F32, FLAGS>), dim3(grid), dim3(kAccumulateThreads), 0, st, codes,
+  const unsigned grid = grid_for((nb + BPW - 1) / BPW, TFP8_COMPRESS_WGS_PER_CU);
+  hipLaunchKernelGGL((k_accumulate<B, F32, FLAGS>), dim3(grid), dim3(kThreads), 0, st, codes,
                      alpha, scale, grad, nb, TBB, sqrtTBB, (float)gscale, C, invC, codes_out,
                      alpha_out, scale_out);
   // the set-aside blocks: codes and s from the inputs (untouched for them), -alpha from alpha_out
-  const unsigned grid_fix =
-      grid_for((nb + 127) / 128, TFP8_ACCUMULATE_FIX_WGS_PER_CU, kFixThreads, false);
-  hipLaunchKernelGGL((k_accumulate_fix<B, F32, FLAGS>), dim3(grid_fix), dim3(kFixThreads), 0, st,
+  const unsigned grid_fix = grid_for((nb + 127) / 128, TFP8_ACCUMULATE_FIX_WGS_PER_CU);
+  hipLaunchKernelGGL((k_accumulate_fix<B, F32, FLAGS>), dim3(grid_fix), dim3(kThreads), 0, st,
                      codes, scale, grad, nb, TBB, C, gscale, codes_out, alpha_out, scale_out);
 }
 

@@ -398,6 +398,49 @@ def test_accumulate_zero_main_gradient_equals_compress(oracle, tfp8):
     check_compress(oracle, tfp8, g, B, what="compress of the same gradient")
 
 
+@pytest.mark.parametrize("dtype,extra_blocks", [("bf16", -3), ("bf16", 13), ("f32", 5)])
+def test_compress_both_launch_shapes(oracle, tfp8, dtype, extra_blocks):
+    # Compress picks its launch shape by input size: below 1.5 GiB four wavefronts per
+    # workgroup in dispatch order, from 1.5 GiB one wavefront per workgroup with each XCD on a
+    # contiguous eighth of the tiles (grid rounded up to a multiple of 8).  Inputs just below
+    # and above the switch, each with a ragged last tile (block count not a multiple of 8).  The
+    # input is one random tile of 2^20 elements in seven power-of-two scalings, so a block read
+    # from the wrong place shows.  Sampled blocks: both ends, the start of each eighth of the
+    # tiles, and 2048 random blocks.
+    B, T, tile = 128, 1.0, 1 << 20
+    esize = 2 if dtype == "bf16" else 4
+    nb = (3 << 29) // esize // B + extra_blocks
+    n = nb * B
+    base = bf16_bits_to_f32(random_bf16_bits(tile, seed=1536, scale=0.05))
+    scaled = [base * np.float32(2.0 ** (t - 3)) for t in range(7)]
+    if dtype == "bf16":
+        scaled = [f32_to_bf16_bits(v) for v in scaled]
+    x = np.empty(n, scaled[0].dtype)
+    for t in range(-(-n // tile)):
+        seg = x[t * tile:(t + 1) * tile]
+        seg[:] = scaled[t % 7][:seg.size]
+    ntiles = -(-nb // 8)
+    eighths = np.array([(k * -(-ntiles // 8)) * 8 for k in range(8)])
+    rng = np.random.default_rng(1536)
+    idx = np.unique(np.concatenate([np.arange(64), np.arange(nb - 64, nb),
+                                    (eighths[:, None] + np.arange(-8, 8)).reshape(-1) % nb,
+                                    rng.integers(0, nb, 2048)]))
+    say(f"  launch shapes: {dtype}, {n * esize / 2**30:.4f} GiB of input, nb = {nb}, "
+        f"{idx.size} sampled blocks")
+    xg = (bits_to_gpu(x) if dtype == "bf16" else f32_to_gpu(x))
+    q, a, s = tfp8.compress(xg, B, T)
+    torch.cuda.synchronize()
+    del xg
+    idx_g = torch.from_numpy(idx).to(DEV)
+    xs = np.ascontiguousarray(x.reshape(nb, B)[idx]).reshape(-1)
+    del x
+    rq, ra, rs, rt = oracle.compress(xs, B, T, with_quot=True)
+    nmis = assert_codes_match(cpu(q.view(nb, B)[idx_g]).reshape(-1), rq, rt,
+                              what=f"launch shapes {dtype} {nb} blocks")
+    assert_scales(cpu(a[idx_g]), cpu(s[idx_g]), ra, rs, what=f"launch shapes {dtype} {nb} blocks")
+    say(f"  launch shapes: tie mismatches {nmis}")
+
+
 def test_offsets_beyond_2_31_elements(oracle, tfp8):
     # n = 513 * 2^22 > 2^31 elements: element indexes pass 2^31, bfloat16 byte offsets pass
     # 2^32 and code byte offsets pass 2^31.  The input is one random tile of 2^22 elements in
