@@ -128,11 +128,34 @@ def _stream(t: torch.Tensor) -> int:
 
 
 def _need_gpu(*ts):
+    """Every tensor on the same GPU and contiguous (the library reads flat buffers)."""
+    dev = None
     for t in ts:
         if not (isinstance(t, torch.Tensor) and t.is_cuda):
             raise ValueError("tfp8 operates on GPU tensors only (no CPU path)")
         if not t.is_contiguous():
             raise ValueError("tfp8 needs contiguous tensors")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"tensors on different devices ({dev} and {t.device})")
+
+
+def _need_buf(t: torch.Tensor, dtype: torch.dtype, numel: int, name: str):
+    """A buffer the kernels read or write: its dtype and exact element count, checked here
+    because the C ABI takes bare pointers and cannot."""
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.numel() != numel:
+        raise ValueError(f"{name} must have {numel} elements, got {t.numel()}")
+
+
+def _blocks(n: int, block: int) -> int:
+    if block not in SUPPORTED_BLOCKS:
+        raise ValueError(f"block must be one of {SUPPORTED_BLOCKS}, got {block}")
+    if n % block:
+        raise ValueError(f"{n} elements are not a multiple of the block size {block}")
+    return n // block
 
 
 def compress(x: torch.Tensor, block: int = 128, target: float = 1.0, out=None, flags: int = 0):
@@ -146,15 +169,20 @@ def compress(x: torch.Tensor, block: int = 128, target: float = 1.0, out=None, f
     else:
         raise ValueError(f"unsupported input dtype {x.dtype}")
     n = x.numel()
-    nb = n // block if block > 0 else 0
+    nb = _blocks(n, block)
     if out is None:
         codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
         alpha = torch.empty(nb, dtype=torch.float32, device=x.device)
         scale = torch.empty(nb, dtype=torch.float32, device=x.device)
     else:
         codes, alpha, scale = out
-    _check(compress_raw(x.data_ptr(), dt, n, block, float(target), codes.data_ptr(),
-                        alpha.data_ptr(), scale.data_ptr(), _stream(x), flags))
+        _need_gpu(x, codes, alpha, scale)
+    _need_buf(codes, torch.uint8, n, "codes")
+    _need_buf(alpha, torch.float32, nb, "alpha")
+    _need_buf(scale, torch.float32, nb, "scale")
+    with torch.cuda.device(x.device):
+        _check(compress_raw(x.data_ptr(), dt, n, block, float(target), codes.data_ptr(),
+                            alpha.data_ptr(), scale.data_ptr(), _stream(x), flags))
     return codes, alpha, scale
 
 
@@ -168,10 +196,19 @@ def decompress(codes: torch.Tensor, alpha: torch.Tensor, scale: torch.Tensor, bl
         dt = BF16
     else:
         raise ValueError(f"unsupported output dtype {dtype}")
+    n = codes.numel()
+    nb = _blocks(n, block)
+    _need_buf(codes, torch.uint8, n, "codes")
+    _need_buf(alpha, torch.float32, nb, "alpha")
+    _need_buf(scale, torch.float32, nb, "scale")
     if out is None:
         out = torch.empty(codes.shape, dtype=dtype, device=codes.device)
-    _check(decompress_raw(codes.data_ptr(), alpha.data_ptr(), scale.data_ptr(), codes.numel(),
-                          block, out.data_ptr(), dt, _stream(codes), flags))
+    else:
+        _need_gpu(codes, out)
+        _need_buf(out, dtype, n, "out")
+    with torch.cuda.device(codes.device):
+        _check(decompress_raw(codes.data_ptr(), alpha.data_ptr(), scale.data_ptr(), n, block,
+                              out.data_ptr(), dt, _stream(codes), flags))
     return out
 
 
@@ -179,18 +216,28 @@ def reduce_fp8(codes: torch.Tensor, alpha: torch.Tensor, scale: torch.Tensor, bl
                target: float = 1.0, out=None, flags: int = 0):
     """codes [P, ...], alpha and scale [P, nb] -> (codes [...], alpha [nb], scale [nb])."""
     _need_gpu(codes, alpha, scale)
+    if codes.dim() < 2:
+        raise ValueError("codes must be stacked as [P, ...]")
     P = codes.shape[0]
     n = codes[0].numel()
-    nb = n // block if block > 0 else 0
+    nb = _blocks(n, block)
+    _need_buf(codes, torch.uint8, P * n, "codes")
+    _need_buf(alpha, torch.float32, P * nb, "alpha")
+    _need_buf(scale, torch.float32, P * nb, "scale")
     if out is None:
         codes_out = torch.empty(codes.shape[1:], dtype=torch.uint8, device=codes.device)
         alpha_out = torch.empty(nb, dtype=torch.float32, device=codes.device)
         scale_out = torch.empty(nb, dtype=torch.float32, device=codes.device)
     else:
         codes_out, alpha_out, scale_out = out
-    _check(reduce_fp8_raw(codes.data_ptr(), alpha.data_ptr(), scale.data_ptr(), P, n, block,
-                          float(target), codes_out.data_ptr(), alpha_out.data_ptr(),
-                          scale_out.data_ptr(), _stream(codes), flags))
+        _need_gpu(codes, codes_out, alpha_out, scale_out)
+        _need_buf(codes_out, torch.uint8, n, "codes_out")
+        _need_buf(alpha_out, torch.float32, nb, "alpha_out")
+        _need_buf(scale_out, torch.float32, nb, "scale_out")
+    with torch.cuda.device(codes.device):
+        _check(reduce_fp8_raw(codes.data_ptr(), alpha.data_ptr(), scale.data_ptr(), P, n, block,
+                              float(target), codes_out.data_ptr(), alpha_out.data_ptr(),
+                              scale_out.data_ptr(), _stream(codes), flags))
     return codes_out, alpha_out, scale_out
 
 
@@ -208,11 +255,20 @@ def accumulate(codes: torch.Tensor, alpha: torch.Tensor, scale: torch.Tensor, gr
     n = codes.numel()
     if grad.numel() != n:
         raise ValueError("grad and codes must have the same number of elements")
+    nb = _blocks(n, block)
+    _need_buf(codes, torch.uint8, n, "codes")
+    _need_buf(alpha, torch.float32, nb, "alpha")
+    _need_buf(scale, torch.float32, nb, "scale")
     if inplace:
         out = (codes, alpha, scale)
     elif out is None:
         out = (torch.empty_like(codes), torch.empty_like(alpha), torch.empty_like(scale))
-    _check(accumulate_raw(codes.data_ptr(), alpha.data_ptr(), scale.data_ptr(), grad.data_ptr(), dt,
-                          n, block, float(target), out[0].data_ptr(), out[1].data_ptr(),
-                          out[2].data_ptr(), _stream(codes), flags))
+    else:
+        _need_gpu(codes, *out)
+        for t, ref, name in zip(out, (codes, alpha, scale), ("codes_out", "alpha_out", "scale_out")):
+            _need_buf(t, ref.dtype, ref.numel(), name)
+    with torch.cuda.device(codes.device):
+        _check(accumulate_raw(codes.data_ptr(), alpha.data_ptr(), scale.data_ptr(), grad.data_ptr(),
+                              dt, n, block, float(target), out[0].data_ptr(), out[1].data_ptr(),
+                              out[2].data_ptr(), _stream(codes), flags))
     return out

@@ -242,6 +242,45 @@ def test_guard_bytes_untouched(tfp8):
     assert np.all(d[:pad] == -3.0) and np.all(d[pad + n:] == -3.0)
 
 
+def test_wrappers_check_buffers_before_launch(tfp8):
+    # the C ABI takes bare pointers; the tensor wrappers check dtypes and element counts of every
+    # buffer first, so a wrong one raises instead of being read or written past its end
+    B, nb = 128, 4
+    n = nb * B
+    x = torch.zeros(n, dtype=torch.bfloat16, device=DEV)
+    u8 = lambda k: torch.zeros(k, dtype=torch.uint8, device=DEV)
+    f32 = lambda k: torch.zeros(k, dtype=torch.float32, device=DEV)
+    with pytest.raises(ValueError, match="block"):
+        tfp8.compress(x, 96)
+    with pytest.raises(ValueError, match="multiple"):
+        tfp8.compress(x[:n - 2], B)
+    with pytest.raises(ValueError, match="alpha"):
+        tfp8.compress(x, B, out=(u8(n), f32(nb - 1), f32(nb)))
+    with pytest.raises(ValueError, match="codes"):
+        tfp8.compress(x, B, out=(f32(n), f32(nb), f32(nb)))
+    with pytest.raises(ValueError, match="scale"):
+        tfp8.decompress(u8(n), f32(nb), f32(nb - 1), B)
+    with pytest.raises(ValueError, match="out"):
+        tfp8.decompress(u8(n), f32(nb), f32(nb), B, torch.float32, out=f32(n - 1))
+    with pytest.raises(ValueError, match="out"):
+        tfp8.decompress(u8(n), f32(nb), f32(nb), B, torch.float32,
+                        out=torch.zeros(n, dtype=torch.bfloat16, device=DEV))
+    with pytest.raises(ValueError, match="stacked"):
+        tfp8.reduce_fp8(u8(n), f32(nb), f32(nb), B)
+    with pytest.raises(ValueError, match="alpha"):
+        tfp8.reduce_fp8(u8(2 * n).view(2, n), f32(nb), f32(2 * nb), B)
+    with pytest.raises(ValueError, match="codes_out"):
+        tfp8.reduce_fp8(u8(2 * n).view(2, n), f32(2 * nb), f32(2 * nb), B,
+                        out=(u8(n + 16), f32(nb), f32(nb)))
+    with pytest.raises(ValueError, match="same number"):
+        tfp8.accumulate(u8(n), f32(nb), f32(nb), x[:n - B], B)
+    with pytest.raises(ValueError, match="scale_out"):
+        tfp8.accumulate(u8(n), f32(nb), f32(nb), x, B, out=(u8(n), f32(nb), f32(nb + 1)))
+    with pytest.raises(ValueError, match="contiguous"):
+        tfp8.decompress(u8(2 * n)[::2], f32(nb), f32(nb), B)
+    torch.cuda.synchronize()
+
+
 def test_bitwise_deterministic_and_stream_safe(tfp8):
     x = bits_to_gpu(make_shard(2).reshape(-1))
     r1 = tfp8.compress(x, 128, 1.0)
