@@ -616,12 +616,20 @@ __global__ __launch_bounds__(kThreads) void k_accumulate(
     // bfloat16-subnormal main block) both terms are carried as v * 2^E0, E0 the larger of their
     // exponents (|gscale (s / alpha) dec| < 2^(es - ea + 15)), with the factor's mantissa and
     // exponent apart.
+    // A main term below 2^-60 of the block's largest |H g| cannot move alpha by more than 2^-60
+    // relative, nor a code unless its quotient lies within 2^-51 of a rounding midpoint: it is
+    // left out rather than carried through that path (mh >= 2^(exponent_of(mh) - 1)).
     const int es = exponent_of(sp), ea = exponent_of(ap);
-    const bool in_range = (sp == 0.0f) || (es - ea > -100 && es - ea < 100);
+    const bool negligible = mh != 0.0f && es - ea + 15 <= exponent_of(mh) - 61;
+    const bool in_range = (sp == 0.0f) || negligible || (es - ea > -100 && es - ea < 100);
     float gm;
     int E0 = 0;
     if (in_range) {
-      gm = (sp == 0.0f) ? 0.0f : sj * (gscale * __fdiv_rn(sp, ap));
+      // the factor needs no correct rounding: the codes are decided against the sum's own
+      // maximum, and a 1-ulp change of it moves w by 2^-23 of the main term
+      gm = (sp == 0.0f || negligible)
+               ? 0.0f
+               : sj * (gscale * (sp * __builtin_amdgcn_rcpf(ap)));
     } else {
       E0 = max(mh == 0.0f ? -(1 << 20) : exponent_of(mh), es - ea + 15);
 #pragma unroll
@@ -648,17 +656,16 @@ __global__ __launch_bounds__(kThreads) void k_accumulate(
     const bool defer = M < 0.5f * fmaxf(mh, fabsf(gm) * Q);
     float cm = 0.0f, a_out = 1.0f, s_out = 0.0f;
     if (!defer) {
-      if (E0 == 0 && M >= 0x1p-40f && M <= 0x1p60f) {
-        // energy of z from the codes' values u = w c (Parseval): alpha = c sqrt(T B^2 / sum u^2)
-        const float c = __fdiv_rn(Q, M);
-        float su = 0.0f;
+      if (E0 == 0 && M >= 0x1p-40f && M <= 0x1p56f) {
+        // energy of z from w (Parseval): alpha = sqrt(T B^2 / sum w^2); with M in this range
+        // the sum of squares stays within float32 (at most B M^2 <= 2^121), and squares that
+        // underflow are below 2^-70 of the largest
+        float sw = 0.0f;
 #pragma unroll
-        for (int r = 0; r < N; ++r) {
-          const float u = v[r] * c;
-          su = fmaf(u, u, su);
-        }
-        const float SU = group_sum<L>(su);
-        a_out = fminf(fmaxf(c * sqrtTBB * __builtin_amdgcn_rsqf(SU), 0x1p-126f), 0x1p126f);
+        for (int r = 0; r < N; ++r) sw = fmaf(v[r], v[r], sw);
+        const float SW = group_sum<L>(sw);
+        const float c = __fdiv_rn(Q, M);
+        a_out = fminf(fmaxf(sqrtTBB * __builtin_amdgcn_rsqf(SW), 0x1p-126f), 0x1p126f);
         s_out = a_out * M * invC;
         cm = c * sj;
       } else {
