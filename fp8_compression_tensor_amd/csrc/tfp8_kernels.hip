@@ -10,10 +10,14 @@
 //
 // Layout.  A block of B elements is held by a group of L lanes (compress and accumulate:
 // L = 8, or 4 at B = 64 so that a lane still holds 16 elements; decompress: L = 8) or B/16
-// lanes (reduce).  In the L-lane kernels lane j of a group holds B/L elements as runs of 8 consecutive
-// elements, run g covering elements [8Lg + 8j, 8Lg + 8j + 8) of the block: each group reads or
-// writes whole runs of 8L consecutive elements.  At L = 8 index bits 0-2 and 6.. live in
-// registers, bits 3-5 across the lanes.
+// lanes (reduce).  In the L-lane kernels lane j of a group holds B/L elements as runs of 8
+// consecutive elements, run g covering elements [8Lg + 8j, 8Lg + 8j + 8) of the block: each
+// group reads or writes whole runs of 8L consecutive elements.  At L = 8 index bits 0-2 and 6..
+// live in registers, bits 3-5 across the lanes.
+//
+// Launch.  One tile (64/L blocks) per wavefront, 16-byte non-temporal loads and stores, no LDS,
+// no atomics.  Compress of an input of 1.5 GiB or more launches one-wavefront workgroups and
+// gives each XCD a contiguous eighth of the tiles (kCompressRemapMinBytes below).
 //
 // Transform.  w = H x (unnormalised) is computed by an in-register FWHT over the register
 // bits and a 3-stage DPP butterfly over the lane bits (tfp8_device.hpp), which leaves lane j
