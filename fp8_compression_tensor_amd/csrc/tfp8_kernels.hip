@@ -15,8 +15,8 @@
 // group reads or writes whole runs of 8L consecutive elements.  At L = 8 index bits 0-2 and 6..
 // live in registers, bits 3-5 across the lanes.
 //
-// Launch.  One tile (64/L blocks) per wavefront, 16-byte non-temporal loads and stores, no LDS,
-// no atomics.  Compress of an input of 1.5 GiB or more launches one-wavefront workgroups and
+// Launch.  One tile (64/L blocks) per wavefront, 8- or 16-byte vector loads and stores per
+// lane, no LDS, no atomics.  Compress of an input of 1.5 GiB or more launches one-wavefront workgroups and
 // gives each XCD a contiguous eighth of the tiles (kCompressRemapMinBytes below).
 //
 // Transform.  w = H x (unnormalised) is computed by an in-register FWHT over the register
