@@ -51,6 +51,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <tuple>
 
 #include "../../include/tfp8.h"
 #include "tfp8_device.hpp"
@@ -925,12 +926,27 @@ unsigned grid_for(int64_t tiles, int per_cu, int nt = kThreads, bool remap = fal
   return (unsigned)g;
 }
 
-tfp8_status launched() {
-  return hipGetLastError() == hipSuccess ? TFP8_OK : TFP8_E_HIP;
+// Launches `kernel` with `args` converted to its parameter types, and returns the status of this
+// launch itself (hipLaunchKernel reports it directly, so an error left over from an earlier,
+// unrelated HIP call is not taken for this launch's).
+template <typename... KArgs, typename... Args>
+tfp8_status launch(void (*kernel)(KArgs...), unsigned grid, int threads, hipStream_t st,
+                   Args... args) {
+  static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel argument count");
+  std::tuple<KArgs...> held(static_cast<KArgs>(args)...);
+  void *argv[sizeof...(KArgs)];
+  std::apply([&argv](auto &...a) {
+    int i = 0;
+    ((argv[i++] = (void *)&a), ...);
+  }, held);
+  return hipLaunchKernel((const void *)kernel, dim3(grid), dim3(threads), argv, 0, st) ==
+                 hipSuccess
+             ? TFP8_OK
+             : TFP8_E_HIP;
 }
 
 template <int B, bool F32, int FLAGS>
-void launch_compress_t(const void *x, int64_t nb, float target, uint8_t *codes, float *alpha,
+tfp8_status launch_compress_t(const void *x, int64_t nb, float target, uint8_t *codes, float *alpha,
                        float *scale, hipStream_t st) {
   constexpr bool ROT = !(FLAGS & kNoRotation);
   const double Q = qmax_of<FLAGS>();
@@ -945,47 +961,50 @@ void launch_compress_t(const void *x, int64_t nb, float target, uint8_t *codes, 
   const bool remap = nb * B * (F32 ? 4 : 2) >= kCompressRemapMinBytes;
   const int nt = remap ? 64 : kThreads;
   const unsigned grid = grid_for((nb + BPW - 1) / BPW, TFP8_COMPRESS_WGS_PER_CU, nt, remap);
-  hipLaunchKernelGGL((k_compress<B, F32, FLAGS>), dim3(grid), dim3(nt), 0, st, x, nb, TBB,
-                     sqrtTB, C, invC, codes, alpha, scale, remap);
+  return launch(k_compress<B, F32, FLAGS>, grid, nt, st, x, nb, TBB, sqrtTB, C, invC, codes,
+                alpha, scale, remap);
 }
 
 template <int B, bool F32>
 tfp8_status launch_compress(const void *x, int64_t nb, float target, uint32_t flags,
                             uint8_t *codes, float *alpha, float *scale, hipStream_t st) {
   switch (flags) {
-    case 0: launch_compress_t<B, F32, 0>(x, nb, target, codes, alpha, scale, st); break;
-    case kInt8: launch_compress_t<B, F32, kInt8>(x, nb, target, codes, alpha, scale, st); break;
-    case kNoRotation: launch_compress_t<B, F32, kNoRotation>(x, nb, target, codes, alpha, scale, st); break;
-    default: launch_compress_t<B, F32, kInt8 | kNoRotation>(x, nb, target, codes, alpha, scale, st); break;
+    case 0: return launch_compress_t<B, F32, 0>(x, nb, target, codes, alpha, scale, st);
+    case kInt8: return launch_compress_t<B, F32, kInt8>(x, nb, target, codes, alpha, scale, st);
+    case kNoRotation:
+      return launch_compress_t<B, F32, kNoRotation>(x, nb, target, codes, alpha, scale, st);
+    default:
+      return launch_compress_t<B, F32, kInt8 | kNoRotation>(x, nb, target, codes, alpha, scale,
+                                                            st);
   }
-  return launched();
 }
 
 template <int B, bool F32, int FLAGS>
-void launch_decompress_t(const uint8_t *codes, const float *alpha, const float *scale, int64_t nb,
+tfp8_status launch_decompress_t(const uint8_t *codes, const float *alpha, const float *scale, int64_t nb,
                          void *out, hipStream_t st) {
   constexpr bool ROT = !(FLAGS & kNoRotation);
   const float inv_sqrt_b = ROT ? (float)(1.0 / sqrt((double)B)) : 1.0f;
   constexpr int BPW = 64 / decompress_lanes(B);  // blocks per tile
   const unsigned grid = grid_for((nb + BPW - 1) / BPW, TFP8_DECOMPRESS_WGS_PER_CU);
-  hipLaunchKernelGGL((k_decompress<B, F32, FLAGS>), dim3(grid), dim3(kThreads), 0, st, codes,
-                     alpha, scale, nb, inv_sqrt_b, out);
+  return launch(k_decompress<B, F32, FLAGS>, grid, kThreads, st, codes, alpha, scale, nb,
+                inv_sqrt_b, out);
 }
 
 template <int B, bool F32>
 tfp8_status launch_decompress(const uint8_t *codes, const float *alpha, const float *scale,
                               int64_t nb, uint32_t flags, void *out, hipStream_t st) {
   switch (flags) {
-    case 0: launch_decompress_t<B, F32, 0>(codes, alpha, scale, nb, out, st); break;
-    case kInt8: launch_decompress_t<B, F32, kInt8>(codes, alpha, scale, nb, out, st); break;
-    case kNoRotation: launch_decompress_t<B, F32, kNoRotation>(codes, alpha, scale, nb, out, st); break;
-    default: launch_decompress_t<B, F32, kInt8 | kNoRotation>(codes, alpha, scale, nb, out, st); break;
+    case 0: return launch_decompress_t<B, F32, 0>(codes, alpha, scale, nb, out, st);
+    case kInt8: return launch_decompress_t<B, F32, kInt8>(codes, alpha, scale, nb, out, st);
+    case kNoRotation:
+      return launch_decompress_t<B, F32, kNoRotation>(codes, alpha, scale, nb, out, st);
+    default:
+      return launch_decompress_t<B, F32, kInt8 | kNoRotation>(codes, alpha, scale, nb, out, st);
   }
-  return launched();
 }
 
 template <int B, int FLAGS>
-void launch_reduce_t(const uint8_t *codes, const float *alpha, const float *scale, int P,
+tfp8_status launch_reduce_t(const uint8_t *codes, const float *alpha, const float *scale, int P,
                      int64_t n, int64_t nb, float target, uint8_t *codes_out, float *alpha_out,
                      float *scale_out, hipStream_t st) {
   // the reduce works on r = sum_p g_p dec(q_p) directly, with or without the rotation: its
@@ -993,15 +1012,15 @@ void launch_reduce_t(const uint8_t *codes, const float *alpha, const float *scal
   const float TB = target * (float)B;
   constexpr int BPW = 64 / (B / 16);
   const unsigned grid = grid_for((nb + BPW - 1) / BPW, TFP8_REDUCE_WGS_PER_CU);
-#define TFP8_LAUNCH_REDUCE(PB)                                                                  \
-  hipLaunchKernelGGL((k_reduce<B, PB, FLAGS>), dim3(grid), dim3(kThreads), 0, st, codes, alpha, \
-                     scale, P, n, nb, TB, codes_out, alpha_out, scale_out)
+#define TFP8_LAUNCH_REDUCE(PB)                                                               \
+  return launch(k_reduce<B, PB, FLAGS>, grid, kThreads, st, codes, alpha, scale, P, n, nb, TB, \
+                codes_out, alpha_out, scale_out)
   switch (P) {
-    case 1: TFP8_LAUNCH_REDUCE(1); break;
-    case 2: TFP8_LAUNCH_REDUCE(2); break;
-    case 4: TFP8_LAUNCH_REDUCE(4); break;
-    case 8: TFP8_LAUNCH_REDUCE(8); break;
-    default: TFP8_LAUNCH_REDUCE(0); break;
+    case 1: TFP8_LAUNCH_REDUCE(1);
+    case 2: TFP8_LAUNCH_REDUCE(2);
+    case 4: TFP8_LAUNCH_REDUCE(4);
+    case 8: TFP8_LAUNCH_REDUCE(8);
+    default: TFP8_LAUNCH_REDUCE(0);
   }
 #undef TFP8_LAUNCH_REDUCE
 }
@@ -1011,16 +1030,14 @@ tfp8_status launch_reduce(const uint8_t *codes, const float *alpha, const float 
                           int64_t n, int64_t nb, float target, uint32_t flags, uint8_t *codes_out,
                           float *alpha_out, float *scale_out, hipStream_t st) {
   if (flags & kInt8)
-    launch_reduce_t<B, kInt8>(codes, alpha, scale, P, n, nb, target, codes_out, alpha_out,
-                              scale_out, st);
-  else
-    launch_reduce_t<B, 0>(codes, alpha, scale, P, n, nb, target, codes_out, alpha_out, scale_out,
-                          st);
-  return launched();
+    return launch_reduce_t<B, kInt8>(codes, alpha, scale, P, n, nb, target, codes_out, alpha_out,
+                                     scale_out, st);
+  return launch_reduce_t<B, 0>(codes, alpha, scale, P, n, nb, target, codes_out, alpha_out,
+                               scale_out, st);
 }
 
 template <int B, bool F32, int FLAGS>
-void launch_accumulate_t(const uint8_t *codes, const float *alpha, const float *scale,
+tfp8_status launch_accumulate_t(const uint8_t *codes, const float *alpha, const float *scale,
                          const void *grad, int64_t nb, float target, uint8_t *codes_out,
                          float *alpha_out, float *scale_out, hipStream_t st) {
   constexpr bool ROT = !(FLAGS & kNoRotation);
@@ -1033,13 +1050,14 @@ void launch_accumulate_t(const uint8_t *codes, const float *alpha, const float *
   const float C = (float)Cd, invC = (float)(1.0 / Cd);
   constexpr int BPW = 64 / lanes_per_block(B);  // blocks per tile
   const unsigned grid = grid_for((nb + BPW - 1) / BPW, TFP8_COMPRESS_WGS_PER_CU);
-  hipLaunchKernelGGL((k_accumulate<B, F32, FLAGS>), dim3(grid), dim3(kThreads), 0, st, codes,
-                     alpha, scale, grad, nb, TBB, sqrtTBB, (float)gscale, C, invC, codes_out,
-                     alpha_out, scale_out);
+  const tfp8_status first =
+      launch(k_accumulate<B, F32, FLAGS>, grid, kThreads, st, codes, alpha, scale, grad, nb, TBB,
+             sqrtTBB, (float)gscale, C, invC, codes_out, alpha_out, scale_out);
+  if (first != TFP8_OK) return first;
   // the set-aside blocks: codes and s from the inputs (untouched for them), -alpha from alpha_out
   const unsigned grid_fix = grid_for((nb + 127) / 128, TFP8_ACCUMULATE_FIX_WGS_PER_CU);
-  hipLaunchKernelGGL((k_accumulate_fix<B, F32, FLAGS>), dim3(grid_fix), dim3(kThreads), 0, st,
-                     codes, scale, grad, nb, TBB, C, gscale, codes_out, alpha_out, scale_out);
+  return launch(k_accumulate_fix<B, F32, FLAGS>, grid_fix, kThreads, st, codes, scale, grad, nb,
+                TBB, C, gscale, codes_out, alpha_out, scale_out);
 }
 
 template <int B, bool F32>
@@ -1047,13 +1065,16 @@ tfp8_status launch_accumulate(const uint8_t *codes, const float *alpha, const fl
                               const void *grad, int64_t nb, float target, uint32_t flags,
                               uint8_t *codes_out, float *alpha_out, float *scale_out,
                               hipStream_t st) {
+#define TFP8_LAUNCH_ACCUMULATE(FL)                                                          \
+  return launch_accumulate_t<B, F32, FL>(codes, alpha, scale, grad, nb, target, codes_out, \
+                                         alpha_out, scale_out, st)
   switch (flags) {
-    case 0: launch_accumulate_t<B, F32, 0>(codes, alpha, scale, grad, nb, target, codes_out, alpha_out, scale_out, st); break;
-    case kInt8: launch_accumulate_t<B, F32, kInt8>(codes, alpha, scale, grad, nb, target, codes_out, alpha_out, scale_out, st); break;
-    case kNoRotation: launch_accumulate_t<B, F32, kNoRotation>(codes, alpha, scale, grad, nb, target, codes_out, alpha_out, scale_out, st); break;
-    default: launch_accumulate_t<B, F32, kInt8 | kNoRotation>(codes, alpha, scale, grad, nb, target, codes_out, alpha_out, scale_out, st); break;
+    case 0: TFP8_LAUNCH_ACCUMULATE(0);
+    case kInt8: TFP8_LAUNCH_ACCUMULATE(kInt8);
+    case kNoRotation: TFP8_LAUNCH_ACCUMULATE(kNoRotation);
+    default: TFP8_LAUNCH_ACCUMULATE(kInt8 | kNoRotation);
   }
-  return launched();
+#undef TFP8_LAUNCH_ACCUMULATE
 }
 
 }  // namespace
