@@ -281,6 +281,67 @@ def test_wrappers_check_buffers_before_launch(tfp8):
     torch.cuda.synchronize()
 
 
+def test_graph_capture_replays_match_eager(tfp8):
+    # The calls allocate nothing and never synchronize, so a stream can capture them in a graph.
+    # compress -> reduce_fp8 -> decompress and an accumulate are captured once, then replayed
+    # three times with eager work in between (outputs overwritten, a new input copied in); each
+    # replay must equal the eager calls on the same input bit for bit.
+    B, P, n = 128, 4, 1 << 18
+    nb = n // B
+    inputs = [bits_to_gpu(np.concatenate([random_bf16_bits(n, seed=40 * k + p, scale=0.05)
+                                          for p in range(P)])) for k in range(3)]
+    grads = [bits_to_gpu(random_bf16_bits(n, seed=900 + k, scale=0.02)) for k in range(3)]
+
+    def eager(x, g):
+        q, a, s = tfp8.compress(x, B, 1.0)
+        rq, ra, rs = tfp8.reduce_fp8(q.view(P, n), a.view(P, nb), s.view(P, nb), B, 1.0)
+        d = tfp8.decompress(rq, ra, rs, B, torch.bfloat16)
+        aq, aa, as_ = tfp8.accumulate(rq, ra, rs, g, B, 1.0)
+        return [q, a, s, rq, ra, rs, d, aq, aa, as_]
+
+    x_in = torch.empty_like(inputs[0])
+    g_in = torch.empty_like(grads[0])
+    outs = [torch.empty(P * n, dtype=torch.uint8, device=DEV), torch.empty(P * nb, device=DEV),
+            torch.empty(P * nb, device=DEV), torch.empty(n, dtype=torch.uint8, device=DEV),
+            torch.empty(nb, device=DEV), torch.empty(nb, device=DEV),
+            torch.empty(n, dtype=torch.bfloat16, device=DEV),
+            torch.empty(n, dtype=torch.uint8, device=DEV), torch.empty(nb, device=DEV),
+            torch.empty(nb, device=DEV)]
+
+    def pipeline():
+        q, a, s, rq, ra, rs, d, aq, aa, as_ = outs
+        tfp8.compress(x_in, B, 1.0, out=(q, a, s))
+        tfp8.reduce_fp8(q.view(P, n), a.view(P, nb), s.view(P, nb), B, 1.0, out=(rq, ra, rs))
+        tfp8.decompress(rq, ra, rs, B, torch.bfloat16, out=d)
+        tfp8.accumulate(rq, ra, rs, g_in, B, 1.0, out=(aq, aa, as_))
+
+    x_in.copy_(inputs[0])
+    g_in.copy_(grads[0])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        pipeline()  # one eager run on a side stream before capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        pipeline()
+    torch.cuda.synchronize()
+    for k in range(3):
+        for t in outs:
+            t.view(torch.uint8).fill_(0xA5)
+        x_in.copy_(inputs[k])
+        g_in.copy_(grads[k])
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        want = eager(inputs[k], grads[k])
+        torch.cuda.synchronize()
+        for i, (got, ref) in enumerate(zip(outs, want)):
+            assert torch.equal(got.view(torch.uint8), ref.view(torch.uint8)), (k, i)
+    say("  graph: 3 replays equal the eager calls")
+
+
 def test_bitwise_deterministic_and_stream_safe(tfp8):
     x = bits_to_gpu(make_shard(2).reshape(-1))
     r1 = tfp8.compress(x, 128, 1.0)
