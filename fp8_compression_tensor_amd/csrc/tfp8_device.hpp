@@ -34,26 +34,14 @@ __device__ __forceinline__ float swz_xor16(float v) {
                             __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
 }
 
-// Max over the L lanes of a group; every lane of the group gets the result.  After the
-// xor-1 and xor-2 steps all lanes of a quad agree, so the mirror steps (xor 7, xor 15) combine
-// whole quads / half-rows exactly like xor 4 / xor 8 would.
-template <int L>
-__device__ __forceinline__ float group_max(float v) {
-  static_assert(L == 4 || L == 8 || L == 16 || L == 32, "group of 4, 8, 16 or 32 lanes");
-  v = fmaxf(v, dpp<kDppXor1>(v));
-  v = fmaxf(v, dpp<kDppXor2>(v));
-  if constexpr (L >= 8) v = fmaxf(v, dpp<kDppHalfMirror>(v));
-  if constexpr (L >= 16) v = fmaxf(v, dpp<kDppRowMirror>(v));
-  if constexpr (L >= 32) v = fmaxf(v, swz_xor16(v));
-  return v;
-}
-
 template <int CTRL>
 __device__ __forceinline__ int dpp_i(int v) {
   return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
 }
 
-// Integer max over the L lanes of a group.
+// Integer max over the L lanes of a group; every lane of the group gets the result.  After the
+// xor-1 and xor-2 steps all lanes of a quad agree, so the mirror steps (xor 7, xor 15) combine
+// whole quads / half-rows exactly like xor 4 / xor 8 would.
 template <int L>
 __device__ __forceinline__ int group_max_i(int v) {
   static_assert(L == 4 || L == 8 || L == 16 || L == 32, "group of 4, 8, 16 or 32 lanes");
@@ -63,6 +51,16 @@ __device__ __forceinline__ int group_max_i(int v) {
   if constexpr (L >= 16) v = max(v, dpp_i<kDppRowMirror>(v));
   if constexpr (L >= 32) v = max(v, __builtin_amdgcn_ds_swizzle(v, 0x401F));
   return v;
+}
+
+// Max over the L lanes of a group of magnitudes (values >= +0); every lane of the group gets
+// the result.  Non-negative floats order like their bit patterns read as signed integers, so
+// the max runs on the integers: an integer max needs no NaN canonicalisation, which lets the
+// compiler fold each lane exchange into the max itself (one v_max_i32 with a DPP operand per
+// step instead of a move and two float maxes).
+template <int L>
+__device__ __forceinline__ float group_max(float v) {
+  return __int_as_float(group_max_i<L>(__float_as_int(v)));
 }
 
 template <int L>

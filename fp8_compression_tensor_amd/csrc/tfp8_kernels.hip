@@ -60,14 +60,16 @@ namespace tfp8 {
 
 constexpr int kThreads = 256;  // 4 wavefronts per workgroup (compress: 1 or 4, see its launch)
 
-// Index of this wavefront among the launch's, for kernels launched with any workgroup size.  With
-// `remap`, workgroup b, which the dispatcher hands to XCD b mod 8 in round robin, takes the slot
-// (b mod 8) * gridDim.x / 8 + b / 8, so that each XCD streams one contiguous eighth of the tiles
-// (the host then launches a multiple of 8 workgroups).
-__device__ __forceinline__ int64_t wave_index(bool remap) {
+// Index of this wavefront among the launch's, for a launch of `wpw` wavefronts per workgroup
+// (passed as an argument: blockDim would be read from the dispatch packet with a memory load at
+// the start of every wavefront).  With `remap`, workgroup b, which the dispatcher hands to XCD
+// b mod 8 in round robin, takes the slot (b mod 8) * gridDim.x / 8 + b / 8, so that each XCD
+// streams one contiguous eighth of the tiles (the host then launches a multiple of 8
+// workgroups).
+__device__ __forceinline__ int64_t wave_index(int wpw, bool remap) {
   int64_t b = blockIdx.x;
   if (remap) b = (b & 7) * (int64_t)(gridDim.x >> 3) + (b >> 3);
-  return (b * blockDim.x + threadIdx.x) >> 6;
+  return b * wpw + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 }
 
 // Variant bits of the *_ex entry points, as compile-time kernel parameters.
@@ -166,6 +168,28 @@ struct CompressIn {
 
 // Lane j of a block's group holds the runs of 8 elements [RS g + 8 j, RS g + 8 j + 8), where
 // RS = 8 L is the run stride for L lanes per block.
+// The same, from the base of a tile (wave-uniform, so it stays in scalar registers) and a lane's
+// 32-bit element offset into it: the loads then take the scalar base plus a vector offset, and
+// no 64-bit address arithmetic runs per lane.
+template <int B, bool F32IN>
+__device__ __forceinline__ void load_compress_at(CompressIn<B, F32IN> &in, const void *tile,
+                                                 uint32_t off) {
+  constexpr int RS = 8 * lanes_per_block(B);
+  constexpr int G = CompressIn<B, F32IN>::kRuns;
+  if constexpr (!F32IN) {
+    const uint16_t *xb = (const uint16_t *)tile + off;
+#pragma unroll
+    for (int g = 0; g < G; ++g) in.d[g] = ld_stream((const u32x4 *)(xb + RS * g));
+  } else {
+    const float *xb = (const float *)tile + off;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      in.d[2 * g] = ld_stream((const u32x4 *)(xb + RS * g));
+      in.d[2 * g + 1] = ld_stream((const u32x4 *)(xb + RS * g + 4));
+    }
+  }
+}
+
 template <int B, bool F32IN>
 __device__ __forceinline__ void load_compress_in(CompressIn<B, F32IN> &in, const void *xin,
                                                  int64_t blk, int j) {
@@ -190,7 +214,8 @@ __global__ __launch_bounds__(kThreads) void k_compress(const void *__restrict__ 
                                                        float TBB, float sqrtTB, float C,
                                                        float invC, uint8_t *__restrict__ codes,
                                                        float *__restrict__ alpha_out,
-                                                       float *__restrict__ scale_out, bool remap) {
+                                                       float *__restrict__ scale_out, int wpw,
+                                                       bool remap) {
   constexpr int L = lanes_per_block(B);  // lanes per block
   constexpr int BPW = 64 / L;            // blocks per wavefront (one tile)
   constexpr int RS = 8 * L;              // run stride
@@ -203,23 +228,30 @@ __global__ __launch_bounds__(kThreads) void k_compress(const void *__restrict__ 
   const int bw = lane / L;
   const int pj = ROT ? lane_perm<L>(j) : j;
   const float sj = ROT ? lane_sign<L>(j) : 1.0f;
-  const int64_t wave = wave_index(remap);
-  const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+  const int64_t wave = wave_index(wpw, remap);
+  const int64_t nwaves = (int64_t)gridDim.x * wpw;
   const int64_t ntiles = (int64_t)(((uint64_t)nb + BPW - 1) / BPW);  // nb >= 0
   // packed bfloat16 (1, 1) and (1, -1), kept in registers for v_dot2_f32_bf16
   const uint32_t ones = 0x3F803F80u, plus_minus = 0xBF803F80u;
 
+  // Tile t covers blocks [t BPW, t BPW + BPW); the group bw of its lanes takes block t BPW + bw.
   // Groups past the last block (ragged last tile) read the last block again and store
   // nothing, so every load is in bounds and every register holds data.
+  constexpr int ES = F32IN ? 4 : 2;  // input element size
+  auto tile_in = [&](int64_t t) { return (const char *)xin + t * (BPW * B * ES); };
+  auto lane_in = [&](int64_t t) {
+    const int64_t last = nb - 1 - t * BPW;  // last block relative to the tile (>= 0)
+    return (uint32_t)((last < bw ? (int)last : bw) * B + 8 * j);
+  };
   CompressIn<B, F32IN> cur;
-  if (wave < ntiles) load_compress_in<B, F32IN>(cur, xin, min(wave * BPW + bw, nb - 1), j);
+  if (wave < ntiles) load_compress_at<B, F32IN>(cur, tile_in(wave), lane_in(wave));
 
   for (int64_t tile = wave; tile < ntiles; tile += nwaves) {
-    const int64_t blk = tile * BPW + bw;
-    const bool active = blk < nb;
+    const int64_t blk0 = tile * BPW;  // first block of the tile (wave-uniform)
+    const bool active = blk0 + bw < nb;
     CompressIn<B, F32IN> nxt;
     if (tile + nwaves < ntiles)
-      load_compress_in<B, F32IN>(nxt, xin, min((tile + nwaves) * BPW + bw, nb - 1), j);
+      load_compress_at<B, F32IN>(nxt, tile_in(tile + nwaves), lane_in(tile + nwaves));
 
     // Widen, energy and the first butterfly stages.  Groups past the last block work on a
     // copy of the last block and store nothing.
@@ -278,17 +310,18 @@ __global__ __launch_bounds__(kThreads) void k_compress(const void *__restrict__ 
     }
 
     if (active) {
-      uint8_t *cb = codes + blk * B + 8 * pj;
+      uint8_t *cb = codes + blk0 * B;         // the tile's codes (wave-uniform)
+      const uint32_t co = bw * B + 8 * pj;    // this lane's runs within them
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         u32x2 w;
         w[0] = encode4<FLAGS>(v[8 * g + 0], v[8 * g + 1], v[8 * g + 2], v[8 * g + 3], cm);
         w[1] = encode4<FLAGS>(v[8 * g + 4], v[8 * g + 5], v[8 * g + 6], v[8 * g + 7], cm);
-        st_stream(w, (u32x2 *)(cb + RS * g));
+        st_stream(w, (u32x2 *)(cb + co + RS * g));
       }
       if (j == 0) {
-        alpha_out[blk] = alpha;
-        scale_out[blk] = s;
+        alpha_out[blk0 + bw] = alpha;
+        scale_out[blk0 + bw] = s;
       }
     }
     cur = nxt;
@@ -962,7 +995,7 @@ tfp8_status launch_compress_t(const void *x, int64_t nb, float target, uint8_t *
   const int nt = remap ? 64 : kThreads;
   const unsigned grid = grid_for((nb + BPW - 1) / BPW, TFP8_COMPRESS_WGS_PER_CU, nt, remap);
   return launch(k_compress<B, F32, FLAGS>, grid, nt, st, x, nb, TBB, sqrtTB, C, invC, codes,
-                alpha, scale, remap);
+                alpha, scale, nt / 64, remap);
 }
 
 template <int B, bool F32>
