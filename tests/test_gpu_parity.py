@@ -541,6 +541,47 @@ def test_compress_both_launch_shapes(oracle, tfp8, dtype, extra_blocks):
     say(f"  launch shapes: tie mismatches {nmis}")
 
 
+def test_compress_large_input_every_block_size_and_variant(oracle, tfp8):
+    # The launch for inputs of 1.5 GiB or more also stores the codes 16 bytes per lane, pairing
+    # the lanes that hold neighbouring runs; the pairing differs between the 8-lane network
+    # (rotation, B >= 128) and natural order (B = 64, or no rotation).  One 1.6 GB bf16 input,
+    # prefixes of it for every block size (each with a ragged last tile), and every flag set at
+    # B = 128 and B = 64; sampled blocks as above.
+    from tiecheck import FLAG_INT8, tie_cap
+
+    tile = 1 << 20
+    n_all = ((3 << 29) // 2 // 128 + 13) * 128
+    base = bf16_bits_to_f32(random_bf16_bits(tile, seed=1537, scale=0.05))
+    scaled = [f32_to_bf16_bits(base * np.float32(2.0 ** (t - 3))) for t in range(7)]
+    x = np.empty(n_all, np.uint16)
+    for t in range(-(-n_all // tile)):
+        seg = x[t * tile:(t + 1) * tile]
+        seg[:] = scaled[t % 7][:seg.size]
+    xg = bits_to_gpu(x)
+    rng = np.random.default_rng(1537)
+    cases = [(64, 0), (256, 0), (512, 0), (128, 1), (128, 2), (128, 3), (64, 2), (64, 1)]
+    for B, flags in cases:
+        nb = n_all // B
+        n = nb * B
+        assert n * 2 >= 3 << 29 and nb % (64 // (4 if B == 64 else 8)) != 0
+        q, a, s = tfp8.compress(xg[:n], B, 1.0, flags=flags)
+        torch.cuda.synchronize()
+        ntiles = -(-nb // (16 if B == 64 else 8))
+        eighths = np.array([k * -(-ntiles // 8) * (16 if B == 64 else 8) for k in range(8)])
+        idx = np.unique(np.concatenate([np.arange(32), np.arange(nb - 32, nb),
+                                        (eighths[:, None] + np.arange(-4, 4)).reshape(-1) % nb,
+                                        rng.integers(0, nb, 1024)]))
+        idx_g = torch.from_numpy(idx).to(DEV)
+        xs = np.ascontiguousarray(x[:n].reshape(nb, B)[idx]).reshape(-1)
+        rq, ra, rs, rt = oracle.compress(xs, B, 1.0, with_quot=True, flags=flags)
+        what = f"large input B={B} flags={flags}"
+        nmis = assert_codes_match(cpu(q.view(nb, B)[idx_g]).reshape(-1), rq, rt,
+                                  max_frac=tie_cap(flags), what=what, int8=bool(flags & FLAG_INT8))
+        assert_scales(cpu(a[idx_g]), cpu(s[idx_g]), ra, rs, what=what)
+        say(f"  {what}: {idx.size} sampled blocks, tie mismatches {nmis}")
+        del q, a, s
+
+
 def test_offsets_beyond_2_31_elements(oracle, tfp8):
     # n = 513 * 2^22 > 2^31 elements: element indexes pass 2^31, bfloat16 byte offsets pass
     # 2^32 and code byte offsets pass 2^31.  The input is one random tile of 2^22 elements in
