@@ -16,8 +16,9 @@
 // live in registers, bits 3-5 across the lanes.
 //
 // Launch.  One tile (64/L blocks) per wavefront, 8- or 16-byte vector loads and stores per
-// lane, no LDS, no atomics.  Compress of an input of 1.5 GiB or more launches one-wavefront workgroups and
-// gives each XCD a contiguous eighth of the tiles (kCompressRemapMinBytes below).
+// lane, no LDS, no atomics.  Compress of an input of 1.5 GiB or more (B >= 128) launches
+// one-wavefront workgroups and gives each XCD a contiguous eighth of the tiles
+// (kCompressRemapMinBytes below).
 //
 // Transform.  w = H x (unnormalised) is computed by an in-register FWHT over the register
 // bits and a 3-stage DPP butterfly over the lane bits (tfp8_device.hpp), which leaves lane j
@@ -945,7 +946,8 @@ int cu_count() {
 // Compress of a large input is 2-4% faster with 64-thread workgroups and each XCD on a
 // contiguous eighth of the tiles: 77% -> 80% of HBM peak for every bf16 input measured from
 // 1.9 to 4.3 GB.  At 1.1 GB the two shapes tie, and on inputs of 134-268 MB the remapped one is
-// 3-10% slower, hence the threshold.  Decompress and the reduce were slower remapped.
+// 3-10% slower, hence the threshold.  At B = 64 (4 lanes per block) the remapped shape was 3%
+// slower on 1.9 GB.  Decompress and the reduce were slower remapped.
 constexpr int64_t kCompressRemapMinBytes = (int64_t)3 << 29;  // 1.5 GiB of input
 
 // The cap without `per_cu` keeps gridDim.x * nt (the work-items of the launch, a 32-bit count
@@ -991,7 +993,7 @@ tfp8_status launch_compress_t(const void *x, int64_t nb, float target, uint8_t *
   constexpr int BPW = 64 / lanes_per_block(B);  // blocks per tile
   // Large inputs stream faster with one wavefront per workgroup and each XCD on a contiguous
   // eighth of the tiles; smaller ones with 4 wavefronts per workgroup in dispatch order.
-  const bool remap = nb * B * (F32 ? 4 : 2) >= kCompressRemapMinBytes;
+  const bool remap = B >= 128 && nb * B * (F32 ? 4 : 2) >= kCompressRemapMinBytes;
   const int nt = remap ? 64 : kThreads;
   const unsigned grid = grid_for((nb + BPW - 1) / BPW, TFP8_COMPRESS_WGS_PER_CU, nt, remap);
   return launch(k_compress<B, F32, FLAGS>, grid, nt, st, x, nb, TBB, sqrtTB, C, invC, codes,

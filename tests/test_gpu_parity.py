@@ -542,11 +542,9 @@ def test_compress_both_launch_shapes(oracle, tfp8, dtype, extra_blocks):
 
 
 def test_compress_large_input_every_block_size_and_variant(oracle, tfp8):
-    # The launch for inputs of 1.5 GiB or more also stores the codes 16 bytes per lane, pairing
-    # the lanes that hold neighbouring runs; the pairing differs between the 8-lane network
-    # (rotation, B >= 128) and natural order (B = 64, or no rotation).  One 1.6 GB bf16 input,
-    # prefixes of it for every block size (each with a ragged last tile), and every flag set at
-    # B = 128 and B = 64; sampled blocks as above.
+    # Inputs of 1.5 GiB or more: the remapped launch at B >= 128 and the dispatch-order one at
+    # B = 64.  One 1.6 GB bf16 input, prefixes of it for every block size (each with a ragged
+    # last tile), and every flag set at B = 128 and B = 64; sampled blocks as above.
     from tiecheck import FLAG_INT8, tie_cap
 
     tile = 1 << 20
