@@ -11,12 +11,13 @@ bfloat16 [8, 4096, 3584], block 128, target 1.0.
 Inputs are generated on the host (seeded, see workloads/) and are resident in HBM before the
 timed region starts.  `value` is the whole step's throughput in GB/s of bfloat16 input
 (8 x 117,440,512 x 2 bytes per step), from the wall clock around exactly K steps.  Per-kernel
-durations come from HIP events on the kernels' stream around every kernel of the timed steps.  `roofline` describes the dominant kernel (compress);
-`cpu_baseline` is the FP64 CPU oracle timed on this host over a bounded sample of the same
-pipeline.  After the timed steps each kernel is also timed over K back-to-back launches, and
-so is the local gradient accumulation on its own workload (GPT-13B-shaped gradients
-[4, 4096, 5120], block 128: main gradient = compressed shard 0, local gradient = shard 1);
-those figures are reported beside the step and are not part of `value`.
+durations come from HIP events on the kernels' stream around every kernel of the timed
+steps.  `roofline` describes the dominant kernel (compress); `cpu_baseline` is the FP64 CPU
+oracle timed on this host over a bounded sample of the same pipeline.  After the timed steps
+each kernel is also timed over K back-to-back launches, and so is the local gradient
+accumulation on its own workload (GPT-13B-shaped gradients [4, 4096, 5120], block 128: main
+gradient = compressed shard 0, local gradient = shard 1); those figures are reported beside
+the step and are not part of `value`.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
        python bench.py --copy-calibrate   (plain 1 GiB device copy, for HBM counter scaling)

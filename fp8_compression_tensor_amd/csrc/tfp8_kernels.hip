@@ -838,6 +838,8 @@ __device__ __forceinline__ void accumulate_block_split(
   }
 }
 
+constexpr int kFixRuns = 2;  // runs of 64 blocks that one wavefront of k_accumulate_fix scans
+
 // Finds the blocks k_accumulate set aside (alpha_out < 0) and redoes them.  A wavefront reads the
 // alphas of kRuns x 64 consecutive blocks at once (kRuns loads in flight per lane), then takes
 // the runs of 64 in turn and works through each run's marked blocks 64 / L at a time, one group
@@ -846,7 +848,7 @@ template <int B, bool F32IN, int FLAGS>
 __global__ __launch_bounds__(kThreads) void k_accumulate_fix(
     const uint8_t *codes, const float *scale, const void *__restrict__ grad, int64_t nb,
     float TBB, float C, double gscale, uint8_t *codes_out, float *alpha_out, float *scale_out) {
-  constexpr int kRuns = 2;
+  constexpr int kRuns = kFixRuns;
   constexpr int L = lanes_per_block(B);
   constexpr int BPW = 64 / L;  // blocks worked on at once: one per group of L lanes
   const int lane = threadIdx.x & 63;
@@ -1090,7 +1092,8 @@ tfp8_status launch_accumulate_t(const uint8_t *codes, const float *alpha, const 
              sqrtTBB, (float)gscale, C, invC, codes_out, alpha_out, scale_out);
   if (first != TFP8_OK) return first;
   // the set-aside blocks: codes and s from the inputs (untouched for them), -alpha from alpha_out
-  const unsigned grid_fix = grid_for((nb + 127) / 128, TFP8_ACCUMULATE_FIX_WGS_PER_CU);
+  const unsigned grid_fix =
+      grid_for((nb + 64 * kFixRuns - 1) / (64 * kFixRuns), TFP8_ACCUMULATE_FIX_WGS_PER_CU);
   return launch(k_accumulate_fix<B, F32, FLAGS>, grid_fix, kThreads, st, codes, scale, grad, nb,
                 TBB, C, gscale, codes_out, alpha_out, scale_out);
 }
