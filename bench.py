@@ -21,7 +21,7 @@ the step and are not part of `value`.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
        python bench.py --copy-calibrate   (plain 1 GiB device copy, for HBM counter scaling)
-       python bench.py --all-configs      (every operation on every workload, warm and with the
+       python bench.py --all-workloads      (every operation on every workload, warm and with the
                                            caches flushed, beside a same-shape copy)
 """
 from __future__ import annotations
@@ -38,8 +38,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "fused FP8 ASH+DS compress GB/s (bf16 in) and % of MI355X HBM peak"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published peak
-CID = 5
-ACC_CID = 4  # GPT-13B-shaped gradients, for the local gradient accumulation
+STEP_WORKLOAD = "qwen2.5-7b-act"  # Qwen2.5-7B-shaped activations, 8 shards: the timed step
+ACC_WORKLOAD = "gpt13b-grad"  # GPT-13B-shaped gradients, for the local gradient accumulation
 TARGET = 1.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "compress_qwen7b_8shards_hbm_traffic.json")
 
@@ -145,7 +145,7 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def all_configs(reps: int):
+def all_workloads(reps: int):
     """Every operation on every workload, warm and with the caches flushed, beside a
     same-shape copy; one JSON object on stdout, a table on stderr."""
     import statistics
@@ -153,11 +153,11 @@ def all_configs(reps: int):
     import numpy as np
     import torch
 
-    from workloads import CONFIGS, make_shards
+    from workloads import WORKLOADS, make_shards
 
     host = {}
-    for cid, cfg in CONFIGS.items():
-        host[cid] = make_shards(cid, count=max(cfg.shards, 2 if cid == 4 else 1))
+    for key, wl in WORKLOADS.items():
+        host[key] = make_shards(key, count=max(wl.shards, 2 if key == ACC_WORKLOAD else 1))
     log("inputs generated")
 
     import fp8_compression_tensor_amd as tfp8
@@ -186,10 +186,10 @@ def all_configs(reps: int):
 
     rows = []
 
-    def measure(cid, op, fn, alg_bytes, elements, B, P, bf16_in=None, copy_fn=None):
+    def measure(key, op, fn, alg_bytes, elements, B, P, bf16_in=None, copy_fn=None):
         wm, wn = timed(fn, False)
         fm, fn_ = timed(fn, True)
-        row = {"config": cid, "op": op, "elements": elements, "block": B, "P": P,
+        row = {"workload": key, "op": op, "elements": elements, "block": B, "P": P,
                "bytes_algorithmic": int(alg_bytes), "warm_us_median": round(wm, 2),
                "warm_us_min": round(wn, 2), "flushed_us_median": round(fm, 2),
                "flushed_us_min": round(fn_, 2),
@@ -203,15 +203,15 @@ def all_configs(reps: int):
             row["copy_GBps_flushed"] = round(cbytes / (cm * 1e-6) / 1e9, 1)
             row["ratio_to_copy"] = round(row["flushed_GBps"] / row["copy_GBps_flushed"], 4)
         rows.append(row)
-        log(f"cfg {cid} {op:28s} n={elements:>10d} B={B} P={P}: warm {wm:9.1f} us, flushed "
+        log(f"{key:15s} {op:28s} n={elements:>10d} B={B} P={P}: warm {wm:9.1f} us, flushed "
             f"{fm:9.1f} us = {row['flushed_GBps']:7.1f} GB/s ({100 * row['flushed_frac_of_peak']:.1f}%)"
             + (f", vs 2:1 add {row['copy_GBps_flushed']:.0f} GB/s: {row['ratio_to_copy']:.3f}"
                if copy_fn is not None else ""))
 
-    for cid, cfg in CONFIGS.items():
-        B, P, n = cfg.block, cfg.shards, cfg.n
+    for key, wl in WORKLOADS.items():
+        B, P, n = wl.block, wl.shards, wl.n
         nb = n // B
-        xs = host[cid]
+        xs = host[key]
         x = torch.from_numpy(xs.reshape(-1).view(np.int16)).to(dev)
         xb = x.view(torch.bfloat16)
         ntot = P * n
@@ -230,9 +230,9 @@ def all_configs(reps: int):
             # a same-ratio reference: two int16 reads and one int16 write per element
             return (lambda: torch.add(x[:m], ya[:m], out=yc[:m])), 6 * m
 
-        measure(cid, "compress", comp(n), n * (3 + 8 / B), n, B, 1, 2 * n, copy(n))
+        measure(key, "compress", comp(n), n * (3 + 8 / B), n, B, 1, 2 * n, copy(n))
         if P > 1:
-            measure(cid, f"compress {P} stacked shards", comp(ntot), ntot * (3 + 8 / B), ntot, B,
+            measure(key, f"compress {P} stacked shards", comp(ntot), ntot * (3 + 8 / B), ntot, B,
                     P, 2 * ntot, copy(ntot))
         comp(ntot)()  # codes of every shard, for the stages below
         for dt, name, ob in ((torch.bfloat16, "decompress bf16", 2), (torch.float32,
@@ -242,7 +242,7 @@ def all_configs(reps: int):
             fn = (lambda out=out, code=code: check(tfp8.decompress_raw(
                 q.data_ptr(), al.data_ptr(), sc.data_ptr(), n, B, out.data_ptr(), code,
                 stream.cuda_stream)))
-            measure(cid, name, fn, n * (1 + 8 / B + ob), n, B, 1)
+            measure(key, name, fn, n * (1 + 8 / B + ob), n, B, 1)
             del out
         if P > 1:
             rq = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -251,7 +251,7 @@ def all_configs(reps: int):
             fn = lambda: check(tfp8.reduce_fp8_raw(q.data_ptr(), al.data_ptr(), sc.data_ptr(), P,
                                                    n, B, TARGET, rq.data_ptr(), ra.data_ptr(),
                                                    rs.data_ptr(), stream.cuda_stream))
-            measure(cid, f"reduce P={P}, {P} x n", fn, (P + 1) * n * (1 + 8 / B), n, B, P)
+            measure(key, f"reduce P={P}, {P} x n", fn, (P + 1) * n * (1 + 8 / B), n, B, P)
             # one rank's share in a P-way reduce-scatter: chunk 0 of every shard, n/P each
             c = n // P
             cq = q[:ntot].view(P, n)[:, :c].contiguous()
@@ -260,10 +260,10 @@ def all_configs(reps: int):
             fn = lambda: check(tfp8.reduce_fp8_raw(cq.data_ptr(), ca.data_ptr(), cs.data_ptr(), P,
                                                    c, B, TARGET, rq.data_ptr(), ra.data_ptr(),
                                                    rs.data_ptr(), stream.cuda_stream))
-            measure(cid, f"reduce P={P}, {P} x n/{P} (one rank)", fn, (P + 1) * c * (1 + 8 / B),
+            measure(key, f"reduce P={P}, {P} x n/{P} (one rank)", fn, (P + 1) * c * (1 + 8 / B),
                     c, B, P)
             del rq, ra, rs, cq, ca, cs
-        if cid == 4:
+        if key == ACC_WORKLOAD:
             # gradient accumulation: main = compressed shard 0, local = shard 1
             comp(n)()
             oq = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -273,11 +273,11 @@ def all_configs(reps: int):
                                                    xb.data_ptr() + 2 * n, tfp8.BF16, n, B,
                                                    TARGET, oq.data_ptr(), oa.data_ptr(),
                                                    os_.data_ptr(), stream.cuda_stream))
-            measure(cid, "accumulate (main + local)", fn, n * (4 + 16 / B), n, B, 1)
+            measure(key, "accumulate (main + local)", fn, n * (4 + 16 / B), n, B, 1)
             del oq, oa, os_
         del x, xb, q, al, sc, ya, yc
         torch.cuda.empty_cache()
-    print(json.dumps({"mode": "all-configs", "reps": reps, "peak_GBps": HBM_PEAK_GBS,
+    print(json.dumps({"mode": "all-workloads", "reps": reps, "peak_GBps": HBM_PEAK_GBS,
                       "copy": "torch.add of two int16 tensors into a third, same element count "
                               "(read:write 2:1 as compress), flushed; ratio = GB/s over its GB/s",
                       "flush": "a 1 GiB read (sum) between launches",
@@ -294,7 +294,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibrate", action="store_true")
-    ap.add_argument("--all-configs", action="store_true",
+    ap.add_argument("--all-workloads", action="store_true",
                     help="time every operation on every workload, warm and flushed (own JSON)")
     args = ap.parse_args()
 
@@ -306,22 +306,22 @@ def main():
     if args.copy_calibrate:
         copy_calibrate(max(args.steps, 1))
         return
-    if args.all_configs:
-        all_configs(max(min(args.steps, 50), 5))
+    if args.all_workloads:
+        all_workloads(max(min(args.steps, 50), 5))
         return
 
-    from workloads import CONFIGS, make_shards
+    from workloads import WORKLOADS, make_shards
 
-    cfg = CONFIGS[CID]
-    B, P, n = cfg.block, cfg.shards, cfg.n
-    log(f"generating {P} shards of {cfg.name} (seeded) ...")
+    wl = WORKLOADS[STEP_WORKLOAD]
+    B, P, n = wl.block, wl.shards, wl.n
+    log(f"generating {P} shards of {wl.label} (seeded) ...")
     t0 = time.perf_counter()
-    xs = make_shards(CID)  # host generation before the GPU is touched
+    xs = make_shards(STEP_WORKLOAD)  # host generation before the GPU is touched
     log(f"  done in {time.perf_counter() - t0:.1f} s")
     # the local gradient accumulation's own workload: GPT-13B-shaped gradients, shard 0 as the
     # main gradient (compressed on the GPU below) and shard 1 as the local gradient
-    gcfg = CONFIGS[ACC_CID]
-    gs = make_shards(ACC_CID, count=2)
+    gcfg = WORKLOADS[ACC_WORKLOAD]
+    gs = make_shards(ACC_WORKLOAD, count=2)
 
     import numpy as np
     import torch
@@ -445,7 +445,7 @@ def main():
         "config": {"workload": "qwen2.5-7b tp activation [8,4096,3584] bf16 x 8 shards, block 128, "
                                "target 1: compress(8 stacked shards) -> reduce_fp8(P=8) -> "
                                "decompress(bf16)",
-                   "shape": list(cfg.shape), "shards": P, "block": B, "target": TARGET},
+                   "shape": list(wl.shape), "shards": P, "block": B, "target": TARGET},
         "roofline": roofline,
         "kernels_ms": {"compress": round(t_c, 4), "reduce_fp8": round(t_r, 4),
                        "decompress": round(t_d, 4)},

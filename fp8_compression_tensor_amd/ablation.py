@@ -20,7 +20,7 @@ For each it reports the round-trip error of x -> codes -> x_hat (float32 output)
                   (the dense near-zero body)
   block_snr_db    median over nonzero blocks of 10 log10(sum x^2 / sum (x_hat - x)^2)
 
-Usage: python -m fp8_compression_tensor_amd.ablation [--configs 1 2 3 4 5]
+Usage: python -m fp8_compression_tensor_amd.ablation [--workloads tiny gpt2.7b-act ...]
 """
 from __future__ import annotations
 
@@ -82,10 +82,10 @@ def ablate(x: torch.Tensor, block: int, target: float = 1.0) -> dict:
 
 def _table(rows):
     cols = ["rel_l2", "zero_collapse", "sign_flip", "body_rel_err", "block_snr_db"]
-    lines = ["| config | codec | " + " | ".join(cols) + " |", "|---" * (len(cols) + 2) + "|"]
-    for cfg, name, m in rows:
+    lines = ["| workload | codec | " + " | ".join(cols) + " |", "|---" * (len(cols) + 2) + "|"]
+    for wname, name, m in rows:
         vals = [f"{m[c]:.3e}" if c != "block_snr_db" else f"{m[c]:.1f}" for c in cols]
-        lines.append(f"| {cfg} | {name} | " + " | ".join(vals) + " |")
+        lines.append(f"| {wname} | {name} | " + " | ".join(vals) + " |")
     return "\n".join(lines)
 
 
@@ -95,22 +95,22 @@ def main(argv=None):
     import numpy as np
 
     sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
-    from workloads import CONFIGS, make_shard
+    from workloads import WORKLOADS, make_shard
 
     ap = argparse.ArgumentParser()
-    ap.add_argument("--configs", type=int, nargs="*", default=[1, 2, 3, 4, 5])
+    ap.add_argument("--workloads", nargs="*", default=list(WORKLOADS), choices=list(WORKLOADS))
     ap.add_argument("--json", action="store_true")
     args = ap.parse_args(argv)
     rows = []
-    for cid in args.configs:
-        cfg = CONFIGS[cid]
-        bits = make_shard(cid, 0).reshape(-1)
+    for key in args.workloads:
+        wl = WORKLOADS[key]
+        bits = make_shard(key, 0).reshape(-1)
         x = torch.from_numpy(bits.view(np.int16)).to("cuda:0").view(torch.bfloat16)
-        for name, m in ablate(x, cfg.block).items():
-            rows.append((f"{cid} ({cfg.name}, B={cfg.block})", name, m))
-        print(f"config {cid} done", file=sys.stderr, flush=True)
+        for name, m in ablate(x, wl.block).items():
+            rows.append((f"{key} ({wl.label}, B={wl.block})", name, m))
+        print(f"{key} done", file=sys.stderr, flush=True)
     if args.json:
-        print(json.dumps([{"config": c, "codec": n, **m} for c, n, m in rows]))
+        print(json.dumps([{"workload": c, "codec": n, **m} for c, n, m in rows]))
     else:
         print(_table(rows))
 

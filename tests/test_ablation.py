@@ -8,7 +8,7 @@ import pytest
 import torch
 
 from fp8_compression_tensor_amd.ablation import VARIANTS, ablate, error_metrics
-from workloads import CONFIGS, bf16_bits_to_f32, make_shard
+from workloads import TINY, WORKLOADS, bf16_bits_to_f32, make_shard
 
 
 def test_error_metrics_hand_computed():
@@ -28,15 +28,15 @@ def test_error_metrics_hand_computed():
 @pytest.mark.gpu
 def test_ablation_matches_oracle(oracle):
     oracle.set_threads(min(16, len(os.sched_getaffinity(0))))
-    cfg = CONFIGS[1]
-    bits = make_shard(1).reshape(-1)
+    wl = WORKLOADS[TINY]
+    bits = make_shard(TINY).reshape(-1)
     x = torch.from_numpy(bits.view(np.int16)).to("cuda:0").view(torch.bfloat16)
-    got = ablate(x, cfg.block)
+    got = ablate(x, wl.block)
     xv = torch.from_numpy(bf16_bits_to_f32(bits))
     for name, flags in VARIANTS.items():
-        q, a, s = oracle.compress(bits, cfg.block, 1.0, flags=flags)
-        xh = torch.from_numpy(oracle.decompress(q, a, s, cfg.block, np.float32, flags=flags))
-        ref = error_metrics(xv, xh, cfg.block)
+        q, a, s = oracle.compress(bits, wl.block, 1.0, flags=flags)
+        xh = torch.from_numpy(oracle.decompress(q, a, s, wl.block, np.float32, flags=flags))
+        ref = error_metrics(xv, xh, wl.block)
         g = got[name]
         print(name, g, flush=True)
         assert math.isclose(g["rel_l2"], ref["rel_l2"], rel_tol=1e-4), (name, g, ref)

@@ -15,8 +15,8 @@ import torch
 from gpu_helpers import (DEV, assert_bf16_match, assert_scales, bits_to_gpu, check_compress,
                          check_decompress, check_reduce, cpu, f32_to_gpu, say, u8_to_gpu)
 from tiecheck import assert_codes_match, assert_rel_close
-from workloads import (CONFIGS, bf16_bits_to_f32, f32_to_bf16_bits, make_shard, make_shards,
-                       random_bf16_bits)
+from workloads import (GPT2_7B, GPT6_7B, GPT13B_GRAD, QWEN7B, TINY, WORKLOADS, bf16_bits_to_f32,
+                       f32_to_bf16_bits, make_shard, make_shards, random_bf16_bits)
 
 pytestmark = pytest.mark.gpu
 
@@ -35,65 +35,65 @@ def _threads(oracle):
     oracle.set_threads(min(16, len(os.sched_getaffinity(0))))
 
 
-# ----------------------------------------------------------------------------- configs 1, 2, 4
+# ----------------------------------------------------------------------------- single-shard workloads
 
-@pytest.mark.parametrize("cid", [1, 2, 4])
-def test_config_compress_decompress(oracle, tfp8, cid):
-    cfg = CONFIGS[cid]
-    say(f"config {cid} ({cfg.name}), block {cfg.block}")
-    x = make_shard(cid).reshape(-1)
-    q, a, s = check_compress(oracle, tfp8, x, cfg.block, what=f"cfg{cid} compress")
-    check_decompress(oracle, tfp8, q, a, s, cfg.block, what=f"cfg{cid} decompress")
+@pytest.mark.parametrize("key", [TINY, GPT2_7B, GPT13B_GRAD])
+def test_workload_compress_decompress(oracle, tfp8, key):
+    wl = WORKLOADS[key]
+    say(f"{key} ({wl.label}), block {wl.block}")
+    x = make_shard(key).reshape(-1)
+    q, a, s = check_compress(oracle, tfp8, x, wl.block, what=f"{key} compress")
+    check_decompress(oracle, tfp8, q, a, s, wl.block, what=f"{key} decompress")
 
 
-# ----------------------------------------------------------------------------- config 3
+# ----------------------------------------------------------------------------- GPT-6.7B shards, P = 4
 
-def test_config3_compress_reduce_decompress(oracle, tfp8):
-    cfg = CONFIGS[3]
-    B, P = cfg.block, cfg.shards
-    say(f"config 3 ({cfg.name}), block {B}, P={P}")
-    xs = make_shards(3)  # [4, 4, 2048, 4096]
+def test_gpt6_7b_compress_reduce_decompress(oracle, tfp8):
+    wl = WORKLOADS[GPT6_7B]
+    B, P = wl.block, wl.shards
+    say(f"{GPT6_7B} ({wl.label}), block {B}, P={P}")
+    xs = make_shards(GPT6_7B)  # [4, 4, 2048, 4096]
     # one call compresses the stacked shards (blocks never straddle shards)
-    q, a, s = check_compress(oracle, tfp8, xs.reshape(-1), B, what="cfg3 compress of 4 stacked shards")
-    n = cfg.n
+    q, a, s = check_compress(oracle, tfp8, xs.reshape(-1), B, what="gpt6.7b compress of 4 stacked shards")
+    n = wl.n
     q, a, s = q.reshape(P, n), a.reshape(P, -1), s.reshape(P, -1)
-    check_decompress(oracle, tfp8, q[0], a[0], s[0], B, what="cfg3 decompress shard 0")
-    _check_reduce(oracle, tfp8, q, a, s, B, what="cfg3 reduce P=4")
+    check_decompress(oracle, tfp8, q[0], a[0], s[0], B, what="gpt6.7b decompress shard 0")
+    _check_reduce(oracle, tfp8, q, a, s, B, what="gpt6.7b reduce P=4")
 
 
 def _check_reduce(oracle, tfp8, q, a, s, B, T=1.0, what="reduce"):
     return check_reduce(oracle, tfp8, q, a, s, B, T, what=what)
 
 
-# ----------------------------------------------------------------------------- config 5
+# ----------------------------------------------------------------------------- Qwen2.5-7B shards, P = 8
 
-def test_config5_pipeline(oracle, tfp8):
-    cfg = CONFIGS[5]
-    B, P, n = cfg.block, cfg.shards, cfg.n
-    say(f"config 5 ({cfg.name}), block {B}, P={P}: generating {P} shards")
-    xs = make_shards(5).reshape(P, n)
+def test_qwen7b_pipeline(oracle, tfp8):
+    wl = WORKLOADS[QWEN7B]
+    B, P, n = wl.block, wl.shards, wl.n
+    say(f"{QWEN7B} ({wl.label}), block {B}, P={P}: generating {P} shards")
+    xs = make_shards(QWEN7B).reshape(P, n)
     say("  compress of the 8 stacked shards (one call), checked on sampled blocks")
     xg = bits_to_gpu(xs.reshape(-1))
     qg, ag, sg = tfp8.compress(xg, B, 1.0)
     torch.cuda.synchronize()
     del xg
     q, a, s = cpu(qg), cpu(ag), cpu(sg)
-    nbt = P * cfg.nblocks
+    nbt = P * wl.nblocks
     rng = np.random.default_rng(55)
     idx = np.sort(rng.choice(nbt, 131072, replace=False))
-    idx = np.union1d(idx, np.arange(0, nbt, cfg.nblocks))  # first block of every shard
+    idx = np.union1d(idx, np.arange(0, nbt, wl.nblocks))  # first block of every shard
     xb = xs.reshape(nbt, B)[idx]
     qr, ar, sr, tr = oracle.compress(xb, B, 1.0, with_quot=True)
-    nmis = assert_codes_match(q.reshape(nbt, B)[idx], qr, tr, what="cfg5 compress codes (sampled)")
-    assert_scales(a[idx], s[idx], ar, sr, what="cfg5 compress (sampled)")
-    say(f"  cfg5 compress: {idx.size} sampled blocks, code tie mismatches {nmis}")
+    nmis = assert_codes_match(q.reshape(nbt, B)[idx], qr, tr, what="qwen2.5-7b compress codes (sampled)")
+    assert_scales(a[idx], s[idx], ar, sr, what="qwen2.5-7b compress (sampled)")
+    say(f"  qwen2.5-7b compress: {idx.size} sampled blocks, code tie mismatches {nmis}")
     # reduce of the oracle's codes of all 8 shards, then decompress of the oracle's reduced
     # tensor, each checked in full
     del q, a, s
     q, a, s = oracle.compress(xs.reshape(-1), B, 1.0)
     q, a, s = q.reshape(P, n), a.reshape(P, -1), s.reshape(P, -1)
-    cq, ca, cs = _check_reduce(oracle, tfp8, q, a, s, B, what="cfg5 reduce P=8")
-    check_decompress(oracle, tfp8, cq, ca, cs, B, what="cfg5 decompress of the reduced tensor")
+    cq, ca, cs = _check_reduce(oracle, tfp8, q, a, s, B, what="qwen2.5-7b reduce P=8")
+    check_decompress(oracle, tfp8, cq, ca, cs, B, what="qwen2.5-7b decompress of the reduced tensor")
 
 
 # ----------------------------------------------------------------------------- edge cases
@@ -143,9 +143,9 @@ def test_block_counts(oracle, tfp8, nblocks):
 @pytest.mark.parametrize("T", [2.0 ** -64, 2.0 ** -10, 37.5, 2.0 ** 20, 2.0 ** 64])
 def test_target_values(oracle, tfp8, T):
     # the contract's bounds 2^-64 and 2^64 included; compress, reduce and accumulate
-    x = make_shard(1).reshape(-1)
-    q, a, s = check_compress(oracle, tfp8, x, 128, T=T, what=f"cfg1 T={T}")
-    xr = np.stack([make_shard(1, p).reshape(-1) for p in range(3)])
+    x = make_shard(TINY).reshape(-1)
+    q, a, s = check_compress(oracle, tfp8, x, 128, T=T, what=f"tiny T={T}")
+    xr = np.stack([make_shard(TINY, p).reshape(-1) for p in range(3)])
     enc = [oracle.compress(v, 128, T) for v in xr]
     check_reduce(oracle, tfp8, np.stack([e[0] for e in enc]), np.stack([e[1] for e in enc]),
                  np.stack([e[2] for e in enc]), 128, T, what=f"reduce T={T}")
@@ -203,7 +203,7 @@ def test_reduce_general(oracle, tfp8, P, B):
 
 def test_reduce_identities(oracle, tfp8):
     B = 128
-    x = make_shard(1).reshape(-1)
+    x = make_shard(TINY).reshape(-1)
     q, a, s = oracle.compress(x, B, 1.0)
     # a contribution and its negation cancel: every block becomes a zero block
     q2, a2, s2 = np.stack([q, q ^ 0x80]), np.stack([a, a]), np.stack([s, s])
@@ -343,7 +343,7 @@ def test_graph_capture_replays_match_eager(tfp8):
 
 
 def test_bitwise_deterministic_and_stream_safe(tfp8):
-    x = bits_to_gpu(make_shard(2).reshape(-1))
+    x = bits_to_gpu(make_shard(GPT2_7B).reshape(-1))
     r1 = tfp8.compress(x, 128, 1.0)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -367,12 +367,12 @@ VARIANTS = [1, 2, 3]  # INT8 codes, no rotation, both
 
 
 @pytest.mark.parametrize("flags", VARIANTS)
-@pytest.mark.parametrize("cid", [1, 2])
-def test_variant_configs(oracle, tfp8, cid, flags):
-    cfg = CONFIGS[cid]
-    x = make_shard(cid).reshape(-1)
-    q, a, s = check_compress(oracle, tfp8, x, cfg.block, what=f"cfg{cid} compress", flags=flags)
-    check_decompress(oracle, tfp8, q, a, s, cfg.block, what=f"cfg{cid} decompress", flags=flags)
+@pytest.mark.parametrize("key", [TINY, GPT2_7B])
+def test_variant_workloads(oracle, tfp8, key, flags):
+    wl = WORKLOADS[key]
+    x = make_shard(key).reshape(-1)
+    q, a, s = check_compress(oracle, tfp8, x, wl.block, what=f"{key} compress", flags=flags)
+    check_decompress(oracle, tfp8, q, a, s, wl.block, what=f"{key} decompress", flags=flags)
 
 
 @pytest.mark.parametrize("flags", VARIANTS)
@@ -429,12 +429,12 @@ def _check_accumulate(oracle, tfp8, q, a, s, g, B, what, flags=0, inplace=False,
 
 def test_accumulate_gradient_workload(oracle, tfp8):
     # the GPT-13B-shaped gradient workload: main gradient = shard 0 compressed, local = shard 1
-    cfg = CONFIGS[4]
-    B = cfg.block
-    x0, x1 = make_shard(4, 0).reshape(-1), make_shard(4, 1).reshape(-1)
+    wl = WORKLOADS[GPT13B_GRAD]
+    B = wl.block
+    x0, x1 = make_shard(GPT13B_GRAD, 0).reshape(-1), make_shard(GPT13B_GRAD, 1).reshape(-1)
     q, a, s = oracle.compress(x0, B, 1.0)
-    _check_accumulate(oracle, tfp8, q, a, s, x1, B, "cfg4 accumulate")
-    _check_accumulate(oracle, tfp8, q, a, s, x1, B, "cfg4 accumulate in place", inplace=True)
+    _check_accumulate(oracle, tfp8, q, a, s, x1, B, "gpt13b-grad accumulate")
+    _check_accumulate(oracle, tfp8, q, a, s, x1, B, "gpt13b-grad accumulate in place", inplace=True)
 
 
 @pytest.mark.parametrize("flags", [0, 1, 2, 3])
@@ -457,10 +457,10 @@ def test_accumulate_activation_shards_with_shared_outliers(oracle, tfp8):
     # the Qwen2.5-7B-shaped activation shards 0 and 1 as main and local gradient: their shared
     # outlier channels have random signs, so about 15% of the blocks cancel and take the exact
     # split path; full size, every element compared
-    cfg = CONFIGS[5]
-    xs = make_shards(5, count=2).reshape(2, -1)
-    q, a, s = oracle.compress(xs[0], cfg.block, 1.0)
-    _check_accumulate(oracle, tfp8, q, a, s, xs[1], cfg.block, "qwen shards accumulate")
+    wl = WORKLOADS[QWEN7B]
+    xs = make_shards(QWEN7B, count=2).reshape(2, -1)
+    q, a, s = oracle.compress(xs[0], wl.block, 1.0)
+    _check_accumulate(oracle, tfp8, q, a, s, xs[1], wl.block, "qwen shards accumulate")
 
 
 @pytest.mark.parametrize("inplace", [False, True])

@@ -4,14 +4,14 @@ import numpy as np
 import pytest
 
 from tiecheck import E4M3_VALUES, INT8_VALUES, assert_codes_match, tie_cap
-from workloads import bf16_bits_to_f32, make_shard, random_bf16_bits
+from workloads import TINY, bf16_bits_to_f32, make_shard, random_bf16_bits
 
 F32_ULP = 2.0 ** -23
 FLAG_SETS = [0, 1, 2, 3]
 
 
 def _main(oracle, flags, B=128):
-    x = make_shard(1).reshape(-1)
+    x = make_shard(TINY).reshape(-1)
     return oracle.compress(x, B, 1.0, flags=flags)
 
 

@@ -13,7 +13,7 @@ import pytest
 from scipy.linalg import hadamard
 
 from tiecheck import E4M3_VALUES, assert_codes_match, code_mismatches
-from workloads import bf16_bits_to_f32, f32_to_bf16_bits, make_shard, random_bf16_bits
+from workloads import TINY, bf16_bits_to_f32, f32_to_bf16_bits, make_shard, random_bf16_bits
 
 F32_ULP = 2.0 ** -23
 
@@ -129,12 +129,12 @@ def test_subnormal_block_clamps_alpha(oracle):
 
 # ------------------------------------------------------------------------------ invariants
 
-def _cfg1(oracle):
-    return make_shard(1).reshape(-1)
+def _tiny_shard(oracle):
+    return make_shard(TINY).reshape(-1)
 
 
 def test_codes_invariant_to_target(oracle):
-    x = _cfg1(oracle)
+    x = _tiny_shard(oracle)
     B = 128
     q1, a1, s1, t1 = oracle.compress(x, B, 1.0, with_quot=True)
     for T in (37.5, 2.0 ** -10, 2.0 ** 20):
@@ -160,7 +160,7 @@ def test_power_of_two_scaling(oracle):
 
 
 def test_negation_flips_signs(oracle):
-    x = _cfg1(oracle)
+    x = _tiny_shard(oracle)
     B = 128
     q, a, s, t = oracle.compress(x, B, 1.0, with_quot=True)
     qn, an, sn = oracle.compress(x ^ np.uint16(0x8000), B, 1.0)
@@ -182,7 +182,7 @@ def test_block_permutation_equivariance(oracle):
 
 
 def test_every_nonzero_block_reaches_qmax_and_no_nan(oracle):
-    x = _cfg1(oracle)
+    x = _tiny_shard(oracle)
     B = 128
     q, a, s = oracle.compress(x, B, 1.0)
     qb = q.reshape(-1, B)
@@ -255,7 +255,7 @@ def _half_step(t):
 
 
 def test_quantization_error_bound(oracle):
-    x = _cfg1(oracle)
+    x = _tiny_shard(oracle)
     B = 128
     q, a, s, t = oracle.compress(x, B, 1.0, with_quot=True)
     err = np.abs(E4M3_VALUES[q] - t)
@@ -267,7 +267,7 @@ def test_quantization_error_bound(oracle):
 
 def test_reconstruction_error_identity(oracle):
     # ||xh - x||_2 = ||s dec(q) - y||_2 / alpha per block (the rotation is orthogonal)
-    x = _cfg1(oracle)
+    x = _tiny_shard(oracle)
     B = 128
     q, a, s, t = oracle.compress(x, B, 1.0, with_quot=True)
     xh = oracle.decompress_f64(q, a, s, B).reshape(-1, B)
@@ -296,7 +296,7 @@ def test_exact_inverse_without_rounding(oracle, B):
 
 
 def test_decompress_dtypes_agree_with_f64(oracle):
-    x = _cfg1(oracle)
+    x = _tiny_shard(oracle)
     B = 128
     q, a, s = oracle.compress(x, B, 1.0)
     r64 = oracle.decompress_f64(q, a, s, B)

@@ -8,7 +8,7 @@ import pytest
 from scipy.linalg import hadamard
 
 from tiecheck import E4M3_VALUES, INT8_VALUES, assert_codes_match, tie_cap
-from workloads import bf16_bits_to_f32, f32_to_bf16_bits, make_shard, random_bf16_bits
+from workloads import TINY, bf16_bits_to_f32, f32_to_bf16_bits, make_shard, random_bf16_bits
 
 F32_ULP = 2.0 ** -23
 INT8, NOROT = 1, 2
@@ -126,7 +126,7 @@ def test_codes_equal_plain_absmax_quantizer_of_the_rotated_block(oracle, flags):
 @pytest.mark.parametrize("flags", FLAG_SETS)
 def test_error_bound_and_reconstruction_identity(oracle, flags):
     B = 128
-    x = make_shard(1).reshape(-1)
+    x = make_shard(TINY).reshape(-1)
     q, a, s, t = oracle.compress(x, B, 1.0, with_quot=True, flags=flags)
     vals = _values(flags)[q]
     if flags & INT8:
@@ -142,7 +142,7 @@ def test_error_bound_and_reconstruction_identity(oracle, flags):
 
 @pytest.mark.parametrize("flags", [INT8, INT8 | NOROT, NOROT])
 def test_codes_invariant_to_target_variants(oracle, flags):
-    x = make_shard(1).reshape(-1)
+    x = make_shard(TINY).reshape(-1)
     q1, a1, s1, t1 = oracle.compress(x, 128, 1.0, with_quot=True, flags=flags)
     qT, aT, sT = oracle.compress(x, 128, 37.5, flags=flags)
     # a different T changes the fp32 roundings of alpha and s, which moves every quotient by a

@@ -22,7 +22,7 @@ Recipe (fixed draw order, numpy PCG64 ``default_rng(seed)``):
 * mixtures are per element: one ``rng.random()`` draw picks the component.
 
 Everything is returned as raw bfloat16 bit patterns (``numpy.uint16``) in the
-row-major order of the config's shape, so a flat view is the buffer the library
+row-major order of the workload's shape, so a flat view is the buffer the library
 compresses.
 """
 from __future__ import annotations
@@ -35,8 +35,13 @@ from typing import Tuple
 import numpy as np
 
 __all__ = [
-    "Config",
-    "CONFIGS",
+    "Workload",
+    "WORKLOADS",
+    "TINY",
+    "GPT2_7B",
+    "GPT6_7B",
+    "GPT13B_GRAD",
+    "QWEN7B",
     "make_shard",
     "make_shards",
     "f32_to_bf16_bits",
@@ -47,11 +52,11 @@ __all__ = [
 
 
 @dataclass(frozen=True)
-class Config:
+class Workload:
     """One synthetic workload: tensor shape, block size and reduce width."""
 
-    cid: int
-    name: str
+    key: str
+    label: str
     shape: Tuple[int, ...]
     block: int
     shards: int  # P: number of simulated rank shards (1 = no reduce)
@@ -68,13 +73,19 @@ class Config:
         return self.n // self.block
 
 
-CONFIGS = {
-    1: Config(1, "tiny-roundtrip 512x1024", (512, 1024), 128, 1),
-    2: Config(2, "gpt-2.7b tp activation [1,2048,2560]", (1, 2048, 2560), 128, 1),
-    3: Config(3, "gpt-6.7b tp activation [4,2048,4096]", (4, 2048, 4096), 256, 4),
-    4: Config(4, "gpt-13b tp gradient [4,4096,5120]", (4, 4096, 5120), 128, 1),
-    5: Config(5, "qwen2.5-7b tp activation [8,4096,3584]", (8, 4096, 3584), 128, 8),
-}
+TINY = "tiny"
+GPT2_7B = "gpt2.7b-act"
+GPT6_7B = "gpt6.7b-act"
+GPT13B_GRAD = "gpt13b-grad"
+QWEN7B = "qwen2.5-7b-act"
+
+WORKLOADS = {w.key: w for w in (
+    Workload(TINY, "tiny-roundtrip 512x1024", (512, 1024), 128, 1),
+    Workload(GPT2_7B, "gpt-2.7b tp activation [1,2048,2560]", (1, 2048, 2560), 128, 1),
+    Workload(GPT6_7B, "gpt-6.7b tp activation [4,2048,4096]", (4, 2048, 4096), 256, 4),
+    Workload(GPT13B_GRAD, "gpt-13b tp gradient [4,4096,5120]", (4, 4096, 5120), 128, 1),
+    Workload(QWEN7B, "qwen2.5-7b tp activation [8,4096,3584]", (8, 4096, 3584), 128, 8),
+)}
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -103,10 +114,10 @@ def _to_bits(v64: np.ndarray) -> np.ndarray:
     return f32_to_bf16_bits(v64.astype(np.float32))
 
 
-def _cfg1(shard: int) -> np.ndarray:
+def _tiny(shard: int) -> np.ndarray:
     # 90% Laplace(0, 0.01), 9% 0.05 * t(3), 1% +-U(5, 50); blocks 0, 1, 2048 and 4095 all-zero.
-    cfg = CONFIGS[1]
-    n = cfg.n
+    wl = WORKLOADS[TINY]
+    n = wl.n
     rng = np.random.default_rng(shard)
     cat = rng.random(n)
     v = rng.laplace(0.0, 0.01, n)
@@ -117,41 +128,41 @@ def _cfg1(shard: int) -> np.ndarray:
     k = int(out.sum())
     v[out] = rng.uniform(5.0, 50.0, k) * _signs(rng, k)
     bits = _to_bits(v)
-    B = cfg.block
+    B = wl.block
     for b in (0, 1, 2048, 4095):
         bits[b * B:(b + 1) * B] = 0
-    return bits.reshape(cfg.shape)
+    return bits.reshape(wl.shape)
 
 
-def _cfg2(shard: int) -> np.ndarray:
+def _gpt2_7b(shard: int) -> np.ndarray:
     # Laplace(0, 0.02) body, 8 fixed outlier channels of +-U(10, 100) in every row.
-    cfg = CONFIGS[2]
-    rows, cols = cfg.shape[0] * cfg.shape[1], cfg.shape[2]
+    wl = WORKLOADS[GPT2_7B]
+    rows, cols = wl.shape[0] * wl.shape[1], wl.shape[2]
     rng = np.random.default_rng(shard)
     ch = np.sort(rng.choice(cols, 8, replace=False))
     v = rng.laplace(0.0, 0.02, rows * cols).reshape(rows, cols)
     k = rows * ch.size
     v[:, ch] = (rng.uniform(10.0, 100.0, k) * _signs(rng, k)).reshape(rows, ch.size)
-    return _to_bits(v.reshape(-1)).reshape(cfg.shape)
+    return _to_bits(v.reshape(-1)).reshape(wl.shape)
 
 
-def _cfg3(shard: int) -> np.ndarray:
+def _gpt6_7b(shard: int) -> np.ndarray:
     # Laplace(0, 0.02) body with 9% of elements replaced by a 0.05 * t(2.5) tail.
-    cfg = CONFIGS[3]
-    n = cfg.n
+    wl = WORKLOADS[GPT6_7B]
+    n = wl.n
     rng = np.random.default_rng(shard)
     cat = rng.random(n)
     v = rng.laplace(0.0, 0.02, n)
     tail = cat >= 0.91
     v[tail] = rng.standard_t(2.5, int(tail.sum())) * 0.05
-    return _to_bits(v).reshape(cfg.shape)
+    return _to_bits(v).reshape(wl.shape)
 
 
-def _cfg4(shard: int) -> np.ndarray:
+def _gpt13b_grad(shard: int) -> np.ndarray:
     # Laplace(0, 1e-4) with 0.1% spikes +-U(1e-2, 1); then 5% of blocks moved into the
     # bfloat16 subnormal range and 1% of blocks (disjoint) set to zero.
-    cfg = CONFIGS[4]
-    n, B, nb = cfg.n, cfg.block, cfg.nblocks
+    wl = WORKLOADS[GPT13B_GRAD]
+    n, B, nb = wl.n, wl.block, wl.nblocks
     rng = np.random.default_rng(shard)
     cat = rng.random(n)
     v = rng.laplace(0.0, 1e-4, n)
@@ -174,52 +185,53 @@ def _cfg4(shard: int) -> np.ndarray:
     q = np.round(scaled * 2.0 ** 133) * 2.0 ** -133  # numpy rounds half to even
     blk[sub_blocks] = f32_to_bf16_bits(q.astype(np.float32))  # exact: q is on the grid
     blk[zero_blocks] = 0
-    return blk.reshape(cfg.shape)
+    return blk.reshape(wl.shape)
 
 
-def _cfg5(shard: int) -> np.ndarray:
+def _qwen7b(shard: int) -> np.ndarray:
     # Laplace(0, 0.02) body with 16 outlier channels +-U(20, 200); the channel set is a
     # property of the model, drawn once from seed 0 and shared by all shards.
-    cfg = CONFIGS[5]
-    rows, cols = cfg.shape[0] * cfg.shape[1], cfg.shape[2]
+    wl = WORKLOADS[QWEN7B]
+    rows, cols = wl.shape[0] * wl.shape[1], wl.shape[2]
     ch = np.sort(np.random.default_rng(0).choice(cols, 16, replace=False))
     rng = np.random.default_rng(shard)
     v = rng.laplace(0.0, 0.02, rows * cols).reshape(rows, cols)
     k = rows * ch.size
     v[:, ch] = (rng.uniform(20.0, 200.0, k) * _signs(rng, k)).reshape(rows, ch.size)
-    return _to_bits(v.reshape(-1)).reshape(cfg.shape)
+    return _to_bits(v.reshape(-1)).reshape(wl.shape)
 
 
-_MAKERS = {1: _cfg1, 2: _cfg2, 3: _cfg3, 4: _cfg4, 5: _cfg5}
+_MAKERS = {TINY: _tiny, GPT2_7B: _gpt2_7b, GPT6_7B: _gpt6_7b, GPT13B_GRAD: _gpt13b_grad,
+           QWEN7B: _qwen7b}
 
 
-def make_shard(cid: int, shard: int = 0) -> np.ndarray:
-    """bfloat16 bits (uint16, config shape) of shard ``shard`` of config ``cid``."""
-    if cid not in _MAKERS:
-        raise ValueError(f"unknown config {cid}")
-    return _MAKERS[cid](shard)
+def make_shard(key: str, shard: int = 0) -> np.ndarray:
+    """bfloat16 bits (uint16, the workload's shape) of shard ``shard`` of workload ``key``."""
+    if key not in _MAKERS:
+        raise ValueError(f"unknown workload {key!r}")
+    return _MAKERS[key](shard)
 
 
-def make_shards(cid: int, count: int | None = None, workers: int | None = None) -> np.ndarray:
-    """All P shards of a config stacked as [P, *shape] (shard p uses seed p).
+def make_shards(key: str, count: int | None = None, workers: int | None = None) -> np.ndarray:
+    """All P shards of a workload stacked as [P, *shape] (shard p uses seed p).
 
     Shards are independent, so they are drawn by a pool of ``workers`` threads (default: up to
     8, bounded by the CPUs this process may use): numpy's bulk generators and array operations
     release the GIL.  Threads rather than processes, so that nothing is forked (forking under a
     profiler's injected runtime, or after the GPU runtime is up, is unsafe)."""
-    cfg = CONFIGS[cid]
-    P = cfg.shards if count is None else count
+    wl = WORKLOADS[key]
+    P = wl.shards if count is None else count
     if workers is None:
         workers = min(8, P, len(os.sched_getaffinity(0)))
-    out = np.empty((P,) + cfg.shape, dtype=np.uint16)
+    out = np.empty((P,) + wl.shape, dtype=np.uint16)
     if workers <= 1 or P == 1:
         for p in range(P):
-            out[p] = make_shard(cid, p)
+            out[p] = make_shard(key, p)
         return out
     from concurrent.futures import ThreadPoolExecutor
 
     def fill(p):
-        out[p] = make_shard(cid, p)
+        out[p] = make_shard(key, p)
 
     with ThreadPoolExecutor(workers) as ex:
         list(ex.map(fill, range(P)))
