@@ -355,6 +355,68 @@ def test_bitwise_deterministic_and_stream_safe(tfp8):
         assert torch.equal(u, v)
 
 
+def test_concurrent_host_threads(tfp8):
+    # The header allows calls from several host threads at once (the library keeps no state
+    # beyond a per-device CU count).  Four threads each run compress -> reduce_fp8 (P = 2) ->
+    # decompress 25 times on their own stream and buffers, concurrently (ctypes releases the
+    # GIL during the calls); every result must equal the same pipeline run alone.
+    import threading
+
+    B, n, T = 128, WORKLOADS[GPT2_7B].n, 1.0
+    nb = n // B
+    jobs = []
+    for t in range(4):
+        x = bits_to_gpu(np.stack([make_shard(GPT2_7B, 2 * t + k).reshape(-1) for k in range(2)]))
+        bufs = dict(x=x.reshape(-1), q=torch.empty(2 * n, dtype=torch.uint8, device=DEV),
+                    a=torch.empty(2 * nb, dtype=torch.float32, device=DEV),
+                    s=torch.empty(2 * nb, dtype=torch.float32, device=DEV),
+                    rq=torch.empty(n, dtype=torch.uint8, device=DEV),
+                    ra=torch.empty(nb, dtype=torch.float32, device=DEV),
+                    rs=torch.empty(nb, dtype=torch.float32, device=DEV),
+                    out=torch.empty(n, dtype=torch.bfloat16, device=DEV))
+        jobs.append(bufs)
+
+    def pipeline(b, stream):
+        assert tfp8.compress_raw(b["x"].data_ptr(), tfp8.BF16, 2 * n, B, T, b["q"].data_ptr(),
+                                 b["a"].data_ptr(), b["s"].data_ptr(), stream) == 0
+        assert tfp8.reduce_fp8_raw(b["q"].data_ptr(), b["a"].data_ptr(), b["s"].data_ptr(), 2, n,
+                                   B, T, b["rq"].data_ptr(), b["ra"].data_ptr(),
+                                   b["rs"].data_ptr(), stream) == 0
+        assert tfp8.decompress_raw(b["rq"].data_ptr(), b["ra"].data_ptr(), b["rs"].data_ptr(), n,
+                                   B, b["out"].data_ptr(), tfp8.BF16, stream) == 0
+
+    alone = []
+    for b in jobs:
+        pipeline(b, torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        alone.append({k: v.clone() for k, v in b.items() if k != "x"})
+        for k in ("q", "rq", "out"):
+            b[k].zero_()
+    torch.cuda.synchronize()
+
+    streams = [torch.cuda.Stream() for _ in jobs]
+    errors = []
+
+    def worker(b, st):
+        try:
+            for _ in range(25):
+                pipeline(b, st.cuda_stream)
+        except Exception as e:  # reported after join
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(b, st)) for b, st in zip(jobs, streams)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for b, ref in zip(jobs, alone):
+        for k, v in ref.items():
+            assert torch.equal(b[k].view(torch.uint8) if b[k].dtype == torch.bfloat16 else b[k],
+                               v.view(torch.uint8) if v.dtype == torch.bfloat16 else v), k
+
+
 def test_zero_length_is_noop(tfp8):
     x = torch.empty(0, dtype=torch.bfloat16, device=DEV)
     q, a, s = tfp8.compress(x, 128, 1.0)
