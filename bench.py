@@ -262,6 +262,30 @@ def all_workloads(reps: int):
                                                    rs.data_ptr(), stream.cuda_stream))
             measure(key, f"reduce P={P}, {P} x n/{P} (one rank)", fn, (P + 1) * c * (1 + 8 / B),
                     c, B, P)
+            # the same share read in place from the stacked shards (row stride n), and from one
+            # buffer of [codes | alpha | scale] messages, one per peer, as one all-to-all would
+            # leave them, packed and with 65 KiB between messages
+            vq, va, vs = q[:ntot].view(P, n), al[:ntot // B].view(P, nb), sc[:ntot // B].view(P, nb)
+            fn = lambda: check(tfp8.reduce_strided_raw(vq.data_ptr(), n, va.data_ptr(), nb,
+                                                       vs.data_ptr(), nb, P, c, B, TARGET,
+                                                       rq.data_ptr(), ra.data_ptr(), rs.data_ptr(),
+                                                       stream.cuda_stream))
+            measure(key, f"reduce P={P}, {P} x n/{P} in place (stride n)", fn,
+                    (P + 1) * c * (1 + 8 / B), c, B, P)
+            cb = c // B
+            for pad in (0, 65536 + 1024):
+                M = (c + 8 * cb + pad + 15) // 16 * 16
+                msg = torch.zeros(P, M, dtype=torch.uint8, device=dev)
+                msg[:, :c].copy_(cq)
+                msg[:, c:c + 4 * cb].view(torch.float32).copy_(ca)
+                msg[:, c + 4 * cb:c + 8 * cb].view(torch.float32).copy_(cs)
+                mp = msg.data_ptr()
+                fn = (lambda mp=mp, M=M: check(tfp8.reduce_strided_raw(
+                    mp, M, mp + c, M // 4, mp + c + 4 * cb, M // 4, P, c, B, TARGET,
+                    rq.data_ptr(), ra.data_ptr(), rs.data_ptr(), stream.cuda_stream)))
+                measure(key, f"reduce P={P}, {P} x n/{P} from messages {M} B apart", fn,
+                        (P + 1) * c * (1 + 8 / B), c, B, P)
+                del msg
             del rq, ra, rs, cq, ca, cs
         if key == ACC_WORKLOAD:
             # gradient accumulation: main = compressed shard 0, local = shard 1

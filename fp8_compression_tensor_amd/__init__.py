@@ -20,7 +20,7 @@ import torch
 __all__ = [
     "compress", "decompress", "reduce_fp8", "compress_raw", "decompress_raw", "reduce_fp8_raw",
     "status_string", "lib", "LIB_PATH", "TFP8Error", "BF16", "F32", "SUPPORTED_BLOCKS",
-    "FLAG_INT8", "FLAG_NO_ROTATION", "accumulate", "accumulate_raw",
+    "FLAG_INT8", "FLAG_NO_ROTATION", "accumulate", "accumulate_raw", "reduce_strided_raw",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtfp8.so")
@@ -64,6 +64,9 @@ def lib() -> ctypes.CDLL:
         L.tfp8_decompress_ex.restype = i32
         L.tfp8_reduce_ex.argtypes = [vp, vp, vp, i32, i64, i32, f32, u32, vp, vp, vp, vp]
         L.tfp8_reduce_ex.restype = i32
+        L.tfp8_reduce_strided.argtypes = [vp, i64, vp, i64, vp, i64, i32, i64, i32, f32, u32,
+                                          vp, vp, vp, vp]
+        L.tfp8_reduce_strided.restype = i32
         L.tfp8_accumulate.argtypes = [vp, vp, vp, vp, i32, i64, i32, f32, u32, vp, vp, vp, vp]
         L.tfp8_accumulate.restype = i32
         L.tfp8_status_string.argtypes = [i32]
@@ -112,6 +115,17 @@ def reduce_fp8_raw(codes_ptr: int, alpha_ptr: int, scale_ptr: int, P: int, n: in
                                     codes_out_ptr, alpha_out_ptr, scale_out_ptr, stream)
     return lib().tfp8_reduce_fp8(codes_ptr, alpha_ptr, scale_ptr, P, n, block, target,
                                  codes_out_ptr, alpha_out_ptr, scale_out_ptr, stream)
+
+
+def reduce_strided_raw(codes_ptr: int, codes_stride: int, alpha_ptr: int, alpha_stride: int,
+                       scale_ptr: int, scale_stride: int, P: int, n: int, block: int,
+                       target: float, codes_out_ptr: int, alpha_out_ptr: int, scale_out_ptr: int,
+                       stream: int = 0, flags: int = 0) -> int:
+    """Contribution p at codes_ptr + p * codes_stride (bytes), alpha_ptr / scale_ptr + p times
+    their stride (float32 elements)."""
+    return lib().tfp8_reduce_strided(codes_ptr, codes_stride, alpha_ptr, alpha_stride, scale_ptr,
+                                     scale_stride, P, n, block, target, flags, codes_out_ptr,
+                                     alpha_out_ptr, scale_out_ptr, stream)
 
 
 def accumulate_raw(codes_ptr: int, alpha_ptr: int, scale_ptr: int, grad_ptr: int, grad_dtype: int,
@@ -212,32 +226,68 @@ def decompress(codes: torch.Tensor, alpha: torch.Tensor, scale: torch.Tensor, bl
     return out
 
 
+def _rows(t: torch.Tensor, dtype: torch.dtype, P: int, m: int, name: str) -> int:
+    """A [P, m] view whose rows are contiguous, at any row stride (for example rows of one receive
+    buffer); returns the row stride in elements."""
+    if not (isinstance(t, torch.Tensor) and t.is_cuda):
+        raise ValueError("tfp8 operates on GPU tensors only (no CPU path)")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != 2 or tuple(t.shape) != (P, m):
+        raise ValueError(f"{name} must be [{P}, {m}], got {list(t.shape)}")
+    if m > 1 and t.stride(1) != 1:
+        raise ValueError(f"the rows of {name} must be contiguous")
+    return t.stride(0) if P > 1 else m
+
+
 def reduce_fp8(codes: torch.Tensor, alpha: torch.Tensor, scale: torch.Tensor, block: int = 128,
                target: float = 1.0, out=None, flags: int = 0):
-    """codes [P, ...], alpha and scale [P, nb] -> (codes [...], alpha [nb], scale [nb])."""
-    _need_gpu(codes, alpha, scale)
+    """codes [P, ...], alpha and scale [P, nb] -> (codes [...], alpha [nb], scale [nb]).
+
+    Contiguous stacks go to tfp8_reduce_fp8.  Otherwise codes must be a [P, n] view and alpha,
+    scale [P, nb] views whose rows are contiguous but may lie at any stride, for example rows of
+    one buffer holding a [codes | alpha | scale] message per peer; those go to
+    tfp8_reduce_strided and give the same result."""
     if codes.dim() < 2:
         raise ValueError("codes must be stacked as [P, ...]")
     P = codes.shape[0]
     n = codes[0].numel()
     nb = _blocks(n, block)
-    _need_buf(codes, torch.uint8, P * n, "codes")
-    _need_buf(alpha, torch.float32, P * nb, "alpha")
-    _need_buf(scale, torch.float32, P * nb, "scale")
+    strided = not (codes.is_contiguous() and alpha.is_contiguous() and scale.is_contiguous())
+    if strided:
+        cst = _rows(codes, torch.uint8, P, n, "codes")
+        ast = _rows(alpha, torch.float32, P, nb, "alpha")
+        sst = _rows(scale, torch.float32, P, nb, "scale")
+        if not (codes.device == alpha.device == scale.device):
+            raise ValueError("tensors on different devices")
+    else:
+        _need_gpu(codes, alpha, scale)
+        _need_buf(codes, torch.uint8, P * n, "codes")
+        _need_buf(alpha, torch.float32, P * nb, "alpha")
+        _need_buf(scale, torch.float32, P * nb, "scale")
     if out is None:
         codes_out = torch.empty(codes.shape[1:], dtype=torch.uint8, device=codes.device)
         alpha_out = torch.empty(nb, dtype=torch.float32, device=codes.device)
         scale_out = torch.empty(nb, dtype=torch.float32, device=codes.device)
     else:
         codes_out, alpha_out, scale_out = out
-        _need_gpu(codes, codes_out, alpha_out, scale_out)
+        _need_gpu(codes_out, alpha_out, scale_out)
+        if codes_out.device != codes.device:
+            raise ValueError(f"tensors on different devices ({codes.device} and {codes_out.device})")
         _need_buf(codes_out, torch.uint8, n, "codes_out")
         _need_buf(alpha_out, torch.float32, nb, "alpha_out")
         _need_buf(scale_out, torch.float32, nb, "scale_out")
     with torch.cuda.device(codes.device):
-        _check(reduce_fp8_raw(codes.data_ptr(), alpha.data_ptr(), scale.data_ptr(), P, n, block,
-                              float(target), codes_out.data_ptr(), alpha_out.data_ptr(),
-                              scale_out.data_ptr(), _stream(codes), flags))
+        if strided:
+            st = reduce_strided_raw(codes.data_ptr(), cst, alpha.data_ptr(), ast,
+                                    scale.data_ptr(), sst, P, n, block, float(target),
+                                    codes_out.data_ptr(), alpha_out.data_ptr(),
+                                    scale_out.data_ptr(), _stream(codes), flags)
+        else:
+            st = reduce_fp8_raw(codes.data_ptr(), alpha.data_ptr(), scale.data_ptr(), P, n, block,
+                                float(target), codes_out.data_ptr(), alpha_out.data_ptr(),
+                                scale_out.data_ptr(), _stream(codes), flags)
+        _check(st)
     return codes_out, alpha_out, scale_out
 
 

@@ -446,13 +446,16 @@ __global__ __launch_bounds__(kThreads) void k_decompress(const uint8_t *__restri
 // --------------------------------------------------------------------------------------------
 // K3: reduce.  B/16 lanes per block, 16 consecutive codes per lane (one 16-byte load per
 // contribution), no Hadamard.  PB > 0: exactly PB contributions, all loads issued before any
-// arithmetic; PB = 0: any P, in chunks of 8.
+// arithmetic; PB = 0: any P, in chunks of 8.  Contribution p's codes start at codes + p cstride
+// and its scales at alpha + p astride, scale + p sstride (cstride = n, astride = sstride = nb
+// for contiguous stacks).
 
 template <int B, int PB, int FLAGS>
 __global__ __launch_bounds__(kThreads) void k_reduce(const uint8_t *__restrict__ codes,
                                                      const float *__restrict__ alpha,
                                                      const float *__restrict__ scale, int P,
-                                                     int64_t n, int64_t nb, float TB,
+                                                     int64_t cstride, int64_t astride,
+                                                     int64_t sstride, int64_t nb, float TB,
                                                      uint8_t *__restrict__ codes_out,
                                                      float *__restrict__ alpha_out,
                                                      float *__restrict__ scale_out) {
@@ -489,9 +492,9 @@ __global__ __launch_bounds__(kThreads) void k_reduce(const uint8_t *__restrict__
 #pragma unroll
       for (int c = 0; c < CH; ++c)
         if (PB > 0 || p0 + c < P) {
-          d[c] = ld_stream((const u32x4 *)(cb + (int64_t)(p0 + c) * n));
-          sp[c] = scale[(int64_t)(p0 + c) * nb + cblk];
-          ap[c] = alpha[(int64_t)(p0 + c) * nb + cblk];
+          d[c] = ld_stream((const u32x4 *)(cb + (int64_t)(p0 + c) * cstride));
+          sp[c] = scale[(int64_t)(p0 + c) * sstride + cblk];
+          ap[c] = alpha[(int64_t)(p0 + c) * astride + cblk];
         }
 #pragma unroll
       for (int c = 0; c < CH; ++c) {
@@ -1042,16 +1045,17 @@ tfp8_status launch_decompress(const uint8_t *codes, const float *alpha, const fl
 
 template <int B, int FLAGS>
 tfp8_status launch_reduce_t(const uint8_t *codes, const float *alpha, const float *scale, int P,
-                     int64_t n, int64_t nb, float target, uint8_t *codes_out, float *alpha_out,
-                     float *scale_out, hipStream_t st) {
+                            int64_t cstride, int64_t astride, int64_t sstride, int64_t nb,
+                            float target, uint8_t *codes_out, float *alpha_out, float *scale_out,
+                            hipStream_t st) {
   // the reduce works on r = sum_p g_p dec(q_p) directly, with or without the rotation: its
   // energy is that of the sum, sum(r^2) = sum(z^2)
   const float TB = target * (float)B;
   constexpr int BPW = 64 / (B / 16);
   const unsigned grid = grid_for((nb + BPW - 1) / BPW, TFP8_REDUCE_WGS_PER_CU);
 #define TFP8_LAUNCH_REDUCE(PB)                                                               \
-  return launch(k_reduce<B, PB, FLAGS>, grid, kThreads, st, codes, alpha, scale, P, n, nb, TB, \
-                codes_out, alpha_out, scale_out)
+  return launch(k_reduce<B, PB, FLAGS>, grid, kThreads, st, codes, alpha, scale, P, cstride,    \
+                astride, sstride, nb, TB, codes_out, alpha_out, scale_out)
   switch (P) {
     case 1: TFP8_LAUNCH_REDUCE(1);
     case 2: TFP8_LAUNCH_REDUCE(2);
@@ -1064,13 +1068,14 @@ tfp8_status launch_reduce_t(const uint8_t *codes, const float *alpha, const floa
 
 template <int B>
 tfp8_status launch_reduce(const uint8_t *codes, const float *alpha, const float *scale, int P,
-                          int64_t n, int64_t nb, float target, uint32_t flags, uint8_t *codes_out,
-                          float *alpha_out, float *scale_out, hipStream_t st) {
+                          int64_t cstride, int64_t astride, int64_t sstride, int64_t nb,
+                          float target, uint32_t flags, uint8_t *codes_out, float *alpha_out,
+                          float *scale_out, hipStream_t st) {
   if (flags & kInt8)
-    return launch_reduce_t<B, kInt8>(codes, alpha, scale, P, n, nb, target, codes_out, alpha_out,
-                                     scale_out, st);
-  return launch_reduce_t<B, 0>(codes, alpha, scale, P, n, nb, target, codes_out, alpha_out,
-                               scale_out, st);
+    return launch_reduce_t<B, kInt8>(codes, alpha, scale, P, cstride, astride, sstride, nb, target,
+                                     codes_out, alpha_out, scale_out, st);
+  return launch_reduce_t<B, 0>(codes, alpha, scale, P, cstride, astride, sstride, nb, target,
+                               codes_out, alpha_out, scale_out, st);
 }
 
 template <int B, bool F32, int FLAGS>
@@ -1119,7 +1124,7 @@ tfp8_status launch_accumulate(const uint8_t *codes, const float *alpha, const fl
 
 extern "C" {
 
-int32_t tfp8_version(void) { return (1 << 16) | 2; }
+int32_t tfp8_version(void) { return (1 << 16) | 3; }
 
 const char *tfp8_status_string(tfp8_status status) {
   switch (status) {
@@ -1210,20 +1215,29 @@ tfp8_status tfp8_decompress(const uint8_t *codes, const float *alpha, const floa
   return tfp8_decompress_ex(codes, alpha, scale, n, block, 0, out, out_dtype, stream);
 }
 
-tfp8_status tfp8_reduce_ex(const uint8_t *codes, const float *alpha, const float *scale, int32_t P,
-                           int64_t n, int32_t block, float target, uint32_t flags,
-                           uint8_t *codes_out, float *alpha_out, float *scale_out, void *stream) {
+// The reduce entry points share this: contribution p at codes + p cstride (bytes) and
+// alpha + p astride, scale + p sstride (floats); contiguous stacks have cstride = n and
+// astride = sstride = n / block.  An input's span runs from its base to the end of its last
+// contribution; no output may overlap any input span or another output.
+static tfp8_status reduce_checked(const uint8_t *codes, int64_t cstride, const float *alpha,
+                                  int64_t astride, const float *scale, int64_t sstride, int32_t P,
+                                  int64_t n, int32_t block, float target, uint32_t flags,
+                                  uint8_t *codes_out, float *alpha_out, float *scale_out,
+                                  void *stream) {
   if (!block_ok(block)) return TFP8_E_BLOCK;
   if (n < 0 || n > TFP8_MAX_N || n % block != 0) return TFP8_E_SIZE;
+  const int64_t nb = n / block;
+  if (cstride > TFP8_MAX_N || astride > TFP8_MAX_N || sstride > TFP8_MAX_N) return TFP8_E_SIZE;
   if (P < 1 || P > 64 || !target_ok(target) || (flags & ~TFP8_FLAGS_ALL)) return TFP8_E_ARG;
+  if (cstride < n || astride < nb || sstride < nb) return TFP8_E_ARG;  // rows would overlap
   if (n == 0) return TFP8_OK;
   if (!codes || !alpha || !scale || !codes_out || !alpha_out || !scale_out) return TFP8_E_NULL;
   if (!aligned(codes, 16) || !aligned(codes_out, 16) || !aligned(alpha, 4) || !aligned(scale, 4) ||
-      !aligned(alpha_out, 4) || !aligned(scale_out, 4))
+      !aligned(alpha_out, 4) || !aligned(scale_out, 4) || cstride % 16 != 0)
     return TFP8_E_ALIGN;
-  const int64_t nb = n / block;
-  const Range ins[3] = {range_of(codes, (int64_t)P * n), range_of(alpha, (int64_t)P * nb * 4),
-                        range_of(scale, (int64_t)P * nb * 4)};
+  const Range ins[3] = {range_of(codes, (int64_t)(P - 1) * cstride + n),
+                        range_of(alpha, ((int64_t)(P - 1) * astride + nb) * 4),
+                        range_of(scale, ((int64_t)(P - 1) * sstride + nb) * 4)};
   const Range outs[3] = {range_of(codes_out, n), range_of(alpha_out, nb * 4),
                          range_of(scale_out, nb * 4)};
   for (int i = 0; i < 3; ++i) {
@@ -1233,13 +1247,35 @@ tfp8_status tfp8_reduce_ex(const uint8_t *codes, const float *alpha, const float
       if (overlap(outs[i], outs[k])) return TFP8_E_ARG;
   }
   hipStream_t st = (hipStream_t)stream;
+#define TFP8_CASE(BB)                                                                          \
+  case BB:                                                                                     \
+    return launch_reduce<BB>(codes, alpha, scale, P, cstride, astride, sstride, nb, target,    \
+                             flags, codes_out, alpha_out, scale_out, st);
   switch (block) {
-    case 64: return launch_reduce<64>(codes, alpha, scale, P, n, nb, target, flags, codes_out, alpha_out, scale_out, st);
-    case 128: return launch_reduce<128>(codes, alpha, scale, P, n, nb, target, flags, codes_out, alpha_out, scale_out, st);
-    case 256: return launch_reduce<256>(codes, alpha, scale, P, n, nb, target, flags, codes_out, alpha_out, scale_out, st);
-    case 512: return launch_reduce<512>(codes, alpha, scale, P, n, nb, target, flags, codes_out, alpha_out, scale_out, st);
+    TFP8_CASE(64)
+    TFP8_CASE(128)
+    TFP8_CASE(256)
+    TFP8_CASE(512)
   }
+#undef TFP8_CASE
   return TFP8_E_BLOCK;
+}
+
+tfp8_status tfp8_reduce_ex(const uint8_t *codes, const float *alpha, const float *scale, int32_t P,
+                           int64_t n, int32_t block, float target, uint32_t flags,
+                           uint8_t *codes_out, float *alpha_out, float *scale_out, void *stream) {
+  const int64_t nb = block_ok(block) ? n / block : 0;
+  return reduce_checked(codes, n, alpha, nb, scale, nb, P, n, block, target, flags, codes_out,
+                        alpha_out, scale_out, stream);
+}
+
+tfp8_status tfp8_reduce_strided(const uint8_t *codes, int64_t codes_stride, const float *alpha,
+                                int64_t alpha_stride, const float *scale, int64_t scale_stride,
+                                int32_t P, int64_t n, int32_t block, float target, uint32_t flags,
+                                uint8_t *codes_out, float *alpha_out, float *scale_out,
+                                void *stream) {
+  return reduce_checked(codes, codes_stride, alpha, alpha_stride, scale, scale_stride, P, n, block,
+                        target, flags, codes_out, alpha_out, scale_out, stream);
 }
 
 tfp8_status tfp8_reduce_fp8(const uint8_t *codes, const float *alpha, const float *scale, int32_t P,

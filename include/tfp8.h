@@ -118,6 +118,25 @@ tfp8_status tfp8_reduce_ex(const uint8_t *codes, const float *alpha, const float
                            int64_t n, int32_t block, float target, uint32_t flags,
                            uint8_t *codes_out, float *alpha_out, float *scale_out, void *stream);
 
+/* The local reduce with the P contributions at caller-chosen strides, so that it can read them
+ * where a collective left them: for example a receive buffer holding one message per peer,
+ * [codes | alpha | scale] back to back, which one all-to-all can fill.  Contribution p is
+ *   codes + p * codes_stride  (bytes),  alpha + p * alpha_stride,  scale + p * scale_stride
+ * (floats), each n codes or n/block scales long.  codes_stride >= n and a multiple of 16;
+ * alpha_stride, scale_stride >= n/block; all strides <= TFP8_MAX_N (TFP8_E_SIZE above it,
+ * TFP8_E_ARG below the row length, TFP8_E_ALIGN for codes_stride % 16 != 0).  The inputs may
+ * overlap one another (they are only read).  Each input's span runs from its pointer to the end
+ * of its last contribution; an output that overlaps any input span, or another output, is
+ * TFP8_E_ARG.  The result is that of tfp8_reduce_ex on the same contributions stacked
+ * contiguously, bit for bit; tfp8_reduce_ex is this call with codes_stride = n and
+ * alpha_stride = scale_stride = n/block.  Same pages as tfp8_reduce_fp8 (the AGoQ page,
+ * section 2.B, reduces chunks received from the other ranks). */
+tfp8_status tfp8_reduce_strided(const uint8_t *codes, int64_t codes_stride, const float *alpha,
+                                int64_t alpha_stride, const float *scale, int64_t scale_stride,
+                                int32_t P, int64_t n, int32_t block, float target, uint32_t flags,
+                                uint8_t *codes_out, float *alpha_out, float *scale_out,
+                                void *stream);
+
 /* Local gradient accumulation: the compressed main gradient (codes[n], alpha[n/block],
  * scale[n/block], as written by tfp8_compress_ex with the same flags) is dequantized, the dense
  * local gradient grad[n] (bfloat16 or float32) is added, and the sum is requantized with the same

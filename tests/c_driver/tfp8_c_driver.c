@@ -90,6 +90,12 @@ static int run_errors(void) {
          TFP8_E_ARG);
   expect("reduce_ex flags", tfp8_reduce_ex(q, a, s, 2, 1024, 128, 1.0f, 8u, q2, a2, s2, NULL),
          TFP8_E_ARG);
+  expect("reduce_strided stride below n",
+         tfp8_reduce_strided(q, 1008, a, 8, s, 8, 2, 1024, 128, 1.0f, 0u, q2, a2, s2, NULL),
+         TFP8_E_ARG);
+  expect("reduce_strided stride % 16",
+         tfp8_reduce_strided(q, 1032, a, 8, s, 8, 2, 1024, 128, 1.0f, 0u, q2, a2, s2, NULL),
+         TFP8_E_ALIGN);
   expect("accumulate NULL grad",
          tfp8_accumulate(q, a, s, NULL, TFP8_BF16, 1024, 128, 1.0f, 0u, q, a, s, NULL),
          TFP8_E_NULL);

@@ -112,6 +112,32 @@ def test_reduce_argument_errors(tfp8):
     assert r(None, None, None, 4, 0, 128, 1.0, None, None, None) == 0
 
 
+def test_reduce_strided_argument_errors(tfp8):
+    r = tfp8.reduce_strided_raw
+    n, nb = 1024, 8  # block 128
+    M = 1 << 16  # one message per peer in a receive buffer: [codes | alpha | scale], 64 KiB apart
+    ins = (FAKE, M, FAKE + n, M // 4, FAKE + n + 4 * nb, M // 4)
+    out0 = FAKE + 4 * M  # past the last of 4 messages
+    outs = (out0, out0 + 4096, out0 + 8192)
+    # stride checks: below the row length, codes stride not a multiple of 16, above 2^40
+    assert r(FAKE, n - 16, *ins[2:], 4, n, 128, 1.0, *outs) == -6
+    assert r(*ins[:3], nb - 1, *ins[4:], 4, n, 128, 1.0, *outs) == -6
+    assert r(*ins[:5], nb - 1, 4, n, 128, 1.0, *outs) == -6
+    assert r(FAKE, M + 8, *ins[2:], 4, n, 128, 1.0, *outs) == -5
+    assert r(FAKE, (1 << 40) + 16, *ins[2:], 4, n, 128, 1.0, *outs) == -2
+    assert r(*ins, 0, n, 128, 1.0, *outs) == -6
+    assert r(*ins, 4, n, 96, 1.0, *outs) == -3
+    assert r(*ins, 4, n, 128, 1.0, *outs, flags=4) == -6
+    assert r(None, M, *ins[2:], 4, n, 128, 1.0, *outs) == -1
+    # an output inside the span of the strided inputs, even in a gap between two messages
+    assert r(*ins, 4, n, 128, 1.0, FAKE + M - 4096, outs[1], outs[2]) == -6
+    assert r(*ins, 4, n, 128, 1.0, outs[0], FAKE + 2 * M + 4096, outs[2]) == -6
+    # n = 0 is valid and launches nothing (the GPU tests pass inputs that overlap each other:
+    # alpha and scale inside the codes' span)
+    assert r(*ins, 4, 0, 128, 1.0, *outs) == 0
+    assert r(None, 0, None, 0, None, 0, 4, 0, 128, 1.0, None, None, None) == 0
+
+
 def test_accumulate_argument_errors(tfp8):
     a = tfp8.accumulate_raw
     ins = (FAKE, FAKE + 8192, FAKE + 12288, FAKE + 16384)

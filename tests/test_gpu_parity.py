@@ -201,6 +201,62 @@ def test_reduce_general(oracle, tfp8, P, B):
     _check_reduce(oracle, tfp8, q, a, s, B, what=f"reduce P={P} B={B}")
 
 
+def _messages(parts, n, nb, pad):
+    """One receive buffer holding a [codes | alpha | scale] message per contribution (the
+    oracle's compressed shards), `pad` bytes apart; returns the buffer and [P, ...] row views."""
+    P = len(parts)
+    M = (n + 8 * nb + pad + 15) // 16 * 16
+    host = np.zeros((P, M), np.uint8)
+    for p, (q, a, s) in enumerate(parts):
+        host[p, :n] = q
+        host[p, n:n + 4 * nb] = np.asarray(a, np.float32).view(np.uint8)
+        host[p, n + 4 * nb:n + 8 * nb] = np.asarray(s, np.float32).view(np.uint8)
+    buf = u8_to_gpu(host)
+    return buf, buf[:, :n], buf[:, n:n + 4 * nb].view(torch.float32), \
+        buf[:, n + 4 * nb:n + 8 * nb].view(torch.float32)
+
+
+@pytest.mark.parametrize("B,P,pad,flags", [(128, 8, 0, 0), (64, 3, 65536 + 1024, 0),
+                                           (256, 5, 16, 1), (512, 2, 4096, 0), (128, 1, 0, 0)])
+def test_reduce_strided_packed_messages(oracle, tfp8, B, P, pad, flags):
+    # the P contributions read where one all-to-all would leave them: a [codes | alpha | scale]
+    # message per peer in one buffer (alpha and scale inside the codes' span); against the
+    # oracle's reduce of the same contributions, and bit for bit against the contiguous call
+    nb = 4097 if B < 512 else 1025  # several tiles and a ragged tail
+    n = nb * B
+    parts = [oracle.compress(random_bf16_bits(n, 100 + p, 0.02 * (p + 1)), B, 1.0, flags=flags)
+             for p in range(P)]
+    buf, qv, av, sv = _messages(parts, n, nb, pad)
+    assert not qv.is_contiguous() or P == 1
+    got = tfp8.reduce_fp8(qv, av, sv, B, 1.0, flags=flags)
+    ref_gpu = tfp8.reduce_fp8(u8_to_gpu(np.stack([p[0] for p in parts])),
+                              f32_to_gpu(np.stack([p[1] for p in parts])),
+                              f32_to_gpu(np.stack([p[2] for p in parts])), B, 1.0, flags=flags)
+    torch.cuda.synchronize()
+    for u, v in zip(got, ref_gpu):
+        assert torch.equal(u, v)
+    rq, ra, rs, rt = oracle.reduce_fp8(np.stack([p[0] for p in parts]),
+                                       np.stack([p[1] for p in parts]),
+                                       np.stack([p[2] for p in parts]), B, 1.0, with_quot=True,
+                                       flags=flags)
+    nmis = assert_codes_match(cpu(got[0]), rq, rt, what="strided reduce codes",
+                              int8=bool(flags & 1))
+    assert_scales(cpu(got[1]), cpu(got[2]), ra, rs, what="strided reduce")
+    say(f"  strided reduce B={B} P={P} pad={pad} flags={flags}: tie mismatches {nmis}")
+
+
+def test_reduce_strided_wrapper_checks(tfp8):
+    buf = torch.zeros(4, 4096, dtype=torch.uint8, device=DEV)
+    a = torch.ones(4, 64, dtype=torch.float32, device=DEV)
+    with pytest.raises(ValueError, match="rows"):  # rows not contiguous
+        tfp8.reduce_fp8(buf[:, ::2], a[:, :16], a[:, 16:32], 128)
+    with pytest.raises(ValueError, match=r"\[4, 16\]"):  # scales of the wrong length
+        tfp8.reduce_fp8(buf[:, :2048], a[:, :8], a[:, 16:32], 128)
+    with pytest.raises(tfp8.TFP8Error, match="TFP8_E_ARG"):  # rows that overlap (stride < row)
+        tfp8.reduce_fp8(buf.view(-1)[:8192].as_strided((4, 2048), (1024, 1)), a[:, :16],
+                        a[:, 16:32], 128)
+
+
 def test_reduce_identities(oracle, tfp8):
     B = 128
     x = make_shard(TINY).reshape(-1)
