@@ -723,7 +723,7 @@ __global__ __launch_bounds__(kThreads) void k_accumulate(
           u32x2 w;
           w[0] = encode4<FLAGS>(v[8 * g + 0], v[8 * g + 1], v[8 * g + 2], v[8 * g + 3], cm);
           w[1] = encode4<FLAGS>(v[8 * g + 4], v[8 * g + 5], v[8 * g + 6], v[8 * g + 7], cm);
-          *(u32x2 *)(cb + RS * g) = w;
+          st_stream(w, (u32x2 *)(cb + RS * g));
         }
         if (j == 0) {
           alpha_out[blk] = a_out;
