@@ -245,6 +245,38 @@ def test_reduce_strided_packed_messages(oracle, tfp8, B, P, pad, flags):
     say(f"  strided reduce B={B} P={P} pad={pad} flags={flags}: tie mismatches {nmis}")
 
 
+def test_sharded_two_shot_dataflow_equals_whole_reduce(oracle, tfp8):
+    # The data flow of a two-shot compressed all-reduce over P ranks, on one GPU: each rank's
+    # chunk (a block-aligned 1/P of every contribution) is reduced where it lies, through the
+    # strided call at row stride n, into its slice of one gathered output.  Blocks are
+    # independent, so the gathered result must equal the whole-tensor reduce bit for bit, and
+    # the whole-tensor reduce matches the oracle.
+    P, B = 8, 128
+    n = WORKLOADS[TINY].n
+    nb, c = n // B, n // P
+    cb = c // B
+    xs = np.stack([make_shard(TINY, p).reshape(-1) for p in range(P)])
+    enc = [oracle.compress(x, B, 1.0) for x in xs]
+    q = u8_to_gpu(np.stack([e[0] for e in enc]))
+    a = f32_to_gpu(np.stack([e[1] for e in enc]))
+    s = f32_to_gpu(np.stack([e[2] for e in enc]))
+    whole = tfp8.reduce_fp8(q, a, s, B, 1.0)
+    gq = torch.empty(n, dtype=torch.uint8, device=DEV)
+    ga = torch.empty(nb, dtype=torch.float32, device=DEV)
+    gs = torch.empty(nb, dtype=torch.float32, device=DEV)
+    for r in range(P):
+        tfp8.reduce_fp8(q[:, r * c:(r + 1) * c], a[:, r * cb:(r + 1) * cb], s[:, r * cb:(r + 1) * cb],
+                        B, 1.0, out=(gq[r * c:(r + 1) * c], ga[r * cb:(r + 1) * cb],
+                                     gs[r * cb:(r + 1) * cb]))
+    torch.cuda.synchronize()
+    for u, v in zip((gq, ga, gs), whole):
+        assert torch.equal(u, v)
+    rq, ra, rs, rt = oracle.reduce_fp8(np.stack([e[0] for e in enc]), np.stack([e[1] for e in enc]),
+                                       np.stack([e[2] for e in enc]), B, 1.0, with_quot=True)
+    assert_codes_match(cpu(gq), rq, rt, what="sharded reduce codes")
+    assert_scales(cpu(ga), cpu(gs), ra, rs, what="sharded reduce")
+
+
 def test_reduce_strided_wrapper_checks(tfp8):
     buf = torch.zeros(4, 4096, dtype=torch.uint8, device=DEV)
     a = torch.ones(4, 64, dtype=torch.float32, device=DEV)
