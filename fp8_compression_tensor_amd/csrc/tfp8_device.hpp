@@ -74,12 +74,13 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
-// Unnormalised Walsh-Hadamard transform of the N values a lane holds (natural order),
-// starting at register stride H0 (H0 = 2 when the stride-1 stage was done at load time).
-template <int N, int H0 = 1>
+// Unnormalised Walsh-Hadamard transform of the N values a lane holds (natural order), over
+// register strides H0 <= h < HN: H0 = 2 when the stride-1 stage was done at load time, and
+// HN < N transforms each run of HN registers on its own.
+template <int N, int H0 = 1, int HN = N>
 __device__ __forceinline__ void fwht_registers(float (&v)[N]) {
 #pragma unroll
-  for (int h = H0; h < N; h <<= 1) {
+  for (int h = H0; h < HN; h <<= 1) {
 #pragma unroll
     for (int i = 0; i < N; i += 2 * h) {
 #pragma unroll

@@ -8,15 +8,16 @@
 // requantize).  The pages give no kernel design for this hardware; what follows is laid out
 // for CDNA4 wavefronts.
 //
-// Layout.  A block of B elements is held by a group of L lanes (compress and accumulate:
-// L = 8, or 4 at B = 64 so that a lane still holds 16 elements; decompress: L = 8) or B/16
-// lanes (reduce).  In the L-lane kernels lane j of a group holds B/L elements as runs of 8
-// consecutive elements, run g covering elements [8Lg + 8j, 8Lg + 8j + 8) of the block: each
-// group reads or writes whole runs of 8L consecutive elements.  At L = 8 index bits 0-2 and 6..
-// live in registers, bits 3-5 across the lanes.
+// Layout.  A block of B elements is held by a group of L lanes (compress: L = 8, with a pair
+// of blocks per group at B = 64; accumulate: L = 8, or 4 at B = 64 so that a lane still holds
+// 16 elements; decompress: L = 8) or B/16 lanes (reduce).  In the L-lane kernels lane j of a
+// group holds B/L elements as runs of 8 consecutive elements, run g covering elements
+// [8Lg + 8j, 8Lg + 8j + 8) of the block: each group reads or writes whole runs of 8L
+// consecutive elements.  At L = 8 index bits 0-2 and 6.. live in registers, bits 3-5 across the
+// lanes (at B = 64 in compress, run g is block g of the pair).
 //
 // Launch.  One tile (64/L blocks) per wavefront, 8- or 16-byte vector loads and stores per
-// lane, no LDS, no atomics.  Compress of an input of 1.5 GiB or more (B >= 128) launches
+// lane, no LDS, no atomics.  Compress of an input of 1.5 GiB or more launches
 // one-wavefront workgroups and gives each XCD a contiguous eighth of the tiles
 // (kCompressRemapMinBytes below).
 //
@@ -156,9 +157,9 @@ __device__ __forceinline__ void scales_exact(float (&v)[N], float M, int E0, flo
 }
 
 // --------------------------------------------------------------------------------------------
-// K1: compress.  One wavefront handles a tile of 64 / L blocks (L = 8 lanes per block, 4 at
-// B = 64) per iteration of a grid-stride loop and prefetches the next iteration's input before
-// working on the current one.
+// K1: compress.  One wavefront handles a tile of 8 lane groups (8 blocks, or 16 at B = 64) per
+// iteration of a grid-stride loop and prefetches the next iteration's input before working on
+// the current one.
 
 template <int B, bool F32IN>
 struct CompressIn {
@@ -171,22 +172,21 @@ struct CompressIn {
 // RS = 8 L is the run stride for L lanes per block.
 // The same, from the base of a tile (wave-uniform, so it stays in scalar registers) and a lane's
 // 32-bit element offset into it: the loads then take the scalar base plus a vector offset, and
-// no 64-bit address arithmetic runs per lane.
+// no 64-bit address arithmetic runs per lane.  Run g is read at off + g * step.
 template <int B, bool F32IN>
 __device__ __forceinline__ void load_compress_at(CompressIn<B, F32IN> &in, const void *tile,
-                                                 uint32_t off) {
-  constexpr int RS = 8 * lanes_per_block(B);
+                                                 uint32_t off, uint32_t step) {
   constexpr int G = CompressIn<B, F32IN>::kRuns;
   if constexpr (!F32IN) {
     const uint16_t *xb = (const uint16_t *)tile + off;
 #pragma unroll
-    for (int g = 0; g < G; ++g) in.d[g] = ld_stream((const u32x4 *)(xb + RS * g));
+    for (int g = 0; g < G; ++g) in.d[g] = ld_stream((const u32x4 *)(xb + step * g));
   } else {
     const float *xb = (const float *)tile + off;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      in.d[2 * g] = ld_stream((const u32x4 *)(xb + RS * g));
-      in.d[2 * g + 1] = ld_stream((const u32x4 *)(xb + RS * g + 4));
+      in.d[2 * g] = ld_stream((const u32x4 *)(xb + step * g));
+      in.d[2 * g + 1] = ld_stream((const u32x4 *)(xb + step * g + 4));
     }
   }
 }
@@ -210,6 +210,13 @@ __device__ __forceinline__ void load_compress_in(CompressIn<B, F32IN> &in, const
   }
 }
 
+// Compress keeps 8 lanes per group at every B.  At B = 64 a group holds a pair of adjacent
+// blocks, one per 64-element run (lane j: elements [8 j, 8 j + 8) of each), so that its loads
+// and stores cover whole 128-byte lines exactly as at B = 128; the transform, the statistics and
+// the scales are then taken per run.  (With 4 lanes per block each load instruction read half a
+// line and each store wrote 32 bytes, and compress ran at 67% of HBM peak against 81%.)
+constexpr int compress_blocks_per_group(int B) { return B == 64 ? 2 : 1; }
+
 template <int B, bool F32IN, int FLAGS>
 __global__ __launch_bounds__(kThreads) void k_compress(const void *__restrict__ xin, int64_t nb,
                                                        float TBB, float sqrtTB, float C,
@@ -217,11 +224,14 @@ __global__ __launch_bounds__(kThreads) void k_compress(const void *__restrict__ 
                                                        float *__restrict__ alpha_out,
                                                        float *__restrict__ scale_out, int wpw,
                                                        bool remap) {
-  constexpr int L = lanes_per_block(B);  // lanes per block
-  constexpr int BPW = 64 / L;            // blocks per wavefront (one tile)
-  constexpr int RS = 8 * L;              // run stride
-  constexpr int N = B / L;               // elements per lane
-  constexpr int G = N / 8;               // runs of 8 consecutive elements per lane
+  constexpr int L = 8;                                  // lanes per group
+  constexpr int BG = compress_blocks_per_group(B);      // blocks per group (one per run at 2)
+  constexpr int BPW = 64 / L * BG;                      // blocks per wavefront (one tile)
+  constexpr int RS = 8 * L;                             // run stride
+  constexpr int N = B * BG / L;                         // elements per lane
+  constexpr int G = N / 8;                              // runs of 8 consecutive elements per lane
+  constexpr int NB = N / BG;                            // a block's registers in a lane
+  static_assert(CompressIn<B, F32IN>::kRuns == G, "compress input layout");
   constexpr bool ROT = !(FLAGS & kNoRotation);
   constexpr float Q = qmax_of<FLAGS>();
   const int lane = threadIdx.x & 63;
@@ -235,29 +245,38 @@ __global__ __launch_bounds__(kThreads) void k_compress(const void *__restrict__ 
   // packed bfloat16 (1, 1) and (1, -1), kept in registers for v_dot2_f32_bf16
   const uint32_t ones = 0x3F803F80u, plus_minus = 0xBF803F80u;
 
-  // Tile t covers blocks [t BPW, t BPW + BPW); the group bw of its lanes takes block t BPW + bw.
-  // Groups past the last block (ragged last tile) read the last block again and store
-  // nothing, so every load is in bounds and every register holds data.
+  // Tile t covers blocks [t BPW, t BPW + BPW); group bw of its lanes takes blocks
+  // t BPW + BG bw + b, b < BG.  A block past the last one (ragged last tile) is read as the last
+  // block instead and stores nothing, so every load is in bounds and every register holds data.
   constexpr int ES = F32IN ? 4 : 2;  // input element size
   auto tile_in = [&](int64_t t) { return (const char *)xin + t * (BPW * B * ES); };
   auto lane_in = [&](int64_t t) {
     const int64_t last = nb - 1 - t * BPW;  // last block relative to the tile (>= 0)
-    return (uint32_t)((last < bw ? (int)last : bw) * B + 8 * j);
+    const int b0 = BG * bw;
+    return (uint32_t)((last < b0 ? (int)last : b0) * B + 8 * j);
+  };
+  // element step from one run to the next: RS within a block; at BG = 2 the next run is the
+  // pair's second block, or the first one again when the second is past the end
+  auto run_step = [&](int64_t t) -> uint32_t {
+    if constexpr (BG == 1) return RS;
+    return (nb - 1 - t * BPW) > BG * bw ? (uint32_t)B : 0u;
   };
   CompressIn<B, F32IN> cur;
-  if (wave < ntiles) load_compress_at<B, F32IN>(cur, tile_in(wave), lane_in(wave));
+  if (wave < ntiles) load_compress_at<B, F32IN>(cur, tile_in(wave), lane_in(wave), run_step(wave));
 
   for (int64_t tile = wave; tile < ntiles; tile += nwaves) {
     const int64_t blk0 = tile * BPW;  // first block of the tile (wave-uniform)
-    const bool active = blk0 + bw < nb;
     CompressIn<B, F32IN> nxt;
     if (tile + nwaves < ntiles)
-      load_compress_at<B, F32IN>(nxt, tile_in(tile + nwaves), lane_in(tile + nwaves));
+      load_compress_at<B, F32IN>(nxt, tile_in(tile + nwaves), lane_in(tile + nwaves),
+                                 run_step(tile + nwaves));
 
-    // Widen, energy and the first butterfly stages.  Groups past the last block work on a
-    // copy of the last block and store nothing.
+    // Widen, energy and the first butterfly stages.  Blocks past the last one work on a copy
+    // of the last block and store nothing.
     float v[N];
-    float ss = 0.0f;
+    float ss[BG];
+#pragma unroll
+    for (int b = 0; b < BG; ++b) ss[b] = 0.0f;
     if constexpr (!F32IN) {
 #pragma unroll
       for (int g = 0; g < G; ++g) {
@@ -269,9 +288,10 @@ __global__ __launch_bounds__(kThreads) void k_compress(const void *__restrict__ 
           for (int q = 0; q < 4; ++q) widen_bf16x2(d[q], v[8 * g + 2 * q], v[8 * g + 2 * q + 1]);
         }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) ss = bf16_pair_sumsq(d[q], ss);
+        for (int q = 0; q < 4; ++q) ss[g * BG / G] = bf16_pair_sumsq(d[q], ss[g * BG / G]);
       }
-      if constexpr (ROT) fwht_registers<N, 2>(v);
+      // register stages within a block: all of them at BG = 1, those inside a run at BG = 2
+      if constexpr (ROT) fwht_registers<N, 2, NB>(v);
     } else {
 #pragma unroll
       for (int g = 0; g < G; ++g)
@@ -281,48 +301,58 @@ __global__ __launch_bounds__(kThreads) void k_compress(const void *__restrict__ 
           v[8 * g + 4 + q] = __uint_as_float(cur.d[2 * g + 1][q]);
         }
 #pragma unroll
-      for (int r = 0; r < N; ++r) ss = fmaf(v[r], v[r], ss);
-      if constexpr (ROT) fwht_registers<N, 1>(v);
+      for (int r = 0; r < N; ++r) ss[r / NB] = fmaf(v[r], v[r], ss[r / NB]);
+      if constexpr (ROT) fwht_registers<N, 1, NB>(v);
     }
     // orthogonal Hadamard rotation, unnormalised: w = H x (1/sqrt(B) and alpha live in s)
     if constexpr (ROT) fwht_lanes<L, N>(v, j);
 
-    float m = 0.0f;
 #pragma unroll
-    for (int r = 0; r < N; ++r) m = fmaxf(m, fabsf(v[r]));
-    const float M = group_max<L>(m);
-    const float SS = group_sum<L>(ss);  // sum(x^2) of the block
-
-    // alpha = sqrt(T B / sum x^2), s = alpha max|w| / (Q sqrt B), codes = code(Q w / max|w|)
-    // (Q = 448 for E4M3; without the rotation w = x and s = alpha max|x| / Q).
-    // For max|w| in [2^-40, 2^60] every quantity stays normal and sum(x^2) is accurate, so the
-    // scales use the single-instruction reciprocal square root (1 ulp, inside the 1e-6 bar);
-    // the code multiplier Q / max|w| is correctly rounded, so that a quotient that is exactly
-    // a rounding midpoint stays exact and rounds to even.  Other blocks (all-zero,
-    // bfloat16-subnormal, huge) take the range-safe path.
-    float cm, alpha, s;
-    if (M >= 0x1p-40f && M <= 0x1p60f) {
-      const float c = __fdiv_rn(Q, M);
-      alpha = fminf(fmaxf(sqrtTB * __builtin_amdgcn_rsqf(SS), 0x1p-126f), 0x1p126f);
-      s = alpha * M * invC;
-      cm = c * sj;
-    } else {
-      scales_exact<L, N>(v, M, 0, TBB, Q, C, sj, cm, alpha, s);
-    }
-
-    if (active) {
-      uint8_t *cb = codes + blk0 * B;         // the tile's codes (wave-uniform)
-      const uint32_t co = bw * B + 8 * pj;    // this lane's runs within them
+    for (int b = 0; b < BG; ++b) {
+      // this block's registers: v[b NB + r], r < NB
+      float m = 0.0f;
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        u32x2 w;
-        w[0] = encode4<FLAGS>(v[8 * g + 0], v[8 * g + 1], v[8 * g + 2], v[8 * g + 3], cm);
-        w[1] = encode4<FLAGS>(v[8 * g + 4], v[8 * g + 5], v[8 * g + 6], v[8 * g + 7], cm);
-        st_stream(w, (u32x2 *)(cb + co + RS * g));
+      for (int r = 0; r < NB; ++r) m = fmaxf(m, fabsf(v[b * NB + r]));
+      const float M = group_max<L>(m);
+      const float SS = group_sum<L>(ss[b]);  // sum(x^2) of the block
+
+      // alpha = sqrt(T B / sum x^2), s = alpha max|w| / (Q sqrt B), codes = code(Q w / max|w|)
+      // (Q = 448 for E4M3; without the rotation w = x and s = alpha max|x| / Q).
+      // For max|w| in [2^-40, 2^60] every quantity stays normal and sum(x^2) is accurate, so
+      // the scales use the single-instruction reciprocal square root (1 ulp, inside the 1e-6
+      // bar); the code multiplier Q / max|w| is correctly rounded, so that a quotient that is
+      // exactly a rounding midpoint stays exact and rounds to even.  Other blocks (all-zero,
+      // bfloat16-subnormal, huge) take the range-safe path.
+      float cm, alpha, s;
+      if (M >= 0x1p-40f && M <= 0x1p60f) {
+        const float c = __fdiv_rn(Q, M);
+        alpha = fminf(fmaxf(sqrtTB * __builtin_amdgcn_rsqf(SS), 0x1p-126f), 0x1p126f);
+        s = alpha * M * invC;
+        cm = c * sj;
+      } else {
+        float h[NB];
+#pragma unroll
+        for (int r = 0; r < NB; ++r) h[r] = v[b * NB + r];
+        scales_exact<L, NB>(h, M, 0, TBB, Q, C, sj, cm, alpha, s);
+#pragma unroll
+        for (int r = 0; r < NB; ++r) v[b * NB + r] = h[r];
       }
-      if (j == 0) {
-        alpha_out[blk0 + bw] = alpha;
-        scale_out[blk0 + bw] = s;
+
+      const int64_t blk = blk0 + BG * bw + b;
+      if (blk < nb) {
+        uint8_t *cb = codes + blk0 * B;            // the tile's codes (wave-uniform)
+        const uint32_t co = BG * bw * B + 8 * pj;  // this lane's runs within them
+#pragma unroll
+        for (int g = b * G / BG; g < (b + 1) * G / BG; ++g) {
+          u32x2 w;
+          w[0] = encode4<FLAGS>(v[8 * g + 0], v[8 * g + 1], v[8 * g + 2], v[8 * g + 3], cm);
+          w[1] = encode4<FLAGS>(v[8 * g + 4], v[8 * g + 5], v[8 * g + 6], v[8 * g + 7], cm);
+          st_stream(w, (u32x2 *)(cb + co + RS * g));
+        }
+        if (j == 0) {
+          alpha_out[blk] = alpha;
+          scale_out[blk] = s;
+        }
       }
     }
     cur = nxt;
@@ -951,8 +981,9 @@ int cu_count() {
 // Compress of a large input is 2-4% faster with 64-thread workgroups and each XCD on a
 // contiguous eighth of the tiles: 77% -> 80% of HBM peak for every bf16 input measured from
 // 1.9 to 4.3 GB.  At 1.1 GB the two shapes tie, and on inputs of 134-268 MB the remapped one is
-// 3-10% slower, hence the threshold.  At B = 64 (4 lanes per block) the remapped shape was 3%
-// slower on 1.9 GB.  Decompress and the reduce were slower remapped.
+// 3-10% slower, hence the threshold.  At B = 64, whose lane groups now read whole lines as at
+// B = 128, the remapped shape is 1% faster on 1.9 GB.  Decompress and the reduce were slower
+// remapped.
 constexpr int64_t kCompressRemapMinBytes = (int64_t)3 << 29;  // 1.5 GiB of input
 
 // The cap without `per_cu` keeps gridDim.x * nt (the work-items of the launch, a 32-bit count
@@ -995,10 +1026,10 @@ tfp8_status launch_compress_t(const void *x, int64_t nb, float target, uint8_t *
   const float sqrtTB = (float)sqrt((double)target * B);
   const double Cd = ROT ? Q * sqrt((double)B) : Q;
   const float C = (float)Cd, invC = (float)(1.0 / Cd);
-  constexpr int BPW = 64 / lanes_per_block(B);  // blocks per tile
+  constexpr int BPW = 64 / 8 * compress_blocks_per_group(B);  // blocks per tile
   // Large inputs stream faster with one wavefront per workgroup and each XCD on a contiguous
   // eighth of the tiles; smaller ones with 4 wavefronts per workgroup in dispatch order.
-  const bool remap = B >= 128 && nb * B * (F32 ? 4 : 2) >= kCompressRemapMinBytes;
+  const bool remap = nb * B * (F32 ? 4 : 2) >= kCompressRemapMinBytes;
   const int nt = remap ? 64 : kThreads;
   const unsigned grid = grid_for((nb + BPW - 1) / BPW, TFP8_COMPRESS_WGS_PER_CU, nt, remap);
   return launch(k_compress<B, F32, FLAGS>, grid, nt, st, x, nb, TBB, sqrtTB, C, invC, codes,

@@ -648,16 +648,19 @@ def test_accumulate_zero_main_gradient_equals_compress(oracle, tfp8):
     check_compress(oracle, tfp8, g, B, what="compress of the same gradient")
 
 
-@pytest.mark.parametrize("dtype,extra_blocks", [("bf16", -3), ("bf16", 13), ("f32", 5)])
-def test_compress_both_launch_shapes(oracle, tfp8, dtype, extra_blocks):
+@pytest.mark.parametrize("dtype,B,extra_blocks", [("bf16", 128, -3), ("bf16", 128, 13),
+                                                  ("f32", 128, 5), ("bf16", 64, -3),
+                                                  ("bf16", 64, 13), ("f32", 64, 5)])
+def test_compress_both_launch_shapes(oracle, tfp8, dtype, B, extra_blocks):
     # Compress picks its launch shape by input size: below 1.5 GiB four wavefronts per
     # workgroup in dispatch order, from 1.5 GiB one wavefront per workgroup with each XCD on a
     # contiguous eighth of the tiles (grid rounded up to a multiple of 8).  Inputs just below
     # and above the switch, each with a ragged last tile (block count not a multiple of 8).  The
     # input is one random tile of 2^20 elements in seven power-of-two scalings, so a block read
     # from the wrong place shows.  Sampled blocks: both ends, the start of each eighth of the
-    # tiles, and 2048 random blocks.
-    B, T, tile = 128, 1.0, 1 << 20
+    # tiles, and 2048 random blocks.  At B = 64 a tile is 16 blocks, a pair per lane group, and
+    # an odd block count leaves the last pair with one block.
+    T, tile = 1.0, 1 << 20
     esize = 2 if dtype == "bf16" else 4
     nb = (3 << 29) // esize // B + extra_blocks
     n = nb * B
@@ -669,8 +672,9 @@ def test_compress_both_launch_shapes(oracle, tfp8, dtype, extra_blocks):
     for t in range(-(-n // tile)):
         seg = x[t * tile:(t + 1) * tile]
         seg[:] = scaled[t % 7][:seg.size]
-    ntiles = -(-nb // 8)
-    eighths = np.array([(k * -(-ntiles // 8)) * 8 for k in range(8)])
+    bpt = 16 if B == 64 else 8  # blocks per tile
+    ntiles = -(-nb // bpt)
+    eighths = np.array([(k * -(-ntiles // 8)) * bpt for k in range(8)])
     rng = np.random.default_rng(1536)
     idx = np.unique(np.concatenate([np.arange(64), np.arange(nb - 64, nb),
                                     (eighths[:, None] + np.arange(-8, 8)).reshape(-1) % nb,
@@ -686,8 +690,9 @@ def test_compress_both_launch_shapes(oracle, tfp8, dtype, extra_blocks):
     del x
     rq, ra, rs, rt = oracle.compress(xs, B, T, with_quot=True)
     nmis = assert_codes_match(cpu(q.view(nb, B)[idx_g]).reshape(-1), rq, rt,
-                              what=f"launch shapes {dtype} {nb} blocks")
-    assert_scales(cpu(a[idx_g]), cpu(s[idx_g]), ra, rs, what=f"launch shapes {dtype} {nb} blocks")
+                              what=f"launch shapes {dtype} B={B} {nb} blocks")
+    assert_scales(cpu(a[idx_g]), cpu(s[idx_g]), ra, rs,
+                  what=f"launch shapes {dtype} B={B} {nb} blocks")
     say(f"  launch shapes: tie mismatches {nmis}")
 
 
