@@ -74,6 +74,29 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// Sum of the squares of the N values a lane holds of one block.  From N = 32 on (B >= 256) the
+// squares go into 8 partial sums added pairwise at the end, so that the float32 rounding error
+// grows with N / 8 + 3 terms instead of N: a sequential sum of 64 similar squares (B = 512) was
+// measured to miss the 1e-6 bar on alpha.  Shorter sums stay sequential (fewer registers).
+// With SCALED, the squares are those of v[r] * c (each product rounded to float32 first).
+template <int N, bool SCALED = false>
+__device__ __forceinline__ float sum_squares(const float *v, float c = 1.0f) {
+  constexpr int K = N < 32 ? 1 : 8;
+  float p[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) p[k] = 0.0f;
+#pragma unroll
+  for (int r = 0; r < N; ++r) {
+    const float u = SCALED ? v[r] * c : v[r];
+    p[r % K] = fmaf(u, u, p[r % K]);
+  }
+  if constexpr (K == 1) {
+    return p[0];
+  } else {
+    return ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+  }
+}
+
 // Unnormalised Walsh-Hadamard transform of the N values a lane holds (natural order), over
 // register strides H0 <= h < HN: H0 = 2 when the stride-1 stage was done at load time, and
 // HN < N transforms each run of HN registers on its own.

@@ -141,13 +141,7 @@ __device__ __forceinline__ void scales_exact(float (&v)[N], float M, int E0, flo
   const bool zero = (M == 0.0f);
   const float c = zero ? 0.0f : __fdiv_rn(Q, M);
   // energy from the codes' values u = v c: sum(u^2) = c^2 sum(v^2) stays in float32 range
-  float su = 0.0f;
-#pragma unroll
-  for (int r = 0; r < N; ++r) {
-    const float u = v[r] * c;
-    su = fmaf(u, u, su);
-  }
-  const float SU = group_sum<L>(su);
+  const float SU = group_sum<L>(sum_squares<N, true>(v, c));
   const float a2 = c * __fsqrt_rn(__fdiv_rn(TBB, SU));
   const float alpha = fminf(fmaxf(scale2(a2, -E), 0x1p-126f), 0x1p126f);
   const float s = __fdiv_rn(scale2(alpha, E) * M, C);
@@ -274,10 +268,17 @@ __global__ __launch_bounds__(kThreads) void k_compress(const void *__restrict__ 
     // Widen, energy and the first butterfly stages.  Blocks past the last one work on a copy
     // of the last block and store nothing.
     float v[N];
-    float ss[BG];
-#pragma unroll
-    for (int b = 0; b < BG; ++b) ss[b] = 0.0f;
+    float ss[BG];  // sum(x^2) of each block's values in this lane
     if constexpr (!F32IN) {
+      // sums of squares from the packed input: from 32 values per lane and block on (B >= 256)
+      // four partial sums, one per dword of a run, added pairwise at the end, so that the
+      // rounding error grows with the runs rather than the values (see sum_squares)
+      constexpr int KQ = NB >= 32 ? 4 : 1;
+      float ssq[BG][KQ];
+#pragma unroll
+      for (int b = 0; b < BG; ++b)
+#pragma unroll
+        for (int k = 0; k < KQ; ++k) ssq[b][k] = 0.0f;
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         const u32x4 d = cur.d[g];
@@ -288,7 +289,15 @@ __global__ __launch_bounds__(kThreads) void k_compress(const void *__restrict__ 
           for (int q = 0; q < 4; ++q) widen_bf16x2(d[q], v[8 * g + 2 * q], v[8 * g + 2 * q + 1]);
         }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) ss[g * BG / G] = bf16_pair_sumsq(d[q], ss[g * BG / G]);
+        for (int q = 0; q < 4; ++q)
+          ssq[g * BG / G][q % KQ] = bf16_pair_sumsq(d[q], ssq[g * BG / G][q % KQ]);
+      }
+#pragma unroll
+      for (int b = 0; b < BG; ++b) {
+        if constexpr (KQ == 4)
+          ss[b] = (ssq[b][0] + ssq[b][1]) + (ssq[b][2] + ssq[b][3]);
+        else
+          ss[b] = ssq[b][0];
       }
       // register stages within a block: all of them at BG = 1, those inside a run at BG = 2
       if constexpr (ROT) fwht_registers<N, 2, NB>(v);
@@ -301,7 +310,7 @@ __global__ __launch_bounds__(kThreads) void k_compress(const void *__restrict__ 
           v[8 * g + 4 + q] = __uint_as_float(cur.d[2 * g + 1][q]);
         }
 #pragma unroll
-      for (int r = 0; r < N; ++r) ss[r / NB] = fmaf(v[r], v[r], ss[r / NB]);
+      for (int b = 0; b < BG; ++b) ss[b] = sum_squares<NB>(&v[b * NB]);
       if constexpr (ROT) fwht_registers<N, 1, NB>(v);
     }
     // orthogonal Hadamard rotation, unnormalised: w = H x (1/sqrt(B) and alpha live in s)
@@ -732,10 +741,7 @@ __global__ __launch_bounds__(kThreads) void k_accumulate(
         // energy of z from w (Parseval): alpha = sqrt(T B^2 / sum w^2); with M in this range
         // the sum of squares stays within float32 (at most B M^2 <= 2^121), and squares that
         // underflow are below 2^-70 of the largest
-        float sw = 0.0f;
-#pragma unroll
-        for (int r = 0; r < N; ++r) sw = fmaf(v[r], v[r], sw);
-        const float SW = group_sum<L>(sw);
+        const float SW = group_sum<L>(sum_squares<N>(v));
         const float c = __fdiv_rn(Q, M);
         a_out = fminf(fmaxf(sqrtTBB * __builtin_amdgcn_rsqf(SW), 0x1p-126f), 0x1p126f);
         s_out = a_out * M * invC;
