@@ -152,7 +152,8 @@ def test_target_values(oracle, tfp8, T):
     _check_accumulate(oracle, tfp8, q, a, s, xr[1], 128, f"accumulate T={T}", T=T)
 
 
-def test_hardware_e4m3_conversion_every_fp32_value(oracle, tfp8):
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_hardware_e4m3_conversion_every_fp32_value(oracle, tfp8, dtype):
     # The kernels' FP8 encode, checked exhaustively through compress: without the rotation a
     # block whose largest magnitude is exactly 448 has code multiplier 448 / 448 = 1, so every
     # other element's code is the conversion of that exact float32 value (the oracle's quotient
@@ -160,9 +161,11 @@ def test_hardware_e4m3_conversion_every_fp32_value(oracle, tfp8):
     # [2^-12, 448], both signs, 511 per block of 512 after a leading 448: round to nearest
     # even at every midpoint, the subnormal grid, rounding to +-0 and the top of the range.
     # No tie allowance: the codes must be identical.
+    # With bfloat16 input, every bfloat16 value in the same range (the widening path).
     B = 512
     lo, hi = np.float32(2.0 ** -12).view(np.uint32), np.float32(448.0).view(np.uint32)
-    pos = np.arange(lo, hi + 1, dtype=np.uint32).view(np.float32)
+    step = 1 if dtype == "f32" else 1 << 16
+    pos = np.arange(lo, hi + 1, step, dtype=np.uint32).view(np.float32)
     vals = np.concatenate([pos, -pos])
     nb = -(-vals.size // (B - 1))
     x = np.ones((nb, B), np.float32)
@@ -172,11 +175,12 @@ def test_hardware_e4m3_conversion_every_fp32_value(oracle, tfp8):
     x[:, 1:] = body.reshape(nb, B - 1)
     x = x.reshape(-1)
     del pos, vals, body
-    say(f"  every float32 in [2^-12, 448], both signs: {x.size} elements, {nb} blocks")
-    q, a, s = tfp8.compress(f32_to_gpu(x), B, 1.0, flags=2)
+    say(f"  every {dtype} value in [2^-12, 448], both signs: {x.size} elements, {nb} blocks")
+    xin = x if dtype == "f32" else f32_to_bf16_bits(x)  # exact: every value is a bfloat16
+    q, a, s = tfp8.compress(f32_to_gpu(x) if dtype == "f32" else bits_to_gpu(xin), B, 1.0, flags=2)
     torch.cuda.synchronize()
     q, a, s = cpu(q), cpu(a), cpu(s)
-    qr, ar, sr = oracle.compress(x, B, 1.0, flags=2)
+    qr, ar, sr = oracle.compress(xin, B, 1.0, flags=2)
     bad = np.nonzero(q != qr)[0]
     assert bad.size == 0, (f"{bad.size} codes differ; first at value {x[bad[0]]!r}: "
                            f"got {q[bad[0]]:#04x}, oracle {qr[bad[0]]:#04x}")
