@@ -152,40 +152,44 @@ def test_target_values(oracle, tfp8, T):
     _check_accumulate(oracle, tfp8, q, a, s, xr[1], 128, f"accumulate T={T}", T=T)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_hardware_e4m3_conversion_every_fp32_value(oracle, tfp8, dtype):
-    # The kernels' FP8 encode, checked exhaustively through compress: without the rotation a
-    # block whose largest magnitude is exactly 448 has code multiplier 448 / 448 = 1, so every
-    # other element's code is the conversion of that exact float32 value (the oracle's quotient
-    # y / s is the same value exactly).  Every float32 bit pattern with magnitude in
-    # [2^-12, 448], both signs, 511 per block of 512 after a leading 448: round to nearest
-    # even at every midpoint, the subnormal grid, rounding to +-0 and the top of the range.
-    # No tie allowance: the codes must be identical.
-    # With bfloat16 input, every bfloat16 value in the same range (the widening path).
+@pytest.mark.parametrize("dtype,flags", [("f32", 2), ("bf16", 2), ("f32", 3)])
+def test_hardware_conversion_every_fp32_value(oracle, tfp8, dtype, flags):
+    # The kernels' code conversion, checked exhaustively through compress: without the rotation
+    # a block whose largest magnitude is exactly Q_max has code multiplier Q_max / Q_max = 1, so
+    # every other element's code is the conversion of that exact input value (the oracle's
+    # quotient y / s is the same value exactly).  E4M3 (flags 2): every float32 bit pattern with
+    # magnitude in [2^-12, 448], both signs, 511 per block of 512 after a leading 448 -- round to
+    # nearest even at every midpoint, the subnormal grid, rounding to +-0 and the top of the
+    # range; with bfloat16 input, every bfloat16 value in that range (the widening path).  INT8
+    # (flags 3): every float32 in [2^-3, 127] after a leading 127 -- the rounding to integers,
+    # ties to even, and the byte packing.  No tie allowance: the codes must be identical.
     B = 512
-    lo, hi = np.float32(2.0 ** -12).view(np.uint32), np.float32(448.0).view(np.uint32)
+    qmax, low = (127.0, 2.0 ** -3) if flags & 1 else (448.0, 2.0 ** -12)
+    lo, hi = np.float32(low).view(np.uint32), np.float32(qmax).view(np.uint32)
     step = 1 if dtype == "f32" else 1 << 16
     pos = np.arange(lo, hi + 1, step, dtype=np.uint32).view(np.float32)
     vals = np.concatenate([pos, -pos])
     nb = -(-vals.size // (B - 1))
     x = np.ones((nb, B), np.float32)
-    x[:, 0] = 448.0
+    x[:, 0] = qmax
     body = x[:, 1:].reshape(-1)
     body[:vals.size] = vals
     x[:, 1:] = body.reshape(nb, B - 1)
     x = x.reshape(-1)
     del pos, vals, body
-    say(f"  every {dtype} value in [2^-12, 448], both signs: {x.size} elements, {nb} blocks")
+    say(f"  every {dtype} value in [{low}, {qmax}], both signs, flags {flags}: {x.size} elements, "
+        f"{nb} blocks")
     xin = x if dtype == "f32" else f32_to_bf16_bits(x)  # exact: every value is a bfloat16
-    q, a, s = tfp8.compress(f32_to_gpu(x) if dtype == "f32" else bits_to_gpu(xin), B, 1.0, flags=2)
+    q, a, s = tfp8.compress(f32_to_gpu(x) if dtype == "f32" else bits_to_gpu(xin), B, 1.0,
+                            flags=flags)
     torch.cuda.synchronize()
     q, a, s = cpu(q), cpu(a), cpu(s)
-    qr, ar, sr = oracle.compress(xin, B, 1.0, flags=2)
+    qr, ar, sr = oracle.compress(xin, B, 1.0, flags=flags)
     bad = np.nonzero(q != qr)[0]
     assert bad.size == 0, (f"{bad.size} codes differ; first at value {x[bad[0]]!r}: "
                            f"got {q[bad[0]]:#04x}, oracle {qr[bad[0]]:#04x}")
-    assert_scales(a, s, ar, sr, what="every-float32 blocks")
-    assert np.all(q.reshape(nb, B)[:, 0] == 0x7E)
+    assert_scales(a, s, ar, sr, what="every-value blocks")
+    assert np.all(q.reshape(nb, B)[:, 0] == (0x7F if flags & 1 else 0x7E))
 
 
 def test_constructed_exact_ties(oracle, tfp8):
