@@ -13,7 +13,8 @@ import pytest
 import torch
 
 from gpu_helpers import (DEV, assert_bf16_match, assert_scales, bits_to_gpu, check_compress,
-                         check_decompress, check_reduce, cpu, f32_to_gpu, say, u8_to_gpu)
+                         check_decompress, check_reduce, cpu, f32_to_gpu, gpu_bf16_bits, say,
+                         u8_to_gpu)
 from tiecheck import assert_codes_match, assert_rel_close
 from workloads import (GPT2_7B, GPT6_7B, GPT13B_GRAD, QWEN7B, TINY, WORKLOADS, bf16_bits_to_f32,
                        f32_to_bf16_bits, make_shard, make_shards, random_bf16_bits)
@@ -190,6 +191,35 @@ def test_hardware_conversion_every_fp32_value(oracle, tfp8, dtype, flags):
                            f"got {q[bad[0]]:#04x}, oracle {qr[bad[0]]:#04x}")
     assert_scales(a, s, ar, sr, what="every-value blocks")
     assert np.all(q.reshape(nb, B)[:, 0] == (0x7F if flags & 1 else 0x7E))
+
+
+@pytest.mark.parametrize("flags", [2, 3])
+def test_hardware_decode_every_code(oracle, tfp8, flags):
+    # The kernels' code decoding, checked exhaustively through decompress: without the rotation
+    # and with alpha = s = 1 the output is the code's value itself.  Every E4M3 code but the two
+    # NaNs (flags 2), or every INT8 code (flags 3), at every position of a block, in float32 and
+    # bfloat16 (every code value is a bfloat16), identical to the oracle's.
+    B = 256
+    codes = np.arange(256, dtype=np.uint8)
+    if not flags & 1:
+        codes = codes[(codes & 0x7F) != 0x7F]  # 0x7F and 0xFF are NaN
+    nb = B  # block k holds the codes rotated by k, so each code meets every position
+    q = np.stack([np.roll(np.resize(codes, B), k) for k in range(nb)]).reshape(-1)
+    a = np.ones(nb, np.float32)
+    s = np.ones(nb, np.float32)
+    qg, ag, sg = u8_to_gpu(q), f32_to_gpu(a), f32_to_gpu(s)
+    o32 = cpu(tfp8.decompress(qg, ag, sg, B, torch.float32, flags=flags))
+    o16 = gpu_bf16_bits(tfp8.decompress(qg, ag, sg, B, torch.bfloat16, flags=flags))
+    r32 = oracle.decompress(q, a, s, B, np.float32, flags=flags)
+    r16 = oracle.decompress(q, a, s, B, np.uint16, flags=flags)
+    # values identical; the bit patterns may differ only in the sign of a zero (code 0x80 is -0,
+    # and the bar compares values, where +0 == -0)
+    for got, ref in ((o32, r32), (bf16_bits_to_f32(o16), bf16_bits_to_f32(r16))):
+        assert np.array_equal(got, ref)
+        diff = np.nonzero(got.view(np.uint32) != ref.view(np.uint32))[0]
+        assert np.all(ref[diff] == 0), ref[diff][:8]
+        say(f"  decode flags {flags}: {got.size} values identical, {diff.size} zeros of the "
+            f"other sign")
 
 
 def test_constructed_exact_ties(oracle, tfp8):
