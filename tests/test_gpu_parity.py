@@ -153,6 +153,22 @@ def test_target_values(oracle, tfp8, T):
     _check_accumulate(oracle, tfp8, q, a, s, xr[1], 128, f"accumulate T={T}", T=T)
 
 
+def _every_value_blocks(dtype, qmax, low, B):
+    """Every float32 (or bfloat16) value with magnitude in [low, qmax], both signs, 511 per block
+    of B = 512 after a leading qmax; the tail is padded with 1.0."""
+    lo, hi = np.float32(low).view(np.uint32), np.float32(qmax).view(np.uint32)
+    step = 1 if dtype == "f32" else 1 << 16
+    pos = np.arange(lo, hi + 1, step, dtype=np.uint32).view(np.float32)
+    vals = np.concatenate([pos, -pos])
+    nb = -(-vals.size // (B - 1))
+    x = np.ones((nb, B), np.float32)
+    x[:, 0] = qmax
+    body = x[:, 1:].reshape(-1)
+    body[:vals.size] = vals
+    x[:, 1:] = body.reshape(nb, B - 1)
+    return x.reshape(-1), nb
+
+
 @pytest.mark.parametrize("dtype,flags", [("f32", 2), ("bf16", 2), ("f32", 3)])
 def test_hardware_conversion_every_fp32_value(oracle, tfp8, dtype, flags):
     # The kernels' code conversion, checked exhaustively through compress: without the rotation
@@ -166,18 +182,7 @@ def test_hardware_conversion_every_fp32_value(oracle, tfp8, dtype, flags):
     # ties to even, and the byte packing.  No tie allowance: the codes must be identical.
     B = 512
     qmax, low = (127.0, 2.0 ** -3) if flags & 1 else (448.0, 2.0 ** -12)
-    lo, hi = np.float32(low).view(np.uint32), np.float32(qmax).view(np.uint32)
-    step = 1 if dtype == "f32" else 1 << 16
-    pos = np.arange(lo, hi + 1, step, dtype=np.uint32).view(np.float32)
-    vals = np.concatenate([pos, -pos])
-    nb = -(-vals.size // (B - 1))
-    x = np.ones((nb, B), np.float32)
-    x[:, 0] = qmax
-    body = x[:, 1:].reshape(-1)
-    body[:vals.size] = vals
-    x[:, 1:] = body.reshape(nb, B - 1)
-    x = x.reshape(-1)
-    del pos, vals, body
+    x, nb = _every_value_blocks(dtype, qmax, low, B)
     say(f"  every {dtype} value in [{low}, {qmax}], both signs, flags {flags}: {x.size} elements, "
         f"{nb} blocks")
     xin = x if dtype == "f32" else f32_to_bf16_bits(x)  # exact: every value is a bfloat16
@@ -191,6 +196,30 @@ def test_hardware_conversion_every_fp32_value(oracle, tfp8, dtype, flags):
                            f"got {q[bad[0]]:#04x}, oracle {qr[bad[0]]:#04x}")
     assert_scales(a, s, ar, sr, what="every-value blocks")
     assert np.all(q.reshape(nb, B)[:, 0] == (0x7F if flags & 1 else 0x7E))
+
+
+def test_accumulate_every_fp32_value_onto_zero_main(oracle, tfp8):
+    # The every-float32 blocks (magnitudes in [2^-12, 448], 64 similar values per lane at
+    # B = 512) as the local gradient added to an all-zero compressed main gradient, without the
+    # rotation: the accumulate's own sum of squares and scales on blocks where a sequential
+    # float32 sum misses the alpha bar.  Codes identical to the oracle's (the quotients are the
+    # inputs exactly), alpha and s within 1e-6.
+    B = 512
+    g, nb = _every_value_blocks("f32", 448.0, 2.0 ** -12, B)
+    n = g.size
+    q0 = np.zeros(n, np.uint8)
+    a0 = np.ones(nb, np.float32)
+    s0 = np.zeros(nb, np.float32)
+    say(f"  accumulate onto zero: {n} elements, {nb} blocks")
+    q, a, s = tfp8.accumulate(u8_to_gpu(q0), f32_to_gpu(a0), f32_to_gpu(s0), f32_to_gpu(g), B, 1.0,
+                              flags=2)
+    torch.cuda.synchronize()
+    q, a, s = cpu(q), cpu(a), cpu(s)
+    qr, ar, sr = oracle.accumulate(q0, a0, s0, g, B, 1.0, flags=2)
+    bad = np.nonzero(q != qr)[0]
+    assert bad.size == 0, (f"{bad.size} codes differ; first at value {g[bad[0]]!r}: "
+                           f"got {q[bad[0]]:#04x}, oracle {qr[bad[0]]:#04x}")
+    assert_scales(a, s, ar, sr, what="accumulate every-value blocks")
 
 
 @pytest.mark.parametrize("flags", [2, 3])
