@@ -906,6 +906,73 @@ def test_offsets_beyond_2_31_elements(oracle, tfp8):
     assert_scales(cpu(ag[idx_g]), cpu(sg[idx_g]), ra, rs, what="offsets accumulate")
 
 
+def test_grid_stride_loops_beyond_2_34_elements(oracle, tfp8):
+    # A launch covers at most 2^30 work-items: from 2^34 elements on (B = 128) the wavefronts of
+    # compress, decompress and accumulate loop over tiles, loading the next tile before working
+    # on the current one.  n = 4097 * 2^22 - 37 * 128 elements (34 GB of bfloat16, a ragged last
+    # tile), built on the GPU from one random tile of 2^22 elements in seven power-of-two
+    # scalings (tile t scaled by 2^((t mod 7) - 3)), so that a block read from the wrong place
+    # shows.  Expected values come from the host copies of the seven variants, never from the
+    # GPU.  Sampled blocks: both ends, the first loop iteration's first blocks (block 2^27),
+    # the blocks around element 2^31 and 2048 random blocks.
+    B, T, tile, ntiles = 128, 1.0, 1 << 22, 4097
+    n = ntiles * tile - 37 * B
+    nb, bpt = n // B, tile // B
+    base = bf16_bits_to_f32(random_bf16_bits(tile, seed=2034, scale=0.05))
+    variants = [f32_to_bf16_bits(base * np.float32(2.0 ** ((t % 7) - 3))) for t in range(7)]
+    enc = [oracle.compress(v, B, T) for v in variants]  # the decompress / accumulate input
+    rng = np.random.default_rng(2034)
+    b27, b31 = 1 << 27, (1 << 31) // B
+    idx = np.unique(np.concatenate([np.arange(64), np.arange(nb - 64, nb),
+                                    np.arange(b27 - 64, b27 + 64), np.arange(b31 - 64, b31 + 64),
+                                    rng.integers(0, nb, 2048)]))
+    idx_g = torch.from_numpy(idx).to(DEV)
+    which, off = (idx // bpt) % 7, idx % bpt  # variant and block within the tile
+    hx = np.concatenate([variants[w].reshape(bpt, B)[o] for w, o in zip(which, off)])
+    hq = np.concatenate([enc[w][0].reshape(bpt, B)[o] for w, o in zip(which, off)])
+    ha = np.array([enc[w][1][o] for w, o in zip(which, off)], np.float32)
+    hs = np.array([enc[w][2][o] for w, o in zip(which, off)], np.float32)
+    say(f"  grid-stride loops: n = {n} ({2 * n / 1e9:.1f} GB of bf16), {idx.size} sampled blocks")
+
+    def tiled(parts, per_tile, dtype, count):
+        # `count` elements made of tile-sized copies of parts[t % 7], filled on the GPU
+        out = torch.empty(ntiles * per_tile, dtype=dtype, device=DEV)
+        src = [torch.from_numpy(np.ascontiguousarray(v)).to(DEV) for v in parts]
+        for t in range(ntiles):
+            out[t * per_tile:(t + 1) * per_tile] = src[t % 7]
+        return out[:count]
+
+    x = tiled([v.view(np.int16) for v in variants], tile, torch.int16, n).view(torch.bfloat16)
+    q, a, s = tfp8.compress(x, B, T)
+    torch.cuda.synchronize()
+    rq, ra, rs, rt = oracle.compress(hx, B, T, with_quot=True)
+    nmis = assert_codes_match(cpu(q.view(nb, B)[idx_g]).reshape(-1), rq, rt,
+                              what="grid-stride compress")
+    assert_scales(cpu(a[idx_g]), cpu(s[idx_g]), ra, rs, what="grid-stride compress")
+    del q, a, s
+    say(f"  grid-stride compress: tie mismatches {nmis}")
+
+    qg = tiled([e[0] for e in enc], tile, torch.uint8, n)
+    ag = tiled([e[1] for e in enc], bpt, torch.float32, nb)
+    sg = tiled([e[2] for e in enc], bpt, torch.float32, nb)
+    out = tfp8.decompress(qg, ag, sg, B, torch.bfloat16)
+    torch.cuda.synchronize()
+    got = out.view(nb, B)[idx_g].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    del out
+    assert_bf16_match(got, oracle.decompress(hq, ha, hs, B, np.uint16),
+                      oracle.decompress_f64(hq, ha, hs, B), what="grid-stride decompress")
+
+    # accumulate in place: main gradient = the tiled codes, local gradient = x
+    tfp8.accumulate(qg, ag, sg, x, B, T, inplace=True)
+    torch.cuda.synchronize()
+    rq, ra, rs, rt = oracle.accumulate(hq, ha, hs, hx, B, T, with_quot=True)
+    assert_codes_match(cpu(qg.view(nb, B)[idx_g]).reshape(-1), rq, rt,
+                       what="grid-stride accumulate")
+    assert_scales(cpu(ag[idx_g]), cpu(sg[idx_g]), ra, rs, what="grid-stride accumulate")
+    del x, qg, ag, sg
+    torch.cuda.empty_cache()
+
+
 def _sweep_input(rng, nb, B):
     """A mixture of block kinds: Laplace bodies at random scales, outlier blocks, zero blocks,
     bfloat16-subnormal blocks and huge blocks."""
