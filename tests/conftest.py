@@ -19,3 +19,17 @@ def oracle():
 
     _oracle.set_threads(min(8, len(os.sched_getaffinity(0))))
     return _oracle
+
+
+def pytest_terminal_summary(terminalreporter):
+    """Report how close to their rounding midpoints the admitted code mismatches were."""
+    try:
+        from tiecheck import tie_window_stats
+    except ImportError:
+        return
+    st = tie_window_stats()
+    if st["admitted"]:
+        terminalreporter.write_line(
+            f"tie mismatches admitted: {st['admitted']}; largest distance from the midpoint "
+            f"{st['max_distance']:.3e} code units, {100 * st['max_window_frac']:.1f}% of the "
+            f"window; {st['over_half_window']} beyond half the window")

@@ -53,6 +53,15 @@ def tie_cap(flags: int) -> float:
     return 1e-2 if (flags & FLAG_NO_ROTATION) else MAX_TIE_FRAC
 
 
+# Over a test session: how much of the tie window the admitted mismatches used (their distance
+# from the midpoint over the window's half-width), and their largest distance in code units.
+_TIE_STATS = {"admitted": 0, "max_window_frac": 0.0, "max_distance": 0.0, "over_half_window": 0}
+
+
+def tie_window_stats() -> dict:
+    return dict(_TIE_STATS)
+
+
 def code_mismatches(got: np.ndarray, ref: np.ndarray, quot: np.ndarray, rel: float = TIE_REL,
                     abs_: float = TIE_ABS, int8: bool = False):
     """Return (n_mismatch, n_inadmissible, first_bad_index or -1)."""
@@ -74,8 +83,16 @@ def code_mismatches(got: np.ndarray, ref: np.ndarray, quot: np.ndarray, rel: flo
         zero_pair = (gm == 0) & (rm == 0)
         adjacent = ((gs == rs) & (np.abs(gm - rm) == 1)) | zero_pair
         mid = np.where(zero_pair, 0.0, 0.5 * (E4M3_VALUES[g] + E4M3_VALUES[r]))
-    near = np.abs(t - mid) <= rel * np.abs(mid) + abs_
+    dist = np.abs(t - mid)
+    window = rel * np.abs(mid) + abs_
+    near = dist <= window
     ok = adjacent & near
+    if ok.any():
+        frac = dist[ok] / window[ok]
+        _TIE_STATS["admitted"] += int(ok.sum())
+        _TIE_STATS["max_window_frac"] = max(_TIE_STATS["max_window_frac"], float(frac.max()))
+        _TIE_STATS["max_distance"] = max(_TIE_STATS["max_distance"], float(dist[ok].max()))
+        _TIE_STATS["over_half_window"] += int((frac > 0.5).sum())
     nbad = int((~ok).sum())
     first = int(bad[np.argmax(~ok)]) if nbad else -1
     return int(bad.size), nbad, first
