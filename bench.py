@@ -91,13 +91,13 @@ def copy_calibrate(steps: int):
     print(json.dumps({"copy_bytes_read": 2 * n, "copy_bytes_written": 2 * n, "copies": steps}))
 
 
-def cpu_baseline(xs, budget_s: float = 20.0):
-    """Time the oracle on a bounded prefix sample of every shard (same pipeline)."""
+def cpu_baseline(xs, block: int, budget_s: float = 20.0):
+    """Time the oracle on a bounded prefix sample of every shard (same pipeline, same block)."""
     import numpy as np
 
     import oracle
 
-    cfg_b = 128
+    cfg_b = block
     P = xs.shape[0]
     cores = len(os.sched_getaffinity(0))
     oracle.set_threads(cores)
@@ -491,7 +491,7 @@ def main():
     del x, codes, out, g, gq
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
-        result["cpu_baseline"] = cpu_baseline(xs)
+        result["cpu_baseline"] = cpu_baseline(xs, B)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
