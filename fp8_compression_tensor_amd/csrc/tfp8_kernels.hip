@@ -437,10 +437,44 @@ __global__ __launch_bounds__(kThreads) void k_decompress(const uint8_t *__restri
 
     // The decoded values are multiples of 2^-9 below 2^8.81 (E4M3) or integers below 2^7
     // (INT8), so every partial sum of the transform is exact in float32 until it passes 2^15
-    // (E4M3; for B <= 128 only the last stage can round, once) or 2^24 (INT8: never).
+    // (E4M3) or 2^24 (INT8: never).  The first six stages stay below 2^15 (64 * 448 < 2^15), so
+    // for B <= 128 only the last stage can round, once, relative to the output itself.  At
+    // B >= 256 (E4M3) a rounding in a later stage but the last would be relative to a partial
+    // sum that the remaining stages may cancel, so the per-element error would be unbounded: the
+    // six exact stages run first (within each run of 8 registers, then across the lanes), and
+    // the remaining R stages run in float64 (exact there), rounded once at the end.  The
+    // transform's output is then correctly rounded at every B.  (Taking the float64 stages only
+    // for blocks whose partial sums could pass 2^15 cost registers and was slower.)
     if constexpr (ROT) {
-      fwht_registers<N, 1>(v);
-      fwht_lanes<L, N>(v, j);
+      if constexpr (N <= 16 || (FLAGS & kInt8)) {
+        fwht_registers<N, 1>(v);
+        fwht_lanes<L, N>(v, j);
+      } else {
+        fwht_registers<N, 1, 8>(v);
+        fwht_lanes<L, N>(v, j);
+        // The remaining R = log2(N / 8) stages only combine registers with the same index mod 8:
+        // one such class of K = N / 8 registers at a time, in float64, where every partial sum
+        // (a multiple of 2^-9 below 2^(15 + R)) is exact; the conversion back is the one rounding.
+        constexpr int K = N / 8;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          double d[K];
+#pragma unroll
+          for (int k = 0; k < K; ++k) d[k] = (double)v[c + 8 * k];
+#pragma unroll
+          for (int h = 1; h < K; h <<= 1)
+#pragma unroll
+            for (int i = 0; i < K; i += 2 * h)
+#pragma unroll
+              for (int k = i; k < i + h; ++k) {
+                const double x = d[k], y = d[k + h];
+                d[k] = x + y;
+                d[k + h] = x - y;
+              }
+#pragma unroll
+          for (int k = 0; k < K; ++k) v[c + 8 * k] = (float)d[k];
+        }
+      }
     }
 
     // (v * s / sqrt(B)) / alpha as two products: s / (sqrt(B) alpha) alone can fall below the

@@ -222,6 +222,37 @@ def test_accumulate_every_fp32_value_onto_zero_main(oracle, tfp8):
     assert_scales(a, s, ar, sr, what="accumulate every-value blocks")
 
 
+@pytest.mark.parametrize("B", [128, 256, 512])
+def test_decompress_cancelling_partial_sums(oracle, tfp8, B):
+    # Codes of +-448 along a Hadamard row make the inverse transform of a block one spike of
+    # 448 B, its partial sums passing 2^15 from the seventh stage on.  In 4 pairs of positions
+    # whose row signs differ, the codes are set to +t and -t (t = m 2^-9, a subnormal code): the
+    # two changes cancel exactly in half of the outputs, which are then exactly 0, while the
+    # partial sums carry 2^-9 bits at magnitudes where float32 keeps only 2^-8.  A float32
+    # rounding in any stage but the last leaves a residue in those zeros (at B >= 256 it did,
+    # before the last stages ran in float64).  Alpha = s = 1; float32 and bfloat16 outputs
+    # against the oracle.
+    rng = np.random.default_rng(B)
+    nb = 257
+    r = np.arange(B)
+    sign = np.array([[(-1) ** bin(i & j).count("1") for j in r] for i in r], np.int8)
+    q = np.empty((nb, B), np.uint8)
+    for b in range(nb):
+        row = sign[rng.integers(1, B)]  # row 0 is all +1: no pair of opposite signs
+        q[b] = np.where(row > 0, 0x7E, 0xFE)  # +-448 along the row
+        free = np.ones(B, bool)
+        for _ in range(4):
+            j1 = int(rng.choice(np.nonzero(free)[0]))
+            j2 = int(rng.choice(np.nonzero(free & (row != row[j1]))[0]))
+            m = int(rng.integers(1, 8))
+            q[b, j1], q[b, j2] = m, 0x80 | m  # +m 2^-9 and -m 2^-9
+            free[[j1, j2]] = False
+    q = q.reshape(-1)
+    a = np.ones(nb, np.float32)
+    s = np.ones(nb, np.float32)
+    check_decompress(oracle, tfp8, q, a, s, B, what=f"cancelling partial sums B={B}")
+
+
 @pytest.mark.parametrize("flags", [2, 3])
 def test_hardware_decode_every_code(oracle, tfp8, flags):
     # The kernels' code decoding, checked exhaustively through decompress: without the rotation
