@@ -75,25 +75,30 @@ __device__ __forceinline__ float group_sum(float v) {
 }
 
 // Sum of the squares of the N values a lane holds of one block.  From N = 32 on (B >= 256) the
-// squares go into 8 partial sums added pairwise at the end, so that the float32 rounding error
-// grows with N / 8 + 3 terms instead of N: a sequential sum of 64 similar squares (B = 512) was
-// measured to miss the 1e-6 bar on alpha.  Shorter sums stay sequential (fewer registers).
-// With SCALED, the squares are those of v[r] * c (each product rounded to float32 first).
+// sum runs in float64, where every square of a float32 value is exact and the additions lose
+// nothing that matters, and is rounded to float32 once: a float32 sum of 64 similar squares
+// (B = 512), even in 8 partial sums, left alpha within a few percent of the 1e-6 bar, and over
+// it once with the other roundings of the exact accumulation path.  Shorter sums stay in float32
+// (sequential: 16 terms at most, and fewer registers).  With SCALED, the squares are those of
+// v[r] * c (each product rounded to float32 first).
 template <int N, bool SCALED = false>
 __device__ __forceinline__ float sum_squares(const float *v, float c = 1.0f) {
-  constexpr int K = N < 32 ? 1 : 8;
-  float p[K];
+  if constexpr (N < 32) {
+    float acc = 0.0f;
 #pragma unroll
-  for (int k = 0; k < K; ++k) p[k] = 0.0f;
-#pragma unroll
-  for (int r = 0; r < N; ++r) {
-    const float u = SCALED ? v[r] * c : v[r];
-    p[r % K] = fmaf(u, u, p[r % K]);
-  }
-  if constexpr (K == 1) {
-    return p[0];
+    for (int r = 0; r < N; ++r) {
+      const float u = SCALED ? v[r] * c : v[r];
+      acc = fmaf(u, u, acc);
+    }
+    return acc;
   } else {
-    return ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+    double acc = 0.0;
+#pragma unroll
+    for (int r = 0; r < N; ++r) {
+      const double u = (double)(SCALED ? v[r] * c : v[r]);
+      acc = fma(u, u, acc);
+    }
+    return (float)acc;
   }
 }
 

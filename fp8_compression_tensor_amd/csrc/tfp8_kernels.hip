@@ -810,25 +810,29 @@ __global__ __launch_bounds__(kThreads) void k_accumulate(
 // k_accumulate).  Its codes and s are still those of the main gradient (never written) and
 // alpha_out holds -alpha.  `active` = 0: work on the block but store nothing.
 //
-// Exact where the terms cancel, in float32.  g is scaled by 2^(K - E), E bounding the exponents
-// of both terms, and split into integers r = rint(t) and remainders l = t - r in [-1/2, 1/2].
-// |r| <= 2^K with K = 24 - log2(B), so every partial sum of H r is an integer of at most 2^24
-// and the transform of r is exact; the transform of l errs by ~2^-18 of 2^K at most.  The main
-// term is added to H r by one FMA with the high part of its factor (the product is exact, so the
-// cancellation happens inside the FMA and the sum rounds once), then its low part and H l.
+// The sum is formed with the roundings of the plain definition, so that it is exact wherever
+// the terms cancel exactly.  The transform of the decoded codes is exact: the first stages in
+// float32 (3 within each run of 8 registers, log2(L) across the lanes: partial sums of multiples
+// of 2^-9 below 64 * 448 < 2^15), the remaining ones in float64.  Multiplying it by s is exact
+// too (24 + 27 significant bits), the divisions by sqrt(B) and by alpha round once each, and
+// adding g rounds once: z matches the float64 reconstruction plus g bit for bit.  Everything
+// after z errs relative to z itself.  z is rotated as compress rotates its input: scaled by
+// 2^(K - E) with max|z| < 2^E and split into integers r = rint(t) and remainders l = t - r in
+// [-1/2, 1/2].  |r| <= 2^K with K = 24 - log2(B), so every partial sum of H r is an integer of
+// at most 2^24 and the transform of r is exact; the transform of l errs by ~2^-18 of 2^K at most.
 template <int B, bool F32IN, int FLAGS>
 __device__ __forceinline__ void accumulate_block_split(
     const uint8_t *codes, const float *scale, const void *__restrict__ grad, int64_t blk,
-    bool active, int j, float TBB, float C, double gscale, uint8_t *codes_out, float *alpha_out,
+    bool active, int j, float TBB, float C, double root_b, uint8_t *codes_out, float *alpha_out,
     float *scale_out) {
   constexpr int L = lanes_per_block(B);
   constexpr int RS = 8 * L;
   constexpr int N = B / L;
   constexpr int G = N / 8;
+  constexpr int NC = N / 8;  // registers per class of the float64 stages
   constexpr bool ROT = !(FLAGS & kNoRotation);
   constexpr float Q = qmax_of<FLAGS>();
   constexpr int K = 24 - (B == 64 ? 6 : B == 128 ? 7 : B == 256 ? 8 : 9);
-  constexpr int kNone = -(1 << 20);
   const int pj = ROT ? lane_perm<L>(j) : j;
   const float sj = ROT ? lane_sign<L>(j) : 1.0f;
 
@@ -836,58 +840,105 @@ __device__ __forceinline__ void accumulate_block_split(
   load_compress_in<B, F32IN>(in, grad, blk, j);
   u32x2 qd[G];
 #pragma unroll
-  for (int g = 0; g < G; ++g) qd[g] = *(const u32x2 *)(codes + blk * B + RS * g + 8 * pj);
+  for (int g = 0; g < G; ++g) qd[g] = *(const u32x2 *)(codes + blk * B + RS * g + 8 * j);
   const float sp = scale[blk], ap = -alpha_out[blk];
 
-  float r[N], l[N];
+  float gv[N];  // g at positions RS g + 8 j + e
   if constexpr (!F32IN) {
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) widen_bf16x2(in.d[g][q], r[8 * g + 2 * q], r[8 * g + 2 * q + 1]);
+      for (int q = 0; q < 4; ++q) widen_bf16x2(in.d[g][q], gv[8 * g + 2 * q], gv[8 * g + 2 * q + 1]);
   } else {
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        r[8 * g + q] = __uint_as_float(in.d[2 * g][q]);
-        r[8 * g + 4 + q] = __uint_as_float(in.d[2 * g + 1][q]);
+        gv[8 * g + q] = __uint_as_float(in.d[2 * g][q]);
+        gv[8 * g + 4 + q] = __uint_as_float(in.d[2 * g + 1][q]);
       }
   }
-  float mg = 0.0f;
+  float v[N];  // decoded codes at positions RS g + 8 j + e, those of g
 #pragma unroll
-  for (int i = 0; i < N; ++i) mg = fmaxf(mg, fabsf(r[i]));
-  mg = group_max<L>(mg);
-  // the main term's factor sj * gscale * s / alpha; |factor * dec| <= |factor| * Q
-  const double f = (sp == 0.0f) ? 0.0 : (double)sj * (gscale * ((double)sp / (double)ap));
-  const int Eg = (mg == 0.0f) ? kNone : exponent_of(mg);
-  const int Ef = (f == 0.0) ? kNone : __builtin_amdgcn_frexp_exp(fabs(f) * (double)Q);
-  const int E = max(Eg, Ef) == kNone ? 0 : max(Eg, Ef);  // |g|, |main term| < 2^E
-  const double ft = __builtin_amdgcn_ldexp(f, K - E);
-  const float hi = (float)ft, lo = (float)(ft - (double)hi);
+  for (int g = 0; g < G; ++g) {
+    decode4<FLAGS>(qd[g][0], v[8 * g + 0], v[8 * g + 1], v[8 * g + 2], v[8 * g + 3]);
+    decode4<FLAGS>(qd[g][1], v[8 * g + 4], v[8 * g + 5], v[8 * g + 6], v[8 * g + 7]);
+  }
+  if constexpr (ROT) {
+    fwht_registers<N, 1, 8>(v);
+    fwht_lanes<L, N>(v, j);
+    // lane j now holds sj * (H dec) at positions RS g + 8 pj + e; lane pj holds position j
+    // (the lane permutation is an involution), so fetch from there and undo that lane's sign
+    if constexpr (L == 8) {
+      const int src = (int)(threadIdx.x & 63) - j + pj;
+      const float ss = lane_sign<L>(pj);
+#pragma unroll
+      for (int i = 0; i < N; ++i) v[i] = ss * __shfl(v[i], src, 64);
+    } else {  // the 4-lane network keeps the natural order
+#pragma unroll
+      for (int i = 0; i < N; ++i) v[i] = sj * v[i];
+    }
+  }
+  double z[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) z[i] = (double)v[i];
+  if constexpr (ROT && NC > 1) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+      for (int h = 1; h < NC; h <<= 1)
+#pragma unroll
+        for (int i = 0; i < NC; i += 2 * h)
+#pragma unroll
+          for (int k = i; k < i + h; ++k) {
+            const double x = z[c + 8 * k], y = z[c + 8 * (k + h)];
+            z[c + 8 * k] = x + y;
+            z[c + 8 * (k + h)] = x - y;
+          }
+  }
+  const double sd = (double)sp;
+  // m / b rounded to nearest from y = RN(1 / b): q = RN(m y) is within an ulp of m / b, the FMA
+  // gives its residual m - b q exactly, and q + (m - b q) y rounds to RN(m / b) (Markstein's
+  // theorem); one division per block instead of one per element
+  const auto div_rn = [](double m, double b, double y) {
+    const double q = m * y;
+    return fma(fma(-q, b, m), y, q);
+  };
+  const double ya = 1.0 / (double)ap, yb = 1.0 / root_b;
+  int ez = 0;  // biased float64 exponent of max|z|; 0 only if every z is zero
 #pragma unroll
   for (int i = 0; i < N; ++i) {
-    const float t = scale2(r[i], K - E);
-    r[i] = __builtin_rintf(t);
-    l[i] = t - r[i];
+    double m = sd * z[i];  // exact
+    if constexpr (ROT) {
+      if constexpr (B == 64 || B == 256) m = m * (B == 64 ? 0.125 : 0.0625);  // exact
+      else m = div_rn(m, root_b, yb);
+    }
+    m = div_rn(m, (double)ap, ya);
+    z[i] = (sp == 0.0f ? 0.0 : m) + (double)gv[i];
+    ez = max(ez, (int)((__double_as_longlong(z[i]) >> 52) & 0x7ff));
+  }
+  ez = group_max_i<L>(ez);
+  // sums of float32 values are float64 normals or zero, so max|z| < 2^E with E = ez - 1022
+  const int E = ez == 0 ? 0 : ez - 1022;
+  float r[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const double t = __builtin_amdgcn_ldexp(z[i], K - E);
+    if constexpr (ROT) {
+      const double ri = __builtin_rint(t);
+      r[i] = (float)ri;
+      v[i] = (float)(t - ri);  // the remainder l
+    } else {
+      r[i] = (float)t;  // one rounding, relative to z
+    }
   }
   if constexpr (ROT) {
     fwht_registers<N, 1>(r);
     fwht_lanes<L, N>(r, j);  // lane j: sj * (H r) at positions RS g + 8 pj + e
-    fwht_registers<N, 1>(l);
-    fwht_lanes<L, N>(l, j);
-  }
+    fwht_registers<N, 1>(v);
+    fwht_lanes<L, N>(v, j);
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float d[8];
-    decode4<FLAGS>(qd[g][0], d[0], d[1], d[2], d[3]);
-    decode4<FLAGS>(qd[g][1], d[4], d[5], d[6], d[7]);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float w = fmaf(d[e], hi, r[8 * g + e]);
-      w = fmaf(d[e], lo, w);
-      r[8 * g + e] = w + l[8 * g + e];
-    }
+    for (int i = 0; i < N; ++i) r[i] = r[i] + v[i];
   }
   float m = 0.0f;
 #pragma unroll
@@ -920,7 +971,7 @@ constexpr int kFixRuns = 2;  // runs of 64 blocks that one wavefront of k_accumu
 template <int B, bool F32IN, int FLAGS>
 __global__ __launch_bounds__(kThreads) void k_accumulate_fix(
     const uint8_t *codes, const float *scale, const void *__restrict__ grad, int64_t nb,
-    float TBB, float C, double gscale, uint8_t *codes_out, float *alpha_out, float *scale_out) {
+    float TBB, float C, double root_b, uint8_t *codes_out, float *alpha_out, float *scale_out) {
   constexpr int kRuns = kFixRuns;
   constexpr int L = lanes_per_block(B);
   constexpr int BPW = 64 / L;  // blocks worked on at once: one per group of L lanes
@@ -950,7 +1001,7 @@ __global__ __launch_bounds__(kThreads) void k_accumulate_fix(
         const int64_t blk = base + __builtin_ctzll(active ? mine : mask);
         for (int i = 0; i < BPW; ++i) mask &= mask - 1;
         accumulate_block_split<B, F32IN, FLAGS>(codes, scale, grad, blk, active, j, TBB, C,
-                                                gscale, codes_out, alpha_out, scale_out);
+                                                root_b, codes_out, alpha_out, scale_out);
       }
     }
   }

@@ -733,6 +733,51 @@ def test_accumulate_edges(oracle, tfp8, B, gdtype, flags):
     _check_accumulate(oracle, tfp8, q, a, s, g, B, f"accumulate B={B} {gdtype}", flags=flags)
 
 
+@pytest.mark.parametrize("flags", [0, 1, 2, 3])
+@pytest.mark.parametrize("B", [64, 128, 256, 512])
+def test_accumulate_exact_cancellation(oracle, tfp8, B, flags):
+    # Main gradients whose reconstruction is exact in float32 (codes 0 or +-Q, alpha = Q' 2^e
+    # with Q' the odd part of Q, s a power of two; exact at every B without the rotation and at
+    # B = 64, 256 with it, where sqrt(B) is a power of two), and local gradients that are exactly
+    # their negatives: the sum is exactly zero, so the result is a zero block.  Half of the
+    # blocks get one small extra term, so that their sum is a one-hot block far below either
+    # term.  A kernel that forms the main term with any error of its own leaves a residue of
+    # that size instead, which the codes of the sum magnify to full scale.  At B = 128, 512 with
+    # the rotation the float32 negative differs from the reconstruction by its rounding error,
+    # which then is the whole sum.
+    from tiecheck import FLAG_INT8
+    rng = np.random.default_rng(9000 + B + flags)
+    nb = 96
+    int8 = bool(flags & FLAG_INT8)
+    qmax, odd = (127, 127) if int8 else (448, 7)
+    pos, neg = (0x7F, 0x81) if int8 else (0x7E, 0xFE)
+    pick = rng.choice(3, size=(nb, B), p=[0.6, 0.2, 0.2])
+    q = np.where(pick == 1, pos, np.where(pick == 2, neg, 0)).astype(np.uint8)
+    q[np.arange(nb), rng.integers(0, B, nb)] = pos           # every block reaches Q
+    a = (odd * 2.0 ** rng.integers(-10, 11, nb)).astype(np.float32)
+    s = (2.0 ** rng.integers(-10, 11, nb)).astype(np.float32)
+    main = oracle.decompress_f64(q.reshape(-1), a, s, B, flags=flags).reshape(nb, B)
+    g = -main.astype(np.float32)
+    bump = np.arange(nb) % 2 == 1
+    k = rng.integers(0, B, nb)
+    g[bump, k[bump]] += (np.abs(main[bump]).max(axis=1) * 2.0 ** -20).astype(np.float32)
+    exact = (flags & 2) or B in (64, 256)
+    if exact:
+        assert np.array_equal(g[~bump].astype(np.float64), -main[~bump])
+    # where the sum is the rounding error of the negative, its codes fall on midpoints more often
+    # than the tie cap (made for the workloads) allows: there only admissibility is checked
+    cq, ca, cs = _check_accumulate(oracle, tfp8, q.reshape(-1), a, s, g.reshape(-1), B,
+                                   f"exact cancellation B={B} flags={flags}", flags=flags,
+                                   tie_ledger=None if exact else [])
+    if exact:
+        assert np.all(cs[~bump] == 0) and np.all(cq.reshape(nb, B)[~bump] == 0)
+        bumped = cq.reshape(nb, B)[bump]
+        if flags & 2:   # a one-hot sum keeps one code
+            assert np.all(np.count_nonzero(bumped, axis=1) == 1)
+        else:           # and rotates to a Hadamard row: every code is +-Q
+            assert np.all(np.isin(bumped, [pos, neg]))
+
+
 def test_accumulate_activation_shards_with_shared_outliers(oracle, tfp8):
     # the Qwen2.5-7B-shaped activation shards 0 and 1 as main and local gradient: their shared
     # outlier channels have random signs, so about 15% of the blocks cancel and take the exact
