@@ -1113,3 +1113,73 @@ def test_random_sweep(oracle, tfp8):
         n = sum(k for f, _, k in ledger if f == fl)
         say(f"  sweep flags={fl}: {mis} tie mismatches in {n} codes")
         assert mis <= tie_cap(fl) * max(n, 1), (fl, mis, n)
+
+
+def _struct_input(rng, nb, B):
+    """Blocks built to stress exactness: Hadamard rows with a few perturbed entries, one-hot
+    blocks with tiny noise, constant and alternating blocks, each at a random power-of-two scale,
+    mixed with the random sweep's kinds.  Their rotated values and sums often land exactly on
+    code midpoints or cancel exactly."""
+    idx = np.arange(B)
+    out = []
+    for _ in range(nb):
+        kind = rng.integers(0, 6)
+        scale = 2.0 ** rng.integers(-40, 40)
+        if kind == 0:
+            r = rng.integers(0, B)
+            v = np.array([(-1.0) ** bin(r & j).count("1") for j in idx])
+            k = rng.integers(0, 6)
+            v[rng.integers(0, B, k)] *= rng.choice([0.5, 1.5, 1e-3, -1.0], k)
+        elif kind == 1:
+            v = np.zeros(B)
+            v[rng.integers(0, B)] = rng.choice([-1.0, 1.0])
+            v[rng.integers(0, B, 3)] += rng.normal(0, 1e-4, 3)
+        elif kind == 2:
+            v = np.full(B, rng.choice([-1.0, 1.0])) + rng.normal(0, 1e-3, B) * (rng.random(B) < 0.1)
+        elif kind == 3:
+            v = np.where(idx % 2 == 0, 1.0, -1.0) * (1 + rng.integers(0, 3, B) / 8)
+        else:
+            v = _sweep_input(rng, 1, B)
+            scale = 1.0
+        out.append(v * scale)
+    return np.concatenate(out)
+
+
+def test_structured_sweep(oracle, tfp8):
+    # 300 seeded cases like the random sweep, on structured blocks, with local gradients that are
+    # the input's negative up to bf16-sized noise (so many blocks cancel exactly or nearly).  By
+    # construction many codes sit exactly on midpoints, so only admissibility is checked here,
+    # not the tie counts.
+    ledger = []
+    for case in range(300):
+        rng = np.random.default_rng(8000 + case)
+        B = int(rng.choice([64, 128, 256, 512]))
+        flags = int(rng.integers(0, 4))
+        f32 = bool(rng.integers(0, 2))
+        nb = int(rng.choice([1, 7, 63, 257]))
+        T = float(2.0 ** rng.integers(-20, 21) * rng.choice([1.0, 0.75, 1.5]))
+        v = _struct_input(rng, nb, B)
+        x = v.astype(np.float32) if f32 else f32_to_bf16_bits(v.astype(np.float32))
+        what = f"structured {case}: B={B} flags={flags} {'f32' if f32 else 'bf16'} nb={nb} T={T}"
+        q, a, s = check_compress(oracle, tfp8, x, B, T=T, what=what, flags=flags,
+                                 tie_ledger=ledger)
+        check_decompress(oracle, tfp8, q, a, s, B, what=what, flags=flags)
+        P = int(rng.choice([1, 2, 3, 8, 16]))
+        enc = [(q, a, s)] + [oracle.compress(
+            f32_to_bf16_bits((_struct_input(rng, nb, B) * rng.choice([-1.0, 1.0])).astype(np.float32)),
+            B, T, flags=flags) for _ in range(P - 1)]
+        check_reduce(oracle, tfp8, np.stack([e[0] for e in enc]), np.stack([e[1] for e in enc]),
+                     np.stack([e[2] for e in enc]), B, T, what=what + f" P={P}", flags=flags,
+                     tie_ledger=ledger)
+        g = -(bf16_bits_to_f32(x) if not f32 else x).astype(np.float64)
+        g = g + rng.normal(0, 1e-3, g.size) * np.abs(g)
+        fresh = rng.random(nb) < 0.3
+        if fresh.any():
+            g.reshape(nb, B)[fresh] = _struct_input(rng, int(fresh.sum()), B).reshape(-1, B)
+        gl = g.astype(np.float32) if rng.integers(0, 2) else f32_to_bf16_bits(g.astype(np.float32))
+        _check_accumulate(oracle, tfp8, q, a, s, gl, B, what + " accumulate", flags=flags,
+                          inplace=bool(rng.integers(0, 2)), T=T, tie_ledger=ledger)
+    for fl in range(4):
+        mis = sum(m for f, m, _ in ledger if f == fl)
+        n = sum(k for f, _, k in ledger if f == fl)
+        say(f"  structured sweep flags={fl}: {mis} tie mismatches in {n} codes")
