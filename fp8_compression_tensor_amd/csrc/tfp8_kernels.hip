@@ -808,7 +808,10 @@ __global__ __launch_bounds__(kThreads) void k_accumulate(
 
 // One set-aside block, by the group of L lanes j = 0..L-1 that holds it (lane layout of
 // k_accumulate).  Its codes and s are still those of the main gradient (never written) and
-// alpha_out holds -alpha.  `active` = 0: work on the block but store nothing.
+// alpha_out holds -alpha.  `active` = 0: work on the block but store nothing.  Lane j reads codes
+// at positions 8 j and writes them at 8 pj, where another lane of the group read; in place that
+// is safe because every stored value depends, through the lane exchanges, on all of the group's
+// loaded codes, so the group's loads have completed before any of its stores.
 //
 // The sum is formed with the roundings of the plain definition, so that it is exact wherever
 // the terms cancel exactly.  The transform of the decoded codes is exact: the first stages in
