@@ -809,7 +809,7 @@ __global__ __launch_bounds__(kThreads) void k_accumulate(
 // One set-aside block, by the group of L lanes j = 0..L-1 that holds it (lane layout of
 // k_accumulate).  Its codes and s are still those of the main gradient (never written) and
 // alpha_out holds -alpha.  `active` = 0: work on the block but store nothing.  Lane j reads codes
-// at positions 8 j and writes them at 8 pj, where another lane of the group read; in place that
+// at positions 8 qj and writes them at 8 pj, where another lane of the group read; in place that
 // is safe because every stored value depends, through the lane exchanges, on all of the group's
 // loaded codes, so the group's loads have completed before any of its stores.
 //
@@ -842,8 +842,13 @@ __device__ __forceinline__ void accumulate_block_split(
   CompressIn<B, F32IN> in;
   load_compress_in<B, F32IN>(in, grad, blk, j);
   u32x2 qd[G];
+  // The lane network sends lane j's result to position pj.  Reading lane j's codes from 8 qj
+  // instead of 8 j, with qj = j ^ (3 bit2(j)) at L = 8 (the transpose of that GF(2)-linear
+  // permutation; identity at L = 4 and without the rotation), makes the network's output land
+  // at lane j's own positions, those of g, with the sign sj (enumerated on the unit vectors).
+  const int qj = ROT && L == 8 ? j ^ (((j >> 2) & 1) * 3) : j;
 #pragma unroll
-  for (int g = 0; g < G; ++g) qd[g] = *(const u32x2 *)(codes + blk * B + RS * g + 8 * j);
+  for (int g = 0; g < G; ++g) qd[g] = *(const u32x2 *)(codes + blk * B + RS * g + 8 * qj);
   const float sp = scale[blk], ap = -alpha_out[blk];
 
   float gv[N];  // g at positions RS g + 8 j + e
@@ -861,7 +866,8 @@ __device__ __forceinline__ void accumulate_block_split(
         gv[8 * g + 4 + q] = __uint_as_float(in.d[2 * g + 1][q]);
       }
   }
-  float v[N];  // decoded codes at positions RS g + 8 j + e, those of g
+  float v[N];  // decoded codes at positions RS g + 8 qj + e; after the transform lane j holds
+               // sj * (H dec) at positions RS g + 8 j + e, those of g
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     decode4<FLAGS>(qd[g][0], v[8 * g + 0], v[8 * g + 1], v[8 * g + 2], v[8 * g + 3]);
@@ -870,17 +876,6 @@ __device__ __forceinline__ void accumulate_block_split(
   if constexpr (ROT) {
     fwht_registers<N, 1, 8>(v);
     fwht_lanes<L, N>(v, j);
-    // lane j now holds sj * (H dec) at positions RS g + 8 pj + e; lane pj holds position j
-    // (the lane permutation is an involution), so fetch from there and undo that lane's sign
-    if constexpr (L == 8) {
-      const int src = (int)(threadIdx.x & 63) - j + pj;
-      const float ss = lane_sign<L>(pj);
-#pragma unroll
-      for (int i = 0; i < N; ++i) v[i] = ss * __shfl(v[i], src, 64);
-    } else {  // the 4-lane network keeps the natural order
-#pragma unroll
-      for (int i = 0; i < N; ++i) v[i] = sj * v[i];
-    }
   }
   double z[N];
 #pragma unroll
@@ -899,7 +894,7 @@ __device__ __forceinline__ void accumulate_block_split(
             z[c + 8 * (k + h)] = x - y;
           }
   }
-  const double sd = (double)sp;
+  const double sd = (double)sj * (double)sp;  // sj = +-1: exact
   // m / b rounded to nearest from y = RN(1 / b): q = RN(m y) is within an ulp of m / b, the FMA
   // gives its residual m - b q exactly, and q + (m - b q) y rounds to RN(m / b) (Markstein's
   // theorem); one division per block instead of one per element
