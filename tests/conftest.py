@@ -32,4 +32,7 @@ def pytest_terminal_summary(terminalreporter):
         terminalreporter.write_line(
             f"tie mismatches admitted: {st['admitted']}; largest distance from the midpoint "
             f"{st['max_distance']:.3e} code units, {100 * st['max_window_frac']:.1f}% of the "
-            f"window; {st['over_half_window']} beyond half the window")
+            f"window; {st['over_half_window']} beyond half the window; largest distance at "
+            f"|mid| <= 8: {st['max_distance_small_mid']:.3e} code units; largest relative distance "
+            f"at |mid| > 8: {st['max_rel_distance_large_mid']:.3e}; window-fraction histogram "
+            f"[0,1/64) [1/64,1/16) [1/16,1/4) [1/4,1/2) [1/2,1]: {st['window_frac_hist']}")

@@ -77,6 +77,41 @@ def assert_bf16_match(got_bits, ref_bits, ref_f64, rel=2.0 ** -20, what="bf16 ou
     return int(bad.size)
 
 
+def assert_codes_match_every_block(got, ref, B: int, quot_of_blocks, max_frac: float,
+                                   what="codes", int8: bool = False):
+    """Whole-tensor code check for tensors too large to carry the oracle's quotients for every
+    element: codes are compared on every element, the exact quotients are fetched only for the
+    blocks that hold a mismatch (``quot_of_blocks(block_indices)`` returns them flattened, in the
+    order given), every mismatch must be an admissible tie, and the tie count is held to
+    ``max_frac`` of the WHOLE tensor.  Returns the number of mismatches."""
+    got = np.asarray(got, np.uint8).reshape(-1, B)
+    ref = np.asarray(ref, np.uint8).reshape(-1, B)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    nbt = got.shape[0]
+    chunk = 1 << 20  # blocks per pass, to bound the temporary mask
+    blocks = [np.nonzero((got[i:i + chunk] != ref[i:i + chunk]).any(axis=1))[0] + i
+              for i in range(0, nbt, chunk)]
+    blocks = np.concatenate(blocks) if blocks else np.zeros(0, np.int64)
+    if blocks.size == 0:
+        return 0
+    t = np.asarray(quot_of_blocks(blocks), np.float64).reshape(-1)
+    assert t.size == blocks.size * B, (t.size, blocks.size)
+    nmis = assert_codes_match(got[blocks], ref[blocks], t, max_frac=1.0, what=what, int8=int8)
+    assert nmis <= max_frac * got.size, (f"{what}: {nmis} tie mismatches of {got.size} exceed "
+                                         f"{max_frac} of the tensor")
+    return nmis
+
+
+def _count_in_blocks(got, ref, B, block_mask, flags, mask_ledger):
+    """Append (flags, mismatches, elements) over the blocks selected by block_mask to the ledger."""
+    if block_mask is None:
+        return
+    m = np.asarray(block_mask, bool).reshape(-1)
+    g = np.asarray(got, np.uint8).reshape(-1, B)[m]
+    r = np.asarray(ref, np.uint8).reshape(-1, B)[m]
+    mask_ledger.append((flags, int((g != r).sum()), int(g.size)))
+
+
 def _tie_cap(flags, ledger):
     """Per-call tie cap, or none when the caller keeps a ledger of (flags, mismatches, elements)
     and holds the total to the cap itself (many small calls: one tie would exceed 1e-4 of 64)."""
@@ -84,7 +119,8 @@ def _tie_cap(flags, ledger):
 
 
 def check_compress(oracle, tfp8, x: np.ndarray, B: int, T: float = 1.0, what="compress",
-                   flags: int = 0, gpu: bool = False, tie_ledger=None):
+                   flags: int = 0, gpu: bool = False, tie_ledger=None, block_mask=None,
+                   mask_ledger=None):
     """GPU compress of host input x (uint16 bfloat16 bits or float32) vs the oracle.
     Returns the oracle's (codes, alpha, scale), the input of any later stage (no oracle input
     ever comes from the GPU), or with gpu=True the GPU's, as numpy arrays."""
@@ -97,6 +133,7 @@ def check_compress(oracle, tfp8, x: np.ndarray, B: int, T: float = 1.0, what="co
                               what=what + " codes", int8=bool(flags & FLAG_INT8))
     if tie_ledger is not None:
         tie_ledger.append((flags, nmis, q.size))
+    _count_in_blocks(q, qr, B, block_mask, flags, mask_ledger)
     ea, es = assert_scales(a, s, ar, sr, what=what)
     say(f"  {what}: n={x.size} B={B} T={T} flags={flags}: code tie mismatches {nmis} "
         f"({nmis / max(x.size, 1):.2e}), max rel err alpha {ea:.2e} scale {es:.2e}")
@@ -122,7 +159,7 @@ def check_decompress(oracle, tfp8, q, a, s, B: int, what="decompress", flags: in
 
 
 def check_reduce(oracle, tfp8, q, a, s, B, T=1.0, what="reduce", flags: int = 0,
-                 gpu: bool = False, tie_ledger=None):
+                 gpu: bool = False, tie_ledger=None, block_mask=None, mask_ledger=None):
     """GPU reduce of stacked codes/scales [P, ...] vs the oracle's reduce by definition.
     Returns the oracle's (codes, alpha, scale), or with gpu=True the GPU's."""
     P, n = q.shape
@@ -135,6 +172,7 @@ def check_reduce(oracle, tfp8, q, a, s, B, T=1.0, what="reduce", flags: int = 0,
                               what=what + " codes", int8=bool(flags & FLAG_INT8))
     if tie_ledger is not None:
         tie_ledger.append((flags, nmis, cq.size))
+    _count_in_blocks(cq, rq, B, block_mask, flags, mask_ledger)
     ea, es = assert_scales(ca, cs, ra, rs, what=what)
     say(f"  {what}: P={P} n={n} B={B} flags={flags}: code tie mismatches {nmis} ({nmis / n:.2e}), "
         f"max rel err alpha {ea:.2e} scale {es:.2e}")

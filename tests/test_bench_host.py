@@ -46,3 +46,11 @@ def test_traffic_record_applies_only_to_its_source(tmp_path):
     assert bench.measured_traffic(str(p), src) is None
     assert bench.measured_traffic(str(tmp_path / "missing.json"), src) is None
 
+
+
+def test_cpu_model_names_the_host_cpu():
+    # taken from lscpu (before the bench touches the GPU), else /proc/cpuinfo
+    m = bench.cpu_model()
+    assert isinstance(m, str) and m and m != "unknown"
+    if shutil.which("lscpu"):
+        assert "lscpu: vendor" in m

@@ -34,8 +34,15 @@ E4M3_VALUES = _E4M3
 # INT8 codes: two's complement bytes
 INT8_VALUES = np.arange(256, dtype=np.int64).astype(np.uint8).view(np.int8).astype(np.float64)
 
-TIE_REL = 2.0 ** -20
-TIE_ABS = 2.0 ** -11
+# Window half-width: TIE_REL * |mid| + TIE_ABS code units.  The GPU forms each quotient from a
+# float32 transform (a few roundings of 2^-24 relative to the block's peak, 448 code units) and a
+# correctly rounded code multiplier, so its quotient errs by ~1e-4 code units at most in absolute
+# terms and a few 2^-24 relative.  Measured over the GPU suite and 33 000 sweep cases with a
+# window twice as wide (2^-20 |mid| + 2^-11), admitted mismatches sat at most 6.9e-5 code units
+# from their midpoints and used at most 16% of that window; this one is half of it, which still
+# leaves them at a third of it.
+TIE_REL = 2.0 ** -21
+TIE_ABS = 2.0 ** -12
 MAX_TIE_FRAC = 1e-4
 
 # Variant flags (the values the C ABI and the oracle use for their *_ex entry points).
@@ -55,11 +62,17 @@ def tie_cap(flags: int) -> float:
 
 # Over a test session: how much of the tie window the admitted mismatches used (their distance
 # from the midpoint over the window's half-width), and their largest distance in code units.
-_TIE_STATS = {"admitted": 0, "max_window_frac": 0.0, "max_distance": 0.0, "over_half_window": 0}
+_TIE_STATS = {"admitted": 0, "max_window_frac": 0.0, "max_distance": 0.0, "over_half_window": 0,
+              "max_distance_small_mid": 0.0, "max_rel_distance_large_mid": 0.0,
+              "window_frac_hist": [0] * 5}
+# buckets of the window fraction: [0, 1/64), [1/64, 1/16), [1/16, 1/4), [1/4, 1/2), [1/2, 1]
+_HIST_EDGES = np.array([1 / 64, 1 / 16, 1 / 4, 1 / 2])
 
 
 def tie_window_stats() -> dict:
-    return dict(_TIE_STATS)
+    st = dict(_TIE_STATS)
+    st["window_frac_hist"] = list(_TIE_STATS["window_frac_hist"])
+    return st
 
 
 def code_mismatches(got: np.ndarray, ref: np.ndarray, quot: np.ndarray, rel: float = TIE_REL,
@@ -93,6 +106,16 @@ def code_mismatches(got: np.ndarray, ref: np.ndarray, quot: np.ndarray, rel: flo
         _TIE_STATS["max_window_frac"] = max(_TIE_STATS["max_window_frac"], float(frac.max()))
         _TIE_STATS["max_distance"] = max(_TIE_STATS["max_distance"], float(dist[ok].max()))
         _TIE_STATS["over_half_window"] += int((frac > 0.5).sum())
+        small = np.abs(mid[ok]) <= 8.0  # where the absolute term dominates the window
+        if small.any():
+            _TIE_STATS["max_distance_small_mid"] = max(_TIE_STATS["max_distance_small_mid"],
+                                                       float(dist[ok][small].max()))
+        if (~small).any():
+            _TIE_STATS["max_rel_distance_large_mid"] = max(
+                _TIE_STATS["max_rel_distance_large_mid"],
+                float((dist[ok][~small] / np.abs(mid[ok][~small])).max()))
+        for b in np.searchsorted(_HIST_EDGES, frac, side="right"):
+            _TIE_STATS["window_frac_hist"][int(b)] += 1
     nbad = int((~ok).sum())
     first = int(bad[np.argmax(~ok)]) if nbad else -1
     return int(bad.size), nbad, first
