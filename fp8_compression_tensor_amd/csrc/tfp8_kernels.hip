@@ -18,8 +18,8 @@
 //
 // Launch.  One tile (64/L blocks) per wavefront, 8- or 16-byte vector loads and stores per
 // lane, no LDS, no atomics.  Compress of an input of 1.5 GiB or more launches
-// one-wavefront workgroups and gives each XCD a contiguous eighth of the tiles
-// (kCompressRemapMinBytes below).
+// one-wavefront workgroups and gives each XCD a contiguous eighth of the tiles, and from that
+// size on compress and decompress stream with non-temporal hints (kStreamMinBytes below).
 //
 // Transform.  w = H x (unnormalised) is computed by an in-register FWHT over the register
 // bits and a 3-stage DPP butterfly over the lane bits (tfp8_device.hpp), which leaves lane j
@@ -101,16 +101,36 @@ __device__ __forceinline__ void decode4(uint32_t w, float &a, float &b, float &c
     unpack_fp8x4(w, a, b, c, d);
 }
 
-// Streaming loads and stores: every input byte is read once and every output byte written
-// once, so they go through the cache hierarchy with the non-temporal hint.
-template <class T>
-__device__ __forceinline__ T ld_stream(const T *p) {
-  return __builtin_nontemporal_load(p);
+// Loads and stores of the streamed data.  Every input byte is read once and every output byte
+// written once.  With NT they carry the non-temporal hint, which keeps a stream larger than the
+// caches from thrashing them; without it they are plain accesses, whose output the 256 MB MALL
+// (the last-level cache in front of HBM) can absorb when the stream is smaller.
+template <bool NT, class T>
+__device__ __forceinline__ T ld(const T *p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  return *p;
 }
-template <class T>
-__device__ __forceinline__ void st_stream(T v, T *p) {
-  __builtin_nontemporal_store(v, p);
+template <bool NT, class T>
+__device__ __forceinline__ void st(T v, T *p) {
+  if constexpr (NT)
+    __builtin_nontemporal_store(v, p);
+  else
+    *p = v;
 }
+
+// Launch modes of compress and decompress (a template parameter; the host picks one by size).
+//   kTilePlain   one tile per wavefront, plain loads and stores: inputs below 1.5 GiB.  Measured
+//                on MI355X with the caches flushed before each launch: 3-7% faster than with
+//                the hints on 100-360 MB streams.
+//   kTileStream  one tile per wavefront, non-temporal hints: inputs of 1.5 GiB or more (7%
+//                faster than plain on a 1.9 GB compress).
+//   kLoopStream  grid-stride loop with the next tile's loads in flight, non-temporal hints: the
+//                launch is capped (past 2^34 elements) and wavefronts take several tiles.
+// The one-tile modes carry no prefetch buffer, which at B = 256 leaves registers for eight
+// wavefronts per SIMD instead of five.
+enum : int { kTilePlain = 0, kTileStream = 1, kLoopStream = 2 };
+constexpr bool mode_nt(int mode) { return mode != kTilePlain; }
+constexpr bool mode_loop(int mode) { return mode == kLoopStream; }
 
 // --------------------------------------------------------------------------------------------
 // Range-safe scales: from the rotated values of one block (held by a group of L lanes) to the
@@ -167,20 +187,20 @@ struct CompressIn {
 // The same, from the base of a tile (wave-uniform, so it stays in scalar registers) and a lane's
 // 32-bit element offset into it: the loads then take the scalar base plus a vector offset, and
 // no 64-bit address arithmetic runs per lane.  Run g is read at off + g * step.
-template <int B, bool F32IN>
+template <bool NT, int B, bool F32IN>
 __device__ __forceinline__ void load_compress_at(CompressIn<B, F32IN> &in, const void *tile,
                                                  uint32_t off, uint32_t step) {
   constexpr int G = CompressIn<B, F32IN>::kRuns;
   if constexpr (!F32IN) {
     const uint16_t *xb = (const uint16_t *)tile + off;
 #pragma unroll
-    for (int g = 0; g < G; ++g) in.d[g] = ld_stream((const u32x4 *)(xb + step * g));
+    for (int g = 0; g < G; ++g) in.d[g] = ld<NT>((const u32x4 *)(xb + step * g));
   } else {
     const float *xb = (const float *)tile + off;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      in.d[2 * g] = ld_stream((const u32x4 *)(xb + step * g));
-      in.d[2 * g + 1] = ld_stream((const u32x4 *)(xb + step * g + 4));
+      in.d[2 * g] = ld<NT>((const u32x4 *)(xb + step * g));
+      in.d[2 * g + 1] = ld<NT>((const u32x4 *)(xb + step * g + 4));
     }
   }
 }
@@ -193,13 +213,13 @@ __device__ __forceinline__ void load_compress_in(CompressIn<B, F32IN> &in, const
   if constexpr (!F32IN) {
     const uint16_t *xb = (const uint16_t *)xin + blk * B + 8 * j;
 #pragma unroll
-    for (int g = 0; g < G; ++g) in.d[g] = ld_stream((const u32x4 *)(xb + RS * g));
+    for (int g = 0; g < G; ++g) in.d[g] = ld<true>((const u32x4 *)(xb + RS * g));
   } else {
     const float *xb = (const float *)xin + blk * B + 8 * j;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      in.d[2 * g] = ld_stream((const u32x4 *)(xb + RS * g));
-      in.d[2 * g + 1] = ld_stream((const u32x4 *)(xb + RS * g + 4));
+      in.d[2 * g] = ld<true>((const u32x4 *)(xb + RS * g));
+      in.d[2 * g + 1] = ld<true>((const u32x4 *)(xb + RS * g + 4));
     }
   }
 }
@@ -211,7 +231,9 @@ __device__ __forceinline__ void load_compress_in(CompressIn<B, F32IN> &in, const
 // line and each store wrote 32 bytes, and compress ran at 67% of HBM peak against 81%.)
 constexpr int compress_blocks_per_group(int B) { return B == 64 ? 2 : 1; }
 
-template <int B, bool F32IN, int FLAGS>
+// MODE: kTilePlain, kTileStream or kLoopStream (above); in the one-tile modes the launch has a
+// wavefront for every tile (the host checks).
+template <int B, bool F32IN, int FLAGS, int MODE>
 __global__ __launch_bounds__(kThreads) void k_compress(const void *__restrict__ xin, int64_t nb,
                                                        float TBB, float sqrtTB, float C,
                                                        float invC, uint8_t *__restrict__ codes,
@@ -227,6 +249,7 @@ __global__ __launch_bounds__(kThreads) void k_compress(const void *__restrict__ 
   constexpr int NB = N / BG;                            // a block's registers in a lane
   static_assert(CompressIn<B, F32IN>::kRuns == G, "compress input layout");
   constexpr bool ROT = !(FLAGS & kNoRotation);
+  constexpr bool NT = mode_nt(MODE), LOOP = mode_loop(MODE);
   constexpr float Q = qmax_of<FLAGS>();
   const int lane = threadIdx.x & 63;
   const int j = lane & (L - 1);
@@ -256,14 +279,15 @@ __global__ __launch_bounds__(kThreads) void k_compress(const void *__restrict__ 
     return (nb - 1 - t * BPW) > BG * bw ? (uint32_t)B : 0u;
   };
   CompressIn<B, F32IN> cur;
-  if (wave < ntiles) load_compress_at<B, F32IN>(cur, tile_in(wave), lane_in(wave), run_step(wave));
+  if (wave < ntiles)
+    load_compress_at<NT, B, F32IN>(cur, tile_in(wave), lane_in(wave), run_step(wave));
 
   for (int64_t tile = wave; tile < ntiles; tile += nwaves) {
     const int64_t blk0 = tile * BPW;  // first block of the tile (wave-uniform)
     CompressIn<B, F32IN> nxt;
-    if (tile + nwaves < ntiles)
-      load_compress_at<B, F32IN>(nxt, tile_in(tile + nwaves), lane_in(tile + nwaves),
-                                 run_step(tile + nwaves));
+    if (LOOP && tile + nwaves < ntiles)
+      load_compress_at<NT, B, F32IN>(nxt, tile_in(tile + nwaves), lane_in(tile + nwaves),
+                                     run_step(tile + nwaves));
 
     // Widen, energy and the first butterfly stages.  Blocks past the last one work on a copy
     // of the last block and store nothing.
@@ -356,7 +380,7 @@ __global__ __launch_bounds__(kThreads) void k_compress(const void *__restrict__ 
           u32x2 w;
           w[0] = encode4<FLAGS>(v[8 * g + 0], v[8 * g + 1], v[8 * g + 2], v[8 * g + 3], cm);
           w[1] = encode4<FLAGS>(v[8 * g + 4], v[8 * g + 5], v[8 * g + 6], v[8 * g + 7], cm);
-          st_stream(w, (u32x2 *)(cb + co + RS * g));
+          st<NT>(w, (u32x2 *)(cb + co + RS * g));
         }
         if (j == 0) {
           alpha_out[blk] = alpha;
@@ -364,6 +388,7 @@ __global__ __launch_bounds__(kThreads) void k_compress(const void *__restrict__ 
         }
       }
     }
+    if constexpr (!LOOP) break;
     cur = nxt;
   }
 }
@@ -382,19 +407,20 @@ struct DecompressIn {
   float s, a;
 };
 
-template <int B>
+template <bool NT, int B>
 __device__ __forceinline__ void load_decompress_in(DecompressIn<B> &in, const uint8_t *codes,
                                                    const float *alpha, const float *scale,
                                                    int64_t blk, int j) {
   constexpr int RS = 8 * decompress_lanes(B);
   const uint8_t *cb = codes + blk * B + 8 * j;
 #pragma unroll
-  for (int g = 0; g < B / RS; ++g) in.d[g] = ld_stream((const u32x2 *)(cb + RS * g));
+  for (int g = 0; g < B / RS; ++g) in.d[g] = ld<NT>((const u32x2 *)(cb + RS * g));
   in.s = scale[blk];
   in.a = alpha[blk];
 }
 
-template <int B, bool F32OUT, int FLAGS>
+// MODE as for k_compress.
+template <int B, bool F32OUT, int FLAGS, int MODE>
 __global__ __launch_bounds__(kThreads) void k_decompress(const uint8_t *__restrict__ codes,
                                                          const float *__restrict__ alpha,
                                                          const float *__restrict__ scale,
@@ -406,6 +432,7 @@ __global__ __launch_bounds__(kThreads) void k_decompress(const uint8_t *__restri
   constexpr int N = B / L;
   constexpr int G = N / 8;
   constexpr bool ROT = !(FLAGS & kNoRotation);
+  constexpr bool NT = mode_nt(MODE), LOOP = mode_loop(MODE);
   const int lane = threadIdx.x & 63;
   const int j = lane & (L - 1);
   const int bw = lane / L;
@@ -417,14 +444,15 @@ __global__ __launch_bounds__(kThreads) void k_decompress(const uint8_t *__restri
 
   DecompressIn<B> cur;  // groups past the last block re-read the last block, store nothing
   if (wave < ntiles)
-    load_decompress_in<B>(cur, codes, alpha, scale, min(wave * BPW + bw, nb - 1), j);
+    load_decompress_in<NT, B>(cur, codes, alpha, scale, min(wave * BPW + bw, nb - 1), j);
 
   for (int64_t tile = wave; tile < ntiles; tile += nwaves) {
     const int64_t blk = tile * BPW + bw;
     const bool active = blk < nb;
     DecompressIn<B> nxt;
-    if (tile + nwaves < ntiles)
-      load_decompress_in<B>(nxt, codes, alpha, scale, min((tile + nwaves) * BPW + bw, nb - 1), j);
+    if (LOOP && tile + nwaves < ntiles)
+      load_decompress_in<NT, B>(nxt, codes, alpha, scale, min((tile + nwaves) * BPW + bw, nb - 1),
+                                j);
 
     float v[N];
 #pragma unroll
@@ -493,8 +521,8 @@ __global__ __launch_bounds__(kThreads) void k_decompress(const uint8_t *__restri
             w0[q] = __float_as_uint(fmaf(v[8 * g + q], f, 0.0f) * ra);
             w1[q] = __float_as_uint(fmaf(v[8 * g + 4 + q], f, 0.0f) * ra);
           }
-          st_stream(w0, (u32x4 *)(ob + RS * g));
-          st_stream(w1, (u32x4 *)(ob + RS * g + 4));
+          st<NT>(w0, (u32x4 *)(ob + RS * g));
+          st<NT>(w1, (u32x4 *)(ob + RS * g + 4));
         }
       } else {
         __bf16 *ob = (__bf16 *)out + blk * B + 8 * pj;
@@ -508,20 +536,23 @@ __global__ __launch_bounds__(kThreads) void k_decompress(const uint8_t *__restri
             w[q] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
                    ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
           }
-          st_stream(w, (u32x4 *)(ob + RS * g));
+          st<NT>(w, (u32x4 *)(ob + RS * g));
         }
       }
     }
+    if constexpr (!LOOP) break;
     cur = nxt;
   }
 }
 
 // --------------------------------------------------------------------------------------------
-// K3: reduce.  B/16 lanes per block, 16 consecutive codes per lane (one 16-byte load per
-// contribution), no Hadamard.  PB > 0: exactly PB contributions, all loads issued before any
+// K3: reduce.  E = 16 consecutive codes per lane (one 16-byte load per contribution), B/E lanes
+// per block, no Hadamard.  PB > 0: exactly PB contributions, all loads issued before any
 // arithmetic; PB = 0: any P, in chunks of 8.  Contribution p's codes start at codes + p cstride
 // and its scales at alpha + p astride, scale + p sstride (cstride = n, astride = sstride = nb
-// for contiguous stacks).
+// for contiguous stacks).  (8 codes per lane, which halves the registers and allows eight
+// wavefronts per SIMD instead of five, measured 2-11% slower.)
+constexpr int kReduceElems = 16;
 
 template <int B, int PB, int FLAGS>
 __global__ __launch_bounds__(kThreads) void k_reduce(const uint8_t *__restrict__ codes,
@@ -532,7 +563,10 @@ __global__ __launch_bounds__(kThreads) void k_reduce(const uint8_t *__restrict__
                                                      uint8_t *__restrict__ codes_out,
                                                      float *__restrict__ alpha_out,
                                                      float *__restrict__ scale_out) {
-  constexpr int L = B / 16;    // lanes per block
+  constexpr int E = kReduceElems;  // codes per lane
+  constexpr int NQ = E / 4;        // dwords per lane
+  using CodesT = u32x4;
+  constexpr int L = B / E;     // lanes per block
   constexpr int BPW = 64 / L;  // blocks per wavefront
   constexpr int CH = PB > 0 ? PB : 8;  // contributions loaded together
   // low bits of g cleared so that g times a code value is exact in float64: E4M3 values have
@@ -550,7 +584,7 @@ __global__ __launch_bounds__(kThreads) void k_reduce(const uint8_t *__restrict__
     const int64_t blk = tile * BPW + bw;
     const bool active = blk < nb;
     const int64_t cblk = active ? blk : nb - 1;  // groups past the end re-read the last block
-    const uint8_t *cb = codes + cblk * B + 16 * j;
+    const uint8_t *cb = codes + cblk * B + E * j;
 
     // r = sum_p g_p dec(q_p) with g_p = s_p / alpha_p, accumulated in float64.  g_p is cut to
     // 49 significant bits (46 for INT8 codes; a relative change below 2^-45), so that its
@@ -558,14 +592,14 @@ __global__ __launch_bounds__(kThreads) void k_reduce(const uint8_t *__restrict__
     // the running sum, each within 2^-53 of it.  Contributions that largely cancel therefore
     // still requantise like the exact sum, and a contribution and its exact negation cancel
     // to exactly zero.  A zero block (s_p = 0) contributes exact zeros.
-    double r64[16];
+    double r64[E];
     for (int p0 = 0; p0 < P; p0 += CH) {
-      u32x4 d[CH];
+      CodesT d[CH];
       float sp[CH], ap[CH];
 #pragma unroll
       for (int c = 0; c < CH; ++c)
         if (PB > 0 || p0 + c < P) {
-          d[c] = ld_stream((const u32x4 *)(cb + (int64_t)(p0 + c) * cstride));
+          d[c] = ld<true>((const CodesT *)(cb + (int64_t)(p0 + c) * cstride));
           sp[c] = scale[(int64_t)(p0 + c) * sstride + cblk];
           ap[c] = alpha[(int64_t)(p0 + c) * astride + cblk];
         }
@@ -579,7 +613,7 @@ __global__ __launch_bounds__(kThreads) void k_reduce(const uint8_t *__restrict__
           ri = fma(ri, fma(-ad, ri, 1.0), ri);
           const double g = __longlong_as_double(__double_as_longlong((double)sp[c] * ri) & kGMask);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
+          for (int q = 0; q < NQ; ++q) {
             float a0, a1, a2, a3;
             decode4<FLAGS>(d[c][q], a0, a1, a2, a3);
             if (p0 + c == 0) {
@@ -598,44 +632,43 @@ __global__ __launch_bounds__(kThreads) void k_reduce(const uint8_t *__restrict__
       }
     }
 
-    float r[16];
+    float r[E];
     float m = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < E; ++i) {
       r[i] = (float)r64[i];
       m = fmaxf(m, fabsf(r[i]));
     }
     float M = group_max<L>(m);
-    int E = 0;
+    int E2 = 0;  // the true sum is r * 2^E2
     if (M != 0.0f && !(M >= 0x1p-100f && M <= 0x1p100f)) {
       // Tiny or huge sum (bfloat16-subnormal blocks, or contributions that cancelled):
       // rescale the float64 sum so that its largest magnitude lies in [1, 2) before rounding
       // it to float32.
       double m64 = 0.0;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) m64 = fmax(m64, fabs(r64[i]));
+      for (int i = 0; i < E; ++i) m64 = fmax(m64, fabs(r64[i]));
       const int e64 = __builtin_amdgcn_frexp_exp(m64);
       const int k = 1 - group_max_i<L>(e64);
       m = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
+      for (int i = 0; i < E; ++i) {
         r[i] = (float)__builtin_amdgcn_ldexp(r64[i], k);
         m = fmaxf(m, fabsf(r[i]));
       }
       M = group_max<L>(m);
-      E -= k;
+      E2 -= k;
     }
 
-    // the true sum is r * 2^E
     float cm, a_out, s_out;
     constexpr float Q = qmax_of<FLAGS>();
-    scales_exact<L, 16>(r, M, E, TB, Q, Q, 1.0f, cm, a_out, s_out);
+    scales_exact<L, E>(r, M, E2, TB, Q, Q, 1.0f, cm, a_out, s_out);
     if (active) {
-      u32x4 w;
+      CodesT w;
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
+      for (int q = 0; q < NQ; ++q)
         w[q] = encode4<FLAGS>(r[4 * q], r[4 * q + 1], r[4 * q + 2], r[4 * q + 3], cm);
-      st_stream(w, (u32x4 *)(codes_out + blk * B + 16 * j));
+      st<true>(w, (CodesT *)(codes_out + blk * B + E * j));
       if (j == 0) {
         alpha_out[blk] = a_out;
         scale_out[blk] = s_out;
@@ -793,7 +826,7 @@ __global__ __launch_bounds__(kThreads) void k_accumulate(
           u32x2 w;
           w[0] = encode4<FLAGS>(v[8 * g + 0], v[8 * g + 1], v[8 * g + 2], v[8 * g + 3], cm);
           w[1] = encode4<FLAGS>(v[8 * g + 4], v[8 * g + 5], v[8 * g + 6], v[8 * g + 7], cm);
-          st_stream(w, (u32x2 *)(cb + RS * g));
+          st<true>(w, (u32x2 *)(cb + RS * g));
         }
         if (j == 0) {
           alpha_out[blk] = a_out;
@@ -1017,7 +1050,7 @@ __global__ __launch_bounds__(kThreads) void k_accumulate_fix(
 #define TFP8_DECOMPRESS_WGS_PER_CU 0
 #endif
 #ifndef TFP8_REDUCE_WGS_PER_CU
-#define TFP8_REDUCE_WGS_PER_CU 32
+#define TFP8_REDUCE_WGS_PER_CU 0
 #endif
 #ifndef TFP8_ACCUMULATE_FIX_WGS_PER_CU
 #define TFP8_ACCUMULATE_FIX_WGS_PER_CU 0
@@ -1046,10 +1079,11 @@ bool target_ok(float t) {
 }
 
 // Workgroups for a launch with one wavefront per tile, capped at `per_cu` workgroups per
-// compute unit (0: no cap) beyond which the wavefronts loop over tiles.  Measured on MI355X:
-// compress and decompress stream fastest with one tile per wavefront and no loop (the
-// hardware keeps the CUs fed as wavefronts retire); the reduce, whose wavefronts each carry
-// P loads in flight, is fastest with 32 workgroups per CU.
+// compute unit (0: no cap) beyond which the wavefronts loop over tiles.  Measured on MI355X with
+// the caches flushed before each launch: compress, decompress and the reduce all stream fastest
+// with one tile per wavefront and no loop (the hardware keeps the CUs fed as wavefronts retire);
+// caps of 2-32 workgroups per CU with prefetching loops were 1-16% slower on 34-940 M-element
+// inputs (the reduce at one rank's share was equal, its full-tensor call 5% slower at 32).
 int cu_count() {
   // compute units of the current device, looked up once per device (any thread may race to
   // fill an entry; they all store the same value)
@@ -1072,8 +1106,9 @@ int cu_count() {
 // 1.9 to 4.3 GB.  At 1.1 GB the two shapes tie, and on inputs of 134-268 MB the remapped one is
 // 3-10% slower, hence the threshold.  At B = 64, whose lane groups now read whole lines as at
 // B = 128, the remapped shape is 1% faster on 1.9 GB.  Decompress and the reduce were slower
-// remapped.
-constexpr int64_t kCompressRemapMinBytes = (int64_t)3 << 29;  // 1.5 GiB of input
+// remapped.  The same size splits the cache hints of compress (its input) and decompress (its
+// output): plain below it, non-temporal from it on (launch modes above).
+constexpr int64_t kStreamMinBytes = (int64_t)3 << 29;  // 1.5 GiB
 
 // The cap without `per_cu` keeps gridDim.x * nt (the work-items of the launch, a 32-bit count
 // in the dispatch packet) at 2^30; larger inputs loop.  Under the XCD remap the count is
@@ -1118,11 +1153,18 @@ tfp8_status launch_compress_t(const void *x, int64_t nb, float target, uint8_t *
   constexpr int BPW = 64 / 8 * compress_blocks_per_group(B);  // blocks per tile
   // Large inputs stream faster with one wavefront per workgroup and each XCD on a contiguous
   // eighth of the tiles; smaller ones with 4 wavefronts per workgroup in dispatch order.
-  const bool remap = nb * B * (F32 ? 4 : 2) >= kCompressRemapMinBytes;
+  const bool remap = nb * B * (F32 ? 4 : 2) >= kStreamMinBytes;
   const int nt = remap ? 64 : kThreads;
-  const unsigned grid = grid_for((nb + BPW - 1) / BPW, TFP8_COMPRESS_WGS_PER_CU, nt, remap);
-  return launch(k_compress<B, F32, FLAGS>, grid, nt, st, x, nb, TBB, sqrtTB, C, invC, codes,
-                alpha, scale, nt / 64, remap);
+  const int64_t tiles = (nb + BPW - 1) / BPW;
+  const unsigned grid = grid_for(tiles, TFP8_COMPRESS_WGS_PER_CU, nt, remap);
+  if ((int64_t)grid * (nt / 64) < tiles)  // capped launch: wavefronts loop over tiles
+    return launch(k_compress<B, F32, FLAGS, kLoopStream>, grid, nt, st, x, nb, TBB, sqrtTB, C,
+                  invC, codes, alpha, scale, nt / 64, remap);
+  if (remap)
+    return launch(k_compress<B, F32, FLAGS, kTileStream>, grid, nt, st, x, nb, TBB, sqrtTB, C,
+                  invC, codes, alpha, scale, nt / 64, remap);
+  return launch(k_compress<B, F32, FLAGS, kTilePlain>, grid, nt, st, x, nb, TBB, sqrtTB, C, invC,
+                codes, alpha, scale, nt / 64, remap);
 }
 
 template <int B, bool F32>
@@ -1145,9 +1187,16 @@ tfp8_status launch_decompress_t(const uint8_t *codes, const float *alpha, const 
   constexpr bool ROT = !(FLAGS & kNoRotation);
   const float inv_sqrt_b = ROT ? (float)(1.0 / sqrt((double)B)) : 1.0f;
   constexpr int BPW = 64 / decompress_lanes(B);  // blocks per tile
-  const unsigned grid = grid_for((nb + BPW - 1) / BPW, TFP8_DECOMPRESS_WGS_PER_CU);
-  return launch(k_decompress<B, F32, FLAGS>, grid, kThreads, st, codes, alpha, scale, nb,
-                inv_sqrt_b, out);
+  const int64_t tiles = (nb + BPW - 1) / BPW;
+  const unsigned grid = grid_for(tiles, TFP8_DECOMPRESS_WGS_PER_CU);
+  if ((int64_t)grid * (kThreads / 64) < tiles)  // capped launch: wavefronts loop over tiles
+    return launch(k_decompress<B, F32, FLAGS, kLoopStream>, grid, kThreads, st, codes, alpha,
+                  scale, nb, inv_sqrt_b, out);
+  if (nb * B * (F32 ? 4 : 2) >= kStreamMinBytes)
+    return launch(k_decompress<B, F32, FLAGS, kTileStream>, grid, kThreads, st, codes, alpha,
+                  scale, nb, inv_sqrt_b, out);
+  return launch(k_decompress<B, F32, FLAGS, kTilePlain>, grid, kThreads, st, codes, alpha, scale,
+                nb, inv_sqrt_b, out);
 }
 
 template <int B, bool F32>
@@ -1171,7 +1220,7 @@ tfp8_status launch_reduce_t(const uint8_t *codes, const float *alpha, const floa
   // the reduce works on r = sum_p g_p dec(q_p) directly, with or without the rotation: its
   // energy is that of the sum, sum(r^2) = sum(z^2)
   const float TB = target * (float)B;
-  constexpr int BPW = 64 / (B / 16);
+  constexpr int BPW = 64 / (B / kReduceElems);
   const unsigned grid = grid_for((nb + BPW - 1) / BPW, TFP8_REDUCE_WGS_PER_CU);
 #define TFP8_LAUNCH_REDUCE(PB)                                                               \
   return launch(k_reduce<B, PB, FLAGS>, grid, kThreads, st, codes, alpha, scale, P, cstride,    \
