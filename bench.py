@@ -176,8 +176,17 @@ def cpu_model() -> str:
 
 
 def all_workloads(reps: int):
-    """Every operation on every workload, warm and with the caches flushed, beside a
-    same-shape copy; one JSON object on stdout, a table on stderr."""
+    """Every operation on every workload, three ways: warm, flushed, and rotating (see below),
+    beside same-byte references; one JSON object on stdout, a table on stderr.
+
+    warm      one launch at a time, back to back on the same buffers, a synchronisation each.
+    flushed   one launch at a time with a 1 GiB read between launches (evicts the L2 and the
+              256 MB MALL).  Plain stores can look fast here: their output waits in the MALL
+              and its write to HBM falls into the next flush, outside the launch.
+    rotating  back-to-back launches that cycle through distinct buffer sets (inputs and
+              outputs) totalling at least 3 GiB (at most 256 sets), timed over whole cycles:
+              nothing stays cached between a set's uses and every write-back is paid inside
+              the sequence.  The steady-state rate of a stream of such calls."""
     import statistics
 
     import numpy as np
@@ -194,18 +203,23 @@ def all_workloads(reps: int):
 
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
     flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB, > L2 + MALL
+    rot_bytes = 3 << 30
 
     def check(st):
         if st != 0:
             raise RuntimeError(tfp8.status_string(st))
+
+    def event():
+        return torch.cuda.Event(enable_timing=True)
 
     def timed(fn, flushed):
         ts = []
         for i in range(reps + 3):
             if flushed:
                 flush.sum()  # reads 1 GiB: evicts the caches without leaving dirty lines
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a, b = event(), event()
             a.record(stream)
             fn()
             b.record(stream)
@@ -214,142 +228,213 @@ def all_workloads(reps: int):
                 ts.append(a.elapsed_time(b) * 1e3)
         return statistics.median(ts), min(ts)
 
+    def rotating(setup, set_bytes):
+        # setup(i) -> launch closure on buffer set i (set 0: the case's own buffers); at most
+        # 256 sets (the small workloads: still more than 1.5x the 256 MB MALL)
+        R = min(256, max(2, -(-rot_bytes // int(set_bytes))))
+        fns = [setup(i) for i in range(R)]
+        # settle: cycle for 0.4 s first, so the timed cycles run at the loaded clock level (right
+        # after the single-launch protocols the clocks are measurably lower)
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 0.4:
+            for f in fns:
+                f()
+            torch.cuda.synchronize()
+        ts = []
+        for _ in range(5):
+            a, b = event(), event()
+            a.record(stream)
+            for k in range(4 * R):
+                fns[k % R]()
+            b.record(stream)
+            b.synchronize()
+            ts.append(a.elapsed_time(b) * 1e3 / (4 * R))
+        del fns
+        torch.cuda.empty_cache()
+        return statistics.median(ts), R
+
     rows = []
 
-    def measure(key, op, fn, alg_bytes, elements, B, P, bf16_in=None, ref=None):
+    def gbps(nbytes, us):
+        return nbytes / (us * 1e-6) / 1e9
+
+    def measure(key, op, setup, alg_bytes, set_bytes, elements, B, P, bf16_in=None, ref=None,
+                rotate=True):
+        fn = setup(0)
         wm, wn = timed(fn, False)
         fm, fn_ = timed(fn, True)
         row = {"workload": key, "op": op, "elements": elements, "block": B, "P": P,
                "bytes_algorithmic": int(alg_bytes), "warm_us_median": round(wm, 2),
                "warm_us_min": round(wn, 2), "flushed_us_median": round(fm, 2),
                "flushed_us_min": round(fn_, 2),
-               "flushed_GBps": round(alg_bytes / (fm * 1e-6) / 1e9, 1),
-               "flushed_frac_of_peak": round(alg_bytes / (fm * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+               "flushed_GBps": round(gbps(alg_bytes, fm), 1),
+               "flushed_frac_of_peak": round(gbps(alg_bytes, fm) / HBM_PEAK_GBS, 4)}
+        if rotate:
+            rm, R = rotating(setup, set_bytes)
+            row.update({"rotating_us": round(rm, 2), "rotating_sets": R,
+                        "rotating_GBps": round(gbps(alg_bytes, rm), 1),
+                        "rotating_frac_of_peak": round(gbps(alg_bytes, rm) / HBM_PEAK_GBS, 4)})
         if bf16_in is not None:
-            row["bf16_in_GBps_flushed"] = round(bf16_in / (fm * 1e-6) / 1e9, 1)
+            row["bf16_in_GBps_flushed"] = round(gbps(bf16_in, fm), 1)
         if ref is not None:
-            rfn, rbytes, rname = ref
-            rm, _ = timed(rfn, True)
-            row["ref"] = rname
-            row["ref_bytes"] = int(rbytes)
-            row["ref_flushed_us_median"] = round(rm, 2)
-            row["ref_GBps_flushed"] = round(rbytes / (rm * 1e-6) / 1e9, 1)
-            row["ratio_to_ref"] = round(row["flushed_GBps"] / row["ref_GBps_flushed"], 4)
+            rsetup, rbytes, rname = ref
+            rfm, _ = timed(rsetup(0), True)
+            row.update({"ref": rname, "ref_bytes": int(rbytes), "ref_flushed_us_median": round(rfm, 2),
+                        "ref_GBps_flushed": round(gbps(rbytes, rfm), 1)})
+            row["ratio_to_ref_flushed"] = round(row["flushed_GBps"] / row["ref_GBps_flushed"], 4)
+            if rotate:
+                rrm, _ = rotating(rsetup, rbytes)
+                row.update({"ref_rotating_us": round(rrm, 2),
+                            "ref_GBps_rotating": round(gbps(rbytes, rrm), 1)})
+                row["ratio_to_ref_rotating"] = round(row["rotating_GBps"] / row["ref_GBps_rotating"],
+                                                     4)
         rows.append(row)
-        log(f"{key:15s} {op:28s} n={elements:>10d} B={B} P={P}: warm {wm:9.1f} us, flushed "
-            f"{fm:9.1f} us = {row['flushed_GBps']:7.1f} GB/s ({100 * row['flushed_frac_of_peak']:.1f}%)"
-            + (f", vs {row['ref']} {row['ref_GBps_flushed']:.0f} GB/s: {row['ratio_to_ref']:.3f}"
+        log(f"{key:15s} {op:44s} n={elements:>10d} B={B} P={P}: warm {wm:8.1f}, flushed {fm:8.1f} us "
+            f"({100 * row['flushed_frac_of_peak']:.1f}%)"
+            + (f", rotating {row['rotating_us']:8.1f} us ({100 * row['rotating_frac_of_peak']:.1f}%)"
+               if rotate else "")
+            + (f"; {row['ref']}: flushed {row['ref_flushed_us_median']:.1f} us"
+               + (f", rotating {row['ref_rotating_us']:.1f} us" if rotate else "")
                if ref is not None else ""))
+
+    def own(t, i):  # set 0 uses the tensor itself, other sets a copy of it
+        return t if i == 0 else t.clone()
 
     for key, wl in WORKLOADS.items():
         B, P, n = wl.block, wl.shards, wl.n
         nb = n // B
         xs = host[key]
         x = torch.from_numpy(xs.reshape(-1).view(np.int16)).to(dev)
-        xb = x.view(torch.bfloat16)
         ntot = P * n
-        q = torch.empty(max(ntot, n), dtype=torch.uint8, device=dev)
-        al = torch.empty(max(ntot, n) // B, dtype=torch.float32, device=dev)
-        sc = torch.empty_like(al)
-        y8 = torch.empty(ntot, dtype=torch.uint8, device=dev)
 
-        def comp(m):
-            return lambda: check(tfp8.compress_raw(xb.data_ptr(), tfp8.BF16, m, B, TARGET,
-                                                   q.data_ptr(), al.data_ptr(), sc.data_ptr(),
-                                                   stream.cuda_stream))
+        def compress_setup(m):
+            def setup(i):
+                xi = own(x[:m], i)
+                q = torch.empty(m, dtype=torch.uint8, device=dev)
+                a = torch.empty(m // B, dtype=torch.float32, device=dev)
+                s_ = torch.empty_like(a)
+                return lambda: check(tfp8.compress_raw(xi.data_ptr(), tfp8.BF16, m, B, TARGET,
+                                                       q.data_ptr(), a.data_ptr(), s_.data_ptr(),
+                                                       sh))
+            return setup
 
         # Same-byte references, torch kernels that move the operation's bytes with no other
         # work: compress reads 2 bytes and writes 1 per element, as an element-wise maximum of
         # the two halves of the input's bytes (uint8) does; the reduce reads P bytes and writes
         # 1, as a maximum over P uint8 rows does.  (torch's dtype-converting copies are not
         # vectorised and reach only ~2 TB/s, so they bound nothing.)
-        x8 = x.view(torch.uint8)
+        def narrow_ref(m):
+            def setup(i):
+                x8 = own(x[:m], i).view(torch.uint8)
+                y8 = torch.empty(m, dtype=torch.uint8, device=dev)
+                return lambda: torch.maximum(x8[:m], x8[m:2 * m], out=y8)
+            return setup, 3 * m, "uint8 max of two halves"
 
-        def narrow(m):
-            return ((lambda: torch.maximum(x8[:m], x8[m:2 * m], out=y8[:m])), 3 * m,
-                    "uint8 max of two halves")
-
-        measure(key, "compress", comp(n), n * (3 + 8 / B), n, B, 1, 2 * n, narrow(n))
+        measure(key, "compress", compress_setup(n), n * (3 + 8 / B), 3 * n, n, B, 1, 2 * n,
+                narrow_ref(n))
         if P > 1:
-            measure(key, f"compress {P} stacked shards", comp(ntot), ntot * (3 + 8 / B), ntot, B,
-                    P, 2 * ntot, narrow(ntot))
-        comp(ntot)()  # codes of every shard, for the stages below
-        for dt, name, ob in ((torch.bfloat16, "decompress bf16", 2), (torch.float32,
-                                                                      "decompress fp32", 4)):
-            out = torch.empty(n, dtype=dt, device=dev)
+            measure(key, f"compress {P} stacked shards", compress_setup(ntot), ntot * (3 + 8 / B),
+                    3 * ntot, ntot, B, P, 2 * ntot, narrow_ref(ntot))
+        # codes of every shard, for the stages below
+        q = torch.empty(ntot, dtype=torch.uint8, device=dev)
+        al = torch.empty(ntot // B, dtype=torch.float32, device=dev)
+        sc = torch.empty_like(al)
+        check(tfp8.compress_raw(x.data_ptr(), tfp8.BF16, ntot, B, TARGET, q.data_ptr(),
+                                al.data_ptr(), sc.data_ptr(), sh))
+        for dt, name, ob in ((torch.bfloat16, "decompress bf16", 2),
+                             (torch.float32, "decompress fp32", 4)):
             code = tfp8.BF16 if dt == torch.bfloat16 else tfp8.F32
-            fn = (lambda out=out, code=code: check(tfp8.decompress_raw(
-                q.data_ptr(), al.data_ptr(), sc.data_ptr(), n, B, out.data_ptr(), code,
-                stream.cuda_stream)))
-            measure(key, name, fn, n * (1 + 8 / B + ob), n, B, 1)
-            del out
+
+            def setup(i, dt=dt, code=code):
+                qi, ai, si = own(q[:n], i), own(al[:nb], i), own(sc[:nb], i)
+                out = torch.empty(n, dtype=dt, device=dev)
+                return lambda: check(tfp8.decompress_raw(qi.data_ptr(), ai.data_ptr(),
+                                                         si.data_ptr(), n, B, out.data_ptr(), code,
+                                                         sh))
+            measure(key, name, setup, n * (1 + 8 / B + ob), n * (1 + ob), n, B, 1)
         if P > 1:
-            rq = torch.empty(n, dtype=torch.uint8, device=dev)
-            ra = torch.empty(nb, dtype=torch.float32, device=dev)
-            rs = torch.empty_like(ra)
-            fn = lambda: check(tfp8.reduce_fp8_raw(q.data_ptr(), al.data_ptr(), sc.data_ptr(), P,
-                                                   n, B, TARGET, rq.data_ptr(), ra.data_ptr(),
-                                                   rs.data_ptr(), stream.cuda_stream))
-            rows_q = q[:ntot].view(P, n)
-            mx = (lambda: torch.amax(rows_q, dim=0, out=y8[:n])), (P + 1) * n, f"max of {P} uint8 rows"
-            measure(key, f"reduce P={P}, {P} x n", fn, (P + 1) * n * (1 + 8 / B), n, B, P, ref=mx)
-            # one rank's share in a P-way reduce-scatter: chunk 0 of every shard, n/P each
+            def reduce_setup(c, stacked):
+                # P contributions of c codes each: the whole shards (c = n) or chunk 0 of each
+                # shard, one rank's share in a P-way reduce-scatter (c = n / P), contiguous
+                cb = c // B
+
+                def setup(i):
+                    qi = q.view(P, n)[:, :c].contiguous() if (i > 0 or not stacked) else q
+                    ai = al.view(P, nb)[:, :cb].contiguous() if (i > 0 or not stacked) else al
+                    si = sc.view(P, nb)[:, :cb].contiguous() if (i > 0 or not stacked) else sc
+                    oq = torch.empty(c, dtype=torch.uint8, device=dev)
+                    oa = torch.empty(cb, dtype=torch.float32, device=dev)
+                    os_ = torch.empty_like(oa)
+                    return lambda: check(tfp8.reduce_fp8_raw(qi.data_ptr(), ai.data_ptr(),
+                                                             si.data_ptr(), P, c, B, TARGET,
+                                                             oq.data_ptr(), oa.data_ptr(),
+                                                             os_.data_ptr(), sh))
+                return setup
+
+            def rows_ref(c):
+                def setup(i):
+                    rows_q = q.view(P, n)[:, :c] if c == n and i == 0 else \
+                        q.view(P, n)[:, :c].contiguous()
+                    y8 = torch.empty(c, dtype=torch.uint8, device=dev)
+                    return lambda: torch.amax(rows_q, dim=0, out=y8)
+                return setup, (P + 1) * c, f"max of {P} uint8 rows"
+
+            measure(key, f"reduce P={P}, {P} x n", reduce_setup(n, True),
+                    (P + 1) * n * (1 + 8 / B), (P + 1) * n, n, B, P, ref=rows_ref(n))
             c = n // P
-            cq = q[:ntot].view(P, n)[:, :c].contiguous()
-            ca = al[:ntot // B].view(P, nb)[:, :c // B].contiguous()
-            cs = sc[:ntot // B].view(P, nb)[:, :c // B].contiguous()
-            fn = lambda: check(tfp8.reduce_fp8_raw(cq.data_ptr(), ca.data_ptr(), cs.data_ptr(), P,
-                                                   c, B, TARGET, rq.data_ptr(), ra.data_ptr(),
-                                                   rs.data_ptr(), stream.cuda_stream))
-            mxc = ((lambda: torch.amax(cq, dim=0, out=y8[:c])), (P + 1) * c,
-                   f"max of {P} uint8 rows")
-            measure(key, f"reduce P={P}, {P} x n/{P} (one rank)", fn, (P + 1) * c * (1 + 8 / B),
-                    c, B, P, ref=mxc)
+            measure(key, f"reduce P={P}, {P} x n/{P} (one rank)", reduce_setup(c, False),
+                    (P + 1) * c * (1 + 8 / B), (P + 1) * c, c, B, P, ref=rows_ref(c))
             # the same share read in place from the stacked shards (row stride n), and from one
             # buffer of [codes | alpha | scale] messages, one per peer, as one all-to-all would
-            # leave them, packed and with 65 KiB between messages
-            vq, va, vs = q[:ntot].view(P, n), al[:ntot // B].view(P, nb), sc[:ntot // B].view(P, nb)
-            fn = lambda: check(tfp8.reduce_strided_raw(vq.data_ptr(), n, va.data_ptr(), nb,
-                                                       vs.data_ptr(), nb, P, c, B, TARGET,
+            # leave them, packed and with 65 KiB between messages (warm and flushed only)
+            rq = torch.empty(c, dtype=torch.uint8, device=dev)
+            ra = torch.empty(c // B, dtype=torch.float32, device=dev)
+            rs = torch.empty_like(ra)
+            fn = lambda: check(tfp8.reduce_strided_raw(q.data_ptr(), n, al.data_ptr(), nb,
+                                                       sc.data_ptr(), nb, P, c, B, TARGET,
                                                        rq.data_ptr(), ra.data_ptr(), rs.data_ptr(),
-                                                       stream.cuda_stream))
-            measure(key, f"reduce P={P}, {P} x n/{P} in place (stride n)", fn,
-                    (P + 1) * c * (1 + 8 / B), c, B, P)
+                                                       sh))
+            measure(key, f"reduce P={P}, {P} x n/{P} in place (stride n)", lambda i: fn,
+                    (P + 1) * c * (1 + 8 / B), 0, c, B, P, rotate=False)
             cb = c // B
             for pad in (0, 65536 + 1024):
                 M = (c + 8 * cb + pad + 15) // 16 * 16
                 msg = torch.zeros(P, M, dtype=torch.uint8, device=dev)
-                msg[:, :c].copy_(cq)
-                msg[:, c:c + 4 * cb].view(torch.float32).copy_(ca)
-                msg[:, c + 4 * cb:c + 8 * cb].view(torch.float32).copy_(cs)
+                msg[:, :c].copy_(q.view(P, n)[:, :c])
+                msg[:, c:c + 4 * cb].view(torch.float32).copy_(al.view(P, nb)[:, :cb])
+                msg[:, c + 4 * cb:c + 8 * cb].view(torch.float32).copy_(sc.view(P, nb)[:, :cb])
                 mp = msg.data_ptr()
                 fn = (lambda mp=mp, M=M: check(tfp8.reduce_strided_raw(
                     mp, M, mp + c, M // 4, mp + c + 4 * cb, M // 4, P, c, B, TARGET,
-                    rq.data_ptr(), ra.data_ptr(), rs.data_ptr(), stream.cuda_stream)))
-                measure(key, f"reduce P={P}, {P} x n/{P} from messages {M} B apart", fn,
-                        (P + 1) * c * (1 + 8 / B), c, B, P)
+                    rq.data_ptr(), ra.data_ptr(), rs.data_ptr(), sh)))
+                measure(key, f"reduce P={P}, {P} x n/{P} from messages {M} B apart",
+                        lambda i, fn=fn: fn, (P + 1) * c * (1 + 8 / B), 0, c, B, P, rotate=False)
                 del msg
-            del rq, ra, rs, cq, ca, cs
+            del rq, ra, rs
         if key == ACC_WORKLOAD:
-            # gradient accumulation: main = compressed shard 0, local = shard 1
-            comp(n)()
-            oq = torch.empty(n, dtype=torch.uint8, device=dev)
-            oa = torch.empty(nb, dtype=torch.float32, device=dev)
-            os_ = torch.empty_like(oa)
-            fn = lambda: check(tfp8.accumulate_raw(q.data_ptr(), al.data_ptr(), sc.data_ptr(),
-                                                   xb.data_ptr() + 2 * n, tfp8.BF16, n, B,
-                                                   TARGET, oq.data_ptr(), oa.data_ptr(),
-                                                   os_.data_ptr(), stream.cuda_stream))
-            measure(key, "accumulate (main + local)", fn, n * (4 + 16 / B), n, B, 1)
-            del oq, oa, os_
-        del x, x8, xb, q, al, sc, y8
+            # gradient accumulation: main = compressed shard 0, local = shard 1, out of place
+            g = x[n:2 * n]
+
+            def setup(i):
+                qi, ai, si, gi = own(q[:n], i), own(al[:nb], i), own(sc[:nb], i), own(g, i)
+                oq = torch.empty(n, dtype=torch.uint8, device=dev)
+                oa = torch.empty(nb, dtype=torch.float32, device=dev)
+                os_ = torch.empty_like(oa)
+                return lambda: check(tfp8.accumulate_raw(qi.data_ptr(), ai.data_ptr(),
+                                                         si.data_ptr(), gi.data_ptr(), tfp8.BF16,
+                                                         n, B, TARGET, oq.data_ptr(),
+                                                         oa.data_ptr(), os_.data_ptr(), sh))
+            measure(key, "accumulate (main + local)", setup, n * (4 + 16 / B), 4 * n, n, B, 1)
+        del x, q, al, sc
         torch.cuda.empty_cache()
     print(json.dumps({"mode": "all-workloads", "reps": reps, "peak_GBps": HBM_PEAK_GBS,
-                      "ref": "same-byte torch reference, flushed: compress vs a uint8 maximum of "
-                             "the two halves of the input's bytes (2 bytes read, 1 written per "
-                             "element), reduce vs a maximum over P uint8 rows; ratio_to_ref = "
-                             "GB/s over its GB/s",
-                      "flush": "a 1 GiB read (sum) between launches",
+                      "protocols": {"warm": "single launches back to back on the same buffers",
+                                    "flushed": "a 1 GiB read (sum) between single launches",
+                                    "rotating": "back-to-back launches cycling through distinct "
+                                                "buffer sets of >= 3 GiB in total"},
+                      "ref": "same-byte torch reference: compress vs a uint8 maximum of the two "
+                             "halves of the input's bytes (2 bytes read, 1 written per element), "
+                             "reduce vs a maximum over P uint8 rows; ratio = GB/s over its GB/s",
                       "rows": rows}), flush=True)
 
 

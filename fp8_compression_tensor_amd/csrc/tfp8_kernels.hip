@@ -18,8 +18,8 @@
 //
 // Launch.  One tile (64/L blocks) per wavefront, 8- or 16-byte vector loads and stores per
 // lane, no LDS, no atomics.  Compress of an input of 1.5 GiB or more launches
-// one-wavefront workgroups and gives each XCD a contiguous eighth of the tiles, and from that
-// size on compress and decompress stream with non-temporal hints (kStreamMinBytes below).
+// one-wavefront workgroups and gives each XCD a contiguous eighth of the tiles
+// (kCompressRemapMinBytes below).
 //
 // Transform.  w = H x (unnormalised) is computed by an in-register FWHT over the register
 // bits and a 3-stage DPP butterfly over the lane bits (tfp8_device.hpp), which leaves lane j
@@ -31,9 +31,10 @@
 // computes c = 448 / max|w| and u = w c (the codes' pre-rounding values), takes the energy
 // sum(x^2) straight from the packed input, and sets
 //   alpha = clamp(sqrt(T B / sum(x^2)), 2^-126, 2^126),  s = alpha max|w| / (448 sqrt(B)).
-// Blocks whose max|w| is outside [2^-40, 2^60] (all-zero, bfloat16-subnormal, huge) go through
-// scales_exact, which first multiplies the block by an exact power of two and takes the energy
-// from sum(u^2) = c^2 B sum(x^2) (the rotation preserves energy).
+// For blocks whose max|w| is outside [2^-40, 2^60] compress stores an all-zero block directly
+// and brings a bfloat16-subnormal or huge block into range by an exact power of two, taking the
+// energy from the scaled w (the rotation preserves energy); the reduce and the accumulation use
+// scales_exact, which does the same for sums whose range it cannot bound in advance.
 //
 // Reduce.  Sum of reconstructions z = sum_p H (s_p dec q_p) / (sqrt(B) alpha_p) = H r / sqrt(B)
 // with r = sum_p (s_p / alpha_p) dec(q_p); requantising z gives y' = alpha' r exactly, so the
@@ -101,36 +102,20 @@ __device__ __forceinline__ void decode4(uint32_t w, float &a, float &b, float &c
     unpack_fp8x4(w, a, b, c, d);
 }
 
-// Loads and stores of the streamed data.  Every input byte is read once and every output byte
-// written once.  With NT they carry the non-temporal hint, which keeps a stream larger than the
-// caches from thrashing them; without it they are plain accesses, whose output the 256 MB MALL
-// (the last-level cache in front of HBM) can absorb when the stream is smaller.
-template <bool NT, class T>
-__device__ __forceinline__ T ld(const T *p) {
-  if constexpr (NT) return __builtin_nontemporal_load(p);
-  return *p;
+// Streaming loads and stores: every input byte is read once and every output byte written
+// once, so they carry the non-temporal hint.  (Plain accesses measure faster when the caches
+// are flushed between single launches, because the output then waits in the 256 MB MALL and
+// its write to HBM falls outside the launch; over back-to-back launches that rotate through
+// more buffers than the caches hold, where every write is paid, the hints are 4-13% faster for
+// compress and decompress on 34-117 M-element inputs.)
+template <class T>
+__device__ __forceinline__ T ld_stream(const T *p) {
+  return __builtin_nontemporal_load(p);
 }
-template <bool NT, class T>
-__device__ __forceinline__ void st(T v, T *p) {
-  if constexpr (NT)
-    __builtin_nontemporal_store(v, p);
-  else
-    *p = v;
+template <class T>
+__device__ __forceinline__ void st_stream(T v, T *p) {
+  __builtin_nontemporal_store(v, p);
 }
-
-// Launch modes of compress and decompress (a template parameter; the host picks one by size).
-//   kTilePlain   one tile per wavefront, plain loads and stores: inputs below 1.5 GiB.  Measured
-//                on MI355X with the caches flushed before each launch: 3-7% faster than with
-//                the hints on 100-360 MB streams.
-//   kTileStream  one tile per wavefront, non-temporal hints: inputs of 1.5 GiB or more (7%
-//                faster than plain on a 1.9 GB compress).
-//   kLoopStream  grid-stride loop with the next tile's loads in flight, non-temporal hints: the
-//                launch is capped (past 2^34 elements) and wavefronts take several tiles.
-// The one-tile modes carry no prefetch buffer, which at B = 256 leaves registers for eight
-// wavefronts per SIMD instead of five.
-enum : int { kTilePlain = 0, kTileStream = 1, kLoopStream = 2 };
-constexpr bool mode_nt(int mode) { return mode != kTilePlain; }
-constexpr bool mode_loop(int mode) { return mode == kLoopStream; }
 
 // --------------------------------------------------------------------------------------------
 // Range-safe scales: from the rotated values of one block (held by a group of L lanes) to the
@@ -187,20 +172,20 @@ struct CompressIn {
 // The same, from the base of a tile (wave-uniform, so it stays in scalar registers) and a lane's
 // 32-bit element offset into it: the loads then take the scalar base plus a vector offset, and
 // no 64-bit address arithmetic runs per lane.  Run g is read at off + g * step.
-template <bool NT, int B, bool F32IN>
+template <int B, bool F32IN>
 __device__ __forceinline__ void load_compress_at(CompressIn<B, F32IN> &in, const void *tile,
                                                  uint32_t off, uint32_t step) {
   constexpr int G = CompressIn<B, F32IN>::kRuns;
   if constexpr (!F32IN) {
     const uint16_t *xb = (const uint16_t *)tile + off;
 #pragma unroll
-    for (int g = 0; g < G; ++g) in.d[g] = ld<NT>((const u32x4 *)(xb + step * g));
+    for (int g = 0; g < G; ++g) in.d[g] = ld_stream((const u32x4 *)(xb + step * g));
   } else {
     const float *xb = (const float *)tile + off;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      in.d[2 * g] = ld<NT>((const u32x4 *)(xb + step * g));
-      in.d[2 * g + 1] = ld<NT>((const u32x4 *)(xb + step * g + 4));
+      in.d[2 * g] = ld_stream((const u32x4 *)(xb + step * g));
+      in.d[2 * g + 1] = ld_stream((const u32x4 *)(xb + step * g + 4));
     }
   }
 }
@@ -213,13 +198,13 @@ __device__ __forceinline__ void load_compress_in(CompressIn<B, F32IN> &in, const
   if constexpr (!F32IN) {
     const uint16_t *xb = (const uint16_t *)xin + blk * B + 8 * j;
 #pragma unroll
-    for (int g = 0; g < G; ++g) in.d[g] = ld<true>((const u32x4 *)(xb + RS * g));
+    for (int g = 0; g < G; ++g) in.d[g] = ld_stream((const u32x4 *)(xb + RS * g));
   } else {
     const float *xb = (const float *)xin + blk * B + 8 * j;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      in.d[2 * g] = ld<true>((const u32x4 *)(xb + RS * g));
-      in.d[2 * g + 1] = ld<true>((const u32x4 *)(xb + RS * g + 4));
+      in.d[2 * g] = ld_stream((const u32x4 *)(xb + RS * g));
+      in.d[2 * g + 1] = ld_stream((const u32x4 *)(xb + RS * g + 4));
     }
   }
 }
@@ -231,9 +216,11 @@ __device__ __forceinline__ void load_compress_in(CompressIn<B, F32IN> &in, const
 // line and each store wrote 32 bytes, and compress ran at 67% of HBM peak against 81%.)
 constexpr int compress_blocks_per_group(int B) { return B == 64 ? 2 : 1; }
 
-// MODE: kTilePlain, kTileStream or kLoopStream (above); in the one-tile modes the launch has a
-// wavefront for every tile (the host checks).
-template <int B, bool F32IN, int FLAGS, int MODE>
+// LOOP = false: the launch has a wavefront for every tile (the host checks), so each wavefront
+// takes one tile and carries no prefetch buffer, which at B = 256 leaves registers for eight
+// wavefronts per SIMD instead of five.  LOOP = true: grid-stride loop with the next tile's loads
+// in flight, for launches capped below one wavefront per tile (past 2^34 elements).
+template <int B, bool F32IN, int FLAGS, bool LOOP>
 __global__ __launch_bounds__(kThreads) void k_compress(const void *__restrict__ xin, int64_t nb,
                                                        float TBB, float sqrtTB, float C,
                                                        float invC, uint8_t *__restrict__ codes,
@@ -249,7 +236,6 @@ __global__ __launch_bounds__(kThreads) void k_compress(const void *__restrict__ 
   constexpr int NB = N / BG;                            // a block's registers in a lane
   static_assert(CompressIn<B, F32IN>::kRuns == G, "compress input layout");
   constexpr bool ROT = !(FLAGS & kNoRotation);
-  constexpr bool NT = mode_nt(MODE), LOOP = mode_loop(MODE);
   constexpr float Q = qmax_of<FLAGS>();
   const int lane = threadIdx.x & 63;
   const int j = lane & (L - 1);
@@ -261,6 +247,7 @@ __global__ __launch_bounds__(kThreads) void k_compress(const void *__restrict__ 
   const int64_t ntiles = (int64_t)(((uint64_t)nb + BPW - 1) / BPW);  // nb >= 0
   // packed bfloat16 (1, 1) and (1, -1), kept in registers for v_dot2_f32_bf16
   const uint32_t ones = 0x3F803F80u, plus_minus = 0xBF803F80u;
+  const float sqrtTBB = __fsqrt_rn(TBB);  // TBB = T B^2 (T B without the rotation)
 
   // Tile t covers blocks [t BPW, t BPW + BPW); group bw of its lanes takes blocks
   // t BPW + BG bw + b, b < BG.  A block past the last one (ragged last tile) is read as the last
@@ -279,15 +266,14 @@ __global__ __launch_bounds__(kThreads) void k_compress(const void *__restrict__ 
     return (nb - 1 - t * BPW) > BG * bw ? (uint32_t)B : 0u;
   };
   CompressIn<B, F32IN> cur;
-  if (wave < ntiles)
-    load_compress_at<NT, B, F32IN>(cur, tile_in(wave), lane_in(wave), run_step(wave));
+  if (wave < ntiles) load_compress_at<B, F32IN>(cur, tile_in(wave), lane_in(wave), run_step(wave));
 
   for (int64_t tile = wave; tile < ntiles; tile += nwaves) {
     const int64_t blk0 = tile * BPW;  // first block of the tile (wave-uniform)
     CompressIn<B, F32IN> nxt;
     if (LOOP && tile + nwaves < ntiles)
-      load_compress_at<NT, B, F32IN>(nxt, tile_in(tile + nwaves), lane_in(tile + nwaves),
-                                     run_step(tile + nwaves));
+      load_compress_at<B, F32IN>(nxt, tile_in(tile + nwaves), lane_in(tile + nwaves),
+                                 run_step(tile + nwaves));
 
     // Widen, energy and the first butterfly stages.  Blocks past the last one work on a copy
     // of the last block and store nothing.
@@ -354,21 +340,33 @@ __global__ __launch_bounds__(kThreads) void k_compress(const void *__restrict__ 
       // For max|w| in [2^-40, 2^60] every quantity stays normal and sum(x^2) is accurate, so
       // the scales use the single-instruction reciprocal square root (1 ulp, inside the 1e-6
       // bar); the code multiplier Q / max|w| is correctly rounded, so that a quotient that is
-      // exactly a rounding midpoint stays exact and rounds to even.  Other blocks (all-zero,
-      // bfloat16-subnormal, huge) take the range-safe path.
+      // exactly a rounding midpoint stays exact and rounds to even.
       float cm, alpha, s;
       if (M >= 0x1p-40f && M <= 0x1p60f) {
         const float c = __fdiv_rn(Q, M);
         alpha = fminf(fmaxf(sqrtTB * __builtin_amdgcn_rsqf(SS), 0x1p-126f), 0x1p126f);
         s = alpha * M * invC;
         cm = c * sj;
+      } else if (M == 0.0f) {
+        // all-zero block: alpha 1, s 0, codes +0
+        cm = 0.0f;
+        alpha = 1.0f;
+        s = 0.0f;
       } else {
-        float h[NB];
+        // bfloat16-subnormal or huge block, where sum(x^2) leaves float32's range: the same
+        // formulas on the block scaled by the exact power of two 2^k that brings max|w| into
+        // [1, 2), with the energy taken from the scaled w (Parseval: sum(w^2) = B sum(x^2)
+        // with the rotation, so alpha = sqrt(T B^2 / sum(w^2)) = sqrt(TBB / sum(w^2))), and k
+        // taken back out of alpha and s.  The codes do not depend on the scaling.
+        const int k = 1 - exponent_of(M);
 #pragma unroll
-        for (int r = 0; r < NB; ++r) h[r] = v[b * NB + r];
-        scales_exact<L, NB>(h, M, 0, TBB, Q, C, sj, cm, alpha, s);
-#pragma unroll
-        for (int r = 0; r < NB; ++r) v[b * NB + r] = h[r];
+        for (int r = 0; r < NB; ++r) v[b * NB + r] = scale2(v[b * NB + r], k);
+        const float Mk = scale2(M, k);
+        const float SW = group_sum<L>(sum_squares<NB>(&v[b * NB]));  // 2^2k sum(w^2)
+        alpha = fminf(fmaxf(scale2(sqrtTBB * __builtin_amdgcn_rsqf(SW), k), 0x1p-126f),
+                      0x1p126f);
+        s = scale2(alpha * Mk, -k) * invC;
+        cm = __fdiv_rn(Q, Mk) * sj;
       }
 
       const int64_t blk = blk0 + BG * bw + b;
@@ -380,7 +378,7 @@ __global__ __launch_bounds__(kThreads) void k_compress(const void *__restrict__ 
           u32x2 w;
           w[0] = encode4<FLAGS>(v[8 * g + 0], v[8 * g + 1], v[8 * g + 2], v[8 * g + 3], cm);
           w[1] = encode4<FLAGS>(v[8 * g + 4], v[8 * g + 5], v[8 * g + 6], v[8 * g + 7], cm);
-          st<NT>(w, (u32x2 *)(cb + co + RS * g));
+          st_stream(w, (u32x2 *)(cb + co + RS * g));
         }
         if (j == 0) {
           alpha_out[blk] = alpha;
@@ -407,20 +405,20 @@ struct DecompressIn {
   float s, a;
 };
 
-template <bool NT, int B>
+template <int B>
 __device__ __forceinline__ void load_decompress_in(DecompressIn<B> &in, const uint8_t *codes,
                                                    const float *alpha, const float *scale,
                                                    int64_t blk, int j) {
   constexpr int RS = 8 * decompress_lanes(B);
   const uint8_t *cb = codes + blk * B + 8 * j;
 #pragma unroll
-  for (int g = 0; g < B / RS; ++g) in.d[g] = ld<NT>((const u32x2 *)(cb + RS * g));
+  for (int g = 0; g < B / RS; ++g) in.d[g] = ld_stream((const u32x2 *)(cb + RS * g));
   in.s = scale[blk];
   in.a = alpha[blk];
 }
 
-// MODE as for k_compress.
-template <int B, bool F32OUT, int FLAGS, int MODE>
+// LOOP as for k_compress.
+template <int B, bool F32OUT, int FLAGS, bool LOOP>
 __global__ __launch_bounds__(kThreads) void k_decompress(const uint8_t *__restrict__ codes,
                                                          const float *__restrict__ alpha,
                                                          const float *__restrict__ scale,
@@ -432,7 +430,6 @@ __global__ __launch_bounds__(kThreads) void k_decompress(const uint8_t *__restri
   constexpr int N = B / L;
   constexpr int G = N / 8;
   constexpr bool ROT = !(FLAGS & kNoRotation);
-  constexpr bool NT = mode_nt(MODE), LOOP = mode_loop(MODE);
   const int lane = threadIdx.x & 63;
   const int j = lane & (L - 1);
   const int bw = lane / L;
@@ -444,15 +441,14 @@ __global__ __launch_bounds__(kThreads) void k_decompress(const uint8_t *__restri
 
   DecompressIn<B> cur;  // groups past the last block re-read the last block, store nothing
   if (wave < ntiles)
-    load_decompress_in<NT, B>(cur, codes, alpha, scale, min(wave * BPW + bw, nb - 1), j);
+    load_decompress_in<B>(cur, codes, alpha, scale, min(wave * BPW + bw, nb - 1), j);
 
   for (int64_t tile = wave; tile < ntiles; tile += nwaves) {
     const int64_t blk = tile * BPW + bw;
     const bool active = blk < nb;
     DecompressIn<B> nxt;
     if (LOOP && tile + nwaves < ntiles)
-      load_decompress_in<NT, B>(nxt, codes, alpha, scale, min((tile + nwaves) * BPW + bw, nb - 1),
-                                j);
+      load_decompress_in<B>(nxt, codes, alpha, scale, min((tile + nwaves) * BPW + bw, nb - 1), j);
 
     float v[N];
 #pragma unroll
@@ -521,8 +517,8 @@ __global__ __launch_bounds__(kThreads) void k_decompress(const uint8_t *__restri
             w0[q] = __float_as_uint(fmaf(v[8 * g + q], f, 0.0f) * ra);
             w1[q] = __float_as_uint(fmaf(v[8 * g + 4 + q], f, 0.0f) * ra);
           }
-          st<NT>(w0, (u32x4 *)(ob + RS * g));
-          st<NT>(w1, (u32x4 *)(ob + RS * g + 4));
+          st_stream(w0, (u32x4 *)(ob + RS * g));
+          st_stream(w1, (u32x4 *)(ob + RS * g + 4));
         }
       } else {
         __bf16 *ob = (__bf16 *)out + blk * B + 8 * pj;
@@ -536,7 +532,7 @@ __global__ __launch_bounds__(kThreads) void k_decompress(const uint8_t *__restri
             w[q] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
                    ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
           }
-          st<NT>(w, (u32x4 *)(ob + RS * g));
+          st_stream(w, (u32x4 *)(ob + RS * g));
         }
       }
     }
@@ -546,13 +542,12 @@ __global__ __launch_bounds__(kThreads) void k_decompress(const uint8_t *__restri
 }
 
 // --------------------------------------------------------------------------------------------
-// K3: reduce.  E = 16 consecutive codes per lane (one 16-byte load per contribution), B/E lanes
-// per block, no Hadamard.  PB > 0: exactly PB contributions, all loads issued before any
+// K3: reduce.  B/16 lanes per block, 16 consecutive codes per lane (one 16-byte load per
+// contribution), no Hadamard.  PB > 0: exactly PB contributions, all loads issued before any
 // arithmetic; PB = 0: any P, in chunks of 8.  Contribution p's codes start at codes + p cstride
 // and its scales at alpha + p astride, scale + p sstride (cstride = n, astride = sstride = nb
 // for contiguous stacks).  (8 codes per lane, which halves the registers and allows eight
 // wavefronts per SIMD instead of five, measured 2-11% slower.)
-constexpr int kReduceElems = 16;
 
 template <int B, int PB, int FLAGS>
 __global__ __launch_bounds__(kThreads) void k_reduce(const uint8_t *__restrict__ codes,
@@ -563,10 +558,7 @@ __global__ __launch_bounds__(kThreads) void k_reduce(const uint8_t *__restrict__
                                                      uint8_t *__restrict__ codes_out,
                                                      float *__restrict__ alpha_out,
                                                      float *__restrict__ scale_out) {
-  constexpr int E = kReduceElems;  // codes per lane
-  constexpr int NQ = E / 4;        // dwords per lane
-  using CodesT = u32x4;
-  constexpr int L = B / E;     // lanes per block
+  constexpr int L = B / 16;    // lanes per block
   constexpr int BPW = 64 / L;  // blocks per wavefront
   constexpr int CH = PB > 0 ? PB : 8;  // contributions loaded together
   // low bits of g cleared so that g times a code value is exact in float64: E4M3 values have
@@ -584,7 +576,7 @@ __global__ __launch_bounds__(kThreads) void k_reduce(const uint8_t *__restrict__
     const int64_t blk = tile * BPW + bw;
     const bool active = blk < nb;
     const int64_t cblk = active ? blk : nb - 1;  // groups past the end re-read the last block
-    const uint8_t *cb = codes + cblk * B + E * j;
+    const uint8_t *cb = codes + cblk * B + 16 * j;
 
     // r = sum_p g_p dec(q_p) with g_p = s_p / alpha_p, accumulated in float64.  g_p is cut to
     // 49 significant bits (46 for INT8 codes; a relative change below 2^-45), so that its
@@ -592,14 +584,14 @@ __global__ __launch_bounds__(kThreads) void k_reduce(const uint8_t *__restrict__
     // the running sum, each within 2^-53 of it.  Contributions that largely cancel therefore
     // still requantise like the exact sum, and a contribution and its exact negation cancel
     // to exactly zero.  A zero block (s_p = 0) contributes exact zeros.
-    double r64[E];
+    double r64[16];
     for (int p0 = 0; p0 < P; p0 += CH) {
-      CodesT d[CH];
+      u32x4 d[CH];
       float sp[CH], ap[CH];
 #pragma unroll
       for (int c = 0; c < CH; ++c)
         if (PB > 0 || p0 + c < P) {
-          d[c] = ld<true>((const CodesT *)(cb + (int64_t)(p0 + c) * cstride));
+          d[c] = ld_stream((const u32x4 *)(cb + (int64_t)(p0 + c) * cstride));
           sp[c] = scale[(int64_t)(p0 + c) * sstride + cblk];
           ap[c] = alpha[(int64_t)(p0 + c) * astride + cblk];
         }
@@ -613,7 +605,7 @@ __global__ __launch_bounds__(kThreads) void k_reduce(const uint8_t *__restrict__
           ri = fma(ri, fma(-ad, ri, 1.0), ri);
           const double g = __longlong_as_double(__double_as_longlong((double)sp[c] * ri) & kGMask);
 #pragma unroll
-          for (int q = 0; q < NQ; ++q) {
+          for (int q = 0; q < 4; ++q) {
             float a0, a1, a2, a3;
             decode4<FLAGS>(d[c][q], a0, a1, a2, a3);
             if (p0 + c == 0) {
@@ -632,43 +624,44 @@ __global__ __launch_bounds__(kThreads) void k_reduce(const uint8_t *__restrict__
       }
     }
 
-    float r[E];
+    float r[16];
     float m = 0.0f;
 #pragma unroll
-    for (int i = 0; i < E; ++i) {
+    for (int i = 0; i < 16; ++i) {
       r[i] = (float)r64[i];
       m = fmaxf(m, fabsf(r[i]));
     }
     float M = group_max<L>(m);
-    int E2 = 0;  // the true sum is r * 2^E2
+    int E = 0;
     if (M != 0.0f && !(M >= 0x1p-100f && M <= 0x1p100f)) {
       // Tiny or huge sum (bfloat16-subnormal blocks, or contributions that cancelled):
       // rescale the float64 sum so that its largest magnitude lies in [1, 2) before rounding
       // it to float32.
       double m64 = 0.0;
 #pragma unroll
-      for (int i = 0; i < E; ++i) m64 = fmax(m64, fabs(r64[i]));
+      for (int i = 0; i < 16; ++i) m64 = fmax(m64, fabs(r64[i]));
       const int e64 = __builtin_amdgcn_frexp_exp(m64);
       const int k = 1 - group_max_i<L>(e64);
       m = 0.0f;
 #pragma unroll
-      for (int i = 0; i < E; ++i) {
+      for (int i = 0; i < 16; ++i) {
         r[i] = (float)__builtin_amdgcn_ldexp(r64[i], k);
         m = fmaxf(m, fabsf(r[i]));
       }
       M = group_max<L>(m);
-      E2 -= k;
+      E -= k;
     }
 
+    // the true sum is r * 2^E
     float cm, a_out, s_out;
     constexpr float Q = qmax_of<FLAGS>();
-    scales_exact<L, E>(r, M, E2, TB, Q, Q, 1.0f, cm, a_out, s_out);
+    scales_exact<L, 16>(r, M, E, TB, Q, Q, 1.0f, cm, a_out, s_out);
     if (active) {
-      CodesT w;
+      u32x4 w;
 #pragma unroll
-      for (int q = 0; q < NQ; ++q)
+      for (int q = 0; q < 4; ++q)
         w[q] = encode4<FLAGS>(r[4 * q], r[4 * q + 1], r[4 * q + 2], r[4 * q + 3], cm);
-      st<true>(w, (CodesT *)(codes_out + blk * B + E * j));
+      st_stream(w, (u32x4 *)(codes_out + blk * B + 16 * j));
       if (j == 0) {
         alpha_out[blk] = a_out;
         scale_out[blk] = s_out;
@@ -826,7 +819,7 @@ __global__ __launch_bounds__(kThreads) void k_accumulate(
           u32x2 w;
           w[0] = encode4<FLAGS>(v[8 * g + 0], v[8 * g + 1], v[8 * g + 2], v[8 * g + 3], cm);
           w[1] = encode4<FLAGS>(v[8 * g + 4], v[8 * g + 5], v[8 * g + 6], v[8 * g + 7], cm);
-          st<true>(w, (u32x2 *)(cb + RS * g));
+          st_stream(w, (u32x2 *)(cb + RS * g));
         }
         if (j == 0) {
           alpha_out[blk] = a_out;
@@ -1106,9 +1099,8 @@ int cu_count() {
 // 1.9 to 4.3 GB.  At 1.1 GB the two shapes tie, and on inputs of 134-268 MB the remapped one is
 // 3-10% slower, hence the threshold.  At B = 64, whose lane groups now read whole lines as at
 // B = 128, the remapped shape is 1% faster on 1.9 GB.  Decompress and the reduce were slower
-// remapped.  The same size splits the cache hints of compress (its input) and decompress (its
-// output): plain below it, non-temporal from it on (launch modes above).
-constexpr int64_t kStreamMinBytes = (int64_t)3 << 29;  // 1.5 GiB
+// remapped.
+constexpr int64_t kCompressRemapMinBytes = (int64_t)3 << 29;  // 1.5 GiB of input
 
 // The cap without `per_cu` keeps gridDim.x * nt (the work-items of the launch, a 32-bit count
 // in the dispatch packet) at 2^30; larger inputs loop.  Under the XCD remap the count is
@@ -1153,17 +1145,14 @@ tfp8_status launch_compress_t(const void *x, int64_t nb, float target, uint8_t *
   constexpr int BPW = 64 / 8 * compress_blocks_per_group(B);  // blocks per tile
   // Large inputs stream faster with one wavefront per workgroup and each XCD on a contiguous
   // eighth of the tiles; smaller ones with 4 wavefronts per workgroup in dispatch order.
-  const bool remap = nb * B * (F32 ? 4 : 2) >= kStreamMinBytes;
+  const bool remap = nb * B * (F32 ? 4 : 2) >= kCompressRemapMinBytes;
   const int nt = remap ? 64 : kThreads;
   const int64_t tiles = (nb + BPW - 1) / BPW;
   const unsigned grid = grid_for(tiles, TFP8_COMPRESS_WGS_PER_CU, nt, remap);
   if ((int64_t)grid * (nt / 64) < tiles)  // capped launch: wavefronts loop over tiles
-    return launch(k_compress<B, F32, FLAGS, kLoopStream>, grid, nt, st, x, nb, TBB, sqrtTB, C,
-                  invC, codes, alpha, scale, nt / 64, remap);
-  if (remap)
-    return launch(k_compress<B, F32, FLAGS, kTileStream>, grid, nt, st, x, nb, TBB, sqrtTB, C,
-                  invC, codes, alpha, scale, nt / 64, remap);
-  return launch(k_compress<B, F32, FLAGS, kTilePlain>, grid, nt, st, x, nb, TBB, sqrtTB, C, invC,
+    return launch(k_compress<B, F32, FLAGS, true>, grid, nt, st, x, nb, TBB, sqrtTB, C, invC,
+                  codes, alpha, scale, nt / 64, remap);
+  return launch(k_compress<B, F32, FLAGS, false>, grid, nt, st, x, nb, TBB, sqrtTB, C, invC,
                 codes, alpha, scale, nt / 64, remap);
 }
 
@@ -1190,13 +1179,10 @@ tfp8_status launch_decompress_t(const uint8_t *codes, const float *alpha, const 
   const int64_t tiles = (nb + BPW - 1) / BPW;
   const unsigned grid = grid_for(tiles, TFP8_DECOMPRESS_WGS_PER_CU);
   if ((int64_t)grid * (kThreads / 64) < tiles)  // capped launch: wavefronts loop over tiles
-    return launch(k_decompress<B, F32, FLAGS, kLoopStream>, grid, kThreads, st, codes, alpha,
-                  scale, nb, inv_sqrt_b, out);
-  if (nb * B * (F32 ? 4 : 2) >= kStreamMinBytes)
-    return launch(k_decompress<B, F32, FLAGS, kTileStream>, grid, kThreads, st, codes, alpha,
-                  scale, nb, inv_sqrt_b, out);
-  return launch(k_decompress<B, F32, FLAGS, kTilePlain>, grid, kThreads, st, codes, alpha, scale,
-                nb, inv_sqrt_b, out);
+    return launch(k_decompress<B, F32, FLAGS, true>, grid, kThreads, st, codes, alpha, scale, nb,
+                  inv_sqrt_b, out);
+  return launch(k_decompress<B, F32, FLAGS, false>, grid, kThreads, st, codes, alpha, scale, nb,
+                inv_sqrt_b, out);
 }
 
 template <int B, bool F32>
@@ -1220,7 +1206,7 @@ tfp8_status launch_reduce_t(const uint8_t *codes, const float *alpha, const floa
   // the reduce works on r = sum_p g_p dec(q_p) directly, with or without the rotation: its
   // energy is that of the sum, sum(r^2) = sum(z^2)
   const float TB = target * (float)B;
-  constexpr int BPW = 64 / (B / kReduceElems);
+  constexpr int BPW = 64 / (B / 16);
   const unsigned grid = grid_for((nb + BPW - 1) / BPW, TFP8_REDUCE_WGS_PER_CU);
 #define TFP8_LAUNCH_REDUCE(PB)                                                               \
   return launch(k_reduce<B, PB, FLAGS>, grid, kThreads, st, codes, alpha, scale, P, cstride,    \
