@@ -849,11 +849,38 @@ __global__ __launch_bounds__(kThreads) void k_accumulate(
 // 2^(K - E) with max|z| < 2^E and split into integers r = rint(t) and remainders l = t - r in
 // [-1/2, 1/2].  |r| <= 2^K with K = 24 - log2(B), so every partial sum of H r is an integer of
 // at most 2^24 and the transform of r is exact; the transform of l errs by ~2^-18 of 2^K at most.
+// The inputs of one set-aside block, as lane j of its group reads them.
+template <int B, bool F32IN>
+struct FixIn {
+  CompressIn<B, F32IN> in;                  // the local gradient g
+  u32x2 qd[B / lanes_per_block(B) / 8];     // the main gradient's codes
+  float sp, ap;                             // its s and alpha
+};
+
+template <int B, bool F32IN, int FLAGS>
+__device__ __forceinline__ void load_fix_in(FixIn<B, F32IN> &f, const uint8_t *codes,
+                                            const float *scale, const void *__restrict__ grad,
+                                            const float *alpha_out, int64_t blk, int j) {
+  constexpr int L = lanes_per_block(B);
+  constexpr int RS = 8 * L;
+  constexpr int G = B / L / 8;
+  constexpr bool ROT = !(FLAGS & kNoRotation);
+  load_compress_in<B, F32IN>(f.in, grad, blk, j);
+  // The lane network sends lane j's result to position pj.  Reading lane j's codes from 8 qj
+  // instead of 8 j, with qj = j ^ (3 bit2(j)) at L = 8 (the transpose of that GF(2)-linear
+  // permutation; identity at L = 4 and without the rotation), makes the network's output land
+  // at lane j's own positions, those of g, with the sign sj (enumerated on the unit vectors).
+  const int qj = ROT && L == 8 ? j ^ (((j >> 2) & 1) * 3) : j;
+#pragma unroll
+  for (int g = 0; g < G; ++g) f.qd[g] = *(const u32x2 *)(codes + blk * B + RS * g + 8 * qj);
+  f.sp = scale[blk];
+  f.ap = -alpha_out[blk];
+}
+
 template <int B, bool F32IN, int FLAGS>
 __device__ __forceinline__ void accumulate_block_split(
-    const uint8_t *codes, const float *scale, const void *__restrict__ grad, int64_t blk,
-    bool active, int j, float TBB, float C, double root_b, uint8_t *codes_out, float *alpha_out,
-    float *scale_out) {
+    const FixIn<B, F32IN> &f, int64_t blk, bool active, int j, float TBB, float C, double root_b,
+    uint8_t *codes_out, float *alpha_out, float *scale_out) {
   constexpr int L = lanes_per_block(B);
   constexpr int RS = 8 * L;
   constexpr int N = B / L;
@@ -864,18 +891,9 @@ __device__ __forceinline__ void accumulate_block_split(
   constexpr int K = 24 - (B == 64 ? 6 : B == 128 ? 7 : B == 256 ? 8 : 9);
   const int pj = ROT ? lane_perm<L>(j) : j;
   const float sj = ROT ? lane_sign<L>(j) : 1.0f;
-
-  CompressIn<B, F32IN> in;
-  load_compress_in<B, F32IN>(in, grad, blk, j);
-  u32x2 qd[G];
-  // The lane network sends lane j's result to position pj.  Reading lane j's codes from 8 qj
-  // instead of 8 j, with qj = j ^ (3 bit2(j)) at L = 8 (the transpose of that GF(2)-linear
-  // permutation; identity at L = 4 and without the rotation), makes the network's output land
-  // at lane j's own positions, those of g, with the sign sj (enumerated on the unit vectors).
-  const int qj = ROT && L == 8 ? j ^ (((j >> 2) & 1) * 3) : j;
-#pragma unroll
-  for (int g = 0; g < G; ++g) qd[g] = *(const u32x2 *)(codes + blk * B + RS * g + 8 * qj);
-  const float sp = scale[blk], ap = -alpha_out[blk];
+  const CompressIn<B, F32IN> &in = f.in;
+  const u32x2 *qd = f.qd;
+  const float sp = f.sp, ap = f.ap;
 
   float gv[N];  // g at positions RS g + 8 j + e
   if constexpr (!F32IN) {
@@ -988,10 +1006,29 @@ __device__ __forceinline__ void accumulate_block_split(
 
 constexpr int kFixRuns = 2;  // runs of 64 blocks that one wavefront of k_accumulate_fix scans
 
+// Position of the n-th set bit (n counted from 0) of m, which has more than n set bits: a binary
+// search on the population counts of the low halves.
+__device__ __forceinline__ int nth_set_bit(uint64_t m, int n) {
+  int pos = 0;
+#pragma unroll
+  for (int w = 32; w >= 1; w >>= 1) {
+    const int c = __popcll(m & ((1ull << w) - 1));
+    if (n >= c) {
+      n -= c;
+      m >>= w;
+      pos += w;
+    }
+  }
+  return pos;
+}
+
 // Finds the blocks k_accumulate set aside (alpha_out < 0) and redoes them.  A wavefront reads the
-// alphas of kRuns x 64 consecutive blocks at once (kRuns loads in flight per lane), then takes
-// the runs of 64 in turn and works through each run's marked blocks 64 / L at a time, one group
-// of L lanes per block.
+// alphas of kRuns x 64 consecutive blocks at once (kRuns loads in flight per lane) and deals the
+// marked blocks of all its runs out in rounds of 64 / L, one block per group of L lanes, with the
+// next round's inputs loaded before the current round's arithmetic.  Groups left without a block
+// in the last round redo that round's first block and store nothing; a round's loads never touch
+// a block that an earlier round stores (each marked block is in exactly one round), so working
+// in place is safe across rounds as within one.
 template <int B, bool F32IN, int FLAGS>
 __global__ __launch_bounds__(kThreads) void k_accumulate_fix(
     const uint8_t *codes, const float *scale, const void *__restrict__ grad, int64_t nb,
@@ -1013,20 +1050,45 @@ __global__ __launch_bounds__(kThreads) void k_accumulate_fix(
       const int64_t b = (t * kRuns + run) * 64 + lane;
       am[run] = b < nb ? alpha_out[b] : 1.0f;
     }
+    uint64_t mask[kRuns];
+    int count = 0;  // marked blocks of the scan (wave-uniform)
+#pragma unroll
     for (int run = 0; run < kRuns; ++run) {
-      const int64_t base = (t * kRuns + run) * 64;
-      uint64_t mask = __ballot(am[run] < 0.0f);
-      while (mask != 0) {
-        // group bw takes the bw-th remaining marked block; groups without one redo the first
-        // (their loads precede every store of the wavefront) and store nothing
-        uint64_t mine = mask;
-        for (int i = 0; i < bw; ++i) mine &= mine - 1;
-        const bool active = mine != 0;
-        const int64_t blk = base + __builtin_ctzll(active ? mine : mask);
-        for (int i = 0; i < BPW; ++i) mask &= mask - 1;
-        accumulate_block_split<B, F32IN, FLAGS>(codes, scale, grad, blk, active, j, TBB, C,
-                                                root_b, codes_out, alpha_out, scale_out);
+      mask[run] = __ballot(am[run] < 0.0f);
+      count += __popcll(mask[run]);
+    }
+    // the idx-th marked block of the scan (idx < count), as an offset from its first block
+    const auto marked = [&](int idx) {
+      int off = 0;
+#pragma unroll
+      for (int run = kRuns - 1; run >= 0; --run) {
+        int before = 0;  // marked blocks in the runs before this one
+#pragma unroll
+        for (int r = 0; r < run; ++r) before += __popcll(mask[r]);
+        if (idx >= before && idx < before + __popcll(mask[run]))
+          off = run * 64 + nth_set_bit(mask[run], idx - before);
       }
+      return off;
+    };
+    const int rounds = (count + BPW - 1) / BPW;
+    if (rounds == 0) continue;
+    const int64_t base = t * kRuns * 64;  // the scan's first block (wave-uniform)
+    // group bw's block of round r: the (r BPW + bw)-th marked one, or the round's first
+    const auto block_of = [&](int r) {
+      const int idx = r * BPW + bw;
+      return marked(idx < count ? idx : r * BPW);
+    };
+    FixIn<B, F32IN> cur;
+    load_fix_in<B, F32IN, FLAGS>(cur, codes, scale, grad, alpha_out, base + block_of(0), j);
+    for (int r = 0; r < rounds; ++r) {
+      FixIn<B, F32IN> nxt;
+      if (r + 1 < rounds)
+        load_fix_in<B, F32IN, FLAGS>(nxt, codes, scale, grad, alpha_out, base + block_of(r + 1), j);
+      // the block is located again rather than carried over: that keeps the registers at five
+      // wavefronts per SIMD
+      accumulate_block_split<B, F32IN, FLAGS>(cur, base + block_of(r), r * BPW + bw < count, j,
+                                              TBB, C, root_b, codes_out, alpha_out, scale_out);
+      cur = nxt;
     }
   }
 }
