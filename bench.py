@@ -605,7 +605,7 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(ach_c, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach_c / HBM_PEAK_GBS, 4),
                 "traffic": (round(traffic / (t_c * 1e-3) / 1e9, 1) if traffic else None),
-                "kernel": "tfp8::k_compress<128, false, 0, 1>",
+                "kernel": "tfp8::k_compress<128, false, 0, false>",
                 "bytes_per_launch_algorithmic": int(alg_c),
                 "launch_us_mean": round(t_c * 1e3, 2), "launch_us_median": round(med_c * 1e3, 2),
                 "launch_us_min": round(d_c[0] * 1e3, 2), "launch_us_max": round(d_c[-1] * 1e3, 2),
