@@ -1,10 +1,12 @@
 """GPU parity: the HIP path through the C ABI against the CPU oracle on the same seeded inputs.
 
-Each stage is also fed the oracle's output of the stage before it, so a mismatch names the
-stage.  Bars: codes identical except admissible rounding ties on <= 1e-4 of the elements;
-alpha and s within 1e-6 relative (zero blocks and clamped alpha exact); float32
-reconstructions within 1e-6 relative (+ 2^-149 absolute for subnormal results); bfloat16
-reconstructions identical except double-rounding ties.
+Each stage is fed the oracle's output of the stage before it, so a mismatch names the stage;
+the end-to-end test of the Qwen-shaped workload alone chains the GPU's own outputs, against the
+oracle's chain, within a bound derived from the per-stage bars.  Bars: codes identical except
+admissible rounding ties on <= 1e-4 of the elements; alpha and s within 1e-6 relative (zero
+blocks and clamped alpha exact); float32 reconstructions within 1e-6 relative (+ 2^-149
+absolute for subnormal results); bfloat16 reconstructions identical except double-rounding
+ties.
 """
 import os
 
