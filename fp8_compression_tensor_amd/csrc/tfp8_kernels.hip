@@ -156,9 +156,9 @@ __device__ __forceinline__ void scales_exact(float (&v)[N], float M, int E0, flo
 }
 
 // --------------------------------------------------------------------------------------------
-// K1: compress.  One wavefront handles a tile of 8 lane groups (8 blocks, or 16 at B = 64) per
-// iteration of a grid-stride loop and prefetches the next iteration's input before working on
-// the current one.
+// K1: compress.  One wavefront handles a tile of 8 lane groups (8 blocks, or 16 at B = 64): one
+// tile per wavefront, or (LOOP, for capped launches) a tile per iteration of a grid-stride loop
+// that prefetches the next iteration's input before working on the current one.
 
 template <int B, bool F32IN>
 struct CompressIn {
@@ -392,8 +392,8 @@ __global__ __launch_bounds__(kThreads) void k_compress(const void *__restrict__ 
 }
 
 // --------------------------------------------------------------------------------------------
-// K2: decompress.  x = H (s dec q) / (sqrt(B) alpha), same lane layout as compress, with the
-// next iteration's codes and scales prefetched.
+// K2: decompress.  x = H (s dec q) / (sqrt(B) alpha), same lane layout as compress; one tile per
+// wavefront, or (LOOP) a grid-stride loop with the next iteration's codes and scales prefetched.
 
 // Decompress keeps 8 lanes per block at every B: its per-block work is small, and at B = 64
 // the 8-lane group reads each block's codes, and writes its output, in whole lines.
@@ -1139,11 +1139,13 @@ bool target_ok(float t) {
 }
 
 // Workgroups for a launch with one wavefront per tile, capped at `per_cu` workgroups per
-// compute unit (0: no cap) beyond which the wavefronts loop over tiles.  Measured on MI355X with
-// the caches flushed before each launch: compress, decompress and the reduce all stream fastest
-// with one tile per wavefront and no loop (the hardware keeps the CUs fed as wavefronts retire);
-// caps of 2-32 workgroups per CU with prefetching loops were 1-16% slower on 34-940 M-element
-// inputs (the reduce at one rank's share was equal, its full-tensor call 5% slower at 32).
+// compute unit (0: no cap) beyond which the wavefronts loop over tiles.  Measured on MI355X:
+// compress, decompress and the reduce all stream fastest with one tile per wavefront and no loop
+// (the hardware keeps the CUs fed as wavefronts retire).  With the caches flushed before each
+// launch, caps of 2-32 workgroups per CU with prefetching loops were 1-16% slower on
+// 34-940 M-element inputs; over back-to-back launches through rotating buffers the uncapped
+// reduce was 4% faster than at 32 workgroups per CU on the full Qwen-shaped tensor, and equal
+// at one rank's share.
 int cu_count() {
   // compute units of the current device, looked up once per device (any thread may race to
   // fill an entry; they all store the same value)
