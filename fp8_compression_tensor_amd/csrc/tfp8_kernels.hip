@@ -219,7 +219,8 @@ constexpr int compress_blocks_per_group(int B) { return B == 64 ? 2 : 1; }
 // LOOP = false: the launch has a wavefront for every tile (the host checks), so each wavefront
 // takes one tile and carries no prefetch buffer, which at B = 256 leaves registers for eight
 // wavefronts per SIMD instead of five.  LOOP = true: grid-stride loop with the next tile's loads
-// in flight, for launches capped below one wavefront per tile (past 2^34 elements).
+// in flight, for launches capped below one wavefront per tile (past 2^27 B elements, 2^34 at
+// B = 64).
 template <int B, bool F32IN, int FLAGS, bool LOOP>
 __global__ __launch_bounds__(kThreads) void k_compress(const void *__restrict__ xin, int64_t nb,
                                                        float TBB, float sqrtTB, float C,

@@ -177,3 +177,117 @@ def check_reduce(oracle, tfp8, q, a, s, B, T=1.0, what="reduce", flags: int = 0,
     say(f"  {what}: P={P} n={n} B={B} flags={flags}: code tie mismatches {nmis} ({nmis / n:.2e}), "
         f"max rel err alpha {ea:.2e} scale {es:.2e}")
     return (cq, ca, cs) if gpu else (rq, ra, rs)
+
+
+# ---- inputs that repeat every seven tiles, checked on every block on the GPU ----------------
+#
+# A tensor of tens of gigabytes cannot be compared with the oracle element by element on the
+# host.  When its input repeats with a period of seven tiles (tile t is parts[t mod 7]), every
+# output block equals the oracle's output for the same block of one of the seven parts, so the
+# expected values are the oracle's outputs for the seven parts, gathered on the GPU by index.
+
+def fill_periodic(dst: torch.Tensor, parts, per_tile: int) -> torch.Tensor:
+    """Fill the flat GPU tensor dst so that tile t (per_tile elements, the last one cut short)
+    is parts[t mod len(parts)]: the first period is uploaded, then doubled by copies of whole
+    periods.  Returns dst."""
+    period = len(parts) * per_tile
+    head = torch.from_numpy(np.ascontiguousarray(np.concatenate(parts))).to(DEV)
+    assert head.dtype == dst.dtype and head.numel() == period, (head.dtype, head.numel())
+    c = min(period, dst.numel())
+    dst[:c] = head[:c]
+    while c < dst.numel():  # c stays a multiple of the period until the last copy
+        k = min(c, dst.numel() - c)
+        dst[c:c + k] = dst[:k]
+        c += k
+    return dst
+
+
+def _periodic_src(k0: int, k1: int, bpt: int) -> torch.Tensor:
+    """Row of the seven parts' stacked outputs that block k of the whole tensor equals."""
+    k = torch.arange(k0, k1, device=DEV, dtype=torch.int64)
+    return torch.div(k, bpt, rounding_mode="floor") % 7 * bpt + k % bpt
+
+
+def assert_periodic_codes(q, a, s, refs, n: int, tile: int, B: int, what: str, flags: int = 0,
+                          chunk: int = 1 << 20):
+    """Codes, alpha and s of a whole periodic tensor against refs[w] = (codes, alpha, scale,
+    quotients), the oracle's output for part w.  Codes and scales are compared on the GPU block
+    by block; the blocks that hold a code mismatch are fetched, every mismatch must be an
+    admissible tie and their count is held to the cap over the whole tensor.  alpha and s follow
+    the rule of assert_scales (1e-6 relative; zero blocks alpha 1, s 0; a clamped alpha
+    exactly).  Returns (tie mismatches, max rel err alpha, max rel err s)."""
+    nb, bpt = n // B, tile // B
+    hq = np.stack([np.asarray(r[0], np.uint8).reshape(bpt, B) for r in refs])
+    ht = np.stack([np.asarray(r[3], np.float64).reshape(bpt, B) for r in refs])
+    rq = u8_to_gpu(hq.reshape(-1, B))
+    ra = torch.from_numpy(np.concatenate([r[1] for r in refs]).astype(np.float64)).to(DEV)
+    rs = torch.from_numpy(np.concatenate([r[2] for r in refs]).astype(np.float64)).to(DEV)
+    qv = q.view(nb, B)
+    bad, worst = [], torch.zeros(2, dtype=torch.float64, device=DEV)
+    nviol = torch.zeros((), dtype=torch.int64, device=DEV)
+    for k0 in range(0, nb, chunk):
+        k1 = min(nb, k0 + chunk)
+        src = _periodic_src(k0, k1, bpt)
+        bad.append(torch.nonzero((qv[k0:k1] != rq[src]).any(1)).view(-1) + k0)
+        ga, gs, ea, es = a[k0:k1].double(), s[k0:k1].double(), ra[src], rs[src]
+        da, ds = (ga - ea).abs(), (gs - es).abs()
+        ok = (da <= 1e-6 * ea.abs()) & (ds <= 1e-6 * es.abs())
+        ok &= (es != 0) | ((gs == 0) & (ga == 1))
+        ok &= ((ea != 2.0 ** 126) & (ea != 2.0 ** -126)) | (ga == ea)
+        nviol += (~ok).sum()
+        zero = torch.zeros((), dtype=torch.float64, device=DEV)
+        worst = torch.maximum(worst, torch.stack([
+            torch.where(ea != 0, da / ea.abs(), zero).max(),
+            torch.where(es != 0, ds / es.abs(), zero).max()]))
+    assert int(nviol) == 0, f"{what}: {int(nviol)} blocks with alpha or s outside the bar"
+    blocks = torch.cat(bad)
+    nmis = 0
+    if blocks.numel():
+        bh = cpu(blocks)
+        w, off = bh // bpt % 7, bh % bpt
+        nmis = assert_codes_match(cpu(qv[blocks]), hq[w, off], ht[w, off], max_frac=1.0,
+                                  what=what + " codes", int8=bool(flags & FLAG_INT8))
+    assert nmis <= tie_cap(flags) * n, (f"{what}: {nmis} tie mismatches of {n} exceed "
+                                        f"{tie_cap(flags)} of the tensor")
+    ea, es = (float(v) for v in cpu(worst))
+    return nmis, ea, es
+
+
+def assert_periodic_decompress(out, refs, n: int, tile: int, B: int, what: str,
+                               chunk: int = 1 << 18):
+    """A whole periodic decompress output against refs[w] = (values, exact float64) from the
+    oracle for part w: float32 outputs within 1e-6 relative (floor 2^-149), bfloat16 outputs
+    identical except adjacent values whose exact result lies within 2^-20 of their midpoint
+    (the rule of assert_bf16_match), all on the GPU.  Returns the bfloat16 tie count (0 for
+    float32)."""
+    nb, bpt = n // B, tile // B
+    bf16 = out.dtype == torch.bfloat16
+    if bf16:
+        rv = torch.from_numpy(np.stack([np.asarray(r[0], np.uint16).view(np.int16)
+                                        for r in refs]).reshape(-1, B)).to(DEV)
+    else:
+        rv = torch.from_numpy(np.stack([np.asarray(r[0], np.float32)
+                                        for r in refs]).reshape(-1, B)).to(DEV)
+    r64 = torch.from_numpy(np.stack([np.asarray(r[1], np.float64)
+                                     for r in refs]).reshape(-1, B)).to(DEV)
+    ov = out.view(nb, B)
+    nmis = torch.zeros((), dtype=torch.int64, device=DEV)
+    nviol = torch.zeros((), dtype=torch.int64, device=DEV)
+    for k0 in range(0, nb, chunk):
+        k1 = min(nb, k0 + chunk)
+        src = _periodic_src(k0, k1, bpt)
+        if not bf16:
+            g, e = ov[k0:k1].double(), rv[src].double()
+            nviol += (~((g - e).abs() <= 1e-6 * e.abs() + 2.0 ** -149)).sum()
+            continue
+        gb, eb = ov[k0:k1].view(torch.int16), rv[src]
+        gv, ev = gb.view(torch.bfloat16).double(), eb.view(torch.bfloat16).double()
+        mis = gv != ev  # +0 and -0 compare equal as values
+        gi, ei = gb[mis].int(), eb[mis].int()
+        adjacent = ((gi & 0x8000) == (ei & 0x8000)) & (((gi & 0x7FFF) - (ei & 0x7FFF)).abs() == 1)
+        mid = 0.5 * (gv[mis] + ev[mis])
+        near = (r64[src][mis] - mid).abs() <= 2.0 ** -20 * mid.abs() + 2.0 ** -150
+        nmis += mis.sum()
+        nviol += (~(adjacent & near)).sum()
+    assert int(nviol) == 0, f"{what}: {int(nviol)} outputs outside the bar"
+    return int(nmis)

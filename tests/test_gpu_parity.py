@@ -15,6 +15,7 @@ import pytest
 import torch
 
 from gpu_helpers import (DEV, assert_bf16_match, assert_codes_match_every_block, assert_scales,
+                         assert_periodic_codes, assert_periodic_decompress, fill_periodic,
                          bits_to_gpu, check_compress, check_decompress, check_reduce, cpu,
                          f32_to_gpu, gpu_bf16_bits, say, u8_to_gpu)
 from tiecheck import assert_codes_match, assert_rel_close
@@ -945,6 +946,22 @@ def test_accumulate_zero_main_gradient_equals_compress(oracle, tfp8):
     check_compress(oracle, tfp8, g, B, what="compress of the same gradient")
 
 
+def _seven_parts(tile, seed, dtype="bf16"):
+    """Seven independent random tiles of `tile` elements, part w scaled by 2^(w - 3), as
+    bfloat16 bits or float32.  A block read from another tile differs in its codes as well as
+    in alpha: a power-of-two scaling of one tile would change alpha alone and leave the codes
+    identical."""
+    parts = []
+    for w in range(7):
+        if dtype == "f32":
+            rng = np.random.default_rng(seed + w)
+            parts.append((rng.standard_normal(tile) * (0.05 * 2.0 ** (w - 3))).astype(np.float32))
+        else:
+            v = bf16_bits_to_f32(random_bf16_bits(tile, seed=seed + w, scale=0.05))
+            parts.append(f32_to_bf16_bits(v * np.float32(2.0 ** (w - 3))))
+    return parts
+
+
 def _tiled_input(scaled, n, tile):
     """Tile t of the input is scaled[t mod 7] (the last one cut to what is left of n)."""
     x = np.empty(n, scaled[0].dtype)
@@ -983,17 +1000,14 @@ def test_compress_both_launch_shapes(oracle, tfp8, dtype, B, extra_blocks):
     # workgroup in dispatch order, from 1.5 GiB one wavefront per workgroup with each XCD on a
     # contiguous eighth of the tiles (grid rounded up to a multiple of 8).  Inputs just below
     # and above the switch, each with a ragged last tile (block count not a multiple of 8).  The
-    # input is one random tile of 2^20 elements in seven power-of-two scalings, so a block read
-    # from the wrong place shows; every block is checked.  At B = 64 a tile is 16 blocks, a pair
+    # input repeats seven random tiles of 2^20 elements, so a block read from the wrong place
+    # shows; every block is checked.  At B = 64 a tile is 16 blocks, a pair
     # per lane group, and an odd block count leaves the last pair with one block.
     tile = 1 << 20
     esize = 2 if dtype == "bf16" else 4
     nb = (3 << 29) // esize // B + extra_blocks
     n = nb * B
-    base = bf16_bits_to_f32(random_bf16_bits(tile, seed=1536, scale=0.05))
-    scaled = [base * np.float32(2.0 ** (t - 3)) for t in range(7)]
-    if dtype == "bf16":
-        scaled = [f32_to_bf16_bits(v) for v in scaled]
+    scaled = _seven_parts(tile, 1536, dtype)
     x = _tiled_input(scaled, n, tile)
     say(f"  launch shapes: {dtype}, {n * esize / 2**30:.4f} GiB of input, nb = {nb}, every block")
     xg = (bits_to_gpu(x) if dtype == "bf16" else f32_to_gpu(x))
@@ -1012,8 +1026,7 @@ def test_compress_large_input_every_block_size_and_variant(oracle, tfp8):
     # last tile), and every flag set at B = 128 and B = 64; every block checked.
     tile = 1 << 20
     n_all = ((3 << 29) // 2 // 128 + 13) * 128
-    base = bf16_bits_to_f32(random_bf16_bits(tile, seed=1537, scale=0.05))
-    scaled = [f32_to_bf16_bits(base * np.float32(2.0 ** (t - 3))) for t in range(7)]
+    scaled = _seven_parts(tile, 1537)
     xg = bits_to_gpu(_tiled_input(scaled, n_all, tile))
     cases = [(64, 0), (256, 0), (512, 0), (128, 1), (128, 2), (128, 3), (64, 2), (64, 1)]
     for B, flags in cases:
@@ -1028,143 +1041,106 @@ def test_compress_large_input_every_block_size_and_variant(oracle, tfp8):
         del q, a, s
 
 
-def test_offsets_beyond_2_31_elements(oracle, tfp8):
-    # n = 513 * 2^22 > 2^31 elements: element indexes pass 2^31, bfloat16 byte offsets pass
-    # 2^32 and code byte offsets pass 2^31.  The input is one random tile of 2^22 elements in
-    # seven power-of-two scalings (tile t scaled by 2^((t mod 7) - 3)), so a read at an offset
-    # cut to 32 bits (512 tiles away) lands on a tile of another scale.  Each stage is fed the
-    # oracle's output of the stage before; outputs are compared on sampled blocks: both ends,
-    # the 128 blocks around element 2^31, and 2048 random blocks.
-    B, T, tile, ntiles = 128, 1.0, 1 << 22, 513
-    n, nb, shift = ntiles * tile, ntiles * tile // B, tile // B
-    base = bf16_bits_to_f32(random_bf16_bits(tile, seed=2031, scale=0.05))
-    variants = [f32_to_bf16_bits(base * np.float32(2.0 ** ((t % 7) - 3))) for t in range(7)]
-    x = np.empty(n, np.uint16)
-    for t in range(ntiles):
-        x[t * tile:(t + 1) * tile] = variants[t % 7]
-    b31 = (1 << 31) // B
-    rng = np.random.default_rng(2031)
-    idx = np.unique(np.concatenate([np.arange(64), np.arange(nb - 64, nb),
-                                    np.arange(b31 - 64, b31 + 64), rng.integers(0, nb, 2048)]))
-    idx_g = torch.from_numpy(idx).to(DEV)
-    prev = (idx - shift) % nb  # block k of a copy rolled by one tile holds block k - shift
-    blocks = lambda a, rows: np.ascontiguousarray(np.asarray(a).reshape(nb, -1)[rows]).reshape(-1)
-    say(f"  offsets: n = 2^31 + {n - (1 << 31)}, {idx.size} sampled blocks")
+# (block, input dtype, tiles of 2^22 elements).  At 513 tiles (2^31 + 2^22 - 37 B elements)
+# element indexes pass 2^31, bfloat16 byte offsets 2^32, float32 ones 2^33 and code byte offsets
+# 2^31, in the launches with a wavefront for every tile.  The larger cases pass the size at
+# which the launches are capped at 2^30 work-items and their wavefronts loop over tiles,
+# loading the next tile before working on the current one: 2^34 elements at B = 64 and 128
+# (2^33 for decompress at B = 64), and 2^35 for compress, decompress and accumulate at B = 256.
+_LARGE_CASES = [(128, "bf16", 513), (64, "bf16", 513), (512, "bf16", 513), (128, "f32", 513),
+                (128, "bf16", 4097), (64, "bf16", 4097), (128, "f32", 4097), (256, "bf16", 8193)]
 
-    q_o, a_o, s_o = oracle.compress(x, B, T)  # every block: the later stages' input
-    xg = bits_to_gpu(x)
+
+@pytest.mark.parametrize("B,dtype,ntiles", _LARGE_CASES)
+def test_large_offsets_and_grid_stride_loops_every_block(oracle, tfp8, B, dtype, ntiles):
+    # n = ntiles * 2^22 - 37 B elements (4.3-69 GB of input, a ragged last tile), built on the
+    # GPU from seven random tiles of 2^22 elements (tile t is part t mod 7), so that a read at
+    # an offset cut to 32 bits (1024 tiles away for codes, 512 for bfloat16, 256 for float32)
+    # or any other wrong place shows.  Compress, decompress to bfloat16 and float32, the reduce
+    # and accumulate each run on the whole tensor; every output block is checked against the
+    # oracle's output for its part.  No expected value comes from the GPU.
+    T, tile = 1.0, 1 << 22
+    n = ntiles * tile - 37 * B
+    nb, bpt = n // B, tile // B
+    f32 = dtype == "f32"
+    variants = _seven_parts(tile, 2034 + 8 * B, dtype)
+    enc = [oracle.compress(v, B, T, with_quot=True) for v in variants]
+    say(f"  large input B={B} {dtype}: n = {n} ({n * (4 if f32 else 2) / 1e9:.1f} GB of "
+        f"input), every block")
+
+    def input_on_gpu():
+        if f32:
+            return fill_periodic(torch.empty(n, dtype=torch.float32, device=DEV), variants, tile)
+        return fill_periodic(torch.empty(n, dtype=torch.int16, device=DEV),
+                             [v.view(np.int16) for v in variants], tile).view(torch.bfloat16)
+
+    def codes_on_gpu(parts):
+        # the oracle's codes, alpha and s of the seven tiles, tiled like the input
+        q = torch.empty(n, dtype=torch.uint8, device=DEV)
+        a, s = (torch.empty(nb, dtype=torch.float32, device=DEV) for _ in range(2))
+        return (fill_periodic(q, [e[0] for e in parts], tile),
+                fill_periodic(a, [e[1] for e in parts], bpt),
+                fill_periodic(s, [e[2] for e in parts], bpt))
 
     # compress
-    q, a, s = tfp8.compress(xg, B, T)
+    x = input_on_gpu()
+    q, a, s = tfp8.compress(x, B, T)
     torch.cuda.synchronize()
-    rq, ra, rs, rt = oracle.compress(blocks(x, idx), B, T, with_quot=True)
-    nmis = assert_codes_match(cpu(q.view(nb, B)[idx_g]).reshape(-1), rq, rt, what="offsets compress")
-    assert_scales(cpu(a[idx_g]), cpu(s[idx_g]), ra, rs, what="offsets compress")
+    del x
+    torch.cuda.empty_cache()
+    nmis, ea, es = assert_periodic_codes(q, a, s, enc, n, tile, B, what="large compress")
     del q, a, s
-    say(f"  offsets compress: tie mismatches {nmis}")
+    torch.cuda.empty_cache()
+    say(f"  large compress: tie mismatches {nmis}, max rel err alpha {ea:.2e} s {es:.2e}")
 
-    # decompress of the oracle's codes
-    qg, ag, sg = u8_to_gpu(q_o), f32_to_gpu(a_o), f32_to_gpu(s_o)
-    out = tfp8.decompress(qg, ag, sg, B, torch.bfloat16)
-    torch.cuda.synchronize()
-    got = out.view(nb, B)[idx_g].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
-    del out
-    qi, ai, si = blocks(q_o, idx), a_o[idx], s_o[idx]
-    assert_bf16_match(got, oracle.decompress(qi, ai, si, B, np.uint16),
-                      oracle.decompress_f64(qi, ai, si, B), what="offsets decompress")
+    # decompress of the oracle's codes, bfloat16 and float32
+    qg, ag, sg = codes_on_gpu(enc)
+    dec = [(e[0], e[1], e[2]) for e in enc]
+    r64 = [oracle.decompress_f64(*d, B) for d in dec]
+    for odt, ndt in ((torch.bfloat16, np.uint16), (torch.float32, np.float32)):
+        out = tfp8.decompress(qg, ag, sg, B, odt)
+        torch.cuda.synchronize()
+        refs = [(oracle.decompress(*d, B, ndt), r) for d, r in zip(dec, r64)]
+        nt = assert_periodic_decompress(out, refs, n, tile, B, what=f"large decompress {odt}")
+        del out
+        torch.cuda.empty_cache()
+        say(f"  large decompress {odt}: " + (f"bf16 tie mismatches {nt}" if nt or ndt == np.uint16
+                                             else "every output within 1e-6"))
+    del r64
 
-    # reduce: contribution 0 = the oracle's codes, contribution 1 = the same rolled by one tile
+    # reduce, P = 2: row 0 the tiled codes, row 1 the same tiles three parts on
     sq = torch.empty((2, n), dtype=torch.uint8, device=DEV)
     sa = torch.empty((2, nb), dtype=torch.float32, device=DEV)
     ss = torch.empty((2, nb), dtype=torch.float32, device=DEV)
-    sq[0] = qg; sq[1, tile:] = qg[:-tile]; sq[1, :tile] = qg[-tile:]
-    for dst, src in ((sa, ag), (ss, sg)):
-        dst[0] = src; dst[1, shift:] = src[:-shift]; dst[1, :shift] = src[-shift:]
+    sq[0], sa[0], ss[0] = qg, ag, sg
+    other = [enc[(w + 3) % 7] for w in range(7)]
+    fill_periodic(sq[1], [e[0] for e in other], tile)
+    fill_periodic(sa[1], [e[1] for e in other], bpt)
+    fill_periodic(ss[1], [e[2] for e in other], bpt)
     cq, ca, cs = tfp8.reduce_fp8(sq, sa, ss, B, T)
     torch.cuda.synchronize()
     del sq, sa, ss
-    rq, ra, rs, rt = oracle.reduce_fp8(np.stack([qi, blocks(q_o, prev)]),
-                                       np.stack([ai, a_o[prev]]), np.stack([si, s_o[prev]]), B, T,
-                                       with_quot=True)
-    assert_codes_match(cpu(cq.view(nb, B)[idx_g]).reshape(-1), rq, rt, what="offsets reduce")
-    assert_scales(cpu(ca[idx_g]), cpu(cs[idx_g]), ra, rs, what="offsets reduce")
+    torch.cuda.empty_cache()
+    refs = [oracle.reduce_fp8(np.stack([e[0], o[0]]), np.stack([e[1], o[1]]),
+                              np.stack([e[2], o[2]]), B, T, with_quot=True)
+            for e, o in zip(enc, other)]
+    nmis, ea, es = assert_periodic_codes(cq, ca, cs, refs, n, tile, B, what="large reduce")
     del cq, ca, cs
+    torch.cuda.empty_cache()
+    say(f"  large reduce: tie mismatches {nmis}, max rel err alpha {ea:.2e} s {es:.2e}")
 
-    # accumulate in place: main gradient = the oracle's codes, local gradient = x rolled by a tile
-    xr = torch.roll(xg, tile)
-    del xg
-    tfp8.accumulate(qg, ag, sg, xr, B, T, inplace=True)
-    torch.cuda.synchronize()
-    rq, ra, rs, rt = oracle.accumulate(qi, ai, si, blocks(x, prev), B, T, with_quot=True)
-    assert_codes_match(cpu(qg.view(nb, B)[idx_g]).reshape(-1), rq, rt, what="offsets accumulate")
-    assert_scales(cpu(ag[idx_g]), cpu(sg[idx_g]), ra, rs, what="offsets accumulate")
-
-
-def test_grid_stride_loops_beyond_2_34_elements(oracle, tfp8):
-    # A launch covers at most 2^30 work-items: from 2^34 elements on (B = 128) the wavefronts of
-    # compress, decompress and accumulate loop over tiles, loading the next tile before working
-    # on the current one.  n = 4097 * 2^22 - 37 * 128 elements (34 GB of bfloat16, a ragged last
-    # tile), built on the GPU from one random tile of 2^22 elements in seven power-of-two
-    # scalings (tile t scaled by 2^((t mod 7) - 3)), so that a block read from the wrong place
-    # shows.  Expected values come from the host copies of the seven variants, never from the
-    # GPU.  Sampled blocks: both ends, the first loop iteration's first blocks (block 2^27),
-    # the blocks around element 2^31 and 2048 random blocks.
-    B, T, tile, ntiles = 128, 1.0, 1 << 22, 4097
-    n = ntiles * tile - 37 * B
-    nb, bpt = n // B, tile // B
-    base = bf16_bits_to_f32(random_bf16_bits(tile, seed=2034, scale=0.05))
-    variants = [f32_to_bf16_bits(base * np.float32(2.0 ** ((t % 7) - 3))) for t in range(7)]
-    enc = [oracle.compress(v, B, T) for v in variants]  # the decompress / accumulate input
-    rng = np.random.default_rng(2034)
-    b27, b31 = 1 << 27, (1 << 31) // B
-    idx = np.unique(np.concatenate([np.arange(64), np.arange(nb - 64, nb),
-                                    np.arange(b27 - 64, b27 + 64), np.arange(b31 - 64, b31 + 64),
-                                    rng.integers(0, nb, 2048)]))
-    idx_g = torch.from_numpy(idx).to(DEV)
-    which, off = (idx // bpt) % 7, idx % bpt  # variant and block within the tile
-    hx = np.concatenate([variants[w].reshape(bpt, B)[o] for w, o in zip(which, off)])
-    hq = np.concatenate([enc[w][0].reshape(bpt, B)[o] for w, o in zip(which, off)])
-    ha = np.array([enc[w][1][o] for w, o in zip(which, off)], np.float32)
-    hs = np.array([enc[w][2][o] for w, o in zip(which, off)], np.float32)
-    say(f"  grid-stride loops: n = {n} ({2 * n / 1e9:.1f} GB of bf16), {idx.size} sampled blocks")
-
-    def tiled(parts, per_tile, dtype, count):
-        # `count` elements made of tile-sized copies of parts[t % 7], filled on the GPU
-        out = torch.empty(ntiles * per_tile, dtype=dtype, device=DEV)
-        src = [torch.from_numpy(np.ascontiguousarray(v)).to(DEV) for v in parts]
-        for t in range(ntiles):
-            out[t * per_tile:(t + 1) * per_tile] = src[t % 7]
-        return out[:count]
-
-    x = tiled([v.view(np.int16) for v in variants], tile, torch.int16, n).view(torch.bfloat16)
-    q, a, s = tfp8.compress(x, B, T)
-    torch.cuda.synchronize()
-    rq, ra, rs, rt = oracle.compress(hx, B, T, with_quot=True)
-    nmis = assert_codes_match(cpu(q.view(nb, B)[idx_g]).reshape(-1), rq, rt,
-                              what="grid-stride compress")
-    assert_scales(cpu(a[idx_g]), cpu(s[idx_g]), ra, rs, what="grid-stride compress")
-    del q, a, s
-    say(f"  grid-stride compress: tie mismatches {nmis}")
-
-    qg = tiled([e[0] for e in enc], tile, torch.uint8, n)
-    ag = tiled([e[1] for e in enc], bpt, torch.float32, nb)
-    sg = tiled([e[2] for e in enc], bpt, torch.float32, nb)
-    out = tfp8.decompress(qg, ag, sg, B, torch.bfloat16)
-    torch.cuda.synchronize()
-    got = out.view(nb, B)[idx_g].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
-    del out
-    assert_bf16_match(got, oracle.decompress(hq, ha, hs, B, np.uint16),
-                      oracle.decompress_f64(hq, ha, hs, B), what="grid-stride decompress")
-
-    # accumulate in place: main gradient = the tiled codes, local gradient = x
+    # accumulate in place: main gradient = the tiled codes, local gradient = the input
+    x = input_on_gpu()
     tfp8.accumulate(qg, ag, sg, x, B, T, inplace=True)
     torch.cuda.synchronize()
-    rq, ra, rs, rt = oracle.accumulate(hq, ha, hs, hx, B, T, with_quot=True)
-    assert_codes_match(cpu(qg.view(nb, B)[idx_g]).reshape(-1), rq, rt,
-                       what="grid-stride accumulate")
-    assert_scales(cpu(ag[idx_g]), cpu(sg[idx_g]), ra, rs, what="grid-stride accumulate")
-    del x, qg, ag, sg
+    del x
+    refs = [oracle.accumulate(e[0], e[1], e[2], v, B, T, with_quot=True)
+            for e, v in zip(enc, variants)]
+    nmis, ea, es = assert_periodic_codes(qg, ag, sg, refs, n, tile, B,
+                                         what="large accumulate")
+    del qg, ag, sg
     torch.cuda.empty_cache()
+    say(f"  large accumulate: tie mismatches {nmis}, max rel err alpha {ea:.2e} s {es:.2e}")
 
 
 def _sweep_input(rng, nb, B):
