@@ -167,11 +167,11 @@ struct CompressIn {
   u32x4 d[kLoads];
 };
 
-// Lane j of a block's group holds the runs of 8 elements [RS g + 8 j, RS g + 8 j + 8), where
-// RS = 8 L is the run stride for L lanes per block.
-// The same, from the base of a tile (wave-uniform, so it stays in scalar registers) and a lane's
-// 32-bit element offset into it: the loads then take the scalar base plus a vector offset, and
-// no 64-bit address arithmetic runs per lane.  Run g is read at off + g * step.
+// Lane j of a block's group holds the runs of 8 elements [RS g + 8 j, RS g + 8 j + 8) of its
+// block, where RS = 8 L is the run stride for L lanes per block.  Compress reads them from
+// the base of a tile (wave-uniform, so it stays in scalar registers) and a lane's 32-bit
+// element offset into it: the loads then take the scalar base plus a vector offset, and no
+// 64-bit address arithmetic runs per lane.  Run g is read at off + g * step.
 template <int B, bool F32IN>
 __device__ __forceinline__ void load_compress_at(CompressIn<B, F32IN> &in, const void *tile,
                                                  uint32_t off, uint32_t step) {
@@ -190,6 +190,7 @@ __device__ __forceinline__ void load_compress_at(CompressIn<B, F32IN> &in, const
   }
 }
 
+// The same runs of block blk, for accumulate.
 template <int B, bool F32IN>
 __device__ __forceinline__ void load_compress_in(CompressIn<B, F32IN> &in, const void *xin,
                                                  int64_t blk, int j) {
@@ -213,7 +214,8 @@ __device__ __forceinline__ void load_compress_in(CompressIn<B, F32IN> &in, const
 // blocks, one per 64-element run (lane j: elements [8 j, 8 j + 8) of each), so that its loads
 // and stores cover whole 128-byte lines exactly as at B = 128; the transform, the statistics and
 // the scales are then taken per run.  (With 4 lanes per block each load instruction read half a
-// line and each store wrote 32 bytes, and compress ran at 67% of HBM peak against 81%.)
+// line and each store wrote 32 bytes: 524 us, 70% of HBM peak, against 485 us with the pair
+// layout on 8 stacked 117 M-element shards.)
 constexpr int compress_blocks_per_group(int B) { return B == 64 ? 2 : 1; }
 
 // LOOP = false: the launch has a wavefront for every tile (the host checks), so each wavefront
@@ -838,23 +840,6 @@ __global__ __launch_bounds__(kThreads) void k_accumulate(
   }
 }
 
-// One set-aside block, by the group of L lanes j = 0..L-1 that holds it (lane layout of
-// k_accumulate).  Its codes and s are still those of the main gradient (never written) and
-// alpha_out holds -alpha.  `active` = 0: work on the block but store nothing.  Lane j reads codes
-// at positions 8 qj and writes them at 8 pj, where another lane of the group read; in place that
-// is safe because every stored value depends, through the lane exchanges, on all of the group's
-// loaded codes, so the group's loads have completed before any of its stores.
-//
-// The sum is formed with the roundings of the plain definition, so that it is exact wherever
-// the terms cancel exactly.  The transform of the decoded codes is exact: the first stages in
-// float32 (3 within each run of 8 registers, log2(L) across the lanes: partial sums of multiples
-// of 2^-9 below 64 * 448 < 2^15), the remaining ones in float64.  Multiplying it by s is exact
-// too (24 + 27 significant bits), the divisions by sqrt(B) and by alpha round once each, and
-// adding g rounds once: z matches the float64 reconstruction plus g bit for bit.  Everything
-// after z errs relative to z itself.  z is rotated as compress rotates its input: scaled by
-// 2^(K - E) with max|z| < 2^E and split into integers r = rint(t) and remainders l = t - r in
-// [-1/2, 1/2].  |r| <= 2^K with K = 24 - log2(B), so every partial sum of H r is an integer of
-// at most 2^24 and the transform of r is exact; the transform of l errs by ~2^-18 of 2^K at most.
 // The inputs of one set-aside block, as lane j of its group reads them.
 template <int B, bool F32IN>
 struct FixIn {
@@ -883,6 +868,23 @@ __device__ __forceinline__ void load_fix_in(FixIn<B, F32IN> &f, const uint8_t *c
   f.ap = -alpha_out[blk];
 }
 
+// One set-aside block, by the group of L lanes j = 0..L-1 that holds it (lane layout of
+// k_accumulate).  Its codes and s are still those of the main gradient (never written) and
+// alpha_out holds -alpha.  `active` = 0: work on the block but store nothing.  Lane j reads codes
+// at positions 8 qj and writes them at 8 pj, where another lane of the group read; in place that
+// is safe because every stored value depends, through the lane exchanges, on all of the group's
+// loaded codes, so the group's loads have completed before any of its stores.
+//
+// The sum is formed with the roundings of the plain definition, so that it is exact wherever
+// the terms cancel exactly.  The transform of the decoded codes is exact: the first stages in
+// float32 (3 within each run of 8 registers, log2(L) across the lanes: partial sums of multiples
+// of 2^-9 below 64 * 448 < 2^15), the remaining ones in float64.  Multiplying it by s is exact
+// too (24 + 27 significant bits), the divisions by sqrt(B) and by alpha round once each, and
+// adding g rounds once: z matches the float64 reconstruction plus g bit for bit.  Everything
+// after z errs relative to z itself.  z is rotated as compress rotates its input: scaled by
+// 2^(K - E) with max|z| < 2^E and split into integers r = rint(t) and remainders l = t - r in
+// [-1/2, 1/2].  |r| <= 2^K with K = 24 - log2(B), so every partial sum of H r is an integer of
+// at most 2^24 and the transform of r is exact; the transform of l errs by ~2^-18 of 2^K at most.
 template <int B, bool F32IN, int FLAGS>
 __device__ __forceinline__ void accumulate_block_split(
     const FixIn<B, F32IN> &f, int64_t blk, bool active, int j, float TBB, float C, double root_b,
@@ -906,7 +908,8 @@ __device__ __forceinline__ void accumulate_block_split(
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) widen_bf16x2(in.d[g][q], gv[8 * g + 2 * q], gv[8 * g + 2 * q + 1]);
+      for (int q = 0; q < 4; ++q)
+        widen_bf16x2(in.d[g][q], gv[8 * g + 2 * q], gv[8 * g + 2 * q + 1]);
   } else {
 #pragma unroll
     for (int g = 0; g < G; ++g)
@@ -1203,8 +1206,8 @@ tfp8_status launch(void (*kernel)(KArgs...), unsigned grid, int threads, hipStre
 }
 
 template <int B, bool F32, int FLAGS>
-tfp8_status launch_compress_t(const void *x, int64_t nb, float target, uint8_t *codes, float *alpha,
-                       float *scale, hipStream_t st) {
+tfp8_status launch_compress_t(const void *x, int64_t nb, float target, uint8_t *codes,
+                              float *alpha, float *scale, hipStream_t st) {
   constexpr bool ROT = !(FLAGS & kNoRotation);
   const double Q = qmax_of<FLAGS>();
   // energy of v: sum(v^2) = B sum(x^2) with the (unnormalised) rotation, sum(x^2) without
@@ -1241,8 +1244,8 @@ tfp8_status launch_compress(const void *x, int64_t nb, float target, uint32_t fl
 }
 
 template <int B, bool F32, int FLAGS>
-tfp8_status launch_decompress_t(const uint8_t *codes, const float *alpha, const float *scale, int64_t nb,
-                         void *out, hipStream_t st) {
+tfp8_status launch_decompress_t(const uint8_t *codes, const float *alpha, const float *scale,
+                                int64_t nb, void *out, hipStream_t st) {
   constexpr bool ROT = !(FLAGS & kNoRotation);
   const float inv_sqrt_b = ROT ? (float)(1.0 / sqrt((double)B)) : 1.0f;
   constexpr int BPW = 64 / decompress_lanes(B);  // blocks per tile
@@ -1305,8 +1308,8 @@ tfp8_status launch_reduce(const uint8_t *codes, const float *alpha, const float 
 
 template <int B, bool F32, int FLAGS>
 tfp8_status launch_accumulate_t(const uint8_t *codes, const float *alpha, const float *scale,
-                         const void *grad, int64_t nb, float target, uint8_t *codes_out,
-                         float *alpha_out, float *scale_out, hipStream_t st) {
+                                const void *grad, int64_t nb, float target, uint8_t *codes_out,
+                                float *alpha_out, float *scale_out, hipStream_t st) {
   constexpr bool ROT = !(FLAGS & kNoRotation);
   const double Q = qmax_of<FLAGS>();
   const double TBBd = (double)target * B * (ROT ? B : 1);  // exact: powers of two

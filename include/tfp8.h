@@ -146,9 +146,9 @@ tfp8_status tfp8_reduce_strided(const uint8_t *codes, int64_t codes_stride, cons
  * names FP16/BF16 as its minimum precision); blocks where the two terms cancel to under half of
  * the larger one are redone by a second kernel that forms the sum in float64 with the roundings of
  * the definition (reconstruction, then + grad), so that terms which cancel exactly give exactly
- * zero and every later error is relative to the sum.  Unlike the other calls this one may work in place:
- * each of codes_out, alpha_out, scale_out may be exactly its input (any other overlap is
- * TFP8_E_ARG).  grad must be 16-byte aligned. */
+ * zero and every later error is relative to the sum.  Unlike the other calls this one may work
+ * in place: each of codes_out, alpha_out, scale_out may be exactly its input (any other overlap
+ * is TFP8_E_ARG).  grad must be 16-byte aligned. */
 tfp8_status tfp8_accumulate(const uint8_t *codes, const float *alpha, const float *scale,
                             const void *grad, tfp8_dtype grad_dtype, int64_t n, int32_t block,
                             float target, uint32_t flags, uint8_t *codes_out, float *alpha_out,
