@@ -2,13 +2,14 @@
 
 Thin binding of the C ABI in ``include/tfp8.h`` (``libtfp8.so``, built in this directory by
 ``build.py``).  This module only marshals arguments: PyTorch supplies device memory and the
-current HIP stream, and every step of compress / decompress / reduce runs in the library's
-kernels.  There is no CPU path: without the built library, or for tensors not on a GPU, the
-calls raise.
+current HIP stream, and every step of compress, decompress, the reduce and the accumulation runs
+in the library's kernels.  There is no CPU path: without the built library, or for tensors not
+on a GPU, the calls raise.
 
 Method: page "TACO: Efficient Communication Compression of Intermediate Tensors for Scalable
-Tensor-Parallel LLM Training" (section 2.B.1-2.B.2); local reduce: page "AGoQ: Activation and
-Gradient Quantization for Memory-Efficient Distributed Training of LLMs" (section 2.B).
+Tensor-Parallel LLM Training" (section 2.B.1-2.B.2); local reduce and gradient accumulation:
+page "AGoQ: Activation and Gradient Quantization for Memory-Efficient Distributed Training of
+LLMs" (section 2.B).
 """
 from __future__ import annotations
 
@@ -273,7 +274,8 @@ def reduce_fp8(codes: torch.Tensor, alpha: torch.Tensor, scale: torch.Tensor, bl
         codes_out, alpha_out, scale_out = out
         _need_gpu(codes_out, alpha_out, scale_out)
         if codes_out.device != codes.device:
-            raise ValueError(f"tensors on different devices ({codes.device} and {codes_out.device})")
+            raise ValueError(
+                f"tensors on different devices ({codes.device} and {codes_out.device})")
         _need_buf(codes_out, torch.uint8, n, "codes_out")
         _need_buf(alpha_out, torch.float32, nb, "alpha_out")
         _need_buf(scale_out, torch.float32, nb, "scale_out")
@@ -292,7 +294,8 @@ def reduce_fp8(codes: torch.Tensor, alpha: torch.Tensor, scale: torch.Tensor, bl
 
 
 def accumulate(codes: torch.Tensor, alpha: torch.Tensor, scale: torch.Tensor, grad: torch.Tensor,
-               block: int = 128, target: float = 1.0, out=None, flags: int = 0, inplace: bool = False):
+               block: int = 128, target: float = 1.0, out=None, flags: int = 0,
+               inplace: bool = False):
     """Compressed main gradient + dense local gradient (bfloat16 or float32, same numel) ->
     compressed sum.  inplace=True overwrites (codes, alpha, scale) and returns them."""
     _need_gpu(codes, alpha, scale, grad)
@@ -315,10 +318,11 @@ def accumulate(codes: torch.Tensor, alpha: torch.Tensor, scale: torch.Tensor, gr
         out = (torch.empty_like(codes), torch.empty_like(alpha), torch.empty_like(scale))
     else:
         _need_gpu(codes, *out)
-        for t, ref, name in zip(out, (codes, alpha, scale), ("codes_out", "alpha_out", "scale_out")):
+        names = ("codes_out", "alpha_out", "scale_out")
+        for t, ref, name in zip(out, (codes, alpha, scale), names):
             _need_buf(t, ref.dtype, ref.numel(), name)
     with torch.cuda.device(codes.device):
-        _check(accumulate_raw(codes.data_ptr(), alpha.data_ptr(), scale.data_ptr(), grad.data_ptr(),
-                              dt, n, block, float(target), out[0].data_ptr(), out[1].data_ptr(),
-                              out[2].data_ptr(), _stream(codes), flags))
+        _check(accumulate_raw(codes.data_ptr(), alpha.data_ptr(), scale.data_ptr(),
+                              grad.data_ptr(), dt, n, block, float(target), out[0].data_ptr(),
+                              out[1].data_ptr(), out[2].data_ptr(), _stream(codes), flags))
     return out
