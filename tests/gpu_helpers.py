@@ -38,17 +38,23 @@ def gpu_bf16_bits(t: torch.Tensor) -> np.ndarray:
     return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
+ALPHA_MIN, ALPHA_MAX = 2.0 ** -126, 2.0 ** 126
+
+
 def assert_scales(alpha, scale, ref_alpha, ref_scale, what="scales"):
-    """Per block: alpha and s within 1e-6 relative; zero blocks exactly (alpha 1, s 0);
-    a clamped alpha exactly."""
+    """Per block: alpha and s within 1e-6 relative; zero blocks exactly (alpha 1, s 0); every
+    alpha inside the clamp range [2^-126, 2^126].  A clamped alpha is held to the same bar, so
+    it is the bound or a value inside the range within 1e-6 of it, not the bound exactly: a block
+    whose exact alpha is the bound itself (or within the kernel's few-ulp alpha error of it) is
+    clamped by the oracle and may land one float inside the range on the GPU."""
     alpha = np.asarray(alpha, np.float32).reshape(-1)
     scale = np.asarray(scale, np.float32).reshape(-1)
     ref_alpha = np.asarray(ref_alpha, np.float32).reshape(-1)
     ref_scale = np.asarray(ref_scale, np.float32).reshape(-1)
     zero = ref_scale == 0
     assert np.all(scale[zero] == 0) and np.all(alpha[zero] == 1), f"{what}: zero blocks differ"
-    clamped = (ref_alpha == np.float32(2.0 ** 126)) | (ref_alpha == np.float32(2.0 ** -126))
-    assert np.array_equal(alpha[clamped], ref_alpha[clamped]), f"{what}: clamped alpha differs"
+    inside = (alpha >= ALPHA_MIN) & (alpha <= ALPHA_MAX)
+    assert inside.all(), f"{what}: {int((~inside).sum())} alpha outside the clamp range"
     ea = assert_rel_close(alpha, ref_alpha, 1e-6, what=what + " alpha")
     es = assert_rel_close(scale, ref_scale, 1e-6, what=what + " scale")
     return ea, es
@@ -214,8 +220,9 @@ def assert_periodic_codes(q, a, s, refs, n: int, tile: int, B: int, what: str, f
     quotients), the oracle's output for part w.  Codes and scales are compared on the GPU block
     by block; the blocks that hold a code mismatch are fetched, every mismatch must be an
     admissible tie and their count is held to the cap over the whole tensor.  alpha and s follow
-    the rule of assert_scales (1e-6 relative; zero blocks alpha 1, s 0; a clamped alpha
-    exactly).  Returns (tie mismatches, max rel err alpha, max rel err s)."""
+    the rule of assert_scales (1e-6 relative; zero blocks alpha 1, s 0; every alpha inside the
+    clamp range, a clamped one within 1e-6 of its bound).  Returns (tie mismatches, max rel err
+    alpha, max rel err s)."""
     nb, bpt = n // B, tile // B
     hq = np.stack([np.asarray(r[0], np.uint8).reshape(bpt, B) for r in refs])
     ht = np.stack([np.asarray(r[3], np.float64).reshape(bpt, B) for r in refs])
@@ -233,7 +240,7 @@ def assert_periodic_codes(q, a, s, refs, n: int, tile: int, B: int, what: str, f
         da, ds = (ga - ea).abs(), (gs - es).abs()
         ok = (da <= 1e-6 * ea.abs()) & (ds <= 1e-6 * es.abs())
         ok &= (es != 0) | ((gs == 0) & (ga == 1))
-        ok &= ((ea != 2.0 ** 126) & (ea != 2.0 ** -126)) | (ga == ea)
+        ok &= (ga >= ALPHA_MIN) & (ga <= ALPHA_MAX)
         nviol += (~ok).sum()
         zero = torch.zeros((), dtype=torch.float64, device=DEV)
         worst = torch.maximum(worst, torch.stack([

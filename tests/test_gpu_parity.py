@@ -4,7 +4,7 @@ Each stage is fed the oracle's output of the stage before it, so a mismatch name
 the end-to-end test of the Qwen-shaped workload alone chains the GPU's own outputs, against the
 oracle's chain, within a bound derived from the per-stage bars.  Bars: codes identical except
 admissible rounding ties on <= 1e-4 of the elements; alpha and s within 1e-6 relative (zero
-blocks and clamped alpha exact); float32 reconstructions within 1e-6 relative (+ 2^-149
+blocks exact, alpha inside its clamp range); float32 reconstructions within 1e-6 relative (+ 2^-149
 absolute for subnormal results); bfloat16 reconstructions identical except double-rounding
 ties.
 """
@@ -272,6 +272,43 @@ def test_target_values(oracle, tfp8, T):
     check_reduce(oracle, tfp8, np.stack([e[0] for e in enc]), np.stack([e[1] for e in enc]),
                  np.stack([e[2] for e in enc]), 128, T, what=f"reduce T={T}")
     _check_accumulate(oracle, tfp8, q, a, s, xr[1], 128, f"accumulate T={T}", T=T)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("flags", [0, 1, 2, 3])
+def test_alpha_exactly_on_the_clamp_bounds(oracle, tfp8, dtype, flags):
+    # Blocks whose exact alpha = sqrt(T B / sum(x^2)) is exactly 2^126, or exactly 2^-126, with
+    # T B not a perfect square: the kernel's rounded sqrt(T B) and reciprocal square root may
+    # put alpha one float inside the clamp range where the oracle stores the bound itself.  The
+    # bar holds it to 1e-6, inside the range.  (A random sweep met such a block: float32
+    # subnormals whose alpha was exactly 2^126.)
+    B = 128
+
+    def blocks(parts):  # one block per (count, magnitude, first position), alternating signs
+        x = np.zeros((len(parts), B), np.float32)
+        for i, (count, mag, first) in enumerate(parts):
+            x[i, first:first + count] = mag * np.where(np.arange(count) % 2 == 0, 1.0, -1.0)
+        return x.reshape(-1)
+
+    cases = [
+        # T B = 12; sum(x^2) = 12 * 2^-252: alpha = 2^126
+        (3.0 / 32, 2.0 ** 126, [(3, 2.0 ** -125, 0), (3, 2.0 ** -125, 61), (12, 2.0 ** -126, 5),
+                                (48, 2.0 ** -127, 80)]),
+        # T B = 3 * 2^-53; sum(x^2) = 3 * 2^199: alpha = 2^-126
+        (3.0 * 2.0 ** -60, 2.0 ** -126, [(6, 2.0 ** 99, 0), (6, 2.0 ** 99, 122),
+                                         (24, 2.0 ** 98, 17)]),
+    ]
+    for T, bound, parts in cases:
+        x = blocks(parts)
+        if dtype == "bf16":
+            x = f32_to_bf16_bits(x)
+            assert np.array_equal(bf16_bits_to_f32(x), blocks(parts))  # exact in bfloat16
+        what = f"alpha on {bound:.3e}, {dtype} flags={flags}"
+        # these sparse power-of-two blocks put many rotated values exactly on code midpoints, so
+        # only admissibility is checked (a ledger lifts the per-call tie cap)
+        q, a, s = check_compress(oracle, tfp8, x, B, T=T, what=what, flags=flags, tie_ledger=[])
+        assert np.all(a == np.float32(bound)), (what, a)  # the construction reaches the bound
+        check_decompress(oracle, tfp8, q, a, s, B, what=what, flags=flags)
 
 
 def _every_value_blocks(dtype, qmax, low, B):
