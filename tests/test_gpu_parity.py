@@ -1084,8 +1084,11 @@ def test_compress_large_input_every_block_size_and_variant(oracle, tfp8):
 # which the launches are capped at 2^30 work-items and their wavefronts loop over tiles,
 # loading the next tile before working on the current one: 2^34 elements at B = 64 and 128
 # (2^33 for decompress at B = 64), and 2^35 for compress, decompress and accumulate at B = 256.
+# The reduce's tiles hold 1024 elements at every B, so it loops past 2^34 at B = 256 and 512
+# too; at B = 512 the other three still launch a wavefront per tile there.
 _LARGE_CASES = [(128, "bf16", 513), (64, "bf16", 513), (512, "bf16", 513), (128, "f32", 513),
-                (128, "bf16", 4097), (64, "bf16", 4097), (128, "f32", 4097), (256, "bf16", 8193)]
+                (128, "bf16", 4097), (64, "bf16", 4097), (128, "f32", 4097), (512, "bf16", 4097),
+                (256, "bf16", 8193)]
 
 
 @pytest.mark.parametrize("B,dtype,ntiles", _LARGE_CASES)
