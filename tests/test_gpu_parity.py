@@ -793,6 +793,92 @@ def test_concurrent_host_threads(tfp8):
                                v.view(torch.uint8) if v.dtype == torch.bfloat16 else v), k
 
 
+def _view_at(numel, byte_offset, dtype):
+    """A contiguous GPU view of `numel` elements starting `byte_offset` bytes past the start of a
+    fresh (256-byte aligned) allocation."""
+    esz = torch.empty(0, dtype=dtype).element_size()
+    assert byte_offset % esz == 0
+    big = torch.empty(numel + 256 // esz, dtype=dtype, device=DEV)
+    v = big[byte_offset // esz:byte_offset // esz + numel]
+    assert v.data_ptr() % 256 == byte_offset
+    return v
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("B", [64, 128, 256, 512])
+def test_buffers_at_minimal_alignment(oracle, tfp8, B, dtype):
+    # Every buffer at the smallest alignment the header allows, as views into larger
+    # allocations: inputs 48 bytes past a 256-byte boundary (so not 32-byte aligned either),
+    # codes and reconstructions 16 bytes past one, alpha and s 4 bytes past one.  Every result
+    # must equal that of the same call on fresh, 256-byte aligned buffers bit for bit; compress
+    # is also held to the oracle.
+    nb, P = 77, 3  # 77 blocks: a ragged last tile at every B
+    n = nb * B
+    rng = np.random.default_rng(4242 + B)
+    v = rng.laplace(0.0, 0.02, (P, n))
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    if dtype == "f32":
+        host = v.astype(np.float32)
+        xs = torch.from_numpy(host).to(DEV)
+    else:
+        host = f32_to_bf16_bits(v.astype(np.float32))
+        xs = torch.from_numpy(host.view(np.int16)).to(DEV).view(torch.bfloat16)
+
+    def odd_x(t):
+        xv = _view_at(t.numel(), 48, tdt)
+        xv.copy_(t.reshape(-1))
+        return xv
+
+    def odd_codes(count, p=1):
+        return (_view_at(p * count, 16, torch.uint8).view(p, count) if p > 1 else
+                _view_at(count, 16, torch.uint8))
+
+    def odd_scales(count, p=1):
+        t = _view_at(p * count, 4, torch.float32)
+        return t.view(p, count) if p > 1 else t
+
+    # compress of each contribution, on aligned and on offset buffers
+    stacks = [odd_codes(n, P), odd_scales(nb, P), odd_scales(nb, P)]
+    for p in range(P):
+        ref = tfp8.compress(xs[p], B, 1.0)
+        got = tfp8.compress(odd_x(xs[p]), B, 1.0,
+                            out=(stacks[0][p], stacks[1][p], stacks[2][p]))
+        torch.cuda.synchronize()
+        for g, r in zip(got, ref):
+            assert torch.equal(g.view(-1), r.view(-1)), f"compress B={B} {dtype} shard {p}"
+    qr, ar, sr, tr = oracle.compress(host[0], B, 1.0, with_quot=True)
+    # admissibility only: one tie would exceed 1e-4 of these 77 blocks
+    assert_codes_match(cpu(stacks[0][0]), qr, tr, max_frac=1.0, what=f"offset compress B={B}")
+    assert_scales(cpu(stacks[1][0]), cpu(stacks[2][0]), ar, sr, what=f"offset compress B={B}")
+
+    # decompress, both output dtypes
+    for odt in (torch.float32, torch.bfloat16):
+        ref = tfp8.decompress(stacks[0][0].clone(), stacks[1][0].clone(), stacks[2][0].clone(),
+                              B, odt)
+        out = _view_at(n, 16, odt)
+        tfp8.decompress(stacks[0][0], stacks[1][0], stacks[2][0], B, odt, out=out)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16 if odt == torch.bfloat16 else torch.int32),
+                           ref.view(torch.int16 if odt == torch.bfloat16 else torch.int32)), \
+            f"decompress B={B} {odt}"
+
+    # reduce of the three, contiguous stacks at offsets, outputs at offsets
+    ref = tfp8.reduce_fp8(stacks[0].clone(), stacks[1].clone(), stacks[2].clone(), B, 1.0)
+    outs = (odd_codes(n), odd_scales(nb), odd_scales(nb))
+    tfp8.reduce_fp8(stacks[0], stacks[1], stacks[2], B, 1.0, out=outs)
+    torch.cuda.synchronize()
+    for g, r in zip(outs, ref):
+        assert torch.equal(g, r), f"reduce B={B} {dtype}"
+
+    # accumulate in place on the offset buffers, against out of place on aligned ones
+    grad = odd_x(xs[1])
+    ref = tfp8.accumulate(outs[0].clone(), outs[1].clone(), outs[2].clone(), xs[1].clone(), B, 1.0)
+    tfp8.accumulate(outs[0], outs[1], outs[2], grad, B, 1.0, inplace=True)
+    torch.cuda.synchronize()
+    for g, r in zip(outs, ref):
+        assert torch.equal(g, r), f"accumulate B={B} {dtype}"
+
+
 def test_zero_length_is_noop(tfp8):
     x = torch.empty(0, dtype=torch.bfloat16, device=DEV)
     q, a, s = tfp8.compress(x, 128, 1.0)
