@@ -1124,8 +1124,8 @@ def test_compress_both_launch_shapes(oracle, tfp8, dtype, B, extra_blocks):
     # contiguous eighth of the tiles (grid rounded up to a multiple of 8).  Inputs just below
     # and above the switch, each with a ragged last tile (block count not a multiple of 8).  The
     # input repeats seven random tiles of 2^20 elements, so a block read from the wrong place
-    # shows; every block is checked.  At B = 64 a tile is 16 blocks, a pair
-    # per lane group, and an odd block count leaves the last pair with one block.
+    # shows; every block is checked.  At B = 64 a tile is 16 blocks, a pair per lane group, and
+    # an odd block count leaves the last pair with one block.
     tile = 1 << 20
     esize = 2 if dtype == "bf16" else 4
     nb = (3 << 29) // esize // B + extra_blocks
@@ -1144,9 +1144,9 @@ def test_compress_both_launch_shapes(oracle, tfp8, dtype, B, extra_blocks):
 
 
 def test_compress_large_input_every_block_size_and_variant(oracle, tfp8):
-    # Inputs of 1.5 GiB or more: the remapped launch at B >= 128 and the dispatch-order one at
-    # B = 64.  One 1.6 GB bf16 input, prefixes of it for every block size (each with a ragged
-    # last tile), and every flag set at B = 128 and B = 64; every block checked.
+    # Inputs of 1.5 GiB or more take the remapped launch at every block size.  One 1.6 GB bf16
+    # input, prefixes of it for every block size (each with a ragged last tile), and every flag
+    # set at B = 128 and B = 64; every block checked.
     tile = 1 << 20
     n_all = ((3 << 29) // 2 // 128 + 13) * 128
     scaled = _seven_parts(tile, 1537)
