@@ -1,7 +1,7 @@
 /*
  * tfp8.h - C ABI of the MI355X (gfx950) FP8 ASH + DS compression library.
  *
- * Three operations on flat buffers in device memory, each launched asynchronously on the
+ * Four operations on flat buffers in device memory, each launched asynchronously on the
  * caller's HIP stream:
  *
  *   tfp8_compress    per block of `block` elements: second moment, adaptive prescale alpha_k
@@ -17,6 +17,8 @@
  *                    Gradient Quantization for Memory-Efficient Distributed Training of LLMs",
  *                    section 2.B (precision-preserving all-reduce); the TACO page, section
  *                    2.B.3, puts the same step between ReduceScatter and AllGather.
+ *   tfp8_accumulate  a compressed main gradient plus a dense local gradient, requantized (the
+ *                    AGoQ page, section 2.B, local accumulation); declared at the end.
  *
  * Definitions (readings of the pages; B = block, T = target, Q = 448):
  *   block k covers x[kB, (k+1)B) of the flat row-major buffer; H is the Sylvester Hadamard
