@@ -40,7 +40,8 @@
 // with r = sum_p (s_p / alpha_p) dec(q_p); requantising z gives y' = alpha' r exactly, so the
 // reduce works on r directly with no Hadamard at all, and max|y'| = alpha' max|r|.  The sum is
 // accumulated in float64 (as fast as unpacked float32 on this chip), which keeps it exact
-// enough that contributions which largely cancel still requantise like the exact sum.
+// enough that contributions which cancel down to about 2^-25 of their peaks still requantise
+// like the exact sum (below that, a float64 sum's rounding noise is what remains).
 //
 // Accumulate (AGoQ page, section 2.B, local accumulation).  A compressed main gradient plus a
 // dense local gradient, requantised, also in the rotated domain: only the local gradient is
@@ -589,9 +590,12 @@ __global__ __launch_bounds__(kThreads) void k_reduce(const uint8_t *__restrict__
     // r = sum_p g_p dec(q_p) with g_p = s_p / alpha_p, accumulated in float64.  g_p is cut to
     // 49 significant bits (46 for INT8 codes; a relative change below 2^-45), so that its
     // product with a code value is exact in float64; the only roundings are those of
-    // the running sum, each within 2^-53 of it.  Contributions that largely cancel therefore
-    // still requantise like the exact sum, and a contribution and its exact negation cancel
-    // to exactly zero.  A zero block (s_p = 0) contributes exact zeros.
+    // the running sum, each within 2^-53 of it.  Each element of r is therefore within
+    // 2^-44 of the sum of its terms' magnitudes: contributions that cancel down to about 2^-25
+    // of their peaks still requantise like the exact sum, and a contribution and its exact
+    // negation cancel to exactly zero when no smaller term is summed between them (one added
+    // to the larger first is rounded away with it, as in any float64 sum).  A zero block
+    // (s_p = 0) contributes exact zeros.
     double r64[16];
     for (int p0 = 0; p0 < P; p0 += CH) {
       u32x4 d[CH];

@@ -99,10 +99,15 @@ tfp8_status tfp8_decompress(const uint8_t *codes, const float *alpha, const floa
 
 /* Local reduce of P contributions of the same n elements, stacked contiguously:
  * codes[P][n], alpha[P][n/block], scale[P][n/block] (contribution p at offset p*n, p*n/block).
- * The contributions are dequantized and summed in the order p = 0..P-1 (float64 accumulation:
- * at least as precise as the FP32 sum of the AGoQ page, and exact for contributions that
- * cancel), and the sum is requantized with the same block and target into codes_out[n],
- * alpha_out[n/block], scale_out[n/block].  1 <= P <= 64. */
+ * The contributions are dequantized and summed in the order p = 0..P-1 in float64 (at least as
+ * precise as the FP32 sum of the AGoQ page), and the sum is requantized with the same block and
+ * target into codes_out[n], alpha_out[n/block], scale_out[n/block].  1 <= P <= 64.
+ * Precision: each element of the sum (in the rotated domain, r = sum_p (s_p / alpha_p) dec(q_p))
+ * is within 2^-44 of the sum of its terms' magnitudes.  Contributions that cancel down to about
+ * 2^-25 of their peaks requantize like the exact sum; a contribution and its exact negation give
+ * exactly zero when no smaller contribution lies between them in the order.  Where a block's
+ * contributions cancel to far below their peaks, its requantized codes carry the float64 sum's
+ * rounding noise, as any float64 evaluation of the sum would. */
 tfp8_status tfp8_reduce_fp8(const uint8_t *codes, const float *alpha, const float *scale, int32_t P,
                             int64_t n, int32_t block, float target, uint8_t *codes_out,
                             float *alpha_out, float *scale_out, void *stream);

@@ -18,7 +18,7 @@ from gpu_helpers import (DEV, assert_bf16_match, assert_codes_match_every_block,
                          assert_periodic_codes, assert_periodic_decompress, fill_periodic,
                          bits_to_gpu, check_compress, check_decompress, check_reduce, cpu,
                          f32_to_gpu, gpu_bf16_bits, say, u8_to_gpu)
-from tiecheck import assert_codes_match, assert_rel_close
+from tiecheck import FLAG_INT8, assert_codes_match, assert_rel_close, rounding_interval
 from workloads import (GPT2_7B, GPT6_7B, GPT13B_GRAD, QWEN7B, TINY, WORKLOADS, bf16_bits_to_f32,
                        f32_to_bf16_bits, make_shard, make_shards, random_bf16_bits)
 
@@ -109,19 +109,6 @@ def test_qwen7b_pipeline(oracle, tfp8):
     check_decompress(oracle, tfp8, cq, ca, cs, B, what="qwen2.5-7b decompress of the reduced tensor")
 
 
-def _rounding_interval(values: np.ndarray):
-    """Lower and upper ends of the set of exact quotients that round to each E4M3 value (half the
-    gaps to the neighbouring values; unbounded past +-448, where rounding saturates)."""
-    from tiecheck import E4M3_VALUES
-
-    u = np.unique(E4M3_VALUES[np.isfinite(E4M3_VALUES)])  # -448 ... 0 ... 448, sorted
-    k = np.searchsorted(u, values)
-    assert np.all(u[k] == values)
-    lo_gap = np.where(k > 0, 0.5 * (u[k] - u[np.maximum(k - 1, 0)]), np.inf)
-    hi_gap = np.where(k < u.size - 1, 0.5 * (u[np.minimum(k + 1, u.size - 1)] - u[k]), np.inf)
-    return values - lo_gap, values + hi_gap
-
-
 def test_qwen7b_end_to_end_chain(oracle, tfp8):
     # GPU compress -> GPU reduce (P = 8) -> GPU decompress, each stage fed the GPU's own output of
     # the stage before (the chain bench.py times), against the oracle's chain on the same shards.
@@ -181,7 +168,7 @@ def test_qwen7b_end_to_end_chain(oracle, tfp8):
         t = rt[mis]
         w = (448.0 / (M[k] * (1 - 1e-6))) * (D.reshape(-1)[mis] + Dmax[k]) \
             + TIE_REL * np.abs(t) + TIE_ABS
-        lo, hi = _rounding_interval(E4M3_VALUES[cq[mis]])
+        lo, hi = rounding_interval(E4M3_VALUES[cq[mis]])
         ok = (lo <= t + w) & (hi >= t - w)
         assert ok.all(), (f"end-to-end: {int((~ok).sum())} final code mismatches of {mis.size} "
                           f"outside the bound; first at {mis[np.argmax(~ok)]}")
@@ -594,6 +581,34 @@ def test_reduce_identities(oracle, tfp8):
     nz = s > 0
     assert_rel_close(cpu(cs)[nz] / cpu(ca)[nz], s[nz].astype(np.float64) / a[nz], 1e-6,
                      what="s/alpha under P=1")
+
+
+@pytest.mark.parametrize("flags", [0, 1])
+def test_reduce_ill_conditioned_blocks(oracle, tfp8, flags):
+    # Blocks whose contributions cancel far below float64's resolution of their peaks:
+    # contribution 0 of the even blocks is 2^90 times the others and contribution 3 its exact
+    # negation, with two ordinary contributions between them.  Summed in that order in float64
+    # the small terms are rounded away against contribution 0 wherever it is nonzero, and the
+    # oracle (original domain) and the kernel (rotated domain) keep different parts of them.
+    # Such blocks are held to the bound both float64 sums satisfy (tiecheck.reduce_sum_bound);
+    # the odd blocks, with the same pattern at ordinary scale, to the tie rule.
+    from tiecheck import TIE_ABS, reduce_quotient_slack, reduce_sum_bound
+
+    B, nb = 128, 64
+    rng = np.random.default_rng(9090)
+    big = rng.laplace(0.0, 1.0, (nb, B)) * np.where(np.arange(nb) % 2 == 0, 2.0 ** 90, 1.0)[:, None]
+    xs = [big, rng.laplace(0.0, 1.0, (nb, B)), rng.laplace(0.0, 1.0, (nb, B)), -big]
+    enc = [oracle.compress(f32_to_bf16_bits(v.astype(np.float32).reshape(-1)), B, 1.0,
+                           flags=flags) for v in xs]
+    q, a, s = (np.stack([e[i] for e in enc]) for i in range(3))
+    # the construction reaches the case: the even blocks are beyond the tie rule, the odd not
+    Q = 127.0 if flags & FLAG_INT8 else 448.0
+    _, ra, rs = oracle.reduce_fp8(q, a, s, B, 1.0, flags=flags)
+    w, _ = reduce_quotient_slack(reduce_sum_bound(a, s, Q), ra, rs, Q)
+    ill = w > TIE_ABS / 8
+    assert ill[0::2].all() and not ill[1::2].any(), ill
+    check_reduce(oracle, tfp8, q, a, s, B, what=f"ill-conditioned reduce flags={flags}",
+                 flags=flags, tie_ledger=[])
 
 
 # ----------------------------------------------------------------------------- robustness

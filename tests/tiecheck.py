@@ -133,6 +133,65 @@ def assert_codes_match(got, ref, quot, max_frac: float = MAX_TIE_FRAC, rel: floa
     return nmis
 
 
+def rounding_interval(values: np.ndarray, int8: bool = False):
+    """Lower and upper ends of the set of exact quotients that round to each code value (half the
+    gaps to the neighbouring values, ends included; unbounded past the largest values, where
+    rounding saturates)."""
+    values = np.asarray(values, np.float64)
+    table = INT8_VALUES[INT8_VALUES >= -127] if int8 else E4M3_VALUES[np.isfinite(E4M3_VALUES)]
+    u = np.unique(table)  # sorted; +0 and -0 are one value
+    k = np.searchsorted(u, values)
+    assert np.all(u[np.minimum(k, u.size - 1)] == values), "not a code value"
+    lo_gap = np.where(k > 0, 0.5 * (u[k] - u[np.maximum(k - 1, 0)]), np.inf)
+    hi_gap = np.where(k < u.size - 1, 0.5 * (u[np.minimum(k + 1, u.size - 1)] - u[k]), np.inf)
+    return values - lo_gap, values + hi_gap
+
+
+# The reduce's sum.  Both sides form, per element, r = sum_p g_p dec(q_p) with g_p = s_p / alpha_p
+# (the oracle as the float64 sum of the reconstructions in the original domain, the kernel in
+# the rotated domain) with float64 roundings: the running sum's (P - 1 of at most 2^-53 of a
+# partial sum), the oracle's reconstructions (two divisions) and transforms, and the kernel's
+# factor g_p cut to 46 significant bits at least.  Mapped to the rotated domain, the oracle errs
+# by at most about sqrt(B) (P + 1) 2^-52 Q sum_p g_p <= 2^-40 Q sum_p g_p (B <= 512, P <= 64; Q
+# the code maximum, Q g_p the peak of contribution p) and the kernel by less, so the two differ
+# by at most REDUCE_SUM_REL Q sum_p g_p per element, with a margin of about 4.  For blocks whose
+# contributions do not cancel that is ~2^-22 code units or less, far inside the tie window; it
+# grows only where the sum cancels far below the contributions' peaks, and there it decides.
+REDUCE_SUM_REL = 2.0 ** -38
+
+
+def reduce_sum_bound(alpha, scale, qmax: float) -> np.ndarray:
+    """Per block: the bound D on |r_gpu - r_ref| from the contributions' scales alpha, scale
+    [P, nb] (zero blocks contribute nothing)."""
+    g = np.asarray(scale, np.float64) / np.asarray(alpha, np.float64)
+    return REDUCE_SUM_REL * qmax * g.sum(axis=0)
+
+
+def reduce_quotient_slack(D, ref_alpha, ref_scale, qmax: float):
+    """Per block: (quotient slack w in code units, reference peak M = max|r_ref|).  The GPU's code
+    i rounds Q r_gpu,i / M_gpu and the oracle's quotient is Q r_ref,i / M_ref; with both r and the
+    peak within D, they differ by at most Q D (1 / M_ref + 1 / (M_ref - D)).  w is infinite where
+    0 < D and M_ref <= 2 D: the block's sum is below the rounding noise of its contributions."""
+    M = np.asarray(ref_scale, np.float64) * qmax / np.asarray(ref_alpha, np.float64)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        w = np.where(M > 2 * D, qmax * D * (1 / M + 1 / (M - D)), np.inf)
+    return np.where(D == 0, 0.0, w), M  # D = 0: every contribution zero, the sum exactly zero
+
+
+def assert_codes_within(got, quot, slack, int8: bool = False, what: str = "codes"):
+    """Every code the rounding of some quotient within slack (per element, code units, plus the
+    tie window's absolute term) of the reference's exact quotient."""
+    g = np.asarray(got, np.uint8).reshape(-1)
+    t = np.asarray(quot, np.float64).reshape(-1)
+    w = np.asarray(slack, np.float64).reshape(-1) + TIE_ABS
+    vals = INT8_VALUES[g] if int8 else E4M3_VALUES[g]
+    lo, hi = rounding_interval(vals, int8)
+    dist = np.maximum(np.maximum(lo - t, t - hi), 0.0)
+    bad = np.nonzero(~(dist <= w))[0]
+    assert bad.size == 0, (f"{what}: {bad.size} codes beyond the float64 sum's bound; first at "
+                           f"{bad[0]}: got {vals[bad[0]]!r} t={t[bad[0]]!r} slack {w[bad[0]]!r}")
+
+
 def assert_rel_close(got, ref, rel: float, floor: float = 0.0, what: str = "values"):
     got = np.asarray(got, np.float64).reshape(-1)
     ref = np.asarray(ref, np.float64).reshape(-1)
