@@ -18,7 +18,8 @@ from gpu_helpers import (DEV, assert_bf16_match, assert_codes_match_every_block,
                          assert_periodic_codes, assert_periodic_decompress, fill_periodic,
                          bits_to_gpu, check_compress, check_decompress, check_reduce, cpu,
                          f32_to_gpu, gpu_bf16_bits, say, u8_to_gpu)
-from tiecheck import FLAG_INT8, assert_codes_match, assert_rel_close, rounding_interval
+from tiecheck import (FLAG_INT8, FLAG_NO_ROTATION, assert_codes_match, assert_rel_close,
+                      rounding_interval)
 from workloads import (GPT2_7B, GPT6_7B, GPT13B_GRAD, QWEN7B, TINY, WORKLOADS, bf16_bits_to_f32,
                        f32_to_bf16_bits, make_shard, make_shards, random_bf16_bits)
 
@@ -296,6 +297,46 @@ def test_alpha_exactly_on_the_clamp_bounds(oracle, tfp8, dtype, flags):
         q, a, s = check_compress(oracle, tfp8, x, B, T=T, what=what, flags=flags, tie_ledger=[])
         assert np.all(a == np.float32(bound)), (what, a)  # the construction reaches the bound
         check_decompress(oracle, tfp8, q, a, s, B, what=what, flags=flags)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("flags", [0, 1, 2, 3])
+@pytest.mark.parametrize("B", [64, 128, 256, 512])
+def test_fast_path_bounds(oracle, tfp8, B, flags, dtype):
+    # Compress takes its fast path for blocks whose peak max|w| (w = H x unnormalised, or x
+    # without the rotation) lies in [2^-40, 2^60], accumulate for sums whose peak lies in
+    # [2^-40, 2^56]; other blocks are brought into range by a power of two first.  Random blocks
+    # scaled by the powers of two that put their peak just below or just above each bound
+    # (scaling by 2^k leaves the codes unchanged), and one-hot blocks whose peak is the bound
+    # itself, must agree with the oracle on either side.  Accumulate adds them as the local
+    # gradient to an all-zero compressed main gradient.
+    from scipy.linalg import hadamard
+
+    rng = np.random.default_rng(4040 + B + 7 * flags + (dtype == "f32"))
+    H = hadamard(B).astype(np.float64) if not flags & FLAG_NO_ROTATION else np.eye(B)
+    blocks = []
+    for bound in (2.0 ** -40, 2.0 ** 56, 2.0 ** 60):
+        for _ in range(8):
+            v = rng.laplace(0.0, 1.0, B)
+            v = bf16_bits_to_f32(f32_to_bf16_bits(v.astype(np.float32))).astype(np.float64)
+            k = np.floor(np.log2(bound / np.abs(H @ v).max()))  # peak * 2^k in (bound / 2, bound]
+            blocks += [v * 2.0 ** k, v * 2.0 ** (k + 1)]        # just below, just above
+        one = np.zeros(B)
+        one[rng.integers(0, B)] = bound * rng.choice([-1.0, 1.0])
+        blocks.append(one)  # peak exactly the bound, with and without the rotation
+    x = np.concatenate(blocks).astype(np.float32)
+    if dtype == "bf16":
+        xb = f32_to_bf16_bits(x)
+        assert np.array_equal(bf16_bits_to_f32(xb), x)  # every value exact in bfloat16
+        x = xb
+    what = f"fast-path bounds B={B} flags={flags} {dtype}"
+    # admissibility only: one tie would exceed 1e-4 of these few blocks
+    q, a, s = check_compress(oracle, tfp8, x, B, what=what, flags=flags, tie_ledger=[])
+    check_decompress(oracle, tfp8, q, a, s, B, what=what, flags=flags)
+    nb = x.size // B
+    zq = np.zeros(x.size, np.uint8)
+    _check_accumulate(oracle, tfp8, zq, np.ones(nb, np.float32), np.zeros(nb, np.float32), x, B,
+                      what + " accumulate", flags=flags, tie_ledger=[])
 
 
 def _every_value_blocks(dtype, qmax, low, B):
