@@ -339,6 +339,40 @@ def test_fast_path_bounds(oracle, tfp8, B, flags, dtype):
                       what + " accumulate", flags=flags, tie_ledger=[])
 
 
+@pytest.mark.parametrize("flags", [0, 1, 2, 3])
+@pytest.mark.parametrize("B", [64, 128, 256, 512])
+def test_reduce_range_bounds(oracle, tfp8, B, flags):
+    # The reduce rescales sums whose peak max|r| lies outside [2^-100, 2^100] by a power of two
+    # before requantising them.  Contributions whose sums straddle both bounds: random blocks
+    # scaled so that one contribution's peak (max|H x| / sqrt(B) with the rotation, max|x|
+    # without) lies just below or just above 2^-100, and constant blocks c 1 whose peak
+    # (sqrt(B) |c| with the rotation, |c| without) lies around 2^100 with |c| < 2^100, reduced
+    # as P = 1, 2 and 3 copies (the sum's peak P times one contribution's).
+    from scipy.linalg import hadamard
+
+    rot = not flags & FLAG_NO_ROTATION
+    H = hadamard(B).astype(np.float64) / np.sqrt(B) if rot else np.eye(B)
+    rng = np.random.default_rng(5050 + B + 7 * flags)
+    blocks = []
+    for _ in range(8):
+        v = rng.laplace(0.0, 1.0, B)
+        v = bf16_bits_to_f32(f32_to_bf16_bits(v.astype(np.float32))).astype(np.float64)
+        k = np.floor(np.log2(2.0 ** -100 / np.abs(H @ v).max()))
+        blocks += [v * 2.0 ** k, v * 2.0 ** (k + 1)]
+    for c in (2.0 ** 94, 2.0 ** 95, 2.0 ** 96, 1.5 * 2.0 ** 96, 2.0 ** 97, 1.5 * 2.0 ** 98,
+              1.5 * 2.0 ** 99):
+        blocks.append(np.full(B, c * rng.choice([-1.0, 1.0])))
+    x = np.concatenate(blocks).astype(np.float32)
+    assert np.abs(x).max() < 2.0 ** 100
+    xb = f32_to_bf16_bits(x)
+    assert np.array_equal(bf16_bits_to_f32(xb), x)
+    q, a, s = oracle.compress(xb, B, 1.0, flags=flags)
+    for P in (1, 2, 3):
+        check_reduce(oracle, tfp8, np.stack([q] * P), np.stack([a] * P), np.stack([s] * P), B,
+                     what=f"reduce range bounds B={B} flags={flags} P={P}", flags=flags,
+                     tie_ledger=[])
+
+
 def _every_value_blocks(dtype, qmax, low, B):
     """Every float32 (or bfloat16) value with magnitude in [low, qmax], both signs, 511 per block
     of B = 512 after a leading qmax; the tail is padded with 1.0."""
