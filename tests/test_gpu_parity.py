@@ -373,6 +373,32 @@ def test_reduce_range_bounds(oracle, tfp8, B, flags):
                      tie_ledger=[])
 
 
+@pytest.mark.parametrize("flags", [0, 1, 2, 3])
+@pytest.mark.parametrize("B", [64, 128, 256, 512])
+def test_accumulate_negligible_main_bound(oracle, tfp8, B, flags):
+    # Accumulate leaves a main-gradient term out when its peak is below about 2^-60 of the local
+    # gradient's transformed peak (it could then move alpha by 2^-60 relative at most, and a code
+    # only at a near-exact tie).  Main-gradient blocks scaled so that their peak relative to the
+    # local gradient's steps across that threshold, from 2^-68 to 2^-52, must agree with the
+    # oracle, which adds every term.
+    from scipy.linalg import hadamard
+
+    H = hadamard(B).astype(np.float64) if not flags & FLAG_NO_ROTATION else np.eye(B)
+    rng = np.random.default_rng(6060 + B + 7 * flags)
+    steps = np.arange(-68, -51)
+    g = rng.laplace(0.0, 1.0, (steps.size, B))
+    g = bf16_bits_to_f32(f32_to_bf16_bits(g.astype(np.float32))).astype(np.float64)
+    m = rng.laplace(0.0, 1.0, (steps.size, B))
+    m = bf16_bits_to_f32(f32_to_bf16_bits(m.astype(np.float32))).astype(np.float64)
+    ratio = np.abs(m @ H.T).max(axis=1) / np.abs(g @ H.T).max(axis=1)
+    m *= 2.0 ** (steps - np.floor(np.log2(ratio)))[:, None]  # peak ratio in [2^step, 2^(step+1))
+    xm = f32_to_bf16_bits(m.astype(np.float32).reshape(-1))
+    assert np.array_equal(bf16_bits_to_f32(xm), m.reshape(-1))
+    q, a, s = oracle.compress(xm, B, 1.0, flags=flags)
+    _check_accumulate(oracle, tfp8, q, a, s, f32_to_bf16_bits(g.astype(np.float32).reshape(-1)), B,
+                      f"negligible main B={B} flags={flags}", flags=flags, tie_ledger=[])
+
+
 def _every_value_blocks(dtype, qmax, low, B):
     """Every float32 (or bfloat16) value with magnitude in [low, qmax], both signs, 511 per block
     of B = 512 after a leading qmax; the tail is padded with 1.0."""
