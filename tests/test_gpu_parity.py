@@ -1540,3 +1540,47 @@ def test_structured_sweep(oracle, tfp8):
         mis = sum(m for f, m, _ in ledger if f == fl)
         n = sum(k for f, _, k in ledger if f == fl)
         say(f"  structured sweep flags={fl}: {mis} tie mismatches in {n} codes")
+
+
+def test_wide_sweep(oracle, tfp8):
+    # 300 seeded cases over wider ranges than the sweeps above: up to 600 blocks, T anywhere in
+    # the contract's [2^-64, 2^64], random and structured blocks mixed within a case, P up to 64
+    # with some contributions the exact negation of the first (sums that cancel below float64's
+    # resolution of their peaks are held to the bound both float64 sums satisfy), and local
+    # gradients at 2^-80 to 2^80 of the main gradient's peak or its negation.  Only admissibility
+    # is checked: the structured blocks land on code midpoints by construction.
+    for case in range(300):
+        rng = np.random.default_rng(20000 + case)
+        B = int(rng.choice([64, 128, 256, 512]))
+        flags = int(rng.integers(0, 4))
+        f32 = bool(rng.integers(0, 2))
+        nb = max(1, int(np.exp(rng.uniform(0, np.log(600)))))
+        T = min(max(float(np.float32(2.0 ** rng.uniform(-64, 64))), 2.0 ** -64), 2.0 ** 64)
+        pick = rng.random(nb) < rng.uniform(0, 1)
+        v = np.where(pick[:, None], _struct_input(rng, nb, B).reshape(nb, B),
+                     _sweep_input(rng, nb, B).reshape(nb, B)).reshape(-1)
+        x = v.astype(np.float32) if f32 else f32_to_bf16_bits(v.astype(np.float32))
+        xf = (x if f32 else bf16_bits_to_f32(x)).astype(np.float64)
+        what = f"wide {case}: B={B} flags={flags} {'f32' if f32 else 'bf16'} nb={nb} T={T:.3e}"
+        q, a, s = check_compress(oracle, tfp8, x, B, T=T, what=what, flags=flags, tie_ledger=[])
+        check_decompress(oracle, tfp8, q, a, s, B, what=what, flags=flags)
+        P = max(1, int(np.exp(rng.uniform(0, np.log(65)))))
+        enc = [(q, a, s)]
+        for _ in range(P - 1):
+            xp = -xf if rng.integers(0, 4) == 0 else _sweep_input(rng, nb, B) * rng.choice([-1.0, 1.0])
+            enc.append(oracle.compress(f32_to_bf16_bits(xp.astype(np.float32)), B, T, flags=flags))
+        check_reduce(oracle, tfp8, np.stack([e[0] for e in enc]), np.stack([e[1] for e in enc]),
+                     np.stack([e[2] for e in enc]), B, T, what=what + f" P={P}", flags=flags,
+                     tie_ledger=[])
+        # each fresh local-gradient block brought to 2^U(-80, 80) of the main block's peak
+        peaks = np.abs(xf.reshape(nb, B)).max(axis=1)
+        fresh = _sweep_input(rng, nb, B).reshape(nb, B)
+        fpk = np.abs(fresh).max(axis=1)
+        target = np.where(peaks > 0, peaks, 1.0) * 2.0 ** rng.uniform(-80, 80, nb)
+        fresh *= np.where(fpk > 0, target / np.where(fpk > 0, fpk, 1.0), 0.0)[:, None]
+        g = np.where((rng.random(nb) < 0.5)[:, None], -xf.reshape(nb, B), fresh)
+        g = np.clip(g, -2.0 ** 99, 2.0 ** 99).reshape(-1)
+        assert np.all(np.isfinite(g))
+        gl = g.astype(np.float32) if rng.integers(0, 2) else f32_to_bf16_bits(g.astype(np.float32))
+        _check_accumulate(oracle, tfp8, q, a, s, gl, B, what + " accumulate", flags=flags,
+                          inplace=bool(rng.integers(0, 2)), T=T, tie_ledger=[])
