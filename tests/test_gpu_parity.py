@@ -305,26 +305,31 @@ def test_alpha_exactly_on_the_clamp_bounds(oracle, tfp8, dtype, flags):
 def test_fast_path_bounds(oracle, tfp8, B, flags, dtype):
     # Compress takes its fast path for blocks whose peak max|w| (w = H x unnormalised, or x
     # without the rotation) lies in [2^-40, 2^60], accumulate for sums whose peak lies in
-    # [2^-40, 2^56]; other blocks are brought into range by a power of two first.  Random blocks
+    # [2^-40, 2^56]; other blocks are brought into range by a power of two first, and
+    # accumulate's exact scale path rescales again outside [2^-100, 2^100].  Random blocks
     # scaled by the powers of two that put their peak just below or just above each bound
     # (scaling by 2^k leaves the codes unchanged), and one-hot blocks whose peak is the bound
     # itself, must agree with the oracle on either side.  Accumulate adds them as the local
-    # gradient to an all-zero compressed main gradient.
+    # gradient to an all-zero compressed main gradient.  Peaks around 2^100 need the rotation
+    # (which gathers a block's energy) to keep every input below the contract's 2^100.
     from scipy.linalg import hadamard
 
     rng = np.random.default_rng(4040 + B + 7 * flags + (dtype == "f32"))
-    H = hadamard(B).astype(np.float64) if not flags & FLAG_NO_ROTATION else np.eye(B)
+    rot = not flags & FLAG_NO_ROTATION
+    H = hadamard(B).astype(np.float64) if rot else np.eye(B)
     blocks = []
-    for bound in (2.0 ** -40, 2.0 ** 56, 2.0 ** 60):
+    for bound in (2.0 ** -100, 2.0 ** -40, 2.0 ** 56, 2.0 ** 60) + ((2.0 ** 100,) if rot else ()):
         for _ in range(8):
             v = rng.laplace(0.0, 1.0, B)
             v = bf16_bits_to_f32(f32_to_bf16_bits(v.astype(np.float32))).astype(np.float64)
             k = np.floor(np.log2(bound / np.abs(H @ v).max()))  # peak * 2^k in (bound / 2, bound]
             blocks += [v * 2.0 ** k, v * 2.0 ** (k + 1)]        # just below, just above
-        one = np.zeros(B)
-        one[rng.integers(0, B)] = bound * rng.choice([-1.0, 1.0])
-        blocks.append(one)  # peak exactly the bound, with and without the rotation
+        if bound < 2.0 ** 100:
+            one = np.zeros(B)
+            one[rng.integers(0, B)] = bound * rng.choice([-1.0, 1.0])
+            blocks.append(one)  # peak exactly the bound, with and without the rotation
     x = np.concatenate(blocks).astype(np.float32)
+    assert np.abs(x).max() < 2.0 ** 100
     if dtype == "bf16":
         xb = f32_to_bf16_bits(x)
         assert np.array_equal(bf16_bits_to_f32(xb), x)  # every value exact in bfloat16
