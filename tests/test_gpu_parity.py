@@ -404,6 +404,26 @@ def test_accumulate_negligible_main_bound(oracle, tfp8, B, flags):
                       f"negligible main B={B} flags={flags}", flags=flags, tie_ledger=[])
 
 
+@pytest.mark.parametrize("gdtype", ["bf16", "f32"])
+@pytest.mark.parametrize("flags", [0, 1, 2, 3])
+@pytest.mark.parametrize("B", [64, 128, 256, 512])
+def test_accumulate_fix_pass_bound(oracle, tfp8, B, flags, gdtype):
+    # Accumulate sets a block aside for its exact pass when the sum's peak is under half the
+    # larger of its two terms' peaks.  With the local gradient g = -lambda xhat (xhat the main
+    # gradient's reconstruction) the sum is (1 - lambda) xhat, so blocks with lambda just below
+    # and just above 1/2 take the two paths; both must agree with the oracle.
+    rng = np.random.default_rng(7070 + B + 7 * flags + (gdtype == "f32"))
+    lam = np.linspace(0.40, 0.60, 41)
+    nb = lam.size
+    xm = f32_to_bf16_bits(rng.laplace(0.0, 1.0, nb * B).astype(np.float32))
+    q, a, s = oracle.compress(xm, B, 1.0, flags=flags)
+    xhat = oracle.decompress_f64(q, a, s, B, flags=flags).reshape(nb, B)
+    g = (-lam[:, None] * xhat).reshape(-1).astype(np.float32)
+    g = g if gdtype == "f32" else f32_to_bf16_bits(g)
+    _check_accumulate(oracle, tfp8, q, a, s, g, B, f"fix-pass bound B={B} flags={flags} {gdtype}",
+                      flags=flags, tie_ledger=[])
+
+
 def _every_value_blocks(dtype, qmax, low, B):
     """Every float32 (or bfloat16) value with magnitude in [low, qmax], both signs, 511 per block
     of B = 512 after a leading qmax; the tail is padded with 1.0."""
