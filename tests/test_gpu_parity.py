@@ -1318,8 +1318,7 @@ _LARGE_CASES = [(128, "bf16", 513), (64, "bf16", 513), (512, "bf16", 513), (128,
                 (256, "bf16", 8193)]
 
 
-@pytest.mark.parametrize("B,dtype,ntiles", _LARGE_CASES)
-def test_large_offsets_and_grid_stride_loops_every_block(oracle, tfp8, B, dtype, ntiles):
+def _large_input_every_block(oracle, tfp8, B, dtype, ntiles, f32_out=True, reduce=True):
     # n = ntiles * 2^22 - 37 B elements (4.3-69 GB of input, a ragged last tile), built on the
     # GPU from seven random tiles of 2^22 elements (tile t is part t mod 7), so that a read at
     # an offset cut to 32 bits (1024 tiles away for codes, 512 for bfloat16, 256 for float32)
@@ -1364,7 +1363,9 @@ def test_large_offsets_and_grid_stride_loops_every_block(oracle, tfp8, B, dtype,
     qg, ag, sg = codes_on_gpu(enc)
     dec = [(e[0], e[1], e[2]) for e in enc]
     r64 = [oracle.decompress_f64(*d, B) for d in dec]
-    for odt, ndt in ((torch.bfloat16, np.uint16), (torch.float32, np.float32)):
+    outs = ((torch.bfloat16, np.uint16), (torch.float32, np.float32)) if f32_out else \
+        ((torch.bfloat16, np.uint16),)
+    for odt, ndt in outs:
         out = tfp8.decompress(qg, ag, sg, B, odt)
         torch.cuda.synchronize()
         refs = [(oracle.decompress(*d, B, ndt), r) for d, r in zip(dec, r64)]
@@ -1376,25 +1377,26 @@ def test_large_offsets_and_grid_stride_loops_every_block(oracle, tfp8, B, dtype,
     del r64
 
     # reduce, P = 2: row 0 the tiled codes, row 1 the same tiles three parts on
-    sq = torch.empty((2, n), dtype=torch.uint8, device=DEV)
-    sa = torch.empty((2, nb), dtype=torch.float32, device=DEV)
-    ss = torch.empty((2, nb), dtype=torch.float32, device=DEV)
-    sq[0], sa[0], ss[0] = qg, ag, sg
-    other = [enc[(w + 3) % 7] for w in range(7)]
-    fill_periodic(sq[1], [e[0] for e in other], tile)
-    fill_periodic(sa[1], [e[1] for e in other], bpt)
-    fill_periodic(ss[1], [e[2] for e in other], bpt)
-    cq, ca, cs = tfp8.reduce_fp8(sq, sa, ss, B, T)
-    torch.cuda.synchronize()
-    del sq, sa, ss
-    torch.cuda.empty_cache()
-    refs = [oracle.reduce_fp8(np.stack([e[0], o[0]]), np.stack([e[1], o[1]]),
-                              np.stack([e[2], o[2]]), B, T, with_quot=True)
-            for e, o in zip(enc, other)]
-    nmis, ea, es = assert_periodic_codes(cq, ca, cs, refs, n, tile, B, what="large reduce")
-    del cq, ca, cs
-    torch.cuda.empty_cache()
-    say(f"  large reduce: tie mismatches {nmis}, max rel err alpha {ea:.2e} s {es:.2e}")
+    if reduce:
+        sq = torch.empty((2, n), dtype=torch.uint8, device=DEV)
+        sa = torch.empty((2, nb), dtype=torch.float32, device=DEV)
+        ss = torch.empty((2, nb), dtype=torch.float32, device=DEV)
+        sq[0], sa[0], ss[0] = qg, ag, sg
+        other = [enc[(w + 3) % 7] for w in range(7)]
+        fill_periodic(sq[1], [e[0] for e in other], tile)
+        fill_periodic(sa[1], [e[1] for e in other], bpt)
+        fill_periodic(ss[1], [e[2] for e in other], bpt)
+        cq, ca, cs = tfp8.reduce_fp8(sq, sa, ss, B, T)
+        torch.cuda.synchronize()
+        del sq, sa, ss
+        torch.cuda.empty_cache()
+        refs = [oracle.reduce_fp8(np.stack([e[0], o[0]]), np.stack([e[1], o[1]]),
+                                  np.stack([e[2], o[2]]), B, T, with_quot=True)
+                for e, o in zip(enc, other)]
+        nmis, ea, es = assert_periodic_codes(cq, ca, cs, refs, n, tile, B, what="large reduce")
+        del cq, ca, cs
+        torch.cuda.empty_cache()
+        say(f"  large reduce: tie mismatches {nmis}, max rel err alpha {ea:.2e} s {es:.2e}")
 
     # accumulate in place: main gradient = the tiled codes, local gradient = the input
     x = input_on_gpu()
@@ -1408,6 +1410,24 @@ def test_large_offsets_and_grid_stride_loops_every_block(oracle, tfp8, B, dtype,
     del qg, ag, sg
     torch.cuda.empty_cache()
     say(f"  large accumulate: tie mismatches {nmis}, max rel err alpha {ea:.2e} s {es:.2e}")
+
+
+@pytest.mark.parametrize("B,dtype,ntiles", _LARGE_CASES)
+def test_large_offsets_and_grid_stride_loops_every_block(oracle, tfp8, B, dtype, ntiles):
+    _large_input_every_block(oracle, tfp8, B, dtype, ntiles)
+
+
+def test_grid_stride_loops_at_block_512_every_block(oracle, tfp8):
+    # At B = 512 the launches of compress, decompress and accumulate loop over tiles from 2^36
+    # elements on: n = 16385 * 2^22 - 37 * 512 (137 GB of bfloat16).  Compress holds 206 GB at its
+    # peak (input and codes), decompress to bfloat16 and accumulate as much; the float32
+    # decompress (275 GB) and the reduce (its loop at B = 512 starts at 2^34 and is checked
+    # above) are left out.
+    torch.cuda.empty_cache()
+    free, _ = torch.cuda.mem_get_info(DEV)
+    if free < 225e9:
+        pytest.skip(f"needs 225 GB of free device memory, {free / 1e9:.0f} GB free")
+    _large_input_every_block(oracle, tfp8, 512, "bf16", 16385, f32_out=False, reduce=False)
 
 
 def _sweep_input(rng, nb, B):
