@@ -1318,7 +1318,7 @@ _LARGE_CASES = [(128, "bf16", 513), (64, "bf16", 513), (512, "bf16", 513), (128,
                 (256, "bf16", 8193)]
 
 
-def _large_input_every_block(oracle, tfp8, B, dtype, ntiles, f32_out=True, reduce=True):
+def _large_input_every_block(oracle, tfp8, B, dtype, ntiles, flags=0, f32_out=True, reduce=True):
     # n = ntiles * 2^22 - 37 B elements (4.3-69 GB of input, a ragged last tile), built on the
     # GPU from seven random tiles of 2^22 elements (tile t is part t mod 7), so that a read at
     # an offset cut to 32 bits (1024 tiles away for codes, 512 for bfloat16, 256 for float32)
@@ -1330,8 +1330,8 @@ def _large_input_every_block(oracle, tfp8, B, dtype, ntiles, f32_out=True, reduc
     nb, bpt = n // B, tile // B
     f32 = dtype == "f32"
     variants = _seven_parts(tile, 2034 + 8 * B, dtype)
-    enc = [oracle.compress(v, B, T, with_quot=True) for v in variants]
-    say(f"  large input B={B} {dtype}: n = {n} ({n * (4 if f32 else 2) / 1e9:.1f} GB of "
+    enc = [oracle.compress(v, B, T, with_quot=True, flags=flags) for v in variants]
+    say(f"  large input B={B} {dtype} flags={flags}: n = {n} ({n * (4 if f32 else 2) / 1e9:.1f} GB of "
         f"input), every block")
 
     def input_on_gpu():
@@ -1350,11 +1350,12 @@ def _large_input_every_block(oracle, tfp8, B, dtype, ntiles, f32_out=True, reduc
 
     # compress
     x = input_on_gpu()
-    q, a, s = tfp8.compress(x, B, T)
+    q, a, s = tfp8.compress(x, B, T, flags=flags)
     torch.cuda.synchronize()
     del x
     torch.cuda.empty_cache()
-    nmis, ea, es = assert_periodic_codes(q, a, s, enc, n, tile, B, what="large compress")
+    nmis, ea, es = assert_periodic_codes(q, a, s, enc, n, tile, B, what="large compress",
+                                         flags=flags)
     del q, a, s
     torch.cuda.empty_cache()
     say(f"  large compress: tie mismatches {nmis}, max rel err alpha {ea:.2e} s {es:.2e}")
@@ -1362,13 +1363,13 @@ def _large_input_every_block(oracle, tfp8, B, dtype, ntiles, f32_out=True, reduc
     # decompress of the oracle's codes, bfloat16 and float32
     qg, ag, sg = codes_on_gpu(enc)
     dec = [(e[0], e[1], e[2]) for e in enc]
-    r64 = [oracle.decompress_f64(*d, B) for d in dec]
+    r64 = [oracle.decompress_f64(*d, B, flags=flags) for d in dec]
     outs = ((torch.bfloat16, np.uint16), (torch.float32, np.float32)) if f32_out else \
         ((torch.bfloat16, np.uint16),)
     for odt, ndt in outs:
-        out = tfp8.decompress(qg, ag, sg, B, odt)
+        out = tfp8.decompress(qg, ag, sg, B, odt, flags=flags)
         torch.cuda.synchronize()
-        refs = [(oracle.decompress(*d, B, ndt), r) for d, r in zip(dec, r64)]
+        refs = [(oracle.decompress(*d, B, ndt, flags=flags), r) for d, r in zip(dec, r64)]
         nt = assert_periodic_decompress(out, refs, n, tile, B, what=f"large decompress {odt}")
         del out
         torch.cuda.empty_cache()
@@ -1386,27 +1387,28 @@ def _large_input_every_block(oracle, tfp8, B, dtype, ntiles, f32_out=True, reduc
         fill_periodic(sq[1], [e[0] for e in other], tile)
         fill_periodic(sa[1], [e[1] for e in other], bpt)
         fill_periodic(ss[1], [e[2] for e in other], bpt)
-        cq, ca, cs = tfp8.reduce_fp8(sq, sa, ss, B, T)
+        cq, ca, cs = tfp8.reduce_fp8(sq, sa, ss, B, T, flags=flags)
         torch.cuda.synchronize()
         del sq, sa, ss
         torch.cuda.empty_cache()
         refs = [oracle.reduce_fp8(np.stack([e[0], o[0]]), np.stack([e[1], o[1]]),
-                                  np.stack([e[2], o[2]]), B, T, with_quot=True)
+                                  np.stack([e[2], o[2]]), B, T, with_quot=True, flags=flags)
                 for e, o in zip(enc, other)]
-        nmis, ea, es = assert_periodic_codes(cq, ca, cs, refs, n, tile, B, what="large reduce")
+        nmis, ea, es = assert_periodic_codes(cq, ca, cs, refs, n, tile, B, what="large reduce",
+                                             flags=flags)
         del cq, ca, cs
         torch.cuda.empty_cache()
         say(f"  large reduce: tie mismatches {nmis}, max rel err alpha {ea:.2e} s {es:.2e}")
 
     # accumulate in place: main gradient = the tiled codes, local gradient = the input
     x = input_on_gpu()
-    tfp8.accumulate(qg, ag, sg, x, B, T, inplace=True)
+    tfp8.accumulate(qg, ag, sg, x, B, T, inplace=True, flags=flags)
     torch.cuda.synchronize()
     del x
-    refs = [oracle.accumulate(e[0], e[1], e[2], v, B, T, with_quot=True)
+    refs = [oracle.accumulate(e[0], e[1], e[2], v, B, T, with_quot=True, flags=flags)
             for e, v in zip(enc, variants)]
     nmis, ea, es = assert_periodic_codes(qg, ag, sg, refs, n, tile, B,
-                                         what="large accumulate")
+                                         what="large accumulate", flags=flags)
     del qg, ag, sg
     torch.cuda.empty_cache()
     say(f"  large accumulate: tie mismatches {nmis}, max rel err alpha {ea:.2e} s {es:.2e}")
@@ -1415,6 +1417,20 @@ def _large_input_every_block(oracle, tfp8, B, dtype, ntiles, f32_out=True, reduc
 @pytest.mark.parametrize("B,dtype,ntiles", _LARGE_CASES)
 def test_large_offsets_and_grid_stride_loops_every_block(oracle, tfp8, B, dtype, ntiles):
     _large_input_every_block(oracle, tfp8, B, dtype, ntiles)
+
+
+# The looping forms of the variants (INT8 codes, the rotation left out, both) at B = 128, and of
+# float32 input at B = 64 and 256 (past 2^34 and 2^35 elements).
+@pytest.mark.parametrize("B,dtype,ntiles,flags", [(128, "bf16", 4097, 1), (128, "bf16", 4097, 2),
+                                                  (128, "bf16", 4097, 3), (64, "f32", 4097, 0),
+                                                  (256, "f32", 8193, 0)])
+def test_grid_stride_loops_variants_and_fp32_every_block(oracle, tfp8, B, dtype, ntiles, flags):
+    torch.cuda.empty_cache()
+    free, _ = torch.cuda.mem_get_info(DEV)
+    need = 4 * ntiles * (1 << 22) * 1.3  # the float32 input and its codes, with room to spare
+    if dtype == "f32" and free < need:
+        pytest.skip(f"needs {need / 1e9:.0f} GB of free device memory, {free / 1e9:.0f} GB free")
+    _large_input_every_block(oracle, tfp8, B, dtype, ntiles, flags=flags)
 
 
 def test_grid_stride_loops_at_block_512_every_block(oracle, tfp8):
