@@ -1319,12 +1319,13 @@ _LARGE_CASES = [(128, "bf16", 513), (64, "bf16", 513), (512, "bf16", 513), (128,
 
 
 def _large_input_every_block(oracle, tfp8, B, dtype, ntiles, flags=0, f32_out=True, reduce=True):
-    # n = ntiles * 2^22 - 37 B elements (4.3-69 GB of input, a ragged last tile), built on the
+    # n = ntiles * 2^22 - 37 B elements (4.3-137 GB of input, a ragged last tile), built on the
     # GPU from seven random tiles of 2^22 elements (tile t is part t mod 7), so that a read at
     # an offset cut to 32 bits (1024 tiles away for codes, 512 for bfloat16, 256 for float32)
-    # or any other wrong place shows.  Compress, decompress to bfloat16 and float32, the reduce
-    # and accumulate each run on the whole tensor; every output block is checked against the
-    # oracle's output for its part.  No expected value comes from the GPU.
+    # or any other wrong place shows.  Compress, decompress to bfloat16 and (f32_out) float32,
+    # the reduce (reduce) and accumulate each run on the whole tensor with the given variant
+    # flags; every output block is checked against the oracle's output for its part.  No
+    # expected value comes from the GPU.
     T, tile = 1.0, 1 << 22
     n = ntiles * tile - 37 * B
     nb, bpt = n // B, tile // B
