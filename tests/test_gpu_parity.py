@@ -1330,6 +1330,14 @@ def _large_input_every_block(oracle, tfp8, B, dtype, ntiles, flags=0, f32_out=Tr
     n = ntiles * tile - 37 * B
     nb, bpt = n // B, tile // B
     f32 = dtype == "f32"
+    # device memory at the largest step (input and codes; codes and a reconstruction; two rows
+    # of codes, their sum and the codes), with a tenth to spare
+    esize = 4 if f32 else 2
+    peak = 1.1 * n * max(esize + 1, 1 + (4 if f32_out else 2), 4 if reduce else 0)
+    torch.cuda.empty_cache()
+    free, _ = torch.cuda.mem_get_info(DEV)
+    if free < peak:
+        pytest.skip(f"needs {peak / 1e9:.0f} GB of free device memory, {free / 1e9:.0f} GB free")
     variants = _seven_parts(tile, 2034 + 8 * B, dtype)
     enc = [oracle.compress(v, B, T, with_quot=True, flags=flags) for v in variants]
     say(f"  large input B={B} {dtype} flags={flags}: n = {n} ({n * (4 if f32 else 2) / 1e9:.1f} GB of "
@@ -1426,11 +1434,6 @@ def test_large_offsets_and_grid_stride_loops_every_block(oracle, tfp8, B, dtype,
                                                   (128, "bf16", 4097, 3), (64, "f32", 4097, 0),
                                                   (256, "f32", 8193, 0)])
 def test_grid_stride_loops_variants_and_fp32_every_block(oracle, tfp8, B, dtype, ntiles, flags):
-    torch.cuda.empty_cache()
-    free, _ = torch.cuda.mem_get_info(DEV)
-    need = 4 * ntiles * (1 << 22) * 1.3  # the float32 input and its codes, with room to spare
-    if dtype == "f32" and free < need:
-        pytest.skip(f"needs {need / 1e9:.0f} GB of free device memory, {free / 1e9:.0f} GB free")
     _large_input_every_block(oracle, tfp8, B, dtype, ntiles, flags=flags)
 
 
@@ -1439,11 +1442,7 @@ def test_grid_stride_loops_at_block_512_every_block(oracle, tfp8):
     # elements on: n = 16385 * 2^22 - 37 * 512 (137 GB of bfloat16).  Compress holds 206 GB at its
     # peak (input and codes), decompress to bfloat16 and accumulate as much; the float32
     # decompress (275 GB) and the reduce (its loop at B = 512 starts at 2^34 and is checked
-    # above) are left out.
-    torch.cuda.empty_cache()
-    free, _ = torch.cuda.mem_get_info(DEV)
-    if free < 225e9:
-        pytest.skip(f"needs 225 GB of free device memory, {free / 1e9:.0f} GB free")
+    # above) are left out.  Like every case here it skips on a device without the memory.
     _large_input_every_block(oracle, tfp8, 512, "bf16", 16385, f32_out=False, reduce=False)
 
 
