@@ -166,35 +166,85 @@ def check_decompress(oracle, tfp8, q, a, s, B: int, what="decompress", flags: in
 
 def check_reduce(oracle, tfp8, q, a, s, B, T=1.0, what="reduce", flags: int = 0,
                  gpu: bool = False, tie_ledger=None, block_mask=None, mask_ledger=None):
-    """GPU reduce of stacked codes/scales [P, ...] vs the oracle's reduce by definition.
-    Blocks whose contributions cancel so far that the float64 sums' rounding noise reaches the
-    tie window (see tiecheck.reduce_sum_bound; none in the workloads) are held to that bound
-    instead of the tie rule.  Returns the oracle's (codes, alpha, scale), or with gpu=True the
-    GPU's."""
+    """GPU reduce of stacked codes/scales [P, ...] vs the oracle's reduce by definition, to the
+    tie rule; a code or scale that fails it is admitted only within the bound both float64 sums
+    satisfy (assert_reduce_matches).  Returns the oracle's (codes, alpha, scale), or with
+    gpu=True the GPU's."""
     P, n = q.shape
-    nb = n // B
     qg, ag, sg = u8_to_gpu(q), f32_to_gpu(a), f32_to_gpu(s)
     cq, ca, cs = tfp8.reduce_fp8(qg, ag, sg, B, T, flags=flags)
     torch.cuda.synchronize()
     cq, ca, cs = cpu(cq), cpu(ca), cpu(cs)
     rq, ra, rs, rt = oracle.reduce_fp8(q, a, s, B, T, with_quot=True, flags=flags)
-    int8 = bool(flags & FLAG_INT8)
-    nill = check_ill_conditioned_reduce(cq, ca, cs, rt, ra, rs, a.reshape(P, nb), s.reshape(P, nb),
-                                        B, int8, what)
-    ill = nill[1]
-    keep = np.repeat(~ill, B)
-    nmis = assert_codes_match(cq[keep], rq[keep], rt[keep], max_frac=_tie_cap(flags, tie_ledger),
-                              what=what + " codes", int8=int8)
+    nmis, nfb, ea, es = assert_reduce_matches(cq, ca, cs, rq, rt, ra, rs, a.reshape(P, -1),
+                                              s.reshape(P, -1), B, flags,
+                                              _tie_cap(flags, tie_ledger), what)
     if tie_ledger is not None:
-        tie_ledger.append((flags, nmis, int(keep.sum())))
-    if block_mask is not None:
-        _count_in_blocks(cq, rq, B, np.asarray(block_mask, bool).reshape(-1) & ~ill, flags,
-                         mask_ledger)
-    ea, es = assert_scales(ca[~ill], cs[~ill], ra[~ill], rs[~ill], what=what)
+        tie_ledger.append((flags, nmis, cq.size))
+    _count_in_blocks(cq, rq, B, block_mask, flags, mask_ledger)
     say(f"  {what}: P={P} n={n} B={B} flags={flags}: code tie mismatches {nmis} ({nmis / n:.2e}), "
         f"max rel err alpha {ea:.2e} scale {es:.2e}"
-        + (f"; {nill[0]} blocks at the float64 sum's bound" if nill[0] else ""))
+        + (f"; {nfb} codes or blocks within the float64 sums' bound" if nfb else ""))
     return (cq, ca, cs) if gpu else (rq, ra, rs)
+
+
+def assert_reduce_matches(cq, ca, cs, rq, rt, ra, rs, alpha_in, scale_in, B: int, flags: int,
+                          max_frac: float, what: str):
+    """A reduce's codes and scales against the oracle's.  Codes: identical except admissible
+    rounding ties, at most max_frac of the elements.  A mismatch that is not such a tie is
+    admitted only if the code is the rounding of some quotient within the float64 sums' slack w
+    of its block (tiecheck.reduce_sum_bound, reduce_quotient_slack; ~1e-8 code units for blocks
+    whose contributions do not cancel, so nothing more than the tie rule is admitted there), or if
+    the block's reference peak lies inside that noise (M <= 2 D).  Scales: alpha' and s' within
+    1e-6 relative, zero blocks exact, alpha inside the clamp range; a block that fails this is
+    admitted only within the relative error D allows, or, with M <= 2 D, with a peak of at most
+    M + D.  Returns (ties, codes and blocks admitted under the bound, max rel err alpha, s over
+    the blocks held to 1e-6)."""
+    from tiecheck import (assert_codes_within, code_mismatches, reduce_quotient_slack,
+                          reduce_sum_bound)
+
+    int8 = bool(flags & FLAG_INT8)
+    Q = 127.0 if int8 else 448.0
+    nb = ra.size
+    D = reduce_sum_bound(alpha_in, scale_in, Q)
+    w, M = reduce_quotient_slack(D, ra, rs, Q)
+    # codes
+    nmis, bad = code_mismatches(cq, rq, rt, int8=int8, return_bad=True)
+    blk = bad // B
+    fin = np.isfinite(w[blk])
+    if fin.any():
+        assert_codes_within(cq[bad[fin]], rt[bad[fin]], w[blk[fin]], int8,
+                            what=what + " codes (float64 sums' bound)")
+    noise_blocks = set(blk[~fin].tolist())
+    nties = nmis - int(bad.size)
+    assert nties <= max_frac * max(cq.size, 1), (f"{what}: {nties} tie mismatches of {cq.size} "
+                                                f"exceed {max_frac}")
+    # scales
+    inside = (ca >= ALPHA_MIN) & (ca <= ALPHA_MAX)
+    assert inside.all(), f"{what}: {int((~inside).sum())} alpha outside the clamp range"
+    a64, s64 = ca.astype(np.float64), cs.astype(np.float64)
+    ra64, rs64 = ra.astype(np.float64), rs.astype(np.float64)
+    zero = rs64 == 0
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ea = np.where(zero, np.where(a64 == 1, 0.0, np.inf), np.abs(a64 / ra64 - 1))
+        es = np.where(zero, np.where(s64 == 0, 0.0, np.inf), np.abs(s64 / rs64 - 1))
+    std = (ea <= 1e-6) & (es <= 1e-6)
+    off = np.nonzero(~std)[0]
+    for k in off:
+        assert D[k] > 0, f"{what}: block {k} of all-zero contributions is not an exact zero block"
+        if np.isfinite(w[k]):
+            rel_a = 1e-6 + 2 * np.sqrt(B) * D[k] / M[k]
+            rel_s = rel_a + 2 * D[k] / M[k] + 1e-6
+            assert ea[k] <= rel_a and es[k] <= rel_s, (f"{what}: block {k} alpha {a64[k]!r} s "
+                                                       f"{s64[k]!r} against {ra64[k]!r}, {rs64[k]!r}")
+        else:
+            assert D[k] > 0 and s64[k] * Q / a64[k] <= M[k] + D[k], (
+                f"{what}: block {k} peak {s64[k] * Q / a64[k]!r} beyond its noise {M[k] + D[k]!r}")
+            noise_blocks.add(int(k))
+    for k in noise_blocks:  # codes of a block inside its noise: only its peak is bounded
+        assert D[k] > 0 and s64[k] * Q / a64[k] <= M[k] + D[k], f"{what}: block {k} beyond its noise"
+    return nties, int(bad.size) + len(off), float(ea[std].max(initial=0.0)), \
+        float(es[std].max(initial=0.0))
 
 
 # ---- inputs that repeat every seven tiles, checked on every block on the GPU ----------------
@@ -311,38 +361,3 @@ def assert_periodic_decompress(out, refs, n: int, tile: int, B: int, what: str,
     assert int(nviol) == 0, f"{what}: {int(nviol)} outputs outside the bar"
     return int(nmis)
 
-
-def check_ill_conditioned_reduce(cq, ca, cs, rt, ra, rs, alpha_in, scale_in, B: int, int8: bool,
-                                 what: str):
-    """The blocks of a reduce whose float64 sum is ill-conditioned: those where the bound D on
-    the two sides' difference (tiecheck.reduce_sum_bound) makes the quotient slack exceed an
-    eighth of the tie window's absolute term.  Their codes must lie within the slack, alpha' and
-    s' within the relative error that D allows (at least 1e-6), and a block whose reference peak
-    is itself within the noise (M_ref <= 2 D, e.g. an exactly zero sum) must come back with a peak
-    of at most M_ref + D.  Returns (count, per-block mask)."""
-    from tiecheck import TIE_ABS, assert_codes_within, reduce_quotient_slack, reduce_sum_bound
-
-    Q = 127.0 if int8 else 448.0
-    D = reduce_sum_bound(alpha_in, scale_in, Q)
-    w, M = reduce_quotient_slack(D, ra, rs, Q)
-    ill = w > TIE_ABS / 8
-    if not ill.any():
-        return 0, ill
-    nb = ill.size
-    inside = (ca >= ALPHA_MIN) & (ca <= ALPHA_MAX)
-    assert inside.all(), f"{what}: alpha outside the clamp range"
-    fin = ill & np.isfinite(w)
-    if fin.any():
-        assert_codes_within(cq.reshape(nb, B)[fin], rt.reshape(nb, B)[fin],
-                            np.repeat(w[fin], B), int8, what=what + " ill-conditioned codes")
-        # alpha' ~ 1/|r|_2 and s' = alpha' M / Q, with |r|_2 >= M and every element within D
-        rel_a = 1e-6 + 2 * np.sqrt(B) * D[fin] / M[fin]
-        rel_s = rel_a + 2 * D[fin] / M[fin] + 1e-6
-        ea = np.abs(ca[fin].astype(np.float64) / ra[fin] - 1)
-        es = np.abs(cs[fin].astype(np.float64) / rs[fin] - 1)
-        assert np.all(ea <= rel_a) and np.all(es <= rel_s), f"{what}: ill-conditioned scales"
-    noise = ill & ~np.isfinite(w)
-    if noise.any():
-        Mg = cs[noise].astype(np.float64) * Q / ca[noise]
-        assert np.all(Mg <= M[noise] + D[noise]), f"{what}: a sum within its noise came back larger"
-    return int(ill.sum()), ill

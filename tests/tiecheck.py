@@ -76,14 +76,15 @@ def tie_window_stats() -> dict:
 
 
 def code_mismatches(got: np.ndarray, ref: np.ndarray, quot: np.ndarray, rel: float = TIE_REL,
-                    abs_: float = TIE_ABS, int8: bool = False):
-    """Return (n_mismatch, n_inadmissible, first_bad_index or -1)."""
+                    abs_: float = TIE_ABS, int8: bool = False, return_bad: bool = False):
+    """Return (n_mismatch, n_inadmissible, first_bad_index or -1), or with return_bad
+    (n_mismatch, indices of the inadmissible mismatches)."""
     got = np.asarray(got, np.uint8).reshape(-1)
     ref = np.asarray(ref, np.uint8).reshape(-1)
     quot = np.asarray(quot, np.float64).reshape(-1)
     bad = np.nonzero(got != ref)[0]
     if bad.size == 0:
-        return 0, 0, -1
+        return (0, bad) if return_bad else (0, 0, -1)
     g, r, t = got[bad], ref[bad], quot[bad]
     if int8:
         gv, rv = INT8_VALUES[g], INT8_VALUES[r]
@@ -116,6 +117,8 @@ def code_mismatches(got: np.ndarray, ref: np.ndarray, quot: np.ndarray, rel: flo
                 float((dist[ok][~small] / np.abs(mid[ok][~small])).max()))
         for b in np.searchsorted(_HIST_EDGES, frac, side="right"):
             _TIE_STATS["window_frac_hist"][int(b)] += 1
+    if return_bad:
+        return int(bad.size), bad[~ok]
     nbad = int((~ok).sum())
     first = int(bad[np.argmax(~ok)]) if nbad else -1
     return int(bad.size), nbad, first
@@ -156,7 +159,9 @@ def rounding_interval(values: np.ndarray, int8: bool = False):
 # the code maximum, Q g_p the peak of contribution p) and the kernel by less, so the two differ
 # by at most REDUCE_SUM_REL Q sum_p g_p per element, with a margin of about 4.  For blocks whose
 # contributions do not cancel that is ~2^-22 code units or less, far inside the tie window; it
-# grows only where the sum cancels far below the contributions' peaks, and there it decides.
+# grows only where the sum cancels far below the contributions' peaks.  The reduce's results are
+# held to the tie rule first; only a code or scale that fails it may be admitted under this
+# bound, and is counted apart from the ties.
 REDUCE_SUM_REL = 2.0 ** -38
 
 
