@@ -716,8 +716,9 @@ def test_reduce_ill_conditioned_blocks(oracle, tfp8, flags):
     # negation, with two ordinary contributions between them.  Summed in that order in float64
     # the small terms are rounded away against contribution 0 wherever it is nonzero, and the
     # oracle (original domain) and the kernel (rotated domain) keep different parts of them.
-    # Such blocks are held to the bound both float64 sums satisfy (tiecheck.reduce_sum_bound);
-    # the odd blocks, with the same pattern at ordinary scale, to the tie rule.
+    # Codes and scales of such blocks that fail the tie rule are admitted within the bound both
+    # float64 sums satisfy (tiecheck.reduce_sum_bound); the odd blocks, with the same pattern at
+    # ordinary scale, have a bound far inside the tie window.
     from tiecheck import TIE_ABS, reduce_quotient_slack, reduce_sum_bound
 
     B, nb = 128, 64
@@ -727,7 +728,8 @@ def test_reduce_ill_conditioned_blocks(oracle, tfp8, flags):
     enc = [oracle.compress(f32_to_bf16_bits(v.astype(np.float32).reshape(-1)), B, 1.0,
                            flags=flags) for v in xs]
     q, a, s = (np.stack([e[i] for e in enc]) for i in range(3))
-    # the construction reaches the case: the even blocks are beyond the tie rule, the odd not
+    # the construction reaches the case: the even blocks' bound dwarfs the tie window, the odd
+    # blocks' does not
     Q = 127.0 if flags & FLAG_INT8 else 448.0
     _, ra, rs = oracle.reduce_fp8(q, a, s, B, 1.0, flags=flags)
     w, _ = reduce_quotient_slack(reduce_sum_bound(a, s, Q), ra, rs, Q)
