@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import (DEV, assert_bf16_match, assert_codes_match_every_block, assert_scales,
+from gpu_helpers import (DEV, assert_codes_match_every_block, assert_scales,
                          assert_periodic_codes, assert_periodic_decompress, fill_periodic,
                          bits_to_gpu, check_compress, check_decompress, check_reduce, cpu,
                          f32_to_gpu, gpu_bf16_bits, say, u8_to_gpu)
