@@ -184,7 +184,7 @@ def check_reduce(oracle, tfp8, q, a, s, B, T=1.0, what="reduce", flags: int = 0,
     _count_in_blocks(cq, rq, B, block_mask, flags, mask_ledger)
     say(f"  {what}: P={P} n={n} B={B} flags={flags}: code tie mismatches {nmis} ({nmis / n:.2e}), "
         f"max rel err alpha {ea:.2e} scale {es:.2e}"
-        + (f"; {nfb} codes or blocks within the float64 sums' bound" if nfb else ""))
+        + (f"; {nfb} codes or blocks in float64 noise at the tie window's scale" if nfb else ""))
     return (cq, ca, cs) if gpu else (rq, ra, rs)
 
 
@@ -195,28 +195,39 @@ def assert_reduce_matches(cq, ca, cs, rq, rt, ra, rs, alpha_in, scale_in, B: int
     admitted only if the code is the rounding of some quotient within the float64 sums' slack w
     of its block (tiecheck.reduce_sum_bound, reduce_quotient_slack; ~1e-8 code units for blocks
     whose contributions do not cancel, so nothing more than the tie rule is admitted there), or if
-    the block's reference peak lies inside that noise (M <= 2 D).  Scales: alpha' and s' within
+    the block's reference peak lies inside that noise (M <= 2 D).  In blocks whose w reaches an
+    eighth of the tie window's absolute term, every mismatch is counted apart from the ties.  Scales: alpha' and s' within
     1e-6 relative, zero blocks exact, alpha inside the clamp range; a block that fails this is
     admitted only within the relative error D allows, or, with M <= 2 D, with a peak of at most
-    M + D.  Returns (ties, codes and blocks admitted under the bound, max rel err alpha, s over
-    the blocks held to 1e-6)."""
+    M + D.  Returns (ties, codes and blocks counted apart, max rel err alpha, s over the blocks
+    held to 1e-6)."""
     from tiecheck import (assert_codes_within, code_mismatches, reduce_quotient_slack,
                           reduce_sum_bound)
+
+    from tiecheck import TIE_ABS
 
     int8 = bool(flags & FLAG_INT8)
     Q = 127.0 if int8 else 448.0
     nb = ra.size
     D = reduce_sum_bound(alpha_in, scale_in, Q)
     w, M = reduce_quotient_slack(D, ra, rs, Q)
-    # codes
-    nmis, bad = code_mismatches(cq, rq, rt, int8=int8, return_bad=True)
+    # codes: the tie rule, and the bound for what fails it.  Mismatches in blocks whose float64
+    # noise can reach the tie window's scale (w above an eighth of its absolute term) may be
+    # noise rather than rounding ties, so they are counted apart and kept out of the tie
+    # statistics and cap.
+    noisy = np.repeat(w > TIE_ABS / 8, B)
+    idx = np.arange(cq.size)
+    nm_q, bad_q = code_mismatches(cq[~noisy], rq[~noisy], rt[~noisy], int8=int8, return_bad=True)
+    nm_n, bad_n = code_mismatches(cq[noisy], rq[noisy], rt[noisy], int8=int8, return_bad=True,
+                                  record=False)
+    bad = np.concatenate([idx[~noisy][bad_q], idx[noisy][bad_n]])
     blk = bad // B
     fin = np.isfinite(w[blk])
     if fin.any():
         assert_codes_within(cq[bad[fin]], rt[bad[fin]], w[blk[fin]], int8,
                             what=what + " codes (float64 sums' bound)")
     noise_blocks = set(blk[~fin].tolist())
-    nties = nmis - int(bad.size)
+    nties = nm_q - int(bad_q.size)
     assert nties <= max_frac * max(cq.size, 1), (f"{what}: {nties} tie mismatches of {cq.size} "
                                                 f"exceed {max_frac}")
     # scales
@@ -243,7 +254,7 @@ def assert_reduce_matches(cq, ca, cs, rq, rt, ra, rs, alpha_in, scale_in, B: int
             noise_blocks.add(int(k))
     for k in noise_blocks:  # codes of a block inside its noise: only its peak is bounded
         assert D[k] > 0 and s64[k] * Q / a64[k] <= M[k] + D[k], f"{what}: block {k} beyond its noise"
-    return nties, int(bad.size) + len(off), float(ea[std].max(initial=0.0)), \
+    return nties, int(bad_q.size) + nm_n + len(off), float(ea[std].max(initial=0.0)), \
         float(es[std].max(initial=0.0))
 
 

@@ -76,9 +76,11 @@ def tie_window_stats() -> dict:
 
 
 def code_mismatches(got: np.ndarray, ref: np.ndarray, quot: np.ndarray, rel: float = TIE_REL,
-                    abs_: float = TIE_ABS, int8: bool = False, return_bad: bool = False):
+                    abs_: float = TIE_ABS, int8: bool = False, return_bad: bool = False,
+                    record: bool = True):
     """Return (n_mismatch, n_inadmissible, first_bad_index or -1), or with return_bad
-    (n_mismatch, indices of the inadmissible mismatches)."""
+    (n_mismatch, indices of the inadmissible mismatches).  With record=False the admitted
+    mismatches are left out of the session's tie statistics."""
     got = np.asarray(got, np.uint8).reshape(-1)
     ref = np.asarray(ref, np.uint8).reshape(-1)
     quot = np.asarray(quot, np.float64).reshape(-1)
@@ -101,7 +103,7 @@ def code_mismatches(got: np.ndarray, ref: np.ndarray, quot: np.ndarray, rel: flo
     window = rel * np.abs(mid) + abs_
     near = dist <= window
     ok = adjacent & near
-    if ok.any():
+    if ok.any() and record:
         frac = dist[ok] / window[ok]
         _TIE_STATS["admitted"] += int(ok.sum())
         _TIE_STATS["max_window_frac"] = max(_TIE_STATS["max_window_frac"], float(frac.max()))
