@@ -1200,6 +1200,39 @@ def test_accumulate_cancelling_blocks(oracle, tfp8, B, gdtype, flags, inplace):
                       inplace=inplace)
 
 
+@pytest.mark.parametrize("B", [64, 128, 256, 512])
+def test_accumulate_each_output_in_place_or_not(oracle, tfp8, B):
+    # Each of codes_out, alpha_out and scale_out may be its input or a separate buffer.  The exact
+    # pass reads the codes, s and the set-aside marks (-alpha in alpha_out) back, so every one of
+    # the 8 combinations is run on blocks that cancel (most of them take that pass) and must equal
+    # the out-of-place call bit for bit.
+    rng = np.random.default_rng(8080 + B)
+    nb = 2 * 64 + 5
+    xm = f32_to_bf16_bits(rng.laplace(0, 0.05, nb * B).astype(np.float32))
+    q, a, s = oracle.compress(xm, B, 1.0)
+    local = -bf16_bits_to_f32(xm).astype(np.float64) + rng.normal(0, 1e-4, nb * B)
+    keep = rng.random(nb) < 0.3
+    local.reshape(nb, B)[keep] = rng.laplace(0, 0.03, (int(keep.sum()), B))
+    gg = bits_to_gpu(f32_to_bf16_bits(local.astype(np.float32)))
+    ref = tfp8.accumulate(u8_to_gpu(q), f32_to_gpu(a), f32_to_gpu(s), gg, B, 1.0)
+    torch.cuda.synchronize()
+    ref = [cpu(t) for t in ref]
+    for combo in range(8):
+        ins = [u8_to_gpu(q), f32_to_gpu(a), f32_to_gpu(s)]
+        outs = [ins[i] if combo >> i & 1 else torch.empty_like(ins[i]) for i in range(3)]
+        st = tfp8.accumulate_raw(ins[0].data_ptr(), ins[1].data_ptr(), ins[2].data_ptr(),
+                                 gg.data_ptr(), tfp8.BF16, q.size, B, 1.0, outs[0].data_ptr(),
+                                 outs[1].data_ptr(), outs[2].data_ptr(),
+                                 torch.cuda.current_stream().cuda_stream)
+        assert st == 0, tfp8.status_string(st)
+        torch.cuda.synchronize()
+        for o, r, name in zip(outs, ref, ("codes", "alpha", "scale")):
+            assert np.array_equal(cpu(o), r), f"B={B} in-place mask {combo:03b}: {name} differ"
+    # and the out-of-place result against the oracle
+    _check_accumulate(oracle, tfp8, q, a, s, f32_to_bf16_bits(local.astype(np.float32)), B,
+                      f"in-place combinations B={B}")
+
+
 def test_accumulate_zero_main_gradient_equals_compress(oracle, tfp8):
     B, nb = 128, 77
     g = random_bf16_bits(nb * B, seed=12, scale=0.2)
