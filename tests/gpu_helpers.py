@@ -190,46 +190,42 @@ def check_reduce(oracle, tfp8, q, a, s, B, T=1.0, what="reduce", flags: int = 0,
 
 def assert_reduce_matches(cq, ca, cs, rq, rt, ra, rs, alpha_in, scale_in, B: int, flags: int,
                           max_frac: float, what: str):
-    """A reduce's codes and scales against the oracle's.  Codes: identical except admissible
-    rounding ties, at most max_frac of the elements.  A mismatch that is not such a tie is
-    admitted only if the code is the rounding of some quotient within the float64 sums' slack w
-    of its block (tiecheck.reduce_sum_bound, reduce_quotient_slack; ~1e-8 code units for blocks
-    whose contributions do not cancel, so nothing more than the tie rule is admitted there), or if
-    the block's reference peak lies inside that noise (M <= 2 D).  In blocks whose w reaches an
-    eighth of the tie window's absolute term, every mismatch is counted apart from the ties.  Scales: alpha' and s' within
-    1e-6 relative, zero blocks exact, alpha inside the clamp range; a block that fails this is
-    admitted only within the relative error D allows, or, with M <= 2 D, with a peak of at most
-    M + D.  Returns (ties, codes and blocks counted apart, max rel err alpha, s over the blocks
-    held to 1e-6)."""
-    from tiecheck import (assert_codes_within, code_mismatches, reduce_quotient_slack,
-                          reduce_sum_bound)
+    """A reduce's codes and scales against the oracle's.
 
-    from tiecheck import TIE_ABS
+    Blocks whose float64 noise stays far inside the tie window (slack w of tiecheck's
+    reduce_quotient_slack under an eighth of its absolute term: every block whose contributions
+    do not cancel by a large factor) are held to the tie rule, their ties capped at max_frac of
+    the elements, and to the 1e-6 scale bar with zero blocks exact.  In the other blocks a code
+    that is not an admissible tie must be the rounding of some quotient within w of the
+    oracle's, alpha' and s' must lie within 1e-6 or the relative error that the bound D allows,
+    and where the reference peak M lies inside the noise (M <= 2 D) the GPU's peak must be at
+    most M + D; their mismatches are counted apart from the ties and kept out of the tie
+    statistics.  Every alpha must lie inside the clamp range.  Returns (ties, codes and blocks
+    counted apart, max rel err alpha, s over the blocks within 1e-6)."""
+    from tiecheck import (TIE_ABS, assert_codes_match, assert_codes_within, code_mismatches,
+                          reduce_quotient_slack, reduce_sum_bound)
 
     int8 = bool(flags & FLAG_INT8)
     Q = 127.0 if int8 else 448.0
-    nb = ra.size
     D = reduce_sum_bound(alpha_in, scale_in, Q)
     w, M = reduce_quotient_slack(D, ra, rs, Q)
-    # codes: the tie rule, and the bound for what fails it.  Mismatches in blocks whose float64
-    # noise can reach the tie window's scale (w above an eighth of its absolute term) may be
-    # noise rather than rounding ties, so they are counted apart and kept out of the tie
-    # statistics and cap.
-    noisy = np.repeat(w > TIE_ABS / 8, B)
-    idx = np.arange(cq.size)
-    nm_q, bad_q = code_mismatches(cq[~noisy], rq[~noisy], rt[~noisy], int8=int8, return_bad=True)
+    noisy_blk = w > TIE_ABS / 8
+    noisy = np.repeat(noisy_blk, B)
+    # codes of the ordinary blocks: the tie rule, the cap over the whole tensor
+    nties = assert_codes_match(cq[~noisy], rq[~noisy], rt[~noisy], max_frac=1.0,
+                               what=what + " codes", int8=int8)
+    assert nties <= max_frac * max(cq.size, 1), (f"{what}: {nties} tie mismatches of {cq.size} "
+                                                f"exceed {max_frac}")
+    # codes of the noisy blocks: the tie rule, else the float64 sums' bound
     nm_n, bad_n = code_mismatches(cq[noisy], rq[noisy], rt[noisy], int8=int8, return_bad=True,
                                   record=False)
-    bad = np.concatenate([idx[~noisy][bad_q], idx[noisy][bad_n]])
+    bad = np.arange(cq.size)[noisy][bad_n]
     blk = bad // B
     fin = np.isfinite(w[blk])
     if fin.any():
         assert_codes_within(cq[bad[fin]], rt[bad[fin]], w[blk[fin]], int8,
                             what=what + " codes (float64 sums' bound)")
     noise_blocks = set(blk[~fin].tolist())
-    nties = nm_q - int(bad_q.size)
-    assert nties <= max_frac * max(cq.size, 1), (f"{what}: {nties} tie mismatches of {cq.size} "
-                                                f"exceed {max_frac}")
     # scales
     inside = (ca >= ALPHA_MIN) & (ca <= ALPHA_MAX)
     assert inside.all(), f"{what}: {int((~inside).sum())} alpha outside the clamp range"
@@ -242,19 +238,18 @@ def assert_reduce_matches(cq, ca, cs, rq, rt, ra, rs, alpha_in, scale_in, B: int
     std = (ea <= 1e-6) & (es <= 1e-6)
     off = np.nonzero(~std)[0]
     for k in off:
-        assert D[k] > 0, f"{what}: block {k} of all-zero contributions is not an exact zero block"
+        assert noisy_blk[k], (f"{what}: block {k} alpha {a64[k]!r} s {s64[k]!r} against "
+                              f"{ra64[k]!r}, {rs64[k]!r}: beyond 1e-6 (zero blocks exactly)")
         if np.isfinite(w[k]):
             rel_a = 1e-6 + 2 * np.sqrt(B) * D[k] / M[k]
             rel_s = rel_a + 2 * D[k] / M[k] + 1e-6
-            assert ea[k] <= rel_a and es[k] <= rel_s, (f"{what}: block {k} alpha {a64[k]!r} s "
-                                                       f"{s64[k]!r} against {ra64[k]!r}, {rs64[k]!r}")
+            assert ea[k] <= rel_a and es[k] <= rel_s, (
+                f"{what}: block {k} alpha {a64[k]!r} s {s64[k]!r} against {ra64[k]!r}, {rs64[k]!r}")
         else:
-            assert D[k] > 0 and s64[k] * Q / a64[k] <= M[k] + D[k], (
-                f"{what}: block {k} peak {s64[k] * Q / a64[k]!r} beyond its noise {M[k] + D[k]!r}")
             noise_blocks.add(int(k))
-    for k in noise_blocks:  # codes of a block inside its noise: only its peak is bounded
-        assert D[k] > 0 and s64[k] * Q / a64[k] <= M[k] + D[k], f"{what}: block {k} beyond its noise"
-    return nties, int(bad_q.size) + nm_n + len(off), float(ea[std].max(initial=0.0)), \
+    for k in noise_blocks:  # a block inside its noise: only its peak is bounded
+        assert s64[k] * Q / a64[k] <= M[k] + D[k], f"{what}: block {k} peak beyond its noise"
+    return nties, nm_n + len(off), float(ea[std].max(initial=0.0)), \
         float(es[std].max(initial=0.0))
 
 
