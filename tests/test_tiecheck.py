@@ -95,3 +95,52 @@ def test_reduce_sum_bound_and_slack():
     assert M[0] == Q and w[0] == pytest.approx(Q * 1e-3 * (1 / Q + 1 / (Q - 1e-3)))
     assert np.isinf(w[1])   # M <= 2 D
     assert w[2] == 0.0      # D = 0: the sum is exactly zero, no slack
+
+
+def test_reduce_sum_bound_holds(oracle):
+    # The bound D between the kernel's and the oracle's float64 reduce sums, against the exact
+    # sum.  For random reduces, including a contribution cancelled exactly by a later one with
+    # smaller ones between them, and pairs that cancel to 2^-30 of their peaks, the oracle's sum
+    # (r = t s' / alpha' from its quotients and scales) and a float64 sum in the kernel's order
+    # (factors s_p / alpha_p cut to 46 significant bits, products exact, one rounding per
+    # addition) each lie within D / 2 of the exact rotated-domain sum r = sum_p (s_p / alpha_p)
+    # dec(q_p), computed with rationals from the stored float32 scales.
+    from fractions import Fraction
+
+    from workloads import f32_to_bf16_bits
+
+    rng = np.random.default_rng(4242)
+    for case in range(24):
+        B = int(rng.choice([64, 128, 256]))
+        P = int(rng.integers(2, 7))
+        flags = int(rng.integers(0, 2))
+        Q = 127.0 if flags else 448.0
+        nb = 2
+        xs = [rng.laplace(0, 1, nb * B) * 2.0 ** rng.uniform(-20, 20) for _ in range(P)]
+        mode = case % 3
+        if mode == 1:   # the last contribution cancels the first, huge one, exactly
+            xs[0] = xs[0] * 2.0 ** 60
+            xs[-1] = -xs[0]
+        elif mode == 2:  # the second nearly cancels the first
+            xs[1] = -xs[0] * (1 + 2.0 ** -30 * rng.standard_normal(nb * B))
+        enc = [oracle.compress(f32_to_bf16_bits(v.astype(np.float32)), B, 1.0, flags=flags)
+               for v in xs]
+        q = np.stack([e[0] for e in enc])
+        a = np.stack([e[1] for e in enc])
+        s = np.stack([e[2] for e in enc])
+        _, ra, rs, rt = oracle.reduce_fp8(q, a, s, B, 1.0, with_quot=True, flags=flags)
+        table = INT8_VALUES if flags else E4M3_VALUES
+        dec = table[q].reshape(P, nb, B)
+        r_ref = rt.reshape(nb, B) * (rs.astype(np.float64) / ra)[:, None]
+        g = s.astype(np.float64) / a.astype(np.float64)
+        g = (g.view(np.int64) & ~np.int64(0x7F)).view(np.float64)  # 46 bits: the coarser cut
+        r_k = np.zeros((nb, B))
+        for p in range(P):
+            r_k = r_k + g[p][:, None] * dec[p]
+        D = reduce_sum_bound(a, s, Q)
+        for k in range(nb):
+            fr = [Fraction(float(s[p, k])) / Fraction(float(a[p, k])) for p in range(P)]
+            exact = np.array([float(sum(fr[p] * Fraction(float(dec[p, k, i])) for p in range(P)))
+                              for i in range(B)])
+            assert np.abs(r_ref[k] - exact).max() <= D[k] / 2, (case, k, "oracle")
+            assert np.abs(r_k[k] - exact).max() <= D[k] / 2, (case, k, "kernel order")
