@@ -1463,13 +1463,17 @@ def test_large_offsets_and_grid_stride_loops_every_block(oracle, tfp8, B, dtype,
     _large_input_every_block(oracle, tfp8, B, dtype, ntiles)
 
 
-# The looping forms of the variants (INT8 codes, the rotation left out, both) at B = 128, and of
-# float32 input at B = 64 and 256 (past 2^34 and 2^35 elements).
+# The looping forms of the variants (INT8 codes, the rotation left out, both) at B = 128, of both
+# together at B = 64, 256 and 512, and of float32 input at B = 64 and 256 (past 2^34, 2^35 and
+# 2^36 elements).
 @pytest.mark.parametrize("B,dtype,ntiles,flags", [(128, "bf16", 4097, 1), (128, "bf16", 4097, 2),
-                                                  (128, "bf16", 4097, 3), (64, "f32", 4097, 0),
-                                                  (256, "f32", 8193, 0)])
+                                                  (128, "bf16", 4097, 3), (64, "bf16", 4097, 3),
+                                                  (256, "bf16", 8193, 3), (512, "bf16", 16385, 3),
+                                                  (64, "f32", 4097, 0), (256, "f32", 8193, 0)])
 def test_grid_stride_loops_variants_and_fp32_every_block(oracle, tfp8, B, dtype, ntiles, flags):
-    _large_input_every_block(oracle, tfp8, B, dtype, ntiles, flags=flags)
+    big = ntiles > 8193  # 137 GB of input: no float32 reconstruction, no reduce (as at flags 0)
+    _large_input_every_block(oracle, tfp8, B, dtype, ntiles, flags=flags, f32_out=not big,
+                             reduce=not big)
 
 
 def test_grid_stride_loops_at_block_512_every_block(oracle, tfp8):
