@@ -44,37 +44,41 @@ class TFP8Error(RuntimeError):
 _lib = None
 
 
+def _declare(L: ctypes.CDLL) -> ctypes.CDLL:
+    """Argument and result types of the C ABI's entry points on an opened build of the library."""
+    vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
+    L.tfp8_compress.argtypes = [vp, i32, i64, i32, f32, vp, vp, vp, vp]
+    L.tfp8_compress.restype = i32
+    L.tfp8_decompress.argtypes = [vp, vp, vp, i64, i32, vp, i32, vp]
+    L.tfp8_decompress.restype = i32
+    L.tfp8_reduce_fp8.argtypes = [vp, vp, vp, i32, i64, i32, f32, vp, vp, vp, vp]
+    L.tfp8_reduce_fp8.restype = i32
+    u32 = ctypes.c_uint32
+    L.tfp8_compress_ex.argtypes = [vp, i32, i64, i32, f32, u32, vp, vp, vp, vp]
+    L.tfp8_compress_ex.restype = i32
+    L.tfp8_decompress_ex.argtypes = [vp, vp, vp, i64, i32, u32, vp, i32, vp]
+    L.tfp8_decompress_ex.restype = i32
+    L.tfp8_reduce_ex.argtypes = [vp, vp, vp, i32, i64, i32, f32, u32, vp, vp, vp, vp]
+    L.tfp8_reduce_ex.restype = i32
+    L.tfp8_reduce_strided.argtypes = [vp, i64, vp, i64, vp, i64, i32, i64, i32, f32, u32,
+                                      vp, vp, vp, vp]
+    L.tfp8_reduce_strided.restype = i32
+    L.tfp8_accumulate.argtypes = [vp, vp, vp, vp, i32, i64, i32, f32, u32, vp, vp, vp, vp]
+    L.tfp8_accumulate.restype = i32
+    L.tfp8_status_string.argtypes = [i32]
+    L.tfp8_status_string.restype = ctypes.c_char_p
+    L.tfp8_version.argtypes = []
+    L.tfp8_version.restype = i32
+    return L
+
+
 def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is not built; run fp8_compression_tensor_amd/build.py "
                                "(or __graft_entry__.build())")
-        L = ctypes.CDLL(LIB_PATH)
-        vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
-        L.tfp8_compress.argtypes = [vp, i32, i64, i32, f32, vp, vp, vp, vp]
-        L.tfp8_compress.restype = i32
-        L.tfp8_decompress.argtypes = [vp, vp, vp, i64, i32, vp, i32, vp]
-        L.tfp8_decompress.restype = i32
-        L.tfp8_reduce_fp8.argtypes = [vp, vp, vp, i32, i64, i32, f32, vp, vp, vp, vp]
-        L.tfp8_reduce_fp8.restype = i32
-        u32 = ctypes.c_uint32
-        L.tfp8_compress_ex.argtypes = [vp, i32, i64, i32, f32, u32, vp, vp, vp, vp]
-        L.tfp8_compress_ex.restype = i32
-        L.tfp8_decompress_ex.argtypes = [vp, vp, vp, i64, i32, u32, vp, i32, vp]
-        L.tfp8_decompress_ex.restype = i32
-        L.tfp8_reduce_ex.argtypes = [vp, vp, vp, i32, i64, i32, f32, u32, vp, vp, vp, vp]
-        L.tfp8_reduce_ex.restype = i32
-        L.tfp8_reduce_strided.argtypes = [vp, i64, vp, i64, vp, i64, i32, i64, i32, f32, u32,
-                                          vp, vp, vp, vp]
-        L.tfp8_reduce_strided.restype = i32
-        L.tfp8_accumulate.argtypes = [vp, vp, vp, vp, i32, i64, i32, f32, u32, vp, vp, vp, vp]
-        L.tfp8_accumulate.restype = i32
-        L.tfp8_status_string.argtypes = [i32]
-        L.tfp8_status_string.restype = ctypes.c_char_p
-        L.tfp8_version.argtypes = []
-        L.tfp8_version.restype = i32
-        _lib = L
+        _lib = _declare(ctypes.CDLL(LIB_PATH))
     return _lib
 
 

@@ -21,8 +21,9 @@ SRC = os.path.join(ROOT, "fp8_compression_tensor_amd", "csrc", "tfp8_kernels.hip
 pytestmark = pytest.mark.skipif(shutil.which("hipcc") is None, reason="hipcc not available")
 
 
-@pytest.fixture(scope="module")
-def kernels(tmp_path_factory):
+def _kernel_bodies(out, extra=()):
+    """Instructions of every kernel in the gfx950 assembly of the library's source, compiled with
+    the library's build flags (plus `extra`), by kernel symbol."""
     import importlib.util
 
     # the library's build flags, loaded under a private name (no sys.path or module clash)
@@ -32,9 +33,8 @@ def kernels(tmp_path_factory):
     spec.loader.exec_module(mod)
     HIPCC_FLAGS = mod.HIPCC_FLAGS
 
-    out = str(tmp_path_factory.mktemp("asm") / "k.s")
     flags = [f for f in HIPCC_FLAGS if f not in ("-shared", "-fPIC")]
-    r = subprocess.run(["hipcc", *flags, "--cuda-device-only", "-S", "-o", out, SRC],
+    r = subprocess.run(["hipcc", *flags, *extra, "--cuda-device-only", "-S", "-o", out, SRC],
                        capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
     text = open(out).read().split("\n")
@@ -53,6 +53,11 @@ def kernels(tmp_path_factory):
             if ins and not ins.startswith(".") and not ins.endswith(":"):
                 cur.append(ins)
     return bodies
+
+
+@pytest.fixture(scope="module")
+def kernels(tmp_path_factory):
+    return _kernel_bodies(str(tmp_path_factory.mktemp("asm") / "k.s"))
 
 
 def _regs(tok):
@@ -121,3 +126,18 @@ def test_dot_results_wait_three_states(kernels):
                     break
     assert checked > 0
     assert not bad, bad[:5]
+
+
+def test_capped_test_build_has_the_same_kernels(kernels, tmp_path):
+    # The GPU tests of the grid-stride loops use a second build of the library with every launch
+    # capped at one workgroup per compute unit (tests/capped_build).  The caps only change the
+    # host's choice of grid: every kernel must compile to the same instructions.
+    import importlib.util
+
+    spec = importlib.util.spec_from_file_location(
+        "_tfp8_capped_build", os.path.join(ROOT, "tests", "capped_build", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    capped = _kernel_bodies(str(tmp_path / "capped.s"), mod.CAPS)
+    assert sorted(capped) == sorted(kernels)
+    assert all(capped[k] == kernels[k] for k in kernels)

@@ -1353,15 +1353,18 @@ _LARGE_CASES = [(128, "bf16", 513), (64, "bf16", 513), (512, "bf16", 513), (128,
                 (256, "bf16", 8193)]
 
 
-def _large_input_every_block(oracle, tfp8, B, dtype, ntiles, flags=0, f32_out=True, reduce=True):
-    # n = ntiles * 2^22 - 37 B elements (4.3-137 GB of input, a ragged last tile), built on the
-    # GPU from seven random tiles of 2^22 elements (tile t is part t mod 7), so that a read at
+def _large_input_every_block(oracle, tfp8, B, dtype, ntiles, flags=0, f32_out=True, reduce=True,
+                             tile=1 << 22, seed=None, cancel=()):
+    # n = ntiles * tile - 37 B elements (4.3-137 GB of input at tiles of 2^22, a ragged last
+    # tile), built on the GPU from seven random tiles (tile t is part t mod 7), so that a read at
     # an offset cut to 32 bits (1024 tiles away for codes, 512 for bfloat16, 256 for float32)
     # or any other wrong place shows.  Compress, decompress to bfloat16 and (f32_out) float32,
     # the reduce (reduce) and accumulate each run on the whole tensor with the given variant
-    # flags; every output block is checked against the oracle's output for its part.  No
-    # expected value comes from the GPU.
-    T, tile = 1.0, 1 << 22
+    # flags; every output block is checked against the oracle's output for its part.  The
+    # accumulation's local gradient is the input with the parts in `cancel` negated: there it
+    # cancels the main gradient down to its quantisation error, and the blocks go to the second
+    # kernel.  No expected value comes from the GPU.
+    T = 1.0
     n = ntiles * tile - 37 * B
     nb, bpt = n // B, tile // B
     f32 = dtype == "f32"
@@ -1373,16 +1376,16 @@ def _large_input_every_block(oracle, tfp8, B, dtype, ntiles, flags=0, f32_out=Tr
     free, _ = torch.cuda.mem_get_info(DEV)
     if free < peak:
         pytest.skip(f"needs {peak / 1e9:.0f} GB of free device memory, {free / 1e9:.0f} GB free")
-    variants = _seven_parts(tile, 2034 + 8 * B, dtype)
+    variants = _seven_parts(tile, 2034 + 8 * B if seed is None else seed, dtype)
     enc = [oracle.compress(v, B, T, with_quot=True, flags=flags) for v in variants]
     say(f"  large input B={B} {dtype} flags={flags}: n = {n} ({n * (4 if f32 else 2) / 1e9:.1f} GB of "
         f"input), every block")
 
-    def input_on_gpu():
+    def input_on_gpu(parts=variants):
         if f32:
-            return fill_periodic(torch.empty(n, dtype=torch.float32, device=DEV), variants, tile)
+            return fill_periodic(torch.empty(n, dtype=torch.float32, device=DEV), parts, tile)
         return fill_periodic(torch.empty(n, dtype=torch.int16, device=DEV),
-                             [v.view(np.int16) for v in variants], tile).view(torch.bfloat16)
+                             [v.view(np.int16) for v in parts], tile).view(torch.bfloat16)
 
     def codes_on_gpu(parts):
         # the oracle's codes, alpha and s of the seven tiles, tiled like the input
@@ -1444,13 +1447,16 @@ def _large_input_every_block(oracle, tfp8, B, dtype, ntiles, flags=0, f32_out=Tr
         torch.cuda.empty_cache()
         say(f"  large reduce: tie mismatches {nmis}, max rel err alpha {ea:.2e} s {es:.2e}")
 
-    # accumulate in place: main gradient = the tiled codes, local gradient = the input
-    x = input_on_gpu()
+    # accumulate in place: main gradient = the tiled codes, local gradient = the input, with the
+    # parts in `cancel` negated (the sign bit flipped: exact in both types)
+    local = [(v ^ np.uint16(0x8000) if v.dtype == np.uint16 else -v) if w in cancel else v
+             for w, v in enumerate(variants)]
+    x = input_on_gpu(local)
     tfp8.accumulate(qg, ag, sg, x, B, T, inplace=True, flags=flags)
     torch.cuda.synchronize()
     del x
     refs = [oracle.accumulate(e[0], e[1], e[2], v, B, T, with_quot=True, flags=flags)
-            for e, v in zip(enc, variants)]
+            for e, v in zip(enc, local)]
     nmis, ea, es = assert_periodic_codes(qg, ag, sg, refs, n, tile, B,
                                          what="large accumulate", flags=flags)
     del qg, ag, sg
@@ -1483,6 +1489,52 @@ def test_grid_stride_loops_at_block_512_every_block(oracle, tfp8):
     # decompress (275 GB) and the reduce (its loop at B = 512 starts at 2^34 and is checked
     # above) are left out.  Like every case here it skips on a device without the memory.
     _large_input_every_block(oracle, tfp8, 512, "bf16", 16385, f32_out=False, reduce=False)
+
+
+# The looping forms again, through a second build of the library with every launch capped at one
+# workgroup per compute unit (tests/capped_build; the kernels compile to the same instructions,
+# checked by tests/test_codegen_hazards.py).  At 2^24 - 37 B elements each wavefront works through
+# 4-32 tiles in turn (compress at B = 512: 4092 tiles over 1024 wavefronts), against one or two in
+# the cases above, at every block size, input type and flag set.  Parts 1 and 4 of the
+# accumulation's local gradient cancel the main gradient, so its second kernel, grid-striding too,
+# redoes two sevenths of the blocks.  The last cases pass the 1.5 GiB at which compress switches to
+# one wavefront per workgroup with each XCD on a contiguous eighth of the tiles: its 256
+# wavefronts then loop 388-3088 times, and the other kernels 97-1544 times.  Among them is float32
+# input at B = 512, whose looping form the full build reaches only past 2^36 elements (275 GB).
+_CAPPED_LIB = os.path.join(os.path.dirname(os.path.abspath(__file__)), "capped_build",
+                           "libtfp8_capped.so")
+_capped_cdll = []
+
+
+@pytest.fixture
+def capped(tfp8, monkeypatch):
+    """The package, its calls routed through the capped build for the test's duration."""
+    import ctypes
+
+    assert os.path.exists(_CAPPED_LIB), (f"{_CAPPED_LIB} is not built; run "
+                                         "tests/capped_build/build.py (or __graft_entry__.build())")
+    if not _capped_cdll:
+        _capped_cdll.append(tfp8._declare(ctypes.CDLL(_CAPPED_LIB)))
+    monkeypatch.setattr(tfp8, "_lib", _capped_cdll[0])
+    yield tfp8
+
+
+@pytest.mark.parametrize("B,dtype,flags", [(B, "bf16", f) for B in (64, 128, 256, 512)
+                                           for f in (0, 1, 2, 3)] +
+                                          [(B, "f32", f) for B in (64, 128, 256, 512)
+                                           for f in (0, 3)])
+def test_capped_launches_loop_every_block(oracle, capped, B, dtype, flags):
+    _large_input_every_block(oracle, capped, B, dtype, 64, flags=flags, tile=1 << 18,
+                             seed=3034 + 8 * B + flags, cancel=(1, 4))
+
+
+@pytest.mark.parametrize("B,dtype,ntiles,flags", [(512, "f32", 97, 0), (512, "f32", 97, 3),
+                                                  (64, "bf16", 193, 0), (256, "bf16", 193, 1)])
+def test_capped_launches_remapped_loop_every_block(oracle, capped, B, dtype, ntiles, flags):
+    n = ntiles * (1 << 22) - 37 * B
+    assert n * (4 if dtype == "f32" else 2) >= 3 << 29  # compress's remapped launch shape
+    _large_input_every_block(oracle, capped, B, dtype, ntiles, flags=flags,
+                             seed=4034 + 8 * B + flags, cancel=(1, 4))
 
 
 def _sweep_input(rng, nb, B):
