@@ -403,20 +403,45 @@ __global__ __launch_bounds__(kThreads) void k_compress(const void *__restrict__ 
 // the 8-lane group reads each block's codes, and writes its output, in whole lines.
 constexpr int decompress_lanes(int) { return 8; }
 
-template <int B>
+// Element layout in a block's 8-lane group.  Each run of 64 elements is spread over the lanes
+// and 8 registers per lane; the transform is the same whatever element bits the lane and
+// register bits stand for, provided the codes are read and the output written with the same
+// assignment (H[i][k] = (-1)^popcount(i & k) does not change when one permutation of the bits
+// is applied to both i and k).
+//   bfloat16 output: lane j holds elements [8 j, 8 j + 8) of the run (lane bits = element bits
+//     3-5), so each lane stores 16 bytes and the group's store instruction writes one whole line.
+//   float32 output: lane j holds elements [4 j, 4 j + 4) and [32 + 4 j, 32 + 4 j + 4) (lane
+//     bits = element bits 2-4; register bit 2 = element bit 5), so each of the two 16-byte
+//     stores of a run covers a whole line across the group.  With the bfloat16 layout each
+//     store instruction covered half of every line the group writes: with non-temporal stores
+//     that cost a second partial write per line, with plain ones the L2 had to join the halves.
+//     The line layout with non-temporal stores was 4-9% faster than the half-line one with plain
+//     stores over back-to-back launches through rotating buffers, on 117 M elements at every B
+//     (102.0 against 108.2 us at B = 128, 117.1 against 122.6 us at B = 256), with the same
+//     output bits.
+template <int B, bool F32OUT>
 struct DecompressIn {
-  u32x2 d[B / (8 * decompress_lanes(B))];
+  u32x2 d[B / (8 * decompress_lanes(B))];  // per run: registers 0-3 and 4-7 as two dwords
   float s, a;
 };
 
-template <int B>
-__device__ __forceinline__ void load_decompress_in(DecompressIn<B> &in, const uint8_t *codes,
-                                                   const float *alpha, const float *scale,
-                                                   int64_t blk, int j) {
+template <int B, bool F32OUT>
+__device__ __forceinline__ void load_decompress_in(DecompressIn<B, F32OUT> &in,
+                                                   const uint8_t *codes, const float *alpha,
+                                                   const float *scale, int64_t blk, int j) {
   constexpr int RS = 8 * decompress_lanes(B);
-  const uint8_t *cb = codes + blk * B + 8 * j;
+  if constexpr (F32OUT) {
+    const uint8_t *cb = codes + blk * B + 4 * j;
 #pragma unroll
-  for (int g = 0; g < B / RS; ++g) in.d[g] = ld_stream((const u32x2 *)(cb + RS * g));
+    for (int g = 0; g < B / RS; ++g) {
+      in.d[g][0] = ld_stream((const uint32_t *)(cb + RS * g));
+      in.d[g][1] = ld_stream((const uint32_t *)(cb + RS * g + 32));
+    }
+  } else {
+    const uint8_t *cb = codes + blk * B + 8 * j;
+#pragma unroll
+    for (int g = 0; g < B / RS; ++g) in.d[g] = ld_stream((const u32x2 *)(cb + RS * g));
+  }
   in.s = scale[blk];
   in.a = alpha[blk];
 }
@@ -443,16 +468,17 @@ __global__ __launch_bounds__(kThreads) void k_decompress(const uint8_t *__restri
   const int64_t nwaves = ((int64_t)gridDim.x * kThreads) >> 6;
   const int64_t ntiles = (int64_t)(((uint64_t)nb + BPW - 1) / BPW);  // nb >= 0
 
-  DecompressIn<B> cur;  // groups past the last block re-read the last block, store nothing
+  DecompressIn<B, F32OUT> cur;  // groups past the last block re-read the last block, store nothing
   if (wave < ntiles)
-    load_decompress_in<B>(cur, codes, alpha, scale, min(wave * BPW + bw, nb - 1), j);
+    load_decompress_in<B, F32OUT>(cur, codes, alpha, scale, min(wave * BPW + bw, nb - 1), j);
 
   for (int64_t tile = wave; tile < ntiles; tile += nwaves) {
     const int64_t blk = tile * BPW + bw;
     const bool active = blk < nb;
-    DecompressIn<B> nxt;
+    DecompressIn<B, F32OUT> nxt;
     if (LOOP && tile + nwaves < ntiles)
-      load_decompress_in<B>(nxt, codes, alpha, scale, min((tile + nwaves) * BPW + bw, nb - 1), j);
+      load_decompress_in<B, F32OUT>(nxt, codes, alpha, scale,
+                                    min((tile + nwaves) * BPW + bw, nb - 1), j);
 
     float v[N];
 #pragma unroll
@@ -472,7 +498,9 @@ __global__ __launch_bounds__(kThreads) void k_decompress(const uint8_t *__restri
     // six exact stages run first (within each run of 8 registers, then across the lanes), and
     // the remaining R stages run in float64 (exact there), rounded once at the end.  The
     // transform's output is then correctly rounded at every B.  (Taking the float64 stages only
-    // for blocks whose partial sums could pass 2^15 cost registers and was slower.)
+    // for blocks whose partial sums could pass 2^15 cost registers and was slower; int32
+    // stages on the values in units of 2^-9, exact as well and bit for bit the same, were
+    // 0.5-3.5% slower.)
     if constexpr (ROT) {
       if constexpr (N <= 16 || (FLAGS & kInt8)) {
         fwht_registers<N, 1>(v);
@@ -512,12 +540,8 @@ __global__ __launch_bounds__(kThreads) void k_decompress(const uint8_t *__restri
 
     if (active) {
       if constexpr (F32OUT) {
-        // A lane's 8 floats are 32 bytes, stored as two 16-byte halves, so each store instruction
-        // covers half of every 128-byte line the group writes.  These stores are plain: the L2
-        // then joins the halves into whole lines before they go to HBM, which non-temporal stores
-        // prevent (measured over back-to-back launches through rotating buffers: 36.4 against
-        // 43.5 us at B = 256, equal at B = 128).
-        float *ob = (float *)out + blk * B + 8 * pj;
+        // the line layout above: registers 0-3 of a run at 4 pj, registers 4-7 at 32 + 4 pj
+        float *ob = (float *)out + blk * B + 4 * pj;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
           u32x4 w0, w1;
@@ -526,8 +550,8 @@ __global__ __launch_bounds__(kThreads) void k_decompress(const uint8_t *__restri
             w0[q] = __float_as_uint(fmaf(v[8 * g + q], f, 0.0f) * ra);
             w1[q] = __float_as_uint(fmaf(v[8 * g + 4 + q], f, 0.0f) * ra);
           }
-          *(u32x4 *)(ob + RS * g) = w0;
-          *(u32x4 *)(ob + RS * g + 4) = w1;
+          st_stream(w0, (u32x4 *)(ob + RS * g));
+          st_stream(w1, (u32x4 *)(ob + RS * g + 32));
         }
       } else {
         __bf16 *ob = (__bf16 *)out + blk * B + 8 * pj;
