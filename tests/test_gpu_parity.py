@@ -14,12 +14,12 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import (DEV, assert_codes_match_every_block, assert_scales,
+from gpu_helpers import (DEV, assert_codes_match_every_block, assert_reduce_matches, assert_scales,
                          assert_periodic_codes, assert_periodic_decompress, fill_periodic,
                          bits_to_gpu, check_compress, check_decompress, check_reduce, cpu,
                          f32_to_gpu, gpu_bf16_bits, say, u8_to_gpu)
 from tiecheck import (FLAG_INT8, FLAG_NO_ROTATION, assert_codes_match, assert_rel_close,
-                      rounding_interval)
+                      rounding_interval, tie_cap)
 from workloads import (GPT2_7B, GPT6_7B, GPT13B_GRAD, QWEN7B, TINY, WORKLOADS, bf16_bits_to_f32,
                        f32_to_bf16_bits, make_shard, make_shards, random_bf16_bits)
 
@@ -1506,16 +1506,23 @@ _CAPPED_LIB = os.path.join(os.path.dirname(os.path.abspath(__file__)), "capped_b
 _capped_cdll = []
 
 
-@pytest.fixture
-def capped(tfp8, monkeypatch):
-    """The package, its calls routed through the capped build for the test's duration."""
+def _capped():
+    """The capped build, opened once and declared like the package's library."""
     import ctypes
+
+    import fp8_compression_tensor_amd as m
 
     assert os.path.exists(_CAPPED_LIB), (f"{_CAPPED_LIB} is not built; run "
                                          "tests/capped_build/build.py (or __graft_entry__.build())")
     if not _capped_cdll:
-        _capped_cdll.append(tfp8._declare(ctypes.CDLL(_CAPPED_LIB)))
-    monkeypatch.setattr(tfp8, "_lib", _capped_cdll[0])
+        _capped_cdll.append(m._declare(ctypes.CDLL(_CAPPED_LIB)))
+    return _capped_cdll[0]
+
+
+@pytest.fixture
+def capped(tfp8, monkeypatch):
+    """The package, its calls routed through the capped build for the test's duration."""
+    monkeypatch.setattr(tfp8, "_lib", _capped())
     yield tfp8
 
 
@@ -1526,6 +1533,74 @@ def capped(tfp8, monkeypatch):
 def test_capped_launches_loop_every_block(oracle, capped, B, dtype, flags):
     _large_input_every_block(oracle, capped, B, dtype, 64, flags=flags, tile=1 << 18,
                              seed=3034 + 8 * B + flags, cancel=(1, 4))
+
+
+def _random_codes(rng, P, n, B, flags):
+    """Codes, alpha and s of P contributions drawn directly (any codes are valid reduce inputs):
+    uniform codes without the E4M3 NaN patterns (INT8: without -128), alpha log-uniform in
+    [2^-8, 2^8], s in [2^-10, 2^2]; block 1 of every contribution is a zero block and block 2 of
+    contribution 0 is the exact negation of contribution 1's."""
+    nb = n // B
+    q = rng.integers(0, 256, (P, n), dtype=np.uint8)
+    if flags & FLAG_INT8:
+        q[q == 0x80] = 0x81
+    else:
+        q[(q & 0x7F) == 0x7F] = 0x7E
+    a = (2.0 ** rng.uniform(-8, 8, (P, nb))).astype(np.float32)
+    sc = (2.0 ** rng.uniform(-10, 2, (P, nb))).astype(np.float32)
+    q[:, B:2 * B] = 0
+    a[:, 1], sc[:, 1] = 1.0, 0.0
+    if P > 1:
+        neg = (-q[1, 2 * B:3 * B].astype(np.int8)).view(np.uint8) if flags & FLAG_INT8 else \
+            q[1, 2 * B:3 * B] ^ 0x80
+        q[0, 2 * B:3 * B] = neg
+        a[0, 2], sc[0, 2] = a[1, 2], sc[1, 2]
+    return q, a, sc
+
+
+@pytest.mark.parametrize("B,P,flags", [(64, 3, 0), (128, 13, 1), (256, 13, 0), (512, 3, 1),
+                                       (64, 64, 1), (256, 64, 0), (512, 64, 0)])
+def test_capped_launches_reduce_any_P(oracle, tfp8, monkeypatch, B, P, flags):
+    # The reduce's general form (any P, in chunks of 8) and its fixed-P forms through the capped
+    # build: n = 2^22 - 37 B elements (2^21 at P = 64) make each of the 1024 wavefronts loop over
+    # 2-4 tiles of 1024 elements.  Every output against the oracle, and bit for bit against the
+    # full library (the grid only changes which wavefront takes which tile).
+    rng = np.random.default_rng(7000 + 10 * B + P + flags)
+    n = (1 << (21 if P == 64 else 22)) - 37 * B
+    q, a, sc = _random_codes(rng, P, n, B, flags)
+    full = tfp8.reduce_fp8(u8_to_gpu(q), f32_to_gpu(a), f32_to_gpu(sc), B, 1.0, flags=flags)
+    with monkeypatch.context() as m:
+        m.setattr(tfp8, "_lib", _capped())
+        got = check_reduce(oracle, tfp8, q, a, sc, B, flags=flags, gpu=True,
+                           what="capped reduce")
+    torch.cuda.synchronize()
+    for u, v in zip(got, full):
+        assert np.array_equal(u, cpu(v)), "capped and full launches differ"
+
+
+@pytest.mark.parametrize("B,P,pad,flags", [(128, 8, 0, 0), (64, 5, 65536 + 1024, 1),
+                                           (512, 13, 16, 0)])
+def test_capped_launches_reduce_strided_messages(oracle, tfp8, monkeypatch, B, P, pad, flags):
+    # the strided reduce from one receive buffer of [codes | alpha | scale] messages, looping
+    # over tiles in the capped build; bit for bit against the full library's contiguous call
+    rng = np.random.default_rng(7500 + B + P)
+    n = (1 << 22) - 37 * B
+    nb = n // B
+    q, a, sc = _random_codes(rng, P, n, B, flags)
+    buf, qv, av, sv = _messages(list(zip(q, a, sc)), n, nb, pad)
+    full = tfp8.reduce_fp8(u8_to_gpu(q), f32_to_gpu(a), f32_to_gpu(sc), B, 1.0, flags=flags)
+    with monkeypatch.context() as m:
+        m.setattr(tfp8, "_lib", _capped())
+        got = tfp8.reduce_fp8(qv, av, sv, B, 1.0, flags=flags)
+    torch.cuda.synchronize()
+    for u, v in zip(got, full):
+        assert torch.equal(u, v), "capped strided and full contiguous reduces differ"
+    rq, ra, rs, rt = oracle.reduce_fp8(q, a, sc, B, 1.0, with_quot=True, flags=flags)
+    nmis, nfb, ea, es = assert_reduce_matches(cpu(got[0]), cpu(got[1]), cpu(got[2]), rq, rt, ra,
+                                              rs, a, sc, B, flags, tie_cap(flags),
+                                              "capped strided reduce")
+    say(f"  capped strided reduce B={B} P={P} pad={pad} flags={flags}: tie mismatches {nmis}"
+        + (f", {nfb} in float64 noise" if nfb else ""))
 
 
 @pytest.mark.parametrize("B,dtype,ntiles,flags", [(512, "f32", 97, 0), (512, "f32", 97, 3),
