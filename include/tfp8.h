@@ -35,7 +35,9 @@
  *     synchronizes; outputs are complete when the stream reaches the launch.
  *   - Element counts are 64-bit, at most TFP8_MAX_N (2^40, several times any one GPU's
  *     memory, so that no byte count or address computed from n can overflow).  n = 0 is a
- *     no-op that returns TFP8_OK.
+ *     no-op: once block, n, the data type, target, flags, P and the strides pass their checks
+ *     the call returns TFP8_OK, and no pointer is examined (NULL, misaligned or overlapping
+ *     pointers are accepted).
  *   - Supported block sizes: 64, 128, 256, 512.
  *   - Alignment: x, out and every codes pointer 16 bytes; alpha and scale 4 bytes.
  *   - Out-of-place (except tfp8_accumulate, which may work in place): an output range that
