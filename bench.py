@@ -332,6 +332,28 @@ def all_workloads(reps: int):
 
         measure(key, "compress", compress_setup(n), n * (3 + 8 / B), 3 * n, n, B, 1, 2 * n,
                 narrow_ref(n))
+
+        # float32 input: the same values widened (exactly), 4 bytes read and 1 written per
+        # element; its same-byte reference is a maximum over the input's four uint8 rows
+        x32 = x[:n].view(torch.bfloat16).float()
+
+        def compress32_setup(i):
+            xi = own(x32, i)
+            q32 = torch.empty(n, dtype=torch.uint8, device=dev)
+            a32 = torch.empty(nb, dtype=torch.float32, device=dev)
+            s32 = torch.empty_like(a32)
+            return lambda: check(tfp8.compress_raw(xi.data_ptr(), tfp8.F32, n, B, TARGET,
+                                                   q32.data_ptr(), a32.data_ptr(), s32.data_ptr(),
+                                                   sh))
+
+        def quarters_ref(i):
+            x8 = own(x32, i).view(torch.uint8).view(4, n)
+            y8 = torch.empty(n, dtype=torch.uint8, device=dev)
+            return lambda: torch.amax(x8, dim=0, out=y8)
+
+        measure(key, "compress fp32 in", compress32_setup, n * (5 + 8 / B), 5 * n, n, B, 1,
+                ref=(quarters_ref, 5 * n, "max of 4 uint8 rows"))
+        del x32
         if P > 1:
             measure(key, f"compress {P} stacked shards", compress_setup(ntot), ntot * (3 + 8 / B),
                     3 * ntot, ntot, B, P, 2 * ntot, narrow_ref(ntot))
