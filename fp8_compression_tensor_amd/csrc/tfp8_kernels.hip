@@ -438,7 +438,9 @@ __global__ __launch_bounds__(kThreads) void k_compress(const void *__restrict__ 
 }
 
 // --------------------------------------------------------------------------------------------
-// K2: decompress.  x = H (s dec q) / (sqrt(B) alpha), same lane layout as compress; one tile per
+// K2: decompress.  x = H (s dec q) / (sqrt(B) alpha), with compress's assignment of each run
+// of 64 elements to 8 lanes (bfloat16 output: that of bfloat16 input; float32 output: that of
+// float32 input); one tile per
 // wavefront, or (LOOP) a grid-stride loop with the next iteration's codes and scales prefetched.
 
 // Decompress keeps 8 lanes per block at every B: its per-block work is small, and at B = 64
@@ -753,9 +755,12 @@ __global__ __launch_bounds__(kThreads) void k_reduce(const uint8_t *__restrict__
 // local gradient g, requantised.  In the rotated domain the main gradient needs no transform:
 // H xhat = sqrt(B) (s / alpha) dec(q) (H unnormalised, (H / sqrt(B))^2 = I), so
 //   w = H z = H g + sqrt(B) (s / alpha) dec(q),
-// and w is requantised exactly like compress requantises H x.  Same lane layout as compress;
-// each lane reads the main gradient's codes at the positions it will write, so the call may
-// work in place.
+// and w is requantised exactly like compress requantises H x.  Lane layout: runs of 8 elements
+// per lane for either gradient type (compress's assignment for bfloat16 input, with 4 lanes
+// per block at B = 64); each lane reads the main gradient's codes at the positions it will write, so
+// the call may work in place.  (A float32 gradient costs the accumulation only a few percent
+// over its bytes: 71-72% of HBM peak against 73-75% for bfloat16, so the line layout of
+// float32 compress is not used here.)
 //
 // Two launches.  k_accumulate works in float32: its rounding errors are ~2^-24 of the larger
 // of the two terms (the float32 transform of g, the product with the factor), which keeps the
