@@ -72,16 +72,17 @@ def _check_reduce(oracle, tfp8, q, a, s, B, T=1.0, what="reduce"):
 
 # ----------------------------------------------------------------------------- Qwen2.5-7B shards, P = 8
 
-def _qwen7b_compressed(oracle, tfp8):
-    """The 8 stacked Qwen2.5-7B-shaped shards compressed by the GPU in one call (the launch that
-    bench.py times: 1.88 GB of input, the XCD-remapped shape) and by the oracle, with the GPU's
-    codes checked on every block and its scales on every block."""
-    wl = WORKLOADS[QWEN7B]
+def _stacked_compressed(oracle, tfp8, key):
+    """The P stacked shards of a workload compressed by the GPU in one call and by the oracle,
+    with the GPU's codes checked on every block and its scales on every block.  For the 8
+    Qwen2.5-7B-shaped shards this is the launch that bench.py times (1.88 GB of input, the
+    XCD-remapped shape)."""
+    wl = WORKLOADS[key]
     B, P, n = wl.block, wl.shards, wl.n
     nbt = P * wl.nblocks
-    say(f"{QWEN7B} ({wl.label}), block {B}, P={P}: generating {P} shards")
-    xs = make_shards(QWEN7B).reshape(P, n)
-    say("  compress of the 8 stacked shards (one call), checked on every block")
+    say(f"{key} ({wl.label}), block {B}, P={P}: generating {P} shards")
+    xs = make_shards(key).reshape(P, n)
+    say(f"  compress of the {P} stacked shards (one call), checked on every block")
     xg = bits_to_gpu(xs.reshape(-1))
     qg, ag, sg = tfp8.compress(xg, B, 1.0)
     torch.cuda.synchronize()
@@ -91,11 +92,15 @@ def _qwen7b_compressed(oracle, tfp8):
     xb = xs.reshape(nbt, B)
     nmis = assert_codes_match_every_block(
         q, qr, B, lambda idx: oracle.compress(xb[idx], B, 1.0, with_quot=True)[3],
-        max_frac=1e-4, what="qwen2.5-7b compress codes (every block)")
-    ea, es = assert_scales(a, s, ar, sr, what="qwen2.5-7b compress (every block)")
-    say(f"  qwen2.5-7b compress: {nbt} blocks, code tie mismatches {nmis} ({nmis / q.size:.2e}), "
+        max_frac=1e-4, what=f"{key} compress codes (every block)")
+    ea, es = assert_scales(a, s, ar, sr, what=f"{key} compress (every block)")
+    say(f"  {key} compress: {nbt} blocks, code tie mismatches {nmis} ({nmis / q.size:.2e}), "
         f"max rel err alpha {ea:.2e} scale {es:.2e}")
     return xs, (qg, ag, sg), (q, a, s), (qr, ar, sr)
+
+
+def _qwen7b_compressed(oracle, tfp8):
+    return _stacked_compressed(oracle, tfp8, QWEN7B)
 
 
 def test_qwen7b_pipeline(oracle, tfp8):
@@ -111,8 +116,18 @@ def test_qwen7b_pipeline(oracle, tfp8):
 
 
 def test_qwen7b_end_to_end_chain(oracle, tfp8):
-    # GPU compress -> GPU reduce (P = 8) -> GPU decompress, each stage fed the GPU's own output of
-    # the stage before (the chain bench.py times), against the oracle's chain on the same shards.
+    # the chain bench.py times: B = 128, P = 8
+    _end_to_end_chain(oracle, tfp8, QWEN7B)
+
+
+def test_gpt6_7b_end_to_end_chain(oracle, tfp8):
+    # B = 256 (decompress with its float64 stages) and the P = 4 reduce
+    _end_to_end_chain(oracle, tfp8, GPT6_7B)
+
+
+def _end_to_end_chain(oracle, tfp8, key):
+    # GPU compress -> GPU reduce (P shards) -> GPU decompress, each stage fed the GPU's own output
+    # of the stage before, against the oracle's chain on the same shards.
     #
     # Bound.  In the rotated domain shard p contributes c_p = (s_p / alpha_p) dec(q_p) and the
     # reduce requantises r = sum_p c_p: its codes are E4M3(448 r / max|r|) and it reconstructs
@@ -127,11 +142,11 @@ def test_qwen7b_end_to_end_chain(oracle, tfp8):
     # max D / max|r| + 1e-6 relative.  Final code mismatches are held to 1e-4 of the elements.
     from tiecheck import E4M3_VALUES, TIE_ABS, TIE_REL
 
-    wl = WORKLOADS[QWEN7B]
+    wl = WORKLOADS[key]
     B, P, n = wl.block, wl.shards, wl.n
     nb = n // B
     T = 1.0
-    xs, (qg, ag, sg), (q, a, s), (qr, ar, sr) = _qwen7b_compressed(oracle, tfp8)
+    xs, (qg, ag, sg), (q, a, s), (qr, ar, sr) = _stacked_compressed(oracle, tfp8, key)
 
     say("  GPU reduce and decompress of the GPU's own compressed shards")
     cqg, cag, csg = tfp8.reduce_fp8(qg.view(P, n), ag.view(P, nb), sg.view(P, nb), B, T)
@@ -160,7 +175,7 @@ def test_qwen7b_end_to_end_chain(oracle, tfp8):
     del q, qr
     Dmax = D.max(axis=1)
     M = 448.0 * rs / ra  # max|r_ref| per block (s' / alpha' = max|r| / 448, fp32-rounded)
-    assert np.all(rs > 0), "a reduced block is zero: the Qwen shards never cancel exactly"
+    assert np.all(rs > 0), "a reduced block is zero: these shards never cancel exactly"
 
     # final codes
     mis = np.nonzero(cq != rq)[0]
@@ -196,7 +211,7 @@ def test_qwen7b_end_to_end_chain(oracle, tfp8):
     e_gpu = np.sqrt(np.dot(og64 - z, og64 - z)) / zn
     e_ref = np.sqrt(np.dot(or64 - z, or64 - z)) / zn
     d_l2 = np.sqrt(np.dot(diff, diff)) / zn
-    say(f"  end to end: {ties.size} compress ties ({ties.size / (P * n):.2e}); {mis.size} final code "
+    say(f"  {key} end to end: {ties.size} compress ties ({ties.size / (P * n):.2e}); {mis.size} final code "
         f"mismatches ({mis.size / n:.2e}); scale rel err max alpha {err_a.max():.2e} s "
         f"{err_s.max():.2e}; reconstruction vs the oracle's: max rel {rel.max():.3e}, mean rel "
         f"{rel.mean():.3e}, rel L2 {d_l2:.3e}; rel L2 error vs the exact sum: GPU chain "
