@@ -72,7 +72,7 @@ def _check_reduce(oracle, tfp8, q, a, s, B, T=1.0, what="reduce"):
 
 # ----------------------------------------------------------------------------- Qwen2.5-7B shards, P = 8
 
-def _stacked_compressed(oracle, tfp8, key):
+def _stacked_compressed(oracle, tfp8, key, flags=0):
     """The P stacked shards of a workload compressed by the GPU in one call and by the oracle,
     with the GPU's codes checked on every block and its scales on every block.  For the 8
     Qwen2.5-7B-shaped shards this is the launch that bench.py times (1.88 GB of input, the
@@ -84,15 +84,16 @@ def _stacked_compressed(oracle, tfp8, key):
     xs = make_shards(key).reshape(P, n)
     say(f"  compress of the {P} stacked shards (one call), checked on every block")
     xg = bits_to_gpu(xs.reshape(-1))
-    qg, ag, sg = tfp8.compress(xg, B, 1.0)
+    qg, ag, sg = tfp8.compress(xg, B, 1.0, flags=flags)
     torch.cuda.synchronize()
     del xg
     q, a, s = cpu(qg), cpu(ag), cpu(sg)
-    qr, ar, sr = oracle.compress(xs.reshape(-1), B, 1.0)
+    qr, ar, sr = oracle.compress(xs.reshape(-1), B, 1.0, flags=flags)
     xb = xs.reshape(nbt, B)
     nmis = assert_codes_match_every_block(
-        q, qr, B, lambda idx: oracle.compress(xb[idx], B, 1.0, with_quot=True)[3],
-        max_frac=1e-4, what=f"{key} compress codes (every block)")
+        q, qr, B, lambda idx: oracle.compress(xb[idx], B, 1.0, with_quot=True, flags=flags)[3],
+        max_frac=tie_cap(flags), what=f"{key} compress codes (every block)",
+        int8=bool(flags & FLAG_INT8))
     ea, es = assert_scales(a, s, ar, sr, what=f"{key} compress (every block)")
     say(f"  {key} compress: {nbt} blocks, code tie mismatches {nmis} ({nmis / q.size:.2e}), "
         f"max rel err alpha {ea:.2e} scale {es:.2e}")
@@ -125,40 +126,52 @@ def test_gpt6_7b_end_to_end_chain(oracle, tfp8):
     _end_to_end_chain(oracle, tfp8, GPT6_7B)
 
 
-def _end_to_end_chain(oracle, tfp8, key):
+@pytest.mark.parametrize("flags", [1, 2, 3])
+def test_gpt6_7b_end_to_end_chain_variants(oracle, tfp8, flags):
+    # the same chain with INT8 codes, without the rotation, and both
+    _end_to_end_chain(oracle, tfp8, GPT6_7B, flags)
+
+
+def _end_to_end_chain(oracle, tfp8, key, flags=0):
     # GPU compress -> GPU reduce (P shards) -> GPU decompress, each stage fed the GPU's own output
     # of the stage before, against the oracle's chain on the same shards.
     #
-    # Bound.  In the rotated domain shard p contributes c_p = (s_p / alpha_p) dec(q_p) and the
-    # reduce requantises r = sum_p c_p: its codes are E4M3(448 r / max|r|) and it reconstructs
-    # H (max|r| / 448) dec(q') / sqrt(B).  The GPU's r differs from the oracle's only through
-    # compress: an admitted tie moves one code of one shard by one E4M3 step (changing r at that
-    # element only), and each of s_p, alpha_p may differ by 1e-6 relative.  So per element
+    # Bound (Q = 448 for E4M3 codes, 127 for INT8; H = I without the rotation).  In the rotated
+    # domain shard p contributes c_p = (s_p / alpha_p) dec(q_p) and the reduce requantises
+    # r = sum_p c_p: its codes are code(Q r / max|r|) and it reconstructs
+    # H (max|r| / Q) dec(q') / sqrt(B).  The GPU's r differs from the oracle's only through
+    # compress: an admitted tie moves one code of one shard by one step of the code format
+    # (changing r at that element only), and each of s_p, alpha_p may differ by 1e-6 relative.
+    # So per element
     #   |r_gpu - r_ref| <= D_i = (1 + e) sum_p f_p |dec(q_gpu,p,i) - dec(q_ref,p,i)|
     #                            + e sum_p f_p |dec(q_ref,p,i)|,      f_p = s_p / alpha_p, e = 2.1e-6,
     # and max|r| moves by at most max_i D_i.  A final code may then differ from the oracle's only
-    # where some quotient within (448 / max|r|) (D_i + max D) of the oracle's exact one, widened by
+    # where some quotient within (Q / max|r|) (D_i + max D) of the oracle's exact one, widened by
     # the tie window, rounds to it; alpha' within 1e-6 + |D|_2 / |r|_2 and s' within that plus
-    # max D / max|r| + 1e-6 relative.  Final code mismatches are held to 1e-4 of the elements.
-    from tiecheck import E4M3_VALUES, TIE_ABS, TIE_REL
+    # max D / max|r| + 1e-6 relative.  Final code mismatches are held to the tie cap of the flags
+    # (1e-4 of the elements; 1e-2 without the rotation).
+    from tiecheck import E4M3_VALUES, INT8_VALUES, TIE_ABS, TIE_REL
 
+    int8 = bool(flags & FLAG_INT8)
+    VALS, Q = (INT8_VALUES, 127.0) if int8 else (E4M3_VALUES, 448.0)
     wl = WORKLOADS[key]
     B, P, n = wl.block, wl.shards, wl.n
     nb = n // B
     T = 1.0
-    xs, (qg, ag, sg), (q, a, s), (qr, ar, sr) = _stacked_compressed(oracle, tfp8, key)
+    xs, (qg, ag, sg), (q, a, s), (qr, ar, sr) = _stacked_compressed(oracle, tfp8, key, flags)
 
     say("  GPU reduce and decompress of the GPU's own compressed shards")
-    cqg, cag, csg = tfp8.reduce_fp8(qg.view(P, n), ag.view(P, nb), sg.view(P, nb), B, T)
-    og = tfp8.decompress(cqg, cag, csg, B, torch.float32)
+    cqg, cag, csg = tfp8.reduce_fp8(qg.view(P, n), ag.view(P, nb), sg.view(P, nb), B, T,
+                                    flags=flags)
+    og = tfp8.decompress(cqg, cag, csg, B, torch.float32, flags=flags)
     torch.cuda.synchronize()
     del qg, ag, sg
     cq, ca, cs, og = cpu(cqg), cpu(cag).astype(np.float64), cpu(csg).astype(np.float64), cpu(og)
     del cqg, cag, csg
     say("  the oracle's chain")
     rq, ra, rs, rt = oracle.reduce_fp8(qr.reshape(P, n), ar.reshape(P, nb), sr.reshape(P, nb), B,
-                                       T, with_quot=True)
-    orf = oracle.decompress(rq, ra, rs, B, np.float32)
+                                       T, with_quot=True, flags=flags)
+    orf = oracle.decompress(rq, ra, rs, B, np.float32, flags=flags)
     ra, rs = ra.astype(np.float64), rs.astype(np.float64)
 
     # D: the bound on |r_gpu - r_ref| per element of the reduced tensor
@@ -166,15 +179,15 @@ def _end_to_end_chain(oracle, tfp8, key):
     f = (sr.astype(np.float64) / ar.astype(np.float64)).reshape(P, nb)
     D = np.zeros((nb, B))
     for p in range(P):
-        D += np.abs(E4M3_VALUES[qr.reshape(P, n)[p]]).reshape(nb, B) * f[p][:, None]
+        D += np.abs(VALS[qr.reshape(P, n)[p]]).reshape(nb, B) * f[p][:, None]
     D *= e
     ties = np.nonzero(q != qr)[0]
     tp, ti = ties // n, ties % n
     np.add.at(D.reshape(-1), ti, (1 + e) * f[tp, ti // B]
-              * np.abs(E4M3_VALUES[q[ties]] - E4M3_VALUES[qr[ties]]))
+              * np.abs(VALS[q[ties]] - VALS[qr[ties]]))
     del q, qr
     Dmax = D.max(axis=1)
-    M = 448.0 * rs / ra  # max|r_ref| per block (s' / alpha' = max|r| / 448, fp32-rounded)
+    M = Q * rs / ra  # max|r_ref| per block (s' / alpha' = max|r| / Q, fp32-rounded)
     assert np.all(rs > 0), "a reduced block is zero: these shards never cancel exactly"
 
     # final codes
@@ -182,13 +195,13 @@ def _end_to_end_chain(oracle, tfp8, key):
     if mis.size:
         k = mis // B
         t = rt[mis]
-        w = (448.0 / (M[k] * (1 - 1e-6))) * (D.reshape(-1)[mis] + Dmax[k]) \
+        w = (Q / (M[k] * (1 - 1e-6))) * (D.reshape(-1)[mis] + Dmax[k]) \
             + TIE_REL * np.abs(t) + TIE_ABS
-        lo, hi = rounding_interval(E4M3_VALUES[cq[mis]])
+        lo, hi = rounding_interval(VALS[cq[mis]], int8=int8)
         ok = (lo <= t + w) & (hi >= t - w)
         assert ok.all(), (f"end-to-end: {int((~ok).sum())} final code mismatches of {mis.size} "
                           f"outside the bound; first at {mis[np.argmax(~ok)]}")
-    assert mis.size <= 1e-4 * n, f"end-to-end: {mis.size} final code mismatches of {n}"
+    assert mis.size <= tie_cap(flags) * n, f"end-to-end: {mis.size} final code mismatches of {n}"
 
     # final scales
     Dl2 = np.sqrt((D * D).sum(axis=1))
@@ -211,7 +224,7 @@ def _end_to_end_chain(oracle, tfp8, key):
     e_gpu = np.sqrt(np.dot(og64 - z, og64 - z)) / zn
     e_ref = np.sqrt(np.dot(or64 - z, or64 - z)) / zn
     d_l2 = np.sqrt(np.dot(diff, diff)) / zn
-    say(f"  {key} end to end: {ties.size} compress ties ({ties.size / (P * n):.2e}); {mis.size} final code "
+    say(f"  {key} flags={flags} end to end: {ties.size} compress ties ({ties.size / (P * n):.2e}); {mis.size} final code "
         f"mismatches ({mis.size / n:.2e}); scale rel err max alpha {err_a.max():.2e} s "
         f"{err_s.max():.2e}; reconstruction vs the oracle's: max rel {rel.max():.3e}, mean rel "
         f"{rel.mean():.3e}, rel L2 {d_l2:.3e}; rel L2 error vs the exact sum: GPU chain "
