@@ -1134,6 +1134,46 @@ def test_accumulate_gradient_workload(oracle, tfp8):
     _check_accumulate(oracle, tfp8, q, a, s, x1, B, "gpt13b-grad accumulate in place", inplace=True)
 
 
+@pytest.mark.parametrize("flags", [0, 1])
+def test_accumulate_micro_batch_chain(oracle, tfp8, flags):
+    # Gradient accumulation over K = 6 micro-batches as AGoQ uses it: the first GPT-13B-shaped
+    # gradient compressed, each later one added in place to the compressed main gradient, then the
+    # result decompressed; on the GPU with its own outputs throughout, and in the oracle.  The two
+    # chains separate only where a step admitted a rounding tie (a tie moves one code by one step,
+    # and the next step carries it on), so the final codes must agree but for a small fraction,
+    # and both reconstructions must be equally close to the exact sum of the K gradients.
+    wl = WORKLOADS[GPT13B_GRAD]
+    B, K, T = wl.block, 6, 1.0
+    gs = make_shards(GPT13B_GRAD, count=K).reshape(K, -1)
+    n = gs.shape[1]
+    say(f"{GPT13B_GRAD}: {K} micro-batch gradients of {n} elements, block {B}, flags {flags}")
+    q, a, sc = tfp8.compress(bits_to_gpu(gs[0]), B, T, flags=flags)
+    for k in range(1, K):
+        tfp8.accumulate(q, a, sc, bits_to_gpu(gs[k]), B, T, inplace=True, flags=flags)
+    out = tfp8.decompress(q, a, sc, B, torch.float32, flags=flags)
+    torch.cuda.synchronize()
+    q, a, sc, out = cpu(q), cpu(a), cpu(sc), cpu(out).astype(np.float64)
+    qr, ar, sr = oracle.compress(gs[0], B, T, flags=flags)
+    for k in range(1, K):
+        qr, ar, sr = oracle.accumulate(qr, ar, sr, gs[k], B, T, flags=flags)
+    ref = oracle.decompress(qr, ar, sr, B, np.float32, flags=flags).astype(np.float64)
+    z = np.zeros(n)
+    for k in range(K):
+        z += bf16_bits_to_f32(gs[k]).astype(np.float64)
+    zn = np.sqrt(np.dot(z, z))
+    e_gpu = np.sqrt(np.dot(out - z, out - z)) / zn
+    e_ref = np.sqrt(np.dot(ref - z, ref - z)) / zn
+    d = np.sqrt(np.dot(out - ref, out - ref)) / zn
+    frac = float((q != qr).mean())
+    ra_err = float(np.max(np.abs(a.astype(np.float64) - ar) / ar))
+    say(f"  micro-batch chain: final codes differing {frac:.2e}, max rel diff alpha {ra_err:.2e}; "
+        f"rel L2 error vs the exact sum: GPU chain {e_gpu:.6e}, oracle chain {e_ref:.6e}; "
+        f"rel L2 difference between the chains {d:.2e}")
+    # K - 1 steps, each admitting ties on at most 1e-4 of the elements, carried forward
+    assert frac <= K * 1e-4, frac
+    assert abs(e_gpu - e_ref) <= 1e-3 * e_ref, (e_gpu, e_ref)
+
+
 @pytest.mark.parametrize("flags", [0, 1, 2, 3])
 @pytest.mark.parametrize("B", [64, 128, 256, 512])
 @pytest.mark.parametrize("gdtype", ["bf16", "f32"])
