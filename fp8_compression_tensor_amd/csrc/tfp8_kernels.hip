@@ -1182,6 +1182,10 @@ __global__ __launch_bounds__(kThreads) void k_accumulate_fix(
 // ============================================================================================
 // Host side of the C ABI: argument checks (before any HIP call), kernel choice, launch shape.
 
+// Build-time caps on each kernel's grid, in workgroups per compute unit (0 = no cap: one
+// wavefront per tile, up to 2^30 work-items).  The library is built without them.  A build with
+// them set makes the kernels' grid-stride loops run at small sizes, for tests of those loops;
+// the caps change only the grid the host picks, not the kernels.
 #ifndef TFP8_COMPRESS_WGS_PER_CU
 #define TFP8_COMPRESS_WGS_PER_CU 0
 #endif
