@@ -447,6 +447,21 @@ def all_workloads(reps: int):
                                                          n, B, TARGET, oq.data_ptr(),
                                                          oa.data_ptr(), os_.data_ptr(), sh))
             measure(key, "accumulate (main + local)", setup, n * (4 + 16 / B), 4 * n, n, B, 1)
+            # the same with the local gradient in float32 (its values widened exactly)
+            g32 = g.view(torch.bfloat16).float()
+
+            def setup32(i):
+                qi, ai, si, gi = own(q[:n], i), own(al[:nb], i), own(sc[:nb], i), own(g32, i)
+                oq = torch.empty(n, dtype=torch.uint8, device=dev)
+                oa = torch.empty(nb, dtype=torch.float32, device=dev)
+                os_ = torch.empty_like(oa)
+                return lambda: check(tfp8.accumulate_raw(qi.data_ptr(), ai.data_ptr(),
+                                                         si.data_ptr(), gi.data_ptr(), tfp8.F32,
+                                                         n, B, TARGET, oq.data_ptr(),
+                                                         oa.data_ptr(), os_.data_ptr(), sh))
+            measure(key, "accumulate, fp32 local gradient", setup32, n * (6 + 16 / B), 6 * n, n, B,
+                    1)
+            del g32
         del x, q, al, sc
         torch.cuda.empty_cache()
     print(json.dumps({"mode": "all-workloads", "reps": reps, "peak_GBps": HBM_PEAK_GBS,
