@@ -36,6 +36,16 @@ def test_library_exports_every_declared_symbol(tfp8):
     assert L.tfp8_version() >> 16 == 1
 
 
+def test_capped_test_build_exports_every_declared_symbol(tfp8):
+    # the launch-capped build that the GPU tests of the grid-stride loops load
+    path = os.path.join(ROOT, "tests", "capped_build", "libtfp8_capped.so")
+    assert os.path.exists(path), f"{path} is not built (tests/capped_build/build.py)"
+    L = tfp8._declare(ctypes.CDLL(path))
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert L.tfp8_version() == tfp8.lib().tfp8_version()
+
+
 def test_status_strings(tfp8):
     for st in range(-7, 1):
         s = tfp8.status_string(st)
