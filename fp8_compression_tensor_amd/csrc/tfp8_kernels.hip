@@ -1134,7 +1134,7 @@ __device__ __forceinline__ void accumulate_block_split(
 // Runs of 64 blocks that one wavefront of k_accumulate_fix scans.  Deeper scans (4, 8, 16 runs)
 // measured 1-8% slower with almost nothing to redo (GPT-13B-shaped gradients) and 4-34% slower
 // with 15% of the blocks to redo (Qwen-shaped shards that share outlier channels): fewer
-// wavefronts then carry the redone blocks.
+// wavefronts then carry the redone blocks.  One run per wavefront was about 1% slower in both.
 constexpr int kFixRuns = 2;
 
 // Position of the n-th set bit (n counted from 0) of m, which has more than n set bits: a binary
