@@ -118,6 +118,34 @@ __device__ __forceinline__ void st_stream(T v, T *p) {
   __builtin_nontemporal_store(v, p);
 }
 
+// Codes of NR runs of 64 elements held in the float32 line layout (lane pj: elements
+// [4 pj, 4 pj + 4) of each run in registers 8 t .. 8 t + 3 of v, [32 + 4 pj, 32 + 4 pj + 4) in
+// 8 t + 4 .. 8 t + 7), stored from run0 on (run t at run0 + RS t).  The two code words of a run
+// (A_pj, B_pj) are not contiguous; lanes pj = 2m and 2m + 1 swap one, so that the even lane
+// stores A_2m A_2m+1 at 8 m and the odd lane B_2m B_2m+1 at 32 + 8 m: 8 contiguous bytes each,
+// every byte of the run once.  The partner (pj ^ 1) is lane j ^ 5 under the lane network's
+// permutation (lane j ^ 1 without the rotation); ds_swizzle reads it (and-mask 31, xor-mask 5 or
+// 1) within the same group of 8 lanes, so under a branch taken by whole groups a lane never
+// reads an inactive one.  All of the swaps are issued before the stores, so that one wait covers
+// them (interleaved, they were slower than no swap at B = 512).
+template <int FLAGS, int NR, int RS, bool ROT>
+__device__ __forceinline__ void store_codes_line(const float *v, float cm, int pj,
+                                                 uint8_t *run0) {
+  const bool odd = pj & 1;
+  u32x2 o[NR];
+#pragma unroll
+  for (int t = 0; t < NR; ++t) {
+    const uint32_t wa = encode4<FLAGS>(v[8 * t + 0], v[8 * t + 1], v[8 * t + 2], v[8 * t + 3], cm);
+    const uint32_t wb = encode4<FLAGS>(v[8 * t + 4], v[8 * t + 5], v[8 * t + 6], v[8 * t + 7], cm);
+    const uint32_t got = __builtin_amdgcn_ds_swizzle(odd ? wa : wb, ROT ? 0x141F : 0x041F);
+    o[t][0] = odd ? got : wa;
+    o[t][1] = odd ? wb : got;
+  }
+  uint8_t *p = run0 + (odd ? 32 + 4 * (pj - 1) : 4 * pj);
+#pragma unroll
+  for (int t = 0; t < NR; ++t) st_stream(o[t], (u32x2 *)(p + RS * t));
+}
+
 // --------------------------------------------------------------------------------------------
 // Range-safe scales: from the rotated values of one block (held by a group of L lanes) to the
 // code multiplier, alpha and s, for any block -- all-zero, bfloat16-subnormal or huge.
@@ -400,31 +428,10 @@ __global__ __launch_bounds__(kThreads) void k_compress(const void *__restrict__ 
             st_stream(w, (u32x2 *)(cb + co + RS * g));
           }
         } else {
-          // Lane pj holds the codes of [4 pj, 4 pj + 4) and [32 + 4 pj, 32 + 4 pj + 4) of each
-          // run (words A_pj, B_pj).  Lanes pj = 2m and 2m + 1 swap one word, so that the even
-          // one stores A_2m A_2m+1 at 8 m and the odd one B_2m B_2m+1 at 32 + 8 m: 8 contiguous
-          // bytes each, every byte of the run once.  The partner (pj ^ 1) is lane j ^ 5 under
-          // the lane network's permutation, lane j ^ 1 without the rotation; ds_swizzle reads
-          // it (and-mask 31, xor-mask 5 or 1), in the same group of 8 lanes, so a lane never
-          // reads one that this branch left inactive.  All of a block's exchanges are issued
-          // before its stores, so that one wait covers them.
+          // the float32 line layout: this block's runs, through the partner swap
           constexpr int GB = G / BG;  // runs of this block in the lane
-          const bool odd = pj & 1;
-          u32x2 o[GB];
-#pragma unroll
-          for (int t = 0; t < GB; ++t) {
-            const int g = b * GB + t;
-            const uint32_t wa =
-                encode4<FLAGS>(v[8 * g + 0], v[8 * g + 1], v[8 * g + 2], v[8 * g + 3], cm);
-            const uint32_t wb =
-                encode4<FLAGS>(v[8 * g + 4], v[8 * g + 5], v[8 * g + 6], v[8 * g + 7], cm);
-            const uint32_t got = __builtin_amdgcn_ds_swizzle(odd ? wa : wb, ROT ? 0x141F : 0x041F);
-            o[t][0] = odd ? got : wa;
-            o[t][1] = odd ? wb : got;
-          }
-          const uint32_t co = BG * bw * B + (odd ? 32 + 4 * (pj - 1) : 4 * pj);
-#pragma unroll
-          for (int t = 0; t < GB; ++t) st_stream(o[t], (u32x2 *)(cb + co + RS * (b * GB + t)));
+          store_codes_line<FLAGS, GB, RS, ROT>(&v[8 * GB * b], cm, pj,
+                                               cb + BG * bw * B + RS * GB * b);
         }
         if (j == 0) {
           alpha_out[blk] = alpha;
@@ -920,23 +927,7 @@ __global__ __launch_bounds__(kThreads) void k_accumulate(
     if (active) {
       if (!defer) {
         if constexpr (LINE) {
-          // the partner swap of compress's float32 path: lanes pj = 2m, 2m + 1 (j and j ^ 5, or
-          // j ^ 1 without the rotation, in the same group) each store 8 contiguous code bytes
-          const bool odd = pj & 1;
-          u32x2 o[G];
-#pragma unroll
-          for (int g = 0; g < G; ++g) {
-            const uint32_t wa =
-                encode4<FLAGS>(v[8 * g + 0], v[8 * g + 1], v[8 * g + 2], v[8 * g + 3], cm);
-            const uint32_t wb =
-                encode4<FLAGS>(v[8 * g + 4], v[8 * g + 5], v[8 * g + 6], v[8 * g + 7], cm);
-            const uint32_t got = __builtin_amdgcn_ds_swizzle(odd ? wa : wb, ROT ? 0x141F : 0x041F);
-            o[g][0] = odd ? got : wa;
-            o[g][1] = odd ? wb : got;
-          }
-          uint8_t *cb = codes_out + blk * B + (odd ? 32 + 4 * (pj - 1) : 4 * pj);
-#pragma unroll
-          for (int g = 0; g < G; ++g) st_stream(o[g], (u32x2 *)(cb + RS * g));
+          store_codes_line<FLAGS, G, RS, ROT>(v, cm, pj, codes_out + blk * B);
         } else {
           uint8_t *cb = codes_out + blk * B + 8 * pj;
 #pragma unroll
