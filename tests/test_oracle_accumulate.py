@@ -59,6 +59,22 @@ def test_two_routes_agree(oracle, flags, gdtype):
 
 
 @pytest.mark.parametrize("flags", FLAG_SETS)
+@pytest.mark.parametrize("route", ["definition", "rotated"])
+def test_target_scaling(oracle, flags, route):
+    # alpha = clamp(sqrt(T / m2)) with m2 the second moment of the sum, which does not depend on
+    # T: a target 4 times larger doubles alpha exactly, hence y and s, and leaves every quotient
+    # and code as it was (no block here reaches the clamp)
+    q, a, s = _main(oracle, flags)
+    g = random_bf16_bits(q.size, seed=11, scale=0.02)
+    f = oracle.accumulate if route == "definition" else oracle.accumulate_rotated
+    for T in (1.0, 2.0 ** -6, 37.5):
+        q1, a1, s1, t1 = f(q, a, s, g, 128, T, with_quot=True, flags=flags)
+        q4, a4, s4, t4 = f(q, a, s, g, 128, 4 * T, with_quot=True, flags=flags)
+        assert np.array_equal(q4, q1) and np.array_equal(t4, t1)
+        assert np.array_equal(a4, 2 * a1) and np.array_equal(s4, 2 * s1)
+
+
+@pytest.mark.parametrize("flags", FLAG_SETS)
 def test_requantisation_error_identity(oracle, flags):
     # ||xhat_out - (xhat_in + g)|| = ||s' (dec q' - t')|| / alpha' per block
     B = 128

@@ -363,6 +363,21 @@ def test_reduce_two_routes_agree(oracle, P, B):
     assert aa[0] == 1.0 and sa[0] == 0.0
 
 
+@pytest.mark.parametrize("route", ["definition", "rotated"])
+def test_reduce_target_scaling(oracle, route):
+    # alpha = clamp(sqrt(T / m2)) with m2 the sum's second moment, which does not depend on T:
+    # a target 4 times larger doubles alpha exactly (sqrt(4 x) = 2 sqrt(x) in binary), hence y and
+    # s, and leaves every quotient and code as it was (no block here reaches the clamp)
+    P, B = 4, 128
+    q, a, s = _shards(oracle, P, B=B, nblk=24)
+    f = oracle.reduce_fp8 if route == "definition" else oracle.reduce_fp8_rotated
+    for T in (1.0, 2.0 ** -6, 37.5):
+        q1, a1, s1, t1 = f(q, a, s, B, T, with_quot=True)
+        q4, a4, s4, t4 = f(q, a, s, B, 4 * T, with_quot=True)
+        assert np.array_equal(q4, q1) and np.array_equal(t4, t1)
+        assert np.array_equal(a4, 2 * a1) and np.array_equal(s4, 2 * s1)
+
+
 def test_reduce_reconstruction_identity(oracle):
     # the reduce's output reconstructs the float64 sum of the reconstructions up to exactly
     # its own requantisation error

@@ -63,6 +63,34 @@ MUTANTS = [
     ("decompress ignores no-rotation",
      "if (!(flags & TFP8_REF_NO_ROTATION)) {\n    tfp8_ref_fwht(out, B);",
      "if (1) {\n    tfp8_ref_fwht(out, B);", 0),
+    ("post-scale from the unrotated input", "for (int i = 0; i < B; ++i) my = fmax(my, fabs(y[i]));",
+     "for (int i = 0; i < B; ++i) my = fmax(my, fabs(v[i]));", 0),
+    ("quotient with the unrounded scale", "double t = y[i] / (double)s;",
+     "double t = y[i] * code_qmax(flags) / my;", 0),
+    ("reduce averages", "for (int i = 0; i < block; ++i) z[i] += xh[i];",
+     "for (int i = 0; i < block; ++i) z[i] += xh[i] / P;", 0),
+    ("reduce ignores the target",
+     "compress_block(z, block, (double)target, flags, codes_out + k * block, alpha_out + k,",
+     "compress_block(z, block, 1.0, flags, codes_out + k * block, alpha_out + k,", 0),
+    ("reduce decodes variant codes as E4M3", "for (int i = 0; i < block; ++i) c[i] = code_value(q[i], flags);",
+     "for (int i = 0; i < block; ++i) c[i] = code_value(q[i], 0);", 0),
+    ("rotated reduce energy without 1/B", "double a = sqrt(T / (sumsq / block));",
+     "double a = sqrt(T / sumsq);", 0),
+    ("rotated reduce quotient without alpha", "double t = (double)alpha2 * r[i] / (double)s2;",
+     "double t = r[i] / (double)s2;", 0),
+    ("accumulate ignores the target",
+     "compress_block(z, block, (double)target, flags, codes_out + k * block, alpha_out + k,",
+     "compress_block(z, block, 1.0, flags, codes_out + k * block, alpha_out + k,", 1),
+    ("accumulate subtracts the local gradient",
+     "for (int i = 0; i < block; ++i) z[i] += load_elem(grad, grad_dtype, k * block + i);",
+     "for (int i = 0; i < block; ++i) z[i] -= load_elem(grad, grad_dtype, k * block + i);", 0),
+    ("accumulate reads block 0's scales", "decompress_block(c, alpha[k], scale[k], block, flags, z);",
+     "decompress_block(c, alpha[0], scale[0], block, flags, z);", 0),
+    ("accumulate decodes variant codes as E4M3",
+     "for (int i = 0; i < block; ++i) c[i] = code_value(codes[k * block + i], flags);",
+     "for (int i = 0; i < block; ++i) c[i] = code_value(codes[k * block + i], 0);", 0),
+    ("rotated accumulate energy without the rotation's 1/B",
+     "double m2 = (rotate ? sumsq / block : sumsq) / block;", "double m2 = sumsq / block;", 0),
 ]
 
 
