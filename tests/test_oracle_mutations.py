@@ -91,6 +91,30 @@ MUTANTS = [
      "for (int i = 0; i < block; ++i) c[i] = code_value(codes[k * block + i], 0);", 0),
     ("rotated accumulate energy without the rotation's 1/B",
      "double m2 = (rotate ? sumsq / block : sumsq) / block;", "double m2 = sumsq / block;", 0),
+    ("INT8 saturates at 128", "if (k > 127.0) k = 127.0;", "if (k > 128.0) k = 128.0;", 0),
+    ("INT8 no negative saturation", "if (k < -127.0) k = -127.0;", "", 0),
+    ("energy from |x|", "for (int i = 0; i < B; ++i) sumsq += v[i] * v[i];",
+     "for (int i = 0; i < B; ++i) sumsq += fabs(v[i]);", 0),
+    ("FWHT misses its last stage", "for (int64_t h = 1; h < len; h <<= 1)",
+     "for (int64_t h = 1; h < len / 2; h <<= 1)", 0),
+    ("bf16 widened by 15 bits", "uint32_t u = (uint32_t)((const uint16_t *)x)[i] << 16;",
+     "uint32_t u = (uint32_t)((const uint16_t *)x)[i] << 15;", 0),
+    ("alpha clamp at 2^-127", "a = fmin(fmax(a, 0x1p-126), 0x1p126);\n  float alpha",
+     "a = fmin(fmax(a, 0x1p-127), 0x1p126);\n  float alpha", 0),
+    ("prescale with the unrounded alpha", "y[i] = (double)alpha * v[i];", "y[i] = a * v[i];", 0),
+    ("zero test on the first element", "for (int i = 0; i < B; ++i) ax = fmax(ax, fabs(v[i]));",
+     "ax = fabs(v[0]);", 0),
+    ("encode subnormal range ends at 2^-7", "if (a < 0x1p-6) {", "if (a < 0x1p-7) {", 0),
+    ("encode exponent carry dropped", "if (k == 16.0) {\n    E += 1;", "if (k == 16.0) {\n    E += 0;", 0),
+    ("decode NaN pattern ignored", "if (e == 15 && m == 7) return NAN;", "", 0),
+    ("bf16 output truncated", "double r = nearbyint(a / step) * step;",
+     "double r = trunc(a / step) * step;", 0),
+    ("bf16 subnormal step 2^-134", "double step = (E < -126) ? 0x1p-133 : ldexp(1.0, E - 7);",
+     "double step = (E < -126) ? 0x1p-134 : ldexp(1.0, E - 7);", 0),
+    ("decompress divides by B", "for (int i = 0; i < B; ++i) out[i] = out[i] / rootB;\n  }\n  for",
+     "for (int i = 0; i < B; ++i) out[i] = out[i] / B;\n  }\n  for", 0),
+    ("decompress zero block left undefined", "for (int i = 0; i < B; ++i) out[i] = 0.0;\n    return;",
+     "return;", 0),
 ]
 
 
