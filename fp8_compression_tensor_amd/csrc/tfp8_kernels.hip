@@ -14,7 +14,10 @@
 // group holds B/L elements as runs of 8 consecutive elements, run g covering elements
 // [8Lg + 8j, 8Lg + 8j + 8) of the block: each group reads or writes whole runs of 8L
 // consecutive elements.  At L = 8 index bits 0-2 and 6.. live in registers, bits 3-5 across the
-// lanes (at B = 64 in compress, run g is block g of the pair).
+// lanes (at B = 64 in compress, run g is block g of the pair).  float32 data (compress's input,
+// decompress's output, accumulate's gradient at 8 lanes per block) takes another assignment
+// within each run of 64: lane j holds [4 j, 4 j + 4) and [32 + 4 j, 32 + 4 j + 4), so that each
+// 16-byte access instruction of a group covers whole lines (see load_compress_at).
 //
 // Launch.  One tile (64/L blocks) per wavefront, 8- or 16-byte vector loads and stores per
 // lane, no LDS, no atomics.  Compress of an input of 1.5 GiB or more launches
@@ -233,7 +236,8 @@ __device__ __forceinline__ void load_compress_at(CompressIn<B, F32IN> &in, const
   }
 }
 
-// The same runs of block blk, for accumulate.
+// Runs of 8 consecutive elements of block blk for either input type (lane j: [RS g + 8 j,
+// RS g + 8 j + 8)): the layout of accumulate at 4 lanes per block, and of its fix pass.
 template <int B, bool F32IN>
 __device__ __forceinline__ void load_compress_in(CompressIn<B, F32IN> &in, const void *xin,
                                                  int64_t blk, int j) {
@@ -977,8 +981,8 @@ __device__ __forceinline__ void load_fix_in(FixIn<B, F32IN> &f, const uint8_t *c
   f.ap = -alpha_out[blk];
 }
 
-// One set-aside block, by the group of L lanes j = 0..L-1 that holds it (lane layout of
-// k_accumulate).  Its codes and s are still those of the main gradient (never written) and
+// One set-aside block, by the group of L lanes j = 0..L-1 that holds it (runs of 8 consecutive
+// elements per lane for either gradient type).  Its codes and s are still those of the main gradient (never written) and
 // alpha_out holds -alpha.  `active` = 0: work on the block but store nothing.  Lane j reads codes
 // at positions 8 qj and writes them at 8 pj, where another lane of the group read; in place that
 // is safe because every stored value depends, through the lane exchanges, on all of the group's
