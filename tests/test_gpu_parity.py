@@ -1680,6 +1680,125 @@ def test_capped_launches_remapped_loop_every_block(oracle, capped, B, dtype, nti
                              seed=4034 + 8 * B + flags, cancel=(1, 4))
 
 
+# The capped launches at the boundary of their loops.  A capped launch has W = 4 x (compute
+# units) wavefronts.  Each kernel runs at three tile counts: W (one tile per wavefront, the last
+# one short by a block: compress and decompress take their one-tile forms), W + 1 (wavefront 0
+# takes a second tile holding a single block, loaded while it works on its first) and 2 W + 1
+# (a third, ragged tile for wavefront 0).  The accumulation's second kernel scans 128 blocks per
+# wavefront and iteration; at B = 64 and 128 it also runs at W + 1 scans, with set-aside blocks in
+# wavefront 0's first and second scans, in the last scan of wavefront W - 1 and in the last
+# block.  Every output against the oracle, and bit for bit against the full library, whose
+# launches take one tile per wavefront.
+def _capped_waves():
+    return 4 * torch.cuda.get_device_properties(DEV).multi_processor_count
+
+
+def _boundary_counts(W, bpt):
+    """Block counts for W tiles of bpt blocks (the last one short by a block), W + 1 tiles (the
+    last holding one block) and 2 W + 1 tiles (the last holding about half)."""
+    return (W * bpt - 1, W * bpt + 1, 2 * W * bpt + max(1, bpt // 2 - 1))
+
+
+def _boundary_input(rng, nb, B, dense=()):
+    """float32 values of nb blocks: Laplace bodies at scales 2^-30..2^30 with zero,
+    bfloat16-subnormal and outlier blocks; the blocks in `dense` are plain Laplace blocks."""
+    v = rng.laplace(0, 1, (nb, B)) * 2.0 ** rng.integers(-30, 30, (nb, 1))
+    kind = rng.integers(0, 16, nb)
+    kind[list(dense)] = 15
+    v[kind == 0] = 0.0
+    v[kind == 1] = rng.integers(-64, 65, (int((kind == 1).sum()), B)) * 2.0 ** -133
+    v[kind == 2, :3] *= 1e3
+    return v.reshape(-1).astype(np.float32)
+
+
+def _same_bits(u, v):
+    u, v = np.ascontiguousarray(u), np.ascontiguousarray(v)
+    return u.shape == v.shape and np.array_equal(u.view(np.uint8), v.view(np.uint8))
+
+
+@pytest.mark.parametrize("B,flags", [(64, 0), (128, 1), (256, 2), (512, 3)])
+def test_capped_launches_at_the_loop_boundary(oracle, tfp8, monkeypatch, B, flags):
+    W = _capped_waves()
+    capped = _capped()
+    rng = np.random.default_rng(8100 + B + flags)
+
+    def both(fn):
+        # fn() through the full library, then through the capped build
+        full = fn()
+        torch.cuda.synchronize()
+        with monkeypatch.context() as m:
+            m.setattr(tfp8, "_lib", capped)
+            got = fn()
+            torch.cuda.synchronize()
+        return full, got
+
+    # compress, bfloat16 and float32 input
+    for f32 in (False, True):
+        for nb in _boundary_counts(W, 16 if B == 64 else 8):
+            v = _boundary_input(rng, nb, B)
+            x = v if f32 else f32_to_bf16_bits(v)
+            what = f"capped compress B={B} flags={flags} {'f32' if f32 else 'bf16'} nb={nb}"
+            say(what)
+            full, got = both(lambda: check_compress(oracle, tfp8, x, B, what=what, flags=flags,
+                                                    gpu=True))
+            for u, w in zip(got, full):
+                assert _same_bits(u, w), what + ": capped and full launches differ"
+
+    # decompress of the oracle's codes, float32 and bfloat16 output
+    for nb in _boundary_counts(W, 8):
+        q, a, s = oracle.compress(f32_to_bf16_bits(_boundary_input(rng, nb, B)), B, 1.0,
+                                  flags=flags)
+        what = f"capped decompress B={B} flags={flags} nb={nb}"
+        say(what)
+        qg, ag, sg = u8_to_gpu(q), f32_to_gpu(a), f32_to_gpu(s)
+        full, got = both(lambda: [cpu(tfp8.decompress(qg, ag, sg, B, torch.float32, flags=flags)),
+                                  gpu_bf16_bits(tfp8.decompress(qg, ag, sg, B, torch.bfloat16,
+                                                                flags=flags))])
+        for u, w in zip(got, full):
+            assert _same_bits(u, w), what + ": capped and full launches differ"
+        with monkeypatch.context() as m:
+            m.setattr(tfp8, "_lib", capped)
+            check_decompress(oracle, tfp8, q, a, s, B, what=what, flags=flags)
+
+    # the reduce: its fixed-P forms (P = 2, 8) and its general form (P = 3), on contributions
+    # compressed by the oracle, the first three blocks of contribution 1 the negation of
+    # contribution 0's
+    for P, nb in zip((2, 3, 8), _boundary_counts(W, 1024 // B)):
+        xs = [_boundary_input(rng, nb, B) for _ in range(P)]
+        xs[1].reshape(nb, B)[:3] = -xs[0].reshape(nb, B)[:3]
+        enc = [oracle.compress(f32_to_bf16_bits(v), B, 1.0, flags=flags) for v in xs]
+        q, a, s = (np.stack([e[k] for e in enc]) for k in range(3))
+        what = f"capped reduce B={B} flags={flags} P={P} nb={nb}"
+        say(what)
+        full, got = both(lambda: check_reduce(oracle, tfp8, q, a, s, B, what=what, flags=flags,
+                                              gpu=True))
+        for u, w in zip(got, full):
+            assert _same_bits(u, w), what + ": capped and full launches differ"
+
+    # the accumulation: the streaming kernel at the boundary of its loop, and at B <= 128 the
+    # second kernel at the boundary of its own (W + 1 scans of 128 blocks)
+    counts = list(_boundary_counts(W, 16 if B == 64 else 8))
+    if B <= 128:
+        counts.append(W * 128 + 3)
+    for i, nb in enumerate(counts):
+        cancel = sorted({0, 5, min(W * 128 - 2, nb - 2), min(W * 128 + 1, nb - 1), nb - 1})
+        v = _boundary_input(rng, nb, B, dense=cancel)
+        x = f32_to_bf16_bits(v)
+        q, a, s = oracle.compress(x, B, 1.0, flags=flags)
+        g = _boundary_input(rng, nb, B)
+        g.reshape(nb, B)[cancel] = -bf16_bits_to_f32(x).reshape(nb, B)[cancel]
+        f32 = i % 2 == 1
+        gl = g if f32 else f32_to_bf16_bits(g)
+        inplace = i == 2
+        what = (f"capped accumulate B={B} flags={flags} {'f32' if f32 else 'bf16'} nb={nb} "
+                f"inplace={inplace}")
+        say(what)
+        full, got = both(lambda: _check_accumulate(oracle, tfp8, q, a, s, gl, B, what,
+                                                   flags=flags, inplace=inplace))
+        for u, w in zip(got, full):
+            assert _same_bits(u, w), what + ": capped and full launches differ"
+
+
 def _sweep_input(rng, nb, B):
     """A mixture of block kinds: Laplace bodies at random scales, outlier blocks, zero blocks,
     bfloat16-subnormal blocks and huge blocks."""
