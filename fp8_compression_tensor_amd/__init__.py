@@ -317,6 +317,8 @@ def accumulate(codes: torch.Tensor, alpha: torch.Tensor, scale: torch.Tensor, gr
     _need_buf(alpha, torch.float32, nb, "alpha")
     _need_buf(scale, torch.float32, nb, "scale")
     if inplace:
+        if out is not None:
+            raise ValueError("give either out or inplace=True, not both")
         out = (codes, alpha, scale)
     elif out is None:
         out = (torch.empty_like(codes), torch.empty_like(alpha), torch.empty_like(scale))

@@ -825,6 +825,9 @@ def test_wrappers_check_buffers_before_launch(tfp8):
         tfp8.accumulate(u8(n), f32(nb), f32(nb), x, B, out=(u8(n), f32(nb), f32(nb + 1)))
     with pytest.raises(ValueError, match="contiguous"):
         tfp8.decompress(u8(2 * n)[::2], f32(nb), f32(nb), B)
+    with pytest.raises(ValueError, match="not both"):
+        tfp8.accumulate(u8(n), f32(nb), f32(nb), x, B, out=(u8(n), f32(nb), f32(nb)),
+                        inplace=True)
     torch.cuda.synchronize()
 
 
