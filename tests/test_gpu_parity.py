@@ -674,6 +674,50 @@ def test_reduce_strided_packed_messages(oracle, tfp8, B, P, pad, flags):
     say(f"  strided reduce B={B} P={P} pad={pad} flags={flags}: tie mismatches {nmis}")
 
 
+def test_reduce_strided_random_layouts(tfp8, monkeypatch):
+    # 300 seeded layouts with the three row strides drawn apart: P in 1..64, every B and flag
+    # set, 3-3000 blocks, the codes' rows n plus up to 1 MiB apart (a multiple of 16 bytes), the
+    # alpha and scale rows nb plus up to 4096 floats apart.  The padding between rows holds
+    # random bytes (codes) and NaN (scales), so a read outside the rows would show.  The strided
+    # call must equal the contiguous call bit for bit (that one is held to the oracle above),
+    # through the full library and through the capped build, whose wavefronts loop over tiles.
+    capped = _capped()
+    rng = np.random.default_rng(9100)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(9100)
+    total = 0
+    for case in range(300):
+        B = int(rng.choice([64, 128, 256, 512]))
+        flags = int(rng.integers(0, 4))
+        P = min(64, int(np.exp(rng.uniform(0, np.log(65)))))
+        nb = int(np.exp(rng.uniform(np.log(3), np.log(3000))))
+        n = nb * B
+        cst = n + 16 * int(rng.integers(0, 1 << 16))
+        ast, sst = nb + int(rng.integers(0, 4097)), nb + int(rng.integers(0, 4097))
+        q, a, s = _random_codes(rng, P, n, B, flags)
+        what = f"strided layout case {case}: B={B} flags={flags} P={P} nb={nb} strides {cst} {ast} {sst}"
+        total += P * n
+        qbuf = torch.randint(0, 256, (P * cst,), dtype=torch.uint8, device=DEV, generator=gen)
+        abuf = torch.full((P * ast,), float("nan"), dtype=torch.float32, device=DEV)
+        sbuf = torch.full((P * sst,), float("nan"), dtype=torch.float32, device=DEV)
+        qv = qbuf.as_strided((P, n), (cst, 1))
+        av = abuf.as_strided((P, nb), (ast, 1))
+        sv = sbuf.as_strided((P, nb), (sst, 1))
+        qv.copy_(u8_to_gpu(q))
+        av.copy_(f32_to_gpu(a))
+        sv.copy_(f32_to_gpu(s))
+        ref = tfp8.reduce_fp8(u8_to_gpu(q), f32_to_gpu(a), f32_to_gpu(s), B, 1.0, flags=flags)
+        got = tfp8.reduce_fp8(qv, av, sv, B, 1.0, flags=flags)
+        with monkeypatch.context() as m:
+            m.setattr(tfp8, "_lib", capped)
+            got_capped = tfp8.reduce_fp8(qv, av, sv, B, 1.0, flags=flags)
+        torch.cuda.synchronize()
+        for u, v, w in zip(ref, got, got_capped):
+            assert _same_bits(cpu(u), cpu(v)), what
+            assert _same_bits(cpu(u), cpu(w)), what + " (capped build)"
+    say(f"  300 strided layouts ({total} codes in all) equal the contiguous reduce bit for bit")
+
+
 def test_sharded_two_shot_dataflow_equals_whole_reduce(oracle, tfp8):
     # The data flow of a two-shot compressed all-reduce over P ranks, on one GPU: each rank's
     # chunk (a block-aligned 1/P of every contribution) is reduced where it lies, through the
