@@ -27,6 +27,8 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
        python bench.py --copy-calibrate   (plain 1 GiB device copy, for HBM counter scaling)
        python bench.py --all-workloads      (every operation on every workload, warm and with the
                                            caches flushed, beside same-byte references)
+       python bench.py --size-curve         (compress, decompress and the reduce from 2^19 to
+                                           2^31 elements, flushed and rotating)
 """
 from __future__ import annotations
 
@@ -175,6 +177,62 @@ def cpu_model() -> str:
     return "unknown"
 
 
+def _event():
+    import torch
+
+    return torch.cuda.Event(enable_timing=True)
+
+
+def _timed(fn, flushed, reps, stream, flush):
+    """Median and minimum duration (us) of single launches fn(), after 3 untimed ones, each
+    bracketed by events on `stream`; with `flushed`, a read of `flush` before each launch."""
+    import statistics
+
+    ts = []
+    for i in range(reps + 3):
+        if flushed:
+            flush.sum()  # reads the buffer: evicts the caches without leaving dirty lines
+        a, b = _event(), _event()
+        a.record(stream)
+        fn()
+        b.record(stream)
+        b.synchronize()
+        if i >= 3:
+            ts.append(a.elapsed_time(b) * 1e3)
+    return statistics.median(ts), min(ts)
+
+
+def _rotating(setup, set_bytes, stream, rot_bytes=3 << 30):
+    """Steady-state duration (us) of back-to-back launches cycling through distinct buffer sets:
+    setup(i) -> launch closure on set i, with enough sets (2 to 256) to total rot_bytes, timed
+    over whole cycles after a 0.4 s settle; median of 5 runs of 4 cycles.  Returns (us, sets)."""
+    import statistics
+
+    import torch
+
+    R = min(256, max(2, -(-rot_bytes // int(set_bytes))))
+    fns = [setup(i) for i in range(R)]
+    # settle: the timed cycles then run at the loaded clock level (right after single-launch
+    # protocols the clocks are measurably lower)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 0.4:
+        for f in fns:
+            f()
+        torch.cuda.synchronize()
+    ts = []
+    for _ in range(5):
+        a, b = _event(), _event()
+        a.record(stream)
+        for k in range(4 * R):
+            fns[k % R]()
+        b.record(stream)
+        b.synchronize()
+        ts.append(a.elapsed_time(b) * 1e3 / (4 * R))
+    del fns
+    torch.cuda.empty_cache()
+    return statistics.median(ts), R
+
+
 def all_workloads(reps: int):
     """Every operation on every workload, three ways: warm, flushed, and rotating (see below),
     beside same-byte references; one JSON object on stdout, a table on stderr.
@@ -187,8 +245,6 @@ def all_workloads(reps: int):
               outputs) totalling at least 3 GiB (at most 256 sets), timed over whole cycles:
               nothing stays cached between a set's uses and every write-back is paid inside
               the sequence.  The steady-state rate of a stream of such calls."""
-    import statistics
-
     import numpy as np
     import torch
 
@@ -211,47 +267,12 @@ def all_workloads(reps: int):
         if st != 0:
             raise RuntimeError(tfp8.status_string(st))
 
-    def event():
-        return torch.cuda.Event(enable_timing=True)
-
     def timed(fn, flushed):
-        ts = []
-        for i in range(reps + 3):
-            if flushed:
-                flush.sum()  # reads 1 GiB: evicts the caches without leaving dirty lines
-            a, b = event(), event()
-            a.record(stream)
-            fn()
-            b.record(stream)
-            b.synchronize()
-            if i >= 3:
-                ts.append(a.elapsed_time(b) * 1e3)
-        return statistics.median(ts), min(ts)
+        return _timed(fn, flushed, reps, stream, flush)
 
     def rotating(setup, set_bytes):
-        # setup(i) -> launch closure on buffer set i (set 0: the case's own buffers); at most
-        # 256 sets (the small workloads: still more than 1.5x the 256 MB MALL)
-        R = min(256, max(2, -(-rot_bytes // int(set_bytes))))
-        fns = [setup(i) for i in range(R)]
-        # settle: cycle for 0.4 s first, so the timed cycles run at the loaded clock level (right
-        # after the single-launch protocols the clocks are measurably lower)
-        t0 = time.perf_counter()
-        while time.perf_counter() - t0 < 0.4:
-            for f in fns:
-                f()
-            torch.cuda.synchronize()
-        ts = []
-        for _ in range(5):
-            a, b = event(), event()
-            a.record(stream)
-            for k in range(4 * R):
-                fns[k % R]()
-            b.record(stream)
-            b.synchronize()
-            ts.append(a.elapsed_time(b) * 1e3 / (4 * R))
-        del fns
-        torch.cuda.empty_cache()
-        return statistics.median(ts), R
+        # at most 256 sets (the small workloads: still more than 1.5x the 256 MB MALL)
+        return _rotating(setup, set_bytes, stream, rot_bytes)
 
     rows = []
 
@@ -475,6 +496,130 @@ def all_workloads(reps: int):
                       "rows": rows}), flush=True)
 
 
+def size_curve(reps: int):
+    """Compress (bfloat16 in), decompress (bfloat16 out) and the P = 8 reduce at B = 128 over
+    sizes from 2^19 to 2^31 elements (the reduce: 2^16 to 2^28 per contribution), flushed and
+    rotating as in --all-workloads, beside the same-byte references; one JSON object on stdout, a
+    table on stderr.  The values are the Qwen2.5-7B-shaped activation shard's, repeated past its
+    117 M elements; the reduce's P contributions are consecutive chunks of their codes."""
+    import numpy as np
+    import torch
+
+    from workloads import WORKLOADS, make_shard
+
+    wl = WORKLOADS[STEP_WORKLOAD]
+    B, P = wl.block, wl.shards
+    xs = make_shard(STEP_WORKLOAD, 0).reshape(-1)
+    log("input generated")
+
+    import fp8_compression_tensor_amd as tfp8
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB, > L2 + MALL
+
+    def check(st):
+        if st != 0:
+            raise RuntimeError(tfp8.status_string(st))
+
+    nmax = 1 << 31
+    x = torch.empty(nmax, dtype=torch.int16, device=dev)
+    src = torch.from_numpy(xs.view(np.int16)).to(dev)
+    for off in range(0, nmax, src.numel()):
+        k = min(src.numel(), nmax - off)
+        x[off:off + k].copy_(src[:k])
+    del src
+    q = torch.empty(nmax, dtype=torch.uint8, device=dev)
+    al = torch.empty(nmax // B, dtype=torch.float32, device=dev)
+    sc = torch.empty_like(al)
+    check(tfp8.compress_raw(x.data_ptr(), tfp8.BF16, nmax, B, TARGET, q.data_ptr(), al.data_ptr(),
+                            sc.data_ptr(), sh))
+
+    def own(t, i):  # set 0 uses the tensor itself, other sets a copy of it
+        return t if i == 0 else t.clone()
+
+    rows = []
+
+    def frac(nbytes, us):
+        return nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS
+
+    def measure(op, m, setup, alg_bytes, ref=None):
+        fm, _ = _timed(setup(0), True, reps, stream, flush)
+        rm, R = _rotating(setup, alg_bytes, stream)
+        row = {"op": op, "elements": m, "block": B, "bytes_algorithmic": int(alg_bytes),
+               "flushed_us": round(fm, 2), "flushed_frac_of_peak": round(frac(alg_bytes, fm), 4),
+               "rotating_us": round(rm, 3), "rotating_sets": R,
+               "rotating_frac_of_peak": round(frac(alg_bytes, rm), 4)}
+        if ref is not None:
+            rsetup, rbytes, rname = ref
+            rfm, _ = _timed(rsetup(0), True, reps, stream, flush)
+            rrm, _ = _rotating(rsetup, rbytes, stream)
+            row.update({"ref": rname, "ref_bytes": int(rbytes), "ref_flushed_us": round(rfm, 2),
+                        "ref_rotating_us": round(rrm, 3),
+                        "ratio_rotating": round(frac(alg_bytes, rm) / frac(rbytes, rrm), 4)})
+        rows.append(row)
+        log(f"{op:24s} n={m:>11d}: flushed {fm:9.1f} us ({100 * row['flushed_frac_of_peak']:.1f}%), "
+            f"rotating {rm:9.2f} us ({100 * row['rotating_frac_of_peak']:.1f}%)"
+            + (f"; {row['ref']}: rotating {row['ref_rotating_us']:.2f} us, ratio "
+               f"{row['ratio_rotating']:.3f}" if ref is not None else ""))
+
+    for e in range(19, 32):
+        m = 1 << e
+        mb = m // B
+
+        def compress_setup(i, m=m, mb=mb):
+            xi = own(x[:m], i)
+            oq = torch.empty(m, dtype=torch.uint8, device=dev)
+            oa = torch.empty(mb, dtype=torch.float32, device=dev)
+            os_ = torch.empty_like(oa)
+            return lambda: check(tfp8.compress_raw(xi.data_ptr(), tfp8.BF16, m, B, TARGET,
+                                                   oq.data_ptr(), oa.data_ptr(), os_.data_ptr(),
+                                                   sh))
+
+        def halves_ref(i, m=m):
+            x8 = own(x[:m], i).view(torch.uint8)
+            y8 = torch.empty(m, dtype=torch.uint8, device=dev)
+            return lambda: torch.maximum(x8[:m], x8[m:], out=y8)
+
+        measure("compress", m, compress_setup, m * (3 + 8 / B),
+                (halves_ref, 3 * m, "uint8 max of two halves"))
+
+        def decompress_setup(i, m=m, mb=mb):
+            qi, ai, si = own(q[:m], i), own(al[:mb], i), own(sc[:mb], i)
+            out = torch.empty(m, dtype=torch.bfloat16, device=dev)
+            return lambda: check(tfp8.decompress_raw(qi.data_ptr(), ai.data_ptr(), si.data_ptr(),
+                                                     m, B, out.data_ptr(), tfp8.BF16, sh))
+
+        measure("decompress bf16", m, decompress_setup, m * (3 + 8 / B))
+
+    for e in range(16, 29):
+        c = 1 << e
+        cb = c // B
+
+        def reduce_setup(i, c=c, cb=cb):
+            qi, ai, si = own(q[:P * c], i), own(al[:P * cb], i), own(sc[:P * cb], i)
+            oq = torch.empty(c, dtype=torch.uint8, device=dev)
+            oa = torch.empty(cb, dtype=torch.float32, device=dev)
+            os_ = torch.empty_like(oa)
+            return lambda: check(tfp8.reduce_fp8_raw(qi.data_ptr(), ai.data_ptr(), si.data_ptr(),
+                                                     P, c, B, TARGET, oq.data_ptr(),
+                                                     oa.data_ptr(), os_.data_ptr(), sh))
+
+        def rows_ref(i, c=c):
+            rq = own(q[:P * c], i).view(P, c)
+            y8 = torch.empty(c, dtype=torch.uint8, device=dev)
+            return lambda: torch.amax(rq, dim=0, out=y8)
+
+        measure(f"reduce P={P}", c, reduce_setup, (P + 1) * c * (1 + 8 / B),
+                (rows_ref, (P + 1) * c, f"max of {P} uint8 rows"))
+    print(json.dumps({"mode": "size-curve", "reps": reps, "peak_GBps": HBM_PEAK_GBS,
+                      "protocols": {"flushed": "a 1 GiB read (sum) between single launches",
+                                    "rotating": "back-to-back launches cycling through distinct "
+                                                "buffer sets of >= 3 GiB in total"},
+                      "rows": rows}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -489,6 +634,8 @@ def main():
     ap.add_argument("--copy-calibrate", action="store_true")
     ap.add_argument("--all-workloads", action="store_true",
                     help="time every operation on every workload, warm and flushed (own JSON)")
+    ap.add_argument("--size-curve", action="store_true",
+                    help="time compress, decompress and the reduce over a range of sizes (own JSON)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -501,6 +648,9 @@ def main():
         return
     if args.all_workloads:
         all_workloads(max(min(args.steps, 50), 5))
+        return
+    if args.size_curve:
+        size_curve(max(min(args.steps, 50), 5))
         return
 
     from workloads import WORKLOADS, make_shards
