@@ -346,6 +346,29 @@ def test_reduce_contribution_and_its_negation_cancel(oracle):
     assert np.all(ao == 1.0) and np.all(so == 0.0) and np.all(qo == 0)
 
 
+@pytest.mark.parametrize("route", ["definition", "rotated"])
+def test_reduce_sums_in_contribution_order(oracle, route):
+    # The sum runs over p = 0, 1, ..., P - 1.  With a large contribution x first, its exact
+    # negation second and a contribution y 2^40 times smaller last, x + (-x) is exactly zero
+    # before y is added, so the reduce of [x, -x, y] is the reduce of [y] alone, bit for bit.
+    # In any other order y would meet x or -x first and lose its low bits to the rounding.
+    B = 128
+    q, a, s = _shards(oracle, 2, B=B, nblk=24)
+    big = s[0] * np.float32(2.0 ** 20)
+    small = s[1] * np.float32(2.0 ** -20)
+    q3 = np.stack([q[0], q[0] ^ 0x80, q[1]])
+    a3 = np.stack([a[0], a[0], a[1]])
+    s3 = np.stack([big, big, small])
+    f = oracle.reduce_fp8 if route == "definition" else oracle.reduce_fp8_rotated
+    q1, a1, s1, t1 = f(q3[2:], a3[2:], s3[2:], B, 1.0, with_quot=True)
+    qr, ar, sr, tr = f(q3, a3, s3, B, 1.0, with_quot=True)
+    assert np.array_equal(qr, q1) and np.array_equal(tr, t1)
+    assert np.array_equal(ar, a1) and np.array_equal(sr, s1)
+    # the pin has teeth: summed from the last contribution down, the result differs
+    qb, ab, sb, tb = f(q3[::-1].copy(), a3[::-1].copy(), s3[::-1].copy(), B, 1.0, with_quot=True)
+    assert not (np.array_equal(tb, t1) and np.array_equal(ab, a1))
+
+
 @pytest.mark.parametrize("P,B", [(4, 256), (8, 128), (3, 64)])
 def test_reduce_two_routes_agree(oracle, P, B):
     q, a, s = _shards(oracle, P, B=B, nblk=40)

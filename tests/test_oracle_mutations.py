@@ -115,6 +115,12 @@ MUTANTS = [
      "for (int i = 0; i < B; ++i) out[i] = out[i] / B;\n  }\n  for", 0),
     ("decompress zero block left undefined", "for (int i = 0; i < B; ++i) out[i] = 0.0;\n    return;",
      "return;", 0),
+    ("reduce sums in reverse order",
+     "    for (int p = 0; p < P; ++p) {\n      const uint8_t *q = codes + (int64_t)p * n + k * block;",
+     "    for (int p = P - 1; p >= 0; --p) {\n      const uint8_t *q = codes + (int64_t)p * n + k * block;",
+     0),
+    ("rotated reduce sums in reverse order", "    for (int p = 0; p < P; ++p) {\n      float s = scale[",
+     "    for (int p = P - 1; p >= 0; --p) {\n      float s = scale[", 0),
 ]
 
 
