@@ -779,6 +779,23 @@ def test_reduce_identities(oracle, tfp8):
     nz = s > 0
     assert_rel_close(cpu(cs)[nz] / cpu(ca)[nz], s[nz].astype(np.float64) / a[nz], 1e-6,
                      what="s/alpha under P=1")
+    # summed in the order p = 0, 1, 2: a large contribution and its exact negation cancel before
+    # a contribution 2^40 times smaller is added, so [x, -x, y] reduces to exactly what [y] alone
+    # does (the products g_p dec(q_p) are exact, and so is each partial sum here), through the
+    # general any-P form and a fixed-P form (a zero contribution appended)
+    y = oracle.compress(make_shard(TINY, 1).reshape(-1), B, 1.0)
+    big = s * np.float32(2.0 ** 20)
+    one = tfp8.reduce_fp8(u8_to_gpu(y[0][None]), f32_to_gpu(y[1][None]),
+                          f32_to_gpu((y[2] * np.float32(2.0 ** -20))[None]), B, 1.0)
+    for P in (3, 4):
+        qs = [q, q ^ 0x80, y[0], np.zeros_like(q)][:P]
+        as_ = [a, a, y[1], np.ones_like(a)][:P]
+        ss = [big, big, y[2] * np.float32(2.0 ** -20), np.zeros_like(s)][:P]
+        got = tfp8.reduce_fp8(u8_to_gpu(np.stack(qs)), f32_to_gpu(np.stack(as_)),
+                              f32_to_gpu(np.stack(ss)), B, 1.0)
+        torch.cuda.synchronize()
+        for u, v in zip(got, one):
+            assert torch.equal(u.view(torch.uint8), v.view(torch.uint8)), f"[x, -x, y] P={P}"
 
 
 @pytest.mark.parametrize("flags", [0, 1])
