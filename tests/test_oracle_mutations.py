@@ -121,6 +121,22 @@ MUTANTS = [
      0),
     ("rotated reduce sums in reverse order", "    for (int p = 0; p < P; ++p) {\n      float s = scale[",
      "    for (int p = P - 1; p >= 0; --p) {\n      float s = scale[", 0),
+    ("bf16 subnormal range ends at 2^-127", "double step = (E < -126) ?", "double step = (E < -127) ?", 0),
+    ("accumulate reads a float32 gradient as bfloat16",
+     "z[i] += load_elem(grad, grad_dtype, k * block + i);",
+     "z[i] += load_elem(grad, TFP8_REF_BF16, k * block + i);", 0),
+    ("rotated accumulate reads a float32 gradient as bfloat16",
+     "w[i] = load_elem(grad, grad_dtype, k * block + i);",
+     "w[i] = load_elem(grad, TFP8_REF_BF16, k * block + i);", 0),
+    ("rotated accumulate post-scale without 1/sqrt(B)",
+     "float s2 = (float)((double)alpha2 * aw / div / Q);",
+     "float s2 = (float)((double)alpha2 * aw / Q);", 0),
+    ("compress max misses the last element",
+     "for (int i = 0; i < B; ++i) my = fmax(my, fabs(y[i]));",
+     "for (int i = 0; i < B - 1; ++i) my = fmax(my, fabs(y[i]));", 0),
+    ("compress energy misses the last element",
+     "for (int i = 0; i < B; ++i) sumsq += v[i] * v[i];",
+     "for (int i = 0; i < B - 1; ++i) sumsq += v[i] * v[i];", 0),
 ]
 
 
