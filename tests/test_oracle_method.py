@@ -369,6 +369,26 @@ def test_reduce_sums_in_contribution_order(oracle, route):
     assert not (np.array_equal(tb, t1) and np.array_equal(ab, a1))
 
 
+def test_reduce_rotated_route_scales_by_the_stored_alpha(oracle):
+    # With one contribution the rotated route's sum is r = (s / alpha) dec(q), formed here in
+    # float64 as the definition states it.  Requantising r uses the stored (float32) prescale:
+    # y = alpha' r, s' = max|y| / Q rounded to float32, and the quotients y / s'.  So the
+    # quotients must be alpha' r / s' and s' must be float32(alpha' max|r| / Q) exactly, with
+    # alpha' = float32(sqrt(T / mean(r^2))) to within its last bit (the sum of squares may round
+    # in another order).  A route that scaled by the unrounded alpha would miss both.
+    B, Q = 128, 448.0
+    q, a, s = _shards(oracle, 1, B=B, nblk=48)
+    qo, ao, so, t = oracle.reduce_fp8_rotated(q, a, s, B, 1.0, with_quot=True)
+    r = (s[0].astype(np.float64) / a[0].astype(np.float64))[:, None] * \
+        E4M3_VALUES[q[0]].reshape(-1, B)
+    a64 = ao.astype(np.float64)
+    assert np.all(s[0] > 0)
+    assert np.array_equal(so, (a64 * np.abs(r).max(axis=1) / Q).astype(np.float32))
+    assert np.array_equal(t.reshape(-1, B), a64[:, None] * r / so.astype(np.float64)[:, None])
+    alpha_def = np.sqrt(1.0 / np.mean(r * r, axis=1)).astype(np.float32)
+    assert np.all(np.abs(ao.view(np.int32) - alpha_def.view(np.int32)) <= 1)
+
+
 @pytest.mark.parametrize("P,B", [(4, 256), (8, 128), (3, 64)])
 def test_reduce_two_routes_agree(oracle, P, B):
     q, a, s = _shards(oracle, P, B=B, nblk=40)

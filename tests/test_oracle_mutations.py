@@ -137,6 +137,21 @@ MUTANTS = [
     ("compress energy misses the last element",
      "for (int i = 0; i < B; ++i) sumsq += v[i] * v[i];",
      "for (int i = 0; i < B - 1; ++i) sumsq += v[i] * v[i];", 0),
+    ("rotated reduce quotient with the unrounded alpha",
+     "double t = (double)alpha2 * r[i] / (double)s2;", "double t = a * r[i] / (double)s2;", 0),
+    ("rotated reduce scale with the unrounded alpha",
+     "float s2 = (float)((double)alpha2 * ar / Q);", "float s2 = (float)(a * ar / Q);", 0),
+    ("scale rounded twice", "float s = (float)(my / code_qmax(flags));",
+     "float s = (float)my / (float)code_qmax(flags);", 0),
+    ("INT8 encode half away from zero", "double k = nearbyint(v);", "double k = round(v);", 0),
+    ("reduce reconstructs variant codes with the rotation",
+     "scale[(int64_t)p * nb + k], block, flags, xh);",
+     "scale[(int64_t)p * nb + k], block, flags & TFP8_REF_INT8, xh);", 0),
+    ("rotated accumulate quotient with the unrounded alpha",
+     "double t = (double)alpha2 * w[i] / div / (double)s2;",
+     "double t = a * w[i] / div / (double)s2;", 0),
+    ("rotated accumulate scale with the unrounded alpha",
+     "float s2 = (float)((double)alpha2 * aw / div / Q);", "float s2 = (float)(a * aw / div / Q);", 0),
 ]
 
 
