@@ -295,6 +295,30 @@ def test_exact_inverse_without_rounding(oracle, B):
     assert np.all(np.abs(back - xv) <= 1e-14 * scale)
 
 
+def test_decompress_bf16_rounds_once(oracle):
+    # The bfloat16 output is the exact reconstruction rounded once.  With alpha = float32(256/257),
+    # s = 1 and the code of 1.0 (no rotation: x = s dec(q) / alpha), the reconstruction 1/alpha
+    # lies 2.3e-10 above 1 + 2^-8, the midpoint between the bfloat16 neighbours 1 and 1 + 2^-7.
+    # Rounded once it is 1 + 2^-7; rounded to float32 first it would become the midpoint itself
+    # and then round to even, 1.
+    from fractions import Fraction
+
+    from tiecheck import FLAG_NO_ROTATION
+
+    B = 64
+    alpha = np.float32(256 / 257)
+    eps = 1 / Fraction(float(alpha)) - Fraction(257, 256)
+    assert 0 < eps < Fraction(1, 2 ** 25)  # the case is the one described
+    one = int(np.flatnonzero(E4M3_VALUES == 1.0)[0])
+    q = np.full(2 * B, one, np.uint8)
+    q[B:] |= 0x80  # block 1: the code of -1.0
+    a, s = np.full(2, alpha, np.float32), np.ones(2, np.float32)
+    out16 = oracle.decompress(q, a, s, B, np.uint16, flags=FLAG_NO_ROTATION)
+    assert np.all(out16[:B] == 0x3F81) and np.all(out16[B:] == 0xBF81)
+    out32 = oracle.decompress(q, a, s, B, np.float32, flags=FLAG_NO_ROTATION)
+    assert np.all(out32[:B] == np.float32(1 + 2.0 ** -8))
+
+
 def test_decompress_dtypes_agree_with_f64(oracle):
     x = _tiny_shard(oracle)
     B = 128

@@ -152,6 +152,13 @@ MUTANTS = [
      "double t = a * w[i] / div / (double)s2;", 0),
     ("rotated accumulate scale with the unrounded alpha",
      "float s2 = (float)((double)alpha2 * aw / div / Q);", "float s2 = (float)(a * aw / div / Q);", 0),
+    ("decompress to bf16 rounds twice",
+     "((uint16_t *)out)[k * block + i] = tfp8_ref_round_bf16(r[i]);",
+     "((uint16_t *)out)[k * block + i] = tfp8_ref_round_bf16((double)(float)r[i]);", 0),
+    ("compress reads float32 input as bfloat16",
+     "v[i] = load_elem(x, x_dtype, k * block + i);\n    compress_block(v, block, (double)target, flags,",
+     "v[i] = load_elem(x, TFP8_REF_BF16, k * block + i);\n    compress_block(v, block, (double)target, flags,",
+     0),
 ]
 
 
