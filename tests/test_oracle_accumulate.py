@@ -58,6 +58,30 @@ def test_two_routes_agree(oracle, flags, gdtype):
     assert np.all(np.abs(ab.astype(np.float64) - aa) <= F32_ULP * aa)
 
 
+@pytest.mark.parametrize("route", ["definition", "rotated"])
+def test_clamps_alpha_of_tiny_sums(oracle, route):
+    # a main gradient compressed from bfloat16-subnormal blocks plus a local gradient of the
+    # same kind: the sum's mean square is below 2^-252, so alpha is clamped at 2^126, in either
+    # route
+    from workloads import f32_to_bf16_bits
+
+    B, nb = 128, 8
+    rng = np.random.default_rng(32)
+
+    def tiny():
+        k = rng.integers(-(2 ** 6), 2 ** 6, (nb, B))
+        k[:, 0] = 2 ** 6
+        return f32_to_bf16_bits((k.astype(np.float64) * 2.0 ** -133).astype(np.float32).reshape(-1))
+
+    q, a, s = oracle.compress(tiny(), B, 1.0)
+    g = tiny()
+    f = oracle.accumulate if route == "definition" else oracle.accumulate_rotated
+    qo, ao, so = f(q, a, s, g, B, 1.0)
+    z = (oracle.decompress_f64(q, a, s, B) + bf16_bits_to_f32(g)).reshape(nb, B)
+    assert np.all(np.sqrt(1.0 / np.mean(z * z, axis=1)) > 2.0 ** 126)
+    assert np.all(ao == np.float32(2.0 ** 126)) and np.all(so > 0)
+
+
 @pytest.mark.parametrize("flags", FLAG_SETS)
 @pytest.mark.parametrize("route", ["definition", "rotated"])
 def test_target_scaling(oracle, flags, route):

@@ -413,6 +413,30 @@ def test_reduce_rotated_route_scales_by_the_stored_alpha(oracle):
     assert np.all(np.abs(ao.view(np.int32) - alpha_def.view(np.int32)) <= 1)
 
 
+def _subnormal_blocks(rng, nb, B):
+    # bfloat16-subnormal blocks k * 2^-133, |k| <= 64, each with a peak of 2^-127: their
+    # sqrt(1/m2) passes 2^126, so compress clamps alpha there
+    k = rng.integers(-(2 ** 6), 2 ** 6, (nb, B))
+    k[:, 0] = 2 ** 6
+    return f32_to_bf16_bits((k.astype(np.float64) * 2.0 ** -133).astype(np.float32).reshape(-1))
+
+
+@pytest.mark.parametrize("route", ["definition", "rotated"])
+def test_reduce_clamps_alpha_of_tiny_sums(oracle, route):
+    # two contributions compressed from bfloat16-subnormal blocks: their sum's mean square is
+    # still below 2^-252, so the reduce's alpha is clamped at 2^126 too, in either route
+    B, nb = 128, 8
+    rng = np.random.default_rng(31)
+    enc = [oracle.compress(_subnormal_blocks(rng, nb, B), B, 1.0) for _ in range(2)]
+    q, a, s = (np.stack([e[i] for e in enc]) for i in range(3))
+    assert np.all(a == np.float32(2.0 ** 126))
+    f = oracle.reduce_fp8 if route == "definition" else oracle.reduce_fp8_rotated
+    qo, ao, so = f(q, a, s, B, 1.0)
+    z = sum(oracle.decompress_f64(q[p], a[p], s[p], B) for p in range(2)).reshape(nb, B)
+    assert np.all(np.sqrt(1.0 / np.mean(z * z, axis=1)) > 2.0 ** 126)
+    assert np.all(ao == np.float32(2.0 ** 126)) and np.all(so > 0)
+
+
 @pytest.mark.parametrize("P,B", [(4, 256), (8, 128), (3, 64)])
 def test_reduce_two_routes_agree(oracle, P, B):
     q, a, s = _shards(oracle, P, B=B, nblk=40)

@@ -159,6 +159,12 @@ MUTANTS = [
      "v[i] = load_elem(x, x_dtype, k * block + i);\n    compress_block(v, block, (double)target, flags,",
      "v[i] = load_elem(x, TFP8_REF_BF16, k * block + i);\n    compress_block(v, block, (double)target, flags,",
      0),
+    ("alpha clamp at 2^127", "a = fmin(fmax(a, 0x1p-126), 0x1p126);",
+     "a = fmin(fmax(a, 0x1p-126), 0x1p127);", 0),
+    ("rotated reduce alpha clamp at 2^127", "a = fmin(fmax(a, 0x1p-126), 0x1p126);",
+     "a = fmin(fmax(a, 0x1p-126), 0x1p127);", 1),
+    ("rotated accumulate alpha clamp at 2^127", "a = fmin(fmax(a, 0x1p-126), 0x1p126);",
+     "a = fmin(fmax(a, 0x1p-126), 0x1p127);", 2),
 ]
 
 
