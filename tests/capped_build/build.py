@@ -2,8 +2,8 @@
 launch capped at one workgroup per compute unit (TFP8_*_WGS_PER_CU = 1), so that inputs of a few
 tens of MB run the kernels' grid-stride loops with many tiles per wavefront.  The caps change
 only the host's choice of grid; the kernels are the same.  The GPU tests route the package's
-calls through this build to check the looping forms at every block size, input type and flag
-set, at sizes the full build reaches only past 2^34-2^36 elements."""
+calls through this capped library to check the looping forms at every block size, input type
+and flag set, at sizes the full library reaches only past 2^34-2^36 elements."""
 from __future__ import annotations
 
 import importlib.util
