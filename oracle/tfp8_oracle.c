@@ -13,7 +13,7 @@
  *
  * Readings where the pages leave a step open:
  *   - a block is `block` consecutive elements of the flat buffer; the Hadamard size is `block`;
- *   - the "second moment (energy)" is the raw mean of squares m2 = sum(v^2)/block;
+ *   - the block's second moment, its energy, is the raw mean of squares m2 = sum(v^2)/block;
  *   - the prescale brings that energy to the target: alpha = sqrt(target/m2), clamped to
  *     [2^-126, 2^126] so that alpha and 1/alpha are normal fp32 numbers;
  *   - the rotation is the Sylvester Hadamard in natural order, normalised by 1/sqrt(block),
