@@ -485,6 +485,33 @@ def test_reduce_reconstruction_identity(oracle):
 
 # ------------------------------------------------------------------------------ arguments
 
+def test_argument_bounds(oracle):
+    # the target's contract is [2^-64, 2^64] with both ends included (the next float32 outside
+    # either end is rejected), and a reduce needs P >= 1
+    B = 128
+    x = random_bf16_bits(2 * B, seed=12)
+    q, a, s = oracle.compress(x, B, 1.0)
+    below = float(np.nextafter(np.float32(2.0 ** -64), np.float32(0)))
+    above = float(np.nextafter(np.float32(2.0 ** 64), np.float32(np.inf)))
+    for T in (2.0 ** -64, 2.0 ** 64):
+        oracle.compress(x, B, T)
+        oracle.reduce_fp8(q[None], a[None], s[None], B, T)
+        oracle.accumulate(q, a, s, x, B, T)
+    for T in (below, above):
+        with pytest.raises(ValueError, match="-6"):
+            oracle.compress(x, B, T)
+        with pytest.raises(ValueError, match="-6"):
+            oracle.reduce_fp8(q[None], a[None], s[None], B, T)
+        with pytest.raises(ValueError, match="-6"):
+            oracle.accumulate(q, a, s, x, B, T)
+    out_q, out_f = np.zeros(2 * B, np.uint8), np.zeros(2, np.float32)
+    for P, want in ((0, -6), (-1, -6), (1, 0)):
+        st = oracle.raw_status("tfp8_ref_reduce_ex", q.ctypes.data, a.ctypes.data, s.ctypes.data,
+                               P, 2 * B, B, 1.0, 0, out_q.ctypes.data, out_f.ctypes.data,
+                               out_f.ctypes.data, None)
+        assert st == want, (P, st)
+
+
 def test_argument_errors(oracle):
     x = np.zeros(256, np.uint16)
     with pytest.raises(ValueError, match="-3"):

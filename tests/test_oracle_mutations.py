@@ -165,6 +165,9 @@ MUTANTS = [
      "a = fmin(fmax(a, 0x1p-126), 0x1p127);", 1),
     ("rotated accumulate alpha clamp at 2^127", "a = fmin(fmax(a, 0x1p-126), 0x1p126);",
      "a = fmin(fmax(a, 0x1p-126), 0x1p127);", 2),
+    ("target lower bound exclusive", "!(target >= 0x1p-64f)", "!(target > 0x1p-64f)", 0),
+    ("target upper bound exclusive", "!(target <= 0x1p64f)", "!(target < 0x1p64f)", 0),
+    ("reduce accepts P = 0", "if (P < 1) return TFP8_REF_E_ARG;", "if (P < 0) return TFP8_REF_E_ARG;", 0),
 ]
 
 
