@@ -18,8 +18,8 @@ from gpu_helpers import (DEV, assert_codes_match_every_block, assert_reduce_matc
                          assert_periodic_codes, assert_periodic_decompress, fill_periodic,
                          bits_to_gpu, check_compress, check_decompress, check_reduce, cpu,
                          f32_to_gpu, gpu_bf16_bits, say, u8_to_gpu)
-from tiecheck import (FLAG_INT8, FLAG_NO_ROTATION, assert_codes_match, assert_rel_close,
-                      rounding_interval, tie_cap)
+from tiecheck import (E4M3_VALUES, FLAG_INT8, FLAG_NO_ROTATION, assert_codes_match,
+                      assert_rel_close, rounding_interval, tie_cap)
 from workloads import (GPT2_7B, GPT6_7B, GPT13B_GRAD, QWEN7B, TINY, WORKLOADS, bf16_bits_to_f32,
                        f32_to_bf16_bits, make_shard, make_shards, random_bf16_bits)
 
@@ -519,6 +519,26 @@ def test_accumulate_every_fp32_value_onto_zero_main(oracle, tfp8):
     assert bad.size == 0, (f"{bad.size} codes differ; first at value {g[bad[0]]!r}: "
                            f"got {q[bad[0]]:#04x}, oracle {qr[bad[0]]:#04x}")
     assert_scales(a, s, ar, sr, what="accumulate every-value blocks")
+
+
+def test_decompress_bf16_at_a_double_rounding_tie(oracle, tfp8):
+    # alpha = float32(256/257), s = 1 and the code of +-1.0 without the rotation reconstruct to
+    # +-1/alpha, 2.3e-10 beyond the bfloat16 midpoint 1 + 2^-8.  The oracle rounds that once, to
+    # 1 + 2^-7; the kernel multiplies in float32, which lands on the midpoint, then rounds to
+    # even.  The float32 output is exact there, and the bfloat16 output is one of the two
+    # neighbours, a mismatch the comparison admits only because the exact value sits at the tie.
+    B = 64
+    one = int(np.flatnonzero(E4M3_VALUES == 1.0)[0])
+    q = np.full(2 * B, one, np.uint8)
+    q[B:] |= 0x80
+    a = np.full(2, np.float32(256 / 257), np.float32)
+    s = np.ones(2, np.float32)
+    o32 = check_decompress(oracle, tfp8, q, a, s, B, what="double-rounding tie",
+                           flags=FLAG_NO_ROTATION)
+    assert np.all(cpu(o32)[:B] == np.float32(1 + 2.0 ** -8))
+    o16 = gpu_bf16_bits(tfp8.decompress(u8_to_gpu(q), f32_to_gpu(a), f32_to_gpu(s), B,
+                                        torch.bfloat16, flags=FLAG_NO_ROTATION))
+    assert set(o16[:B].tolist()) <= {0x3F80, 0x3F81} and set(o16[B:].tolist()) <= {0xBF80, 0xBF81}
 
 
 @pytest.mark.parametrize("B", [128, 256, 512])
